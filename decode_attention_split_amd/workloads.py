@@ -1,0 +1,121 @@
+"""Decode-attention workloads: the per-layer geometries of Gemma-3/4-style hybrid stacks.
+
+Geometry sources (page titles and sections):
+  * "Gemma 4 12B (unified multimodal)" record, "KV geometry, now derived" and the
+    layer_types passage: 40 sliding layers with 8 KV heads of head_dim 256, 8 full
+    layers with 1 KV head of global_head_dim 512, full layers at 0-based indices
+    5, 11, ..., 47, attention_k_eq_v true, bounded sliding window.
+  * "Gemma4-26B-A4B on Apple Silicon", Results (Break 4): per-layer-type head dims and
+    KV-head counts; K/V sharing on full layers.  Threats to validity: the query scale
+    defaults to 1/sqrt(head_dim) per geometry.
+  * "Gemma support" pull request, Summary: soft-capping, sliding-window layers, mixed
+    256/512 head sizes, K = V global attention.
+
+Nothing here computes attention; these are shapes, seeds and counts.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import List, Optional
+
+import numpy as np
+
+LINEAR = 0
+RING = 1
+
+
+def default_scale(head_dim: int) -> float:
+    """float32(1/sqrt(head_dim)): the default query pre-attention scale."""
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+@dataclass(frozen=True)
+class LayerGeom:
+    """One attention layer's decode geometry."""
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    kind: int            # LINEAR or RING
+    capacity: int        # ring: W slots; linear: C positions
+    window: int          # <= 0: full causal
+    k_eq_v: bool         # one cached tensor serves as keys and values
+    softcap: float = 0.0  # <= 0: off
+    scale: Optional[float] = None  # None: 1/sqrt(head_dim)
+
+    @property
+    def q_scale(self) -> float:
+        return default_scale(self.head_dim) if self.scale is None else float(np.float32(self.scale))
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def kv_bytes_per_token(self, count_v_for_k_eq_v: bool = False) -> int:
+        """bf16 bytes one token adds to this layer's cache (K, plus V unless K = V)."""
+        tensors = 1 if (self.k_eq_v and not count_v_for_k_eq_v) else 2
+        return self.num_kv_heads * self.head_dim * tensors * 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    ctx_lo: int
+    ctx_hi: int
+    layers: List[LayerGeom] = field(default_factory=list)
+
+    @property
+    def num_layers(self) -> int:
+        return len(self.layers)
+
+
+def sliding_geom(num_q, num_kv, window, softcap=0.0, scale=None, head_dim=256):
+    return LayerGeom(num_q, num_kv, head_dim, RING, window, window, False, softcap, scale)
+
+
+def global_geom(num_q, capacity, head_dim=512, num_kv=1, softcap=0.0, scale=None):
+    return LayerGeom(num_q, num_kv, head_dim, LINEAR, capacity, 0, True, softcap, scale)
+
+
+def gemma4_12b_layer_types(num_layers: int = 48, period: int = 6) -> List[str]:
+    """Layer schedule: full attention at 0-based index l when l % period == period - 1."""
+    return ["full_attention" if (l % period) == period - 1 else "sliding_attention"
+            for l in range(num_layers)]
+
+
+def hybrid_layers(num_layers=48, sliding=None, full=None) -> List[LayerGeom]:
+    sliding = sliding or sliding_geom(16, 8, 1024)
+    full = full or global_geom(16, 16384)
+    return [full if t == "full_attention" else sliding for t in gemma4_12b_layer_types(num_layers)]
+
+
+def kv_bytes_per_token(layers: List[LayerGeom], count_v_for_k_eq_v: bool = False) -> int:
+    return sum(g.kv_bytes_per_token(count_v_for_k_eq_v) for g in layers)
+
+
+# The five synthetic workloads (seed = index).
+TINY = Workload("tiny sliding decode, B1 4q/1kv hd256 ctx64 ring w32 softcap50", 1, 1, 64, 64,
+                [sliding_geom(4, 1, 32, softcap=50.0, scale=1.0 / 16)])
+G3_1B_SLIDING = Workload("gemma3-1b sliding layer, B32 4q/1kv hd256 ring w512 ctx U[1,1024]", 2, 32,
+                         1, 1024, [sliding_geom(4, 1, 512, scale=1.0 / 16)])
+G4_12B_SLIDING = Workload("gemma4-12b sliding layer, B64 16q/8kv hd256 ring w1024 ctx U[512,8192]"
+                          " softcap50", 3, 64, 512, 8192,
+                          [sliding_geom(16, 8, 1024, softcap=50.0, scale=1.0 / 16)])
+G4_12B_GLOBAL = Workload("gemma4-12b global layer, B16 16q/1kv K=V hd512 linear C32768"
+                         " ctx U[4096,32768]", 4, 16, 4096, 32768, [global_geom(16, 32768)])
+HYBRID_48 = Workload("48-layer hybrid decode step, B32 ctx U[1,16384]: 40 sliding (16q/8kv hd256"
+                     " ring w1024) + 8 global (16q/1kv K=V hd512 linear C16384)", 5, 32, 1, 16384,
+                     hybrid_layers(48, sliding_geom(16, 8, 1024), global_geom(16, 16384)))
+
+ALL = [TINY, G3_1B_SLIDING, G4_12B_SLIDING, G4_12B_GLOBAL, HYBRID_48]
+
+
+def layer_seed(workload: Workload, layer: int) -> int:
+    """Per-layer seed of a multi-layer workload (single-layer workloads use the seed)."""
+    return workload.seed if workload.num_layers == 1 else workload.seed * 1000 + layer
+
+
+def with_batch(w: Workload, batch: int) -> Workload:
+    return replace(w, batch=batch)

@@ -1,0 +1,308 @@
+/*
+ * oracle.c -- fp64 reference for single-token decode attention over bf16 KV caches.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this file's library.  The GPU library never includes, links
+ * or calls anything here, and nothing here includes or links the GPU library.
+ *
+ * What it computes is the plain, unsplit definition of masked softmax attention for
+ * one query token per sequence, with no blocking, splitting or reordering:
+ *
+ *   for every batch row b and query head h (KV head g = h / G, G = Hq / Hkv):
+ *     P  = positions p with 0 <= p <= q_pos, p < ctx, inside the window
+ *          (window w > 0: p > q_pos - w) and still present in the cache
+ *          (ring of W slots: p >= ctx - W; linear of C slots: p < C)
+ *     s_p = scale * <q[b,h,:], K[b,g,slot(p),:]>, then s_p <- c*tanh(s_p/c) when the
+ *           soft-cap c is on
+ *     out = sum_p softmax(s)_p * V[b,g,slot(p),:],  V = K when no V cache is given
+ *     slot(p) = p mod W (ring) or p (linear)
+ *
+ * Sources (titles and sections of the pages this follows):
+ *  - "Gemma support" pull request, Summary: attention logit soft-capping,
+ *    sliding-window layers, mixed 256/512 head sizes, K = V global attention.
+ *  - "Gemma 4 12B (unified multimodal)" record, KV geometry and "required kernel
+ *    class" passages: a local layer reads exactly w KV entries; attention_k_eq_v;
+ *    the rotating (ring) cache of sliding layers, in the "(6) On Apple Silicon" item.
+ *  - "Gemma4-26B-A4B on Apple Silicon" analysis, Results (Break 4): per-layer-type
+ *    head dims and KV-head counts, no separate value projection on full layers;
+ *    Threats to validity: the query scale defaults to 1/sqrt(head_dim).
+ *  - "Gemma support", Performance: split decode attention (the merge algebra in
+ *    oracle_split_merge_f64 is the textbook log-sum-exp identity it rests on).
+ * Readings where the pages are silent: the soft-cap is c*tanh(s/c) and is off for
+ * c <= 0 or non-finite c; the scale multiplies the raw dot product before the cap;
+ * the window is inclusive of the current token and holds exactly w positions; query
+ * head h reads KV head h / G; an empty valid set gives out = 0 and lse = -inf.
+ *
+ * Arithmetic: every bf16 input is widened exactly (bits << 16 -> float -> double);
+ * scale and softcap are widened from their float32 values; libm exp, tanh, log in
+ * double.  Results are double; callers round to float32 where they need to.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ENOMEM (-2)
+
+/* Precondition flags reported per batch row. */
+#define OR_FLAG_QPOS_GE_CTX 1   /* q_pos >= ctx: positions above ctx-1 do not exist   */
+#define OR_FLAG_EVICTED 2       /* ring: window or full attention needs evicted slots */
+#define OR_FLAG_LINEAR_OVER 4   /* linear: ctx > C, positions >= C do not exist       */
+#define OR_FLAG_NEGATIVE 8      /* ctx < 0 or q_pos < 0                               */
+
+enum { OR_LINEAR = 0, OR_RING = 1 };
+
+double oracle_bf16_to_f64(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Membership of position p in the valid set P of one batch row (plain predicate). */
+static int in_valid_set(long p, long ctx, long q_pos, long window, int kind, long cap) {
+  if (p < 0) return 0;
+  if (p > q_pos) return 0;                        /* causal: nothing after the query  */
+  if (p > ctx - 1) return 0;                      /* only positions already written   */
+  if (window > 0 && p < q_pos - window + 1) return 0; /* exactly w positions up to q */
+  if (kind == OR_RING && p < ctx - cap) return 0; /* overwritten in a ring of W slots */
+  if (kind == OR_LINEAR && p >= cap) return 0;    /* never stored in a linear cache   */
+  return 1;
+}
+
+static long slot_of(long p, int kind, long cap) { return kind == OR_RING ? p % cap : p; }
+
+/* Flags for one batch row; 0 when every precondition holds. */
+int32_t oracle_row_flags(int32_t ctx, int32_t q_pos, int32_t window, int32_t kind, int32_t cap) {
+  int32_t f = 0;
+  if (ctx < 0 || q_pos < 0) f |= OR_FLAG_NEGATIVE;
+  if (q_pos >= ctx) f |= OR_FLAG_QPOS_GE_CTX;
+  if (kind == OR_LINEAR && ctx > cap) f |= OR_FLAG_LINEAR_OVER;
+  if (kind == OR_RING) {
+    /* oldest position the query wants: q_pos - w + 1 with a window, else 0 */
+    long want_lo = window > 0 ? (long)q_pos - window + 1 : 0;
+    if (want_lo < 0) want_lo = 0;
+    long present_lo = (long)ctx - cap;
+    if (want_lo < present_lo && want_lo <= q_pos) f |= OR_FLAG_EVICTED;
+  }
+  return f;
+}
+
+/* Valid set of one batch row: writes the ascending positions and their slots; returns
+ * how many there are.  positions/slots may be NULL to only count. */
+int64_t oracle_valid_positions(int32_t ctx, int32_t q_pos, int32_t window, int32_t kind,
+                               int32_t cap, int64_t* positions, int64_t* slots) {
+  int64_t n = 0;
+  for (long p = 0; p < (long)ctx; ++p) {
+    if (!in_valid_set(p, ctx, q_pos, window, kind, cap)) continue;
+    if (positions) positions[n] = p;
+    if (slots) slots[n] = slot_of(p, kind, cap);
+    ++n;
+  }
+  return n;
+}
+
+typedef struct {
+  int B, Hq, Hkv, D, cap, kind;
+  const uint16_t *q, *k, *v;
+  const int32_t *ctx, *qpos;
+  int window;
+  double softcap; /* <= 0: off */
+  double scale;
+  double *out, *lse, *probs;
+  long probs_len;
+  long next_unit;
+  pthread_mutex_t mu;
+} decode_job;
+
+static void decode_unit(decode_job* J, long unit, double* s_buf, long* p_buf) {
+  const int b = (int)(unit / J->Hq), h = (int)(unit % J->Hq);
+  const int G = J->Hq / J->Hkv, g = h / G, D = J->D;
+  const long ctx = J->ctx[b], qp = J->qpos[b];
+  const uint16_t* qrow = J->q + ((long)b * J->Hq + h) * D;
+  const uint16_t* kbase = J->k + ((long)b * J->Hkv + g) * (long)J->cap * D;
+  const uint16_t* vbase = (J->v ? J->v : J->k) + ((long)b * J->Hkv + g) * (long)J->cap * D;
+  double* orow = J->out + ((long)b * J->Hq + h) * D;
+
+  long n = 0;
+  for (long p = 0; p < ctx; ++p)
+    if (in_valid_set(p, ctx, qp, J->window, J->kind, J->cap)) p_buf[n++] = p;
+
+  if (J->probs)
+    for (long i = 0; i < J->probs_len; ++i) J->probs[unit * J->probs_len + i] = 0.0;
+  if (n == 0) {
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    if (J->lse) J->lse[unit] = -INFINITY;
+    return;
+  }
+  /* logits, in ascending position order */
+  for (long i = 0; i < n; ++i) {
+    const uint16_t* krow = kbase + slot_of(p_buf[i], J->kind, J->cap) * D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += oracle_bf16_to_f64(qrow[d]) * oracle_bf16_to_f64(krow[d]);
+    double s = J->scale * dot;
+    if (J->softcap > 0.0) s = J->softcap * tanh(s / J->softcap);
+    s_buf[i] = s;
+  }
+  double m = s_buf[0];
+  for (long i = 1; i < n; ++i)
+    if (s_buf[i] > m) m = s_buf[i];
+  double l = 0.0;
+  for (long i = 0; i < n; ++i) {
+    s_buf[i] = exp(s_buf[i] - m);
+    l += s_buf[i];
+  }
+  for (int d = 0; d < D; ++d) orow[d] = 0.0;
+  for (long i = 0; i < n; ++i) {
+    const uint16_t* vrow = vbase + slot_of(p_buf[i], J->kind, J->cap) * D;
+    const double w = s_buf[i] / l;
+    for (int d = 0; d < D; ++d) orow[d] += w * oracle_bf16_to_f64(vrow[d]);
+    if (J->probs && p_buf[i] < J->probs_len) J->probs[unit * J->probs_len + p_buf[i]] = w;
+  }
+  if (J->lse) J->lse[unit] = m + log(l);
+}
+
+static void* decode_worker(void* arg) {
+  decode_job* J = (decode_job*)arg;
+  long maxctx = 1;
+  for (int b = 0; b < J->B; ++b)
+    if (J->ctx[b] > maxctx) maxctx = J->ctx[b];
+  double* s_buf = (double*)malloc(sizeof(double) * maxctx);
+  long* p_buf = (long*)malloc(sizeof(long) * maxctx);
+  if (!s_buf || !p_buf) {
+    free(s_buf);
+    free(p_buf);
+    return (void*)1;
+  }
+  const long units = (long)J->B * J->Hq;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    long u = J->next_unit++;
+    pthread_mutex_unlock(&J->mu);
+    if (u >= units) break;
+    decode_unit(J, u, s_buf, p_buf);
+  }
+  free(s_buf);
+  free(p_buf);
+  return NULL;
+}
+
+int oracle_num_threads_default(void) {
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+/*
+ * Decode attention for every (b, h).  q [B,Hq,D]; k_cache and v_cache [B,Hkv,cap,D]
+ * (bf16 bits, contiguous); v_cache NULL means V = K.  out [B,Hq,D] double; lse [B*Hq]
+ * (may be NULL); probs [B*Hq, probs_len] indexed by absolute position (may be NULL);
+ * flags [B] receives the precondition flags (may be NULL).  nthreads <= 0: all cores.
+ * Returns 0, or OR_EINVAL / OR_ENOMEM.
+ */
+int oracle_decode_f64(int B, int Hq, int Hkv, int D, int cap, int kind, const uint16_t* q,
+                      const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* ctx_lens,
+                      const int32_t* q_pos, int window, float softcap, float scale, double* out,
+                      double* lse, double* probs, long probs_len, int32_t* flags, int nthreads) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || cap <= 0 || Hq % Hkv != 0) return OR_EINVAL;
+  if (kind != OR_LINEAR && kind != OR_RING) return OR_EINVAL;
+  if (!q || !k_cache || !ctx_lens || !q_pos || !out) return OR_EINVAL;
+  if (!isfinite(scale)) return OR_EINVAL;
+  if (flags)
+    for (int b = 0; b < B; ++b) flags[b] = oracle_row_flags(ctx_lens[b], q_pos[b], window, kind, cap);
+  decode_job J;
+  J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.cap = cap; J.kind = kind;
+  J.q = q; J.k = k_cache; J.v = v_cache; J.ctx = ctx_lens; J.qpos = q_pos;
+  J.window = window;
+  J.softcap = (isfinite(softcap) && softcap > 0.0f) ? (double)softcap : 0.0;
+  J.scale = (double)scale;
+  J.out = out; J.lse = lse; J.probs = probs; J.probs_len = probs ? probs_len : 0;
+  J.next_unit = 0;
+  pthread_mutex_init(&J.mu, NULL);
+  if (nthreads <= 0) nthreads = oracle_num_threads_default();
+  long units = (long)B * Hq;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  if (!th) return OR_ENOMEM;
+  int rc = OR_OK;
+  for (int t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, decode_worker, &J);
+  for (int t = 0; t < nthreads; ++t) {
+    void* r = NULL;
+    pthread_join(th[t], &r);
+    if (r) rc = OR_ENOMEM;
+  }
+  free(th);
+  pthread_mutex_destroy(&J.mu);
+  return rc;
+}
+
+/*
+ * Cache append: cache[b, g, slot(pos_b), :] <- new[b, g, :] for every (b, g), with
+ * slot(p) = p mod W (ring) or p (linear).  new [B,Hkv,D]; cache [B,Hkv,cap,D].
+ * Returns OR_EINVAL for a negative position or a linear position >= C.
+ */
+int oracle_append(int B, int Hkv, int D, int cap, int kind, uint16_t* cache, const uint16_t* new_rows,
+                  const int32_t* pos) {
+  if (B < 0 || Hkv <= 0 || D <= 0 || cap <= 0 || !cache || !new_rows || !pos) return OR_EINVAL;
+  for (int b = 0; b < B; ++b) {
+    if (pos[b] < 0 || (kind == OR_LINEAR && pos[b] >= cap)) return OR_EINVAL;
+  }
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      long s = slot_of(pos[b], kind, cap);
+      uint16_t* dst = cache + (((long)b * Hkv + g) * cap + s) * D;
+      const uint16_t* src = new_rows + ((long)b * Hkv + g) * D;
+      for (int d = 0; d < D; ++d) dst[d] = src[d];
+    }
+  return OR_OK;
+}
+
+/*
+ * Split-and-merge in fp64 for ONE query row, used only to pin the merge algebra.
+ * logits [n] (already scaled and capped), values [n, D] (double), a partition of
+ * 0..n-1 into nparts consecutive pieces given by cut points starts[0..nparts]
+ * (starts[0] = 0, starts[nparts] = n; an empty piece is allowed).  Each piece yields
+ * (m_s, l_s, acc_s) with m_s = max, l_s = sum exp(s - m_s), acc_s = sum exp(s - m_s) v;
+ * the merge is M = max m_s, L = sum l_s e^{m_s - M}, out = sum e^{m_s - M} acc_s / L.
+ * An empty piece has m = -inf, l = 0, acc = 0 and contributes nothing.  out [D];
+ * returns lse = M + log L (-inf when n = 0, and then out = 0).
+ */
+double oracle_split_merge_f64(long n, int D, const double* logits, const double* values, int nparts,
+                              const long* starts, double* out) {
+  double M = -INFINITY;
+  double* ms = (double*)malloc(sizeof(double) * (nparts > 0 ? nparts : 1));
+  double* ls = (double*)malloc(sizeof(double) * (nparts > 0 ? nparts : 1));
+  double* accs = (double*)calloc((size_t)(nparts > 0 ? nparts : 1) * D, sizeof(double));
+  for (int s = 0; s < nparts; ++s) {
+    double m = -INFINITY, l = 0.0;
+    for (long i = starts[s]; i < starts[s + 1]; ++i)
+      if (logits[i] > m) m = logits[i];
+    for (long i = starts[s]; i < starts[s + 1]; ++i) {
+      double e = exp(logits[i] - m);
+      l += e;
+      for (int d = 0; d < D; ++d) accs[(long)s * D + d] += e * values[i * D + d];
+    }
+    ms[s] = m;
+    ls[s] = l;
+    if (m > M) M = m;
+  }
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  double L = 0.0;
+  if (M == -INFINITY) {
+    free(ms); free(ls); free(accs);
+    return -INFINITY;
+  }
+  for (int s = 0; s < nparts; ++s) {
+    if (ls[s] == 0.0) continue;
+    double f = exp(ms[s] - M);
+    L += ls[s] * f;
+    for (int d = 0; d < D; ++d) out[d] += f * accs[(long)s * D + d];
+  }
+  for (int d = 0; d < D; ++d) out[d] /= L;
+  free(ms); free(ls); free(accs);
+  (void)n;
+  return M + log(L);
+}
