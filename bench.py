@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark: one 48-layer hybrid decode step (append + split-KV decode per layer).
+
+Workload (synthetic, seeded): batch 32, per-sequence context uniform on [1, 16384];
+layers at 0-based index l with l % 6 == 5 are global (16 query heads on 1 KV head,
+K = V, head_dim 512, linear cache of 16384 positions, full causal), every other layer
+is sliding (16 query heads on 8 KV heads, head_dim 256, bf16 ring of W = w = 1024),
+no soft-cap, query scale 1/sqrt(head_dim).  Each step appends the current token
+(position ctx - 1) to every layer's cache and then attends with q_pos = ctx - 1.
+
+Prints ONE JSON line.  `value` is effective KV GB/s of the whole step: algorithmic
+bytes (valid K rows, plus V rows unless K = V, plus q, out, the int inputs, and the
+append's reads and writes) divided by the step time, with every input resident in
+HBM.  `roofline` is for the dominant kernel (the sliding-layer split-decode kernel),
+timed with HIP events around each of its launches on the stream it runs on.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode attention effective KV GB/s and % of HBM peak; layer-tokens/sec"
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def valid_keys(g, ctx):
+    """Keys a row attends to at q_pos = ctx - 1: the newest min(ctx, w) positions for a
+    sliding layer (ring of W >= w slots), all ctx positions for a full-causal layer."""
+    import numpy as np
+    return np.minimum(ctx, g.window) if g.window > 0 else ctx.copy()
+
+
+def layer_bytes(g, B, ctx):
+    """Algorithmic bytes of one layer: decode reads + writes, append reads + writes."""
+    n = valid_keys(g, ctx).astype("int64")
+    tensors = 1 if g.k_eq_v else 2
+    kv = int(n.sum()) * g.num_kv_heads * g.head_dim * 2 * tensors
+    q = B * g.num_q_heads * g.head_dim * 2
+    out = B * g.num_q_heads * g.head_dim * 4
+    ints = 2 * B * 4
+    append = 2 * B * g.num_kv_heads * g.head_dim * 2 * tensors + B * 4
+    return {"kv": kv, "decode": kv + q + out + ints, "append": append}
+
+
+def read_traffic(kernel_tag):
+    """Counter-measured HBM bytes per launch from profiles/, or None when absent or when
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(PROFILES, f"hbm_traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for rel in kv.get("sources", "").split():
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    if kv.get("sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the per-GPU workload is the whole step at its real shape)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from decode_attention_split_amd import api, synth
+    from decode_attention_split_amd import workloads as wl
+    from decode_attention_split_amd.hybrid import HybridKVCache
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.HYBRID_48
+    B, L = w.batch, w.num_layers
+
+    # ---- inputs, resident in HBM before timing
+    gen_cpu = synth.generator(w.seed)
+    ctx = synth.uniform_int(gen_cpu, B, w.ctx_lo, w.ctx_hi).numpy().astype(np.int32)
+    gdev = synth.generator(w.seed, device=dev)
+
+    def fill(li, name, shape):
+        return synth.normal_bf16(gdev, shape, device=dev)
+
+    t0 = time.time()
+    cache = HybridKVCache(w.layers, B, w.ctx_hi, device=dev, fill=fill)
+    qs = [synth.normal_bf16(gdev, (B, g.num_q_heads, g.head_dim), device=dev) for g in w.layers]
+    k_new = [synth.normal_bf16(gdev, (B, g.num_kv_heads, g.head_dim), device=dev)
+             for g in w.layers]
+    v_new = [None if g.k_eq_v else synth.normal_bf16(gdev, (B, g.num_kv_heads, g.head_dim),
+                                                     device=dev) for g in w.layers]
+    outs = [torch.empty((B, g.num_q_heads, g.head_dim), dtype=torch.float32, device=dev)
+            for g in w.layers]
+    ctx_t = torch.from_numpy(ctx).to(dev)
+    qpos_t = ctx_t - 1
+    pos_t = ctx_t - 1
+    torch.cuda.synchronize()
+    log(f"inputs ready: {cache.bytes() / 2**30:.2f} GiB of caches in {time.time() - t0:.1f}s")
+
+    per_layer = [layer_bytes(g, B, ctx) for g in w.layers]
+    step_bytes = sum(x["decode"] + x["append"] for x in per_layer)
+    sliding = [i for i, g in enumerate(w.layers) if not g.k_eq_v]
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for li in range(L):
+            cache.append(li, k_new[li], v_new[li], pos_t)
+            if ev is not None and li in ev:
+                ev[li][0].record(stream)
+            cache.decode(li, qs[li], ctx_t, qpos_t, out=outs[li])
+            if ev is not None and li in ev:
+                ev[li][1].record(stream)
+
+    graph = None
+    if args.graph:
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    def run_step(ev=None):
+        if graph is not None and ev is None:
+            graph.replay()
+        else:
+            step(ev)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"step: {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms)")
+
+    # ---- dominant kernel: each sliding-layer decode launch bracketed by events
+    kern_steps = max(1, min(args.steps, 10))
+    durs = []
+    for _ in range(kern_steps):
+        ev = {li: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for li in sliding}
+        step(ev)
+        torch.cuda.synchronize()
+        durs += [ev[li][0].elapsed_time(ev[li][1]) for li in sliding]
+    kern_ms = float(np.mean(durs))
+    kern_bytes = float(np.mean([per_layer[li]["decode"] for li in sliding]))
+    kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"sliding decode kernel: {kern_ms * 1e3:.2f} us avg over {len(durs)} launches, "
+        f"{kern_gbps:.1f} GB/s")
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "48-layer hybrid decode step (append + decode per layer): 40 sliding "
+                        "layers 16q/8kv hd256 ring w=W=1024 + 8 global layers 16q/1kv K=V "
+                        "hd512 linear C=16384 at l%6==5; batch 32; ctx U[1,16384] seed 5; "
+                        "no softcap; scale 1/sqrt(hd)",
+            "batch": B, "layers": L, "ctx_mean": float(ctx.mean()),
+            "accumulate": "fp32", "graph": bool(args.graph),
+            "algorithmic_bytes_per_step": int(step_bytes),
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "layer_tokens_per_s": round(B * L / (ms_step * 1e-3), 1),
+        "roofline": {
+            "kernel": "sliding-layer split decode (hd256, 16q/8kv, ring 1024), per launch",
+            "bound": "hbm",
+            "achieved": round(kern_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic("sliding_decode_hybrid48"),
+            "bytes_per_launch": int(kern_bytes),
+            "avg_launch_us": round(kern_ms * 1e3, 3),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cache, qs, ctx, w, per_layer, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cache, qs, ctx, w, per_layer, target_s):
+    """The fp64 oracle, as it stands, on whole layers of the same step (all 32 rows),
+    taken in schedule order until about target_s seconds of oracle time."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import oracle
+    from decode_attention_split_amd import synth
+
+    ctx = np.asarray(ctx, np.int32)
+    qpos = ctx - 1
+    done_bytes, spent, layers = 0, 0.0, []
+    threads = oracle.num_threads_default()
+    for li, g in enumerate(w.layers):
+        k = synth.bits(cache.k[li])
+        v = None if cache.v[li] is None else synth.bits(cache.v[li])
+        q = synth.bits(qs[li])
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, ctx, qpos, g.window, g.softcap, g.q_scale, g.kind, nthreads=threads)
+        spent += time.perf_counter() - t0
+        done_bytes += per_layer[li]["decode"]
+        layers.append(li)
+        del k, v
+        log(f"oracle layer {li}: {spent:.1f}s cumulative")
+        if spent >= target_s and li % 6 == 5:
+            break
+    units = max(g.num_q_heads for g in w.layers) * len(ctx)
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(min(threads, units)),
+        "kind": "oracle",
+        "sample": f"layers {layers[0]}-{layers[-1]} of the 48-layer step (whole layers, all "
+                  f"{len(ctx)} rows, decode only), {spent:.1f}s of oracle time",
+    }
+
+
+if __name__ == "__main__":
+    main()

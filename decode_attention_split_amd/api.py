@@ -1,0 +1,184 @@
+"""Python binding of libgemma_attn: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/gemma_attn.h).  torch provides device memory and the current stream; this
+module checks tensor dtypes, devices and contiguity, passes raw pointers, and raises
+GemmaAttnError when the library returns a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+LINEAR = 0
+RING = 1
+IMPL_AUTO, IMPL_VALU, IMPL_MFMA = 0, 1, 2
+
+GA_OK = 0
+ERRORS = {
+    -1: "GA_ERR_NULL", -2: "GA_ERR_DIMS", -3: "GA_ERR_HEAD_DIM", -4: "GA_ERR_GQA",
+    -5: "GA_ERR_KIND", -6: "GA_ERR_WINDOW", -7: "GA_ERR_WORKSPACE", -8: "GA_ERR_SCALE",
+    -9: "GA_ERR_V_MISMATCH", -10: "GA_ERR_ARCH", -11: "GA_ERR_LAUNCH", -12: "GA_ERR_OPTS",
+    -13: "GA_ERR_MAX_CTX", -14: "GA_ERR_TOO_LARGE",
+}
+FLAG_QPOS_GE_CTX, FLAG_EVICTED, FLAG_LINEAR_OVER, FLAG_NEGATIVE, FLAG_OVER_MAX_CTX = 1, 2, 4, 8, 16
+
+
+class GemmaAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        msg = _lib.load().gemma_attn_strerror(self.code).decode()
+        super().__init__(f"{where}: {ERRORS.get(self.code, self.code)} ({msg})")
+
+
+def _check(code: int, where: str):
+    if code != GA_OK:
+        raise GemmaAttnError(code, where)
+
+
+def make_shape(batch, num_q_heads, num_kv_heads, head_dim, capacity, kind, max_ctx=0):
+    return _lib.ga_shape(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                         int(capacity), int(kind), int(max_ctx))
+
+
+def make_opts(split_keys=0, impl=IMPL_AUTO):
+    o = _lib.ga_decode_opts()
+    o.split_keys = int(split_keys)
+    o.impl = int(impl)
+    return o
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def version() -> int:
+    return int(_lib.load().gemma_attn_version())
+
+
+def workspace_bytes(shape, window: int, split_keys: int = 0, impl: int = IMPL_AUTO) -> int:
+    lib = _lib.load()
+    opts = make_opts(split_keys, impl)
+    n = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window), ctypes.byref(opts))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid shape/window/options for gemma_attn_decode")
+    return int(n)
+
+
+def shape_of(q, k_cache, kind, max_ctx=0):
+    B, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k_cache {tuple(k_cache.shape)} disagree")
+    return make_shape(B, Hq, Hkv, D, cap, kind, max_ctx)
+
+
+def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
+           kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
+           impl: int = IMPL_AUTO, stream=None):
+    """Single-token decode attention; returns out [B, Hq, D] float32 (see gemma_attn.h).
+
+    v_cache None means K = V (k_cache serves as keys and values).  workspace, when
+    given, is a uint8 device tensor of at least workspace_bytes(...) bytes; otherwise
+    one is allocated here with torch (the library itself never allocates).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    if v_cache is not None:
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+        if v_cache.shape != k_cache.shape:
+            raise ValueError("v_cache must have the shape of k_cache")
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    shape = shape_of(q, k_cache, kind, max_ctx)
+    if ctx_lens.numel() != shape.batch or q_pos.numel() != shape.batch:
+        raise ValueError("ctx_lens and q_pos must have one entry per batch row")
+    if out is None:
+        out = torch.empty((shape.batch, shape.num_q_heads, shape.head_dim), dtype=torch.float32,
+                          device=q.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (shape.batch, shape.num_q_heads, shape.head_dim):
+            raise ValueError("out must be [B, Hq, D]")
+    opts = make_opts(split_keys, impl)
+    lib = _lib.load()
+    need = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window), ctypes.byref(opts))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # let the library report the precise error below
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib.gemma_attn_decode_ex(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(ctx_lens), _ptr(q_pos), int(window), float(softcap),
+                                  float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+                                  ctypes.byref(opts), _stream_handle(stream))
+    _check(rc, "gemma_attn_decode")
+    return out
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, pos, kind: int, stream=None):
+    """cache[b, g, slot(pos_b), :] <- new[b, g, :] for K (and V unless K = V)."""
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    if (v_cache is None) != (v_new is None):
+        _check(-9, "gemma_kv_append")
+    if v_cache is not None:
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+        _need(v_new, "v_new", torch.bfloat16, 3)
+        if v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
+            raise ValueError("V tensors must have the shapes of the K tensors")
+    _need(pos, "pos", torch.int32, 1)
+    B, Hkv, cap, D = k_cache.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or pos.numel() != B:
+        raise ValueError("k_new must be [B, Hkv, D] and pos [B]")
+    shape = make_shape(B, Hkv, Hkv, D, cap, kind)
+    rc = _lib.load().gemma_kv_append(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_new), _ptr(v_new), _ptr(pos), _stream_handle(stream))
+    _check(rc, "gemma_kv_append")
+
+
+def validate(shape, ctx_lens, q_pos, window: int, flags=None, stream=None):
+    """Per-row precondition flags (FLAG_*) as an int32 device tensor."""
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    if flags is None:
+        flags = torch.empty((shape.batch,), dtype=torch.int32, device=ctx_lens.device)
+    rc = _lib.load().gemma_attn_validate(ctypes.byref(shape), _ptr(ctx_lens), _ptr(q_pos),
+                                         int(window), _ptr(flags), _stream_handle(stream))
+    _check(rc, "gemma_attn_validate")
+    return flags
+
+
+def debug_ranges(shape, ctx_lens, q_pos, window: int, stream=None):
+    """(lo, hi, slot(lo), n) per row, as the decode kernels compute them: int32 [B, 4]."""
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    out = torch.empty((shape.batch, 4), dtype=torch.int32, device=ctx_lens.device)
+    rc = _lib.load().gemma_attn_debug_ranges(ctypes.byref(shape), _ptr(ctx_lens), _ptr(q_pos),
+                                             int(window), _ptr(out), _stream_handle(stream))
+    _check(rc, "gemma_attn_debug_ranges")
+    return out

@@ -1,0 +1,275 @@
+// api.hip -- the C ABI of libgemma_attn: argument checks, split planning and launches.
+// Every check that needs no device runs first, so a bad call is rejected before any
+// HIP call is made; nothing is launched on error.  The library never allocates, frees
+// or synchronises; all work is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "ga_internal.h"
+#include "gemma_attn.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+constexpr int kTargetBlocks = 2048;  // ~8 work-groups per CU on 256 CUs
+constexpr int kMaxSplitKeys = 65536;
+
+int32_t check_arch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return GA_ERR_ARCH;
+  }
+  if (dev >= kMaxDevices) return GA_ERR_ARCH;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return GA_ERR_ARCH;
+    }
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? GA_OK : GA_ERR_ARCH;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_shape(const ga_shape* s, int32_t window) {
+  if (!s) return GA_ERR_NULL;
+  if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->capacity <= 0)
+    return GA_ERR_DIMS;
+  if (s->head_dim != 256 && s->head_dim != 512) return GA_ERR_HEAD_DIM;
+  if (s->num_q_heads % s->num_kv_heads != 0) return GA_ERR_GQA;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (!ga::decode_valu_supported(s->head_dim, G)) return GA_ERR_GQA;
+  if (s->kind != GA_CACHE_LINEAR && s->kind != GA_CACHE_RING) return GA_ERR_KIND;
+  if (s->max_ctx < 0) return GA_ERR_MAX_CTX;
+  const long long max_ctx = s->max_ctx == 0 ? s->capacity : s->max_ctx;
+  if (s->kind == GA_CACHE_LINEAR && max_ctx > s->capacity) return GA_ERR_MAX_CTX;
+  if (s->kind == GA_CACHE_RING) {
+    if (window > s->capacity) return GA_ERR_WINDOW;
+    if (window <= 0 && max_ctx > s->capacity) return GA_ERR_WINDOW;
+  }
+  // 32-bit index and grid limits
+  const long long rows = (long long)s->batch * s->num_kv_heads * s->capacity;
+  if (rows * s->head_dim / 8 > (1LL << 40) || (long long)s->batch * s->num_q_heads > (1LL << 30))
+    return GA_ERR_TOO_LARGE;
+  return GA_OK;
+}
+
+struct Plan {
+  int impl;        // GA_IMPL_VALU / GA_IMPL_MFMA
+  int split_keys;  // Ts
+  int n_split;     // S
+  int max_keys;    // S * Ts
+  size_t ws_bytes;
+};
+
+// Upper bound on valid keys per row from host-known values only.
+long long max_keys_bound(const ga_shape* s, int32_t window) {
+  long long n = s->max_ctx == 0 ? s->capacity : s->max_ctx;
+  if (n > s->capacity) n = s->capacity;  // ring: at most W present; linear: at most C
+  if (window > 0 && n > window) n = window;
+  return n;
+}
+
+int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, Plan* p) {
+  const int D = s->head_dim, G = s->num_q_heads / s->num_kv_heads;
+  int impl = GA_IMPL_AUTO, ts = 0;
+  if (o) {
+    for (int i = 0; i < 6; ++i)
+      if (o->reserved[i] != 0) return GA_ERR_OPTS;
+    impl = o->impl;
+    ts = o->split_keys;
+    if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
+    if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
+  }
+  // The MFMA path exists for the K = V global geometry (head_dim 512, 16 query heads on
+  // one KV head); K = V is only known at decode time, so AUTO resolves there.
+  if (impl == GA_IMPL_MFMA && !ga::decode_mfma_supported(D, G, true)) return GA_ERR_OPTS;
+  const long long nmax = max_keys_bound(s, window);
+  const long long units = (long long)s->batch * s->num_kv_heads;
+  if (ts == 0) {
+    // Enough work-groups to fill the chip, but at least 128 keys each so the per-split
+    // partial (G * (D + 2) floats) stays small next to the split's KV bytes.
+    long long want_splits = units > 0 ? (kTargetBlocks + units - 1) / units : 1;
+    long long t = nmax > 0 ? (nmax + want_splits - 1) / want_splits : 64;
+    t = (t + 63) / 64 * 64;
+    if (t < 128) t = 128;
+    if (t > kMaxSplitKeys) t = kMaxSplitKeys;
+    ts = (int)t;
+  }
+  long long S = nmax > 0 ? (nmax + ts - 1) / ts : 1;
+  if (S < 1) S = 1;
+  if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
+  p->impl = impl;
+  p->split_keys = ts;
+  p->n_split = (int)S;
+  p->max_keys = (int)(S * ts);
+  p->ws_bytes = S > 1 ? (size_t)s->batch * s->num_q_heads * (size_t)S * (size_t)(D + 2) * 4u : 0;
+  return GA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gemma_attn_version(void) { return 100; }
+
+const char* gemma_attn_strerror(int32_t st) {
+  switch (st) {
+    case GA_OK: return "ok";
+    case GA_ERR_NULL: return "a required pointer is NULL or not 16-byte aligned";
+    case GA_ERR_DIMS: return "invalid dimensions (batch < 0, or a head count or capacity <= 0)";
+    case GA_ERR_HEAD_DIM: return "head_dim must be 256 or 512";
+    case GA_ERR_GQA: return "num_q_heads must be num_kv_heads times 1, 2, 4, 8 or 16";
+    case GA_ERR_KIND: return "cache kind must be GA_CACHE_LINEAR or GA_CACHE_RING";
+    case GA_ERR_WINDOW:
+      return "ring cache: window exceeds the ring capacity, or full attention while the "
+             "context can exceed it";
+    case GA_ERR_WORKSPACE: return "workspace missing or smaller than ga_decode_workspace_bytes";
+    case GA_ERR_SCALE: return "scale must be finite";
+    case GA_ERR_V_MISMATCH: return "v_cache and v_new must both be NULL (K = V) or both set";
+    case GA_ERR_ARCH: return "no HIP device, or the current device is not gfx950 (MI355X)";
+    case GA_ERR_LAUNCH: return "kernel launch failed";
+    case GA_ERR_OPTS: return "decode options invalid or unsupported for this shape";
+    case GA_ERR_MAX_CTX: return "max_ctx must be >= 0 and, for a linear cache, <= capacity";
+    case GA_ERR_TOO_LARGE: return "sizes overflow the kernels' index or grid range";
+    default: return "unknown status";
+  }
+}
+
+size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window,
+                                 const ga_decode_opts* opts) {
+  if (check_shape(shape, window) != GA_OK) return SIZE_MAX;
+  Plan p;
+  if (make_plan(shape, window, opts, &p) != GA_OK) return SIZE_MAX;
+  return p.ws_bytes;
+}
+
+int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
+                             const ga_bf16* v_cache, const int32_t* ctx_lens, const int32_t* q_pos,
+                             int32_t window, float softcap, float scale, float* out, void* workspace,
+                             size_t workspace_bytes, const ga_decode_opts* opts, void* stream) {
+  int32_t st = check_shape(shape, window);
+  if (st != GA_OK) return st;
+  if (!q || !k_cache || !ctx_lens || !q_pos || !out) return GA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || (v_cache && !aligned16(v_cache)) ||
+      !aligned16(out) || !aligned16(workspace))
+    return GA_ERR_NULL;
+  if (!std::isfinite(scale)) return GA_ERR_SCALE;
+  Plan p;
+  st = make_plan(shape, window, opts, &p);
+  if (st != GA_OK) return st;
+  const int D = shape->head_dim, G = shape->num_q_heads / shape->num_kv_heads;
+  const bool k_eq_v = v_cache == nullptr || v_cache == k_cache;
+  int impl = p.impl;
+  if (impl == GA_IMPL_MFMA && !k_eq_v) return GA_ERR_OPTS;
+  if (impl == GA_IMPL_AUTO)
+    impl = ga::decode_mfma_supported(D, G, k_eq_v) ? GA_IMPL_MFMA : GA_IMPL_VALU;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return GA_ERR_WORKSPACE;
+  st = check_arch();
+  if (st != GA_OK) return st;
+  if (shape->batch == 0) return GA_OK;
+
+  ga::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = k_eq_v ? k_cache : v_cache;
+  a.ctx = ctx_lens;
+  a.q_pos = q_pos;
+  a.out = out;
+  float* ws = static_cast<float*>(workspace);
+  const size_t n_acc = (size_t)shape->batch * shape->num_q_heads * (size_t)p.n_split * D;
+  a.part_acc = p.n_split > 1 ? ws : nullptr;
+  a.part_ml = p.n_split > 1 ? ws + n_acc : nullptr;
+  a.B = shape->batch;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.D = D;
+  a.cap = shape->capacity;
+  a.kind = shape->kind;
+  a.window = window;
+  a.scale = scale;
+  const bool cap_on = std::isfinite(softcap) && softcap > 0.0f;
+  a.softcap = cap_on ? softcap : 0.0f;
+  a.inv_softcap = cap_on ? 1.0f / softcap : 0.0f;
+  a.split_keys = p.split_keys;
+  a.n_split = p.n_split;
+  a.max_keys = p.max_keys;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = impl == GA_IMPL_MFMA ? ga::decode_mfma_launch(a, s)
+                                      : ga::decode_valu_launch(a, k_eq_v, s);
+  if (e == hipSuccess && p.n_split > 1) e = ga::merge_launch(a, s);
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_attn_decode(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
+                          const ga_bf16* v_cache, const int32_t* ctx_lens, const int32_t* q_pos,
+                          int32_t window, float softcap, float scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return gemma_attn_decode_ex(shape, q, k_cache, v_cache, ctx_lens, q_pos, window, softcap, scale,
+                              out, workspace, workspace_bytes, nullptr, stream);
+}
+
+int32_t gemma_kv_append(const ga_shape* shape, ga_bf16* k_cache, ga_bf16* v_cache,
+                        const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
+                        void* stream) {
+  if (!shape) return GA_ERR_NULL;
+  if (shape->batch < 0 || shape->num_kv_heads <= 0 || shape->num_q_heads <= 0 ||
+      shape->capacity <= 0)
+    return GA_ERR_DIMS;
+  if (shape->head_dim != 256 && shape->head_dim != 512) return GA_ERR_HEAD_DIM;
+  if (shape->kind != GA_CACHE_LINEAR && shape->kind != GA_CACHE_RING) return GA_ERR_KIND;
+  if (!k_cache || !k_new || !pos) return GA_ERR_NULL;
+  if ((v_cache == nullptr) != (v_new == nullptr)) return GA_ERR_V_MISMATCH;
+  if (!aligned16(k_cache) || !aligned16(k_new) || !aligned16(v_cache) || !aligned16(v_new))
+    return GA_ERR_NULL;
+  int32_t st = check_arch();
+  if (st != GA_OK) return st;
+  hipError_t e = ga::append_launch(shape->batch, shape->num_kv_heads, shape->head_dim,
+                                   shape->capacity, shape->kind, k_cache, v_cache, k_new, v_new,
+                                   pos, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_attn_validate(const ga_shape* shape, const int32_t* ctx_lens, const int32_t* q_pos,
+                            int32_t window, int32_t* dev_flags, void* stream) {
+  int32_t st = check_shape(shape, window);
+  if (st != GA_OK) return st;
+  if (!ctx_lens || !q_pos || !dev_flags) return GA_ERR_NULL;
+  st = check_arch();
+  if (st != GA_OK) return st;
+  const int max_ctx = shape->max_ctx == 0 ? shape->capacity : shape->max_ctx;
+  hipError_t e = ga::validate_launch(shape->batch, shape->capacity, shape->kind, window, max_ctx,
+                                     ctx_lens, q_pos, dev_flags, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_attn_debug_ranges(const ga_shape* shape, const int32_t* ctx_lens,
+                                const int32_t* q_pos, int32_t window, int32_t* dev_out,
+                                void* stream) {
+  int32_t st = check_shape(shape, window);
+  if (st != GA_OK) return st;
+  if (!ctx_lens || !q_pos || !dev_out) return GA_ERR_NULL;
+  Plan p;
+  st = make_plan(shape, window, nullptr, &p);
+  if (st != GA_OK) return st;
+  st = check_arch();
+  if (st != GA_OK) return st;
+  hipError_t e = ga::ranges_launch(shape->batch, shape->capacity, shape->kind, window, p.max_keys,
+                                   ctx_lens, q_pos, dev_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+}  // extern "C"

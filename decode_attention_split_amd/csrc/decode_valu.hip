@@ -1,0 +1,307 @@
+// decode_valu.hip -- split-KV flash-decode on the vector ALUs (gfx950, wave64).
+//
+// One work-group handles one split (a run of split_keys consecutive valid keys) of one
+// (batch row, KV head).  Inside a wave, aligned groups of L lanes each own one key per
+// step: lane j of a group holds the elements d = 8 * (c * L + j) + e (c < D / (8 L),
+// e < 8) of that key's row, loaded straight from HBM with 16-byte loads (a group reads
+// 16 L contiguous bytes per load, a full row over D / (8 L) loads).  The G query heads
+// that share the KV head stay in registers as packed bf16, so q . k is v_dot2 on the raw
+// bf16 data with fp32 accumulation, finished by a DPP butterfly over the group.  Every
+// group keeps its own online-softmax state (m, l, acc[G][D / L]) and the groups and
+// waves are merged once at the end, so the key loop has no barrier and no LDS traffic:
+// each lane consumes exactly the bytes it loaded, and staging through LDS would only add
+// a write and a read per byte.  With K = V the row loaded for the logits is the row
+// used for the values (read once, used twice).
+//
+// Softmax runs in log2 units: s2 = log2(e) * cap(scale * q.k).  The running max is only
+// raised when a logit exceeds it by more than kRescaleLog2 (2^8), so the accumulator
+// rescale (G * D / L multiplies) happens a handful of times per group rather than per
+// key; exp2(s2 - m) <= 2^8 keeps everything well inside fp32.  The result is unchanged:
+// (m, l, acc) stay mutually consistent whatever reference m is used.
+//
+// Definition followed: "Gemma support" pull request, Summary (soft-capping, sliding
+// window, head sizes 256/512, K = V) and Performance (split decode attention); the key
+// range is ga::row_range ("Gemma 4 12B (unified multimodal)" record: exactly w entries).
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+namespace {
+
+constexpr float kRescaleLog2 = 8.0f;
+
+constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+template <int D, int G>
+struct ValuCfg {
+  static constexpr int L = clampi(G * D / 64, 8, D / 8);  // lanes per key: acc <= 64..128 VGPRs
+  static constexpr int DPL = D / L;                        // elements per lane per key
+  static constexpr int NCH = DPL / 8;                      // 16-byte loads per lane per key
+  static constexpr int GPW = 64 / L;                       // keys per wave per step
+  static constexpr int NW = clampi(8192 / (G * D), 1, 4);  // waves per work-group
+  static constexpr int NG = GPW * NW;                      // keys per work-group per step
+  static_assert(NCH >= 1 && DPL % 8 == 0, "lane slice must be whole 16-byte chunks");
+};
+
+template <int D, int G, bool KV_SHARED>
+__global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
+    decode_valu_kernel(DecodeArgs a) {
+  using C = ValuCfg<D, G>;
+  constexpr int L = C::L, DPL = C::DPL, NCH = C::NCH, GPW = C::GPW, NW = C::NW, NG = C::NG;
+  constexpr int ROW16 = D / 8;  // 16-byte chunks per cache row
+
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane / L;
+  const int j = lane % L;
+
+  const int S = a.n_split;
+  int bid = blockIdx.x;
+  const int split = bid % S;
+  bid /= S;
+  const int g = bid % a.Hkv;
+  const int b = bid / a.Hkv;
+  const int h0 = g * G;
+
+  const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(r.n, k_begin + a.split_keys);
+  if (k_begin >= k_end) {
+    if (S == 1) {  // the only split of an empty row: the output is 0
+      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
+        a.out[((size_t)b * a.Hq + h0) * D + idx] = 0.0f;
+    }
+    return;  // with S > 1 the merge never reads splits past the row's end
+  }
+
+  // Query heads of this KV head, as packed bf16 pairs, in this lane's element order.
+  uint32_t qr[G][DPL / 2];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint4 v = qp[c * L + j];
+      qr[hh][4 * c + 0] = v.x;
+      qr[hh][4 * c + 1] = v.y;
+      qr[hh][4 * c + 2] = v.z;
+      qr[hh][4 * c + 3] = v.w;
+    }
+  }
+
+  const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
+  const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + row0 * ROW16;
+  const uint4* vbase = reinterpret_cast<const uint4*>(KV_SHARED ? a.k : a.v) + row0 * ROW16;
+
+  float acc[G][DPL];
+  float m[G], l[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
+  }
+
+  const int my_off = wave * GPW + grp;
+  const int n_steps = (k_end - k_begin + NG - 1) / NG;
+  const float scale = a.scale;
+  const float softcap = a.softcap, inv_softcap = a.inv_softcap;
+
+  auto load = [&](uint4(&kr)[NCH], uint4(&vr)[NCH], int step) {
+    const int i = k_begin + step * NG + my_off;
+    const int ic = i < k_end ? i : k_end - 1;  // past the end: re-read a valid row
+    const size_t slot = (size_t)key_slot(r, ic, a.cap);
+    const uint4* kp = kbase + slot * ROW16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kr[c] = kp[c * L + j];
+    if constexpr (!KV_SHARED) {
+      const uint4* vp = vbase + slot * ROW16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) vr[c] = vp[c * L + j];
+    }
+  };
+
+  auto compute = [&](const uint4(&kr)[NCH], const uint4(&vr)[NCH], int step) {
+    const int i = k_begin + step * NG + my_off;
+    const bool valid = i < k_end;
+    float s[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        d0 = dot2_bf16(qr[hh][4 * c + 0], kr[c].x, d0);
+        d1 = dot2_bf16(qr[hh][4 * c + 1], kr[c].y, d1);
+        d0 = dot2_bf16(qr[hh][4 * c + 2], kr[c].z, d0);
+        d1 = dot2_bf16(qr[hh][4 * c + 3], kr[c].w, d1);
+      }
+      s[hh] = group_sum<L>(d0 + d1);
+    }
+    float p[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float x = s[hh] * scale;
+      if (softcap > 0.0f) x = softcap_tanh(x, softcap, inv_softcap);
+      x = valid ? x * kLog2e : -INFINITY;
+      if (x > m[hh] + kRescaleLog2) {
+        const float f = exp2_fast(m[hh] - x);  // 0 on the first key (m = -inf)
+        l[hh] *= f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[hh][e] *= f;
+        m[hh] = x;
+      }
+      p[hh] = valid ? exp2_fast(x - m[hh]) : 0.0f;
+      l[hh] += p[hh];
+    }
+    const uint4(&vv)[NCH] = KV_SHARED ? kr : vr;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t w[4] = {vv[c].x, vv[c].y, vv[c].z, vv[c].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float lo = bf16_lo(w[t]), hi = bf16_hi(w[t]);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          acc[hh][8 * c + 2 * t] = fmaf(p[hh], lo, acc[hh][8 * c + 2 * t]);
+          acc[hh][8 * c + 2 * t + 1] = fmaf(p[hh], hi, acc[hh][8 * c + 2 * t + 1]);
+        }
+      }
+    }
+  };
+
+  // Two register buffers: the next step's rows are in flight while this step computes.
+  uint4 ka[NCH], va[NCH], kb[NCH], vb[NCH];
+  load(ka, va, 0);
+  for (int st = 0; st < n_steps; st += 2) {
+    if (st + 1 < n_steps) load(kb, vb, st + 1);
+    compute(ka, va, st);
+    if (st + 1 >= n_steps) break;
+    if (st + 2 < n_steps) load(ka, va, st + 2);
+    compute(kb, vb, st + 1);
+  }
+
+  // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements).
+#pragma unroll
+  for (int off = L; off < 64; off <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float mo = __shfl_xor(m[hh], off, 64);
+      const float lo = __shfl_xor(l[hh], off, 64);
+      const float mn = fmaxf(m[hh], mo);
+      const float fs = m[hh] == -INFINITY ? 0.0f : exp2_fast(m[hh] - mn);
+      const float fo = mo == -INFINITY ? 0.0f : exp2_fast(mo - mn);
+      l[hh] = l[hh] * fs + lo * fo;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float ao = __shfl_xor(acc[hh][e], off, 64);
+        acc[hh][e] = acc[hh][e] * fs + ao * fo;
+      }
+      m[hh] = mn;
+    }
+  }
+
+  // Merge the waves through LDS, then write the output or this split's partial.
+  if (lane < L) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float4* dst = reinterpret_cast<float4*>(&s_acc[wave][hh][8 * (c * L + j)]);
+        dst[0] = make_float4(acc[hh][8 * c + 0], acc[hh][8 * c + 1], acc[hh][8 * c + 2],
+                             acc[hh][8 * c + 3]);
+        dst[1] = make_float4(acc[hh][8 * c + 4], acc[hh][8 * c + 5], acc[hh][8 * c + 6],
+                             acc[hh][8 * c + 7]);
+      }
+      if (j == 0) {
+        s_m[wave][hh] = m[hh];
+        s_l[wave][hh] = l[hh];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hh]);
+    float Lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = s_m[w][hh] == -INFINITY ? 0.0f : exp2_fast(s_m[w][hh] - M);
+      Lsum += s_l[w][hh] * f;
+      o += s_acc[w][hh][d] * f;
+    }
+    const size_t bh = (size_t)b * a.Hq + h0 + hh;
+    if (S == 1) {
+      a.out[bh * D + d] = Lsum > 0.0f ? o / Lsum : 0.0f;
+    } else {
+      a.part_acc[(bh * S + split) * D + d] = o;
+      if (d == 0) {
+        a.part_ml[(bh * S + split) * 2 + 0] = M;
+        a.part_ml[(bh * S + split) * 2 + 1] = Lsum;
+      }
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  using C = ValuCfg<D, G>;
+  const long long blocks = (long long)a.B * a.Hkv * a.n_split;
+  if (blocks <= 0) return hipSuccess;
+  if (k_eq_v)
+    hipLaunchKernelGGL((decode_valu_kernel<D, G, true>), dim3((unsigned)blocks), dim3(C::NW * 64),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu_kernel<D, G, false>), dim3((unsigned)blocks),
+                       dim3(C::NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_dg<D, 1>(a, k_eq_v, stream);
+    case 2: return launch_dg<D, 2>(a, k_eq_v, stream);
+    case 4: return launch_dg<D, 4>(a, k_eq_v, stream);
+    case 8: return launch_dg<D, 8>(a, k_eq_v, stream);
+    case 16: return launch_dg<D, 16>(a, k_eq_v, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+int keys_per_iter_d(int G) {
+  switch (G) {
+    case 1: return ValuCfg<D, 1>::NG;
+    case 2: return ValuCfg<D, 2>::NG;
+    case 4: return ValuCfg<D, 4>::NG;
+    case 8: return ValuCfg<D, 8>::NG;
+    case 16: return ValuCfg<D, 16>::NG;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+bool decode_valu_supported(int D, int G) {
+  return (D == 256 || D == 512) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+int decode_valu_keys_per_iter(int D, int G) {
+  return D == 256 ? keys_per_iter_d<256>(G) : D == 512 ? keys_per_iter_d<512>(G) : 0;
+}
+
+hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  if (a.D == 256) return launch_d<256>(a, k_eq_v, stream);
+  if (a.D == 512) return launch_d<512>(a, k_eq_v, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ga

@@ -1,0 +1,146 @@
+// merge_append.hip -- log-sum-exp merge of split partials, cache append, and the two
+// debug kernels (precondition flags, key-range dump).  gfx950.
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+namespace {
+
+// LSE merge ("Gemma support" pull request, Performance: split decode attention).
+// Split s of row (b, h) left m_s (log2 units), l_s = sum 2^(s2 - m_s) and
+// acc_s = sum 2^(s2 - m_s) v.  With M = max m_s:
+//   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   out = 0 for an empty row.
+// One work-group per (b, h); the row's split count comes from the same row_range the
+// split kernel used, so exactly the splits that were written are read.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxSplitsLds = 1024;
+
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
+  __shared__ float s_w[kMergeMaxSplitsLds];
+  __shared__ float s_red[kMergeThreads / 64];
+  const size_t bh = blockIdx.x;
+  const int b = (int)(bh / a.Hq);
+  const int S = a.n_split, D = a.D;
+  const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S
+  float* out = a.out + bh * D;
+  if (ns == 0) {
+    for (int d = threadIdx.x; d < D; d += kMergeThreads) out[d] = 0.0f;
+    return;
+  }
+  const float* ml = a.part_ml + bh * S * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  // split weights 2^(m_s - M) into LDS, and L = sum_s l_s 2^(m_s - M)
+  float lsum = 0.0f;
+  for (int s = threadIdx.x; s < ns; s += kMergeThreads) {
+    const float w = exp2_fast(ml[2 * s] - M);
+    if (s < kMergeMaxSplitsLds) s_w[s] = w;
+    lsum += ml[2 * s + 1] * w;
+  }
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = lsum;
+  __syncthreads();
+  float Lsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) Lsum += s_red[w];
+  const float inv = 1.0f / Lsum;
+  const float* acc = a.part_acc + bh * S * D;
+  for (int d = threadIdx.x; d < D; d += kMergeThreads) {
+    float o = 0.0f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = s < kMergeMaxSplitsLds ? s_w[s] : exp2_fast(ml[2 * s] - M);
+      o = fmaf(w, acc[(size_t)s * D + d], o);
+    }
+    out[d] = o * inv;
+  }
+}
+
+// Cache append: one lane per 16-byte chunk of a new row; bit-exact copies.
+__global__ void append_kernel(int B, int Hkv, int D, int cap, int kind, uint4* k_cache,
+                              uint4* v_cache, const uint4* k_new, const uint4* v_new,
+                              const int32_t* pos) {
+  const int chunks = D / 8;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (long long)B * Hkv * chunks) return;
+  const int c = (int)(t % chunks);
+  const long long bg = t / chunks;
+  const int b = (int)(bg / Hkv);
+  const int p = pos[b];
+  if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) return;  // out of range: skipped
+  const int slot = kind == GA_CACHE_RING ? p % cap : p;
+  const size_t dst = ((size_t)bg * cap + slot) * chunks + c;
+  const size_t src = (size_t)bg * chunks + c;
+  k_cache[dst] = k_new[src];
+  if (v_cache) v_cache[dst] = v_new[src];
+}
+
+__global__ void validate_kernel(int B, int cap, int kind, int window, int max_ctx,
+                                const int32_t* ctx_lens, const int32_t* q_pos, int32_t* flags) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const long long ctx = ctx_lens[b], qp = q_pos[b];
+  int f = 0;
+  if (ctx < 0 || qp < 0) f |= GA_FLAG_NEGATIVE;
+  if (qp >= ctx) f |= GA_FLAG_QPOS_GE_CTX;
+  if (kind == GA_CACHE_LINEAR && ctx > cap) f |= GA_FLAG_LINEAR_OVER;
+  if (kind == GA_CACHE_RING) {
+    long long want_lo = window > 0 ? qp - window + 1 : 0;
+    if (want_lo < 0) want_lo = 0;
+    if (want_lo < ctx - cap && want_lo <= qp) f |= GA_FLAG_EVICTED;
+  }
+  if (ctx > max_ctx) f |= GA_FLAG_OVER_MAX_CTX;
+  flags[b] = f;
+}
+
+__global__ void ranges_kernel(int B, int cap, int kind, int window, int max_keys,
+                              const int32_t* ctx_lens, const int32_t* q_pos, int32_t* out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const RowRange r = row_range(ctx_lens[b], q_pos[b], window, kind, cap, max_keys);
+  out[4 * b + 0] = r.lo;
+  out[4 * b + 1] = r.hi;
+  out[4 * b + 2] = r.slot_lo;
+  out[4 * b + 3] = r.n;
+}
+
+}  // namespace
+
+hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream) {
+  const long long blocks = (long long)a.B * a.Hq;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t append_launch(int B, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
+                         uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* pos, hipStream_t stream) {
+  const long long n = (long long)B * Hkv * (D / 8);
+  if (n <= 0) return hipSuccess;
+  const int threads = 256;
+  const long long blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, B, Hkv, D,
+                     cap, kind, reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache),
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                     pos);
+  return hipGetLastError();
+}
+
+hipError_t validate_launch(int B, int cap, int kind, int window, int max_ctx, const int32_t* ctx,
+                           const int32_t* q_pos, int32_t* flags, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(validate_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, cap, kind,
+                     window, max_ctx, ctx, q_pos, flags);
+  return hipGetLastError();
+}
+
+hipError_t ranges_launch(int B, int cap, int kind, int window, int max_keys, const int32_t* ctx,
+                         const int32_t* q_pos, int32_t* out, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ranges_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, cap, kind,
+                     window, max_keys, ctx, q_pos, out);
+  return hipGetLastError();
+}
+
+}  // namespace ga

@@ -1,0 +1,192 @@
+/*
+ * gemma_attn.h -- single-token decode attention for hybrid sliding/global stacks on
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers, sizes and status codes.
+ *
+ * What is computed (one query token per sequence, per layer):
+ *   for batch row b, query head h, KV head g = h / G with G = Hq / Hkv:
+ *     valid positions P_b = { p : max(lo_w, lo_ring, 0) <= p <= min(q_pos_b, ctx_b - 1) }
+ *       lo_w    = q_pos_b - window + 1 when window > 0 (exactly `window` positions,
+ *                 the current one included), else 0 (full causal);
+ *       lo_ring = ctx_b - W for a ring cache of W slots (older entries are overwritten)
+ *     s_p  = scale * dot(q[b,h,:], K[b,g,slot(p),:])        (fp32 accumulation)
+ *     s_p <- softcap * tanh(s_p / softcap)   when 0 < softcap < inf
+ *     out[b,h,:] = sum_p softmax(s)_p * V[b,g,slot(p),:]    (V = K when K = V)
+ *     slot(p) = p mod W (ring) or p (linear); an empty P_b gives out = 0.
+ *   Passages defining the operation (page titles and sections):
+ *     - "Gemma support" pull request, Summary: attention logit soft-capping,
+ *       sliding-window layers, mixed 256/512 head sizes, K = V global attention;
+ *       Performance: split decode attention for head sizes 256/512.
+ *     - "Gemma 4 12B (unified multimodal)" record: a local layer reads exactly w KV
+ *       entries ("required kernel class"); per-layer-type cache management; the
+ *       rotating (ring) KV cache of sliding layers ("(6) On Apple Silicon");
+ *       attention_k_eq_v; head_dim 256 / 8 KV heads sliding, 512 / 1 KV head global.
+ *     - "Gemma4-26B-A4B on Apple Silicon", Results (Break 4): K/V sharing on full
+ *       layers, no separate value projection; Threats to validity: query scale
+ *       defaults to 1/sqrt(head_dim).
+ *     - same record, "(4) On Hopper": one KV head and batch 1 cannot fill a GPU
+ *       without splitting the keys, which is why the keys are split across CUs and
+ *       merged by log-sum-exp.
+ *
+ * Layout (all contiguous, row-major, bf16 as raw uint16 bits):
+ *   q        [B, Hq, D]          out [B, Hq, D] float32
+ *   caches   [B, Hkv, capacity, D]   (head-major: each (b, g) is one run of rows)
+ *   ctx_lens, q_pos, pos: int32 [B] in DEVICE memory
+ * Every pointer except the shape/opts structs is a device pointer.
+ *
+ * Ownership and execution: the caller owns every buffer.  The library keeps no
+ * pointer after a call returns, never allocates, frees or synchronises device memory,
+ * and enqueues all work on `stream` (a hipStream_t; NULL = the default stream).  Calls
+ * return as soon as the work is enqueued.  The only state kept is a per-device cache
+ * of the architecture check.
+ *
+ * Errors: every entry point returns int32_t, GA_OK (0) or a negative GA_ERR_* code
+ * (gemma_attn_strerror names it).  Arguments are checked on the host before anything
+ * is launched; on error nothing is launched.  Nothing throws across the ABI.
+ * Preconditions on device data (0 <= q_pos < ctx; linear: ctx <= C; ring: the window's
+ * positions are still present, q_pos - window + 1 >= ctx - W) belong to the caller:
+ * the kernels clamp every index so a violation never reads or writes out of bounds,
+ * and gemma_attn_validate reports it.
+ */
+#ifndef GEMMA_ATTN_H
+#define GEMMA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t ga_bf16; /* raw bf16 bits */
+
+enum { GA_CACHE_LINEAR = 0, GA_CACHE_RING = 1 };
+
+/* Status codes. */
+enum {
+  GA_OK = 0,
+  GA_ERR_NULL = -1,          /* a required pointer is NULL                                */
+  GA_ERR_DIMS = -2,          /* batch < 0, a head count or capacity <= 0                  */
+  GA_ERR_HEAD_DIM = -3,      /* head_dim is not 256 or 512                                */
+  GA_ERR_GQA = -4,           /* num_q_heads is not a multiple of num_kv_heads, or G > 16  */
+  GA_ERR_KIND = -5,          /* kind is neither GA_CACHE_LINEAR nor GA_CACHE_RING         */
+  GA_ERR_WINDOW = -6,        /* ring: window > W, or window <= 0 while max_ctx may exceed W */
+  GA_ERR_WORKSPACE = -7,     /* workspace NULL or smaller than ga_decode_workspace_bytes  */
+  GA_ERR_SCALE = -8,         /* scale is not finite                                       */
+  GA_ERR_V_MISMATCH = -9,    /* exactly one of v_cache / v_new is NULL                    */
+  GA_ERR_ARCH = -10,         /* no device, or the current device is not gfx950            */
+  GA_ERR_LAUNCH = -11,       /* a kernel launch failed (hipGetLastError)                  */
+  GA_ERR_OPTS = -12,         /* decode options out of range or not valid for this shape   */
+  GA_ERR_MAX_CTX = -13,      /* max_ctx < 0, or linear max_ctx > capacity                 */
+  GA_ERR_TOO_LARGE = -14     /* a size overflows the 32-bit grid or index arithmetic      */
+};
+
+/* Shape of one layer's decode call. */
+typedef struct ga_shape {
+  int32_t batch;        /* B >= 0 (0: nothing to do)                                  */
+  int32_t num_q_heads;  /* Hq > 0                                                     */
+  int32_t num_kv_heads; /* Hkv > 0, Hq % Hkv == 0, G = Hq / Hkv <= 16                 */
+  int32_t head_dim;     /* D: 256 or 512                                              */
+  int32_t capacity;     /* ring: W slots; linear: C positions                         */
+  int32_t kind;         /* GA_CACHE_LINEAR or GA_CACHE_RING                           */
+  int32_t max_ctx;      /* host upper bound on every ctx_lens[b]; 0 means `capacity`  */
+} ga_shape;
+
+/* Implementation choice for the split kernel. */
+enum { GA_IMPL_AUTO = 0, GA_IMPL_VALU = 1, GA_IMPL_MFMA = 2 };
+
+/* Optional decode options (NULL = all automatic). */
+typedef struct ga_decode_opts {
+  int32_t split_keys; /* keys per split work unit: 0 = automatic; otherwise a multiple
+                         of 64 in [64, 65536].  Results are split-invariant within
+                         rounding.                                                     */
+  int32_t impl;       /* GA_IMPL_*; MFMA exists for head_dim 512 with G = 16 and K = V */
+  int32_t reserved[6]; /* must be zero                                                 */
+} ga_decode_opts;
+
+/*
+ * Bytes of device workspace gemma_attn_decode needs for this shape, window and options:
+ * split partials (m, l, acc) in fp32, [B, Hq, S, D + 2] with S the host upper bound of
+ * splits per row.  0 when every row fits in one split (no workspace is touched).
+ * Returns SIZE_MAX when the arguments are invalid (the decode call would fail).
+ */
+size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window, const ga_decode_opts* opts);
+
+/*
+ * Single-token decode attention (see the definition above).
+ *   q        device bf16 [B, Hq, D]
+ *   k_cache  device bf16 [B, Hkv, capacity, D]
+ *   v_cache  device bf16, same shape, or NULL when K = V (the K tensor is read once per
+ *            tile and used as both keys and values)
+ *   ctx_lens device int32 [B]: positions 0..ctx-1 have been appended
+ *   q_pos    device int32 [B]: absolute position of the query token (usually ctx - 1)
+ *   window   > 0: sliding window of `window` positions; <= 0: full causal
+ *   softcap  > 0 and finite: tanh soft-cap of the scaled logits; otherwise off
+ *   scale    finite query scale applied to the fp32 dot products
+ *   out      device float32 [B, Hq, D], fully overwritten
+ *   workspace/workspace_bytes  device scratch of at least ga_decode_workspace_bytes
+ *            (may be NULL when that is 0); contents need not be initialised
+ * Launches the split kernel and, when any row can need more than one split, the
+ * log-sum-exp merge kernel, both on `stream`.
+ */
+int32_t gemma_attn_decode(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
+                          const ga_bf16* v_cache, const int32_t* ctx_lens, const int32_t* q_pos,
+                          int32_t window, float softcap, float scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* gemma_attn_decode with explicit options (split size, implementation); opts may be NULL. */
+int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
+                             const ga_bf16* v_cache, const int32_t* ctx_lens, const int32_t* q_pos,
+                             int32_t window, float softcap, float scale, float* out, void* workspace,
+                             size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
+
+/*
+ * Cache append of one token per sequence: cache[b, g, slot(pos_b), :] <- new[b, g, :]
+ * for K, and for V unless K = V.  Ring: slot = pos mod W; linear: slot = pos.
+ *   k_new, v_new device bf16 [B, Hkv, D]; v_cache and v_new are both NULL for K = V.
+ *   pos device int32 [B]: absolute position of the new token (>= 0; linear: < C).
+ * A row whose position is out of range (negative, or >= C for linear) is skipped:
+ * nothing is written for it.  The copy is bit-exact.
+ * Passages: "Gemma 4 12B (unified multimodal)" record, per-layer-type cache management
+ * and the rotating KV cache of sliding layers; "gemma-4-E2B-CoreAI" model card,
+ * the KV cache that grows on the device during decode.
+ */
+int32_t gemma_kv_append(const ga_shape* shape, ga_bf16* k_cache, ga_bf16* v_cache,
+                        const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
+                        void* stream);
+
+/* Precondition flags written by gemma_attn_validate, per batch row. */
+enum {
+  GA_FLAG_QPOS_GE_CTX = 1, /* q_pos >= ctx                                         */
+  GA_FLAG_EVICTED = 2,     /* ring: the window (or full attention) needs overwritten slots */
+  GA_FLAG_LINEAR_OVER = 4, /* linear: ctx > C                                      */
+  GA_FLAG_NEGATIVE = 8,    /* ctx < 0 or q_pos < 0                                 */
+  GA_FLAG_OVER_MAX_CTX = 16 /* ctx > shape->max_ctx (the workspace bound)          */
+};
+
+/*
+ * Debug check of the device-side preconditions: writes GA_FLAG_* bits for each row to
+ * dev_flags (device int32 [B]) on `stream`.  The decode itself does not need it.
+ */
+int32_t gemma_attn_validate(const ga_shape* shape, const int32_t* ctx_lens, const int32_t* q_pos,
+                            int32_t window, int32_t* dev_flags, void* stream);
+
+/*
+ * Debug dump of the key range each row attends to, computed by the same device code
+ * the decode kernels use: dev_out (device int32 [B, 4]) receives
+ * (lo, hi, slot(lo), n) with n = hi - lo + 1 (n = 0 and lo = hi + 1 for an empty row).
+ */
+int32_t gemma_attn_debug_ranges(const ga_shape* shape, const int32_t* ctx_lens,
+                                const int32_t* q_pos, int32_t window, int32_t* dev_out,
+                                void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gemma_attn_strerror(int32_t status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int32_t gemma_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMA_ATTN_H */

@@ -1,0 +1,165 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load and export every function include/gemma_attn.h declares, and
+every host-side argument check must fire before any HIP call (so these calls never
+touch device memory: the pointers passed are never dereferenced).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from decode_attention_split_amd import _lib
+from decode_attention_split_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemma_attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert "gemma_attn_decode" in names and "gemma_kv_append" in names
+    assert sorted(names) == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    lib = _lib.load()
+    assert lib.gemma_attn_version() >= 100
+    for code in [0] + list(api.ERRORS) + [-999, 5]:
+        s = lib.gemma_attn_strerror(code)
+        assert s is not None and len(s) > 0
+
+
+def shape(B=2, Hq=16, Hkv=8, D=256, cap=1024, kind=api.RING, max_ctx=0):
+    return api.make_shape(B, Hq, Hkv, D, cap, kind, max_ctx)
+
+
+def call_decode(s, window=1024, softcap=0.0, scale=0.0625, v=FAKE, ws=FAKE, ws_bytes=1 << 40,
+                q=FAKE, k=FAKE, ctx=FAKE, qpos=FAKE, out=FAKE, opts=None):
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    return lib.gemma_attn_decode_ex(ctypes.byref(s), P(q), P(k), P(v) if v else None, P(ctx),
+                                    P(qpos), window, softcap, scale, P(out), P(ws) if ws else None,
+                                    ws_bytes, ctypes.byref(opts) if opts else None, None)
+
+
+def no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=shape(D=128)), -3),
+    (dict(s=shape(D=384)), -3),
+    (dict(s=shape(Hq=12, Hkv=8)), -4),
+    (dict(s=shape(Hq=24, Hkv=1)), -4),    # G = 24 is not supported
+    (dict(s=shape(Hq=6, Hkv=2)), -4),     # G = 3 is not supported
+    (dict(s=shape(B=-1)), -2),
+    (dict(s=shape(Hkv=0)), -2),
+    (dict(s=shape(cap=0)), -2),
+    (dict(s=shape(kind=2)), -5),
+    (dict(s=shape(cap=512), window=1024), -6),             # ring window > W
+    (dict(s=shape(cap=512, max_ctx=4096), window=0), -6),  # full attention, ctx may exceed W
+    (dict(s=shape(kind=api.LINEAR, cap=512, max_ctx=513), window=0), -13),
+    (dict(s=shape(max_ctx=-5)), -13),
+    (dict(s=shape(), scale=math.inf), -8),
+    (dict(s=shape(), scale=math.nan), -8),
+    (dict(s=shape(), q=0), -1),
+    (dict(s=shape(), k=0), -1),
+    (dict(s=shape(), ctx=0), -1),
+    (dict(s=shape(), qpos=0), -1),
+    (dict(s=shape(), out=0), -1),
+    (dict(s=shape(), q=FAKE + 8), -1),                     # not 16-byte aligned
+    (dict(s=shape(B=64), ws=0, ws_bytes=0), -7),
+    (dict(s=shape(B=64), ws_bytes=16), -7),
+    (dict(s=shape(), opts=api.make_opts(split_keys=100)), -12),
+    (dict(s=shape(), opts=api.make_opts(split_keys=32)), -12),
+    (dict(s=shape(), opts=api.make_opts(impl=7)), -12),
+    (dict(s=shape(), opts=api.make_opts(impl=api.IMPL_MFMA)), -12),  # MFMA: D512 G16 only
+])
+def test_decode_rejects_bad_arguments_before_any_launch(kw, code):
+    assert call_decode(**kw) == code
+
+
+def test_reserved_option_fields_must_be_zero():
+    o = api.make_opts()
+    o.reserved[3] = 1
+    assert call_decode(shape(), opts=o) == -12
+
+
+@pytest.mark.skipif(not no_gpu(), reason="checks the no-device path")
+def test_valid_decode_without_a_gpu_reports_arch_error():
+    assert call_decode(shape()) == -10
+    s = shape(B=0)
+    assert call_decode(s, ws=0, ws_bytes=0) == -10
+
+
+def test_workspace_bytes_closed_form():
+    lib = _lib.load()
+    # B 64, Hq 16, D 256, ring W = w = 1024, split 256 keys -> S = 4 splits
+    s = shape(B=64, Hq=16, Hkv=8, D=256, cap=1024, max_ctx=8192)
+    o = api.make_opts(split_keys=256)
+    n = lib.ga_decode_workspace_bytes(ctypes.byref(s), 1024, ctypes.byref(o))
+    assert n == 64 * 16 * 4 * (256 + 2) * 4
+    # one split covers every row: no workspace
+    o = api.make_opts(split_keys=1024)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 1024, ctypes.byref(o)) == 0
+    # a window shorter than the ring bounds the keys: w = 100 -> one 128-key split
+    o = api.make_opts(split_keys=128)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 100, ctypes.byref(o)) == 0
+    # linear C 32768, full causal, split 512: S = 64
+    s = shape(B=16, Hq=16, Hkv=1, D=512, cap=32768, kind=api.LINEAR)
+    o = api.make_opts(split_keys=512)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == \
+        16 * 16 * 64 * 514 * 4
+    # invalid shape -> SIZE_MAX
+    bad = shape(D=100)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(bad), 0, None) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v_cache=FAKE, v_new=0), -9),
+    (dict(v_cache=0, v_new=FAKE), -9),
+    (dict(k_cache=0), -1),
+    (dict(pos=0), -1),
+    (dict(D=100), -3),
+    (dict(kind=5), -5),
+    (dict(Hkv=0), -2),
+])
+def test_append_rejects_bad_arguments(kw, code):
+    lib = _lib.load()
+    args = dict(k_cache=FAKE, v_cache=FAKE, k_new=FAKE, v_new=FAKE, pos=FAKE, D=256, kind=api.RING,
+                Hkv=8)
+    args.update(kw)
+    s = api.make_shape(4, 8, args["Hkv"], args["D"], 1024, args["kind"])
+    P = ctypes.c_void_p
+    rc = lib.gemma_kv_append(ctypes.byref(s), P(args["k_cache"]) if args["k_cache"] else None,
+                             P(args["v_cache"]) if args["v_cache"] else None, P(args["k_new"]),
+                             P(args["v_new"]) if args["v_new"] else None,
+                             P(args["pos"]) if args["pos"] else None, None)
+    assert rc == code
+
+
+def test_append_and_debug_calls_without_a_gpu():
+    if not no_gpu():
+        pytest.skip("checks the no-device path")
+    lib = _lib.load()
+    s = api.make_shape(4, 8, 8, 256, 1024, api.RING)
+    P = ctypes.c_void_p
+    assert lib.gemma_kv_append(ctypes.byref(s), P(FAKE), None, P(FAKE), None, P(FAKE), None) == -10
+    assert lib.gemma_attn_validate(ctypes.byref(s), P(FAKE), P(FAKE), 1024, P(FAKE), None) == -10
+    assert lib.gemma_attn_debug_ranges(ctypes.byref(s), P(FAKE), P(FAKE), 1024, P(FAKE),
+                                       None) == -10

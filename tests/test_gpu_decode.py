@@ -1,0 +1,250 @@
+"""GPU: decode attention against the fp64 oracle, and the invariants of the method.
+
+Every parity case poisons the slots outside each row's valid set with bf16 NaN, so a
+stray read shows up as a NaN output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_split_amd import api, synth
+from decode_attention_split_amd import workloads as wl
+
+from common import (LayerInputs, assert_parity, default_scale, errors, f32, gen_layer, log,
+                    oracle_out, poison_invalid_slots)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, window, softcap, scale, kind, **kw):
+    out = api.decode(inp.q, inp.k, inp.v, inp.ctx_t, inp.qpos_t, window, softcap, scale, kind,
+                     **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def layer_case(seed, B, geom: wl.LayerGeom, ctx_lo, ctx_hi, ctx=None, poison=True):
+    inp = gen_layer(seed, B, geom.num_q_heads, geom.num_kv_heads, geom.head_dim, geom.capacity,
+                    geom.k_eq_v, ctx_lo, ctx_hi, ctx)
+    if poison:
+        poison_invalid_slots(inp, geom.window, geom.kind, geom.capacity)
+    return inp.to_device()
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_tiny_sliding_decode():
+    w = wl.TINY
+    g = w.layers[0]
+    inp = layer_case(w.seed, w.batch, g, w.ctx_lo, w.ctx_hi)
+    log(f"tiny: {w.name}")
+    out = run(inp, g.window, g.softcap, g.q_scale, g.kind)
+    assert_parity(out, oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind), "tiny")
+
+
+@pytest.mark.parametrize("w", [wl.G3_1B_SLIDING, wl.G4_12B_SLIDING], ids=["g3_1b", "g4_12b"])
+def test_sliding_layer_full_size(w):
+    g = w.layers[0]
+    log(f"full size: {w.name}")
+    inp = layer_case(w.seed, w.batch, g, w.ctx_lo, w.ctx_hi)
+    out = run(inp, g.window, g.softcap, g.q_scale, g.kind)
+    assert_parity(out, oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind), w.name)
+
+
+def test_global_layer_full_size_sampled_rows():
+    w = wl.G4_12B_GLOBAL
+    g = w.layers[0]
+    log(f"full size: {w.name}")
+    inp = layer_case(w.seed, w.batch, g, w.ctx_lo, w.ctx_hi, poison=False)
+    out = run(inp, g.window, g.softcap, g.q_scale, g.kind)
+    rows = sorted({0, 1, int(np.argmax(inp.ctx)), int(np.argmin(inp.ctx))})
+    ref = oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind, rows=rows)
+    assert_parity(out[rows], ref, f"{w.name} rows {rows}")
+
+
+@pytest.mark.parametrize("layer", [0, 5, 46, 47])
+def test_hybrid_step_layer_sampled_rows(layer):
+    w = wl.HYBRID_48
+    g = w.layers[layer]
+    log(f"hybrid layer {layer}: {'global' if g.k_eq_v else 'sliding'}")
+    inp = layer_case(wl.layer_seed(w, layer), w.batch, g, w.ctx_lo, w.ctx_hi, poison=False)
+    out = run(inp, g.window, g.softcap, g.q_scale, g.kind, max_ctx=min(w.ctx_hi, g.capacity)
+              if g.kind == api.LINEAR else w.ctx_hi)
+    rows = sorted({0, 7, int(np.argmax(inp.ctx)), int(np.argmin(inp.ctx))})
+    ref = oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind, rows=rows)
+    assert_parity(out[rows], ref, f"hybrid layer {layer} rows {rows}")
+
+
+# ------------------------------------------------------------------ geometry sweep
+
+@pytest.mark.parametrize("D", [256, 512])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("k_eq_v", [False, True])
+def test_geometry_sweep(D, G, k_eq_v):
+    """Small shapes that still span several splits and steps with ragged tails."""
+    Hkv = 2 if G <= 4 else 1
+    B = 3
+    kind = api.RING if not k_eq_v else api.LINEAR
+    cap = 200 if kind == api.RING else 700
+    window = 150 if kind == api.RING else 0
+    geom = wl.LayerGeom(G * Hkv, Hkv, D, kind, cap, window, k_eq_v, 30.0 if G % 2 == 0 else 0.0)
+    seed = D * 100 + G * 10 + int(k_eq_v)
+    inp = layer_case(seed, B, geom, 1, 3 * cap if kind == api.RING else cap, ctx=None)
+    log(f"sweep D={D} G={G} k_eq_v={k_eq_v} ctx={inp.ctx.tolist()}")
+    ref = oracle_out(inp, window, geom.softcap, geom.q_scale, kind)
+    for split in [0, 64, 128]:
+        out = run(inp, window, geom.softcap, geom.q_scale, kind, split_keys=split,
+                  max_ctx=int(inp.ctx.max()) if kind == api.RING else cap)
+        assert_parity(out, ref, f"split={split}")
+
+
+# ------------------------------------------------------------------ window / wrap alignment
+
+@pytest.mark.parametrize("W", [64, 1024])
+def test_window_and_wrap_alignments(W):
+    """ctx around multiples of the window and of the split size: where other engines
+    mis-selected sliding-window keys at particular seq_len/page alignments."""
+    w = W
+    ctxs = [1, w - 1, w, w + 1, 2 * w - 1, 2 * w, 2 * w + 1, 3 * w + 64, 5 * w - 63]
+    geom = wl.sliding_geom(4, 2, w, softcap=50.0, scale=1.0 / 16)
+    inp = layer_case(W, len(ctxs), geom, 1, 1, ctx=ctxs)
+    ref = oracle_out(inp, w, geom.softcap, geom.q_scale, geom.kind)
+    for split in [0, 64, 192, 1024]:
+        out = run(inp, w, geom.softcap, geom.q_scale, geom.kind, split_keys=split,
+                  max_ctx=max(ctxs))
+        assert_parity(out, ref, f"W={W} split={split}")
+
+
+def test_causal_query_below_newest_and_partial_window():
+    """q_pos < ctx - 1 masks the later positions; windows narrower than the ring."""
+    geom = wl.LayerGeom(8, 4, 256, api.RING, 256, 100, False, 0.0, 0.0625)
+    inp = gen_layer(77, 6, 8, 4, 256, 256, False, 1, 1, ctx=[300, 300, 257, 256, 100, 5])
+    inp.qpos = np.array([299, 250, 200, 255, 50, 0], np.int32)
+    poison_invalid_slots(inp, geom.window, geom.kind, geom.capacity)
+    inp.to_device()
+    ref = oracle_out(inp, geom.window, 0.0, 0.0625, geom.kind)
+    out = run(inp, geom.window, 0.0, 0.0625, geom.kind, max_ctx=300)
+    assert_parity(out, ref, "causal/partial window")
+
+
+def test_empty_rows_give_zero():
+    geom = wl.global_geom(16, 512)
+    inp = gen_layer(78, 3, 16, 1, 512, 512, True, 1, 1, ctx=[0, 10, 0]).to_device()
+    for split in [0, 64]:
+        out = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=split)
+        assert (out[0] == 0).all() and (out[2] == 0).all()
+        assert torch.isfinite(out[1]).all() and out[1].abs().sum() > 0
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_constant_values_give_constant_output():
+    """V = 1 everywhere: every softmax row sums to 1, so out = 1."""
+    geom = wl.sliding_geom(16, 8, 1024)
+    inp = gen_layer(79, 8, 16, 8, 256, 1024, False, 1, 5000)
+    inp.v_bits[:] = 0x3F80
+    inp.to_device()
+    for split in [0, 64, 1024]:
+        out = run(inp, 1024, 0.0, 1.0, api.RING, split_keys=split, max_ctx=5000)
+        assert (out - 1.0).abs().max().item() < 1e-5
+
+
+def test_single_valid_key_returns_that_row_bitwise():
+    """ctx = 1, or window = 1: the output is that V row exactly."""
+    inp = gen_layer(80, 4, 16, 8, 256, 64, False, 1, 1, ctx=[1, 40, 64, 200])
+    inp.to_device()
+    out = run(inp, 1, 50.0, 0.0625, api.RING, max_ctx=200)
+    v = synth.from_bits(inp.v_bits, "cuda").float()
+    for b, c in enumerate(inp.ctx):
+        slot = (c - 1) % 64
+        for h in range(16):
+            assert torch.equal(out[b, h], v[b, h // 2, slot]), (b, h)
+
+
+def test_split_count_invariance():
+    g = wl.global_geom(16, 4096)
+    inp = gen_layer(81, 4, 16, 1, 512, 4096, True, 100, 4096).to_device()
+    base = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=4096)
+    for split in [64, 128, 448, 1024, 0]:
+        out = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=split)
+        max_abs, rel = errors(out, base.double().cpu().numpy())
+        assert max_abs < 2e-5 and rel < 2e-5, (split, max_abs, rel)
+
+
+def test_k_eq_v_null_equals_same_values_passed_twice():
+    inp = gen_layer(82, 4, 16, 1, 512, 2048, True, 1, 2048).to_device()
+    a = run(inp, 0, 0.0, default_scale(512), api.LINEAR, impl=api.IMPL_VALU)
+    copy = inp.k.clone()
+    b = api.decode(inp.q, inp.k, copy, inp.ctx_t, inp.qpos_t, 0, 0.0, default_scale(512),
+                   api.LINEAR, impl=api.IMPL_VALU)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_ring_equals_linear_bitwise():
+    """The same history in a ring and in a linear cache gives the same output bit for
+    bit: keys are visited in position order in both layouts."""
+    B, Hkv, D, W, total = 3, 2, 256, 128, 700
+    gen = synth.generator(83)
+    hist_k = synth.bits(synth.normal_bf16(gen, (B, Hkv, total, D)))
+    hist_v = synth.bits(synth.normal_bf16(gen, (B, Hkv, total, D)))
+    ring_k = np.full((B, Hkv, W, D), synth.BF16_NAN, np.uint16)
+    ring_v = ring_k.copy()
+    ctx = np.array([700, 555, 129], np.int32)
+    for b in range(B):
+        for p in range(max(0, ctx[b] - W), ctx[b]):
+            ring_k[b, :, p % W] = hist_k[b, :, p]
+            ring_v[b, :, p % W] = hist_v[b, :, p]
+    q = synth.normal_bf16(synth.generator(84), (B, 8, D)).cuda()
+    ctx_t = torch.from_numpy(ctx).cuda()
+    qp = ctx_t - 1
+    a = api.decode(q, synth.from_bits(ring_k, "cuda"), synth.from_bits(ring_v, "cuda"), ctx_t, qp,
+                   W, 0.0, 0.0625, api.RING, max_ctx=700)
+    b = api.decode(q, synth.from_bits(hist_k, "cuda"), synth.from_bits(hist_v, "cuda"), ctx_t, qp,
+                   W, 0.0, 0.0625, api.LINEAR)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all()
+    assert torch.equal(a, b)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    inp = gen_layer(85, 3, 8, 2, 256, 512, False, 100, 512).to_device()
+    a = run(inp, 256, 0.0, 0.0625, api.RING, max_ctx=512)
+    k_rep = inp.k.repeat_interleave(4, dim=1).contiguous()
+    v_rep = inp.v.repeat_interleave(4, dim=1).contiguous()
+    b = api.decode(inp.q, k_rep, v_rep, inp.ctx_t, inp.qpos_t, 256, 0.0, 0.0625, api.RING,
+                   max_ctx=512)
+    torch.cuda.synchronize()
+    max_abs, rel = errors(a, b.double().cpu().numpy())
+    assert max_abs < 1e-5 and rel < 1e-5
+
+
+def test_violated_preconditions_stay_in_bounds_and_are_flagged():
+    """q_pos >= ctx, ctx beyond max_ctx: the kernels clamp, outputs stay finite, and
+    validate reports the rows."""
+    geom = wl.sliding_geom(4, 2, 64)
+    inp = gen_layer(86, 4, 4, 2, 256, 64, False, 1, 1, ctx=[10, 500, 64, 3])
+    inp.qpos = np.array([20, 499, 63, 2], np.int32)
+    inp.to_device()
+    out = run(inp, 64, 0.0, 0.0625, api.RING, max_ctx=100)
+    assert torch.isfinite(out).all()
+    s = api.make_shape(4, 4, 2, 256, 64, api.RING, 100)
+    flags = api.validate(s, inp.ctx_t, inp.qpos_t, 64).cpu().numpy()
+    assert flags[0] & api.FLAG_QPOS_GE_CTX
+    assert flags[1] & api.FLAG_OVER_MAX_CTX
+    assert flags[2] == 0 and flags[3] == 0
+
+
+def test_device_errors_launch_nothing():
+    inp = gen_layer(87, 2, 4, 1, 256, 64, False, 10, 20).to_device()
+    out = torch.full((2, 4, 256), 7.0, device="cuda")
+    with pytest.raises(api.GemmaAttnError) as e:
+        api.decode(inp.q, inp.k, inp.v, inp.ctx_t, inp.qpos_t, 65, 0.0, 0.0625, api.RING, out=out)
+    assert e.value.code == -6
+    with pytest.raises(api.GemmaAttnError) as e:
+        api.decode(inp.q, inp.k, inp.v, inp.ctx_t, inp.qpos_t, 64, 0.0, math.nan, api.RING, out=out)
+    assert e.value.code == -8
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
