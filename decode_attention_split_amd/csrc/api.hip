@@ -82,20 +82,13 @@ long long max_keys_bound(const ga_shape* s, int32_t window) {
   return n;
 }
 
-int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, Plan* p) {
-  const int D = s->head_dim, G = s->num_q_heads / s->num_kv_heads;
-  int impl = GA_IMPL_AUTO, ts = 0;
-  if (o) {
-    for (int i = 0; i < 6; ++i)
-      if (o->reserved[i] != 0) return GA_ERR_OPTS;
-    impl = o->impl;
-    ts = o->split_keys;
-    if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
-    if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
-  }
-  // The MFMA path exists for the K = V global geometry (head_dim 512, 16 query heads on
-  // one KV head); K = V is only known at decode time, so AUTO resolves there.
-  if (impl == GA_IMPL_MFMA && !ga::decode_mfma_supported(D, G, true)) return GA_ERR_OPTS;
+bool mfma_eligible(const ga_shape* s, bool k_eq_v) {
+  const int G = s->num_q_heads / s->num_kv_heads;
+  return ga::decode_mfma_supported(s->head_dim, G, k_eq_v) &&
+         (long long)s->batch * s->num_kv_heads <= ga::kMfmaMaxUnits;
+}
+
+int32_t valu_plan(const ga_shape* s, int32_t window, int ts, Plan* p) {
   const long long nmax = max_keys_bound(s, window);
   const long long units = (long long)s->batch * s->num_kv_heads;
   if (ts == 0) {
@@ -111,12 +104,56 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, Pl
   long long S = nmax > 0 ? (nmax + ts - 1) / ts : 1;
   if (S < 1) S = 1;
   if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
-  p->impl = impl;
+  p->impl = GA_IMPL_VALU;
   p->split_keys = ts;
   p->n_split = (int)S;
   p->max_keys = (int)(S * ts);
-  p->ws_bytes = S > 1 ? (size_t)s->batch * s->num_q_heads * (size_t)S * (size_t)(D + 2) * 4u : 0;
+  p->ws_bytes = S > 1 ? (size_t)s->batch * s->num_q_heads * (size_t)S * (size_t)(s->head_dim + 2) * 4u
+                      : 0;
   return GA_OK;
+}
+
+void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
+  long long nmax = max_keys_bound(s, window);
+  p->impl = GA_IMPL_MFMA;
+  p->split_keys = 0;
+  p->n_split = 0;
+  p->max_keys = (int)(nmax > 0 ? nmax : 1);
+  p->ws_bytes = ga::decode_mfma_workspace_bytes(s->batch, s->num_kv_heads);
+}
+
+// k_eq_v: 1 / 0 when known (a decode call), -1 for a workspace query, which then sizes
+// for whichever implementation AUTO may pick.
+int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, int k_eq_v,
+                  Plan* p) {
+  int impl = GA_IMPL_AUTO, ts = 0;
+  if (o) {
+    for (int i = 0; i < 6; ++i)
+      if (o->reserved[i] != 0) return GA_ERR_OPTS;
+    impl = o->impl;
+    ts = o->split_keys;
+    if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
+    if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
+  }
+  if (impl == GA_IMPL_MFMA) {
+    // the matrix-core kernel balances keys over a fixed grid: no split size to choose
+    if (ts != 0 || k_eq_v == 0 || !mfma_eligible(s, true)) return GA_ERR_OPTS;
+    mfma_plan(s, window, p);
+    return GA_OK;
+  }
+  if (impl == GA_IMPL_AUTO && ts == 0 && k_eq_v != 0 && mfma_eligible(s, true)) {
+    if (k_eq_v == 1) {
+      mfma_plan(s, window, p);
+      return GA_OK;
+    }
+    Plan v;
+    int32_t st = valu_plan(s, window, 0, &v);
+    if (st != GA_OK) return st;
+    mfma_plan(s, window, p);
+    if (v.ws_bytes > p->ws_bytes) p->ws_bytes = v.ws_bytes;
+    return GA_OK;
+  }
+  return valu_plan(s, window, ts, p);
 }
 
 }  // namespace
@@ -152,7 +189,7 @@ size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window,
                                  const ga_decode_opts* opts) {
   if (check_shape(shape, window) != GA_OK) return SIZE_MAX;
   Plan p;
-  if (make_plan(shape, window, opts, &p) != GA_OK) return SIZE_MAX;
+  if (make_plan(shape, window, opts, -1, &p) != GA_OK) return SIZE_MAX;
   return p.ws_bytes;
 }
 
@@ -167,15 +204,11 @@ int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_b
       !aligned16(out) || !aligned16(workspace))
     return GA_ERR_NULL;
   if (!std::isfinite(scale)) return GA_ERR_SCALE;
-  Plan p;
-  st = make_plan(shape, window, opts, &p);
-  if (st != GA_OK) return st;
-  const int D = shape->head_dim, G = shape->num_q_heads / shape->num_kv_heads;
   const bool k_eq_v = v_cache == nullptr || v_cache == k_cache;
-  int impl = p.impl;
-  if (impl == GA_IMPL_MFMA && !k_eq_v) return GA_ERR_OPTS;
-  if (impl == GA_IMPL_AUTO)
-    impl = ga::decode_mfma_supported(D, G, k_eq_v) ? GA_IMPL_MFMA : GA_IMPL_VALU;
+  Plan p;
+  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p);
+  if (st != GA_OK) return st;
+  const int D = shape->head_dim;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return GA_ERR_WORKSPACE;
   st = check_arch();
   if (st != GA_OK) return st;
@@ -189,9 +222,20 @@ int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_b
   a.q_pos = q_pos;
   a.out = out;
   float* ws = static_cast<float*>(workspace);
-  const size_t n_acc = (size_t)shape->batch * shape->num_q_heads * (size_t)p.n_split * D;
-  a.part_acc = p.n_split > 1 ? ws : nullptr;
-  a.part_ml = p.n_split > 1 ? ws + n_acc : nullptr;
+  a.part_acc = nullptr;
+  a.part_ml = nullptr;
+  a.plan = nullptr;
+  a.n_blocks = 0;
+  if (p.impl == GA_IMPL_MFMA) {
+    const size_t slots = (size_t)ga::kMfmaBlocks + (size_t)shape->batch * shape->num_kv_heads;
+    a.part_acc = ws;
+    a.part_ml = ws + slots * 16 * D;
+    a.plan = reinterpret_cast<int*>(a.part_ml + slots * 16 * 2);
+  } else if (p.n_split > 1) {
+    const size_t n_acc = (size_t)shape->batch * shape->num_q_heads * (size_t)p.n_split * D;
+    a.part_acc = ws;
+    a.part_ml = ws + n_acc;
+  }
   a.B = shape->batch;
   a.Hq = shape->num_q_heads;
   a.Hkv = shape->num_kv_heads;
@@ -208,9 +252,13 @@ int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_b
   a.max_keys = p.max_keys;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = impl == GA_IMPL_MFMA ? ga::decode_mfma_launch(a, s)
-                                      : ga::decode_valu_launch(a, k_eq_v, s);
-  if (e == hipSuccess && p.n_split > 1) e = ga::merge_launch(a, s);
+  hipError_t e;
+  if (p.impl == GA_IMPL_MFMA) {
+    e = ga::decode_mfma_launch(a, s);
+  } else {
+    e = ga::decode_valu_launch(a, k_eq_v, s);
+    if (e == hipSuccess && p.n_split > 1) e = ga::merge_launch(a, s);
+  }
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
 }
 
@@ -263,7 +311,7 @@ int32_t gemma_attn_debug_ranges(const ga_shape* shape, const int32_t* ctx_lens,
   if (st != GA_OK) return st;
   if (!ctx_lens || !q_pos || !dev_out) return GA_ERR_NULL;
   Plan p;
-  st = make_plan(shape, window, nullptr, &p);
+  st = make_plan(shape, window, nullptr, 0, &p);
   if (st != GA_OK) return st;
   st = check_arch();
   if (st != GA_OK) return st;

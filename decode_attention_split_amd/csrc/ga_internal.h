@@ -25,8 +25,15 @@ struct DecodeArgs {
   float inv_softcap;
   int split_keys;         // keys per split (Ts)
   int n_split;            // S, splits per row (host upper bound)
-  int max_keys;           // S * Ts: rows longer than this keep their newest keys
+  int max_keys;           // rows longer than this keep their newest keys
+  int* plan;              // matrix-core path: per-unit key prefix sums [B * Hkv + 1]
+  int n_blocks;           // matrix-core path: work-groups of the decode launch
 };
+
+// Matrix-core path limits: units (batch rows x KV heads) per call, and the fixed grid
+// (one work-group of 4 waves per CU of an MI355X).
+constexpr int kMfmaMaxUnits = 1024;
+constexpr int kMfmaBlocks = 256;
 
 // Split kernels.  Each launch covers B * Hkv * S work-groups; with S == 1 the split
 // kernel writes `out` directly, otherwise it writes partials for merge_launch.
@@ -34,9 +41,10 @@ hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stre
 int decode_valu_keys_per_iter(int D, int G);   // split_keys must be a multiple of this
 bool decode_valu_supported(int D, int G);
 
+// Matrix-core path (head_dim 512, G = 16, K = V): decode plus its unit merge.
 hipError_t decode_mfma_launch(const DecodeArgs& a, hipStream_t stream);
-int decode_mfma_keys_per_iter();
 bool decode_mfma_supported(int D, int G, bool k_eq_v);
+size_t decode_mfma_workspace_bytes(int B, int Hkv);  // partials + plan
 
 hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream);
 

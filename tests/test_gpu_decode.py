@@ -168,7 +168,8 @@ def test_split_count_invariance():
     inp = gen_layer(81, 4, 16, 1, 512, 4096, True, 100, 4096).to_device()
     base = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=4096)
     for split in [64, 128, 448, 1024, 0]:
-        out = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=split)
+        out = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=split,
+                  impl=api.IMPL_VALU)
         max_abs, rel = errors(out, base.double().cpu().numpy())
         assert max_abs < 2e-5 and rel < 2e-5, (split, max_abs, rel)
 
@@ -248,3 +249,61 @@ def test_device_errors_launch_nothing():
     assert e.value.code == -8
     torch.cuda.synchronize()
     assert (out == 7.0).all()
+
+
+# ------------------------------------------------------------------ matrix-core global path
+
+@pytest.mark.parametrize("case", ["one_long_row", "many_short_rows", "tile_edges", "ring_kv_shared"])
+def test_mfma_partition_cases(case):
+    """The matrix-core kernel cuts the batch's keys into equal chunks per work-group:
+    one row spread over every work-group, hundreds of rows shorter than a tile, rows
+    ending exactly on / next to tile and chunk edges, empty rows in between."""
+    kind, cap, window, Hkv = api.LINEAR, 40000, 0, 1
+    if case == "one_long_row":
+        ctx = [40000]
+    elif case == "many_short_rows":
+        ctx = list(np.random.default_rng(90).integers(0, 40, size=600))
+        cap = 64
+    elif case == "tile_edges":
+        ctx = [16, 17, 15, 1, 0, 32, 4096, 4095, 4097, 0, 33, 1000]
+        cap = 4097
+    else:  # a ring cache, two KV heads of 16 query heads each
+        kind, cap, window, Hkv = api.RING, 512, 300, 2
+        ctx = [1, 299, 300, 301, 512, 513, 1500, 2047]
+    B = len(ctx)
+    inp = gen_layer(91, B, 16 * Hkv, Hkv, 512, cap, True, 1, 1, ctx=ctx)
+    if B <= 64:
+        poison_invalid_slots(inp, window, kind, cap)
+    inp.to_device()
+    max_ctx = cap if kind == api.LINEAR else max(ctx)
+    scale = default_scale(512)
+    out = run(inp, window, 0.0, scale, kind, impl=api.IMPL_MFMA, max_ctx=max_ctx)
+    rows = list(range(B)) if B <= 64 else list(range(0, B, 7))
+    ref = oracle_out(inp, window, 0.0, scale, kind, rows=rows)
+    assert_parity(out[rows], ref, f"mfma {case}")
+    empty = [b for b in range(B) if ctx[b] == 0]
+    if empty:
+        assert (out[empty] == 0).all()
+
+
+def test_mfma_matches_valu_and_softcap():
+    inp = gen_layer(92, 8, 16, 1, 512, 3000, True, 1, 3000).to_device()
+    scale = default_scale(512)
+    for cap in [0.0, 30.0]:
+        a = run(inp, 0, cap, scale, api.LINEAR, impl=api.IMPL_MFMA)
+        b = run(inp, 0, cap, scale, api.LINEAR, impl=api.IMPL_VALU)
+        max_abs, rel = errors(a, b.double().cpu().numpy())
+        log(f"  mfma vs valu cap={cap}: max_abs={max_abs:.2e} rel={rel:.2e}")
+        assert max_abs < 1e-4 and rel < 1e-4
+    ref = oracle_out(inp, 0, 30.0, scale, api.LINEAR)
+    assert_parity(run(inp, 0, 30.0, scale, api.LINEAR, impl=api.IMPL_MFMA), ref, "mfma softcap")
+
+
+def test_mfma_single_key_rows_are_exact():
+    """One valid key: P = 1 exactly splits into hi = 1, lo = 0, so the output is the row."""
+    inp = gen_layer(93, 3, 16, 1, 512, 64, True, 1, 1, ctx=[1, 1, 1]).to_device()
+    out = run(inp, 0, 0.0, default_scale(512), api.LINEAR, impl=api.IMPL_MFMA)
+    k = synth.from_bits(inp.k_bits, "cuda").float()
+    for b in range(3):
+        for h in range(16):
+            assert torch.equal(out[b, h], k[b, 0, 0])
