@@ -24,6 +24,7 @@ class ga_decode_opts(ctypes.Structure):
 
 # Every symbol include/gemma_attn.h declares.
 EXPORTS = ["ga_decode_workspace_bytes", "gemma_attn_decode", "gemma_attn_decode_ex",
+           "gemma_attn_decode_append",
            "gemma_kv_append", "gemma_attn_validate", "gemma_attn_debug_ranges",
            "gemma_attn_strerror", "gemma_attn_version"]
 
@@ -48,6 +49,9 @@ def load():
     lib.gemma_attn_decode.restype = i32
     lib.gemma_attn_decode_ex.argtypes = [SP, P, P, P, P, P, i32, f32, f32, P, P, sz, OP, P]
     lib.gemma_attn_decode_ex.restype = i32
+    lib.gemma_attn_decode_append.argtypes = [SP, P, P, P, P, P, P, P, P, i32, f32, f32, P, P, sz,
+                                             OP, P]
+    lib.gemma_attn_decode_append.restype = i32
     lib.gemma_kv_append.argtypes = [SP, P, P, P, P, P, P]
     lib.gemma_kv_append.restype = i32
     lib.gemma_attn_validate.argtypes = [SP, P, P, i32, P, P]

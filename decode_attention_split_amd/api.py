@@ -95,15 +95,8 @@ def shape_of(q, k_cache, kind, max_ctx=0):
     return make_shape(B, Hq, Hkv, D, cap, kind, max_ctx)
 
 
-def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
-           kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
-           impl: int = IMPL_AUTO, stream=None):
-    """Single-token decode attention; returns out [B, Hq, D] float32 (see gemma_attn.h).
-
-    v_cache None means K = V (k_cache serves as keys and values).  workspace, when
-    given, is a uint8 device tensor of at least workspace_bytes(...) bytes; otherwise
-    one is allocated here with torch (the library itself never allocates).
-    """
+def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, workspace, max_ctx,
+                   split_keys, impl):
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     if v_cache is not None:
@@ -126,17 +119,56 @@ def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, sc
     lib = _lib.load()
     need = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window), ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
-        need = 0  # let the library report the precise error below
+        need = 0  # let the library report the precise error
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, 1)
+    return shape, out, opts, workspace
+
+
+def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
+           kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
+           impl: int = IMPL_AUTO, stream=None):
+    """Single-token decode attention; returns out [B, Hq, D] float32 (see gemma_attn.h).
+
+    v_cache None means K = V (k_cache serves as keys and values).  workspace, when
+    given, is a uint8 device tensor of at least workspace_bytes(...) bytes; otherwise
+    one is allocated here with torch (the library itself never allocates).
+    """
+    shape, out, opts, workspace = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window,
+                                                 kind, out, workspace, max_ctx, split_keys, impl)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    rc = lib.gemma_attn_decode_ex(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                  _ptr(ctx_lens), _ptr(q_pos), int(window), float(softcap),
-                                  float(scale), _ptr(out), _ptr(workspace), ws_bytes,
-                                  ctypes.byref(opts), _stream_handle(stream))
+    rc = _lib.load().gemma_attn_decode_ex(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens), _ptr(q_pos),
+        int(window), float(softcap), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+        ctypes.byref(opts), _stream_handle(stream))
     _check(rc, "gemma_attn_decode")
+    return out
+
+
+def decode_append(q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, window: int,
+                  softcap: float, scale: float, kind: int, out=None, workspace=None,
+                  max_ctx: int = 0, split_keys: int = 0, impl: int = IMPL_AUTO, stream=None):
+    """kv_append(k_cache, v_cache, k_new, v_new, pos) then decode(...), in one launch."""
+    shape, out, opts, workspace = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window,
+                                                 kind, out, workspace, max_ctx, split_keys, impl)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    if (v_cache is None) != (v_new is None):
+        _check(-9, "gemma_attn_decode_append")
+    if v_new is not None:
+        _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(pos, "pos", torch.int32, 1)
+    B, Hkv, _, D = k_cache.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or (v_new is not None and v_new.shape != k_new.shape) \
+            or pos.numel() != B:
+        raise ValueError("k_new / v_new must be [B, Hkv, D] and pos [B]")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = _lib.load().gemma_attn_decode_append(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        _ptr(pos), _ptr(ctx_lens), _ptr(q_pos), int(window), float(softcap), float(scale),
+        _ptr(out), _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream_handle(stream))
+    _check(rc, "gemma_attn_decode_append")
     return out
 
 

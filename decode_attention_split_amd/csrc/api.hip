@@ -18,7 +18,8 @@ constexpr int kMaxDevices = 64;
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other.
 std::atomic<int> g_arch_ok[kMaxDevices];
 
-constexpr int kTargetBlocks = 2048;  // ~8 work-groups per CU on 256 CUs
+constexpr int kTargetBlocks = 256;   // one work-group per CU of an MI355X
+constexpr int kWideBelowBlocks = 512;  // fewer work-groups than this: use the wide variant
 constexpr int kMaxSplitKeys = 65536;
 
 int32_t check_arch() {
@@ -68,6 +69,7 @@ int32_t check_shape(const ga_shape* s, int32_t window) {
 
 struct Plan {
   int impl;        // GA_IMPL_VALU / GA_IMPL_MFMA
+  int n_waves;     // vector path: waves per work-group (0: default)
   int split_keys;  // Ts
   int n_split;     // S
   int max_keys;    // S * Ts
@@ -92,8 +94,9 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, Plan* p) {
   const long long nmax = max_keys_bound(s, window);
   const long long units = (long long)s->batch * s->num_kv_heads;
   if (ts == 0) {
-    // Enough work-groups to fill the chip, but at least 128 keys each so the per-split
-    // partial (G * (D + 2) floats) stays small next to the split's KV bytes.
+    // Enough work-groups to reach every CU, but at least 128 keys each so the per-split
+    // partial (G * (D + 2) floats) stays small next to the split's KV bytes.  Rows that
+    // fit one split are written directly, with no partials and no merge launch.
     long long want_splits = units > 0 ? (kTargetBlocks + units - 1) / units : 1;
     long long t = nmax > 0 ? (nmax + want_splits - 1) / want_splits : 64;
     t = (t + 63) / 64 * 64;
@@ -105,6 +108,8 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, Plan* p) {
   if (S < 1) S = 1;
   if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
   p->impl = GA_IMPL_VALU;
+  const int wide = ga::decode_valu_wide_waves(s->head_dim, s->num_q_heads / s->num_kv_heads);
+  p->n_waves = (wide > 0 && units * S < kWideBelowBlocks) ? wide : 0;
   p->split_keys = ts;
   p->n_split = (int)S;
   p->max_keys = (int)(S * ts);
@@ -116,6 +121,7 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, Plan* p) {
 void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
   long long nmax = max_keys_bound(s, window);
   p->impl = GA_IMPL_MFMA;
+  p->n_waves = 0;
   p->split_keys = 0;
   p->n_split = 0;
   p->max_keys = (int)(nmax > 0 ? nmax : 1);
@@ -193,13 +199,24 @@ size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window,
   return p.ws_bytes;
 }
 
-int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
-                             const ga_bf16* v_cache, const int32_t* ctx_lens, const int32_t* q_pos,
-                             int32_t window, float softcap, float scale, float* out, void* workspace,
-                             size_t workspace_bytes, const ga_decode_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode, optionally fused with the cache append of one token per row (k_new != nullptr).
+int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, ga_bf16* v_cache,
+                    const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* new_pos,
+                    const int32_t* ctx_lens, const int32_t* q_pos, int32_t window, float softcap,
+                    float scale, float* out, void* workspace, size_t workspace_bytes,
+                    const ga_decode_opts* opts, void* stream) {
   int32_t st = check_shape(shape, window);
   if (st != GA_OK) return st;
   if (!q || !k_cache || !ctx_lens || !q_pos || !out) return GA_ERR_NULL;
+  if (k_new) {
+    if (!new_pos) return GA_ERR_NULL;
+    if ((v_cache == nullptr) != (v_new == nullptr)) return GA_ERR_V_MISMATCH;
+    if (!aligned16(k_new) || !aligned16(v_new)) return GA_ERR_NULL;
+  }
   if (!aligned16(q) || !aligned16(k_cache) || (v_cache && !aligned16(v_cache)) ||
       !aligned16(out) || !aligned16(workspace))
     return GA_ERR_NULL;
@@ -250,6 +267,12 @@ int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_b
   a.split_keys = p.split_keys;
   a.n_split = p.n_split;
   a.max_keys = p.max_keys;
+  a.n_waves = p.n_waves;
+  a.k_new = k_new;
+  a.v_new = k_eq_v ? nullptr : v_new;
+  a.new_pos = k_new ? new_pos : nullptr;
+  a.k_dst = k_cache;
+  a.v_dst = k_eq_v ? nullptr : v_cache;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -260,6 +283,31 @@ int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_b
     if (e == hipSuccess && p.n_split > 1) e = ga::merge_launch(a, s);
   }
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
+                             const ga_bf16* v_cache, const int32_t* ctx_lens, const int32_t* q_pos,
+                             int32_t window, float softcap, float scale, float* out, void* workspace,
+                             size_t workspace_bytes, const ga_decode_opts* opts, void* stream) {
+  // The caches are only read when nothing is appended.
+  return decode_impl(shape, q, const_cast<ga_bf16*>(k_cache), const_cast<ga_bf16*>(v_cache),
+                     nullptr, nullptr, nullptr, ctx_lens, q_pos, window, softcap, scale, out,
+                     workspace, workspace_bytes, opts, stream);
+}
+
+int32_t gemma_attn_decode_append(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache,
+                                 ga_bf16* v_cache, const ga_bf16* k_new, const ga_bf16* v_new,
+                                 const int32_t* pos, const int32_t* ctx_lens,
+                                 const int32_t* q_pos, int32_t window, float softcap, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 const ga_decode_opts* opts, void* stream) {
+  if (!k_new) return GA_ERR_NULL;
+  return decode_impl(shape, q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, window,
+                     softcap, scale, out, workspace, workspace_bytes, opts, stream);
 }
 
 int32_t gemma_attn_decode(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,

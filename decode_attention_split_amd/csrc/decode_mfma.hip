@@ -7,26 +7,33 @@
 // the HBM roofline ("Gemma4-26B-A4B on Apple Silicon", Results, Break 4: 16 query heads
 // on one shared K/V head, no separate value projection).
 //
-// Work partition: the valid keys of all (batch row, KV head) units are laid end to end
-// (prefix sums of the per-unit counts, computed on the device from ctx_lens / q_pos) and
-// cut into gridDim.x equal chunks, one per work-group.  Ragged contexts with few units
-// (a single KV head, batch 16-32) therefore still spread evenly over every CU -- the
-// failure mode of decode kernels that ignore key splitting ("Gemma 4 12B (unified
-// multimodal)" record, item (4): 2 of 132 SMs busy).  A unit cut across work-groups is
-// finished by merge_units_kernel (log-sum-exp); a unit inside one work-group is written
-// directly.  Partial slot of (work-group i, unit u) is i + u: slots never collide.
+// Work partition: the chip gets NB work-groups' worth of keys, C = ceil(T / NB) keys each
+// (T = valid keys of the whole batch, rounded to tiles), and every (batch row, KV head)
+// unit u with n_u keys gets k_u = ceil(n_u / C) work-groups, each an equal tile-aligned
+// share of that unit's keys.  The counts come from prefix sums computed on the device
+// from ctx_lens / q_pos, so ragged contexts with few units (one KV head, batch 16-32)
+// still spread evenly over every CU -- the failure mode of decode kernels that ignore
+// key splitting ("Gemma 4 12B (unified multimodal)" record, item (4): 2 of 132 SMs
+// busy) -- and no work-group ever switches units, so its load pipeline never drains.
+// Sum k_u <= NB + units, the grid size.  A unit with k_u = 1 is written directly; the
+// others leave one partial per work-group (slot = work-group index) for
+// merge_units_kernel (log-sum-exp).
 //
-// Per wave, 16-key tiles:
-//   S^T[16 keys][16 heads] = K[16][512] . Q^T[512][16] with v_mfma_f32_16x16x32_bf16:
-//     lane l loads key (l % 16), d = 32 j + 8 (l / 16) + 0..7 for j < 16 straight into the
-//     A operand (16-byte loads), Q^T is held in registers in the same d order;
-//   the same registers are written once to LDS (row stride 1056 B);
-//   O^T[512][16] += V^T[512][16 keys] . P^T[16 keys][16 heads] with
-//     v_mfma_f32_16x16x16_bf16: the A operand comes from LDS with ds_read_b64_tr_b16
-//     (lanes 4e..4e+3 of a 16-lane block read 16 consecutive d of key e; lane i then holds
-//     the 4 keys at column d0 + i), and the B operand is P exactly as the S^T MFMA left it
-//     (lane l: head l % 16, keys 4 (l / 16) + 0..3).  P is split into bf16 hi + lo parts
-//     so the probabilities keep ~16 mantissa bits; the bf16 cache data is exact.
+// Per work-group of 4 waves, 16-key tiles; wave w owns head_dim slice [128 w, 128 w + 128):
+//   partial S^T[16 keys][16 heads] = K[16][slice] . Q^T[slice][16] with
+//     v_mfma_f32_16x16x32_bf16 (4 per tile): lane l loads key (l % 16), d = 128 w + 32 j +
+//     8 (l / 16) + 0..7 straight into the A operand (16-byte loads, 4 tiles in flight),
+//     Q^T is held in registers in the same d order;
+//   the 4 partials are summed through LDS (one barrier per tile), in the same order in
+//     every wave, so every wave holds the identical S^T and the identical softmax state;
+//   the wave's K = V slice goes once to its own LDS rows (288 B stride) and
+//   O^T[slice][16] += V^T[slice][16 keys] . P^T[16 keys][16 heads] with
+//     v_mfma_f32_16x16x16_bf16: the A operand comes from ds_read_b64_tr_b16 (lanes
+//     4e..4e+3 of a 16-lane block read 16 consecutive d of key e; lane i then holds the
+//     4 keys at column d0 + i), the B operand is P exactly as the S^T MFMA left it (lane
+//     l: head l % 16, keys 4 (l / 16) + 0..3), split into bf16 hi + lo parts so the
+//     probabilities keep ~16 mantissa bits (the bf16 cache data is exact).
+// Each wave writes its own slice of the output or partial: no end-of-segment merge.
 // The K = V row is read from HBM once and used for both products.  Softmax state per
 // head is fp32 in log2 units with lazy rescaling (max raised only past +8).
 #include "ga_device.h"
@@ -38,10 +45,18 @@ namespace {
 constexpr int MD = 512;        // head_dim
 constexpr int MG = 16;         // query heads per KV head
 constexpr int TK = 16;         // keys per tile
-constexpr int MNW = 4;         // waves per work-group
-constexpr int ROWB = 1056;     // LDS bytes per tile row: 1024 + 32 (bank spread of tr reads)
-constexpr int TILE_LDS = TK * ROWB;
+constexpr int MNW = 4;         // waves per work-group, one head_dim slice each
+constexpr int DQ = MD / MNW;   // head_dim slice of a wave
+constexpr int ROWQ = DQ * 2 + 32;   // LDS bytes per key row of a wave's slice (bank spread)
+constexpr int WAVE_TILE = TK * ROWQ;
 constexpr float kRescaleLog2 = 8.0f;
+// LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
+// (160 KiB each): every CU then holds the same number of equal-work work-groups.
+constexpr int kLdsCU = 160 * 1024;
+constexpr int kLdsOther = 2 * MNW * 64 * 16 + 2 * (kMfmaMaxUnits + 1) * 4 + MNW * 4;
+constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
+constexpr int kLdsKV = MNW * WAVE_TILE > kLdsTile ? MNW * WAVE_TILE : kLdsTile;
+static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -75,240 +90,276 @@ __device__ __forceinline__ int chunk_keys(int T, int NB) {
   return T > 0 ? (per + TK - 1) / TK * TK : TK;
 }
 
-__global__ void __launch_bounds__(MNW * 64, 1) decode_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_tiles[MNW * TILE_LDS];
-  __shared__ int s_pref[kMfmaMaxUnits + 1];
-  __shared__ float s_m[MNW][MG];
-  __shared__ float s_l[MNW][MG];
+// Sum over the work-group (every thread gets it).
+__device__ __forceinline__ int block_sum(int v, int* s_red, int wave, int lane) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < MNW; ++w) t += s_red[w];
+  return t;
+}
+
+// Inclusive prefix sums of s[1..n] in place (s[0] is left as is), by wave 0.
+__device__ __forceinline__ void wave0_scan(int* s, int n, int wave, int lane) {
+  if (wave != 0) return;
+  int carry = 0;
+  for (int base = 1; base <= n; base += 64) {
+    const int idx = base + lane;
+    int v = idx <= n ? s[idx] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (idx <= n) s[idx] = v + carry;
+    carry += __shfl(v, 63, 64);
+  }
+}
+
+__global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_kv[kLdsKV];
+  __shared__ floatx4_t s_part[2][MNW][64];
+  __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
+  __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
+  __shared__ int s_red[MNW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.B * a.Hkv;
 
-  // ---- prefix sums of valid keys per unit (every work-group computes them)
-  for (int u = tid; u < R; u += MNW * 64) s_pref[u + 1] = unit_keys(a, u);
-  if (tid == 0) s_pref[0] = 0;
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 1; base <= R; base += 64) {
-      const int idx = base + lane;
-      int v = idx <= R ? s_pref[idx] : 0;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-      }
-      if (idx <= R) s_pref[idx] = v + carry;
-      carry += __shfl(v, 63, 64);
-    }
+  // ---- the partition (every work-group computes it; work-group 0 also publishes it)
+  for (int u = tid; u < R; u += MNW * 64) s_n[u + 1] = unit_keys(a, u);
+  if (tid == 0) {
+    s_n[0] = 0;
+    s_k[0] = 0;
   }
   __syncthreads();
-  const int T = s_pref[R];
+  wave0_scan(s_n, R, wave, lane);
+  __syncthreads();
+  // k_u = ceil(n_u / C) <= n_u / C + 1, so with C = T / (NB - R') (R' non-empty units)
+  // the work-groups with work never exceed NB: all of them are resident at once.
+  int nonempty = 0;
+  for (int u = tid; u < R; u += MNW * 64) nonempty += (s_n[u + 1] > s_n[u]) ? 1 : 0;
+  nonempty = block_sum(nonempty, s_red, wave, lane);
+  const int nb_eff = a.n_blocks - nonempty >= a.n_blocks / 4 ? a.n_blocks - nonempty : a.n_blocks;
+  const int C = chunk_keys(s_n[R], nb_eff);
+  for (int u = tid; u < R; u += MNW * 64) s_k[u + 1] = (s_n[u + 1] - s_n[u] + C - 1) / C;
+  __syncthreads();
+  wave0_scan(s_k, R, wave, lane);
+  __syncthreads();
   if (blockIdx.x == 0)
-    for (int u = tid; u <= R; u += MNW * 64) a.plan[u] = s_pref[u];
-  const int C = chunk_keys(T, gridDim.x);
-  const int a0 = blockIdx.x * C;
-  if (a0 >= T) return;
-  const int e0 = min(a0 + C, T);
-
-  // first unit whose keys reach past a0
-  int lo_u = 0, hi_u = R - 1;
-  while (lo_u < hi_u) {
-    const int mid = (lo_u + hi_u) >> 1;
-    if (s_pref[mid + 1] > a0) hi_u = mid; else lo_u = mid + 1;
+    for (int u = tid; u <= R; u += MNW * 64) a.plan[u] = s_k[u];
+  // fused append: work-group u (< R <= grid) writes unit u's new row
+  if (blockIdx.x < R) {
+    const int ub = blockIdx.x / a.Hkv;
+    write_appended_row(a, ub, blockIdx.x % a.Hkv, appended_slot(a, ub), tid);
   }
-
-  char* my_tile = s_tiles + wave * TILE_LDS;
-  char* lds_w = my_tile + l16 * ROWB + lg * 16;                    // A-operand row writes
-  char* lds_r = my_tile + (4 * lg + (l16 >> 2)) * ROWB + (l16 & 3) * 8;  // transposed reads
-
-  for (int u = lo_u; u < R && s_pref[u] < e0; ++u) {
-    const int seg_lo = max(a0, s_pref[u]) - s_pref[u];
-    const int seg_hi = min(e0, s_pref[u + 1]) - s_pref[u];
-    if (seg_hi <= seg_lo) continue;  // empty unit (uniform across the work-group)
-    const int b = u / a.Hkv, g = u % a.Hkv;
-    const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
-    const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
-
-    // Q^T operand: head l16, d = 32 j + 8 lg + 0..7
-    uint4 qv[16];
-    {
-      const uint4* qp = reinterpret_cast<const uint4*>(a.q + (head0 + l16) * MD);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) qv[j] = qp[4 * j + lg];
+  const int g_id = blockIdx.x;
+  if (g_id >= s_k[R]) return;
+  // unit of this work-group: the u with s_k[u] <= g_id < s_k[u + 1]
+  int u, hi_u = R - 1;
+  {
+    int lo_u = 0;
+    while (lo_u < hi_u) {
+      const int mid = (lo_u + hi_u) >> 1;
+      if (s_k[mid + 1] > g_id) hi_u = mid; else lo_u = mid + 1;
     }
-    const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + (size_t)u * a.cap * (MD / 8);
+    u = lo_u;
+  }
+  const int n_u = s_n[u + 1] - s_n[u];
+  const int k_u = s_k[u + 1] - s_k[u];
+  const int part = g_id - s_k[u];
+  const int per = ((n_u + k_u - 1) / k_u + TK - 1) / TK * TK;
+  const int seg_lo = part * per;
+  const int seg_hi = min(n_u, seg_lo + per);  // non-empty: (k_u - 1) * per < n_u
 
-    floatx4_t acc[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.0f;
+  const int b = u / a.Hkv, g = u % a.Hkv;
+  const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
 
-    const int n_tiles = (seg_hi - seg_lo + TK - 1) / TK;
-    const int nt = n_tiles > wave ? (n_tiles - wave + MNW - 1) / MNW : 0;  // this wave's tiles
+  char* my_tile = s_kv + wave * WAVE_TILE;
+  char* lds_w = my_tile + l16 * ROWQ + lg * 16;                          // row writes
+  char* lds_r = my_tile + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;  // transposed reads
+  int par = 0;  // s_part double buffer
 
-    auto load = [&](uint4(&rg)[16], int t) {
-      const int key = seg_lo + (wave + MNW * t) * TK + l16;
-      const int kc = key < seg_hi ? key : seg_hi - 1;
-      const uint4* rp = kbase + (size_t)key_slot(r, kc, a.cap) * (MD / 8);
+  // Q^T operand for this wave's slice: head l16, d = 128 w + 32 j + 8 lg + 0..7
+  uint4 qv[4];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + (head0 + l16) * MD);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) rg[j] = rp[4 * j + lg];
-    };
+    for (int j = 0; j < 4; ++j) qv[j] = qp[16 * wave + 4 * j + lg];
+  }
+  const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + (size_t)u * a.cap * (MD / 8);
+  const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
+  const uint4* knew = a.new_pos ? reinterpret_cast<const uint4*>(a.k_new) + (size_t)u * (MD / 8)
+                                : kbase;
 
-    auto process = [&](uint4(&rg)[16], int t) {
-      const int k0 = seg_lo + (wave + MNW * t) * TK;
-      // logits of 16 keys x 16 heads
-      floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+  floatx4_t acc[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s = mfma_k32(rg[j], qv[j], s);
-      // keep the tile in LDS for the transposed P.V reads, then refill the registers
-#pragma unroll
-      for (int j = 0; j < 16; ++j) *reinterpret_cast<uint4*>(lds_w + j * 64) = rg[j];
-      if (t + 2 < nt) load(rg, t + 2);
-      // softmax: lane holds head l16, keys k0 + 4 lg + i
-      float x[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = s[i] * a.scale;
-        if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
-        x[i] = (k0 + 4 * lg + i < seg_hi) ? v * kLog2e : -INFINITY;
-        mx = fmaxf(mx, x[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (mx > m + kRescaleLog2) {
-        const float f = exp2_fast(m - mx);
-        l *= f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= f;
-        m = mx;
-      }
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = exp2_fast(x[i] - m);
-        l += p[i];
-      }
-      const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
-      const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-      const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-      const short4_t ph = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
-      const short4_t pl = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
-#pragma unroll
-      for (int db = 0; db < 32; ++db) {
-        const short4_t va =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_r + db * 32));
-        acc[db] = mfma_k16(va, ph, acc[db]);
-        acc[db] = mfma_k16(va, pl, acc[db]);
-      }
-    };
+  for (int i = 0; i < 8; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
 
-    uint4 ra[16], rb[16];
-    if (nt > 0) load(ra, 0);
-    if (nt > 1) load(rb, 1);
-    for (int t = 0; t < nt; t += 2) {
-      process(ra, t);
-      if (t + 1 >= nt) break;
-      process(rb, t + 1);
-    }
+  const int nt = (seg_hi - seg_lo + TK - 1) / TK;
 
-    // ---- merge the waves of this work-group for this unit segment
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (lane < MG) {
-      s_m[wave][lane] = m;
-      s_l[wave][lane] = l;
-    }
-    __syncthreads();  // also: every wave is done with its tile LDS
-    float M = -INFINITY;
+  auto load = [&](uint4(&rg)[4], int t) {
+    const int key = seg_lo + t * TK + l16;
+    const int kc = key < seg_hi ? key : seg_hi - 1;
+    const int slot = key_slot(r, kc, a.cap);
+    const uint4* rp = (slot == new_slot ? knew : kbase + (size_t)slot * (MD / 8)) + 16 * wave + lg;
 #pragma unroll
-    for (int w = 0; w < MNW; ++w) M = fmaxf(M, s_m[w][l16]);
-    float Lsum = 0.0f;
+    for (int j = 0; j < 4; ++j) rg[j] = rp[4 * j];
+  };
+
+  auto step = [&](uint4(&rg)[4], int t) {
+    const int k0 = seg_lo + t * TK;
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < MNW; ++w) {
-      const float mw = s_m[w][l16];
-      Lsum += mw == -INFINITY ? 0.0f : s_l[w][l16] * exp2_fast(mw - M);
-    }
-    const float fown = m == -INFINITY ? 0.0f : exp2_fast(m - M);
-    floatx4_t* buf0 = reinterpret_cast<floatx4_t*>(s_tiles);             // 32 KiB
-    floatx4_t* buf1 = reinterpret_cast<floatx4_t*>(s_tiles + 32 * 1024);  // 32 KiB
-    if (wave >= 2) {
-      floatx4_t* dst = wave == 2 ? buf0 : buf1;
+    for (int j = 0; j < 4; ++j) s = mfma_k32(rg[j], qv[j], s);
+    s_part[par][wave][lane] = s;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) dst[db * 64 + lane] = acc[db] * fown;
-    }
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(lds_w + j * 64) = rg[j];
+    load(rg, t + 4);  // unconditional (clamped past the end): keeps wait counts partial
     __syncthreads();
-    if (wave < 2) {
-      const floatx4_t* src = wave == 0 ? buf0 : buf1;
+    const floatx4_t full =
+        ((s_part[par][0][lane] + s_part[par][1][lane]) + s_part[par][2][lane]) +
+        s_part[par][3][lane];
+    par ^= 1;
+    // softmax: lane holds head l16, keys k0 + 4 lg + i
+    float x[4];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) acc[db] = acc[db] * fown + src[db * 64 + lane];
+    for (int i = 0; i < 4; ++i) {
+      float v = full[i] * a.scale;
+      if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
+      x[i] = (k0 + 4 * lg + i < seg_hi) ? v * kLog2e : -INFINITY;
+      mx = fmaxf(mx, x[i]);
     }
-    __syncthreads();
-    if (wave == 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > m + kRescaleLog2) {
+      const float f = exp2_fast(m - mx);
+      l *= f;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) buf0[db * 64 + lane] = acc[db];
+      for (int i = 0; i < 8; ++i) acc[i] *= f;
+      m = mx;
     }
-    __syncthreads();
-    if (wave == 0) {
+    float p[4];
 #pragma unroll
-      for (int db = 0; db < 32; ++db) acc[db] += buf0[db * 64 + lane];
-      const bool whole = seg_lo == 0 && seg_hi == r.n;
-      if (whole) {
-        const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-        float* o = a.out + (head0 + l16) * MD + 4 * lg;
-#pragma unroll
-        for (int db = 0; db < 32; ++db)
-          *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db] * inv;
-      } else {
-        const size_t slot = (size_t)blockIdx.x + u;
-        float* o = a.part_acc + (slot * MG + l16) * MD + 4 * lg;
-#pragma unroll
-        for (int db = 0; db < 32; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db];
-        if (lane < MG) {
-          a.part_ml[(slot * MG + lane) * 2 + 0] = M;
-          a.part_ml[(slot * MG + lane) * 2 + 1] = Lsum;
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_fast(x[i] - m);
+      l += p[i];
     }
-    __syncthreads();  // LDS is reused by the next segment's tiles
+    const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+    const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const short4_t ph = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
+    const short4_t pl = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const short4_t va =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_r + db * 32));
+      acc[db] = mfma_k16(va, ph, acc[db]);
+      acc[db] = mfma_k16(va, pl, acc[db]);
+    }
+  };
+
+  // Straight-line loop body over whole groups of 4 tiles; the last 0-3 tiles run after
+  // it, so the loop header never sees a path with a buffer's loads still unconsumed
+  // (which would make the compiler drain every prefetch there).
+  uint4 r0[4], r1[4], r2[4], r3[4];
+  load(r0, 0);
+  load(r1, 1);
+  load(r2, 2);
+  load(r3, 3);
+  int t = 0;
+  for (; t + 3 < nt; t += 4) {
+    step(r0, t);
+    step(r1, t + 1);
+    step(r2, t + 2);
+    step(r3, t + 3);
+  }
+  if (t < nt) step(r0, t);
+  if (t + 1 < nt) step(r1, t + 1);
+  if (t + 2 < nt) step(r2, t + 2);
+
+  // ---- this wave's slice of the result (m and l are identical in every wave)
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (k_u == 1) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* o = a.out + (head0 + l16) * MD + DQ * wave + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db] * inv;
+  } else {
+    const size_t slot = (size_t)g_id;
+    float* o = a.part_acc + (slot * MG + l16) * MD + DQ * wave + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db];
+    if (wave == 0 && lane < MG) {
+      a.part_ml[(slot * MG + lane) * 2 + 0] = m;
+      a.part_ml[(slot * MG + lane) * 2 + 1] = l;
+    }
   }
 }
 
-// Finishes the units that were cut across work-groups; writes 0 for empty units.
-// One work-group per (unit, head).
-__global__ void __launch_bounds__(256) merge_units_kernel(DecodeArgs a) {
+// Finishes the units that were split over several work-groups; writes 0 for empty
+// units.  One work-group per (unit, head); each thread owns two output elements and
+// runs an online log-sum-exp over the unit's partial slots, 16 slots per batch of
+// independent loads (slot weights and partial sums are loaded together).
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 16;
+
+__global__ void __launch_bounds__(kMergeThreads) merge_units_kernel(DecodeArgs a) {
   const int u = blockIdx.x / MG, h = blockIdx.x % MG;
-  const int R = a.B * a.Hkv;
-  const int T = a.plan[R];
-  const int P0 = a.plan[u], P1 = a.plan[u + 1];
+  const int tid = threadIdx.x;
+  const int K0 = a.plan[u], K1 = a.plan[u + 1];
   const size_t head = ((size_t)(u / a.Hkv) * a.Hq + (size_t)(u % a.Hkv) * MG + h);
   float* out = a.out + head * MD;
-  if (P1 <= P0) {
-    for (int d = threadIdx.x; d < MD; d += 256) out[d] = 0.0f;
+  const int ks = K1 - K0;
+  if (ks == 0) {  // no valid keys
+    for (int d = tid; d < MD; d += kMergeThreads) out[d] = 0.0f;
     return;
   }
-  const int C = chunk_keys(T, a.n_blocks);
-  const int i0 = P0 / C, i1 = (P1 - 1) / C;
-  if (i0 == i1) return;  // written directly by the decode kernel
-  float M = -INFINITY;
-  for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[(((size_t)i + u) * MG + h) * 2]);
-  float L = 0.0f;
-  for (int i = i0; i <= i1; ++i) {
-    const size_t sl = ((size_t)i + u) * MG + h;
-    L += a.part_ml[sl * 2 + 1] * exp2_fast(a.part_ml[sl * 2] - M);
+  if (ks == 1) return;  // written directly by the decode kernel
+  const float* ml = a.part_ml + ((size_t)K0 * MG + h) * 2;
+  const float* acc = a.part_acc + ((size_t)K0 * MG + h) * MD;
+  const size_t ml_stride = (size_t)MG * 2, acc_stride = (size_t)MG * MD;
+  const int d0 = tid, d1 = tid + kMergeThreads;  // MD == 2 * kMergeThreads
+  float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int s0 = 0; s0 < ks; s0 += kMergeBatch) {
+    float mb[kMergeBatch], lb[kMergeBatch], a0[kMergeBatch], a1[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int s = min(s0 + i, ks - 1);
+      mb[i] = ml[s * ml_stride];
+      lb[i] = ml[s * ml_stride + 1];
+      a0[i] = acc[s * acc_stride + d0];
+      a1[i] = acc[s * acc_stride + d1];
+    }
+    float mnew = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (s0 + i < ks) mnew = fmaxf(mnew, mb[i]);
+    const float f = M == -INFINITY ? 0.0f : exp2_fast(M - mnew);
+    L *= f;
+    o0 *= f;
+    o1 *= f;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i >= ks) break;
+      const float w = exp2_fast(mb[i] - mnew);
+      L = fmaf(lb[i], w, L);
+      o0 = fmaf(a0[i], w, o0);
+      o1 = fmaf(a1[i], w, o1);
+    }
+    M = mnew;
   }
   const float inv = 1.0f / L;
-  for (int d = threadIdx.x; d < MD; d += 256) {
-    float o = 0.0f;
-    for (int i = i0; i <= i1; ++i) {
-      const size_t sl = ((size_t)i + u) * MG + h;
-      o = fmaf(exp2_fast(a.part_ml[sl * 2] - M), a.part_acc[sl * MD + d], o);
-    }
-    out[d] = o * inv;
-  }
+  out[d0] = o0 * inv;
+  out[d1] = o1 * inv;
 }
 
 }  // namespace
@@ -317,7 +368,7 @@ bool decode_mfma_supported(int D, int G, bool k_eq_v) { return D == MD && G == M
 
 size_t decode_mfma_workspace_bytes(int B, int Hkv) {
   const size_t units = (size_t)B * Hkv;
-  const size_t slots = (size_t)kMfmaBlocks + units;
+  const size_t slots = (size_t)kMfmaBlocks + units;  // >= sum of k_u, the grid size
   return slots * MG * MD * 4 + slots * MG * 2 * 4 + (units + 1) * 4;
 }
 
@@ -327,7 +378,8 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   if (R > kMfmaMaxUnits) return hipErrorInvalidValue;
   a.n_blocks = kMfmaBlocks;
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3(kMfmaBlocks), dim3(MNW * 64), 0, stream, a);
+  hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)(kMfmaBlocks + R)), dim3(MNW * 64), 0,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);

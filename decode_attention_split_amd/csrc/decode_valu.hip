@@ -32,21 +32,29 @@ constexpr float kRescaleLog2 = 8.0f;
 
 constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Waves per work-group: the default keeps the end-of-split LDS merge buffer at 32 KiB;
+// the wide variant doubles it when that still fits in 64 KiB, for launches with few
+// work-groups (one split per row) that need more waves in flight per CU.
 template <int D, int G>
+constexpr int valu_nw_base() { return clampi(8192 / (G * D), 1, 4); }
+template <int D, int G>
+constexpr bool valu_nw_wide_ok() { return valu_nw_base<D, G>() == 4 && G * D <= 2048; }
+
+template <int D, int G, int NW_>
 struct ValuCfg {
   static constexpr int L = clampi(G * D / 64, 8, D / 8);  // lanes per key: acc <= 64..128 VGPRs
   static constexpr int DPL = D / L;                        // elements per lane per key
   static constexpr int NCH = DPL / 8;                      // 16-byte loads per lane per key
   static constexpr int GPW = 64 / L;                       // keys per wave per step
-  static constexpr int NW = clampi(8192 / (G * D), 1, 4);  // waves per work-group
+  static constexpr int NW = NW_;                           // waves per work-group
   static constexpr int NG = GPW * NW;                      // keys per work-group per step
   static_assert(NCH >= 1 && DPL % 8 == 0, "lane slice must be whole 16-byte chunks");
 };
 
-template <int D, int G, bool KV_SHARED>
-__global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
+template <int D, int G, int NW_, bool KV_SHARED>
+__global__ void __launch_bounds__(NW_ * 64)
     decode_valu_kernel(DecodeArgs a) {
-  using C = ValuCfg<D, G>;
+  using C = ValuCfg<D, G, NW_>;
   constexpr int L = C::L, DPL = C::DPL, NCH = C::NCH, GPW = C::GPW, NW = C::NW, NG = C::NG;
   constexpr int ROW16 = D / 8;  // 16-byte chunks per cache row
 
@@ -67,6 +75,8 @@ __global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
   const int b = bid / a.Hkv;
   const int h0 = g * G;
 
+  const int new_slot = appended_slot(a, b);
+  if (split == 0) write_appended_row(a, b, g, new_slot, threadIdx.x);
   const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
   const int k_begin = split * a.split_keys;
   const int k_end = min(r.n, k_begin + a.split_keys);
@@ -96,6 +106,12 @@ __global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
   const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
   const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + row0 * ROW16;
   const uint4* vbase = reinterpret_cast<const uint4*>(KV_SHARED ? a.k : a.v) + row0 * ROW16;
+  // fused append: the appended token's rows, read in place of its slot
+  const size_t unit = (size_t)b * a.Hkv + g;
+  const uint4* knew = a.new_pos ? reinterpret_cast<const uint4*>(a.k_new) + unit * ROW16 : kbase;
+  const uint4* vnew =
+      a.new_pos ? reinterpret_cast<const uint4*>(KV_SHARED ? a.k_new : a.v_new) + unit * ROW16
+                : vbase;
 
   float acc[G][DPL];
   float m[G], l[G];
@@ -115,12 +131,13 @@ __global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
   auto load = [&](uint4(&kr)[NCH], uint4(&vr)[NCH], int step) {
     const int i = k_begin + step * NG + my_off;
     const int ic = i < k_end ? i : k_end - 1;  // past the end: re-read a valid row
-    const size_t slot = (size_t)key_slot(r, ic, a.cap);
-    const uint4* kp = kbase + slot * ROW16;
+    const int slot = key_slot(r, ic, a.cap);
+    const bool fresh = slot == new_slot;
+    const uint4* kp = fresh ? knew : kbase + (size_t)slot * ROW16;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) kr[c] = kp[c * L + j];
     if constexpr (!KV_SHARED) {
-      const uint4* vp = vbase + slot * ROW16;
+      const uint4* vp = fresh ? vnew : vbase + (size_t)slot * ROW16;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) vr[c] = vp[c * L + j];
     }
@@ -175,15 +192,21 @@ __global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
   };
 
   // Two register buffers: the next step's rows are in flight while this step computes.
+  // The loads are unconditional (past the end they re-read the last valid row), so every
+  // path through the loop has the same loads outstanding and the compiler's wait counts
+  // stay partial instead of draining the prefetch.  The loop body is straight-line (no
+  // early exit) and the odd last step runs after it, so the loop header never sees a
+  // path with a buffer's loads still unconsumed.
   uint4 ka[NCH], va[NCH], kb[NCH], vb[NCH];
   load(ka, va, 0);
-  for (int st = 0; st < n_steps; st += 2) {
-    if (st + 1 < n_steps) load(kb, vb, st + 1);
+  int st = 0;
+  for (; st + 1 < n_steps; st += 2) {
+    load(kb, vb, st + 1);
     compute(ka, va, st);
-    if (st + 1 >= n_steps) break;
-    if (st + 2 < n_steps) load(ka, va, st + 2);
+    load(ka, va, st + 2);
     compute(kb, vb, st + 1);
   }
+  if (st < n_steps) compute(ka, va, st);
 
   // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements).
 #pragma unroll
@@ -250,18 +273,26 @@ __global__ void __launch_bounds__((ValuCfg<D, G>::NW * 64))
   }
 }
 
-template <int D, int G>
-hipError_t launch_dg(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
-  using C = ValuCfg<D, G>;
+template <int D, int G, int NW>
+hipError_t launch_dgw(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
   const long long blocks = (long long)a.B * a.Hkv * a.n_split;
   if (blocks <= 0) return hipSuccess;
   if (k_eq_v)
-    hipLaunchKernelGGL((decode_valu_kernel<D, G, true>), dim3((unsigned)blocks), dim3(C::NW * 64),
+    hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, true>), dim3((unsigned)blocks), dim3(NW * 64),
                        0, stream, a);
   else
-    hipLaunchKernelGGL((decode_valu_kernel<D, G, false>), dim3((unsigned)blocks),
-                       dim3(C::NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, false>), dim3((unsigned)blocks),
+                       dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  constexpr int base = valu_nw_base<D, G>();
+  if constexpr (valu_nw_wide_ok<D, G>()) {
+    if (a.n_waves == 2 * base) return launch_dgw<D, G, 2 * base>(a, k_eq_v, stream);
+  }
+  return launch_dgw<D, G, base>(a, k_eq_v, stream);
 }
 
 template <int D>
@@ -277,13 +308,13 @@ hipError_t launch_d(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
 }
 
 template <int D>
-int keys_per_iter_d(int G) {
+int wide_waves_d(int G) {
   switch (G) {
-    case 1: return ValuCfg<D, 1>::NG;
-    case 2: return ValuCfg<D, 2>::NG;
-    case 4: return ValuCfg<D, 4>::NG;
-    case 8: return ValuCfg<D, 8>::NG;
-    case 16: return ValuCfg<D, 16>::NG;
+    case 1: return valu_nw_wide_ok<D, 1>() ? 2 * valu_nw_base<D, 1>() : 0;
+    case 2: return valu_nw_wide_ok<D, 2>() ? 2 * valu_nw_base<D, 2>() : 0;
+    case 4: return valu_nw_wide_ok<D, 4>() ? 2 * valu_nw_base<D, 4>() : 0;
+    case 8: return valu_nw_wide_ok<D, 8>() ? 2 * valu_nw_base<D, 8>() : 0;
+    case 16: return valu_nw_wide_ok<D, 16>() ? 2 * valu_nw_base<D, 16>() : 0;
     default: return 0;
   }
 }
@@ -294,8 +325,8 @@ bool decode_valu_supported(int D, int G) {
   return (D == 256 || D == 512) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
-int decode_valu_keys_per_iter(int D, int G) {
-  return D == 256 ? keys_per_iter_d<256>(G) : D == 512 ? keys_per_iter_d<512>(G) : 0;
+int decode_valu_wide_waves(int D, int G) {
+  return D == 256 ? wide_waves_d<256>(G) : D == 512 ? wide_waves_d<512>(G) : 0;
 }
 
 hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {

@@ -28,17 +28,55 @@ struct DecodeArgs {
   int max_keys;           // rows longer than this keep their newest keys
   int* plan;              // matrix-core path: per-unit key prefix sums [B * Hkv + 1]
   int n_blocks;           // matrix-core path: work-groups of the decode launch
+  int n_waves;            // vector path: waves per work-group (0: the default)
+  // Fused cache append (gemma_attn_decode_append); new_pos == nullptr: none.
+  const uint16_t* k_new;  // [B, Hkv, D]
+  const uint16_t* v_new;  // [B, Hkv, D], or nullptr for K = V
+  const int32_t* new_pos; // [B] absolute position of the appended token
+  uint16_t* k_dst;        // == k, writable
+  uint16_t* v_dst;        // == v, writable (nullptr for K = V)
 };
 
+// Fused append: the physical slot the appended token of batch row b goes to, or -1 when
+// nothing is appended (no fused append, or a position out of range, which the plain
+// append skips too).
+__device__ __forceinline__ int appended_slot(const DecodeArgs& a, int b) {
+  if (!a.new_pos) return -1;
+  const int p = a.new_pos[b];
+  if (p < 0 || (a.kind == GA_CACHE_LINEAR && p >= a.cap)) return -1;
+  return a.kind == GA_CACHE_RING ? p % a.cap : p;
+}
+
+// Fused append: copy the new K (and V) row of unit (b, g) into its slot, bit for bit.
+// Called by exactly one work-group per unit; threads tid < D / 8 each move 16 bytes.
+// No work-group of the same launch reads that slot from the cache: every reader of a key
+// whose slot equals the appended slot takes the row from k_new / v_new instead, which is
+// what the cache holds after an append, so the launch equals append-then-decode.
+__device__ __forceinline__ void write_appended_row(const DecodeArgs& a, int b, int g, int slot,
+                                                   int tid) {
+  const int chunks = a.D / 8;
+  if (slot < 0 || tid >= chunks) return;
+  const size_t unit = (size_t)b * a.Hkv + g;
+  const size_t dst = (unit * a.cap + slot) * chunks + tid;
+  reinterpret_cast<uint4*>(a.k_dst)[dst] = reinterpret_cast<const uint4*>(a.k_new)[unit * chunks + tid];
+  if (a.v_dst)
+    reinterpret_cast<uint4*>(a.v_dst)[dst] =
+        reinterpret_cast<const uint4*>(a.v_new)[unit * chunks + tid];
+}
+
 // Matrix-core path limits: units (batch rows x KV heads) per call, and the fixed grid
-// (one work-group of 4 waves per CU of an MI355X).
+// (work-groups of 4 waves, kMfmaBlocksPerCU per CU of an MI355X).
 constexpr int kMfmaMaxUnits = 1024;
-constexpr int kMfmaBlocks = 256;
+#ifndef GA_MFMA_BLOCKS_PER_CU
+#define GA_MFMA_BLOCKS_PER_CU 2
+#endif
+constexpr int kMfmaBlocksPerCU = GA_MFMA_BLOCKS_PER_CU;
+constexpr int kMfmaBlocks = 256 * kMfmaBlocksPerCU;
 
 // Split kernels.  Each launch covers B * Hkv * S work-groups; with S == 1 the split
 // kernel writes `out` directly, otherwise it writes partials for merge_launch.
 hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream);
-int decode_valu_keys_per_iter(int D, int G);   // split_keys must be a multiple of this
+int decode_valu_wide_waves(int D, int G);   // waves of the wide variant, 0 if none
 bool decode_valu_supported(int D, int G);
 
 // Matrix-core path (head_dim 512, G = 16, K = V): decode plus its unit merge.

@@ -17,42 +17,54 @@ constexpr int kMergeMaxSplitsLds = 1024;
 
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   __shared__ float s_w[kMergeMaxSplitsLds];
-  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float s_red[2][kMergeThreads / 64];
   const size_t bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.n_split, D = a.D;
   const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
   const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S
   float* out = a.out + bh * D;
   if (ns == 0) {
-    for (int d = threadIdx.x; d < D; d += kMergeThreads) out[d] = 0.0f;
+    for (int d = tid; d < D; d += kMergeThreads) out[d] = 0.0f;
     return;
   }
   const float* ml = a.part_ml + bh * S * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  float mloc = -INFINITY;
+  for (int s = tid; s < ns; s += kMergeThreads) mloc = fmaxf(mloc, ml[2 * s]);
+  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+  if (lane == 0) s_red[0][wave] = mloc;
+  __syncthreads();
+  float M = s_red[0][0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[0][w]);
   // split weights 2^(m_s - M) into LDS, and L = sum_s l_s 2^(m_s - M)
   float lsum = 0.0f;
-  for (int s = threadIdx.x; s < ns; s += kMergeThreads) {
+  for (int s = tid; s < ns; s += kMergeThreads) {
     const float w = exp2_fast(ml[2 * s] - M);
     if (s < kMergeMaxSplitsLds) s_w[s] = w;
     lsum += ml[2 * s + 1] * w;
   }
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = lsum;
+  if (lane == 0) s_red[1][wave] = lsum;
   __syncthreads();
   float Lsum = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) Lsum += s_red[w];
+  for (int w = 0; w < kMergeThreads / 64; ++w) Lsum += s_red[1][w];
   const float inv = 1.0f / Lsum;
   const float* acc = a.part_acc + bh * S * D;
-  for (int d = threadIdx.x; d < D; d += kMergeThreads) {
-    float o = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = s < kMergeMaxSplitsLds ? s_w[s] : exp2_fast(ml[2 * s] - M);
-      o = fmaf(w, acc[(size_t)s * D + d], o);
+  auto weight = [&](int s) { return s < kMergeMaxSplitsLds ? s_w[s] : exp2_fast(ml[2 * s] - M); };
+  for (int d = tid; d < D; d += kMergeThreads) {
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {  // four independent loads in flight
+      o0 = fmaf(weight(s + 0), acc[(size_t)(s + 0) * D + d], o0);
+      o1 = fmaf(weight(s + 1), acc[(size_t)(s + 1) * D + d], o1);
+      o2 = fmaf(weight(s + 2), acc[(size_t)(s + 2) * D + d], o2);
+      o3 = fmaf(weight(s + 3), acc[(size_t)(s + 3) * D + d], o3);
     }
-    out[d] = o * inv;
+    for (; s < ns; ++s) o0 = fmaf(weight(s), acc[(size_t)s * D + d], o0);
+    out[d] = ((o0 + o1) + (o2 + o3)) * inv;
   }
 }
 

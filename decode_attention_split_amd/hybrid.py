@@ -70,9 +70,24 @@ class HybridKVCache:
                           max_ctx=self.shape(g).max_ctx, split_keys=split_keys, impl=impl,
                           stream=stream)
 
-    def step(self, q_list, k_new_list, v_new_list, pos, ctx_lens, q_pos, outs, stream=None):
+    def decode_append(self, layer: int, q, k_new, v_new, pos, ctx_lens, q_pos, out=None,
+                      split_keys=0, impl=api.IMPL_AUTO, stream=None):
+        """Append the new token to this layer's cache and attend, in one launch."""
+        g = self.layers[layer]
+        return api.decode_append(q, self.k[layer], self.v[layer], k_new,
+                                 None if g.k_eq_v else v_new, pos, ctx_lens, q_pos, g.window,
+                                 g.softcap, g.q_scale, g.kind, out=out, workspace=self.workspace,
+                                 max_ctx=self.shape(g).max_ctx, split_keys=split_keys, impl=impl,
+                                 stream=stream)
+
+    def step(self, q_list, k_new_list, v_new_list, pos, ctx_lens, q_pos, outs, stream=None,
+             fused=True):
         """One decode step through every layer: append the new token, then attend."""
         for li in range(len(self.layers)):
-            self.append(li, k_new_list[li], v_new_list[li], pos, stream=stream)
-            self.decode(li, q_list[li], ctx_lens, q_pos, out=outs[li], stream=stream)
+            if fused:
+                self.decode_append(li, q_list[li], k_new_list[li], v_new_list[li], pos, ctx_lens,
+                                   q_pos, out=outs[li], stream=stream)
+            else:
+                self.append(li, k_new_list[li], v_new_list[li], pos, stream=stream)
+                self.decode(li, q_list[li], ctx_lens, q_pos, out=outs[li], stream=stream)
         return outs

@@ -140,6 +140,22 @@ int32_t gemma_attn_decode_ex(const ga_shape* shape, const ga_bf16* q, const ga_b
                              size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
 
 /*
+ * Cache append fused with decode, in one launch: exactly gemma_kv_append(shape, k_cache,
+ * v_cache, k_new, v_new, pos) followed by gemma_attn_decode_ex(...) on the same stream,
+ * bit for bit (cache contents and output).  One work-group per (b, g) writes the new row;
+ * every key whose slot is the appended slot is read from k_new / v_new instead of the
+ * cache, so no work-group reads a slot while it is being written.  Arguments as in the
+ * two calls; k_new [B, Hkv, D] and pos [B] device pointers must be non-NULL, and v_new is
+ * NULL exactly when v_cache is (K = V).  Saves the separate append launch per layer.
+ */
+int32_t gemma_attn_decode_append(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache,
+                                 ga_bf16* v_cache, const ga_bf16* k_new, const ga_bf16* v_new,
+                                 const int32_t* pos, const int32_t* ctx_lens,
+                                 const int32_t* q_pos, int32_t window, float softcap, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 const ga_decode_opts* opts, void* stream);
+
+/*
  * Cache append of one token per sequence: cache[b, g, slot(pos_b), :] <- new[b, g, :]
  * for K, and for V unless K = V.  Ring: slot = pos mod W; linear: slot = pos.
  *   k_new, v_new device bf16 [B, Hkv, D]; v_cache and v_new are both NULL for K = V.

@@ -83,8 +83,8 @@ def no_gpu():
     (dict(s=shape(), qpos=0), -1),
     (dict(s=shape(), out=0), -1),
     (dict(s=shape(), q=FAKE + 8), -1),                     # not 16-byte aligned
-    (dict(s=shape(B=64), ws=0, ws_bytes=0), -7),
-    (dict(s=shape(B=64), ws_bytes=16), -7),
+    (dict(s=shape(B=2), ws=0, ws_bytes=0), -7),        # 16 units x 8 splits need partials
+    (dict(s=shape(B=2), ws_bytes=16), -7),
     (dict(s=shape(), opts=api.make_opts(split_keys=100)), -12),
     (dict(s=shape(), opts=api.make_opts(split_keys=32)), -12),
     (dict(s=shape(), opts=api.make_opts(impl=7)), -12),
@@ -126,10 +126,10 @@ def test_workspace_bytes_closed_form():
     assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == \
         16 * 16 * 64 * 514 * 4
     # K = V global geometry: AUTO may pick the matrix-core path, whose workspace is
-    # (256 work-groups + B * Hkv units) partial slots of 16 heads x (512 + 2) floats, plus
+    # (512 work-groups + B * Hkv units) partial slots of 16 heads x (512 + 2) floats, plus
     # B * Hkv + 1 ints of prefix sums; the query covers the larger of the two paths
     s = shape(B=16, Hq=16, Hkv=1, D=512, cap=32768, kind=api.LINEAR)
-    mfma = (256 + 16) * 16 * 514 * 4 + 17 * 4
+    mfma = (512 + 16) * 16 * 514 * 4 + 17 * 4
     o = api.make_opts(impl=api.IMPL_MFMA)
     assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == mfma
     auto = lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, None)

@@ -307,3 +307,62 @@ def test_mfma_single_key_rows_are_exact():
     for b in range(3):
         for h in range(16):
             assert torch.equal(out[b, h], k[b, 0, 0])
+
+
+# ------------------------------------------------------------------ fused append + decode
+
+@pytest.mark.parametrize("case", ["sliding_ring", "sliding_split", "global_mfma", "global_valu",
+                                  "ring_overwrites_valid", "positions_out_of_range"])
+def test_decode_append_equals_append_then_decode(case):
+    """One launch of gemma_attn_decode_append leaves the same cache bytes and the same
+    output bits as gemma_kv_append followed by gemma_attn_decode."""
+    rng = np.random.default_rng(hash(case) % 1000)
+    impl, split, window = api.IMPL_AUTO, 0, 0
+    if case in ("sliding_ring", "sliding_split", "ring_overwrites_valid"):
+        B, Hq, Hkv, D, cap, kind, k_eq_v, window = 5, 16, 8, 256, 64, api.RING, False, 64
+        ctx = np.array([1, 63, 64, 65, 300], np.int32)
+        pos = ctx - 1
+        if case == "sliding_split":
+            split = 64
+            cap, window = 256, 200
+            ctx = np.array([1, 199, 200, 201, 900], np.int32)
+            pos = ctx - 1
+        if case == "ring_overwrites_valid":
+            # appending position ctx (one past the context) overwrites the slot of ctx - W,
+            # which is still valid: it must then read back as the new row
+            pos = ctx.copy()
+    elif case == "positions_out_of_range":
+        B, Hq, Hkv, D, cap, kind, k_eq_v = 4, 16, 1, 512, 300, api.LINEAR, True
+        ctx = np.array([10, 299, 300, 5], np.int32)
+        pos = np.array([-1, 299, 300, 4], np.int32)  # -1 and C are skipped
+    else:
+        B, Hq, Hkv, D, cap, kind, k_eq_v = 6, 16, 1, 512, 3000, api.LINEAR, True
+        ctx = np.array([1, 17, 1500, 2999, 3000, 700], np.int32)
+        pos = ctx - 1
+        impl = api.IMPL_MFMA if case == "global_mfma" else api.IMPL_VALU
+    inp = gen_layer(94, B, Hq, Hkv, D, cap, k_eq_v, 1, 1, ctx=ctx).to_device()
+    gen = synth.generator(95)
+    k_new = synth.normal_bf16(gen, (B, Hkv, D)).cuda()
+    v_new = None if k_eq_v else synth.normal_bf16(gen, (B, Hkv, D)).cuda()
+    pos_t = torch.from_numpy(pos).cuda()
+    max_ctx = int(ctx.max()) if kind == api.RING else cap
+    scale = default_scale(D)
+    # reference: append, then decode
+    k1, v1 = inp.k.clone(), None if k_eq_v else inp.v.clone()
+    api.kv_append(k1, v1, k_new, v_new, pos_t, kind)
+    ref = api.decode(inp.q, k1, v1, inp.ctx_t, inp.qpos_t, window, 20.0, scale, kind,
+                     max_ctx=max_ctx, split_keys=split, impl=impl)
+    # fused
+    k2, v2 = inp.k.clone(), None if k_eq_v else inp.v.clone()
+    got = api.decode_append(inp.q, k2, v2, k_new, v_new, pos_t, inp.ctx_t, inp.qpos_t, window,
+                            20.0, scale, kind, max_ctx=max_ctx, split_keys=split, impl=impl)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), "cache differs"
+    if not k_eq_v:
+        assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), "V cache differs"
+    assert torch.isfinite(got).all()
+    assert torch.equal(got, ref), (got - ref).abs().max().item()
+    # and the result agrees with the oracle on the appended cache
+    host = LayerInputs(inp.q_bits, synth.bits(k1), None if k_eq_v else synth.bits(v1), ctx,
+                       inp.qpos)
+    assert_parity(got, oracle_out(host, window, 20.0, scale, kind), f"decode_append {case}")
