@@ -11,8 +11,9 @@ no soft-cap, query scale 1/sqrt(head_dim).  Each step appends the current token
 Prints ONE JSON line.  `value` is effective KV GB/s of the whole step: algorithmic
 bytes (valid K rows, plus V rows unless K = V, plus q, out, the int inputs, and the
 append's reads and writes) divided by the step time, with every input resident in
-HBM.  `roofline` is for the dominant kernel (the sliding-layer split-decode kernel),
-timed with HIP events around each of its launches on the stream it runs on.
+HBM.  `roofline` is for the dominant kernel (the sliding-layer fused append + decode,
+40 of the 48 launches), timed with HIP events around back-to-back launches of it on the
+stream it runs on.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -37,6 +38,13 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run a 1 GiB device-to-device copy (counter calibration)")
+    p.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                   help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
+    p.add_argument("--command", default="", help="command line recorded in summaries")
     return p.parse_args()
 
 
@@ -66,7 +74,6 @@ def layer_bytes(g, B, ctx):
 def read_traffic(kernel_tag):
     """Counter-measured HBM bytes per launch from profiles/, or None when absent or when
     the kernel sources changed since the counters were taken."""
-    import hashlib
     path = os.path.join(PROFILES, f"hbm_traffic_{kernel_tag}.txt")
     if not os.path.exists(path):
         return None
@@ -75,10 +82,8 @@ def read_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for rel in kv.get("sources", "").split():
-        h.update(open(os.path.join(ROOT, rel), "rb").read())
-    if kv.get("sources_sha256") != h.hexdigest():
+    rels = kv.get("sources", "").split()
+    if not rels or kv.get("sources_sha256") != sources_digest(rels):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -86,8 +91,81 @@ def read_traffic(kernel_tag):
         return None
 
 
+# Sources whose change invalidates counter-measured traffic of the dominant kernel.
+TRAFFIC_SOURCES = ["decode_attention_split_amd/csrc/decode_valu.hip",
+                   "decode_attention_split_amd/csrc/ga_device.h",
+                   "decode_attention_split_amd/csrc/ga_internal.h",
+                   "decode_attention_split_amd/csrc/api.hip"]
+DOMINANT = "decode_valu_kernel<256, 2"
+COPY_BYTES = 1 << 30
+
+
+def sources_digest(rels):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in rels:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_trace(path, command):
+    """Markdown summary of a rocprofv3 kernel_stats.csv (durations in microseconds)."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    print(f"# rocprofv3 kernel statistics\n\ncommand: `{command}`\n")
+    print("| kernel | calls | avg us | min us | max us | share % |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        print(f"| `{name[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.2f} |")
+
+
+def summarize_counters(fetch_csv, write_csv, command):
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and WRITE_SIZE runs (KiB
+    per dispatch), each scaled by what the counter reads for the 1 GiB calibration copy."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def calib(vals):
+        copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs if v > 1e8]
+        return COPY_BYTES / (sum(copies) / len(copies))
+
+    f_scale, w_scale = calib(fetch), calib(write)
+    dom = [k for k in fetch if DOMINANT in k]
+    f = sum(sum(fetch[k]) for k in dom) / sum(len(fetch[k]) for k in dom)
+    w = sum(sum(write[k]) for k in dom) / sum(len(write[k]) for k in dom)
+    print("# HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    print(f"command: {command}")
+    print(f"kernel: {dom[0][:100] if dom else 'n/a'}")
+    print(f"fetch_calibration (1 GiB copy bytes / counter bytes): {f_scale:.4f}")
+    print(f"write_calibration (1 GiB copy bytes / counter bytes): {w_scale:.4f}")
+    print(f"fetch_bytes_per_launch: {f * f_scale:.0f}")
+    print(f"write_bytes_per_launch: {w * w_scale:.0f}")
+    print(f"hbm_bytes_per_launch: {f * f_scale + w * w_scale:.0f}")
+    print(f"sources: {' '.join(TRAFFIC_SOURCES)}")
+    print(f"sources_sha256: {sources_digest(TRAFFIC_SOURCES)}")
+
+
 def main():
     args = parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the per-GPU workload is the whole step at its real shape)", file=sys.stderr)
@@ -131,21 +209,25 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready: {cache.bytes() / 2**30:.2f} GiB of caches in {time.time() - t0:.1f}s")
 
+    if args.calibrate_copy:
+        src = torch.ones((COPY_BYTES // 4,), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     per_layer = [layer_bytes(g, B, ctx) for g in w.layers]
     step_bytes = sum(x["decode"] + x["append"] for x in per_layer)
     sliding = [i for i, g in enumerate(w.layers) if not g.k_eq_v]
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step():
         # per layer, one launch: append the current token to the cache and attend
         for li in range(L):
-            if ev is not None and li in ev:
-                ev[li][0].record(stream)
             cache.decode_append(li, qs[li], k_new[li], v_new[li], pos_t, ctx_t, qpos_t,
                                 out=outs[li])
-            if ev is not None and li in ev:
-                ev[li][1].record(stream)
 
     graph = None
     if args.graph:
@@ -156,11 +238,11 @@ def main():
             step()
         torch.cuda.synchronize()
 
-    def run_step(ev=None):
-        if graph is not None and ev is None:
+    def run_step():
+        if graph is not None:
             graph.replay()
         else:
-            step(ev)
+            step()
 
     for _ in range(args.warmup):
         run_step()
@@ -180,20 +262,26 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"step: {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms)")
 
-    # ---- dominant kernel: each sliding-layer decode launch bracketed by events
-    kern_steps = max(1, min(args.steps, 10))
-    durs = []
+    # ---- dominant kernel: the sliding-layer fused append + decode, launched back to back
+    # for every sliding layer of the step, bracketed by one event pair on its stream (an
+    # event pair around each launch would add its own overhead to every launch).
+    kern_steps = max(1, args.steps)
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record(stream)
     for _ in range(kern_steps):
-        ev = {li: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for li in sliding}
-        step(ev)
-        torch.cuda.synchronize()
-        durs += [ev[li][0].elapsed_time(ev[li][1]) for li in sliding]
-    kern_ms = float(np.mean(durs))
+        for li in sliding:
+            cache.decode_append(li, qs[li], k_new[li], v_new[li], pos_t, ctx_t, qpos_t,
+                                out=outs[li])
+    k1.record(stream)
+    torch.cuda.synchronize()
+    n_launch = kern_steps * len(sliding)
+    kern_ms = k0.elapsed_time(k1) / n_launch
     kern_bytes = float(np.mean([per_layer[li]["decode"] + per_layer[li]["append"]
                                 for li in sliding]))
     kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"sliding decode kernel: {kern_ms * 1e3:.2f} us avg over {len(durs)} launches, "
+    log(f"sliding decode kernel: {kern_ms * 1e3:.2f} us avg over {n_launch} launches, "
         f"{kern_gbps:.1f} GB/s")
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
