@@ -237,8 +237,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
       x[i] = (k0 + 4 * lg + i < seg_hi) ? v * kLog2e : -INFINITY;
       mx = fmaxf(mx, x[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);  // over the 16 keys of the tile (four lane rows)
     if (mx > m + kRescaleLog2) {
       const float f = exp2_fast(m - mx);
       l *= f;
@@ -286,8 +285,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   if (t + 2 < nt) step(r2, t + 2);
 
   // ---- this wave's slice of the result (m and l are identical in every wave)
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = rows_sum(l);
   if (k_u == 1) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     float* o = a.out + (head0 + l16) * MD + DQ * wave + 4 * lg;

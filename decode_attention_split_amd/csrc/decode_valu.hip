@@ -22,6 +22,8 @@
 // Definition followed: "Gemma support" pull request, Summary (soft-capping, sliding
 // window, head sizes 256/512, K = V) and Performance (split decode attention); the key
 // range is ga::row_range ("Gemma 4 12B (unified multimodal)" record: exactly w entries).
+#include <type_traits>
+
 #include "ga_device.h"
 #include "ga_internal.h"
 
@@ -29,6 +31,10 @@ namespace ga {
 namespace {
 
 constexpr float kRescaleLog2 = 8.0f;
+#ifndef GA_VALU_NBUF
+#define GA_VALU_NBUF 2
+#endif
+constexpr int NBUF = GA_VALU_NBUF;  // register buffers of KV rows (prefetch depth + 1)
 
 constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -191,42 +197,50 @@ __global__ void __launch_bounds__(NW_ * 64)
     }
   };
 
-  // Two register buffers: the next step's rows are in flight while this step computes.
-  // The loads are unconditional (past the end they re-read the last valid row), so every
-  // path through the loop has the same loads outstanding and the compiler's wait counts
-  // stay partial instead of draining the prefetch.  The loop body is straight-line (no
-  // early exit) and the odd last step runs after it, so the loop header never sees a
-  // path with a buffer's loads still unconsumed.
-  uint4 ka[NCH], va[NCH], kb[NCH], vb[NCH];
-  load(ka, va, 0);
-  int st = 0;
-  for (; st + 1 < n_steps; st += 2) {
-    load(kb, vb, st + 1);
-    compute(ka, va, st);
-    load(ka, va, st + 2);
-    compute(kb, vb, st + 1);
-  }
-  if (st < n_steps) compute(ka, va, st);
-
-  // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements).
+  // NBUF register buffers: the next NBUF - 1 steps' rows are in flight while a step
+  // computes.  The loads are unconditional (past the end they re-read the last valid
+  // row), so every path through the loop has the same loads outstanding and the
+  // compiler's wait counts stay partial instead of draining the prefetch.  The loop body
+  // is straight-line (no early exit) and the last steps run after it, so the loop
+  // header never sees a path with a buffer's loads still unconsumed.
+  uint4 kbuf[NBUF][NCH], vbuf[NBUF][NCH];
 #pragma unroll
-  for (int off = L; off < 64; off <<= 1) {
+  for (int i = 0; i < NBUF - 1; ++i) load(kbuf[i], vbuf[i], i);
+  int st = 0;
+  for (; st + NBUF - 1 < n_steps; st += NBUF) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      load(kbuf[(i + NBUF - 1) % NBUF], vbuf[(i + NBUF - 1) % NBUF], st + i + NBUF - 1);
+      compute(kbuf[i], vbuf[i], st + i);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (st + i < n_steps) compute(kbuf[i], vbuf[i], st + i);
+
+  // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements),
+  // exchanging values with DPP / permlane swaps on the VALU.
+  auto merge_groups = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float mo = __shfl_xor(m[hh], off, 64);
-      const float lo = __shfl_xor(l[hh], off, 64);
+      const float mo = xor_lane<OFF>(m[hh], lane);
+      const float lo = xor_lane<OFF>(l[hh], lane);
       const float mn = fmaxf(m[hh], mo);
       const float fs = m[hh] == -INFINITY ? 0.0f : exp2_fast(m[hh] - mn);
       const float fo = mo == -INFINITY ? 0.0f : exp2_fast(mo - mn);
       l[hh] = l[hh] * fs + lo * fo;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        const float ao = __shfl_xor(acc[hh][e], off, 64);
+        const float ao = xor_lane<OFF>(acc[hh][e], lane);
         acc[hh][e] = acc[hh][e] * fs + ao * fo;
       }
       m[hh] = mn;
     }
-  }
+  };
+  if constexpr (L <= 8) merge_groups(std::integral_constant<int, 8>());
+  if constexpr (L <= 16) merge_groups(std::integral_constant<int, 16>());
+  if constexpr (L <= 32) merge_groups(std::integral_constant<int, 32>());
 
   // Merge the waves through LDS, then write the output or this split's partial.
   if (lane < L) {

@@ -92,8 +92,37 @@ constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i inside each 8
 constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i inside each 16
+constexpr int kDppRowRor8 = 0x128;     // rotate a 16-lane row by 8: lane ^ 8
 
-// Sum over aligned groups of L lanes; every lane of the group gets the total.
+// The two values of the lane pair {l, l ^ 16} (or {l, l ^ 32}), lower lane first, in both
+// lanes of the pair: gfx950's v_permlane16_swap / v_permlane32_swap, all on the VALU.
+__device__ __forceinline__ void lane_pair16(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false,
+                                                  false);
+  lo = __int_as_float(r[0]);
+  hi = __int_as_float(r[1]);
+}
+__device__ __forceinline__ void lane_pair32(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false,
+                                                  false);
+  lo = __int_as_float(r[0]);
+  hi = __int_as_float(r[1]);
+}
+
+// Value held by lane (lane ^ OFF), OFF in {8, 16, 32}, without going through LDS.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane offset");
+  if constexpr (OFF == 8) {
+    return dpp<kDppRowRor8>(v);
+  } else {
+    float lo, hi;
+    if constexpr (OFF == 16) lane_pair16(v, lo, hi); else lane_pair32(v, lo, hi);
+    return (lane & OFF) ? lo : hi;
+  }
+}
+
+// Sum over aligned groups of L lanes; every lane of the group gets the same total.
 template <int L>
 __device__ __forceinline__ float group_sum(float x) {
   static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group size");
@@ -101,9 +130,33 @@ __device__ __forceinline__ float group_sum(float x) {
   x += dpp<kDppQuadSwap2>(x);
   x += dpp<kDppHalfMirror>(x);
   if constexpr (L >= 16) x += dpp<kDppMirror>(x);
-  if constexpr (L >= 32) x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-  if constexpr (L >= 64) x += __shfl_xor(x, 32, 64);
+  float lo, hi;
+  if constexpr (L >= 32) {
+    lane_pair16(x, lo, hi);
+    x = lo + hi;
+  }
+  if constexpr (L >= 64) {
+    lane_pair32(x, lo, hi);
+    x = lo + hi;
+  }
   return x;
+}
+
+// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48); every
+// lane gets the same result.
+__device__ __forceinline__ float rows_max(float x) {
+  float lo, hi;
+  lane_pair16(x, lo, hi);
+  x = fmaxf(lo, hi);
+  lane_pair32(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float lo, hi;
+  lane_pair16(x, lo, hi);
+  x = lo + hi;
+  lane_pair32(x, lo, hi);
+  return lo + hi;
 }
 
 }  // namespace ga
