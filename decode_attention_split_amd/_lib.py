@@ -19,7 +19,7 @@ class ga_shape(ctypes.Structure):
 
 class ga_decode_opts(ctypes.Structure):
     _fields_ = [("split_keys", ctypes.c_int32), ("impl", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("deterministic", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 # Every symbol include/gemma_attn.h declares.

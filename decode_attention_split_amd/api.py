@@ -45,10 +45,11 @@ def make_shape(batch, num_q_heads, num_kv_heads, head_dim, capacity, kind, max_c
                          int(capacity), int(kind), int(max_ctx))
 
 
-def make_opts(split_keys=0, impl=IMPL_AUTO):
+def make_opts(split_keys=0, impl=IMPL_AUTO, deterministic=False):
     o = _lib.ga_decode_opts()
     o.split_keys = int(split_keys)
     o.impl = int(impl)
+    o.deterministic = int(bool(deterministic))
     return o
 
 
@@ -96,7 +97,7 @@ def shape_of(q, k_cache, kind, max_ctx=0):
 
 
 def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, workspace, max_ctx,
-                   split_keys, impl):
+                   split_keys, impl, deterministic):
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     if v_cache is not None:
@@ -115,7 +116,7 @@ def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, work
         _need(out, "out", torch.float32, 3)
         if tuple(out.shape) != (shape.batch, shape.num_q_heads, shape.head_dim):
             raise ValueError("out must be [B, Hq, D]")
-    opts = make_opts(split_keys, impl)
+    opts = make_opts(split_keys, impl, deterministic)
     lib = _lib.load()
     need = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window), ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
@@ -129,7 +130,7 @@ def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, work
 
 def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
            kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
-           impl: int = IMPL_AUTO, stream=None):
+           impl: int = IMPL_AUTO, deterministic: bool = False, stream=None):
     """Single-token decode attention; returns out [B, Hq, D] float32 (see gemma_attn.h).
 
     v_cache None means K = V (k_cache serves as keys and values).  workspace, when
@@ -137,7 +138,8 @@ def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, sc
     one is allocated here with torch (the library itself never allocates).
     """
     shape, out, opts, workspace = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window,
-                                                 kind, out, workspace, max_ctx, split_keys, impl)
+                                                 kind, out, workspace, max_ctx, split_keys, impl,
+                                                 deterministic)
     ws_bytes = 0 if workspace is None else workspace.numel()
     rc = _lib.load().gemma_attn_decode_ex(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens), _ptr(q_pos),
@@ -149,10 +151,12 @@ def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, sc
 
 def decode_append(q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, window: int,
                   softcap: float, scale: float, kind: int, out=None, workspace=None,
-                  max_ctx: int = 0, split_keys: int = 0, impl: int = IMPL_AUTO, stream=None):
+                  max_ctx: int = 0, split_keys: int = 0, impl: int = IMPL_AUTO,
+                  deterministic: bool = False, stream=None):
     """kv_append(k_cache, v_cache, k_new, v_new, pos) then decode(...), in one launch."""
     shape, out, opts, workspace = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window,
-                                                 kind, out, workspace, max_ctx, split_keys, impl)
+                                                 kind, out, workspace, max_ctx, split_keys, impl,
+                                                 deterministic)
     _need(k_new, "k_new", torch.bfloat16, 3)
     if (v_cache is None) != (v_new is None):
         _check(-9, "gemma_attn_decode_append")

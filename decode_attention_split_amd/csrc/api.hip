@@ -134,8 +134,9 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
                   Plan* p) {
   int impl = GA_IMPL_AUTO, ts = 0;
   if (o) {
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
       if (o->reserved[i] != 0) return GA_ERR_OPTS;
+    if (o->deterministic != 0 && o->deterministic != 1) return GA_ERR_OPTS;
     impl = o->impl;
     ts = o->split_keys;
     if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
@@ -268,6 +269,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   a.n_split = p.n_split;
   a.max_keys = p.max_keys;
   a.n_waves = p.n_waves;
+  a.deterministic = opts ? opts->deterministic : 0;
   a.k_new = k_new;
   a.v_new = k_eq_v ? nullptr : v_new;
   a.new_pos = k_new ? new_pos : nullptr;

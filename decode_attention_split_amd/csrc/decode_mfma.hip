@@ -152,13 +152,18 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   __syncthreads();
   if (blockIdx.x == 0)
     for (int u = tid; u <= R; u += MNW * 64) a.plan[u] = s_k[u];
-  // fused append: work-group u (< R <= grid) writes unit u's new row
-  if (blockIdx.x < R) {
-    const int ub = blockIdx.x / a.Hkv;
-    write_appended_row(a, ub, blockIdx.x % a.Hkv, appended_slot(a, ub), tid);
+  // fused append: work-group u (< R <= grid) moves unit u's new row (stored at the end)
+  AppendRow app;
+  {
+    const int u = blockIdx.x < R ? blockIdx.x : 0;
+    const int ub = u / a.Hkv;
+    app.load(a, ub, u % a.Hkv, appended_slot(a, ub), tid, blockIdx.x < R);
   }
   const int g_id = blockIdx.x;
-  if (g_id >= s_k[R]) return;
+  if (g_id >= s_k[R]) {
+    app.store(a);
+    return;
+  }
   // unit of this work-group: the u with s_k[u] <= g_id < s_k[u + 1]
   int u, hi_u = R - 1;
   {
@@ -284,6 +289,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   if (t + 1 < nt) step(r1, t + 1);
   if (t + 2 < nt) step(r2, t + 2);
 
+  app.store(a);
   // ---- this wave's slice of the result (m and l are identical in every wave)
   l = rows_sum(l);
   if (k_u == 1) {
@@ -376,8 +382,12 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   if (R > kMfmaMaxUnits) return hipErrorInvalidValue;
   a.n_blocks = kMfmaBlocks;
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)(kMfmaBlocks + R)), dim3(MNW * 64), 0,
-                     stream, a);
+  // Work-groups with work: with R <= 3/4 NB at most R units are non-empty, the kernel
+  // takes C = T / (NB - non-empty) and the sum of k_u stays <= NB; past that it takes
+  // C = T / NB and the sum stays <= NB + R.  Work-groups u < R also carry unit u's append.
+  const unsigned grid =
+      (unsigned)(R <= kMfmaBlocks - kMfmaBlocks / 4 ? kMfmaBlocks : kMfmaBlocks + R);
+  hipLaunchKernelGGL(decode_mfma_kernel, dim3(grid), dim3(MNW * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);

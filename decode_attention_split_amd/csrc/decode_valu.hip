@@ -31,10 +31,6 @@ namespace ga {
 namespace {
 
 constexpr float kRescaleLog2 = 8.0f;
-#ifndef GA_VALU_NBUF
-#define GA_VALU_NBUF 2
-#endif
-constexpr int NBUF = GA_VALU_NBUF;  // register buffers of KV rows (prefetch depth + 1)
 
 constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -81,8 +77,11 @@ __global__ void __launch_bounds__(NW_ * 64)
   const int b = bid / a.Hkv;
   const int h0 = g * G;
 
+  // Fused append: split 0 of each unit moves the new row; its loads are issued here and
+  // the stores happen after the key loop, so nothing waits on them.
   const int new_slot = appended_slot(a, b);
-  if (split == 0) write_appended_row(a, b, g, new_slot, threadIdx.x);
+  AppendRow app;
+  app.load(a, b, g, new_slot, threadIdx.x, split == 0);
   const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
   const int k_begin = split * a.split_keys;
   const int k_end = min(r.n, k_begin + a.split_keys);
@@ -91,8 +90,12 @@ __global__ void __launch_bounds__(NW_ * 64)
       for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
         a.out[((size_t)b * a.Hq + h0) * D + idx] = 0.0f;
     }
+    app.store(a);
     return;  // with S > 1 the merge never reads splits past the row's end
   }
+  __shared__ int s_next;  // next wave-step to hand out
+  if (threadIdx.x == 0) s_next = 0;
+  __syncthreads();
 
   // Query heads of this KV head, as packed bf16 pairs, in this lane's element order.
   uint32_t qr[G][DPL / 2];
@@ -129,13 +132,23 @@ __global__ void __launch_bounds__(NW_ * 64)
     for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
   }
 
-  const int my_off = wave * GPW + grp;
-  const int n_steps = (k_end - k_begin + NG - 1) / NG;
+  // Wave-step s covers keys k_begin + s * GPW + grp (one per lane group).  Steps are
+  // handed out to waves as they ask for them (an LDS counter), so waves that the SIMD
+  // arbiter serves less still finish together with the others; in deterministic mode the
+  // order is static (wave w takes w, w + NW, ...), which fixes the summation order.
+  const int n_wsteps = (k_end - k_begin + GPW - 1) / GPW;
   const float scale = a.scale;
   const float softcap = a.softcap, inv_softcap = a.inv_softcap;
+  int taken = 0;
+  auto grab = [&]() -> int {
+    if (a.deterministic) return wave + NW * (taken++);
+    int s = 0;
+    if (lane == 0) s = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(s);
+  };
 
   auto load = [&](uint4(&kr)[NCH], uint4(&vr)[NCH], int step) {
-    const int i = k_begin + step * NG + my_off;
+    const int i = k_begin + step * GPW + grp;
     const int ic = i < k_end ? i : k_end - 1;  // past the end: re-read a valid row
     const int slot = key_slot(r, ic, a.cap);
     const bool fresh = slot == new_slot;
@@ -150,7 +163,7 @@ __global__ void __launch_bounds__(NW_ * 64)
   };
 
   auto compute = [&](const uint4(&kr)[NCH], const uint4(&vr)[NCH], int step) {
-    const int i = k_begin + step * NG + my_off;
+    const int i = k_begin + step * GPW + grp;
     const bool valid = i < k_end;
     float s[G];
 #pragma unroll
@@ -197,26 +210,26 @@ __global__ void __launch_bounds__(NW_ * 64)
     }
   };
 
-  // NBUF register buffers: the next NBUF - 1 steps' rows are in flight while a step
-  // computes.  The loads are unconditional (past the end they re-read the last valid
-  // row), so every path through the loop has the same loads outstanding and the
-  // compiler's wait counts stay partial instead of draining the prefetch.  The loop body
-  // is straight-line (no early exit) and the last steps run after it, so the loop
-  // header never sees a path with a buffer's loads still unconsumed.
-  uint4 kbuf[NBUF][NCH], vbuf[NBUF][NCH];
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) load(kbuf[i], vbuf[i], i);
-  int st = 0;
-  for (; st + NBUF - 1 < n_steps; st += NBUF) {
-#pragma unroll
-    for (int i = 0; i < NBUF; ++i) {
-      load(kbuf[(i + NBUF - 1) % NBUF], vbuf[(i + NBUF - 1) % NBUF], st + i + NBUF - 1);
-      compute(kbuf[i], vbuf[i], st + i);
-    }
+  // Two register buffers: the next step's rows are in flight while a step computes.  The
+  // loads are unconditional (past the end they re-read the last valid row) and the loop
+  // body is straight-line with its test at the bottom, so every path into the loop
+  // header carries the same outstanding loads (buffer a only) and the compiler keeps
+  // partial vmcnt waits instead of draining the prefetch.  Grabs are increasing per wave,
+  // so sa < sb < n_wsteps inside the loop.
+  uint4 ka[NCH], va[NCH], kb[NCH], vb[NCH];
+  int sa = grab();
+  load(ka, va, sa);
+  int sb = grab();
+  while (sb < n_wsteps) {
+    load(kb, vb, sb);
+    compute(ka, va, sa);
+    sa = grab();
+    load(ka, va, sa);
+    compute(kb, vb, sb);
+    sb = grab();
   }
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (st + i < n_steps) compute(kbuf[i], vbuf[i], st + i);
+  if (sa < n_wsteps) compute(ka, va, sa);
+  app.store(a);
 
   // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements),
   // exchanging values with DPP / permlane swaps on the VALU.

@@ -35,6 +35,7 @@ struct DecodeArgs {
   const int32_t* new_pos; // [B] absolute position of the appended token
   uint16_t* k_dst;        // == k, writable
   uint16_t* v_dst;        // == v, writable (nullptr for K = V)
+  int deterministic;      // vector path: fixed step order (bit-reproducible sums)
 };
 
 // Fused append: the physical slot the appended token of batch row b goes to, or -1 when
@@ -47,22 +48,39 @@ __device__ __forceinline__ int appended_slot(const DecodeArgs& a, int b) {
   return a.kind == GA_CACHE_RING ? p % a.cap : p;
 }
 
-// Fused append: copy the new K (and V) row of unit (b, g) into its slot, bit for bit.
-// Called by exactly one work-group per unit; threads tid < D / 8 each move 16 bytes.
-// No work-group of the same launch reads that slot from the cache: every reader of a key
-// whose slot equals the appended slot takes the row from k_new / v_new instead, which is
-// what the cache holds after an append, so the launch equals append-then-decode.
-__device__ __forceinline__ void write_appended_row(const DecodeArgs& a, int b, int g, int slot,
-                                                   int tid) {
-  const int chunks = a.D / 8;
-  if (slot < 0 || tid >= chunks) return;
-  const size_t unit = (size_t)b * a.Hkv + g;
-  const size_t dst = (unit * a.cap + slot) * chunks + tid;
-  reinterpret_cast<uint4*>(a.k_dst)[dst] = reinterpret_cast<const uint4*>(a.k_new)[unit * chunks + tid];
-  if (a.v_dst)
-    reinterpret_cast<uint4*>(a.v_dst)[dst] =
-        reinterpret_cast<const uint4*>(a.v_new)[unit * chunks + tid];
-}
+// Fused append: moves the new K (and V) row of unit (b, g) into its slot, bit for bit.
+// Used by exactly one work-group per unit; threads tid < D / 8 each move 16 bytes.  load()
+// issues the reads at the start of the work-group, store() writes at its end, so the
+// work-group never waits on them.  No work-group of the same launch reads that slot from
+// the cache: every reader of a key whose slot equals the appended slot takes the row from
+// k_new / v_new instead, which is what the cache holds after an append, so the launch
+// equals append-then-decode.
+struct AppendRow {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 k, v;
+  size_t dst;
+  bool on;
+  // The loads are unconditional (from the first 16 bytes of q when this thread moves
+  // nothing), so no branch joins around them and nothing waits for them before store().
+  __device__ __forceinline__ void load(const DecodeArgs& a, int b, int g, int slot, int tid,
+                                       bool mine) {
+    const int chunks = a.D / 8;
+    on = mine && slot >= 0 && tid < chunks;
+    const size_t unit = (size_t)b * a.Hkv + g;
+    dst = (unit * a.cap + (on ? slot : 0)) * chunks + tid;
+    const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
+    const u32x4* ks = on ? reinterpret_cast<const u32x4*>(a.k_new) + unit * chunks + tid : q;
+    const u32x4* vs = on && a.v_dst ? reinterpret_cast<const u32x4*>(a.v_new) + unit * chunks + tid
+                                    : ks;
+    k = *ks;
+    v = *vs;
+  }
+  __device__ __forceinline__ void store(const DecodeArgs& a) const {
+    if (!on) return;
+    reinterpret_cast<u32x4*>(a.k_dst)[dst] = k;
+    if (a.v_dst) reinterpret_cast<u32x4*>(a.v_dst)[dst] = v;
+  }
+};
 
 // Matrix-core path limits: units (batch rows x KV heads) per call, and the fixed grid
 // (work-groups of 4 waves, kMfmaBlocksPerCU per CU of an MI355X).

@@ -100,7 +100,10 @@ typedef struct ga_decode_opts {
                          of 64 in [64, 65536].  Results are split-invariant within
                          rounding.                                                     */
   int32_t impl;       /* GA_IMPL_*; MFMA exists for head_dim 512 with G = 16 and K = V */
-  int32_t reserved[6]; /* must be zero                                                 */
+  int32_t deterministic; /* 1: the vector kernel visits keys in a fixed order, so repeated
+                            calls give identical bits; 0 (default): keys are handed to
+                            waves dynamically, which is faster and equal within rounding */
+  int32_t reserved[5]; /* must be zero                                                 */
 } ga_decode_opts;
 
 /*

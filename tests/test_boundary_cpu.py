@@ -100,6 +100,13 @@ def test_reserved_option_fields_must_be_zero():
     assert call_decode(shape(), opts=o) == -12
 
 
+def test_deterministic_option_is_a_flag():
+    o = api.make_opts(deterministic=True)
+    assert o.deterministic == 1
+    o.deterministic = 2
+    assert call_decode(shape(), opts=o) == -12
+
+
 @pytest.mark.skipif(not no_gpu(), reason="checks the no-device path")
 def test_valid_decode_without_a_gpu_reports_arch_error():
     assert call_decode(shape()) == -10

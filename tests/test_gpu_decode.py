@@ -176,10 +176,10 @@ def test_split_count_invariance():
 
 def test_k_eq_v_null_equals_same_values_passed_twice():
     inp = gen_layer(82, 4, 16, 1, 512, 2048, True, 1, 2048).to_device()
-    a = run(inp, 0, 0.0, default_scale(512), api.LINEAR, impl=api.IMPL_VALU)
+    a = run(inp, 0, 0.0, default_scale(512), api.LINEAR, impl=api.IMPL_VALU, deterministic=True)
     copy = inp.k.clone()
     b = api.decode(inp.q, inp.k, copy, inp.ctx_t, inp.qpos_t, 0, 0.0, default_scale(512),
-                   api.LINEAR, impl=api.IMPL_VALU)
+                   api.LINEAR, impl=api.IMPL_VALU, deterministic=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
@@ -202,12 +202,35 @@ def test_ring_equals_linear_bitwise():
     ctx_t = torch.from_numpy(ctx).cuda()
     qp = ctx_t - 1
     a = api.decode(q, synth.from_bits(ring_k, "cuda"), synth.from_bits(ring_v, "cuda"), ctx_t, qp,
-                   W, 0.0, 0.0625, api.RING, max_ctx=700)
+                   W, 0.0, 0.0625, api.RING, max_ctx=700, deterministic=True)
     b = api.decode(q, synth.from_bits(hist_k, "cuda"), synth.from_bits(hist_v, "cuda"), ctx_t, qp,
-                   W, 0.0, 0.0625, api.LINEAR)
+                   W, 0.0, 0.0625, api.LINEAR, deterministic=True)
     torch.cuda.synchronize()
     assert torch.isfinite(a).all()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("geom", ["sliding", "global_valu"])
+def test_deterministic_mode_repeats_bits_and_dynamic_agrees(geom):
+    """With deterministic set, repeated calls give identical bits; the default (keys
+    handed to waves as they free up) sums the same terms in another order, so it agrees
+    to within a few float32 roundings."""
+    if geom == "sliding":
+        g = wl.sliding_geom(16, 8, 1024)
+        inp = layer_case(86, 8, g, 1, 8192)
+        kw = dict(max_ctx=8192)
+    else:
+        g = wl.global_geom(16, 6000)
+        inp = layer_case(87, 4, g, 1000, 6000)
+        kw = dict(impl=api.IMPL_VALU)
+    args = (g.window, 0.0, g.q_scale, g.kind)
+    d1 = run(inp, *args, deterministic=True, **kw)
+    d2 = run(inp, *args, deterministic=True, **kw)
+    assert torch.equal(d1, d2)
+    for _ in range(3):
+        dyn = run(inp, *args, **kw)
+        max_abs, rel = errors(dyn, d1.double().cpu().numpy())
+        assert max_abs < 2e-5 and rel < 2e-5, (max_abs, rel)
 
 
 def test_gqa_equals_mha_with_repeated_kv():
@@ -253,7 +276,8 @@ def test_device_errors_launch_nothing():
 
 # ------------------------------------------------------------------ matrix-core global path
 
-@pytest.mark.parametrize("case", ["one_long_row", "many_short_rows", "tile_edges", "ring_kv_shared"])
+@pytest.mark.parametrize("case", ["one_long_row", "many_short_rows", "rows_at_grid_bound",
+                                  "tile_edges", "ring_kv_shared"])
 def test_mfma_partition_cases(case):
     """The matrix-core kernel cuts the batch's keys into equal chunks per work-group:
     one row spread over every work-group, hundreds of rows shorter than a tile, rows
@@ -264,6 +288,11 @@ def test_mfma_partition_cases(case):
     elif case == "many_short_rows":
         ctx = list(np.random.default_rng(90).integers(0, 40, size=600))
         cap = 64
+    elif case == "rows_at_grid_bound":
+        # 384 = 3/4 of the 512 work-groups, all non-empty: the last unit count for which
+        # the launch uses the plain grid; one work-group per row plus the chunked rest
+        ctx = list(np.random.default_rng(92).integers(1, 400, size=384))
+        cap = 400
     elif case == "tile_edges":
         ctx = [16, 17, 15, 1, 0, 32, 4096, 4095, 4097, 0, 33, 1000]
         cap = 4097
@@ -351,11 +380,12 @@ def test_decode_append_equals_append_then_decode(case):
     k1, v1 = inp.k.clone(), None if k_eq_v else inp.v.clone()
     api.kv_append(k1, v1, k_new, v_new, pos_t, kind)
     ref = api.decode(inp.q, k1, v1, inp.ctx_t, inp.qpos_t, window, 20.0, scale, kind,
-                     max_ctx=max_ctx, split_keys=split, impl=impl)
+                     max_ctx=max_ctx, split_keys=split, impl=impl, deterministic=True)
     # fused
     k2, v2 = inp.k.clone(), None if k_eq_v else inp.v.clone()
     got = api.decode_append(inp.q, k2, v2, k_new, v_new, pos_t, inp.ctx_t, inp.qpos_t, window,
-                            20.0, scale, kind, max_ctx=max_ctx, split_keys=split, impl=impl)
+                            20.0, scale, kind, max_ctx=max_ctx, split_keys=split, impl=impl,
+                            deterministic=True)
     torch.cuda.synchronize()
     assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), "cache differs"
     if not k_eq_v:
