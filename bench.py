@@ -45,7 +45,14 @@ def parse_args():
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
     p.add_argument("--command", default="", help="command line recorded in summaries")
+    p.add_argument("--workload", default="hybrid48", choices=sorted(SINGLE_LAYER) + ["hybrid48"],
+                   help="hybrid48: the 48-layer step (default); others: one layer type")
     return p.parse_args()
+
+
+# Single-layer workloads measured with --workload (the default line is the 48-layer step).
+SINGLE_LAYER = {"hd128_sliding": "HD128_SLIDING", "g4_12b_sliding": "G4_12B_SLIDING",
+                "g4_12b_global": "G4_12B_GLOBAL"}
 
 
 def log(msg):
@@ -170,6 +177,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the per-GPU workload is the whole step at its real shape)", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "hybrid48":
+        bench_single_layer(args)
+        return
     import numpy as np
     import torch
 
@@ -324,6 +334,113 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cache, qs, ctx, w, per_layer, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_single_layer(args):
+    """One layer type: fused append + decode of its workload, rotating over enough cache
+    copies (>= 1 GiB in all) that no launch finds its keys in the 256 MB Infinity Cache."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    from decode_attention_split_amd import api, synth
+    from decode_attention_split_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = getattr(wl, SINGLE_LAYER[args.workload])
+    g = w.layers[0]
+    B = w.batch
+    gen_cpu = synth.generator(w.seed)
+    ctx = synth.uniform_int(gen_cpu, B, w.ctx_lo, w.ctx_hi).numpy().astype(np.int32)
+    gdev = synth.generator(w.seed, device=dev)
+    cache_shape = (B, g.num_kv_heads, g.capacity, g.head_dim)
+    cache_bytes = int(np.prod(cache_shape)) * 2 * (1 if g.k_eq_v else 2)
+    copies = int(min(8, max(1, math.ceil((1 << 30) / cache_bytes))))
+    sets = []
+    for _ in range(copies):
+        q = synth.normal_bf16(gdev, (B, g.num_q_heads, g.head_dim), device=dev)
+        k = synth.normal_bf16(gdev, cache_shape, device=dev)
+        v = None if g.k_eq_v else synth.normal_bf16(gdev, cache_shape, device=dev)
+        sets.append((q, k, v))
+    k_new = synth.normal_bf16(gdev, (B, g.num_kv_heads, g.head_dim), device=dev)
+    v_new = None if g.k_eq_v else synth.normal_bf16(gdev, k_new.shape, device=dev)
+    out = torch.empty((B, g.num_q_heads, g.head_dim), dtype=torch.float32, device=dev)
+    ctx_t = torch.from_numpy(ctx).to(dev)
+    pos_t = ctx_t - 1
+    max_ctx = w.ctx_hi if g.kind == api.RING else g.capacity
+    shape = api.make_shape(B, g.num_q_heads, g.num_kv_heads, g.head_dim, g.capacity, g.kind,
+                           max_ctx)
+    ws = torch.empty((max(1, api.workspace_bytes(shape, g.window)),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, k, v = sets[i % copies]
+        api.decode_append(q, k, v, k_new, v_new, pos_t, ctx_t, pos_t, g.window, g.softcap,
+                          g.q_scale, g.kind, out=out, workspace=ws, max_ctx=max_ctx)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    lb = layer_bytes(g, B, ctx)
+    nbytes = lb["decode"] + lb["append"]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"{w.name}: {ms * 1e3:.2f} us per launch, {gbps:.1f} GB/s, {copies} cache copies")
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + " (one layer: fused append + decode)", "batch": B,
+                   "layers": 1, "ctx_mean": float(ctx.mean()), "accumulate": "fp32",
+                   "algorithmic_bytes_per_step": int(nbytes), "cache_copies": copies},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "layer_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "roofline": {"kernel": "fused append + decode, per launch", "bound": "hbm",
+                     "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        q, k, v = sets[0]
+        qb, kb, vb = synth.bits(q), synth.bits(k), None if v is None else synth.bits(v)
+        threads = oracle.num_threads_default()
+        rows, spent, done = 0, 0.0, 0
+        chunk = 4
+        while rows < B and spent < args.cpu_seconds:
+            sl = slice(rows, min(B, rows + chunk))
+            t0 = time.perf_counter()
+            oracle.decode(qb[sl], kb[sl], None if vb is None else vb[sl], ctx[sl], ctx[sl] - 1,
+                          g.window, g.softcap, g.q_scale, g.kind, nthreads=threads)
+            spent += time.perf_counter() - t0
+            done += layer_bytes(g, sl.stop - sl.start, ctx[sl])["decode"]
+            rows = sl.stop
+        result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
+                                  "cores": int(min(threads, rows * g.num_q_heads)),
+                                  "kind": "oracle",
+                                  "sample": f"rows 0-{rows - 1} of the layer (decode only), "
+                                            f"{spent:.1f}s of oracle time"}
     print(json.dumps(result), flush=True)
 
 

@@ -44,11 +44,15 @@ int32_t check_arch() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// head sizes 128 (test matrix of the "Gemma support" pull request), 256 (sliding layers)
+// and 512 (global layers)
+bool head_dim_ok(int d) { return d == 128 || d == 256 || d == 512; }
+
 int32_t check_shape(const ga_shape* s, int32_t window) {
   if (!s) return GA_ERR_NULL;
   if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->capacity <= 0)
     return GA_ERR_DIMS;
-  if (s->head_dim != 256 && s->head_dim != 512) return GA_ERR_HEAD_DIM;
+  if (!head_dim_ok(s->head_dim)) return GA_ERR_HEAD_DIM;
   if (s->num_q_heads % s->num_kv_heads != 0) return GA_ERR_GQA;
   const int G = s->num_q_heads / s->num_kv_heads;
   if (!ga::decode_valu_supported(s->head_dim, G)) return GA_ERR_GQA;
@@ -174,7 +178,7 @@ const char* gemma_attn_strerror(int32_t st) {
     case GA_OK: return "ok";
     case GA_ERR_NULL: return "a required pointer is NULL or not 16-byte aligned";
     case GA_ERR_DIMS: return "invalid dimensions (batch < 0, or a head count or capacity <= 0)";
-    case GA_ERR_HEAD_DIM: return "head_dim must be 256 or 512";
+    case GA_ERR_HEAD_DIM: return "head_dim must be 128, 256 or 512";
     case GA_ERR_GQA: return "num_q_heads must be num_kv_heads times 1, 2, 4, 8 or 16";
     case GA_ERR_KIND: return "cache kind must be GA_CACHE_LINEAR or GA_CACHE_RING";
     case GA_ERR_WINDOW:
@@ -327,7 +331,7 @@ int32_t gemma_kv_append(const ga_shape* shape, ga_bf16* k_cache, ga_bf16* v_cach
   if (shape->batch < 0 || shape->num_kv_heads <= 0 || shape->num_q_heads <= 0 ||
       shape->capacity <= 0)
     return GA_ERR_DIMS;
-  if (shape->head_dim != 256 && shape->head_dim != 512) return GA_ERR_HEAD_DIM;
+  if (!head_dim_ok(shape->head_dim)) return GA_ERR_HEAD_DIM;
   if (shape->kind != GA_CACHE_LINEAR && shape->kind != GA_CACHE_RING) return GA_ERR_KIND;
   if (!k_cache || !k_new || !pos) return GA_ERR_NULL;
   if ((v_cache == nullptr) != (v_new == nullptr)) return GA_ERR_V_MISMATCH;

@@ -39,8 +39,12 @@ constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi 
 // work-groups (one split per row) that need more waves in flight per CU.
 template <int D, int G>
 constexpr int valu_nw_base() { return clampi(8192 / (G * D), 1, 4); }
+// The wide variant doubles the waves of small work-groups; only where a lane's
+// accumulators stay at 64 (the lanes per key are not clamped at D / 8), else it spills.
 template <int D, int G>
-constexpr bool valu_nw_wide_ok() { return valu_nw_base<D, G>() == 4 && G * D <= 2048; }
+constexpr bool valu_nw_wide_ok() {
+  return valu_nw_base<D, G>() == 4 && G * D <= 2048 && G * D / clampi(G * D / 64, 8, D / 8) <= 64;
+}
 
 template <int D, int G, int NW_>
 struct ValuCfg {
@@ -349,14 +353,20 @@ int wide_waves_d(int G) {
 }  // namespace
 
 bool decode_valu_supported(int D, int G) {
-  return (D == 256 || D == 512) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  return (D == 128 || D == 256 || D == 512) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
 int decode_valu_wide_waves(int D, int G) {
-  return D == 256 ? wide_waves_d<256>(G) : D == 512 ? wide_waves_d<512>(G) : 0;
+  switch (D) {
+    case 128: return wide_waves_d<128>(G);
+    case 256: return wide_waves_d<256>(G);
+    case 512: return wide_waves_d<512>(G);
+    default: return 0;
+  }
 }
 
 hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  if (a.D == 128) return launch_d<128>(a, k_eq_v, stream);
   if (a.D == 256) return launch_d<256>(a, k_eq_v, stream);
   if (a.D == 512) return launch_d<512>(a, k_eq_v, stream);
   return hipErrorInvalidValue;

@@ -9,7 +9,11 @@ Geometry sources (page titles and sections):
     KV-head counts; K/V sharing on full layers.  Threats to validity: the query scale
     defaults to 1/sqrt(head_dim) per geometry.
   * "Gemma support" pull request, Summary: soft-capping, sliding-window layers, mixed
-    256/512 head sizes, K = V global attention.
+    256/512 head sizes, K = V global attention; Test plan: kernel tests over head sizes
+    128 to 512.
+  * "Gemma 4 12B (unified multimodal)" record, "KV geometry, now derived":
+    num_kv_shared_layers (0 for that model) counts layers that take a neighbour's cache
+    instead of keeping their own.
 
 Nothing here computes attention; these are shapes, seeds and counts.
 """
@@ -91,8 +95,33 @@ def hybrid_layers(num_layers=48, sliding=None, full=None) -> List[LayerGeom]:
     return [full if t == "full_attention" else sliding for t in gemma4_12b_layer_types(num_layers)]
 
 
-def kv_bytes_per_token(layers: List[LayerGeom], count_v_for_k_eq_v: bool = False) -> int:
-    return sum(g.kv_bytes_per_token(count_v_for_k_eq_v) for g in layers)
+def kv_share_sources(layers: List[LayerGeom], num_kv_shared_layers: int = 0) -> List[int]:
+    """Index of the layer whose cache each layer reads (itself when it owns one).
+
+    Reading of num_kv_shared_layers (the pages name the field, and say that a layer
+    sharing cache takes it from a neighbour): the last N layers of the stack keep no
+    cache; each reads the cache of the nearest earlier non-shared layer with the same
+    geometry.  Those owners come first in the stack, so within one step an owner has
+    appended the token before any layer that shares its cache attends.
+    """
+    n = len(layers)
+    if not 0 <= num_kv_shared_layers < n:
+        raise ValueError(f"num_kv_shared_layers must be in [0, {n})")
+    first_shared = n - num_kv_shared_layers
+    src = list(range(n))
+    for l in range(first_shared, n):
+        owners = [o for o in range(first_shared) if layers[o] == layers[l]]
+        if not owners:
+            raise ValueError(f"layer {l}: no earlier layer with the same geometry to share")
+        src[l] = owners[-1]
+    return src
+
+
+def kv_bytes_per_token(layers: List[LayerGeom], count_v_for_k_eq_v: bool = False,
+                       sources: Optional[List[int]] = None) -> int:
+    """Cache bytes one token adds across the stack; layers that share a cache add none."""
+    owners = range(len(layers)) if sources is None else sorted(set(sources))
+    return sum(layers[i].kv_bytes_per_token(count_v_for_k_eq_v) for i in owners)
 
 
 # The five synthetic workloads (seed = index).
@@ -110,6 +139,12 @@ HYBRID_48 = Workload("48-layer hybrid decode step, B32 ctx U[1,16384]: 40 slidin
                      hybrid_layers(48, sliding_geom(16, 8, 1024), global_geom(16, 16384)))
 
 ALL = [TINY, G3_1B_SLIDING, G4_12B_SLIDING, G4_12B_GLOBAL, HYBRID_48]
+
+# Extra single-layer workloads for the head sizes the kernel tests span (128 to 512):
+# the long-context sliding layer of the 12B geometry at head_dim 128.
+HD128_SLIDING = Workload("hd128 sliding layer, B64 16q/8kv hd128 ring w1024 ctx U[512,8192]"
+                         " softcap50", 6, 64, 512, 8192,
+                         [sliding_geom(16, 8, 1024, softcap=50.0, head_dim=128)])
 
 
 def layer_seed(workload: Workload, layer: int) -> int:

@@ -15,7 +15,8 @@
  *   Passages defining the operation (page titles and sections):
  *     - "Gemma support" pull request, Summary: attention logit soft-capping,
  *       sliding-window layers, mixed 256/512 head sizes, K = V global attention;
- *       Performance: split decode attention for head sizes 256/512.
+ *       Performance: split decode attention for head sizes 256/512; Test plan:
+ *       kernel tests over head sizes 128 to 512 (hence head_dim 128 is accepted too).
  *     - "Gemma 4 12B (unified multimodal)" record: a local layer reads exactly w KV
  *       entries ("required kernel class"); per-layer-type cache management; the
  *       rotating (ring) KV cache of sliding layers ("(6) On Apple Silicon");
@@ -66,7 +67,7 @@ enum {
   GA_OK = 0,
   GA_ERR_NULL = -1,          /* a required pointer is NULL                                */
   GA_ERR_DIMS = -2,          /* batch < 0, a head count or capacity <= 0                  */
-  GA_ERR_HEAD_DIM = -3,      /* head_dim is not 256 or 512                                */
+  GA_ERR_HEAD_DIM = -3,      /* head_dim is not 128, 256 or 512                           */
   GA_ERR_GQA = -4,           /* num_q_heads is not a multiple of num_kv_heads, or G > 16  */
   GA_ERR_KIND = -5,          /* kind is neither GA_CACHE_LINEAR nor GA_CACHE_RING         */
   GA_ERR_WINDOW = -6,        /* ring: window > W, or window <= 0 while max_ctx may exceed W */
@@ -85,7 +86,7 @@ typedef struct ga_shape {
   int32_t batch;        /* B >= 0 (0: nothing to do)                                  */
   int32_t num_q_heads;  /* Hq > 0                                                     */
   int32_t num_kv_heads; /* Hkv > 0, Hq % Hkv == 0, G = Hq / Hkv <= 16                 */
-  int32_t head_dim;     /* D: 256 or 512                                              */
+  int32_t head_dim;     /* D: 128, 256 or 512                                         */
   int32_t capacity;     /* ring: W slots; linear: C positions                         */
   int32_t kind;         /* GA_CACHE_LINEAR or GA_CACHE_RING                           */
   int32_t max_ctx;      /* host upper bound on every ctx_lens[b]; 0 means `capacity`  */

@@ -62,7 +62,8 @@ def no_gpu():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(s=shape(D=128)), -3),
+    (dict(s=shape(D=64)), -3),
+    (dict(s=shape(D=384)), -3),
     (dict(s=shape(D=384)), -3),
     (dict(s=shape(Hq=12, Hkv=8)), -4),
     (dict(s=shape(Hq=24, Hkv=1)), -4),    # G = 24 is not supported

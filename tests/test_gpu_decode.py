@@ -44,7 +44,8 @@ def test_tiny_sliding_decode():
     assert_parity(out, oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind), "tiny")
 
 
-@pytest.mark.parametrize("w", [wl.G3_1B_SLIDING, wl.G4_12B_SLIDING], ids=["g3_1b", "g4_12b"])
+@pytest.mark.parametrize("w", [wl.G3_1B_SLIDING, wl.G4_12B_SLIDING, wl.HD128_SLIDING],
+                         ids=["g3_1b", "g4_12b", "hd128"])
 def test_sliding_layer_full_size(w):
     g = w.layers[0]
     log(f"full size: {w.name}")
@@ -79,7 +80,7 @@ def test_hybrid_step_layer_sampled_rows(layer):
 
 # ------------------------------------------------------------------ geometry sweep
 
-@pytest.mark.parametrize("D", [256, 512])
+@pytest.mark.parametrize("D", [128, 256, 512])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("k_eq_v", [False, True])
 def test_geometry_sweep(D, G, k_eq_v):
@@ -98,6 +99,42 @@ def test_geometry_sweep(D, G, k_eq_v):
         out = run(inp, window, geom.softcap, geom.q_scale, kind, split_keys=split,
                   max_ctx=int(inp.ctx.max()) if kind == api.RING else cap)
         assert_parity(out, ref, f"split={split}")
+
+
+# ------------------------------------------------------------------ cross-layer cache sharing
+
+def test_shared_layers_attend_over_the_owner_cache():
+    """A 12-layer stack whose last 4 layers share caches: one fused step appends once per
+    owner, and each layer's output equals the oracle over its owner's cache after the
+    step (a sharing layer sees the token its owner appended)."""
+    from decode_attention_split_amd.hybrid import HybridKVCache
+    layers = wl.hybrid_layers(12, wl.sliding_geom(8, 4, 128), wl.global_geom(16, 1024))
+    src = wl.kv_share_sources(layers, 4)
+    B = 3
+    ctx = np.array([1, 300, 1024], np.int32)
+    gd = synth.generator(96)
+    fill = lambda li, name, shape: synth.normal_bf16(gd, shape).cuda()
+    cache = HybridKVCache(layers, B, 1024, device="cuda", fill=fill, kv_source=src)
+    qs = [synth.normal_bf16(gd, (B, g.num_q_heads, g.head_dim)).cuda() for g in layers]
+    kn = [synth.normal_bf16(gd, (B, g.num_kv_heads, g.head_dim)).cuda() for g in layers]
+    vn = [None if g.k_eq_v else synth.normal_bf16(gd, (B, g.num_kv_heads, g.head_dim)).cuda()
+          for g in layers]
+    outs = [torch.empty((B, g.num_q_heads, g.head_dim), dtype=torch.float32, device="cuda")
+            for g in layers]
+    ctx_t = torch.from_numpy(ctx).cuda()
+    pos = ctx_t - 1
+    cache.step(qs, kn, vn, pos, ctx_t, pos, outs)
+    torch.cuda.synchronize()
+    for l, g in enumerate(layers):
+        s = src[l]
+        # the owner's slot of the newest token holds the owner's new row
+        slot = (ctx - 1) % g.capacity if g.kind == api.RING else ctx - 1
+        for b in range(B):
+            assert torch.equal(cache.k[l][b, :, slot[b]], kn[s][b]), (l, b)
+        inp = LayerInputs(synth.bits(qs[l]), synth.bits(cache.k[l]),
+                          None if g.k_eq_v else synth.bits(cache.v[l]), ctx, ctx - 1)
+        ref = oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind)
+        assert_parity(outs[l], ref, f"layer {l} (cache of {s})")
 
 
 # ------------------------------------------------------------------ window / wrap alignment
