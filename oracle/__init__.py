@@ -1,4 +1,4 @@
-"""fp64 oracle for single-token decode attention over bf16 KV caches.
+"""fp64 oracle for decode attention over bf16 KV caches (one or T query tokens per row).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
 baseline leg of ``bench.py`` may import this package.  The GPU library and its Python
@@ -43,6 +43,10 @@ def _load():
     lib.oracle_decode_f64.argtypes = [ctypes.c_int] * 6 + [P, P, P, P, P, ctypes.c_int, f32, f32,
                                                            P, P, P, ctypes.c_long, P, ctypes.c_int]
     lib.oracle_decode_f64.restype = ctypes.c_int
+    lib.oracle_decode_multi_f64.argtypes = [ctypes.c_int] * 7 + [P, P, P, P, P, ctypes.c_int, f32,
+                                                                 f32, P, P, P, ctypes.c_long, P,
+                                                                 ctypes.c_int]
+    lib.oracle_decode_multi_f64.restype = ctypes.c_int
     lib.oracle_append.argtypes = [ctypes.c_int] * 5 + [P, P, P]
     lib.oracle_append.restype = ctypes.c_int
     lib.oracle_valid_positions.argtypes = [i32, i32, i32, i32, i32, P, P]
@@ -110,6 +114,46 @@ def decode(q, k_cache, v_cache, ctx_lens, q_pos, window, softcap, scale, kind, p
     if rc != 0:
         raise ValueError(f"oracle_decode_f64 failed: {rc}")
     return out, lse, probs, flags
+
+
+def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos0, window, softcap, scale, kind,
+                 probs_len=0, nthreads=0):
+    """Plain fp64 decode attention for T consecutive query tokens per batch row.
+
+    q [B,T,Hq,D]; token t of row b sits at position q_pos0[b] + t and is masked at that
+    position (causal limit and window of its own), against the same cache rows.
+    Returns (out [B,T,Hq,D], lse [B,T,Hq], probs [B,T,Hq,probs_len] or None, flags [B,T]).
+    """
+    lib = _load()
+    q = _u16(q)
+    k_cache = _u16(k_cache)
+    v_cache = None if v_cache is None else _u16(v_cache)
+    B, T, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k_cache.shape
+    if Bk != B or Dk != D or (v_cache is not None and v_cache.shape != k_cache.shape):
+        raise ValueError("shape mismatch")
+    ctx_lens, q_pos0 = _i32(ctx_lens), _i32(q_pos0)
+    out = np.zeros((B, T, Hq, D), np.float64)
+    lse = np.zeros((B, T, Hq), np.float64)
+    probs = np.zeros((B, T, Hq, probs_len), np.float64) if probs_len > 0 else None
+    flags = np.zeros((B, T), np.int32)
+    rc = lib.oracle_decode_multi_f64(B, T, Hq, Hkv, D, cap, int(kind), _ptr(q), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(ctx_lens), _ptr(q_pos0), int(window),
+                                     float(softcap), float(scale), _ptr(out), _ptr(lse),
+                                     _ptr(probs), int(probs_len), _ptr(flags), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_multi_f64 failed: {rc}")
+    return out, lse, probs, flags
+
+
+def append_tokens(cache, new_rows, pos0, kind):
+    """Append T tokens per row in order t = 0..T-1 at positions pos0[b] + t (a later
+    token overwrites an earlier one that lands in the same ring slot)."""
+    new_rows = _u16(new_rows)
+    B, T = new_rows.shape[:2]
+    pos0 = _i32(pos0)
+    for t in range(T):
+        append(cache, np.ascontiguousarray(new_rows[:, t]), pos0 + t, kind)
 
 
 def append(cache, new_rows, pos, kind):

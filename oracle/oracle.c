@@ -6,9 +6,11 @@
  * or calls anything here, and nothing here includes or links the GPU library.
  *
  * What it computes is the plain, unsplit definition of masked softmax attention for
- * one query token per sequence, with no blocking, splitting or reordering:
+ * one query token per sequence (or T consecutive query tokens per sequence, each with
+ * its own causal and window mask), with no blocking, splitting or reordering:
  *
- *   for every batch row b and query head h (KV head g = h / G, G = Hq / Hkv):
+ *   for every batch row b, query token t (at position q_pos = q_pos0_b + t) and query
+ *   head h (KV head g = h / G, G = Hq / Hkv):
  *     P  = positions p with 0 <= p <= q_pos, p < ctx, inside the window
  *          (window w > 0: p > q_pos - w) and still present in the cache
  *          (ring of W slots: p >= ctx - W; linear of C slots: p < C)
@@ -27,7 +29,10 @@
  *    head dims and KV-head counts, no separate value projection on full layers;
  *    Threats to validity: the query scale defaults to 1/sqrt(head_dim).
  *  - "Gemma support", Performance: split decode attention (the merge algebra in
- *    oracle_split_merge_f64 is the textbook log-sum-exp identity it rests on).
+ *    oracle_split_merge_f64 is the textbook log-sum-exp identity it rests on); its flash
+ *    prefill for head_dim 256 and the spec-decode (k = 7) with sliding-window item of the
+ *    "Gemma 4 12B (unified multimodal)" record ("(2)"): several query tokens of one
+ *    sequence against the same cache, each masked at its own position.
  * Readings where the pages are silent: the soft-cap is c*tanh(s/c) and is off for
  * c <= 0 or non-finite c; the scale multiplies the raw dot product before the cap;
  * the window is inclusive of the current token and holds exactly w positions; query
@@ -107,7 +112,7 @@ int64_t oracle_valid_positions(int32_t ctx, int32_t q_pos, int32_t window, int32
 }
 
 typedef struct {
-  int B, Hq, Hkv, D, cap, kind;
+  int B, T, Hq, Hkv, D, cap, kind;
   const uint16_t *q, *k, *v;
   const int32_t *ctx, *qpos;
   int window;
@@ -119,14 +124,17 @@ typedef struct {
   pthread_mutex_t mu;
 } decode_job;
 
+/* One query row: unit = (b * T + t) * Hq + h. */
 static void decode_unit(decode_job* J, long unit, double* s_buf, long* p_buf) {
-  const int b = (int)(unit / J->Hq), h = (int)(unit % J->Hq);
+  const long bt = unit / J->Hq;
+  const int h = (int)(unit % J->Hq);
+  const int b = (int)(bt / J->T), t = (int)(bt % J->T);
   const int G = J->Hq / J->Hkv, g = h / G, D = J->D;
-  const long ctx = J->ctx[b], qp = J->qpos[b];
-  const uint16_t* qrow = J->q + ((long)b * J->Hq + h) * D;
+  const long ctx = J->ctx[b], qp = (long)J->qpos[b] + t;
+  const uint16_t* qrow = J->q + unit * D;
   const uint16_t* kbase = J->k + ((long)b * J->Hkv + g) * (long)J->cap * D;
   const uint16_t* vbase = (J->v ? J->v : J->k) + ((long)b * J->Hkv + g) * (long)J->cap * D;
-  double* orow = J->out + ((long)b * J->Hq + h) * D;
+  double* orow = J->out + unit * D;
 
   long n = 0;
   for (long p = 0; p < ctx; ++p)
@@ -178,7 +186,7 @@ static void* decode_worker(void* arg) {
     free(p_buf);
     return (void*)1;
   }
-  const long units = (long)J->B * J->Hq;
+  const long units = (long)J->B * J->T * J->Hq;
   for (;;) {
     pthread_mutex_lock(&J->mu);
     long u = J->next_unit++;
@@ -197,25 +205,30 @@ int oracle_num_threads_default(void) {
 }
 
 /*
- * Decode attention for every (b, h).  q [B,Hq,D]; k_cache and v_cache [B,Hkv,cap,D]
- * (bf16 bits, contiguous); v_cache NULL means V = K.  out [B,Hq,D] double; lse [B*Hq]
- * (may be NULL); probs [B*Hq, probs_len] indexed by absolute position (may be NULL);
- * flags [B] receives the precondition flags (may be NULL).  nthreads <= 0: all cores.
- * Returns 0, or OR_EINVAL / OR_ENOMEM.
+ * Decode attention for every (b, t, h) with T query tokens per batch row.  q [B,T,Hq,D];
+ * k_cache and v_cache [B,Hkv,cap,D] (bf16 bits, contiguous); v_cache NULL means V = K;
+ * q_pos0 [B] is the position of token 0, token t sits at q_pos0[b] + t.  out [B,T,Hq,D]
+ * double; lse [B*T*Hq] (may be NULL); probs [B*T*Hq, probs_len] indexed by absolute
+ * position (may be NULL); flags [B*T] receives each token's precondition flags (may be
+ * NULL).  nthreads <= 0: all cores.  Returns 0, or OR_EINVAL / OR_ENOMEM.
  */
-int oracle_decode_f64(int B, int Hq, int Hkv, int D, int cap, int kind, const uint16_t* q,
-                      const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* ctx_lens,
-                      const int32_t* q_pos, int window, float softcap, float scale, double* out,
-                      double* lse, double* probs, long probs_len, int32_t* flags, int nthreads) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || cap <= 0 || Hq % Hkv != 0) return OR_EINVAL;
+int oracle_decode_multi_f64(int B, int T, int Hq, int Hkv, int D, int cap, int kind,
+                            const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int32_t* ctx_lens, const int32_t* q_pos0, int window,
+                            float softcap, float scale, double* out, double* lse, double* probs,
+                            long probs_len, int32_t* flags, int nthreads) {
+  if (B < 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || cap <= 0 || Hq % Hkv != 0)
+    return OR_EINVAL;
   if (kind != OR_LINEAR && kind != OR_RING) return OR_EINVAL;
-  if (!q || !k_cache || !ctx_lens || !q_pos || !out) return OR_EINVAL;
+  if (!q || !k_cache || !ctx_lens || !q_pos0 || !out) return OR_EINVAL;
   if (!isfinite(scale)) return OR_EINVAL;
   if (flags)
-    for (int b = 0; b < B; ++b) flags[b] = oracle_row_flags(ctx_lens[b], q_pos[b], window, kind, cap);
+    for (int b = 0; b < B; ++b)
+      for (int t = 0; t < T; ++t)
+        flags[(long)b * T + t] = oracle_row_flags(ctx_lens[b], q_pos0[b] + t, window, kind, cap);
   decode_job J;
-  J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.cap = cap; J.kind = kind;
-  J.q = q; J.k = k_cache; J.v = v_cache; J.ctx = ctx_lens; J.qpos = q_pos;
+  J.B = B; J.T = T; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.cap = cap; J.kind = kind;
+  J.q = q; J.k = k_cache; J.v = v_cache; J.ctx = ctx_lens; J.qpos = q_pos0;
   J.window = window;
   J.softcap = (isfinite(softcap) && softcap > 0.0f) ? (double)softcap : 0.0;
   J.scale = (double)scale;
@@ -223,20 +236,33 @@ int oracle_decode_f64(int B, int Hq, int Hkv, int D, int cap, int kind, const ui
   J.next_unit = 0;
   pthread_mutex_init(&J.mu, NULL);
   if (nthreads <= 0) nthreads = oracle_num_threads_default();
-  long units = (long)B * Hq;
+  long units = (long)B * T * Hq;
   if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
   if (!th) return OR_ENOMEM;
   int rc = OR_OK;
-  for (int t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, decode_worker, &J);
-  for (int t = 0; t < nthreads; ++t) {
+  for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, decode_worker, &J);
+  for (int i = 0; i < nthreads; ++i) {
     void* r = NULL;
-    pthread_join(th[t], &r);
+    pthread_join(th[i], &r);
     if (r) rc = OR_ENOMEM;
   }
   free(th);
   pthread_mutex_destroy(&J.mu);
   return rc;
+}
+
+/*
+ * Decode attention for every (b, h), one query token per row at q_pos[b]: the T = 1
+ * case of oracle_decode_multi_f64.  q [B,Hq,D]; out [B,Hq,D]; lse [B*Hq]; flags [B].
+ */
+int oracle_decode_f64(int B, int Hq, int Hkv, int D, int cap, int kind, const uint16_t* q,
+                      const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* ctx_lens,
+                      const int32_t* q_pos, int window, float softcap, float scale, double* out,
+                      double* lse, double* probs, long probs_len, int32_t* flags, int nthreads) {
+  return oracle_decode_multi_f64(B, 1, Hq, Hkv, D, cap, kind, q, k_cache, v_cache, ctx_lens,
+                                 q_pos, window, softcap, scale, out, lse, probs, probs_len, flags,
+                                 nthreads);
 }
 
 /*
