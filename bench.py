@@ -52,7 +52,7 @@ def parse_args():
 
 # Single-layer workloads measured with --workload (the default line is the 48-layer step).
 SINGLE_LAYER = {"hd128_sliding": "HD128_SLIDING", "g4_12b_sliding": "G4_12B_SLIDING",
-                "g4_12b_global": "G4_12B_GLOBAL"}
+                "g4_12b_global": "G4_12B_GLOBAL", "spec_decode_sliding": "SPEC_DECODE_SLIDING"}
 
 
 def log(msg):
@@ -352,6 +352,8 @@ def bench_single_layer(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = getattr(wl, SINGLE_LAYER[args.workload])
+    if w.tokens > 1:
+        return bench_multi_token(args, w)
     g = w.layers[0]
     B = w.batch
     gen_cpu = synth.generator(w.seed)
@@ -441,6 +443,124 @@ def bench_single_layer(args):
                                   "kind": "oracle",
                                   "sample": f"rows 0-{rows - 1} of the layer (decode only), "
                                             f"{spent:.1f}s of oracle time"}
+    print(json.dumps(result), flush=True)
+
+
+def multi_token_bytes(g, B, T, ctx):
+    """Algorithmic bytes of one multi-token step (T tokens per row at ctx - T .. ctx - 1):
+    every key any token attends to, read once (the union of the T windows), plus q, out,
+    the int inputs, and the append of T rows."""
+    import numpy as np
+    span = np.minimum(ctx, g.window + T - 1) if g.window > 0 else ctx.copy()
+    tensors = 1 if g.k_eq_v else 2
+    kv = int(span.astype("int64").sum()) * g.num_kv_heads * g.head_dim * 2 * tensors
+    q = B * T * g.num_q_heads * g.head_dim * 2
+    out = B * T * g.num_q_heads * g.head_dim * 4
+    ints = 2 * B * 4
+    append = 2 * B * T * g.num_kv_heads * g.head_dim * 2 * tensors + B * 4
+    return {"kv": kv, "decode": kv + q + out + ints, "append": append}
+
+
+def bench_multi_token(args, w):
+    """T tokens per row: gemma_kv_append_multi then gemma_attn_decode_multi per step,
+    rotating over enough cache copies (>= 1 GiB) to keep the Infinity Cache out of it."""
+    import numpy as np
+    import torch
+    from decode_attention_split_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = w.layers[0]
+    B, T = w.batch, w.tokens
+    gen_cpu = synth.generator(w.seed)
+    ctx = synth.uniform_int(gen_cpu, B, w.ctx_lo, w.ctx_hi).numpy().astype(np.int32)
+    gdev = synth.generator(w.seed, device=dev)
+    cache_shape = (B, g.num_kv_heads, g.capacity, g.head_dim)
+    cache_bytes = int(np.prod(cache_shape)) * 2 * (1 if g.k_eq_v else 2)
+    copies = int(min(8, max(1, math.ceil((1 << 30) / cache_bytes))))
+    sets = []
+    for _ in range(copies):
+        q = synth.normal_bf16(gdev, (B, T, g.num_q_heads, g.head_dim), device=dev)
+        k = synth.normal_bf16(gdev, cache_shape, device=dev)
+        v = None if g.k_eq_v else synth.normal_bf16(gdev, cache_shape, device=dev)
+        sets.append((q, k, v))
+    k_new = synth.normal_bf16(gdev, (B, T, g.num_kv_heads, g.head_dim), device=dev)
+    v_new = None if g.k_eq_v else synth.normal_bf16(gdev, k_new.shape, device=dev)
+    out = torch.empty((B, T, g.num_q_heads, g.head_dim), dtype=torch.float32, device=dev)
+    ctx_t = torch.from_numpy(ctx).to(dev)
+    q0_t = ctx_t - T
+    max_ctx = w.ctx_hi if g.kind == api.RING else g.capacity
+    shape = api.make_shape(B, g.num_q_heads, g.num_kv_heads, g.head_dim, g.capacity, g.kind,
+                           max_ctx)
+    ws = torch.empty((max(1, api.workspace_bytes_multi(shape, T, g.window)),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, k, v = sets[i % copies]
+        api.kv_append_multi(k, v, k_new, v_new, q0_t, g.kind)
+        api.decode_multi(q, k, v, ctx_t, q0_t, g.window, g.softcap, g.q_scale, g.kind, out=out,
+                         workspace=ws, max_ctx=max_ctx)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    lb = multi_token_bytes(g, B, T, ctx)
+    nbytes = lb["decode"] + lb["append"]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"{w.name}: {ms * 1e3:.2f} us per step (append + decode), {gbps:.1f} GB/s")
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + " (one layer: T-token append + multi-token decode)",
+                   "batch": B, "tokens": T, "layers": 1, "ctx_mean": float(ctx.mean()),
+                   "accumulate": "fp32", "algorithmic_bytes_per_step": int(nbytes),
+                   "cache_copies": copies},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "layer_tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "roofline": {"kernel": "T-token append + multi-token decode, per step", "bound": "hbm",
+                     "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        q, k, v = sets[0]
+        qb, kb, vb = synth.bits(q), synth.bits(k), None if v is None else synth.bits(v)
+        threads = oracle.num_threads_default()
+        rows, spent, done = 0, 0.0, 0
+        while rows < B and spent < args.cpu_seconds:
+            sl = slice(rows, min(B, rows + 2))
+            t0 = time.perf_counter()
+            oracle.decode_multi(qb[sl], kb[sl], None if vb is None else vb[sl], ctx[sl],
+                                ctx[sl] - T, g.window, g.softcap, g.q_scale, g.kind,
+                                nthreads=threads)
+            spent += time.perf_counter() - t0
+            done += multi_token_bytes(g, sl.stop - sl.start, T, ctx[sl])["decode"]
+            rows = sl.stop
+        result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
+                                  "cores": int(min(threads, rows * T * g.num_q_heads)),
+                                  "kind": "oracle",
+                                  "sample": f"rows 0-{rows - 1} of the layer, all {T} tokens "
+                                            f"(decode only), {spent:.1f}s of oracle time"}
     print(json.dumps(result), flush=True)
 
 

@@ -88,6 +88,16 @@ def workspace_bytes(shape, window: int, split_keys: int = 0, impl: int = IMPL_AU
     return int(n)
 
 
+def workspace_bytes_multi(shape, num_tokens: int, window: int, split_keys: int = 0) -> int:
+    lib = _lib.load()
+    opts = make_opts(split_keys)
+    n = lib.ga_decode_multi_workspace_bytes(ctypes.byref(shape), int(num_tokens), int(window),
+                                            ctypes.byref(opts))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid shape/tokens/window/options for gemma_attn_decode_multi")
+    return int(n)
+
+
 def shape_of(q, k_cache, kind, max_ctx=0):
     B, Hq, D = q.shape
     Bk, Hkv, cap, Dk = k_cache.shape
@@ -174,6 +184,87 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, windo
         _ptr(out), _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream_handle(stream))
     _check(rc, "gemma_attn_decode_append")
     return out
+
+
+def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
+                 kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
+                 deterministic: bool = False, stream=None):
+    """T query tokens per row: q [B, T, Hq, D], token t at position q_pos[b] + t; returns
+    out [B, T, Hq, D] float32 (see gemma_attn_decode_multi in gemma_attn.h)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    if v_cache is not None:
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+        if v_cache.shape != k_cache.shape:
+            raise ValueError("v_cache must have the shape of k_cache")
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    B, T, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k_cache {tuple(k_cache.shape)} disagree")
+    if ctx_lens.numel() != B or q_pos.numel() != B:
+        raise ValueError("ctx_lens and q_pos must have one entry per batch row")
+    shape = make_shape(B, Hq, Hkv, D, cap, kind, max_ctx)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32, 4)
+        if tuple(out.shape) != (B, T, Hq, D):
+            raise ValueError("out must be [B, T, Hq, D]")
+    opts = make_opts(split_keys, IMPL_AUTO, deterministic)
+    lib = _lib.load()
+    need = lib.ga_decode_multi_workspace_bytes(ctypes.byref(shape), int(T), int(window),
+                                               ctypes.byref(opts))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # let the library report the precise error
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib.gemma_attn_decode_multi(
+        ctypes.byref(shape), int(T), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens),
+        _ptr(q_pos), int(window), float(softcap), float(scale), _ptr(out), _ptr(workspace),
+        ws_bytes, ctypes.byref(opts), _stream_handle(stream))
+    _check(rc, "gemma_attn_decode_multi")
+    return out
+
+
+def kv_append_multi(k_cache, v_cache, k_new, v_new, pos, kind: int, stream=None):
+    """T tokens per row: k_new / v_new [B, T, Hkv, D] at positions pos[b] + t, in order."""
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(k_new, "k_new", torch.bfloat16, 4)
+    if (v_cache is None) != (v_new is None):
+        _check(-9, "gemma_kv_append_multi")
+    if v_cache is not None:
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+        _need(v_new, "v_new", torch.bfloat16, 4)
+        if v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
+            raise ValueError("V tensors must have the shapes of the K tensors")
+    _need(pos, "pos", torch.int32, 1)
+    B, Hkv, cap, D = k_cache.shape
+    T = k_new.shape[1]
+    if tuple(k_new.shape) != (B, T, Hkv, D) or pos.numel() != B:
+        raise ValueError("k_new must be [B, T, Hkv, D] and pos [B]")
+    shape = make_shape(B, Hkv, Hkv, D, cap, kind)
+    rc = _lib.load().gemma_kv_append_multi(ctypes.byref(shape), int(T), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(pos),
+                                           _stream_handle(stream))
+    _check(rc, "gemma_kv_append_multi")
+
+
+def validate_multi(shape, num_tokens: int, ctx_lens, q_pos, window: int, stream=None):
+    """Per-token precondition flags (FLAG_*) as an int32 device tensor [B, T]."""
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    flags = torch.empty((shape.batch, int(num_tokens)), dtype=torch.int32,
+                        device=ctx_lens.device)
+    rc = _lib.load().gemma_attn_validate_multi(ctypes.byref(shape), int(num_tokens),
+                                               _ptr(ctx_lens), _ptr(q_pos), int(window),
+                                               _ptr(flags), _stream_handle(stream))
+    _check(rc, "gemma_attn_validate_multi")
+    return flags
 
 
 def kv_append(k_cache, v_cache, k_new, v_new, pos, kind: int, stream=None):

@@ -21,6 +21,11 @@ std::atomic<int> g_arch_ok[kMaxDevices];
 constexpr int kTargetBlocks = 256;   // one work-group per CU of an MI355X
 constexpr int kWideBelowBlocks = 512;  // fewer work-groups than this: use the wide variant
 constexpr int kMaxSplitKeys = 65536;
+#ifndef GA_MULTI_MAX_ROWS
+#define GA_MULTI_MAX_ROWS 8
+#endif
+constexpr int kMultiMaxRows = GA_MULTI_MAX_ROWS;  // multi-token: query rows per unit
+constexpr int kMaxTokens = 4096;  // multi-token: query tokens per row
 
 int32_t check_arch() {
   int dev = -1;
@@ -48,7 +53,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // and 512 (global layers)
 bool head_dim_ok(int d) { return d == 128 || d == 256 || d == 512; }
 
-int32_t check_shape(const ga_shape* s, int32_t window) {
+int32_t check_shape(const ga_shape* s, int32_t window, int32_t T = 1) {
   if (!s) return GA_ERR_NULL;
   if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->capacity <= 0)
     return GA_ERR_DIMS;
@@ -60,13 +65,20 @@ int32_t check_shape(const ga_shape* s, int32_t window) {
   if (s->max_ctx < 0) return GA_ERR_MAX_CTX;
   const long long max_ctx = s->max_ctx == 0 ? s->capacity : s->max_ctx;
   if (s->kind == GA_CACHE_LINEAR && max_ctx > s->capacity) return GA_ERR_MAX_CTX;
+  if (T < 1) return GA_ERR_DIMS;
+  if (T > kMaxTokens) return GA_ERR_TOO_LARGE;
   if (s->kind == GA_CACHE_RING) {
     if (window > s->capacity) return GA_ERR_WINDOW;
     if (window <= 0 && max_ctx > s->capacity) return GA_ERR_WINDOW;
+    // T tokens at ctx - T .. ctx - 1: the first one's window starts T - 1 positions before
+    // the last one's, so a ring that the context can overrun must keep w + T - 1 slots
+    if (window > 0 && max_ctx > s->capacity && (long long)window + T - 1 > s->capacity)
+      return GA_ERR_WINDOW;
   }
   // 32-bit index and grid limits
   const long long rows = (long long)s->batch * s->num_kv_heads * s->capacity;
-  if (rows * s->head_dim / 8 > (1LL << 40) || (long long)s->batch * s->num_q_heads > (1LL << 30))
+  if (rows * s->head_dim / 8 > (1LL << 40) ||
+      (long long)s->batch * T * s->num_q_heads > (1LL << 30))
     return GA_ERR_TOO_LARGE;
   return GA_OK;
 }
@@ -77,6 +89,9 @@ struct Plan {
   int split_keys;  // Ts
   int n_split;     // S
   int max_keys;    // S * Ts
+  int T = 1;       // query tokens per row
+  int Tc = 1;      // tokens per unit (multi-token)
+  int n_chunks = 1;
   size_t ws_bytes;
 };
 
@@ -94,9 +109,28 @@ bool mfma_eligible(const ga_shape* s, bool k_eq_v) {
          (long long)s->batch * s->num_kv_heads <= ga::kMfmaMaxUnits;
 }
 
-int32_t valu_plan(const ga_shape* s, int32_t window, int ts, Plan* p) {
-  const long long nmax = max_keys_bound(s, window);
-  const long long units = (long long)s->batch * s->num_kv_heads;
+// Tokens per unit for T query tokens: the largest power of two that keeps heads x tokens
+// within kMultiMaxRows (one token when the heads alone reach it) and does not exceed the
+// power of two at or above T.
+int tokens_per_unit(int G, int T) {
+  if (T <= 1) return 1;
+  int tc = 1;
+  while (tc < T && G * tc * 2 <= kMultiMaxRows) tc *= 2;
+  return tc;
+}
+
+int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int Tc = tokens_per_unit(G, T);
+  const int n_chunks = (T + Tc - 1) / Tc;
+  long long nmax = max_keys_bound(s, window);
+  if (T > 1 && window > 0) {
+    // a unit's keys: the union of Tc consecutive tokens' windows
+    long long u = max_keys_bound(s, 0);
+    if (u > (long long)window + Tc - 1) u = (long long)window + Tc - 1;
+    nmax = u;
+  }
+  const long long units = (long long)s->batch * s->num_kv_heads * n_chunks;
   if (ts == 0) {
     // Enough work-groups to reach every CU, but at least 128 keys each so the per-split
     // partial (G * (D + 2) floats) stays small next to the split's KV bytes.  Rows that
@@ -112,12 +146,16 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, Plan* p) {
   if (S < 1) S = 1;
   if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
   p->impl = GA_IMPL_VALU;
-  const int wide = ga::decode_valu_wide_waves(s->head_dim, s->num_q_heads / s->num_kv_heads);
+  const int wide = ga::decode_valu_wide_waves(s->head_dim, G * Tc);
   p->n_waves = (wide > 0 && units * S < kWideBelowBlocks) ? wide : 0;
   p->split_keys = ts;
   p->n_split = (int)S;
   p->max_keys = (int)(S * ts);
-  p->ws_bytes = S > 1 ? (size_t)s->batch * s->num_q_heads * (size_t)S * (size_t)(s->head_dim + 2) * 4u
+  p->T = T;
+  p->Tc = Tc;
+  p->n_chunks = n_chunks;
+  p->ws_bytes = S > 1 ? (size_t)s->batch * T * s->num_q_heads * (size_t)S *
+                            (size_t)(s->head_dim + 2) * 4u
                       : 0;
   return GA_OK;
 }
@@ -135,7 +173,7 @@ void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
 // k_eq_v: 1 / 0 when known (a decode call), -1 for a workspace query, which then sizes
 // for whichever implementation AUTO may pick.
 int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, int k_eq_v,
-                  Plan* p) {
+                  Plan* p, int T = 1) {
   int impl = GA_IMPL_AUTO, ts = 0;
   if (o) {
     for (int i = 0; i < 5; ++i)
@@ -145,6 +183,11 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
     ts = o->split_keys;
     if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
     if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
+  }
+  if (T > 1) {
+    // several query tokens: the vector kernel with per-row masks
+    if (impl == GA_IMPL_MFMA) return GA_ERR_OPTS;
+    return valu_plan(s, window, ts, T, p);
   }
   if (impl == GA_IMPL_MFMA) {
     // the matrix-core kernel balances keys over a fixed grid: no split size to choose
@@ -158,20 +201,20 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
       return GA_OK;
     }
     Plan v;
-    int32_t st = valu_plan(s, window, 0, &v);
+    int32_t st = valu_plan(s, window, 0, 1, &v);
     if (st != GA_OK) return st;
     mfma_plan(s, window, p);
     if (v.ws_bytes > p->ws_bytes) p->ws_bytes = v.ws_bytes;
     return GA_OK;
   }
-  return valu_plan(s, window, ts, p);
+  return valu_plan(s, window, ts, 1, p);
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t gemma_attn_version(void) { return 100; }
+int32_t gemma_attn_version(void) { return 200; }
 
 const char* gemma_attn_strerror(int32_t st) {
   switch (st) {
@@ -182,8 +225,8 @@ const char* gemma_attn_strerror(int32_t st) {
     case GA_ERR_GQA: return "num_q_heads must be num_kv_heads times 1, 2, 4, 8 or 16";
     case GA_ERR_KIND: return "cache kind must be GA_CACHE_LINEAR or GA_CACHE_RING";
     case GA_ERR_WINDOW:
-      return "ring cache: window exceeds the ring capacity, or full attention while the "
-             "context can exceed it";
+      return "ring cache: window exceeds the ring capacity, full attention while the "
+             "context can exceed it, or (several tokens) window + tokens - 1 exceeds it";
     case GA_ERR_WORKSPACE: return "workspace missing or smaller than ga_decode_workspace_bytes";
     case GA_ERR_SCALE: return "scale must be finite";
     case GA_ERR_V_MISMATCH: return "v_cache and v_new must both be NULL (K = V) or both set";
@@ -204,6 +247,14 @@ size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window,
   return p.ws_bytes;
 }
 
+size_t ga_decode_multi_workspace_bytes(const ga_shape* shape, int32_t num_tokens, int32_t window,
+                                       const ga_decode_opts* opts) {
+  if (check_shape(shape, window, num_tokens) != GA_OK) return SIZE_MAX;
+  Plan p;
+  if (make_plan(shape, window, opts, -1, &p, num_tokens) != GA_OK) return SIZE_MAX;
+  return p.ws_bytes;
+}
+
 }  // extern "C"
 
 namespace {
@@ -213,8 +264,8 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
                     const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* new_pos,
                     const int32_t* ctx_lens, const int32_t* q_pos, int32_t window, float softcap,
                     float scale, float* out, void* workspace, size_t workspace_bytes,
-                    const ga_decode_opts* opts, void* stream) {
-  int32_t st = check_shape(shape, window);
+                    const ga_decode_opts* opts, void* stream, int32_t T = 1) {
+  int32_t st = check_shape(shape, window, T);
   if (st != GA_OK) return st;
   if (!q || !k_cache || !ctx_lens || !q_pos || !out) return GA_ERR_NULL;
   if (k_new) {
@@ -228,7 +279,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   if (!std::isfinite(scale)) return GA_ERR_SCALE;
   const bool k_eq_v = v_cache == nullptr || v_cache == k_cache;
   Plan p;
-  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p);
+  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p, T);
   if (st != GA_OK) return st;
   const int D = shape->head_dim;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return GA_ERR_WORKSPACE;
@@ -254,7 +305,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
     a.part_ml = ws + slots * 16 * D;
     a.plan = reinterpret_cast<int*>(a.part_ml + slots * 16 * 2);
   } else if (p.n_split > 1) {
-    const size_t n_acc = (size_t)shape->batch * shape->num_q_heads * (size_t)p.n_split * D;
+    const size_t n_acc = (size_t)shape->batch * T * shape->num_q_heads * (size_t)p.n_split * D;
     a.part_acc = ws;
     a.part_ml = ws + n_acc;
   }
@@ -274,6 +325,11 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   a.max_keys = p.max_keys;
   a.n_waves = p.n_waves;
   a.deterministic = opts ? opts->deterministic : 0;
+  a.T = p.T;
+  a.Tc = p.Tc;
+  a.n_chunks = p.n_chunks;
+  a.Gh = shape->num_q_heads / shape->num_kv_heads;
+  a.max_union = p.max_keys;
   a.k_new = k_new;
   a.v_new = k_eq_v ? nullptr : v_new;
   a.new_pos = k_new ? new_pos : nullptr;
@@ -339,7 +395,7 @@ int32_t gemma_kv_append(const ga_shape* shape, ga_bf16* k_cache, ga_bf16* v_cach
     return GA_ERR_NULL;
   int32_t st = check_arch();
   if (st != GA_OK) return st;
-  hipError_t e = ga::append_launch(shape->batch, shape->num_kv_heads, shape->head_dim,
+  hipError_t e = ga::append_launch(shape->batch, 1, shape->num_kv_heads, shape->head_dim,
                                    shape->capacity, shape->kind, k_cache, v_cache, k_new, v_new,
                                    pos, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
@@ -353,8 +409,57 @@ int32_t gemma_attn_validate(const ga_shape* shape, const int32_t* ctx_lens, cons
   st = check_arch();
   if (st != GA_OK) return st;
   const int max_ctx = shape->max_ctx == 0 ? shape->capacity : shape->max_ctx;
-  hipError_t e = ga::validate_launch(shape->batch, shape->capacity, shape->kind, window, max_ctx,
-                                     ctx_lens, q_pos, dev_flags, static_cast<hipStream_t>(stream));
+  hipError_t e = ga::validate_launch(shape->batch, 1, shape->capacity, shape->kind, window,
+                                     max_ctx, ctx_lens, q_pos, dev_flags,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_attn_decode_multi(const ga_shape* shape, int32_t num_tokens, const ga_bf16* q,
+                                const ga_bf16* k_cache, const ga_bf16* v_cache,
+                                const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
+                                float softcap, float scale, float* out, void* workspace,
+                                size_t workspace_bytes, const ga_decode_opts* opts,
+                                void* stream) {
+  return decode_impl(shape, q, const_cast<ga_bf16*>(k_cache), const_cast<ga_bf16*>(v_cache),
+                     nullptr, nullptr, nullptr, ctx_lens, q_pos, window, softcap, scale, out,
+                     workspace, workspace_bytes, opts, stream, num_tokens);
+}
+
+int32_t gemma_kv_append_multi(const ga_shape* shape, int32_t num_tokens, ga_bf16* k_cache,
+                              ga_bf16* v_cache, const ga_bf16* k_new, const ga_bf16* v_new,
+                              const int32_t* pos, void* stream) {
+  if (!shape) return GA_ERR_NULL;
+  if (shape->batch < 0 || shape->num_kv_heads <= 0 || shape->num_q_heads <= 0 ||
+      shape->capacity <= 0 || num_tokens < 1)
+    return GA_ERR_DIMS;
+  if (num_tokens > kMaxTokens) return GA_ERR_TOO_LARGE;
+  if (!head_dim_ok(shape->head_dim)) return GA_ERR_HEAD_DIM;
+  if (shape->kind != GA_CACHE_LINEAR && shape->kind != GA_CACHE_RING) return GA_ERR_KIND;
+  if (!k_cache || !k_new || !pos) return GA_ERR_NULL;
+  if ((v_cache == nullptr) != (v_new == nullptr)) return GA_ERR_V_MISMATCH;
+  if (!aligned16(k_cache) || !aligned16(k_new) || !aligned16(v_cache) || !aligned16(v_new))
+    return GA_ERR_NULL;
+  int32_t st = check_arch();
+  if (st != GA_OK) return st;
+  hipError_t e = ga::append_launch(shape->batch, num_tokens, shape->num_kv_heads,
+                                   shape->head_dim, shape->capacity, shape->kind, k_cache,
+                                   v_cache, k_new, v_new, pos, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_attn_validate_multi(const ga_shape* shape, int32_t num_tokens,
+                                  const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
+                                  int32_t* dev_flags, void* stream) {
+  int32_t st = check_shape(shape, window, num_tokens);
+  if (st != GA_OK) return st;
+  if (!ctx_lens || !q_pos || !dev_flags) return GA_ERR_NULL;
+  st = check_arch();
+  if (st != GA_OK) return st;
+  const int max_ctx = shape->max_ctx == 0 ? shape->capacity : shape->max_ctx;
+  hipError_t e = ga::validate_launch(shape->batch, num_tokens, shape->capacity, shape->kind,
+                                     window, max_ctx, ctx_lens, q_pos, dev_flags,
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
 }
 

@@ -57,7 +57,10 @@ struct ValuCfg {
   static_assert(NCH >= 1 && DPL % 8 == 0, "lane slice must be whole 16-byte chunks");
 };
 
-template <int D, int G, int NW_, bool KV_SHARED>
+// G is the number of query rows a unit serves: the query heads of one KV head (one
+// token), or with MULTI those heads for each of the Tc tokens of a chunk (row hh is
+// token hh / Gh, head hh % Gh), every row masked at its own position.
+template <int D, int G, int NW_, bool KV_SHARED, bool MULTI>
 __global__ void __launch_bounds__(NW_ * 64)
     decode_valu_kernel(DecodeArgs a) {
   using C = ValuCfg<D, G, NW_>;
@@ -77,35 +80,68 @@ __global__ void __launch_bounds__(NW_ * 64)
   int bid = blockIdx.x;
   const int split = bid % S;
   bid /= S;
+  int chunk = 0;
+  if constexpr (MULTI) {
+    chunk = bid % a.n_chunks;
+    bid /= a.n_chunks;
+  }
   const int g = bid % a.Hkv;
   const int b = bid / a.Hkv;
   const int h0 = g * G;
+
+  // Query row hh of this unit: its token, whether it exists, and its row index in q /
+  // out / the partials ([B, Hq] rows, or [B, T, Hq] rows with MULTI).
+  auto row_token = [&](int hh) { return MULTI ? chunk * a.Tc + hh / a.Gh : 0; };
+  auto row_active = [&](int hh) { return !MULTI || row_token(hh) < a.T; };
+  auto row_index = [&](int hh) -> size_t {
+    if constexpr (!MULTI) return (size_t)b * a.Hq + h0 + hh;
+    const int t = min(row_token(hh), a.T - 1);  // inactive rows alias the last token
+    return ((size_t)b * a.T + t) * a.Hq + (size_t)g * a.Gh + hh % a.Gh;
+  };
 
   // Fused append: split 0 of each unit moves the new row; its loads are issued here and
   // the stores happen after the key loop, so nothing waits on them.
   const int new_slot = appended_slot(a, b);
   AppendRow app;
   app.load(a, b, g, new_slot, threadIdx.x, split == 0);
-  const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const RowRange r = unit_range(a, b, chunk);
   const int k_begin = split * a.split_keys;
   const int k_end = min(r.n, k_begin + a.split_keys);
   if (k_begin >= k_end) {
-    if (S == 1) {  // the only split of an empty row: the output is 0
+    if (S == 1) {  // the only split of an empty unit: the output is 0
       for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
-        a.out[((size_t)b * a.Hq + h0) * D + idx] = 0.0f;
+        if (row_active(idx / D)) a.out[row_index(idx / D) * D + idx % D] = 0.0f;
     }
     app.store(a);
-    return;  // with S > 1 the merge never reads splits past the row's end
+    return;  // with S > 1 the merge never reads splits past the unit's end
   }
   __shared__ int s_next;  // next wave-step to hand out
   if (threadIdx.x == 0) s_next = 0;
   __syncthreads();
 
+  // MULTI: each row's own valid positions [row_lo, row_hi] (empty: lo > hi).
+  int row_lo[MULTI ? G : 1], row_hi[MULTI ? G : 1];
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      row_lo[hh] = 1;
+      row_hi[hh] = 0;
+      if (row_active(hh)) {
+        const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + row_token(hh), a.window, a.kind,
+                                      a.cap, a.max_keys);
+        if (rr.n > 0) {
+          row_lo[hh] = rr.lo;
+          row_hi[hh] = rr.hi;
+        }
+      }
+    }
+  }
+
   // Query heads of this KV head, as packed bf16 pairs, in this lane's element order.
   uint32_t qr[G][DPL / 2];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D);
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + row_index(hh) * D);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const uint4 v = qp[c * L + j];
@@ -169,6 +205,7 @@ __global__ void __launch_bounds__(NW_ * 64)
   auto compute = [&](const uint4(&kr)[NCH], const uint4(&vr)[NCH], int step) {
     const int i = k_begin + step * GPW + grp;
     const bool valid = i < k_end;
+    const int pos = r.lo + i;  // absolute position of the key (MULTI masks)
     float s[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -185,9 +222,11 @@ __global__ void __launch_bounds__(NW_ * 64)
     float p[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
+      bool vh = valid;
+      if constexpr (MULTI) vh = vh && pos >= row_lo[hh] && pos <= row_hi[hh];
       float x = s[hh] * scale;
       if (softcap > 0.0f) x = softcap_tanh(x, softcap, inv_softcap);
-      x = valid ? x * kLog2e : -INFINITY;
+      x = vh ? x * kLog2e : -INFINITY;
       if (x > m[hh] + kRescaleLog2) {
         const float f = exp2_fast(m[hh] - x);  // 0 on the first key (m = -inf)
         l[hh] *= f;
@@ -195,7 +234,7 @@ __global__ void __launch_bounds__(NW_ * 64)
         for (int e = 0; e < DPL; ++e) acc[hh][e] *= f;
         m[hh] = x;
       }
-      p[hh] = valid ? exp2_fast(x - m[hh]) : 0.0f;
+      p[hh] = vh ? exp2_fast(x - m[hh]) : 0.0f;
       l[hh] += p[hh];
     }
     const uint4(&vv)[NCH] = KV_SHARED ? kr : vr;
@@ -281,6 +320,7 @@ __global__ void __launch_bounds__(NW_ * 64)
 
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int hh = idx / D, d = idx % D;
+    if (!row_active(hh)) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hh]);
@@ -291,7 +331,7 @@ __global__ void __launch_bounds__(NW_ * 64)
       Lsum += s_l[w][hh] * f;
       o += s_acc[w][hh][d] * f;
     }
-    const size_t bh = (size_t)b * a.Hq + h0 + hh;
+    const size_t bh = row_index(hh);
     if (S == 1) {
       a.out[bh * D + d] = Lsum > 0.0f ? o / Lsum : 0.0f;
     } else {
@@ -306,14 +346,20 @@ __global__ void __launch_bounds__(NW_ * 64)
 
 template <int D, int G, int NW>
 hipError_t launch_dgw(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
-  const long long blocks = (long long)a.B * a.Hkv * a.n_split;
+  const long long blocks = (long long)a.B * a.Hkv * a.n_chunks * a.n_split;
   if (blocks <= 0) return hipSuccess;
-  if (k_eq_v)
-    hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, true>), dim3((unsigned)blocks), dim3(NW * 64),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, false>), dim3((unsigned)blocks),
-                       dim3(NW * 64), 0, stream, a);
+  const dim3 grid((unsigned)blocks), block(NW * 64);
+  if (a.T > 1) {
+    if (k_eq_v)
+      hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (k_eq_v)
+      hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -328,7 +374,7 @@ hipError_t launch_dg(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
-  switch (a.Hq / a.Hkv) {
+  switch (a.Gh * a.Tc) {  // query rows per unit
     case 1: return launch_dg<D, 1>(a, k_eq_v, stream);
     case 2: return launch_dg<D, 2>(a, k_eq_v, stream);
     case 4: return launch_dg<D, 4>(a, k_eq_v, stream);

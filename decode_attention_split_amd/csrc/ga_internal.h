@@ -5,20 +5,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ga_device.h"
 #include "gemma_attn.h"
 
 namespace ga {
 
 // Everything a split-decode launch needs; plain values and device pointers.
 struct DecodeArgs {
-  const uint16_t* q;      // [B, Hq, D]
+  const uint16_t* q;      // [B, Hq, D]  (multi-token: [B, T, Hq, D])
   const uint16_t* k;      // [B, Hkv, cap, D]
   const uint16_t* v;      // same, or == k when K = V
   const int32_t* ctx;     // [B]
-  const int32_t* q_pos;   // [B]
-  float* out;             // [B, Hq, D]
-  float* part_acc;        // [B, Hq, S, D]   (unused when S == 1)
-  float* part_ml;         // [B, Hq, S, 2]   (m in log2 units, l)
+  const int32_t* q_pos;   // [B]  (multi-token: position of token 0; token t at + t)
+  float* out;             // [B, Hq, D]  (multi-token: [B, T, Hq, D])
+  float* part_acc;        // [rows, S, D]   (unused when S == 1; rows = B * T * Hq)
+  float* part_ml;         // [rows, S, 2]   (m in log2 units, l)
   int B, Hq, Hkv, D, cap, kind, window;
   float scale;            // query scale on the fp32 dot product
   float softcap;          // > 0: on
@@ -36,7 +37,45 @@ struct DecodeArgs {
   uint16_t* k_dst;        // == k, writable
   uint16_t* v_dst;        // == v, writable (nullptr for K = V)
   int deterministic;      // vector path: fixed step order (bit-reproducible sums)
+  // Multi-token decode: T query tokens per row, handled in chunks of Tc tokens; a unit
+  // (b, g, chunk) walks the union of its tokens' key ranges (at most max_union keys).
+  int T = 1, Tc = 1, n_chunks = 1;
+  int Gh = 1;             // query heads per KV head (Hq / Hkv)
+  int max_union = 0;
 };
+
+// Key range a decode unit walks.  One token: that row's range.  Several tokens: the
+// union of the ranges of tokens t0 = chunk * Tc .. t1 of batch row b.  Each token's
+// range is an interval whose ends never decrease with the position and move by at most
+// one per token, so the union of the non-empty ones is one interval.  It lies inside
+// the cache's present positions (ring: ctx - W .. ctx - 1), so its slots wrap at most
+// once.  Longer than max_union only when preconditions are violated: then it keeps its
+// newest keys, as row_range does.
+__device__ __forceinline__ RowRange unit_range(const DecodeArgs& a, int b, int chunk) {
+  if (a.T == 1) return row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const int ctx = a.ctx[b], q0 = a.q_pos[b];
+  const int t0 = chunk * a.Tc;
+  const int t1 = min(a.T, t0 + a.Tc) - 1;
+  int lo = 0, hi = -1;
+  for (int t = t0; t <= t1; ++t) {
+    const RowRange r = row_range(ctx, q0 + t, a.window, a.kind, a.cap, a.max_keys);
+    if (r.n <= 0) continue;
+    if (hi < lo) lo = r.lo;  // first non-empty token
+    hi = r.hi;
+  }
+  int n = hi - lo + 1;
+  if (n < 0) n = 0;
+  if (n > a.max_union) {
+    lo = hi - a.max_union + 1;
+    n = a.max_union;
+  }
+  RowRange u;
+  u.lo = lo;
+  u.hi = n > 0 ? hi : lo - 1;
+  u.n = n;
+  u.slot_lo = n > 0 ? (a.kind == GA_CACHE_RING ? lo % a.cap : lo) : 0;
+  return u;
+}
 
 // Fused append: the physical slot the appended token of batch row b goes to, or -1 when
 // nothing is appended (no fused append, or a position out of range, which the plain
@@ -104,12 +143,15 @@ size_t decode_mfma_workspace_bytes(int B, int Hkv);  // partials + plan
 
 hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream);
 
-hipError_t append_launch(int B, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
+// T tokens per row at positions pos[b] + t (T = 1: the single-token append).
+hipError_t append_launch(int B, int T, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
                          uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* pos, hipStream_t stream);
 
-hipError_t validate_launch(int B, int cap, int kind, int window, int max_ctx, const int32_t* ctx,
-                           const int32_t* q_pos, int32_t* flags, hipStream_t stream);
+// Flags of the B * T query tokens at positions q_pos[b] + t.
+hipError_t validate_launch(int B, int T, int cap, int kind, int window, int max_ctx,
+                           const int32_t* ctx, const int32_t* q_pos, int32_t* flags,
+                           hipStream_t stream);
 hipError_t ranges_launch(int B, int cap, int kind, int window, int max_keys, const int32_t* ctx,
                          const int32_t* q_pos, int32_t* out, hipStream_t stream);
 

@@ -10,7 +10,7 @@ namespace {
 // Split s of row (b, h) left m_s (log2 units), l_s = sum 2^(s2 - m_s) and
 // acc_s = sum 2^(s2 - m_s) v.  With M = max m_s:
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   out = 0 for an empty row.
-// One work-group per (b, h); the row's split count comes from the same row_range the
+// One work-group per row; the row's split count comes from the same unit_range the
 // split kernel used, so exactly the splits that were written are read.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeMaxSplitsLds = 1024;
@@ -18,11 +18,12 @@ constexpr int kMergeMaxSplitsLds = 1024;
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   __shared__ float s_w[kMergeMaxSplitsLds];
   __shared__ float s_red[2][kMergeThreads / 64];
-  const size_t bh = blockIdx.x;
-  const int b = (int)(bh / a.Hq);
+  const size_t bh = blockIdx.x;  // row (b, h), or (b, t, h) with several tokens
+  const int b = (int)(bh / ((size_t)a.T * a.Hq));
+  const int t = (int)(bh / a.Hq % a.T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.n_split, D = a.D;
-  const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const RowRange r = unit_range(a, b, t / a.Tc);
   const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S
   float* out = a.out + bh * D;
   if (ns == 0) {
@@ -40,8 +41,14 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[0][w]);
   // split weights 2^(m_s - M) into LDS, and L = sum_s l_s 2^(m_s - M)
   float lsum = 0.0f;
+  // With several tokens a split may hold no key of this row (m = -inf): weight 0; a row
+  // with no key at all (M = -inf) gives 0.
+  auto split_weight = [&](int s) {
+    const float ms = ml[2 * s];
+    return ms == -INFINITY ? 0.0f : exp2_fast(ms - M);
+  };
   for (int s = tid; s < ns; s += kMergeThreads) {
-    const float w = exp2_fast(ml[2 * s] - M);
+    const float w = split_weight(s);
     if (s < kMergeMaxSplitsLds) s_w[s] = w;
     lsum += ml[2 * s + 1] * w;
   }
@@ -51,9 +58,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   float Lsum = 0.0f;
 #pragma unroll
   for (int w = 0; w < kMergeThreads / 64; ++w) Lsum += s_red[1][w];
-  const float inv = 1.0f / Lsum;
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   const float* acc = a.part_acc + bh * S * D;
-  auto weight = [&](int s) { return s < kMergeMaxSplitsLds ? s_w[s] : exp2_fast(ml[2 * s] - M); };
+  auto weight = [&](int s) { return s < kMergeMaxSplitsLds ? s_w[s] : split_weight(s); };
   for (int d = tid; d < D; d += kMergeThreads) {
     float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
     int s = 0;
@@ -68,30 +75,36 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   }
 }
 
-// Cache append: one lane per 16-byte chunk of a new row; bit-exact copies.
-__global__ void append_kernel(int B, int Hkv, int D, int cap, int kind, uint4* k_cache,
+// Cache append: one lane per 16-byte chunk of a new row; bit-exact copies.  T tokens
+// per row sit at positions pos[b] + t; one lane writes its chunk for t = 0..T-1 in order,
+// so when two tokens land in the same ring slot the later one stays.
+__global__ void append_kernel(int B, int T, int Hkv, int D, int cap, int kind, uint4* k_cache,
                               uint4* v_cache, const uint4* k_new, const uint4* v_new,
                               const int32_t* pos) {
   const int chunks = D / 8;
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (long long)B * Hkv * chunks) return;
-  const int c = (int)(t % chunks);
-  const long long bg = t / chunks;
-  const int b = (int)(bg / Hkv);
-  const int p = pos[b];
-  if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) return;  // out of range: skipped
-  const int slot = kind == GA_CACHE_RING ? p % cap : p;
-  const size_t dst = ((size_t)bg * cap + slot) * chunks + c;
-  const size_t src = (size_t)bg * chunks + c;
-  k_cache[dst] = k_new[src];
-  if (v_cache) v_cache[dst] = v_new[src];
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)B * Hkv * chunks) return;
+  const int c = (int)(i % chunks);
+  const long long bg = i / chunks;
+  const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
+  for (int t = 0; t < T; ++t) {
+    const long long p = (long long)pos[b] + t;
+    if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) continue;  // out of range: skipped
+    const int slot = kind == GA_CACHE_RING ? (int)(p % cap) : (int)p;
+    const size_t dst = ((size_t)bg * cap + slot) * chunks + c;
+    const size_t src = (((size_t)b * T + t) * Hkv + g) * chunks + c;
+    k_cache[dst] = k_new[src];
+    if (v_cache) v_cache[dst] = v_new[src];
+  }
 }
 
-__global__ void validate_kernel(int B, int cap, int kind, int window, int max_ctx,
+// Precondition flags of every query token (b, t) at position q_pos[b] + t.
+__global__ void validate_kernel(int B, int T, int cap, int kind, int window, int max_ctx,
                                 const int32_t* ctx_lens, const int32_t* q_pos, int32_t* flags) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  const long long ctx = ctx_lens[b], qp = q_pos[b];
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)B * T) return;
+  const int b = (int)(i / T), t = (int)(i % T);
+  const long long ctx = ctx_lens[b], qp = (long long)q_pos[b] + t;
   int f = 0;
   if (ctx < 0 || qp < 0) f |= GA_FLAG_NEGATIVE;
   if (qp >= ctx) f |= GA_FLAG_QPOS_GE_CTX;
@@ -102,7 +115,7 @@ __global__ void validate_kernel(int B, int cap, int kind, int window, int max_ct
     if (want_lo < ctx - cap && want_lo <= qp) f |= GA_FLAG_EVICTED;
   }
   if (ctx > max_ctx) f |= GA_FLAG_OVER_MAX_CTX;
-  flags[b] = f;
+  flags[i] = f;
 }
 
 __global__ void ranges_kernel(int B, int cap, int kind, int window, int max_keys,
@@ -119,31 +132,33 @@ __global__ void ranges_kernel(int B, int cap, int kind, int window, int max_keys
 }  // namespace
 
 hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream) {
-  const long long blocks = (long long)a.B * a.Hq;
+  const long long blocks = (long long)a.B * a.T * a.Hq;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t append_launch(int B, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
+hipError_t append_launch(int B, int T, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
                          uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* pos, hipStream_t stream) {
   const long long n = (long long)B * Hkv * (D / 8);
-  if (n <= 0) return hipSuccess;
+  if (n <= 0 || T <= 0) return hipSuccess;
   const int threads = 256;
   const long long blocks = (n + threads - 1) / threads;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, B, Hkv, D,
-                     cap, kind, reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache),
-                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
-                     pos);
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, B, T, Hkv,
+                     D, cap, kind, reinterpret_cast<uint4*>(k_cache),
+                     reinterpret_cast<uint4*>(v_cache), reinterpret_cast<const uint4*>(k_new),
+                     reinterpret_cast<const uint4*>(v_new), pos);
   return hipGetLastError();
 }
 
-hipError_t validate_launch(int B, int cap, int kind, int window, int max_ctx, const int32_t* ctx,
-                           const int32_t* q_pos, int32_t* flags, hipStream_t stream) {
-  if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(validate_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, cap, kind,
-                     window, max_ctx, ctx, q_pos, flags);
+hipError_t validate_launch(int B, int T, int cap, int kind, int window, int max_ctx,
+                           const int32_t* ctx, const int32_t* q_pos, int32_t* flags,
+                           hipStream_t stream) {
+  const long long n = (long long)B * T;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, B,
+                     T, cap, kind, window, max_ctx, ctx, q_pos, flags);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ class Workload:
     ctx_lo: int
     ctx_hi: int
     layers: List[LayerGeom] = field(default_factory=list)
+    tokens: int = 1  # query tokens per row (T > 1: multi-token decode)
 
     @property
     def num_layers(self) -> int:
@@ -145,6 +146,16 @@ ALL = [TINY, G3_1B_SLIDING, G4_12B_SLIDING, G4_12B_GLOBAL, HYBRID_48]
 HD128_SLIDING = Workload("hd128 sliding layer, B64 16q/8kv hd128 ring w1024 ctx U[512,8192]"
                          " softcap50", 6, 64, 512, 8192,
                          [sliding_geom(16, 8, 1024, softcap=50.0, head_dim=128)])
+
+# Speculative verification on the 12B sliding layer: 7 draft tokens plus the current one
+# (T = 8, the k = 7 spec decode of the "Gemma 4 12B (unified multimodal)" record, item
+# "(2)"), each masked at its own position.  The ring keeps w + T - 1 = 1031 slots so the
+# first token's window is still present.
+SPEC_DECODE_SLIDING = Workload("gemma4-12b sliding layer verifying 7 draft tokens (T=8), B64 "
+                               "16q/8kv hd256 ring W=1031 w1024 ctx U[512,8192] softcap50", 7,
+                               64, 512, 8192,
+                               [LayerGeom(16, 8, 256, RING, 1031, 1024, False, 50.0, 1.0 / 16)],
+                               tokens=8)
 
 
 def layer_seed(workload: Workload, layer: int) -> int:

@@ -70,7 +70,8 @@ enum {
   GA_ERR_HEAD_DIM = -3,      /* head_dim is not 128, 256 or 512                           */
   GA_ERR_GQA = -4,           /* num_q_heads is not a multiple of num_kv_heads, or G > 16  */
   GA_ERR_KIND = -5,          /* kind is neither GA_CACHE_LINEAR nor GA_CACHE_RING         */
-  GA_ERR_WINDOW = -6,        /* ring: window > W, or window <= 0 while max_ctx may exceed W */
+  GA_ERR_WINDOW = -6,        /* ring: window > W, or window <= 0 while max_ctx may exceed W,
+                                or (multi-token) window + T - 1 > W while it may           */
   GA_ERR_WORKSPACE = -7,     /* workspace NULL or smaller than ga_decode_workspace_bytes  */
   GA_ERR_SCALE = -8,         /* scale is not finite                                       */
   GA_ERR_V_MISMATCH = -9,    /* exactly one of v_cache / v_new is NULL                    */
@@ -108,10 +109,15 @@ typedef struct ga_decode_opts {
 } ga_decode_opts;
 
 /*
- * Bytes of device workspace gemma_attn_decode needs for this shape, window and options:
- * split partials (m, l, acc) in fp32, [B, Hq, S, D + 2] with S the host upper bound of
- * splits per row.  0 when every row fits in one split (no workspace is touched).
- * Returns SIZE_MAX when the arguments are invalid (the decode call would fail).
+ * Bytes of device workspace gemma_attn_decode needs for this shape, window and options.
+ * Vector path: split partials in fp32, acc [B, Hq, S, D] then (m, l) [B, Hq, S, 2], with
+ * S the host upper bound of splits per row; 0 when every row fits in one split (no
+ * workspace is touched).  Matrix-core path (head_dim 512, 16 query heads per KV head,
+ * K = V): one partial per work-group with work, acc [P, 16, 512] and (m, l) [P, 16, 2]
+ * in fp32 with P = 512 + B * Hkv slots, then the per-unit work-group prefix sums
+ * [B * Hkv + 1] int32.  With GA_IMPL_AUTO and no split size given, the maximum of both,
+ * since the implementation is picked per call.  Returns SIZE_MAX when the arguments
+ * are invalid (the decode call would fail).
  */
 size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window, const ga_decode_opts* opts);
 
@@ -174,6 +180,44 @@ int32_t gemma_kv_append(const ga_shape* shape, ga_bf16* k_cache, ga_bf16* v_cach
                         const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
                         void* stream);
 
+/*
+ * Multi-token decode: T = num_tokens consecutive query tokens per sequence (speculative
+ * verification of T - 1 draft tokens, or a chunk of prefill) against the same cache,
+ * each token masked at its own position.  Token t of row b sits at position
+ * q_pos[b] + t and attends to the positions p with
+ *     max(0, q_pos[b] + t - window + 1 [window > 0], ctx_b - W [ring]) <= p
+ *     p <= min(q_pos[b] + t, ctx_b - 1)      (linear also p < C),
+ * i.e. exactly the single-token definition applied per token.  Passages: "Gemma
+ * support" pull request, Performance (flash prefill for head_dim 256, split decode) and
+ * the spec-decode (k = 7) with sliding-window item "(2)" of the "Gemma 4 12B (unified
+ * multimodal)" record, where a kernel mis-selected the window's keys at some
+ * seq_len / page alignments.
+ *   q        device bf16 [B, T, Hq, D]        out  device float32 [B, T, Hq, D]
+ *   q_pos    device int32 [B]: position of token 0 (usually ctx - T after appending)
+ *   other arguments as in gemma_attn_decode_ex (GA_IMPL_MFMA is not offered here).
+ * Ring caches: when the context can exceed W (max_ctx > W) the ring must keep
+ * window + T - 1 slots (token 0's window begins T - 1 positions before token T-1's);
+ * a smaller ring is refused with GA_ERR_WINDOW.  Work: each unit (b, KV head, chunk of
+ * tokens) reads the union of its tokens' key ranges once.  T = 1 is gemma_attn_decode_ex.
+ */
+size_t ga_decode_multi_workspace_bytes(const ga_shape* shape, int32_t num_tokens, int32_t window,
+                                       const ga_decode_opts* opts);
+int32_t gemma_attn_decode_multi(const ga_shape* shape, int32_t num_tokens, const ga_bf16* q,
+                                const ga_bf16* k_cache, const ga_bf16* v_cache,
+                                const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
+                                float softcap, float scale, float* out, void* workspace,
+                                size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
+
+/*
+ * Append of T = num_tokens tokens per sequence at positions pos[b] + t, t = 0..T-1, in
+ * that order (when two tokens land in the same ring slot the later one stays).
+ *   k_new, v_new device bf16 [B, T, Hkv, D]; pos device int32 [B].
+ * Out-of-range positions are skipped, as in gemma_kv_append (its T = 1 case).
+ */
+int32_t gemma_kv_append_multi(const ga_shape* shape, int32_t num_tokens, ga_bf16* k_cache,
+                              ga_bf16* v_cache, const ga_bf16* k_new, const ga_bf16* v_new,
+                              const int32_t* pos, void* stream);
+
 /* Precondition flags written by gemma_attn_validate, per batch row. */
 enum {
   GA_FLAG_QPOS_GE_CTX = 1, /* q_pos >= ctx                                         */
@@ -189,6 +233,12 @@ enum {
  */
 int32_t gemma_attn_validate(const ga_shape* shape, const int32_t* ctx_lens, const int32_t* q_pos,
                             int32_t window, int32_t* dev_flags, void* stream);
+
+/* gemma_attn_validate for T = num_tokens tokens per row at q_pos[b] + t: dev_flags is
+ * device int32 [B, T]. */
+int32_t gemma_attn_validate_multi(const ga_shape* shape, int32_t num_tokens,
+                                  const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
+                                  int32_t* dev_flags, void* stream);
 
 /*
  * Debug dump of the key range each row attends to, computed by the same device code

@@ -182,3 +182,61 @@ def test_append_and_debug_calls_without_a_gpu():
     assert lib.gemma_attn_validate(ctypes.byref(s), P(FAKE), P(FAKE), 1024, P(FAKE), None) == -10
     assert lib.gemma_attn_debug_ranges(ctypes.byref(s), P(FAKE), P(FAKE), 1024, P(FAKE),
                                        None) == -10
+
+
+# ------------------------------------------------------------------ multi-token entry points
+
+def call_decode_multi(s, T, window=1024, ws=FAKE, ws_bytes=1 << 40, opts=None, v=FAKE):
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    return lib.gemma_attn_decode_multi(ctypes.byref(s), T, P(FAKE), P(FAKE), P(v) if v else None,
+                                       P(FAKE), P(FAKE), window, 0.0, 0.0625, P(FAKE),
+                                       P(ws) if ws else None, ws_bytes,
+                                       ctypes.byref(opts) if opts else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=shape(), T=0), -2),                                   # no tokens
+    (dict(s=shape(), T=5000), -14),                               # beyond the token limit
+    # ring of W = w = 1024 that the context can overrun: 8 tokens need 1031 slots
+    (dict(s=shape(cap=1024, max_ctx=8192), T=8), -6),
+    (dict(s=shape(cap=1031, max_ctx=8192), T=8, ws=0, ws_bytes=0), -7),
+    (dict(s=shape(cap=1031, max_ctx=8192), T=8, opts=api.make_opts(impl=api.IMPL_MFMA)), -12),
+    (dict(s=shape(cap=1031, max_ctx=8192), T=8, opts=api.make_opts(split_keys=100)), -12),
+])
+def test_decode_multi_rejects_bad_arguments_before_any_launch(kw, code):
+    assert call_decode_multi(**kw) == code
+
+
+@pytest.mark.skipif(not no_gpu(), reason="checks the no-device path")
+def test_valid_decode_multi_without_a_gpu_reports_arch_error():
+    # a ring of exactly w slots is fine while the context cannot exceed it
+    assert call_decode_multi(shape(cap=1024, max_ctx=1024), 8) == -10
+    assert call_decode_multi(shape(cap=1031, max_ctx=8192), 8) == -10
+
+
+def test_multi_workspace_closed_form():
+    """B 4, 16q/8kv (G = 2), hd256, ring 1031 for w 1024, T = 8 tokens: 4 tokens per unit
+    (2 heads x 4 tokens = 8 rows), 2 chunks; a unit's keys are at most w + 4 - 1 = 1027;
+    64 units want 4 splits of ceil(1027 / 4) = 257 -> 320 keys, S = ceil(1027 / 320) = 4.
+    Partials: B * T * Hq * S * (D + 2) floats."""
+    lib = _lib.load()
+    s = shape(B=4, cap=1031, max_ctx=8192)
+    n = lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, None)
+    assert n == 4 * 8 * 16 * 4 * (256 + 2) * 4
+    # T = 1 is the single-token plan
+    o = api.make_opts()
+    assert lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 1, 1024, ctypes.byref(o)) == \
+        lib.ga_decode_workspace_bytes(ctypes.byref(s), 1024, ctypes.byref(o))
+
+
+def test_append_multi_argument_checks():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    s = shape()
+    assert lib.gemma_kv_append_multi(ctypes.byref(s), 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                     P(FAKE), None) == -2
+    assert lib.gemma_kv_append_multi(ctypes.byref(s), 4, P(FAKE), None, P(FAKE), P(FAKE),
+                                     P(FAKE), None) == -9
+    assert lib.gemma_attn_validate_multi(ctypes.byref(shape(cap=1024, max_ctx=8192)), 8, P(FAKE),
+                                         P(FAKE), 1024, P(FAKE), None) == -6

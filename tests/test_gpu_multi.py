@@ -1,0 +1,190 @@
+"""GPU: multi-token decode (T query tokens per row, each masked at its own position), the
+T-token append and the per-token precondition flags, against the fp64 oracle.
+
+Parity cases poison every slot outside the union of a row's tokens' valid sets with bf16
+NaN, so a stray read shows up as a NaN output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_split_amd import api, synth
+
+from common import BF16_NAN, assert_parity, default_scale, log
+
+pytestmark = pytest.mark.gpu
+
+
+class MultiInputs:
+    def __init__(self, seed, B, T, Hq, Hkv, D, cap, k_eq_v, ctx, q0=None):
+        gen = synth.generator(seed)
+        self.q_bits = synth.bits(synth.normal_bf16(gen, (B, T, Hq, D)))
+        self.k_bits = synth.bits(synth.normal_bf16(gen, (B, Hkv, cap, D)))
+        self.v_bits = None if k_eq_v else synth.bits(synth.normal_bf16(gen, (B, Hkv, cap, D)))
+        self.ctx = np.asarray(ctx, np.int32)
+        self.q0 = self.ctx - T if q0 is None else np.asarray(q0, np.int32)
+        self.T, self.cap = T, cap
+
+    def poison(self, window, kind):
+        for bits in [self.k_bits] + ([self.v_bits] if self.v_bits is not None else []):
+            for b in range(bits.shape[0]):
+                keep = np.zeros(self.cap, bool)
+                for t in range(self.T):
+                    _, slots = oracle.valid_positions(self.ctx[b], self.q0[b] + t, window, kind,
+                                                      self.cap)
+                    keep[slots] = True
+                bits[b][:, ~keep, :] = BF16_NAN
+        return self
+
+    def to_device(self):
+        self.q = synth.from_bits(self.q_bits, "cuda")
+        self.k = synth.from_bits(self.k_bits, "cuda")
+        self.v = None if self.v_bits is None else synth.from_bits(self.v_bits, "cuda")
+        self.ctx_t = torch.from_numpy(self.ctx.copy()).cuda()
+        self.q0_t = torch.from_numpy(self.q0.copy()).cuda()
+        return self
+
+    def oracle(self, window, softcap, scale, kind, rows=None):
+        rows = np.arange(self.q_bits.shape[0]) if rows is None else np.asarray(rows)
+        out, _, _, flags = oracle.decode_multi(
+            self.q_bits[rows], self.k_bits[rows],
+            None if self.v_bits is None else self.v_bits[rows], self.ctx[rows], self.q0[rows],
+            window, softcap, scale, kind)
+        return out, flags
+
+    def run(self, window, softcap, scale, kind, **kw):
+        out = api.decode_multi(self.q, self.k, self.v, self.ctx_t, self.q0_t, window, softcap,
+                               scale, kind, **kw)
+        torch.cuda.synchronize()
+        return out
+
+
+@pytest.mark.parametrize("D,G,Hkv", [(128, 2, 2), (256, 1, 2), (256, 2, 4), (256, 4, 1),
+                                     (512, 8, 1), (512, 16, 1), (128, 16, 1)])
+@pytest.mark.parametrize("T", [2, 5, 8])
+@pytest.mark.parametrize("kind", [api.RING, api.LINEAR])
+def test_multi_token_parity_sweep(D, G, Hkv, T, kind):
+    """Several splits, chunks of tokens and ragged tails; rows whose first tokens precede
+    the sequence start (negative positions attend to nothing)."""
+    w = 96
+    if kind == api.RING:
+        cap, window = w + T - 1, w
+        ctx = [1, T, w, w + 1, 3 * cap + 5]
+        max_ctx = max(ctx)
+    else:
+        cap, window = 400, (w if G % 2 == 0 else 0)
+        ctx = [1, T, 150, 399, 400]
+        max_ctx = cap
+    k_eq_v = (G == 16)
+    inp = MultiInputs(D * 10 + G * 100 + T, len(ctx), T, G * Hkv, Hkv, D, cap, k_eq_v, ctx)
+    inp.poison(window, kind).to_device()
+    softcap = 30.0 if T % 2 == 0 else 0.0
+    ref, _ = inp.oracle(window, softcap, default_scale(D), kind)
+    for split in [0, 64]:
+        out = inp.run(window, softcap, default_scale(D), kind, max_ctx=max_ctx, split_keys=split)
+        assert_parity(out, ref, f"D={D} G={G} T={T} kind={kind} split={split}")
+
+
+@pytest.mark.parametrize("W", [64, 1024])
+def test_multi_token_window_edges(W):
+    """Draft tokens straddling multiples of the window and of the ring: where a
+    spec-decode kernel mis-selected sliding-window keys at certain seq_len alignments."""
+    T = 8
+    w = W
+    cap = w + T - 1
+    ctxs = [T, w - 1, w, w + 1, w + T - 1, 2 * w, 2 * w + 3, 3 * w + T, 5 * w - 1]
+    inp = MultiInputs(W + 7, len(ctxs), T, 16, 8, 256, cap, False, ctxs)
+    inp.poison(w, api.RING).to_device()
+    ref, flags = inp.oracle(w, 50.0, 1.0 / 16, api.RING)
+    assert not flags.any()
+    for split in [0, 64, 256]:
+        out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=max(ctxs), split_keys=split)
+        assert_parity(out, ref, f"W={W} split={split}")
+
+
+def test_multi_token_causal_inside_the_cache():
+    """Query tokens below the newest cached position (q_pos + T < ctx): each token still
+    sees only positions up to its own."""
+    T = 4
+    ctx = [50, 300, 300]
+    q0 = [10, 0, 250]
+    inp = MultiInputs(17, 3, T, 8, 2, 256, 300, False, ctx, q0)
+    inp.poison(0, api.LINEAR).to_device()
+    ref, _ = inp.oracle(0, 0.0, 0.0625, api.LINEAR)
+    out = inp.run(0, 0.0, 0.0625, api.LINEAR, max_ctx=300)
+    assert_parity(out, ref, "causal inside")
+
+
+def test_multi_T1_equals_single_token_decode_bitwise():
+    inp = MultiInputs(21, 4, 1, 16, 8, 256, 128, False, [1, 64, 128, 200])
+    inp.poison(128, api.RING).to_device()
+    a = inp.run(128, 0.0, 0.0625, api.RING, max_ctx=200, deterministic=True)
+    b = api.decode(inp.q[:, 0].contiguous(), inp.k, inp.v, inp.ctx_t, inp.q0_t, 128, 0.0, 0.0625,
+                   api.RING, max_ctx=200, deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, 0], b)
+
+
+def test_spec_decode_sliding_layer_full_size_sampled_rows():
+    """The 12B sliding layer verifying 7 draft tokens (T = 8): B 64, ring of 1031 slots,
+    window 1024, ctx U[512, 8192]."""
+    T, w = 8, 1024
+    gen = synth.generator(3)
+    ctx = synth.uniform_int(gen, 64, 512, 8192).numpy().astype(np.int32)
+    inp = MultiInputs(33, 64, T, 16, 8, 256, w + T - 1, False, ctx).to_device()
+    out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=8192)
+    rows = sorted({0, 1, int(np.argmax(ctx)), int(np.argmin(ctx))})
+    ref, _ = inp.oracle(w, 50.0, 1.0 / 16, api.RING, rows=rows)
+    log(f"spec decode rows {rows}")
+    assert_parity(out[rows], ref, "spec decode T=8")
+
+
+def test_append_multi_matches_oracle_bitwise():
+    B, T, Hkv, D = 3, 6, 2, 256
+    for kind, cap, pos0 in [(api.RING, 4, [0, 7, 1000]), (api.LINEAR, 16, [-2, 5, 12])]:
+        gen = synth.generator(40 + kind)
+        k = synth.normal_bf16(gen, (B, Hkv, cap, D))
+        v = synth.normal_bf16(gen, (B, Hkv, cap, D))
+        kn = synth.normal_bf16(gen, (B, T, Hkv, D))
+        vn = synth.normal_bf16(gen, (B, T, Hkv, D))
+        ref_k, ref_v = synth.bits(k).copy(), synth.bits(v).copy()
+        if kind == api.RING:
+            oracle.append_tokens(ref_k, synth.bits(kn), np.asarray(pos0, np.int32), kind)
+            oracle.append_tokens(ref_v, synth.bits(vn), np.asarray(pos0, np.int32), kind)
+        else:
+            # the oracle refuses out-of-range positions; the library skips them, so the
+            # expected cache is the definition: write token t at pos0 + t when 0 <= p < C
+            for b in range(B):
+                for t in range(T):
+                    p = pos0[b] + t
+                    if 0 <= p < cap:
+                        ref_k[b, :, p] = synth.bits(kn)[b, t]
+                        ref_v[b, :, p] = synth.bits(vn)[b, t]
+        kd, vd = k.cuda(), v.cuda()
+        api.kv_append_multi(kd, vd, kn.cuda(), vn.cuda(),
+                            torch.tensor(pos0, dtype=torch.int32, device="cuda"), kind)
+        torch.cuda.synchronize()
+        assert np.array_equal(synth.bits(kd.cpu()), ref_k), kind
+        assert np.array_equal(synth.bits(vd.cpu()), ref_v), kind
+
+
+def test_validate_multi_matches_oracle_flags():
+    T, w, W = 4, 8, 8  # a ring of exactly w slots: the first tokens need evicted keys
+    ctx = np.array([5, 8, 30, 0], np.int32)
+    q0 = ctx - T
+    shape = api.make_shape(4, 2, 1, 128, W, api.RING, 30)
+    # the host refuses this ring for decoding T tokens (window + T - 1 > W) ...
+    with pytest.raises(api.GemmaAttnError) as e:
+        api.validate_multi(shape, T, torch.from_numpy(ctx).cuda(), torch.from_numpy(q0).cuda(), w)
+    assert e.value.code == -6
+    # ... and accepts it while the context never exceeds W, flagging per token
+    shape = api.make_shape(4, 2, 1, 128, W, api.RING, 8)
+    ctx = np.array([5, 8, 8, 0], np.int32)
+    q0 = np.array([1, 4, -1, 0], np.int32)
+    flags = api.validate_multi(shape, T, torch.from_numpy(ctx).cuda(),
+                               torch.from_numpy(q0).cuda(), w).cpu().numpy()
+    q = np.zeros((4, T, 2, 128), np.uint16)
+    kc = np.zeros((4, 1, W, 128), np.uint16)
+    _, _, _, ref = oracle.decode_multi(q, kc, None, ctx, q0, w, 0.0, 1.0, oracle.RING)
+    assert np.array_equal(flags & 15, ref), (flags, ref)
