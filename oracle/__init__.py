@@ -55,6 +55,17 @@ def _load():
     lib.oracle_row_flags.restype = i32
     lib.oracle_split_merge_f64.argtypes = [ctypes.c_long, ctypes.c_int, P, P, ctypes.c_int, P, P]
     lib.oracle_split_merge_f64.restype = f64
+    lib.oracle_decode_fp8_multi_f64.argtypes = [ctypes.c_int] * 7 + [P] * 7 + [
+        ctypes.c_int, f32, f32, P, P, P, ctypes.c_long, P, ctypes.c_int]
+    lib.oracle_decode_fp8_multi_f64.restype = ctypes.c_int
+    lib.oracle_append_fp8.argtypes = [ctypes.c_int] * 6 + [P, P, P, P]
+    lib.oracle_append_fp8.restype = ctypes.c_int
+    lib.oracle_quantize_row_fp8.argtypes = [ctypes.c_int, P, P, P]
+    lib.oracle_quantize_row_fp8.restype = None
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f64.restype = f64
+    lib.oracle_f32_to_e4m3.argtypes = [f32]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = f64
     lib.oracle_num_threads_default.restype = ctypes.c_int
@@ -143,6 +154,88 @@ def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos0, window, softcap, scale, 
                                      _ptr(probs), int(probs_len), _ptr(flags), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_decode_multi_f64 failed: {rc}")
+    return out, lse, probs, flags
+
+
+def e4m3_to_f64(code: int) -> float:
+    """Value of an OCP e4m3 (fn) code (NaN for 0x7f / 0xff)."""
+    return _load().oracle_e4m3_to_f64(int(code) & 0xFF)
+
+
+def f32_to_e4m3(x: float) -> int:
+    """Round-to-nearest-even e4m3 code of a float32 value (saturating at +-448)."""
+    return int(_load().oracle_f32_to_e4m3(float(np.float32(x))))
+
+
+def quantize_rows_fp8(x_bits):
+    """Quantize bf16 rows (uint16 bits [..., D]) to (codes uint8 [..., D], scales f32 [...])."""
+    lib = _load()
+    x = _u16(x_bits)
+    D = x.shape[-1]
+    flat = x.reshape(-1, D)
+    codes = np.zeros(flat.shape, np.uint8)
+    scales = np.zeros((flat.shape[0],), np.float32)
+    for r in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[r])
+        c = np.zeros((D,), np.uint8)
+        sc = np.zeros((1,), np.float32)
+        lib.oracle_quantize_row_fp8(D, _ptr(row), _ptr(c), _ptr(sc))
+        codes[r] = c
+        scales[r] = sc[0]
+    return codes.reshape(x.shape), scales.reshape(x.shape[:-1])
+
+
+def append_fp8(codes, scales, new_rows, pos0, kind):
+    """In-place quantizing append of T tokens per row: codes [B,Hkv,cap,D] uint8, scales
+    [B,Hkv,cap] float32, new_rows [B,T,Hkv,D] bf16 bits, token t at pos0[b] + t (out-of-range
+    positions skipped)."""
+    lib = _load()
+    for a, dt in ((codes, np.uint8), (scales, np.float32)):
+        if not (isinstance(a, np.ndarray) and a.flags.c_contiguous and a.dtype == dt):
+            raise TypeError("codes / scales must be C-contiguous uint8 / float32 arrays")
+    new_rows = _u16(new_rows)
+    B, Hkv, cap, D = codes.shape
+    T = new_rows.shape[1]
+    if new_rows.shape != (B, T, Hkv, D) or scales.shape != (B, Hkv, cap):
+        raise ValueError("shape mismatch")
+    rc = lib.oracle_append_fp8(B, T, Hkv, D, cap, int(kind), _ptr(codes), _ptr(scales),
+                               _ptr(new_rows), _ptr(_i32(pos0)))
+    if rc != 0:
+        raise ValueError(f"oracle_append_fp8 failed: {rc}")
+
+
+def decode_fp8_multi(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos0, window, softcap,
+                     scale, kind, probs_len=0, nthreads=0):
+    """decode_multi over fp8 caches (values code * row scale); v_codes None: V = K.
+    q [B,T,Hq,D] bf16 bits (a [B,Hq,D] q is taken as T = 1 and returns [B,Hq,D])."""
+    lib = _load()
+    q = _u16(q)
+    single = q.ndim == 3
+    if single:
+        q = q[:, None]
+    B, T, Hq, D = q.shape
+    k_codes = np.ascontiguousarray(k_codes, np.uint8)
+    k_scales = np.ascontiguousarray(k_scales, np.float32)
+    if v_codes is not None:
+        v_codes = np.ascontiguousarray(v_codes, np.uint8)
+        v_scales = np.ascontiguousarray(v_scales, np.float32)
+    Bk, Hkv, cap, Dk = k_codes.shape
+    if Bk != B or Dk != D or k_scales.shape != (B, Hkv, cap):
+        raise ValueError("shape mismatch")
+    ctx_lens, q_pos0 = _i32(ctx_lens), _i32(q_pos0)
+    out = np.zeros((B, T, Hq, D), np.float64)
+    lse = np.zeros((B, T, Hq), np.float64)
+    probs = np.zeros((B, T, Hq, probs_len), np.float64) if probs_len > 0 else None
+    flags = np.zeros((B, T), np.int32)
+    rc = lib.oracle_decode_fp8_multi_f64(B, T, Hq, Hkv, D, cap, int(kind), _ptr(q), _ptr(k_codes),
+                                         _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                                         _ptr(ctx_lens), _ptr(q_pos0), int(window),
+                                         float(softcap), float(scale), _ptr(out), _ptr(lse),
+                                         _ptr(probs), int(probs_len), _ptr(flags), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_fp8_multi_f64 failed: {rc}")
+    if single:
+        return out[:, 0], lse[:, 0], None if probs is None else probs[:, 0], flags[:, 0]
     return out, lse, probs, flags
 
 

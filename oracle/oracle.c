@@ -38,6 +38,17 @@
  * the window is inclusive of the current token and holds exactly w positions; query
  * head h reads KV head h / G; an empty valid set gives out = 0 and lse = -inf.
  *
+ * Quantized caches (oracle_decode_fp8_multi_f64): each cached row is D fp8 e4m3 codes
+ * (OCP 8-bit float: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, largest finite 448) and one float32 scale; its values are code * scale,
+ * and attention is the same definition over those values.  A row is quantized from
+ * bf16 as: amax = max |x| (float32), inv = 448 / amax (float32, 0 for amax = 0), code =
+ * round-to-nearest-even e4m3 of x * inv (float32 product, clamped to +-448), stored
+ * scale = amax / 448 (float32).  Passages: the fp8_e4m3 KV cache and BF16-Q + FP8-KV
+ * sliding-window item "(2)" and the rotating quantized cache of item "(6)" of the "Gemma
+ * 4 12B (unified multimodal)" record; the per-row dynamic scale is a reading (the pages
+ * give no scale granularity).
+ *
  * Arithmetic: every bf16 input is widened exactly (bits << 16 -> float -> double);
  * scale and softcap are widened from their float32 values; libm exp, tanh, log in
  * double.  Results are double; callers round to float32 where they need to.
@@ -114,6 +125,10 @@ int64_t oracle_valid_positions(int32_t ctx, int32_t q_pos, int32_t window, int32
 typedef struct {
   int B, T, Hq, Hkv, D, cap, kind;
   const uint16_t *q, *k, *v;
+  /* fp8 caches (fp8 != 0): codes [B,Hkv,cap,D] and float32 scales [B,Hkv,cap] */
+  int fp8;
+  const uint8_t *k8, *v8;
+  const float *ks, *vs;
   const int32_t *ctx, *qpos;
   int window;
   double softcap; /* <= 0: off */
@@ -124,6 +139,65 @@ typedef struct {
   pthread_mutex_t mu;
 } decode_job;
 
+/* OCP e4m3 (fn) code -> value: exponent field 0 is subnormal (m / 8 * 2^-6); 0x7f and
+ * 0xff are NaN; there are no infinities. */
+double oracle_e4m3_to_f64(uint8_t c) {
+  const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+/* Round-to-nearest-even of a float32 to e4m3; magnitudes above 448 saturate to +-448
+ * (the quantizer clamps before converting, so it never relies on this). */
+uint8_t oracle_f32_to_e4m3(float x) {
+  const int sgn = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  if (isnan(x)) return 0x7f;
+  if (a >= 448.0) return (uint8_t)(sgn | 0x7e);
+  if (a < ldexp(1.0, -6)) {  /* subnormal range: multiples of 2^-9 */
+    const double q = nearbyint(ldexp(a, 9));  /* 0..8, ties to even */
+    return (uint8_t)(sgn | (int)q);           /* q = 8 is 0x08 = 2^-6, the smallest normal */
+  }
+  int e;
+  const double f = frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  int E = e - 1;                 /* a = (2f) * 2^E, 2f in [1, 2) */
+  double m = nearbyint((2.0 * f - 1.0) * 8.0);  /* 0..8, ties to even */
+  if (m == 8.0) {
+    m = 0.0;
+    E += 1;
+  }
+  return (uint8_t)(sgn | ((E + 7) << 3) | (int)m);
+}
+
+/* Quantize one bf16 row of D values to e4m3 codes and a float32 scale (see header). */
+void oracle_quantize_row_fp8(int D, const uint16_t* x, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    const float v = fabsf((float)oracle_bf16_to_f64(x[d]));
+    if (v > amax) amax = v;
+  }
+  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+  for (int d = 0; d < D; ++d) {
+    float y = (float)oracle_bf16_to_f64(x[d]) * inv;
+    y = fminf(fmaxf(y, -448.0f), 448.0f);
+    codes[d] = oracle_f32_to_e4m3(y);
+  }
+  *scale = amax / 448.0f;
+}
+
+/* Cached value (row = (b * Hkv + g) * cap + slot, element d) of K (which = 0) or V. */
+static double cache_value(const decode_job* J, int which, long row, int d) {
+  const long idx = row * J->D + d;
+  if (J->fp8) {
+    const uint8_t* c = (which == 1 && J->v8) ? J->v8 : J->k8;
+    const float* sc = (which == 1 && J->v8) ? J->vs : J->ks;
+    return oracle_e4m3_to_f64(c[idx]) * (double)sc[row];
+  }
+  const uint16_t* c = (which == 1 && J->v) ? J->v : J->k;
+  return oracle_bf16_to_f64(c[idx]);
+}
+
 /* One query row: unit = (b * T + t) * Hq + h. */
 static void decode_unit(decode_job* J, long unit, double* s_buf, long* p_buf) {
   const long bt = unit / J->Hq;
@@ -132,8 +206,7 @@ static void decode_unit(decode_job* J, long unit, double* s_buf, long* p_buf) {
   const int G = J->Hq / J->Hkv, g = h / G, D = J->D;
   const long ctx = J->ctx[b], qp = (long)J->qpos[b] + t;
   const uint16_t* qrow = J->q + unit * D;
-  const uint16_t* kbase = J->k + ((long)b * J->Hkv + g) * (long)J->cap * D;
-  const uint16_t* vbase = (J->v ? J->v : J->k) + ((long)b * J->Hkv + g) * (long)J->cap * D;
+  const long row0 = ((long)b * J->Hkv + g) * (long)J->cap;
   double* orow = J->out + unit * D;
 
   long n = 0;
@@ -149,9 +222,9 @@ static void decode_unit(decode_job* J, long unit, double* s_buf, long* p_buf) {
   }
   /* logits, in ascending position order */
   for (long i = 0; i < n; ++i) {
-    const uint16_t* krow = kbase + slot_of(p_buf[i], J->kind, J->cap) * D;
+    const long krow = row0 + slot_of(p_buf[i], J->kind, J->cap);
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += oracle_bf16_to_f64(qrow[d]) * oracle_bf16_to_f64(krow[d]);
+    for (int d = 0; d < D; ++d) dot += oracle_bf16_to_f64(qrow[d]) * cache_value(J, 0, krow, d);
     double s = J->scale * dot;
     if (J->softcap > 0.0) s = J->softcap * tanh(s / J->softcap);
     s_buf[i] = s;
@@ -166,9 +239,9 @@ static void decode_unit(decode_job* J, long unit, double* s_buf, long* p_buf) {
   }
   for (int d = 0; d < D; ++d) orow[d] = 0.0;
   for (long i = 0; i < n; ++i) {
-    const uint16_t* vrow = vbase + slot_of(p_buf[i], J->kind, J->cap) * D;
+    const long vrow = row0 + slot_of(p_buf[i], J->kind, J->cap);
     const double w = s_buf[i] / l;
-    for (int d = 0; d < D; ++d) orow[d] += w * oracle_bf16_to_f64(vrow[d]);
+    for (int d = 0; d < D; ++d) orow[d] += w * cache_value(J, 1, vrow, d);
     if (J->probs && p_buf[i] < J->probs_len) J->probs[unit * J->probs_len + p_buf[i]] = w;
   }
   if (J->lse) J->lse[unit] = m + log(l);
@@ -204,6 +277,38 @@ int oracle_num_threads_default(void) {
   return n > 0 ? (int)n : 1;
 }
 
+static int run_decode(decode_job* J, const int32_t* ctx_lens, const int32_t* q_pos0, int window,
+                      float softcap, float scale, int32_t* flags, int nthreads) {
+  const int B = J->B, T = J->T, Hq = J->Hq;
+  if (flags)
+    for (int b = 0; b < B; ++b)
+      for (int t = 0; t < T; ++t)
+        flags[(long)b * T + t] = oracle_row_flags(ctx_lens[b], q_pos0[b] + t, window, J->kind,
+                                                  J->cap);
+  J->ctx = ctx_lens;
+  J->qpos = q_pos0;
+  J->window = window;
+  J->softcap = (isfinite(softcap) && softcap > 0.0f) ? (double)softcap : 0.0;
+  J->scale = (double)scale;
+  J->next_unit = 0;
+  pthread_mutex_init(&J->mu, NULL);
+  if (nthreads <= 0) nthreads = oracle_num_threads_default();
+  long units = (long)B * T * Hq;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  if (!th) return OR_ENOMEM;
+  int rc = OR_OK;
+  for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, decode_worker, J);
+  for (int i = 0; i < nthreads; ++i) {
+    void* r = NULL;
+    pthread_join(th[i], &r);
+    if (r) rc = OR_ENOMEM;
+  }
+  free(th);
+  pthread_mutex_destroy(&J->mu);
+  return rc;
+}
+
 /*
  * Decode attention for every (b, t, h) with T query tokens per batch row.  q [B,T,Hq,D];
  * k_cache and v_cache [B,Hkv,cap,D] (bf16 bits, contiguous); v_cache NULL means V = K;
@@ -222,34 +327,61 @@ int oracle_decode_multi_f64(int B, int T, int Hq, int Hkv, int D, int cap, int k
   if (kind != OR_LINEAR && kind != OR_RING) return OR_EINVAL;
   if (!q || !k_cache || !ctx_lens || !q_pos0 || !out) return OR_EINVAL;
   if (!isfinite(scale)) return OR_EINVAL;
-  if (flags)
-    for (int b = 0; b < B; ++b)
-      for (int t = 0; t < T; ++t)
-        flags[(long)b * T + t] = oracle_row_flags(ctx_lens[b], q_pos0[b] + t, window, kind, cap);
   decode_job J;
+  memset(&J, 0, sizeof(J));
   J.B = B; J.T = T; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.cap = cap; J.kind = kind;
-  J.q = q; J.k = k_cache; J.v = v_cache; J.ctx = ctx_lens; J.qpos = q_pos0;
-  J.window = window;
-  J.softcap = (isfinite(softcap) && softcap > 0.0f) ? (double)softcap : 0.0;
-  J.scale = (double)scale;
+  J.q = q; J.k = k_cache; J.v = v_cache;
   J.out = out; J.lse = lse; J.probs = probs; J.probs_len = probs ? probs_len : 0;
-  J.next_unit = 0;
-  pthread_mutex_init(&J.mu, NULL);
-  if (nthreads <= 0) nthreads = oracle_num_threads_default();
-  long units = (long)B * T * Hq;
-  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
-  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
-  if (!th) return OR_ENOMEM;
-  int rc = OR_OK;
-  for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, decode_worker, &J);
-  for (int i = 0; i < nthreads; ++i) {
-    void* r = NULL;
-    pthread_join(th[i], &r);
-    if (r) rc = OR_ENOMEM;
-  }
-  free(th);
-  pthread_mutex_destroy(&J.mu);
-  return rc;
+  return run_decode(&J, ctx_lens, q_pos0, window, softcap, scale, flags, nthreads);
+}
+
+/*
+ * oracle_decode_multi_f64 over fp8 caches: k_codes [B,Hkv,cap,D] e4m3 codes with
+ * k_scales [B,Hkv,cap] float32, V likewise, or v_codes NULL for K = V.  Each cached
+ * value is code * scale (exact in double); the rest is the same definition.
+ */
+int oracle_decode_fp8_multi_f64(int B, int T, int Hq, int Hkv, int D, int cap, int kind,
+                                const uint16_t* q, const uint8_t* k_codes, const float* k_scales,
+                                const uint8_t* v_codes, const float* v_scales,
+                                const int32_t* ctx_lens, const int32_t* q_pos0, int window,
+                                float softcap, float scale, double* out, double* lse,
+                                double* probs, long probs_len, int32_t* flags, int nthreads) {
+  if (B < 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || cap <= 0 || Hq % Hkv != 0)
+    return OR_EINVAL;
+  if (kind != OR_LINEAR && kind != OR_RING) return OR_EINVAL;
+  if (!q || !k_codes || !k_scales || !ctx_lens || !q_pos0 || !out) return OR_EINVAL;
+  if ((v_codes == NULL) != (v_scales == NULL)) return OR_EINVAL;
+  if (!isfinite(scale)) return OR_EINVAL;
+  decode_job J;
+  memset(&J, 0, sizeof(J));
+  J.B = B; J.T = T; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.cap = cap; J.kind = kind;
+  J.q = q; J.fp8 = 1; J.k8 = k_codes; J.ks = k_scales; J.v8 = v_codes; J.vs = v_scales;
+  J.out = out; J.lse = lse; J.probs = probs; J.probs_len = probs ? probs_len : 0;
+  return run_decode(&J, ctx_lens, q_pos0, window, softcap, scale, flags, nthreads);
+}
+
+/*
+ * Quantizing append of T tokens per row into an fp8 cache: token t of row b (new_rows
+ * [B,T,Hkv,D] bf16) goes to position pos0[b] + t, slot p mod W (ring) or p (linear), in
+ * order t = 0..T-1; positions that are negative or (linear) >= C are skipped.
+ */
+int oracle_append_fp8(int B, int T, int Hkv, int D, int cap, int kind, uint8_t* codes,
+                      float* scales, const uint16_t* new_rows, const int32_t* pos0) {
+  if (B < 0 || T <= 0 || Hkv <= 0 || D <= 0 || cap <= 0 || !codes || !scales || !new_rows ||
+      !pos0)
+    return OR_EINVAL;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t) {
+      const long p = (long)pos0[b] + t;
+      if (p < 0 || (kind == OR_LINEAR && p >= cap)) continue;
+      const long s = slot_of(p, kind, cap);
+      for (int g = 0; g < Hkv; ++g) {
+        const long row = ((long)b * Hkv + g) * cap + s;
+        oracle_quantize_row_fp8(D, new_rows + (((long)b * T + t) * Hkv + g) * D,
+                                codes + row * D, scales + row);
+      }
+    }
+  return OR_OK;
 }
 
 /*
