@@ -52,7 +52,8 @@ def parse_args():
 
 # Single-layer workloads measured with --workload (the default line is the 48-layer step).
 SINGLE_LAYER = {"hd128_sliding": "HD128_SLIDING", "g4_12b_sliding": "G4_12B_SLIDING",
-                "g4_12b_global": "G4_12B_GLOBAL", "spec_decode_sliding": "SPEC_DECODE_SLIDING"}
+                "g4_12b_global": "G4_12B_GLOBAL", "spec_decode_sliding": "SPEC_DECODE_SLIDING",
+                "fp8_sliding": "FP8_SLIDING"}
 
 
 def log(msg):
@@ -99,7 +100,8 @@ def read_traffic(kernel_tag):
 
 
 # Sources whose change invalidates counter-measured traffic of the dominant kernel.
-TRAFFIC_SOURCES = ["decode_attention_split_amd/csrc/decode_valu.hip",
+TRAFFIC_SOURCES = ["decode_attention_split_amd/csrc/decode_valu_impl.h",
+                   "decode_attention_split_amd/csrc/decode_valu_d256.hip",
                    "decode_attention_split_amd/csrc/ga_device.h",
                    "decode_attention_split_amd/csrc/ga_internal.h",
                    "decode_attention_split_amd/csrc/api.hip"]
@@ -354,6 +356,8 @@ def bench_single_layer(args):
     w = getattr(wl, SINGLE_LAYER[args.workload])
     if w.tokens > 1:
         return bench_multi_token(args, w)
+    if w.kv_dtype == "fp8":
+        return bench_fp8(args, w)
     g = w.layers[0]
     B = w.batch
     gen_cpu = synth.generator(w.seed)
@@ -561,6 +565,134 @@ def bench_multi_token(args, w):
                                   "kind": "oracle",
                                   "sample": f"rows 0-{rows - 1} of the layer, all {T} tokens "
                                             f"(decode only), {spent:.1f}s of oracle time"}
+    print(json.dumps(result), flush=True)
+
+
+def fp8_layer_bytes(g, B, ctx):
+    """Algorithmic bytes of one fp8 layer step: per valid key D codes plus a float32 scale
+    (K, and V unless K = V), q, out, the int inputs, and the quantizing append (read the
+    bf16 row, write its codes and scale)."""
+    import numpy as np
+    n = valid_keys(g, ctx).astype("int64")
+    tensors = 1 if g.k_eq_v else 2
+    kv = int(n.sum()) * g.num_kv_heads * (g.head_dim + 4) * tensors
+    q = B * g.num_q_heads * g.head_dim * 2
+    out = B * g.num_q_heads * g.head_dim * 4
+    ints = 2 * B * 4
+    append = B * g.num_kv_heads * (g.head_dim * 2 + g.head_dim + 4) * tensors + B * 4
+    return {"kv": kv, "decode": kv + q + out + ints, "append": append}
+
+
+def bench_fp8(args, w):
+    """One layer over fp8 caches: quantizing append of the current token, then decode,
+    rotating over enough cache copies (>= 1 GiB) to keep the Infinity Cache out of it."""
+    import numpy as np
+    import torch
+    from decode_attention_split_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = w.layers[0]
+    B = w.batch
+    ctx = synth.uniform_int(synth.generator(w.seed), B, w.ctx_lo, w.ctx_hi).numpy() \
+        .astype(np.int32)
+    gdev = synth.generator(w.seed, device=dev)
+    W = g.capacity
+    tensors = 1 if g.k_eq_v else 2
+    cache_bytes = B * g.num_kv_heads * W * (g.head_dim + 4) * tensors
+    copies = int(min(8, max(1, math.ceil((1 << 30) / cache_bytes))))
+    ctx_t = torch.from_numpy(ctx).to(dev)
+    sets = []
+    for _ in range(copies):
+        # fill each cache by quantizing W random bf16 tokens per row (positions ctx-W..ctx-1)
+        kc = torch.empty((B, g.num_kv_heads, W, g.head_dim), dtype=torch.uint8, device=dev)
+        ks = torch.empty((B, g.num_kv_heads, W), dtype=torch.float32, device=dev)
+        vc = None if g.k_eq_v else torch.empty_like(kc)
+        vs = None if g.k_eq_v else torch.empty_like(ks)
+        for part in range(0, W, 256):
+            n = min(256, W - part)
+            kn = synth.normal_bf16(gdev, (B, n, g.num_kv_heads, g.head_dim), device=dev)
+            vn = None if g.k_eq_v else synth.normal_bf16(gdev, kn.shape, device=dev)
+            api.kv_append_fp8(kc, ks, vc, vs, kn, vn, ctx_t - W + part, g.kind)
+        q = synth.normal_bf16(gdev, (B, g.num_q_heads, g.head_dim), device=dev)
+        sets.append((q, kc, ks, vc, vs))
+    k_new = synth.normal_bf16(gdev, (B, g.num_kv_heads, g.head_dim), device=dev)
+    v_new = None if g.k_eq_v else synth.normal_bf16(gdev, k_new.shape, device=dev)
+    out = torch.empty((B, g.num_q_heads, g.head_dim), dtype=torch.float32, device=dev)
+    pos_t = ctx_t - 1
+    max_ctx = w.ctx_hi if g.kind == api.RING else g.capacity
+    shape = api.make_shape(B, g.num_q_heads, g.num_kv_heads, g.head_dim, W, g.kind, max_ctx)
+    ws = torch.empty((max(1, api.workspace_bytes_fp8(shape, 1, g.window)),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, kc, ks, vc, vs = sets[i % copies]
+        api.kv_append_fp8(kc, ks, vc, vs, k_new, v_new, pos_t, g.kind)
+        api.decode_fp8(q, kc, ks, vc, vs, ctx_t, pos_t, g.window, g.softcap, g.q_scale, g.kind,
+                       out=out, workspace=ws, max_ctx=max_ctx)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    lb = fp8_layer_bytes(g, B, ctx)
+    nbytes = lb["decode"] + lb["append"]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"{w.name}: {ms * 1e3:.2f} us per step (append + decode), {gbps:.1f} GB/s")
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 cache, bf16 q, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": w.name + " (one layer: quantizing append + decode)",
+                   "batch": B, "layers": 1, "ctx_mean": float(ctx.mean()), "accumulate": "fp32",
+                   "algorithmic_bytes_per_step": int(nbytes), "cache_copies": copies},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "layer_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "roofline": {"kernel": "fp8 quantizing append + decode, per step", "bound": "hbm",
+                     "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        q, kc, ks, vc, vs = sets[0]
+        qb = synth.bits(q)
+        kcn, ksn = kc.cpu().numpy(), ks.cpu().numpy()
+        vcn = None if vc is None else vc.cpu().numpy()
+        vsn = None if vs is None else vs.cpu().numpy()
+        threads = oracle.num_threads_default()
+        rows, spent, done = 0, 0.0, 0
+        while rows < B and spent < args.cpu_seconds:
+            sl = slice(rows, min(B, rows + 4))
+            t0 = time.perf_counter()
+            oracle.decode_fp8_multi(qb[sl], kcn[sl], ksn[sl], None if vcn is None else vcn[sl],
+                                    None if vsn is None else vsn[sl], ctx[sl], ctx[sl] - 1,
+                                    g.window, g.softcap, g.q_scale, g.kind, nthreads=threads)
+            spent += time.perf_counter() - t0
+            done += fp8_layer_bytes(g, sl.stop - sl.start, ctx[sl])["decode"]
+            rows = sl.stop
+        result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
+                                  "cores": int(min(threads, rows * g.num_q_heads)),
+                                  "kind": "oracle",
+                                  "sample": f"rows 0-{rows - 1} of the layer (decode only), "
+                                            f"{spent:.1f}s of oracle time"}
     print(json.dumps(result), flush=True)
 
 

@@ -28,7 +28,8 @@ EXPORTS = ["ga_decode_workspace_bytes", "gemma_attn_decode", "gemma_attn_decode_
            "gemma_kv_append", "gemma_attn_validate", "gemma_attn_debug_ranges",
            "gemma_attn_strerror", "gemma_attn_version",
            "ga_decode_multi_workspace_bytes", "gemma_attn_decode_multi", "gemma_kv_append_multi",
-           "gemma_attn_validate_multi"]
+           "gemma_attn_validate_multi", "gemma_kv_append_fp8", "ga_decode_fp8_workspace_bytes",
+           "gemma_attn_decode_fp8"]
 
 _lib = None
 
@@ -69,6 +70,13 @@ def load():
     lib.gemma_kv_append_multi.restype = i32
     lib.gemma_attn_validate_multi.argtypes = [SP, i32, P, P, i32, P, P]
     lib.gemma_attn_validate_multi.restype = i32
+    lib.gemma_kv_append_fp8.argtypes = [SP, i32, P, P, P, P, P, P, P, P]
+    lib.gemma_kv_append_fp8.restype = i32
+    lib.ga_decode_fp8_workspace_bytes.argtypes = [SP, i32, i32, OP]
+    lib.ga_decode_fp8_workspace_bytes.restype = sz
+    lib.gemma_attn_decode_fp8.argtypes = [SP, i32, P, P, P, P, P, P, P, i32, f32, f32, P, P, sz,
+                                          OP, P]
+    lib.gemma_attn_decode_fp8.restype = i32
     lib.gemma_attn_strerror.argtypes = [i32]
     lib.gemma_attn_strerror.restype = ctypes.c_char_p
     lib.gemma_attn_version.argtypes = []

@@ -267,6 +267,96 @@ def validate_multi(shape, num_tokens: int, ctx_lens, q_pos, window: int, stream=
     return flags
 
 
+def workspace_bytes_fp8(shape, num_tokens: int, window: int, split_keys: int = 0) -> int:
+    lib = _lib.load()
+    opts = make_opts(split_keys)
+    n = lib.ga_decode_fp8_workspace_bytes(ctypes.byref(shape), int(num_tokens), int(window),
+                                          ctypes.byref(opts))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid shape/tokens/window/options for gemma_attn_decode_fp8")
+    return int(n)
+
+
+def kv_append_fp8(k_codes, k_scales, v_codes, v_scales, k_new, v_new, pos, kind: int,
+                  stream=None):
+    """Quantizing append: k_new / v_new bf16 [B, T, Hkv, D] (or [B, Hkv, D] for T = 1) into
+    uint8 codes [B, Hkv, cap, D] and float32 scales [B, Hkv, cap] at positions pos[b] + t."""
+    _need(k_codes, "k_codes", torch.uint8, 4)
+    _need(k_scales, "k_scales", torch.float32, 3)
+    if k_new.dim() == 3:
+        k_new = k_new.unsqueeze(1)
+        v_new = None if v_new is None else v_new.unsqueeze(1)
+    _need(k_new, "k_new", torch.bfloat16, 4)
+    if (v_codes is None) != (v_new is None) or (v_codes is None) != (v_scales is None):
+        _check(-9, "gemma_kv_append_fp8")
+    if v_codes is not None:
+        _need(v_codes, "v_codes", torch.uint8, 4)
+        _need(v_scales, "v_scales", torch.float32, 3)
+        _need(v_new, "v_new", torch.bfloat16, 4)
+        if v_codes.shape != k_codes.shape or v_new.shape != k_new.shape:
+            raise ValueError("V tensors must have the shapes of the K tensors")
+    _need(pos, "pos", torch.int32, 1)
+    B, Hkv, cap, D = k_codes.shape
+    T = k_new.shape[1]
+    if tuple(k_new.shape) != (B, T, Hkv, D) or tuple(k_scales.shape) != (B, Hkv, cap) \
+            or pos.numel() != B:
+        raise ValueError("k_new must be [B, T, Hkv, D], k_scales [B, Hkv, cap] and pos [B]")
+    shape = make_shape(B, Hkv, Hkv, D, cap, kind)
+    rc = _lib.load().gemma_kv_append_fp8(ctypes.byref(shape), int(T), _ptr(k_codes),
+                                         _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                                         _ptr(k_new), _ptr(v_new), _ptr(pos),
+                                         _stream_handle(stream))
+    _check(rc, "gemma_kv_append_fp8")
+
+
+def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos, window: int,
+               softcap: float, scale: float, kind: int, out=None, workspace=None,
+               max_ctx: int = 0, split_keys: int = 0, deterministic: bool = False, stream=None):
+    """Decode over fp8 caches; q [B, Hq, D] (one token) or [B, T, Hq, D] (T tokens at
+    q_pos[b] + t); returns out of the same shape, float32 (see gemma_attn_decode_fp8)."""
+    single = q.dim() == 3
+    q4 = q.unsqueeze(1) if single else q
+    _need(q4, "q", torch.bfloat16, 4)
+    _need(k_codes, "k_codes", torch.uint8, 4)
+    _need(k_scales, "k_scales", torch.float32, 3)
+    if v_codes is not None:
+        _need(v_codes, "v_codes", torch.uint8, 4)
+        _need(v_scales, "v_scales", torch.float32, 3)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    B, T, Hq, D = q4.shape
+    Bk, Hkv, cap, Dk = k_codes.shape
+    if Bk != B or Dk != D or tuple(k_scales.shape) != (B, Hkv, cap):
+        raise ValueError("q, k_codes and k_scales disagree")
+    if ctx_lens.numel() != B or q_pos.numel() != B:
+        raise ValueError("ctx_lens and q_pos must have one entry per batch row")
+    shape = make_shape(B, Hq, Hkv, D, cap, kind, max_ctx)
+    want = (B, Hq, D) if single else (B, T, Hq, D)
+    if out is None:
+        out = torch.empty(want, dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32, len(want))
+        if tuple(out.shape) != want:
+            raise ValueError(f"out must be {list(want)}")
+    opts = make_opts(split_keys, IMPL_AUTO, deterministic)
+    lib = _lib.load()
+    need = lib.ga_decode_fp8_workspace_bytes(ctypes.byref(shape), int(T), int(window),
+                                             ctypes.byref(opts))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # let the library report the precise error
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib.gemma_attn_decode_fp8(
+        ctypes.byref(shape), int(T), _ptr(q4), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+        _ptr(v_scales), _ptr(ctx_lens), _ptr(q_pos), int(window), float(softcap), float(scale),
+        _ptr(out), _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream_handle(stream))
+    _check(rc, "gemma_attn_decode_fp8")
+    return out
+
+
 def kv_append(k_cache, v_cache, k_new, v_new, pos, kind: int, stream=None):
     """cache[b, g, slot(pos_b), :] <- new[b, g, :] for K (and V unless K = V)."""
     _need(k_cache, "k_cache", torch.bfloat16, 4)

@@ -173,7 +173,7 @@ void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
 // k_eq_v: 1 / 0 when known (a decode call), -1 for a workspace query, which then sizes
 // for whichever implementation AUTO may pick.
 int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, int k_eq_v,
-                  Plan* p, int T = 1) {
+                  Plan* p, int T = 1, bool vector_only = false) {
   int impl = GA_IMPL_AUTO, ts = 0;
   if (o) {
     for (int i = 0; i < 5; ++i)
@@ -184,8 +184,8 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
     if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
     if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
   }
-  if (T > 1) {
-    // several query tokens: the vector kernel with per-row masks
+  if (T > 1 || vector_only) {
+    // several query tokens (per-row masks) or an fp8 cache: the vector kernel
     if (impl == GA_IMPL_MFMA) return GA_ERR_OPTS;
     return valu_plan(s, window, ts, T, p);
   }
@@ -255,18 +255,47 @@ size_t ga_decode_multi_workspace_bytes(const ga_shape* shape, int32_t num_tokens
   return p.ws_bytes;
 }
 
+size_t ga_decode_fp8_workspace_bytes(const ga_shape* shape, int32_t num_tokens, int32_t window,
+                                     const ga_decode_opts* opts) {
+  if (check_shape(shape, window, num_tokens) != GA_OK) return SIZE_MAX;
+  Plan p;
+  if (make_plan(shape, window, opts, -1, &p, num_tokens, true) != GA_OK) return SIZE_MAX;
+  return p.ws_bytes;
+}
+
 }  // extern "C"
 
 namespace {
 
-// Decode, optionally fused with the cache append of one token per row (k_new != nullptr).
+// fp8 e4m3 caches: codes and float32 row scales of K, and of V unless K = V.
+struct Fp8Cache {
+  const uint8_t* k;
+  const float* ks;
+  const uint8_t* v;
+  const float* vs;
+};
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Decode, optionally fused with the cache append of one token per row (k_new != nullptr),
+// over bf16 caches (k_cache / v_cache) or fp8 caches (f8 != nullptr).
 int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, ga_bf16* v_cache,
                     const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* new_pos,
                     const int32_t* ctx_lens, const int32_t* q_pos, int32_t window, float softcap,
                     float scale, float* out, void* workspace, size_t workspace_bytes,
-                    const ga_decode_opts* opts, void* stream, int32_t T = 1) {
+                    const ga_decode_opts* opts, void* stream, int32_t T = 1,
+                    const Fp8Cache* f8 = nullptr) {
   int32_t st = check_shape(shape, window, T);
   if (st != GA_OK) return st;
+  if (f8) {
+    if (!f8->k || !f8->ks) return GA_ERR_NULL;
+    if ((f8->v == nullptr) != (f8->vs == nullptr)) return GA_ERR_V_MISMATCH;
+    if (!aligned16(f8->k) || !aligned16(f8->v) || !aligned4(f8->ks) || !aligned4(f8->vs))
+      return GA_ERR_NULL;
+    // the bf16 cache checks below look at the codes (never dereferenced as bf16)
+    k_cache = reinterpret_cast<ga_bf16*>(const_cast<uint8_t*>(f8->k));
+    v_cache = reinterpret_cast<ga_bf16*>(const_cast<uint8_t*>(f8->v));
+  }
   if (!q || !k_cache || !ctx_lens || !q_pos || !out) return GA_ERR_NULL;
   if (k_new) {
     if (!new_pos) return GA_ERR_NULL;
@@ -279,7 +308,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   if (!std::isfinite(scale)) return GA_ERR_SCALE;
   const bool k_eq_v = v_cache == nullptr || v_cache == k_cache;
   Plan p;
-  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p, T);
+  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p, T, f8 != nullptr);
   if (st != GA_OK) return st;
   const int D = shape->head_dim;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return GA_ERR_WORKSPACE;
@@ -330,6 +359,13 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   a.n_chunks = p.n_chunks;
   a.Gh = shape->num_q_heads / shape->num_kv_heads;
   a.max_union = p.max_keys;
+  if (f8) {
+    a.fp8 = 1;
+    a.k8 = f8->k;
+    a.k_scale = f8->ks;
+    a.v8 = k_eq_v ? f8->k : f8->v;
+    a.v_scale = k_eq_v ? f8->ks : f8->vs;
+  }
   a.k_new = k_new;
   a.v_new = k_eq_v ? nullptr : v_new;
   a.new_pos = k_new ? new_pos : nullptr;
@@ -445,6 +481,44 @@ int32_t gemma_kv_append_multi(const ga_shape* shape, int32_t num_tokens, ga_bf16
   hipError_t e = ga::append_launch(shape->batch, num_tokens, shape->num_kv_heads,
                                    shape->head_dim, shape->capacity, shape->kind, k_cache,
                                    v_cache, k_new, v_new, pos, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const ga_bf16* q,
+                              const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales,
+                              const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
+                              float softcap, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, const ga_decode_opts* opts, void* stream) {
+  const Fp8Cache f8{k_codes, k_scales, v_codes, v_scales};
+  return decode_impl(shape, q, nullptr, nullptr, nullptr, nullptr, nullptr, ctx_lens, q_pos,
+                     window, softcap, scale, out, workspace, workspace_bytes, opts, stream,
+                     num_tokens, &f8);
+}
+
+int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* k_codes,
+                            float* k_scales, uint8_t* v_codes, float* v_scales,
+                            const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
+                            void* stream) {
+  if (!shape) return GA_ERR_NULL;
+  if (shape->batch < 0 || shape->num_kv_heads <= 0 || shape->num_q_heads <= 0 ||
+      shape->capacity <= 0 || num_tokens < 1)
+    return GA_ERR_DIMS;
+  if (num_tokens > kMaxTokens) return GA_ERR_TOO_LARGE;
+  if (!head_dim_ok(shape->head_dim)) return GA_ERR_HEAD_DIM;
+  if (shape->kind != GA_CACHE_LINEAR && shape->kind != GA_CACHE_RING) return GA_ERR_KIND;
+  if (!k_codes || !k_scales || !k_new || !pos) return GA_ERR_NULL;
+  if ((v_codes == nullptr) != (v_new == nullptr) || (v_codes == nullptr) != (v_scales == nullptr))
+    return GA_ERR_V_MISMATCH;
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned4(k_scales) || !aligned4(v_scales))
+    return GA_ERR_NULL;
+  int32_t st = check_arch();
+  if (st != GA_OK) return st;
+  hipError_t e = ga::append_fp8_launch(shape->batch, num_tokens, shape->num_kv_heads,
+                                       shape->head_dim, shape->capacity, shape->kind, k_codes,
+                                       k_scales, v_codes, v_scales, k_new, v_new, pos,
+                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
 }
 

@@ -1,0 +1,507 @@
+// decode_valu_impl.h -- split-KV flash-decode on the vector ALUs (gfx950, wave64).
+//
+// Kernel templates and launchers; decode_valu_d{128,256,512}.hip each instantiate
+// valu_launch_d for one head dim (compiled in parallel), decode_valu.hip dispatches.
+//
+// One work-group handles one split (a run of split_keys consecutive valid keys) of one
+// (batch row, KV head).  Inside a wave, aligned groups of L lanes each own one key per
+// step: lane j of a group holds the elements d = 8 * (c * L + j) + e (c < D / (8 L),
+// e < 8) of that key's row, loaded straight from HBM with 16-byte loads (a group reads
+// 16 L contiguous bytes per load, a full row over D / (8 L) loads).  The G query heads
+// that share the KV head stay in registers as packed bf16, so q . k is v_dot2 on the raw
+// bf16 data with fp32 accumulation, finished by a DPP butterfly over the group.  Every
+// group keeps its own online-softmax state (m, l, acc[G][D / L]) and the groups and
+// waves are merged once at the end, so the key loop has no barrier and no LDS traffic:
+// each lane consumes exactly the bytes it loaded, and staging through LDS would only add
+// a write and a read per byte.  With K = V the row loaded for the logits is the row
+// used for the values (read once, used twice).
+//
+// Softmax runs in log2 units: s2 = log2(e) * cap(scale * q.k).  The running max is only
+// raised when a logit exceeds it by more than kRescaleLog2 (2^8), so the accumulator
+// rescale (G * D / L multiplies) happens a handful of times per group rather than per
+// key; exp2(s2 - m) <= 2^8 keeps everything well inside fp32.  The result is unchanged:
+// (m, l, acc) stay mutually consistent whatever reference m is used.
+//
+// Definition followed: "Gemma support" pull request, Summary (soft-capping, sliding
+// window, head sizes 256/512, K = V) and Performance (split decode attention); the key
+// range is ga::row_range ("Gemma 4 12B (unified multimodal)" record: exactly w entries).
+#pragma once
+
+#include <type_traits>
+
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+namespace {
+
+constexpr float kRescaleLog2 = 8.0f;
+
+constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Waves per work-group: the default keeps the end-of-split LDS merge buffer at 32 KiB;
+// the wide variant doubles it when that still fits in 64 KiB, for launches with few
+// work-groups (one split per row) that need more waves in flight per CU.
+template <int D, int G>
+constexpr int valu_nw_base() { return clampi(8192 / (G * D), 1, 4); }
+// The wide variant doubles the waves of small work-groups; only where a lane's
+// accumulators stay at 64 (the lanes per key are not clamped at D / 8), else it spills.
+template <int D, int G>
+constexpr bool valu_nw_wide_ok() {
+  return valu_nw_base<D, G>() == 4 && G * D <= 2048 && G * D / clampi(G * D / 64, 8, D / 8) <= 64;
+}
+
+template <int D, int G, int NW_>
+struct ValuCfg {
+  static constexpr int L = clampi(G * D / 64, 8, D / 8);  // lanes per key: acc <= 64..128 VGPRs
+  static constexpr int DPL = D / L;                        // elements per lane per key
+  static constexpr int NCH = DPL / 8;                      // 16-byte loads per lane per key
+  static constexpr int GPW = 64 / L;                       // keys per wave per step
+  static constexpr int NW = NW_;                           // waves per work-group
+  static constexpr int NG = GPW * NW;                      // keys per work-group per step
+  static_assert(NCH >= 1 && DPL % 8 == 0, "lane slice must be whole 16-byte chunks");
+};
+
+// G is the number of query rows a unit serves: the query heads of one KV head (one
+// token), or with MULTI those heads for each of the Tc tokens of a chunk (row hh is
+// token hh / Gh, head hh % Gh), every row masked at its own position.
+// 32-bit word i of a 16- or 8-byte load chunk (i is a compile-time constant after
+// unrolling).
+__device__ __forceinline__ uint32_t chunk_word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t chunk_word(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+
+// FP8: the cache holds e4m3 codes with one float32 scale per row (K and V each); a key's
+// logit is scale_k * <q, codes> and its value weight p * scale_v multiplies the codes.
+template <int D, int G, int NW_, bool KV_SHARED, bool MULTI, bool FP8>
+__global__ void __launch_bounds__(NW_ * 64)
+    decode_valu_kernel(DecodeArgs a) {
+  using C = ValuCfg<D, G, NW_>;
+  constexpr int L = C::L, DPL = C::DPL, GPW = C::GPW, NW = C::NW, NG = C::NG;
+  constexpr int ROW16 = D / 8;  // 16-byte chunks per bf16 row
+  // A lane owns elements EPC * (c * L + j) + e (e < EPC) of each row, for its NCH load
+  // chunks c: 8 bf16 or 16 fp8 codes per 16-byte chunk (8 codes in 8 bytes when a lane
+  // owns only 8 elements).
+  constexpr int EPC = FP8 ? (DPL >= 16 ? 16 : 8) : 8;
+  constexpr int NCH = DPL / EPC;
+  using Chunk = std::conditional_t<FP8 && EPC == 8, uint2, uint4>;
+  constexpr int ROWC = (FP8 ? D : 2 * D) / (int)sizeof(Chunk);  // chunks per cache row
+  static_assert(NCH >= 1 && DPL % EPC == 0, "lane slice must be whole load chunks");
+
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane / L;
+  const int j = lane % L;
+
+  const int S = a.n_split;
+  int bid = blockIdx.x;
+  const int split = bid % S;
+  bid /= S;
+  int chunk = 0;
+  if constexpr (MULTI) {
+    chunk = bid % a.n_chunks;
+    bid /= a.n_chunks;
+  }
+  const int g = bid % a.Hkv;
+  const int b = bid / a.Hkv;
+  const int h0 = g * G;
+
+  // Query row hh of this unit: its token, whether it exists, and its row index in q /
+  // out / the partials ([B, Hq] rows, or [B, T, Hq] rows with MULTI).
+  auto row_token = [&](int hh) { return MULTI ? chunk * a.Tc + hh / a.Gh : 0; };
+  auto row_active = [&](int hh) { return !MULTI || row_token(hh) < a.T; };
+  auto row_index = [&](int hh) -> size_t {
+    if constexpr (!MULTI) return (size_t)b * a.Hq + h0 + hh;
+    const int t = min(row_token(hh), a.T - 1);  // inactive rows alias the last token
+    return ((size_t)b * a.T + t) * a.Hq + (size_t)g * a.Gh + hh % a.Gh;
+  };
+
+  // Fused append: split 0 of each unit moves the new row; its loads are issued here and
+  // the stores happen after the key loop, so nothing waits on them.
+  const int new_slot = appended_slot(a, b);
+  AppendRow app;
+  app.load(a, b, g, new_slot, threadIdx.x, split == 0);
+  const RowRange r = unit_range(a, b, chunk);
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(r.n, k_begin + a.split_keys);
+  if (k_begin >= k_end) {
+    if (S == 1) {  // the only split of an empty unit: the output is 0
+      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
+        if (row_active(idx / D)) a.out[row_index(idx / D) * D + idx % D] = 0.0f;
+    }
+    app.store(a);
+    return;  // with S > 1 the merge never reads splits past the unit's end
+  }
+  __shared__ int s_next;  // next wave-step to hand out
+  if (threadIdx.x == 0) s_next = 0;
+  __syncthreads();
+
+  // MULTI: each row's own valid positions [row_lo, row_hi] (empty: lo > hi).
+  int row_lo[MULTI ? G : 1], row_hi[MULTI ? G : 1];
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      row_lo[hh] = 1;
+      row_hi[hh] = 0;
+      if (row_active(hh)) {
+        const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + row_token(hh), a.window, a.kind,
+                                      a.cap, a.max_keys);
+        if (rr.n > 0) {
+          row_lo[hh] = rr.lo;
+          row_hi[hh] = rr.hi;
+        }
+      }
+    }
+  }
+
+  // Query rows of this unit in this lane's element order: packed bf16 pairs for the
+  // bf16 cache (dot2 products), float32 values for the fp8 cache.
+  uint32_t qr[G][FP8 ? 1 : DPL / 2];
+  float qf[G][FP8 ? DPL : 1];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + row_index(hh) * D);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int h8 = 0; h8 < EPC / 8; ++h8) {
+        const uint4 v = qp[(EPC / 8) * (c * L + j) + h8];
+        if constexpr (FP8) {
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qf[hh][EPC * c + 8 * h8 + 2 * i] = bf16_lo(w4[i]);
+            qf[hh][EPC * c + 8 * h8 + 2 * i + 1] = bf16_hi(w4[i]);
+          }
+        } else {
+          qr[hh][4 * c + 0] = v.x;
+          qr[hh][4 * c + 1] = v.y;
+          qr[hh][4 * c + 2] = v.z;
+          qr[hh][4 * c + 3] = v.w;
+        }
+      }
+    }
+  }
+
+  const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
+  const void* kmem = FP8 ? (const void*)a.k8 : (const void*)a.k;
+  const void* vmem = FP8 ? (const void*)(KV_SHARED ? a.k8 : a.v8)
+                         : (const void*)(KV_SHARED ? a.k : a.v);
+  const Chunk* kbase = reinterpret_cast<const Chunk*>(kmem) + row0 * ROWC;
+  const Chunk* vbase = reinterpret_cast<const Chunk*>(vmem) + row0 * ROWC;
+  const float* kscale = FP8 ? a.k_scale + row0 : nullptr;
+  const float* vscale = FP8 ? (KV_SHARED ? a.k_scale : a.v_scale) + row0 : nullptr;
+  // fused append (bf16 caches): the appended token's rows, read in place of its slot
+  const size_t unit = (size_t)b * a.Hkv + g;
+  const Chunk* knew =
+      !FP8 && a.new_pos ? reinterpret_cast<const Chunk*>(a.k_new) + unit * ROW16 : kbase;
+  const Chunk* vnew =
+      !FP8 && a.new_pos
+          ? reinterpret_cast<const Chunk*>(KV_SHARED ? a.k_new : a.v_new) + unit * ROW16
+          : vbase;
+
+  float acc[G][DPL];
+  float m[G], l[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
+  }
+
+  // Wave-step s covers keys k_begin + s * GPW + grp (one per lane group).  Steps are
+  // handed out to waves as they ask for them (an LDS counter), so waves that the SIMD
+  // arbiter serves less still finish together with the others; in deterministic mode the
+  // order is static (wave w takes w, w + NW, ...), which fixes the summation order.
+  const int n_wsteps = (k_end - k_begin + GPW - 1) / GPW;
+  const float scale = a.scale;
+  const float softcap = a.softcap, inv_softcap = a.inv_softcap;
+  int taken = 0;
+  auto grab = [&]() -> int {
+    if (a.deterministic) return wave + NW * (taken++);
+    int s = 0;
+    if (lane == 0) s = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(s);
+  };
+
+  // sc[0] / sc[1]: the key's K / V row scales (fp8 caches only)
+  auto load = [&](Chunk(&kr)[NCH], Chunk(&vr)[NCH], float(&sc)[2], int step) {
+    const int i = k_begin + step * GPW + grp;
+    const int ic = i < k_end ? i : k_end - 1;  // past the end: re-read a valid row
+    const int slot = key_slot(r, ic, a.cap);
+    const bool fresh = !FP8 && slot == new_slot;
+    const Chunk* kp = fresh ? knew : kbase + (size_t)slot * ROWC;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kr[c] = kp[c * L + j];
+    if constexpr (!KV_SHARED) {
+      const Chunk* vp = fresh ? vnew : vbase + (size_t)slot * ROWC;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) vr[c] = vp[c * L + j];
+    }
+    if constexpr (FP8) {
+      sc[0] = kscale[slot];
+      sc[1] = KV_SHARED ? sc[0] : vscale[slot];
+    }
+  };
+
+  // e4m3 codes of one chunk -> float32 values (v_cvt_pk_f32_fp8, exact)
+  auto widen_fp8 = [&](const Chunk& ch, float* out) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int w = 0; w < EPC / 4; ++w) {
+      const int word = (int)chunk_word(ch, w);
+      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      out[4 * w + 0] = lo.x;
+      out[4 * w + 1] = lo.y;
+      out[4 * w + 2] = hi.x;
+      out[4 * w + 3] = hi.y;
+    }
+  };
+
+  auto compute = [&](const Chunk(&kr)[NCH], const Chunk(&vr)[NCH], const float(&sc)[2],
+                     int step) {
+    const int i = k_begin + step * GPW + grp;
+    const bool valid = i < k_end;
+    const int pos = r.lo + i;  // absolute position of the key (MULTI masks)
+    float s[G];
+    if constexpr (FP8) {
+      float kf[DPL];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) widen_fp8(kr[c], &kf[EPC * c]);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; e += 2) {
+          d0 = fmaf(qf[hh][e], kf[e], d0);
+          d1 = fmaf(qf[hh][e + 1], kf[e + 1], d1);
+        }
+        s[hh] = group_sum<L>(d0 + d1) * sc[0];
+      }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          d0 = dot2_bf16(qr[hh][4 * c + 0], chunk_word(kr[c], 0), d0);
+          d1 = dot2_bf16(qr[hh][4 * c + 1], chunk_word(kr[c], 1), d1);
+          d0 = dot2_bf16(qr[hh][4 * c + 2], chunk_word(kr[c], 2), d0);
+          d1 = dot2_bf16(qr[hh][4 * c + 3], chunk_word(kr[c], 3), d1);
+        }
+        s[hh] = group_sum<L>(d0 + d1);
+      }
+    }
+    float p[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      bool vh = valid;
+      if constexpr (MULTI) vh = vh && pos >= row_lo[hh] && pos <= row_hi[hh];
+      float x = s[hh] * scale;
+      if (softcap > 0.0f) x = softcap_tanh(x, softcap, inv_softcap);
+      x = vh ? x * kLog2e : -INFINITY;
+      if (x > m[hh] + kRescaleLog2) {
+        const float f = exp2_fast(m[hh] - x);  // 0 on the first key (m = -inf)
+        l[hh] *= f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[hh][e] *= f;
+        m[hh] = x;
+      }
+      p[hh] = vh ? exp2_fast(x - m[hh]) : 0.0f;
+      l[hh] += p[hh];
+    }
+    const Chunk(&vv)[NCH] = KV_SHARED ? kr : vr;
+    if constexpr (FP8) {
+      float pv[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) pv[hh] = p[hh] * sc[1];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float vf[EPC];
+        widen_fp8(vv[c], vf);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh)
+            acc[hh][EPC * c + e] = fmaf(pv[hh], vf[e], acc[hh][EPC * c + e]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = chunk_word(vv[c], t);
+          const float lo = bf16_lo(w), hi = bf16_hi(w);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            acc[hh][8 * c + 2 * t] = fmaf(p[hh], lo, acc[hh][8 * c + 2 * t]);
+            acc[hh][8 * c + 2 * t + 1] = fmaf(p[hh], hi, acc[hh][8 * c + 2 * t + 1]);
+          }
+        }
+      }
+    }
+  };
+
+  // Two register buffers: the next step's rows are in flight while a step computes.  The
+  // loads are unconditional (past the end they re-read the last valid row) and the loop
+  // body is straight-line with its test at the bottom, so every path into the loop
+  // header carries the same outstanding loads (buffer a only) and the compiler keeps
+  // partial vmcnt waits instead of draining the prefetch.  Grabs are increasing per wave,
+  // so sa < sb < n_wsteps inside the loop.
+  Chunk ka[NCH], va[NCH], kb[NCH], vb[NCH];
+  float ca[2] = {1.0f, 1.0f}, cb[2] = {1.0f, 1.0f};
+  int sa = grab();
+  load(ka, va, ca, sa);
+  int sb = grab();
+  while (sb < n_wsteps) {
+    load(kb, vb, cb, sb);
+    compute(ka, va, ca, sa);
+    sa = grab();
+    load(ka, va, ca, sa);
+    compute(kb, vb, cb, sb);
+    sb = grab();
+  }
+  if (sa < n_wsteps) compute(ka, va, ca, sa);
+  app.store(a);
+
+  // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements),
+  // exchanging values with DPP / permlane swaps on the VALU.
+  auto merge_groups = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float mo = xor_lane<OFF>(m[hh], lane);
+      const float lo = xor_lane<OFF>(l[hh], lane);
+      const float mn = fmaxf(m[hh], mo);
+      const float fs = m[hh] == -INFINITY ? 0.0f : exp2_fast(m[hh] - mn);
+      const float fo = mo == -INFINITY ? 0.0f : exp2_fast(mo - mn);
+      l[hh] = l[hh] * fs + lo * fo;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float ao = xor_lane<OFF>(acc[hh][e], lane);
+        acc[hh][e] = acc[hh][e] * fs + ao * fo;
+      }
+      m[hh] = mn;
+    }
+  };
+  if constexpr (L <= 8) merge_groups(std::integral_constant<int, 8>());
+  if constexpr (L <= 16) merge_groups(std::integral_constant<int, 16>());
+  if constexpr (L <= 32) merge_groups(std::integral_constant<int, 32>());
+
+  // Merge the waves through LDS, then write the output or this split's partial.
+  if (lane < L) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float4* dst = reinterpret_cast<float4*>(&s_acc[wave][hh][EPC * (c * L + j)]);
+#pragma unroll
+        for (int q4 = 0; q4 < EPC / 4; ++q4)
+          dst[q4] = make_float4(acc[hh][EPC * c + 4 * q4 + 0], acc[hh][EPC * c + 4 * q4 + 1],
+                                acc[hh][EPC * c + 4 * q4 + 2], acc[hh][EPC * c + 4 * q4 + 3]);
+      }
+      if (j == 0) {
+        s_m[wave][hh] = m[hh];
+        s_l[wave][hh] = l[hh];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int hh = idx / D, d = idx % D;
+    if (!row_active(hh)) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hh]);
+    float Lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = s_m[w][hh] == -INFINITY ? 0.0f : exp2_fast(s_m[w][hh] - M);
+      Lsum += s_l[w][hh] * f;
+      o += s_acc[w][hh][d] * f;
+    }
+    const size_t bh = row_index(hh);
+    if (S == 1) {
+      a.out[bh * D + d] = Lsum > 0.0f ? o / Lsum : 0.0f;
+    } else {
+      a.part_acc[(bh * S + split) * D + d] = o;
+      if (d == 0) {
+        a.part_ml[(bh * S + split) * 2 + 0] = M;
+        a.part_ml[(bh * S + split) * 2 + 1] = Lsum;
+      }
+    }
+  }
+}
+
+template <int D, int G, int NW>
+hipError_t launch_dgw(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  const long long blocks = (long long)a.B * a.Hkv * a.n_chunks * a.n_split;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(NW * 64);
+  const bool multi = a.T > 1;
+  // K = V, several tokens, fp8 cache: one instantiation per combination
+#define GA_VALU_LAUNCH(KV, MU, F8)                                                             \
+  hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, KV, MU, F8>), grid, block, 0, stream, a)
+  if (a.fp8) {
+    if (multi) {
+      if (k_eq_v) GA_VALU_LAUNCH(true, true, true); else GA_VALU_LAUNCH(false, true, true);
+    } else {
+      if (k_eq_v) GA_VALU_LAUNCH(true, false, true); else GA_VALU_LAUNCH(false, false, true);
+    }
+  } else {
+    if (multi) {
+      if (k_eq_v) GA_VALU_LAUNCH(true, true, false); else GA_VALU_LAUNCH(false, true, false);
+    } else {
+      if (k_eq_v) GA_VALU_LAUNCH(true, false, false); else GA_VALU_LAUNCH(false, false, false);
+    }
+  }
+#undef GA_VALU_LAUNCH
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  constexpr int base = valu_nw_base<D, G>();
+  if constexpr (valu_nw_wide_ok<D, G>()) {
+    if (a.n_waves == 2 * base) return launch_dgw<D, G, 2 * base>(a, k_eq_v, stream);
+  }
+  return launch_dgw<D, G, base>(a, k_eq_v, stream);
+}
+
+template <int D>
+int wide_waves_d(int G) {
+  switch (G) {
+    case 1: return valu_nw_wide_ok<D, 1>() ? 2 * valu_nw_base<D, 1>() : 0;
+    case 2: return valu_nw_wide_ok<D, 2>() ? 2 * valu_nw_base<D, 2>() : 0;
+    case 4: return valu_nw_wide_ok<D, 4>() ? 2 * valu_nw_base<D, 4>() : 0;
+    case 8: return valu_nw_wide_ok<D, 8>() ? 2 * valu_nw_base<D, 8>() : 0;
+    case 16: return valu_nw_wide_ok<D, 16>() ? 2 * valu_nw_base<D, 16>() : 0;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+// All instantiations for one head dim (explicitly instantiated per head dim).
+template <int D>
+hipError_t valu_launch_d(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  switch (a.Gh * a.Tc) {  // query rows per unit
+    case 1: return launch_dg<D, 1>(a, k_eq_v, stream);
+    case 2: return launch_dg<D, 2>(a, k_eq_v, stream);
+    case 4: return launch_dg<D, 4>(a, k_eq_v, stream);
+    case 8: return launch_dg<D, 8>(a, k_eq_v, stream);
+    case 16: return launch_dg<D, 16>(a, k_eq_v, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+
+}  // namespace ga

@@ -42,6 +42,13 @@ struct DecodeArgs {
   int T = 1, Tc = 1, n_chunks = 1;
   int Gh = 1;             // query heads per KV head (Hq / Hkv)
   int max_union = 0;
+  // fp8 e4m3 caches (fp8 != 0): codes [B, Hkv, cap, D] and float32 row scales
+  // [B, Hkv, cap]; for K = V the V fields equal the K fields.
+  int fp8 = 0;
+  const uint8_t* k8 = nullptr;
+  const uint8_t* v8 = nullptr;
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
 };
 
 // Key range a decode unit walks.  One token: that row's range.  Several tokens: the
@@ -147,6 +154,13 @@ hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream);
 hipError_t append_launch(int B, int T, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
                          uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* pos, hipStream_t stream);
+
+// Quantizing append of T tokens per row into fp8 caches (codes + row scales); V
+// pointers are nullptr for K = V.
+hipError_t append_fp8_launch(int B, int T, int Hkv, int D, int cap, int kind, uint8_t* k_codes,
+                             float* k_scales, uint8_t* v_codes, float* v_scales,
+                             const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos,
+                             hipStream_t stream);
 
 // Flags of the B * T query tokens at positions q_pos[b] + t.
 hipError_t validate_launch(int B, int T, int cap, int kind, int window, int max_ctx,

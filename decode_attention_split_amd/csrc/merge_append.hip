@@ -98,6 +98,63 @@ __global__ void append_kernel(int B, int T, int Hkv, int D, int cap, int kind, u
   }
 }
 
+// Quantizing append into fp8 e4m3 caches: one wave per (b, KV head) walks the T tokens
+// in order (so a later token that lands in the same ring slot stays); lane i < D / 8
+// holds 8 consecutive values of the row.  Per row: amax = max |x|, inv = 448 / amax,
+// code = round-to-nearest-even e4m3 of clamp(x * inv, +-448), scale = amax / 448, all in
+// float32 with correctly rounded division, as the plain definition states.
+__device__ __forceinline__ void quantize_store_row(const uint4* src, uint2* dst_codes,
+                                                   float* dst_scale, int lane, int chunks) {
+  const bool on = lane < chunks;
+  const uint4 w = on ? src[lane] : make_uint4(0, 0, 0, 0);
+  float x[8];
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(ws[i]);
+    x[2 * i + 1] = bf16_hi(ws[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] * inv, -448.0f), 448.0f);
+  // codes of elements 0..3 in bytes 0..3 of the first dword, 4..7 in the second (the
+  // second operand of each conversion lands in the higher byte of its pair)
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  if (on) dst_codes[lane] = make_uint2((uint32_t)w0, (uint32_t)w1);
+  if (lane == 0) *dst_scale = amax / 448.0f;
+}
+
+__global__ void __launch_bounds__(64)
+    append_fp8_kernel(int B, int T, int Hkv, int D, int cap, int kind, uint8_t* k_codes,
+                      float* k_scales, uint8_t* v_codes, float* v_scales, const uint4* k_new,
+                      const uint4* v_new, const int32_t* pos) {
+  const int bg = blockIdx.x;  // b * Hkv + g
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int lane = threadIdx.x;
+  const int chunks = D / 8;
+  for (int t = 0; t < T; ++t) {
+    const long long p = (long long)pos[b] + t;
+    if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) continue;  // out of range: skipped
+    const int slot = kind == GA_CACHE_RING ? (int)(p % cap) : (int)p;
+    const size_t row = (size_t)bg * cap + slot;
+    const size_t src = (((size_t)b * T + t) * Hkv + g) * chunks;
+    quantize_store_row(k_new + src, reinterpret_cast<uint2*>(k_codes + row * D),
+                       k_scales + row, lane, chunks);
+    if (v_codes)
+      quantize_store_row(v_new + src, reinterpret_cast<uint2*>(v_codes + row * D),
+                         v_scales + row, lane, chunks);
+  }
+}
+
 // Precondition flags of every query token (b, t) at position q_pos[b] + t.
 __global__ void validate_kernel(int B, int T, int cap, int kind, int window, int max_ctx,
                                 const int32_t* ctx_lens, const int32_t* q_pos, int32_t* flags) {
@@ -149,6 +206,19 @@ hipError_t append_launch(int B, int T, int Hkv, int D, int cap, int kind, uint16
                      D, cap, kind, reinterpret_cast<uint4*>(k_cache),
                      reinterpret_cast<uint4*>(v_cache), reinterpret_cast<const uint4*>(k_new),
                      reinterpret_cast<const uint4*>(v_new), pos);
+  return hipGetLastError();
+}
+
+hipError_t append_fp8_launch(int B, int T, int Hkv, int D, int cap, int kind, uint8_t* k_codes,
+                             float* k_scales, uint8_t* v_codes, float* v_scales,
+                             const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos,
+                             hipStream_t stream) {
+  const long long units = (long long)B * Hkv;
+  if (units <= 0 || T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_fp8_kernel, dim3((unsigned)units), dim3(64), 0, stream, B, T, Hkv, D,
+                     cap, kind, k_codes, k_scales, v_codes, v_scales,
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                     pos);
   return hipGetLastError();
 }
 

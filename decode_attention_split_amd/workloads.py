@@ -70,6 +70,7 @@ class Workload:
     ctx_hi: int
     layers: List[LayerGeom] = field(default_factory=list)
     tokens: int = 1  # query tokens per row (T > 1: multi-token decode)
+    kv_dtype: str = "bf16"  # "bf16" or "fp8" (e4m3 codes + float32 row scales)
 
     @property
     def num_layers(self) -> int:
@@ -146,6 +147,13 @@ ALL = [TINY, G3_1B_SLIDING, G4_12B_SLIDING, G4_12B_GLOBAL, HYBRID_48]
 HD128_SLIDING = Workload("hd128 sliding layer, B64 16q/8kv hd128 ring w1024 ctx U[512,8192]"
                          " softcap50", 6, 64, 512, 8192,
                          [sliding_geom(16, 8, 1024, softcap=50.0, head_dim=128)])
+
+# The 12B sliding layer over an fp8 cache (e4m3 codes, one float32 scale per row): half
+# the bytes per key (the fp8_e4m3 KV cache of the "Gemma 4 12B (unified multimodal)"
+# record, item "(2)").
+FP8_SLIDING = replace(G4_12B_SLIDING, name="gemma4-12b sliding layer, fp8 e4m3 cache with "
+                      "per-row scales, B64 16q/8kv hd256 ring w1024 ctx U[512,8192] softcap50",
+                      seed=8, kv_dtype="fp8")
 
 # Speculative verification on the 12B sliding layer: 7 draft tokens plus the current one
 # (T = 8, the k = 7 spec decode of the "Gemma 4 12B (unified multimodal)" record, item

@@ -218,6 +218,46 @@ int32_t gemma_kv_append_multi(const ga_shape* shape, int32_t num_tokens, ga_bf16
                               ga_bf16* v_cache, const ga_bf16* k_new, const ga_bf16* v_new,
                               const int32_t* pos, void* stream);
 
+/*
+ * Quantized (fp8) caches: each cached row is D e4m3 codes (OCP 8-bit float: 4 exponent
+ * bits with bias 7, 3 mantissa bits, largest finite 448, no infinities) plus one float32
+ * scale, and stands for the values code * scale.  Half the bytes of a bf16 cache per
+ * key.  Passages: the fp8_e4m3 KV cache (BF16 queries with FP8 KV on sliding-window
+ * layers, item "(2)") and the rotating quantized cache (item "(6)") of the "Gemma 4 12B
+ * (unified multimodal)" record.  The per-row scale is this library's choice.
+ *   k_codes  device uint8 [B, Hkv, capacity, D] (16-byte aligned)
+ *   k_scales device float32 [B, Hkv, capacity]
+ *   v_codes / v_scales  the same for V, or both NULL for K = V
+ *
+ * Quantizing append of T = num_tokens tokens per row (T = 1: one token), at positions
+ * pos[b] + t in order t = 0..T-1 (a later token landing in the same ring slot stays;
+ * out-of-range positions are skipped).  For each new row x (bf16 [D]): amax = max |x|,
+ * inv = 448 / amax (0 when amax = 0), code_d = round-to-nearest-even e4m3 of
+ * clamp(x_d * inv, -448, 448), scale = amax / 448, in float32 with correctly rounded
+ * division.  k_new, v_new: device bf16 [B, T, Hkv, D]; v_* NULL for K = V.
+ */
+int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* k_codes,
+                            float* k_scales, uint8_t* v_codes, float* v_scales,
+                            const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
+                            void* stream);
+
+/*
+ * Decode over fp8 caches: T = num_tokens query tokens per row (q [B, T, Hq, D], out
+ * [B, T, Hq, D], token t at q_pos[b] + t; T = 1 is single-token decode with q [B, Hq, D]).
+ * Same definition, with every cached value code * scale; the logits accumulate
+ * q . codes in float32 and multiply by the row's K scale, the value weights carry the
+ * row's V scale.  The vector kernel serves every shape (GA_IMPL_MFMA is refused).
+ * Workspace: ga_decode_fp8_workspace_bytes (same layout as the vector path's).
+ */
+size_t ga_decode_fp8_workspace_bytes(const ga_shape* shape, int32_t num_tokens, int32_t window,
+                                     const ga_decode_opts* opts);
+int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const ga_bf16* q,
+                              const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales,
+                              const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
+                              float softcap, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
+
 /* Precondition flags written by gemma_attn_validate, per batch row. */
 enum {
   GA_FLAG_QPOS_GE_CTX = 1, /* q_pos >= ctx                                         */

@@ -1,0 +1,202 @@
+"""GPU: fp8 e4m3 caches (codes + per-row float32 scales): the quantizing append bit for
+bit, and decode (one or several query tokens) against the fp64 oracle over the same codes.
+
+Parity cases poison every slot outside the valid set: codes 0x7f (NaN) and scale NaN, so
+a stray read turns the output NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_split_amd import api, synth
+from decode_attention_split_amd import workloads as wl
+
+from common import assert_parity, default_scale, errors, log
+
+pytestmark = pytest.mark.gpu
+
+FP8_NAN = 0x7F
+
+
+class Fp8Inputs:
+    """Random finite codes and positive row scales (host copies) and device tensors."""
+
+    def __init__(self, seed, B, T, Hq, Hkv, D, cap, k_eq_v, ctx, q0=None):
+        rng = np.random.default_rng(seed)
+        finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+        gen = synth.generator(seed)
+        self.q_bits = synth.bits(synth.normal_bf16(gen, (B, T, Hq, D)))
+        self.kc = rng.choice(finite, size=(B, Hkv, cap, D))
+        self.ks = rng.uniform(0.002, 0.02, (B, Hkv, cap)).astype(np.float32)
+        self.vc = None if k_eq_v else rng.choice(finite, size=(B, Hkv, cap, D))
+        self.vs = None if k_eq_v else rng.uniform(0.002, 0.02, (B, Hkv, cap)).astype(np.float32)
+        self.ctx = np.asarray(ctx, np.int32)
+        self.q0 = self.ctx - T if q0 is None else np.asarray(q0, np.int32)
+        self.T, self.cap = T, cap
+
+    def poison(self, window, kind):
+        for c, sc in [(self.kc, self.ks)] + ([(self.vc, self.vs)] if self.vc is not None else []):
+            for b in range(c.shape[0]):
+                keep = np.zeros(self.cap, bool)
+                for t in range(self.T):
+                    _, slots = oracle.valid_positions(self.ctx[b], self.q0[b] + t, window, kind,
+                                                      self.cap)
+                    keep[slots] = True
+                c[b][:, ~keep, :] = FP8_NAN
+                sc[b][:, ~keep] = np.nan
+        return self
+
+    def to_device(self):
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.q = synth.from_bits(self.q_bits, "cuda")
+        self.kc_d, self.ks_d, self.vc_d, self.vs_d = t(self.kc), t(self.ks), t(self.vc), t(self.vs)
+        self.ctx_t, self.q0_t = t(self.ctx), t(self.q0)
+        return self
+
+    def oracle(self, window, softcap, scale, kind, rows=None):
+        rows = np.arange(self.q_bits.shape[0]) if rows is None else np.asarray(rows)
+        pick = lambda a: None if a is None else a[rows]
+        out, _, _, flags = oracle.decode_fp8_multi(
+            self.q_bits[rows], self.kc[rows], self.ks[rows], pick(self.vc), pick(self.vs),
+            self.ctx[rows], self.q0[rows], window, softcap, scale, kind)
+        return out, flags
+
+    def run(self, window, softcap, scale, kind, **kw):
+        q = self.q[:, 0].contiguous() if self.T == 1 else self.q
+        out = api.decode_fp8(q, self.kc_d, self.ks_d, self.vc_d, self.vs_d, self.ctx_t, self.q0_t,
+                             window, softcap, scale, kind, **kw)
+        torch.cuda.synchronize()
+        return out.unsqueeze(1) if self.T == 1 else out
+
+
+@pytest.mark.parametrize("D", [128, 256, 512])
+@pytest.mark.parametrize("k_eq_v", [False, True])
+@pytest.mark.parametrize("T", [1, 4])
+def test_append_fp8_matches_oracle_bitwise(D, k_eq_v, T):
+    B, Hkv = 3, 2
+    for kind, cap, pos0 in [(api.RING, 8, [0, 5, 1001]), (api.LINEAR, 16, [-2, 3, 14])]:
+        gen = synth.generator(D + T + kind)
+        kn = synth.normal_bf16(gen, (B, T, Hkv, D)) * 3
+        kn[0, 0, 0] = 0  # an all-zero row: codes 0, scale 0
+        vn = None if k_eq_v else synth.normal_bf16(gen, (B, T, Hkv, D))
+        kc = np.full((B, Hkv, cap, D), 0x11, np.uint8)
+        ks = np.full((B, Hkv, cap), 7.0, np.float32)
+        vc, vs = (None, None) if k_eq_v else (kc.copy(), ks.copy())
+        dev = [None if a is None else torch.from_numpy(a.copy()).cuda() for a in (kc, ks, vc, vs)]
+        api.kv_append_fp8(dev[0], dev[1], dev[2], dev[3], kn.cuda(),
+                          None if vn is None else vn.cuda(),
+                          torch.tensor(pos0, dtype=torch.int32, device="cuda"), kind)
+        torch.cuda.synchronize()
+        oracle.append_fp8(kc, ks, synth.bits(kn), np.asarray(pos0, np.int32), kind)
+        assert np.array_equal(dev[0].cpu().numpy(), kc), (kind, "K codes")
+        assert np.array_equal(dev[1].cpu().numpy().view(np.uint32), ks.view(np.uint32)), \
+            (kind, "K scales")
+        if not k_eq_v:
+            oracle.append_fp8(vc, vs, synth.bits(vn), np.asarray(pos0, np.int32), kind)
+            assert np.array_equal(dev[2].cpu().numpy(), vc), (kind, "V codes")
+            assert np.array_equal(dev[3].cpu().numpy().view(np.uint32), vs.view(np.uint32))
+
+
+@pytest.mark.parametrize("D,G,Hkv", [(128, 4, 2), (256, 1, 2), (256, 2, 4), (256, 8, 1),
+                                     (512, 2, 1), (512, 16, 1)])
+@pytest.mark.parametrize("kind", [api.RING, api.LINEAR])
+@pytest.mark.parametrize("T", [1, 3])
+def test_fp8_decode_parity_sweep(D, G, Hkv, kind, T):
+    w = 100
+    if kind == api.RING:
+        cap, window = w + T - 1, w
+        ctx = [1, 37, w, w + 1, 5 * cap + 3]
+        max_ctx = max(ctx)
+    else:
+        cap, window = 500, (w if G <= 2 else 0)
+        ctx = [1, 37, 300, 499, 500]
+        max_ctx = cap
+    inp = Fp8Inputs(D + 10 * G + 100 * T + kind, len(ctx), T, G * Hkv, Hkv, D, cap, G == 16, ctx)
+    inp.poison(window, kind).to_device()
+    softcap = 30.0 if G % 2 == 0 else 0.0
+    ref, _ = inp.oracle(window, softcap, default_scale(D), kind)
+    for split in [0, 64]:
+        out = inp.run(window, softcap, default_scale(D), kind, max_ctx=max_ctx, split_keys=split)
+        assert_parity(out, ref, f"fp8 D={D} G={G} kind={kind} T={T} split={split}")
+
+
+def test_fp8_spec_decode_window_edges():
+    """BF16 queries, FP8 cache, 8 query tokens on a sliding window: the combination that
+    mis-selected window keys at some seq_len alignments in another engine."""
+    T, w = 8, 64
+    cap = w + T - 1
+    ctxs = [T, w - 1, w, w + 1, w + T - 1, 2 * w, 2 * w + 3, 3 * w + T, 5 * w - 1]
+    inp = Fp8Inputs(55, len(ctxs), T, 16, 8, 256, cap, False, ctxs)
+    inp.poison(w, api.RING).to_device()
+    ref, flags = inp.oracle(w, 50.0, 1.0 / 16, api.RING)
+    assert not flags.any()
+    for split in [0, 64]:
+        out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=max(ctxs), split_keys=split)
+        assert_parity(out, ref, f"fp8 spec split={split}")
+
+
+def test_fp8_equals_bf16_kernel_on_exactly_representable_values():
+    """With power-of-two row scales every code * scale is a bf16 value: the fp8 and bf16
+    kernels then see the same numbers (rounding order aside)."""
+    B, Hq, Hkv, D, cap = 4, 16, 8, 256, 256
+    rng = np.random.default_rng(5)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    kc = rng.choice(finite, size=(B, Hkv, cap, D))
+    vc = rng.choice(finite, size=(B, Hkv, cap, D))
+    ks = np.ldexp(1.0, rng.integers(-8, -3, (B, Hkv, cap))).astype(np.float32)
+    vs = np.ldexp(1.0, rng.integers(-8, -3, (B, Hkv, cap))).astype(np.float32)
+    tv = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).float()
+    kb = (tv(kc) * torch.from_numpy(ks)[..., None]).to(torch.bfloat16).cuda()
+    vb = (tv(vc) * torch.from_numpy(vs)[..., None]).to(torch.bfloat16).cuda()
+    q = synth.normal_bf16(synth.generator(6), (B, Hq, D)).cuda()
+    ctx = torch.tensor([1, 100, 255, 256], dtype=torch.int32, device="cuda")
+    a = api.decode_fp8(q, torch.from_numpy(kc).cuda(), torch.from_numpy(ks).cuda(),
+                       torch.from_numpy(vc).cuda(), torch.from_numpy(vs).cuda(), ctx, ctx - 1, 0,
+                       0.0, 0.0625, api.LINEAR)
+    b = api.decode(q, kb, vb, ctx, ctx - 1, 0, 0.0, 0.0625, api.LINEAR)
+    torch.cuda.synchronize()
+    max_abs, rel = errors(a, b.double().cpu().numpy())
+    # two float32 sums of the same terms in different orders; outputs reach ~30 in size
+    assert max_abs < 1e-4 and rel < 1e-5, (max_abs, rel)
+
+
+def test_fp8_sliding_layer_full_size_sampled_rows():
+    """The 12B sliding-layer geometry (B 64, 16q/8kv, hd256, ring W = w = 1024, ctx
+    U[512, 8192], soft-cap 50) on an fp8 cache filled by one quantizing append of 1024
+    tokens per row; sampled rows checked against the oracle (codes and outputs)."""
+    w = wl.G4_12B_SLIDING
+    g = w.layers[0]
+    B, Hkv, D, W = w.batch, g.num_kv_heads, g.head_dim, g.capacity
+    ctx = synth.uniform_int(synth.generator(w.seed), B, w.ctx_lo, w.ctx_hi).numpy() \
+        .astype(np.int32)
+    gd = synth.generator(77, device="cuda")
+    kc = torch.empty((B, Hkv, W, D), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty((B, Hkv, W), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    ctx_t = torch.from_numpy(ctx).cuda()
+    pos0 = ctx_t - W  # the newest W positions of every row
+    kn = synth.normal_bf16(gd, (B, W, Hkv, D), device="cuda")
+    vn = synth.normal_bf16(gd, (B, W, Hkv, D), device="cuda")
+    api.kv_append_fp8(kc, ks, vc, vs, kn, vn, pos0, api.RING)
+    q = synth.normal_bf16(gd, (B, g.num_q_heads, D), device="cuda")
+    out = api.decode_fp8(q, kc, ks, vc, vs, ctx_t, ctx_t - 1, g.window, g.softcap, g.q_scale,
+                         g.kind, max_ctx=w.ctx_hi)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, int(np.argmax(ctx)), int(np.argmin(ctx))})
+    log(f"fp8 sliding rows {rows}")
+    kcr, ksr = kc[rows].cpu().numpy(), ks[rows].cpu().numpy()
+    vcr, vsr = vc[rows].cpu().numpy(), vs[rows].cpu().numpy()
+    # the cache holds exactly the oracle's quantization of the appended rows
+    for i, b in enumerate(rows):
+        for t in (0, 517, W - 1):
+            if int(ctx[b]) - W + t < 0:
+                continue  # negative positions are skipped by the append
+            slot = (int(ctx[b]) - W + t) % W
+            c, s = oracle.quantize_rows_fp8(synth.bits(kn[b, t].cpu()))
+            assert np.array_equal(kcr[i, :, slot], c) and np.array_equal(ksr[i, :, slot], s)
+    ref, _, _, _ = oracle.decode_fp8_multi(synth.bits(q[rows].cpu()), kcr, ksr, vcr, vsr,
+                                           ctx[rows], ctx[rows] - 1, g.window, g.softcap,
+                                           g.q_scale, g.kind)
+    assert_parity(out[rows], ref, "fp8 sliding full size")
