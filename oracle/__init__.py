@@ -66,6 +66,10 @@ def _load():
     lib.oracle_e4m3_to_f64.restype = f64
     lib.oracle_f32_to_e4m3.argtypes = [f32]
     lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_f64_to_bf16.argtypes = [f64]
+    lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_rope_row.argtypes = [ctypes.c_int, P, ctypes.c_long, f64, ctypes.c_int, P, P]
+    lib.oracle_rope_row.restype = None
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = f64
     lib.oracle_num_threads_default.restype = ctypes.c_int
@@ -237,6 +241,32 @@ def decode_fp8_multi(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos0, 
     if single:
         return out[:, 0], lse[:, 0], None if probs is None else probs[:, 0], flags[:, 0]
     return out, lse, probs, flags
+
+
+def f64_to_bf16(x: float) -> int:
+    """bf16 bits of the double x rounded to nearest, ties to even."""
+    return int(_load().oracle_f64_to_bf16(float(x)))
+
+
+def rope(x_bits, positions, base, rotary_dim):
+    """Rotary embedding of bf16 rows x [..., D] (uint16 bits) at positions (broadcast over
+    the row index: one position per row of x.reshape(-1, D)).  Returns (bf16 bits, float64
+    values before rounding)."""
+    lib = _load()
+    x = _u16(x_bits)
+    D = x.shape[-1]
+    flat = x.reshape(-1, D)
+    pos = np.broadcast_to(np.asarray(positions, np.int64).reshape(-1), (flat.shape[0],))
+    out = np.zeros(flat.shape, np.uint16)
+    out64 = np.zeros(flat.shape, np.float64)
+    for r in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[r])
+        o = np.zeros((D,), np.uint16)
+        o64 = np.zeros((D,), np.float64)
+        lib.oracle_rope_row(D, _ptr(row), int(pos[r]), float(base), int(rotary_dim), _ptr(o),
+                            _ptr(o64))
+        out[r], out64[r] = o, o64
+    return out.reshape(x.shape), out64.reshape(x.shape)
 
 
 def append_tokens(cache, new_rows, pos0, kind):

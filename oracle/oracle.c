@@ -49,6 +49,16 @@
  * 4 12B (unified multimodal)" record; the per-row dynamic scale is a reading (the pages
  * give no scale granularity).
  *
+ * Rotary position embedding (oracle_rope_row): sliding layers use base 10,000 over the
+ * whole head, full layers base 1,000,000 applied as a partial rotary to the low part of
+ * the head dimension with no positional encoding on the rest ("Gemma support" pull
+ * request, Summary: own RoPE base for sliding layers, proportional RoPE; "Gemma4-26B-A4B
+ * on Apple Silicon", Results (Break 4): dual bases, partial rotary on full layers, and
+ * Ablations / negative controls: the rotary acts on the low portion of the head dimension;
+ * the model-loader page's header: bases 10,000 and 1,000,000).  Readings: the first R (even) elements rotate in rotate-half pairs
+ * (i, i + R/2), angle p * base^(-2i/R) for i < R/2; the rest pass through; computed in
+ * double and rounded once to bf16 (round to nearest even).
+ *
  * Arithmetic: every bf16 input is widened exactly (bits << 16 -> float -> double);
  * scale and softcap are widened from their float32 values; libm exp, tanh, log in
  * double.  Results are double; callers round to float32 where they need to.
@@ -168,6 +178,38 @@ uint8_t oracle_f32_to_e4m3(float x) {
     E += 1;
   }
   return (uint8_t)(sgn | ((E + 7) << 3) | (int)m);
+}
+
+/* Round a double to the nearest bf16 (ties to even), directly (no float step, so no
+ * double rounding); inputs here are finite and far from the bf16 range limits. */
+uint16_t oracle_f64_to_bf16(double x) {
+  if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+  int e;
+  const double f = frexp(fabs(x), &e);       /* |x| = f * 2^e, f in [0.5, 1) */
+  const double m = nearbyint(ldexp(f, 8));   /* 8 significant bits, ties to even: 128..256 */
+  const float r = (float)ldexp(m, e - 8);    /* exactly representable */
+  uint32_t u;
+  memcpy(&u, &r, 4);
+  return (uint16_t)((u >> 16) | (signbit(x) ? 0x8000 : 0));
+}
+
+/* Rotary embedding of one bf16 row x[D] at position p (see header): out_bf16 [D] gets the
+ * rounded result, out_f64 [D] (may be NULL) the unrounded one. */
+void oracle_rope_row(int D, const uint16_t* x, long p, double base, int R, uint16_t* out_bf16,
+                     double* out_f64) {
+  for (int d = 0; d < D; ++d) {
+    double y = oracle_bf16_to_f64(x[d]);
+    if (d < R) {
+      const int half = R / 2;
+      const int i = d < half ? d : d - half;
+      const double ang = (double)p * pow(base, -2.0 * i / R);
+      const double c = cos(ang), s = sin(ang);
+      const double a = oracle_bf16_to_f64(x[i]), b = oracle_bf16_to_f64(x[i + half]);
+      y = d < half ? a * c - b * s : b * c + a * s;
+    }
+    if (out_f64) out_f64[d] = y;
+    out_bf16[d] = oracle_f64_to_bf16(y);
+  }
 }
 
 /* Quantize one bf16 row of D values to e4m3 codes and a float32 scale (see header). */
