@@ -45,8 +45,10 @@ def parse_args():
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
     p.add_argument("--command", default="", help="command line recorded in summaries")
-    p.add_argument("--workload", default="hybrid48", choices=sorted(SINGLE_LAYER) + ["hybrid48"],
-                   help="hybrid48: the 48-layer step (default); others: one layer type")
+    p.add_argument("--workload", default="hybrid48",
+                   choices=sorted(SINGLE_LAYER) + ["hybrid48", "hybrid48_rope"],
+                   help="hybrid48: the 48-layer step (default); hybrid48_rope: the same step "
+                        "with the rotary embedding fused into each append; others: one layer")
     return p.parse_args()
 
 
@@ -179,7 +181,7 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the per-GPU workload is the whole step at its real shape)", file=sys.stderr)
         sys.exit(2)
-    if args.workload != "hybrid48":
+    if args.workload not in ("hybrid48", "hybrid48_rope"):
         bench_single_layer(args)
         return
     import numpy as np
@@ -195,7 +197,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = wl.HYBRID_48
+    rope = args.workload == "hybrid48_rope"
+    w = wl.HYBRID_48_ROPE if rope else wl.HYBRID_48
     B, L = w.batch, w.num_layers
 
     # ---- inputs, resident in HBM before timing
@@ -230,12 +233,21 @@ def main():
         del src, dst
 
     per_layer = [layer_bytes(g, B, ctx) for g in w.layers]
+    if rope:  # the fused rotary pass also reads q and writes the rotated q
+        for g, x in zip(w.layers, per_layer):
+            x["append"] += 2 * B * g.num_q_heads * g.head_dim * 2
     step_bytes = sum(x["decode"] + x["append"] for x in per_layer)
+    q_rot = [torch.empty_like(q) for q in qs] if rope else None
     sliding = [i for i, g in enumerate(w.layers) if not g.k_eq_v]
 
     stream = torch.cuda.current_stream()
 
     def step():
+        if rope:  # per layer: fused rotary + append, then decode with the rotated q
+            for li in range(L):
+                cache.rope_append(li, qs[li], q_rot[li], k_new[li], v_new[li], pos_t)
+                cache.decode(li, q_rot[li], ctx_t, qpos_t, out=outs[li])
+            return
         # per layer, one launch: append the current token to the cache and attend
         for li in range(L):
             cache.decode_append(li, qs[li], k_new[li], v_new[li], pos_t, ctx_t, qpos_t,
@@ -290,8 +302,8 @@ def main():
     torch.cuda.synchronize()
     n_launch = kern_steps * len(sliding)
     kern_ms = k0.elapsed_time(k1) / n_launch
-    kern_bytes = float(np.mean([per_layer[li]["decode"] + per_layer[li]["append"]
-                                for li in sliding]))
+    kern_bytes = float(np.mean([sum(layer_bytes(w.layers[li], B, ctx)[k]
+                                    for k in ("decode", "append")) for li in sliding]))
     kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"sliding decode kernel: {kern_ms * 1e3:.2f} us avg over {n_launch} launches, "
         f"{kern_gbps:.1f} GB/s")
@@ -311,7 +323,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "48-layer hybrid decode step (append + decode per layer): 40 sliding "
+            "workload": ("rotary embedding fused with the append, then decode, per layer "
+                         "(sliding base 1e4 over 256, global base 1e6 over 128); " if rope
+                         else "") +
+                        "48-layer hybrid decode step (append + decode per layer): 40 sliding "
                         "layers 16q/8kv hd256 ring w=W=1024 + 8 global layers 16q/1kv K=V "
                         "hd512 linear C=16384 at l%6==5; batch 32; ctx U[1,16384] seed 5; "
                         "no softcap; scale 1/sqrt(hd)",

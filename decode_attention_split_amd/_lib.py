@@ -29,7 +29,7 @@ EXPORTS = ["ga_decode_workspace_bytes", "gemma_attn_decode", "gemma_attn_decode_
            "gemma_attn_strerror", "gemma_attn_version",
            "ga_decode_multi_workspace_bytes", "gemma_attn_decode_multi", "gemma_kv_append_multi",
            "gemma_attn_validate_multi", "gemma_kv_append_fp8", "ga_decode_fp8_workspace_bytes",
-           "gemma_attn_decode_fp8"]
+           "gemma_attn_decode_fp8", "gemma_rope_append"]
 
 _lib = None
 
@@ -77,6 +77,8 @@ def load():
     lib.gemma_attn_decode_fp8.argtypes = [SP, i32, P, P, P, P, P, P, P, i32, f32, f32, P, P, sz,
                                           OP, P]
     lib.gemma_attn_decode_fp8.restype = i32
+    lib.gemma_rope_append.argtypes = [SP, i32, P, P, P, P, P, P, P, f32, i32, P]
+    lib.gemma_rope_append.restype = i32
     lib.gemma_attn_strerror.argtypes = [i32]
     lib.gemma_attn_strerror.restype = ctypes.c_char_p
     lib.gemma_attn_version.argtypes = []

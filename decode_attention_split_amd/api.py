@@ -357,6 +357,47 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos, window:
     return out
 
 
+def rope_append(q, q_out, k_cache, v_cache, k_new, v_new, pos, kind: int, rope_base: float,
+                rotary_dim: int, stream=None):
+    """Rotary embedding of q (-> q_out, may be q) and k_new fused with the append of T
+    tokens per row at pos[b] + t; q [B, Hq, D] or [B, T, Hq, D], k_new / v_new [B, Hkv, D]
+    or [B, T, Hkv, D] (see gemma_rope_append)."""
+    single = q.dim() == 3
+    q4 = q.unsqueeze(1) if single else q
+    o4 = q_out.unsqueeze(1) if single else q_out
+    kn = None if k_new is None else (k_new.unsqueeze(1) if k_new.dim() == 3 else k_new)
+    vn = None if v_new is None else (v_new.unsqueeze(1) if v_new.dim() == 3 else v_new)
+    _need(q4, "q", torch.bfloat16, 4)
+    _need(o4, "q_out", torch.bfloat16, 4)
+    _need(pos, "pos", torch.int32, 1)
+    B, T, Hq, D = q4.shape
+    if (v_cache is None) != (vn is None):
+        _check(-9, "gemma_rope_append")
+    if k_cache is None:  # rotate q only
+        if kn is not None or v_cache is not None:
+            raise ValueError("k_new / v_cache need a k_cache")
+        Hkv, cap = Hq, 1
+    else:
+        _need(k_cache, "k_cache", torch.bfloat16, 4)
+        _need(kn, "k_new", torch.bfloat16, 4)
+        if v_cache is not None:
+            _need(v_cache, "v_cache", torch.bfloat16, 4)
+            _need(vn, "v_new", torch.bfloat16, 4)
+        Bk, Hkv, cap, Dk = k_cache.shape
+        if tuple(kn.shape) != (B, T, Hkv, D) or Bk != B or Dk != D or \
+                (vn is not None and (vn.shape != kn.shape or v_cache.shape != k_cache.shape)):
+            raise ValueError("shape mismatch (new rows [B,T,Hkv,D], caches [B,Hkv,cap,D])")
+    if o4.shape != q4.shape or pos.numel() != B:
+        raise ValueError("q_out must have q's shape and pos one entry per row")
+    shape = make_shape(B, Hq, Hkv, D, cap, kind)
+    rc = _lib.load().gemma_rope_append(ctypes.byref(shape), int(T), _ptr(q4), _ptr(o4),
+                                       _ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn),
+                                       _ptr(pos), float(rope_base), int(rotary_dim),
+                                       _stream_handle(stream))
+    _check(rc, "gemma_rope_append")
+    return q_out
+
+
 def kv_append(k_cache, v_cache, k_new, v_new, pos, kind: int, stream=None):
     """cache[b, g, slot(pos_b), :] <- new[b, g, :] for K (and V unless K = V)."""
     _need(k_cache, "k_cache", torch.bfloat16, 4)

@@ -522,6 +522,37 @@ int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* 
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
 }
 
+int32_t gemma_rope_append(const ga_shape* shape, int32_t num_tokens, const ga_bf16* q,
+                          ga_bf16* q_out, ga_bf16* k_cache, ga_bf16* v_cache,
+                          const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
+                          float rope_base, int32_t rotary_dim, void* stream) {
+  if (!shape) return GA_ERR_NULL;
+  if (shape->batch < 0 || shape->num_kv_heads <= 0 || shape->num_q_heads <= 0 ||
+      shape->capacity <= 0 || num_tokens < 1)
+    return GA_ERR_DIMS;
+  if (num_tokens > kMaxTokens) return GA_ERR_TOO_LARGE;
+  if (!head_dim_ok(shape->head_dim)) return GA_ERR_HEAD_DIM;
+  if (shape->num_q_heads % shape->num_kv_heads != 0) return GA_ERR_GQA;
+  if (shape->kind != GA_CACHE_LINEAR && shape->kind != GA_CACHE_RING) return GA_ERR_KIND;
+  if (rotary_dim < 0 || rotary_dim > shape->head_dim || rotary_dim % 2 != 0 ||
+      !(rope_base > 0.0f) || !std::isfinite(rope_base))
+    return GA_ERR_OPTS;
+  if (!q || !q_out || !pos) return GA_ERR_NULL;
+  if ((k_cache == nullptr) != (k_new == nullptr)) return GA_ERR_NULL;  // q only: both NULL
+  if ((v_cache == nullptr) != (v_new == nullptr)) return GA_ERR_V_MISMATCH;
+  if (!k_cache && v_cache) return GA_ERR_V_MISMATCH;
+  if ((long long)shape->batch * num_tokens * (shape->num_q_heads + 2LL * shape->num_kv_heads) >
+      (1LL << 31) - 1)
+    return GA_ERR_TOO_LARGE;
+  int32_t st = check_arch();
+  if (st != GA_OK) return st;
+  hipError_t e = ga::rope_append_launch(
+      shape->batch, num_tokens, shape->num_q_heads, shape->num_kv_heads, shape->head_dim,
+      shape->capacity, shape->kind, rotary_dim, (double)rope_base, q, q_out, k_cache, v_cache,
+      k_new, v_new, pos, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
 int32_t gemma_attn_validate_multi(const ga_shape* shape, int32_t num_tokens,
                                   const int32_t* ctx_lens, const int32_t* q_pos, int32_t window,
                                   int32_t* dev_flags, void* stream) {

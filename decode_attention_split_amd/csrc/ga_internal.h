@@ -162,6 +162,13 @@ hipError_t append_fp8_launch(int B, int T, int Hkv, int D, int cap, int kind, ui
                              const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos,
                              hipStream_t stream);
 
+// Rotary embedding of q (-> q_out) and of k_new fused with the append of T tokens per row
+// at positions pos[b] + t (v_new appended unrotated; v_cache nullptr for K = V).
+hipError_t rope_append_launch(int B, int T, int Hq, int Hkv, int D, int cap, int kind, int R,
+                              double base, const uint16_t* q, uint16_t* q_out, uint16_t* k_cache,
+                              uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
+                              const int32_t* pos, hipStream_t stream);
+
 // Flags of the B * T query tokens at positions q_pos[b] + t.
 hipError_t validate_launch(int B, int T, int cap, int kind, int window, int max_ctx,
                            const int32_t* ctx, const int32_t* q_pos, int32_t* flags,

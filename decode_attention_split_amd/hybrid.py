@@ -113,10 +113,31 @@ class HybridKVCache:
                                  max_ctx=self.shape(g).max_ctx, split_keys=split_keys, impl=impl,
                                  deterministic=deterministic, stream=stream)
 
+    def rope_append(self, layer: int, q, q_out, k_new, v_new, pos, stream=None):
+        """Rotary embedding of q (-> q_out) and of the new K row, fused with the append (a
+        layer that shares another's cache only rotates q)."""
+        g = self.layers[layer]
+        if not self.owns_cache(layer):
+            return api.rope_append(q, q_out, None, None, None, None, pos, g.kind, g.rope_base,
+                                   g.rotary_dim, stream=stream)
+        return api.rope_append(q, q_out, self.k[layer], self.v[layer], k_new,
+                               None if g.k_eq_v else v_new, pos, g.kind, g.rope_base,
+                               g.rotary_dim, stream=stream)
+
     def step(self, q_list, k_new_list, v_new_list, pos, ctx_lens, q_pos, outs, stream=None,
-             fused=True, deterministic=False):
-        """One decode step through every layer: append the new token, then attend."""
+             fused=True, deterministic=False, q_rot=None):
+        """One decode step through every layer: append the new token, then attend.  Layers
+        with a rotary embedding (rope_base > 0) run the fused rotary + append, then decode
+        with the rotated q (written to q_rot[layer], or in place when q_rot is None)."""
         for li in range(len(self.layers)):
+            g = self.layers[li]
+            if g.rope_base > 0:
+                qo = q_list[li] if q_rot is None else q_rot[li]
+                self.rope_append(li, q_list[li], qo, k_new_list[li], v_new_list[li], pos,
+                                 stream=stream)
+                self.decode(li, qo, ctx_lens, q_pos, out=outs[li], deterministic=deterministic,
+                            stream=stream)
+                continue
             if fused:
                 self.decode_append(li, q_list[li], k_new_list[li], v_new_list[li], pos, ctx_lens,
                                    q_pos, out=outs[li], deterministic=deterministic,

@@ -46,6 +46,8 @@ class LayerGeom:
     k_eq_v: bool         # one cached tensor serves as keys and values
     softcap: float = 0.0  # <= 0: off
     scale: Optional[float] = None  # None: 1/sqrt(head_dim)
+    rope_base: float = 0.0  # > 0: rotary embedding applied by the step (base)
+    rotary_dim: int = 0     # rotated elements at the low end of the head (even)
 
     @property
     def q_scale(self) -> float:
@@ -83,6 +85,19 @@ def sliding_geom(num_q, num_kv, window, softcap=0.0, scale=None, head_dim=256):
 
 def global_geom(num_q, capacity, head_dim=512, num_kv=1, softcap=0.0, scale=None):
     return LayerGeom(num_q, num_kv, head_dim, LINEAR, capacity, 0, True, softcap, scale)
+
+
+def with_rope(g: LayerGeom, base: float, rotary_dim: int) -> LayerGeom:
+    return replace(g, rope_base=float(base), rotary_dim=int(rotary_dim))
+
+
+# Rotary embedding per layer type: sliding layers base 10,000 over the whole head, full
+# layers base 1,000,000 on the low part of the head ("Gemma support" pull request, Summary;
+# "Gemma4-26B-A4B on Apple Silicon", Results (Break 4) and Ablations / negative controls;
+# the model-loader page's header).  The pages do not give the rotated fraction of a full
+# layer's head; a quarter (128 of 512) is this reading.
+SLIDING_ROPE_BASE, GLOBAL_ROPE_BASE = 1e4, 1e6
+GLOBAL_ROTARY_FRACTION = 4
 
 
 def gemma4_12b_layer_types(num_layers: int = 48, period: int = 6) -> List[str]:
@@ -141,6 +156,14 @@ HYBRID_48 = Workload("48-layer hybrid decode step, B32 ctx U[1,16384]: 40 slidin
                      hybrid_layers(48, sliding_geom(16, 8, 1024), global_geom(16, 16384)))
 
 ALL = [TINY, G3_1B_SLIDING, G4_12B_SLIDING, G4_12B_GLOBAL, HYBRID_48]
+
+# The 48-layer step with the rotary embedding fused into each layer's append.
+HYBRID_48_ROPE = replace(
+    HYBRID_48, name=HYBRID_48.name + "; rotary embedding fused with the append (sliding base "
+    "1e4 over 256, global base 1e6 over 128)",
+    layers=hybrid_layers(48, with_rope(sliding_geom(16, 8, 1024), SLIDING_ROPE_BASE, 256),
+                         with_rope(global_geom(16, 16384), GLOBAL_ROPE_BASE,
+                                   512 // GLOBAL_ROTARY_FRACTION)))
 
 # Extra single-layer workloads for the head sizes the kernel tests span (128 to 512):
 # the long-context sliding layer of the 12B geometry at head_dim 128.

@@ -258,6 +258,29 @@ int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const g
                               float softcap, float scale, float* out, void* workspace,
                               size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
 
+/*
+ * Rotary position embedding fused with the cache append, one launch for T = num_tokens
+ * tokens per row at positions pos[b] + t (T = 1: decode):
+ *   q_out[b,t,h,:] = rope(q[b,t,h,:], pos[b] + t)            (q, q_out [B, T, Hq, D])
+ *   k_cache[b,g,slot(pos[b]+t),:] = rope(k_new[b,t,g,:], ...) (k_new [B, T, Hkv, D])
+ *   v_cache[...] = v_new[b,t,g,:] unrotated (v_cache and v_new NULL for K = V)
+ * rope(x, p): the first R = rotary_dim elements (even, 0 <= R <= D) rotate in rotate-half
+ * pairs (i, i + R/2) by the angle p * rope_base^(-2i/R); elements R..D-1 pass through.
+ * Sliding layers: base 10,000 over the whole head; full layers: base 1,000,000 on the low
+ * part of the head only ("Gemma support" pull request, Summary: own RoPE base for sliding
+ * layers, proportional RoPE; "Gemma4-26B-A4B on Apple Silicon", Results (Break 4) and
+ * Ablations / negative controls; the pair layout and the frequency exponent over R are
+ * this library's reading).  Computed in double, rounded once to bf16 (nearest, ties to
+ * even).  q_out may equal q (in place).  Append rules as in gemma_kv_append_multi
+ * (out-of-range positions skipped; the latest token owns a shared ring slot).  One pass
+ * over q and the new rows replaces a rotary pass plus an append pass.  k_cache, k_new,
+ * v_cache and v_new all NULL rotates q only (a layer that reads another layer's cache).
+ */
+int32_t gemma_rope_append(const ga_shape* shape, int32_t num_tokens, const ga_bf16* q,
+                          ga_bf16* q_out, ga_bf16* k_cache, ga_bf16* v_cache,
+                          const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
+                          float rope_base, int32_t rotary_dim, void* stream);
+
 /* Precondition flags written by gemma_attn_validate, per batch row. */
 enum {
   GA_FLAG_QPOS_GE_CTX = 1, /* q_pos >= ctx                                         */
