@@ -160,9 +160,10 @@ __global__ void __launch_bounds__(64)
 // Results (Break 4) and Ablations / negative controls: partial rotary on the low part of
 // the head dimension on full layers).  The first R elements rotate in rotate-half pairs
 // (i, i + R/2) by pos * base^(-2i/R); the rest pass through; double precision, rounded once
-// to bf16 (nearest, ties to even).  One 64-lane block per row: q rows -> q_out, k rows ->
-// their cache slot, v rows copied unrotated to theirs (no k / v rows without a cache).  Each lane loads its elements and
-// their partners before a barrier and stores after it, so q_out may alias q.
+// to bf16 (nearest, ties to even).  One block of D threads per row (a thread per element):
+// q rows -> q_out, k rows -> their cache slot, v rows copied unrotated to theirs (no k / v
+// rows without a cache).  Every thread reads its element and its partner before a barrier
+// and writes after it, so q_out may alias q.
 
 // double -> bf16 bits, nearest with ties to even, in one rounding
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
@@ -174,14 +175,13 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return (uint16_t)((__float_as_uint(r) >> 16) | (signbit(x) ? 0x8000u : 0u));
 }
 
-constexpr int kRopeMaxPerLane = 512 / 64;  // elements per lane at the largest head dim
-
-__global__ void __launch_bounds__(64)
+// One thread per element (blockDim.x = D), one block per row.
+__global__ void __launch_bounds__(512)
     rope_append_kernel(int B, int T, int Hq, int Hkv, int D, int cap, int kind, int R,
                        double base, const uint16_t* q, uint16_t* q_out, uint16_t* k_cache,
                        uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
                        const int32_t* pos) {
-  const int lane = threadIdx.x;
+  const int d = threadIdx.x;
   const int rows_per_tok = Hq + (k_cache ? Hkv : 0) + (v_cache ? Hkv : 0);
   const long long row = blockIdx.x;  // ((b * T + t) * rows_per_tok + r)
   const int r = (int)(row % rows_per_tok);
@@ -207,32 +207,19 @@ __global__ void __launch_bounds__(64)
     dst = (is_k ? k_cache : v_cache) + (((long long)b * Hkv + g) * cap + slot) * D;
     rotate = is_k;
   }
-  const int half = R / 2;
-  uint16_t y[kRopeMaxPerLane];
-#pragma unroll
-  for (int k = 0; k < kRopeMaxPerLane; ++k) {
-    const int d = lane + 64 * k;
-    if (d >= D) break;
-    const uint16_t xd = src[d];
-    if (!rotate || d >= R) {
-      y[k] = xd;
-      continue;
-    }
+  uint16_t y = src[d];
+  if (rotate && d < R) {
+    const int half = R / 2;
     const int i = d < half ? d : d - half;
     const double a = (double)__uint_as_float((uint32_t)src[i] << 16);
     const double bb = (double)__uint_as_float((uint32_t)src[i + half] << 16);
     const double ang = (double)p * pow(base, -2.0 * i / R);
     double sn, cs;
     sincos(ang, &sn, &cs);
-    y[k] = f64_to_bf16(d < half ? a * cs - bb * sn : bb * cs + a * sn);
+    y = f64_to_bf16(d < half ? a * cs - bb * sn : bb * cs + a * sn);
   }
   __syncthreads();  // every element and partner of the row is read before any write
-#pragma unroll
-  for (int k = 0; k < kRopeMaxPerLane; ++k) {
-    const int d = lane + 64 * k;
-    if (d >= D) break;
-    dst[d] = y[k];
-  }
+  dst[d] = y;
 }
 
 // Precondition flags of every query token (b, t) at position q_pos[b] + t.
@@ -308,7 +295,7 @@ hipError_t rope_append_launch(int B, int T, int Hq, int Hkv, int D, int cap, int
                               const int32_t* pos, hipStream_t stream) {
   const long long rows = (long long)B * T * (Hq + (k_cache ? Hkv : 0) + (v_cache ? Hkv : 0));
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)rows), dim3(64), 0, stream, B, T, Hq, Hkv,
+  hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)rows), dim3(D), 0, stream, B, T, Hq, Hkv,
                      D, cap, kind, R, base, q, q_out, k_cache, v_cache, k_new, v_new, pos);
   return hipGetLastError();
 }
