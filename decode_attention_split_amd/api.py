@@ -188,7 +188,7 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, windo
 
 def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
                  kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
-                 deterministic: bool = False, stream=None):
+                 deterministic: bool = False, impl: int = IMPL_AUTO, stream=None):
     """T query tokens per row: q [B, T, Hq, D], token t at position q_pos[b] + t; returns
     out [B, T, Hq, D] float32 (see gemma_attn_decode_multi in gemma_attn.h)."""
     _need(q, "q", torch.bfloat16, 4)
@@ -212,7 +212,7 @@ def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: flo
         _need(out, "out", torch.float32, 4)
         if tuple(out.shape) != (B, T, Hq, D):
             raise ValueError("out must be [B, T, Hq, D]")
-    opts = make_opts(split_keys, IMPL_AUTO, deterministic)
+    opts = make_opts(split_keys, impl, deterministic)
     lib = _lib.load()
     need = lib.ga_decode_multi_workspace_bytes(ctypes.byref(shape), int(T), int(window),
                                                ctypes.byref(opts))

@@ -14,8 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgemma_attn.so")
 SOURCES = ["api.hip", "decode_valu.hip", "decode_valu_d128.hip", "decode_valu_d256.hip",
-           "decode_valu_d512.hip", "decode_mfma.hip", "merge_append.hip"]
-HEADERS = ["ga_device.h", "ga_internal.h", "decode_valu_impl.h"]
+           "decode_valu_d512.hip", "decode_mfma.hip", "decode_rows16.hip", "merge_append.hip"]
+HEADERS = ["ga_device.h", "ga_internal.h", "ga_mfma.h", "decode_valu_impl.h"]
 
 HIPCC = "/opt/rocm/bin/hipcc"
 HIPCC_FLAGS = [

@@ -92,6 +92,7 @@ struct Plan {
   int T = 1;       // query tokens per row
   int Tc = 1;      // tokens per unit (multi-token)
   int n_chunks = 1;
+  bool rows16 = false;  // multi-token on the matrix cores (16 query rows per unit)
   size_t ws_bytes;
 };
 
@@ -160,6 +161,43 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   return GA_OK;
 }
 
+constexpr int kRows16Waves = 2048;  // one-wave work-groups wanted (8 per CU)
+
+// Several tokens on the matrix cores: 16 query rows per unit (16 / G tokens of G heads),
+// splits sized so that about kRows16Waves single-wave work-groups cover the chip.
+int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int Tc = 16 / G;
+  const int n_chunks = (T + Tc - 1) / Tc;
+  long long nmax = max_keys_bound(s, 0);
+  if (window > 0 && nmax > (long long)window + Tc - 1) nmax = (long long)window + Tc - 1;
+  const long long units = (long long)s->batch * s->num_kv_heads * n_chunks;
+  if (ts == 0) {
+    const long long want = units > 0 ? (kRows16Waves + units - 1) / units : 1;
+    long long t = nmax > 0 ? (nmax + want - 1) / want : 64;
+    t = (t + 63) / 64 * 64;
+    if (t < 64) t = 64;
+    if (t > kMaxSplitKeys) t = kMaxSplitKeys;
+    ts = (int)t;
+  }
+  long long S = nmax > 0 ? (nmax + ts - 1) / ts : 1;
+  if (S < 1) S = 1;
+  if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
+  p->impl = GA_IMPL_MFMA;
+  p->rows16 = true;
+  p->n_waves = 0;
+  p->split_keys = ts;
+  p->n_split = (int)S;
+  p->max_keys = (int)(S * ts);
+  p->T = T;
+  p->Tc = Tc;
+  p->n_chunks = n_chunks;
+  p->ws_bytes = S > 1 ? (size_t)s->batch * T * s->num_q_heads * (size_t)S *
+                            (size_t)(s->head_dim + 2) * 4u
+                      : 0;
+  return GA_OK;
+}
+
 void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
   long long nmax = max_keys_bound(s, window);
   p->impl = GA_IMPL_MFMA;
@@ -184,9 +222,31 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
     if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
     if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
   }
-  if (T > 1 || vector_only) {
-    // several query tokens (per-row masks) or an fp8 cache: the vector kernel
+  if (vector_only) {  // fp8 caches: the vector kernel
     if (impl == GA_IMPL_MFMA) return GA_ERR_OPTS;
+    return valu_plan(s, window, ts, T, p);
+  }
+  if (T > 1) {
+    // several query tokens (per-row masks): 16 query rows per unit on the matrix cores
+    // when heads x tokens fill at least half of them, else the vector kernel
+    const int G = s->num_q_heads / s->num_kv_heads;
+    const bool ok = k_eq_v != -1 ? ga::decode_rows16_supported(s->head_dim, k_eq_v == 1)
+                                 : ga::decode_rows16_supported(s->head_dim, false) ||
+                                       ga::decode_rows16_supported(s->head_dim, true);
+    if (impl == GA_IMPL_MFMA) {
+      if (!ok) return GA_ERR_OPTS;
+      return rows16_plan(s, window, ts, T, p);
+    }
+    if (impl == GA_IMPL_AUTO && ok && (long long)G * T >= 8) {
+      if (k_eq_v != -1) return rows16_plan(s, window, ts, T, p);
+      Plan v;  // workspace query: size for whichever the call may pick
+      int32_t st = valu_plan(s, window, ts, T, &v);
+      if (st != GA_OK) return st;
+      st = rows16_plan(s, window, ts, T, p);
+      if (st != GA_OK) return st;
+      if (v.ws_bytes > p->ws_bytes) p->ws_bytes = v.ws_bytes;
+      return GA_OK;
+    }
     return valu_plan(s, window, ts, T, p);
   }
   if (impl == GA_IMPL_MFMA) {
@@ -328,7 +388,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   a.part_ml = nullptr;
   a.plan = nullptr;
   a.n_blocks = 0;
-  if (p.impl == GA_IMPL_MFMA) {
+  if (p.impl == GA_IMPL_MFMA && !p.rows16) {
     const size_t slots = (size_t)ga::kMfmaBlocks + (size_t)shape->batch * shape->num_kv_heads;
     a.part_acc = ws;
     a.part_ml = ws + slots * 16 * D;
@@ -374,7 +434,10 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (p.impl == GA_IMPL_MFMA) {
+  if (p.rows16) {
+    e = ga::decode_rows16_launch(a, k_eq_v, s);
+    if (e == hipSuccess && p.n_split > 1) e = ga::merge_launch(a, s);
+  } else if (p.impl == GA_IMPL_MFMA) {
     e = ga::decode_mfma_launch(a, s);
   } else {
     e = ga::decode_valu_launch(a, k_eq_v, s);

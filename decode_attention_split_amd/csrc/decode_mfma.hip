@@ -38,6 +38,7 @@
 // head is fp32 in log2 units with lazy rescaling (max raised only past +8).
 #include "ga_device.h"
 #include "ga_internal.h"
+#include "ga_mfma.h"
 
 namespace ga {
 namespace {
@@ -58,26 +59,6 @@ constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
 constexpr int kLdsKV = MNW * WAVE_TILE > kLdsTile ? MNW * WAVE_TILE : kLdsTile;
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const float2_t f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
-}
-
-__device__ __forceinline__ floatx4_t mfma_k32(const uint4& a, const uint4& b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 // Valid-key count of unit u (batch row b = u / Hkv).
 __device__ __forceinline__ int unit_keys(const DecodeArgs& a, int u) {

@@ -1,0 +1,237 @@
+// decode_rows16.hip -- matrix-core split decode for 16 query rows per KV head: several
+// query tokens per sequence (speculative verification, chunked prefill) on the same
+// caches, each row masked at its own position.
+//
+// Why matrix cores: with 16 query rows on one KV head every cached byte feeds about 16
+// flops (q.k and p.v for each row), so the vector kernel, which reduces every row's dot
+// product across the lanes of a key, runs out of ALU long before HBM.  Here one wave is
+// one work-group and owns one split (a run of keys of one unit = batch row, KV head,
+// chunk of tokens); per 16-key tile:
+//   S^T[16 keys][16 rows] = K[16][D] . Q^T[D][16]: D / 32 v_mfma_f32_16x16x32_bf16, the
+//     K operand loaded straight from HBM (lane: key l16, d = 8 lg + 32 j + 0..7), Q^T read
+//     from LDS in the same d order;
+//   S^T leaves lane l holding row l16 for keys 4 lg + 0..3, which is exactly the B operand
+//     of the P.V product, so the softmax works in place (row max / sum over the four lane
+//     groups) and P goes to the matrix cores as bf16 hi + lo parts (~16 mantissa bits);
+//   the V rows go to LDS once and come back transposed with ds_read_b64_tr_b16 as the A
+//     operand of O^T[D][16] += V^T[D][16 keys] . P^T[16 keys][16 rows]: D / 16 pairs of
+//     v_mfma_f32_16x16x16_bf16.
+// One register buffer each for K and V, refilled as soon as a tile's products have used it
+// (several waves per SIMD hide the latency); LDS is double-buffered by tile.  Each split
+// leaves (m, l, acc) for the log-sum-exp merge, or writes the output when it is the only
+// split.  Softmax in log2 units, lazily rescaled (max raised only past +8); masked keys
+// weigh exactly zero.
+//
+// Definition followed: the same single-token definition per query token ("Gemma support"
+// pull request, Summary and Performance; "Gemma 4 12B (unified multimodal)" record: the
+// window of exactly w entries, spec decode with sliding windows in item (2)); key ranges
+// from ga::unit_range / ga::row_range, as in every other kernel.
+#include "ga_device.h"
+#include "ga_internal.h"
+#include "ga_mfma.h"
+
+namespace ga {
+namespace {
+
+constexpr float kRescaleLog2R16 = 8.0f;
+
+template <int D, bool KV_SHARED>
+__global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
+  constexpr int NJ = D / 32;         // 16-byte K chunks per lane = QK products per tile
+  constexpr int NDB = D / 16;        // 16-wide head_dim blocks of the output
+  constexpr int ROWB = D * 2 + 32;   // LDS bytes per key row (padding spreads the banks)
+  constexpr int QROWB = D * 2 + 16;  // LDS bytes per query row
+  __shared__ __attribute__((aligned(16))) char s_v[2][16 * ROWB];
+  __shared__ __attribute__((aligned(16))) char s_q[16 * QROWB];
+
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  const int S = a.n_split;
+  int bid = blockIdx.x;
+  const int split = bid % S;
+  bid /= S;
+  const int chunk = bid % a.n_chunks;
+  bid /= a.n_chunks;
+  const int g = bid % a.Hkv;
+  const int b = bid / a.Hkv;
+
+  // this lane's query row: l16 -> token chunk * Tc + l16 / Gh, head g * Gh + l16 % Gh
+  const int tok = chunk * a.Tc + l16 / a.Gh;
+  const bool row_on = tok < a.T;
+  const size_t row =
+      ((size_t)b * a.T + (row_on ? tok : a.T - 1)) * a.Hq + (size_t)g * a.Gh + l16 % a.Gh;
+
+  const RowRange r = unit_range(a, b, chunk);
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(r.n, k_begin + a.split_keys);
+  if (k_begin >= k_end) {
+    if (S == 1 && row_on) {  // the only split of an empty unit: the output is 0
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<floatx4_t*>(a.out + row * D + 16 * db + 4 * lg) =
+            floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  // the row's own valid positions (empty: lo > hi)
+  int row_lo = 1, row_hi = 0;
+  if (row_on) {
+    const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + tok, a.window, a.kind, a.cap,
+                                  a.max_keys);
+    if (rr.n > 0) {
+      row_lo = rr.lo;
+      row_hi = rr.hi;
+    }
+  }
+
+  // Q^T operand (row l16, d = 8 lg + 32 j + 0..7) parked in LDS and read per product,
+  // which keeps the registers for the K / V tiles in flight and the accumulators
+  {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + row * D);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      *reinterpret_cast<u32x4_t*>(s_q + l16 * QROWB + (lg + 4 * j) * 16) = qp[4 * j + lg];
+  }
+  const char* q_lds = s_q + l16 * QROWB + lg * 16;
+  const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
+  // (native 4 x u32 vectors: arrays of them stay in registers)
+  const u32x4_t* kbase = reinterpret_cast<const u32x4_t*>(a.k) + row0 * (D / 8);
+  const u32x4_t* vbase = reinterpret_cast<const u32x4_t*>(KV_SHARED ? a.k : a.v) + row0 * (D / 8);
+
+  floatx4_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
+
+  const int nt = (k_end - k_begin + 15) / 16;
+  u32x4_t kr[NJ], vr[KV_SHARED ? 1 : NJ];
+  // key k_begin + 16 t + l16 of the tile (past the end: re-read the last valid key)
+  auto key_row = [&](int t) {
+    const int i = k_begin + 16 * t + l16;
+    return (size_t)key_slot(r, i < k_end ? i : k_end - 1, a.cap) * (D / 8);
+  };
+  auto load_k = [&](int t) {
+    const u32x4_t* p = kbase + key_row(t) + lg;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kr[j] = p[4 * j];
+  };
+  auto load_v = [&](int t) {
+    if constexpr (!KV_SHARED) {
+      const u32x4_t* p = vbase + key_row(t) + lg;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) vr[j] = p[4 * j];
+    }
+  };
+  load_k(0);
+  load_v(0);
+  __syncthreads();  // the Q rows are in LDS
+
+  for (int t = 0; t < nt; ++t) {
+    const int k0 = k_begin + 16 * t;
+    // S^T for the tile
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      s = mfma_k32(kr[j], *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
+    // V rows of the tile to LDS (key l16, d = 8 lg + 32 j), then refill the registers
+    char* tile = s_v[t & 1];
+    {
+      char* w = tile + l16 * ROWB + lg * 16;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if constexpr (KV_SHARED)
+          *reinterpret_cast<u32x4_t*>(w + j * 64) = kr[j];
+        else
+          *reinterpret_cast<u32x4_t*>(w + j * 64) = vr[j];
+      }
+    }
+    load_k(t + 1 < nt ? t + 1 : t);
+    load_v(t + 1 < nt ? t + 1 : t);
+    __syncthreads();  // one wave: orders the LDS writes before the transposed reads
+
+    // softmax: lane holds row l16, keys k0 + 4 lg + i
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = k0 + 4 * lg + i;
+      const int pos = r.lo + key;
+      float v = s[i] * a.scale;
+      if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
+      const bool ok = key < k_end && pos >= row_lo && pos <= row_hi;
+      x[i] = ok ? v * kLog2e : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = rows_max(mx);  // over the 16 keys of the tile (four lane groups)
+    if (mx > m + kRescaleLog2R16) {
+      const float f = exp2_fast(m - mx);  // 0 while m = -inf
+      l *= f;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) acc[i] *= f;
+      m = mx;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = x[i] == -INFINITY ? 0.0f : exp2_fast(x[i] - m);
+      l += p[i];
+    }
+    const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+    const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const short4_t ph = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
+    const short4_t pl = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
+    const char* rd = tile + (4 * lg + (l16 >> 2)) * ROWB + (l16 & 3) * 8;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(rd + db * 32));
+      acc[db] = mfma_k16(va, ph, acc[db]);
+      acc[db] = mfma_k16(va, pl, acc[db]);
+    }
+  }
+
+  l = rows_sum(l);
+  if (!row_on) return;
+  if (S == 1) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* o = a.out + row * D + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db] * inv;
+  } else {
+    const size_t ps = row * S + split;
+    float* o = a.part_acc + ps * D + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db];
+    if (lg == 0) {
+      a.part_ml[ps * 2 + 0] = m;
+      a.part_ml[ps * 2 + 1] = l;
+    }
+  }
+}
+
+}  // namespace
+
+bool decode_rows16_supported(int D, bool k_eq_v) {
+  return D == 128 || D == 256 || (D == 512 && k_eq_v);
+}
+
+hipError_t decode_rows16_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
+  const long long blocks = (long long)a.B * a.Hkv * a.n_chunks * a.n_split;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(64);
+  if (a.D == 128) {
+    if (k_eq_v) hipLaunchKernelGGL((decode_rows16_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_rows16_kernel<128, false>), grid, block, 0, stream, a);
+  } else if (a.D == 256) {
+    if (k_eq_v) hipLaunchKernelGGL((decode_rows16_kernel<256, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_rows16_kernel<256, false>), grid, block, 0, stream, a);
+  } else if (a.D == 512 && k_eq_v) {
+    hipLaunchKernelGGL((decode_rows16_kernel<512, true>), grid, block, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ga

@@ -1,0 +1,46 @@
+// ga_mfma.h -- matrix-core helpers shared by the MFMA decode kernels (gfx950).
+//
+// Lane layouts (wave64, l16 = lane % 16, lg = lane / 16), verified on the GPU:
+//   v_mfma_f32_16x16x32_bf16  A[m][k]: lane holds m = l16, k = 8 lg + 0..7;
+//                             B[k][n]: lane holds n = l16, k = 8 lg + 0..7;
+//                             C[m][n]: lane holds n = l16, m = 4 lg + 0..3.
+//   v_mfma_f32_16x16x16_bf16  A: m = l16, k = 4 lg + 0..3; B: n = l16, k = 4 lg + 0..3.
+//   ds_read_b64_tr_b16        within a 16-lane block, lane i receives element i of each of
+//                             the four 8-byte rows read by lanes 4e..4e+3 (a 4x16 -> 16x4
+//                             transpose of bf16 values).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
+}
+
+__device__ __forceinline__ floatx4_t mfma_k32(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma_k32(u32x4_t a, u32x4_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+}  // namespace ga

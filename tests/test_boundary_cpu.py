@@ -201,7 +201,9 @@ def call_decode_multi(s, T, window=1024, ws=FAKE, ws_bytes=1 << 40, opts=None, v
     # ring of W = w = 1024 that the context can overrun: 8 tokens need 1031 slots
     (dict(s=shape(cap=1024, max_ctx=8192), T=8), -6),
     (dict(s=shape(cap=1031, max_ctx=8192), T=8, ws=0, ws_bytes=0), -7),
-    (dict(s=shape(cap=1031, max_ctx=8192), T=8, opts=api.make_opts(impl=api.IMPL_MFMA)), -12),
+    # matrix cores for several tokens: head_dim 512 only with K = V
+    (dict(s=shape(D=512, Hq=16, Hkv=1, cap=4096, kind=api.LINEAR), T=8, v=FAKE + 4096,
+          opts=api.make_opts(impl=api.IMPL_MFMA)), -12),
     (dict(s=shape(cap=1031, max_ctx=8192), T=8, opts=api.make_opts(split_keys=100)), -12),
 ])
 def test_decode_multi_rejects_bad_arguments_before_any_launch(kw, code):
@@ -216,14 +218,22 @@ def test_valid_decode_multi_without_a_gpu_reports_arch_error():
 
 
 def test_multi_workspace_closed_form():
-    """B 4, 16q/8kv (G = 2), hd256, ring 1031 for w 1024, T = 8 tokens: 4 tokens per unit
-    (2 heads x 4 tokens = 8 rows), 2 chunks; a unit's keys are at most w + 4 - 1 = 1027;
-    64 units want 4 splits of ceil(1027 / 4) = 257 -> 320 keys, S = ceil(1027 / 320) = 4.
-    Partials: B * T * Hq * S * (D + 2) floats."""
+    """B 4, 16q/8kv (G = 2), hd256, ring 1031 for w 1024, T = 8 tokens.
+    Vector kernel: 4 tokens per unit (2 heads x 4 tokens = 8 rows), 2 chunks; a unit's keys
+    are at most w + 4 - 1 = 1027; 64 units want 4 splits of ceil(1027 / 4) = 257 -> 320
+    keys, S = ceil(1027 / 320) = 4.  Matrix cores: 8 tokens per unit (16 rows), 1 chunk,
+    at most w + 8 - 1 = 1031 keys; 32 units want 64 one-wave splits of ceil(1031 / 64) =
+    17 -> 64 keys, S = 17.  Partials: B * T * Hq * S * (D + 2) floats; the automatic choice
+    sizes for the larger."""
     lib = _lib.load()
     s = shape(B=4, cap=1031, max_ctx=8192)
-    n = lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, None)
-    assert n == 4 * 8 * 16 * 4 * (256 + 2) * 4
+    valu = api.make_opts(impl=api.IMPL_VALU)
+    mfma = api.make_opts(impl=api.IMPL_MFMA)
+    n_v = lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, ctypes.byref(valu))
+    n_m = lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, ctypes.byref(mfma))
+    assert n_v == 4 * 8 * 16 * 4 * (256 + 2) * 4
+    assert n_m == 4 * 8 * 16 * 17 * (256 + 2) * 4
+    assert lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, None) == max(n_v, n_m)
     # T = 1 is the single-token plan
     o = api.make_opts()
     assert lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 1, 1024, ctypes.byref(o)) == \

@@ -64,9 +64,13 @@ class MultiInputs:
                                      (512, 8, 1), (512, 16, 1), (128, 16, 1)])
 @pytest.mark.parametrize("T", [2, 5, 8])
 @pytest.mark.parametrize("kind", [api.RING, api.LINEAR])
-def test_multi_token_parity_sweep(D, G, Hkv, T, kind):
+@pytest.mark.parametrize("impl", [api.IMPL_VALU, api.IMPL_MFMA], ids=["valu", "mfma"])
+def test_multi_token_parity_sweep(D, G, Hkv, T, kind, impl):
     """Several splits, chunks of tokens and ragged tails; rows whose first tokens precede
-    the sequence start (negative positions attend to nothing)."""
+    the sequence start (negative positions attend to nothing).  Both implementations: the
+    vector kernel and the matrix-core kernel for 16 query rows per KV head."""
+    if impl == api.IMPL_MFMA and D == 512 and G != 16:
+        pytest.skip("matrix-core multi-token path: head_dim 512 only with K = V")
     w = 96
     if kind == api.RING:
         cap, window = w + T - 1, w
@@ -82,8 +86,9 @@ def test_multi_token_parity_sweep(D, G, Hkv, T, kind):
     softcap = 30.0 if T % 2 == 0 else 0.0
     ref, _ = inp.oracle(window, softcap, default_scale(D), kind)
     for split in [0, 64]:
-        out = inp.run(window, softcap, default_scale(D), kind, max_ctx=max_ctx, split_keys=split)
-        assert_parity(out, ref, f"D={D} G={G} T={T} kind={kind} split={split}")
+        out = inp.run(window, softcap, default_scale(D), kind, max_ctx=max_ctx, split_keys=split,
+                      impl=impl)
+        assert_parity(out, ref, f"D={D} G={G} T={T} kind={kind} split={split} impl={impl}")
 
 
 @pytest.mark.parametrize("W", [64, 1024])
@@ -133,11 +138,14 @@ def test_spec_decode_sliding_layer_full_size_sampled_rows():
     gen = synth.generator(3)
     ctx = synth.uniform_int(gen, 64, 512, 8192).numpy().astype(np.int32)
     inp = MultiInputs(33, 64, T, 16, 8, 256, w + T - 1, False, ctx).to_device()
-    out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=8192)
+    out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=8192)  # matrix cores (auto)
     rows = sorted({0, 1, int(np.argmax(ctx)), int(np.argmin(ctx))})
     ref, _ = inp.oracle(w, 50.0, 1.0 / 16, api.RING, rows=rows)
     log(f"spec decode rows {rows}")
     assert_parity(out[rows], ref, "spec decode T=8")
+    # the vector kernel on the same inputs agrees on every row
+    out_v = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=8192, impl=api.IMPL_VALU)
+    assert_parity(out, out_v.double().cpu().numpy(), "spec decode mfma vs valu")
 
 
 def test_append_multi_matches_oracle_bitwise():
