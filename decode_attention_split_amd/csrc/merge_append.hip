@@ -75,27 +75,65 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   }
 }
 
-// Cache append: one lane per 16-byte chunk of a new row; bit-exact copies.  T tokens
-// per row sit at positions pos[b] + t; one lane writes its chunk for t = 0..T-1 in order,
-// so when two tokens land in the same ring slot the later one stays.
+// The same merge with one wave per row (four rows per work-group), for rows with few
+// splits: the weights are recomputed per lane from the (m, l) pairs the whole wave reads,
+// so there is no LDS and no barrier; lane i owns elements i, i + 64, ... of the row.
+constexpr int kMergeWaveMaxSplits = 64;
+
+__global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const size_t rows = (size_t)a.B * a.T * a.Hq;
+  const size_t bh = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= rows) return;
+  const int b = (int)(bh / ((size_t)a.T * a.Hq));
+  const int t = (int)(bh / a.Hq % a.T);
+  const int S = a.n_split, D = a.D;
+  const RowRange r = unit_range(a, b, t / a.Tc);
+  const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S
+  float* out = a.out + bh * D;
+  const float* ml = a.part_ml + bh * S * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  float Lsum = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const float ms = ml[2 * s];
+    Lsum += ms == -INFINITY ? 0.0f : ml[2 * s + 1] * exp2_fast(ms - M);
+  }
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  const float* acc = a.part_acc + bh * S * D;
+  for (int d = lane; d < D; d += 64) {
+    float o = 0.0f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = ml[2 * s];
+      const float w = ms == -INFINITY ? 0.0f : exp2_fast(ms - M);
+      o = fmaf(w, acc[(size_t)s * D + d], o);
+    }
+    out[d] = o * inv;
+  }
+}
+
+// Cache append: one lane per 16-byte chunk of a new row and token; bit-exact copies.  T
+// tokens per row sit at positions pos[b] + t; when two tokens of the call land in the same
+// ring slot (t + W < T), only the later one writes, so the latest token stays.
 __global__ void append_kernel(int B, int T, int Hkv, int D, int cap, int kind, uint4* k_cache,
                               uint4* v_cache, const uint4* k_new, const uint4* v_new,
                               const int32_t* pos) {
   const int chunks = D / 8;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)B * Hkv * chunks) return;
+  if (i >= (long long)B * T * Hkv * chunks) return;
   const int c = (int)(i % chunks);
-  const long long bg = i / chunks;
-  const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
-  for (int t = 0; t < T; ++t) {
-    const long long p = (long long)pos[b] + t;
-    if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) continue;  // out of range: skipped
-    const int slot = kind == GA_CACHE_RING ? (int)(p % cap) : (int)p;
-    const size_t dst = ((size_t)bg * cap + slot) * chunks + c;
-    const size_t src = (((size_t)b * T + t) * Hkv + g) * chunks + c;
-    k_cache[dst] = k_new[src];
-    if (v_cache) v_cache[dst] = v_new[src];
-  }
+  const long long btg = i / chunks;  // (b * T + t) * Hkv + g
+  const int g = (int)(btg % Hkv);
+  const long long bt = btg / Hkv;
+  const int b = (int)(bt / T), t = (int)(bt % T);
+  const long long p = (long long)pos[b] + t;
+  if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) return;  // out of range: skipped
+  if (kind == GA_CACHE_RING && t + cap < T) return;              // a later token owns it
+  const int slot = kind == GA_CACHE_RING ? (int)(p % cap) : (int)p;
+  const size_t dst = (((size_t)b * Hkv + g) * cap + slot) * chunks + c;
+  const size_t src = (size_t)btg * chunks + c;
+  k_cache[dst] = k_new[src];
+  if (v_cache) v_cache[dst] = v_new[src];
 }
 
 // Quantizing append into fp8 e4m3 caches: one wave per (b, KV head) walks the T tokens
@@ -256,16 +294,20 @@ __global__ void ranges_kernel(int B, int cap, int kind, int window, int max_keys
 }  // namespace
 
 hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream) {
-  const long long blocks = (long long)a.B * a.T * a.Hq;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a);
+  const long long rows = (long long)a.B * a.T * a.Hq;
+  if (rows <= 0) return hipSuccess;
+  if (a.n_split <= kMergeWaveMaxSplits)
+    hipLaunchKernelGGL(merge_wave_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t append_launch(int B, int T, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
                          uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* pos, hipStream_t stream) {
-  const long long n = (long long)B * Hkv * (D / 8);
+  const long long n = (long long)B * T * Hkv * (D / 8);
   if (n <= 0 || T <= 0) return hipSuccess;
   const int threads = 256;
   const long long blocks = (n + threads - 1) / threads;
