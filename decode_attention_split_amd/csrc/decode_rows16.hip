@@ -17,9 +17,10 @@
 //     operand of O^T[D][16] += V^T[D][16 keys] . P^T[16 keys][16 rows]: D / 16 pairs of
 //     v_mfma_f32_16x16x16_bf16.
 // One register buffer each for K and V, refilled as soon as a tile's products have used it
-// (several waves per SIMD hide the latency); LDS is double-buffered by tile.  Each split
-// leaves (m, l, acc) for the log-sum-exp merge, or writes the output when it is the only
-// split.  Softmax in log2 units, lazily rescaled (max raised only past +8); masked keys
+// (several waves per SIMD hide the latency), one LDS tile.  Each split leaves (m, l, acc)
+// for the log-sum-exp merge kernel, or writes the output when it is the only split.  (A
+// merge by the last split to arrive would need a device-scope release per work-group,
+// which on this chip writes back the L2 and costs more than the separate merge.)  Softmax in log2 units, lazily rescaled (max raised only past +8); masked keys
 // weigh exactly zero.
 //
 // Definition followed: the same single-token definition per query token ("Gemma support"
@@ -41,7 +42,7 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
   constexpr int NDB = D / 16;        // 16-wide head_dim blocks of the output
   constexpr int ROWB = D * 2 + 32;   // LDS bytes per key row (padding spreads the banks)
   constexpr int QROWB = D * 2 + 16;  // LDS bytes per query row
-  __shared__ __attribute__((aligned(16))) char s_v[2][16 * ROWB];
+  __shared__ __attribute__((aligned(16))) char s_v[16 * ROWB];
   __shared__ __attribute__((aligned(16))) char s_q[16 * QROWB];
 
   const int lane = threadIdx.x;
@@ -66,7 +67,9 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
   const int k_begin = split * a.split_keys;
   const int k_end = min(r.n, k_begin + a.split_keys);
   if (k_begin >= k_end) {
-    if (S == 1 && row_on) {  // the only split of an empty unit: the output is 0
+    // the only split of an empty unit writes its zero output; with several splits the
+    // merge writes it
+    if (S == 1 && row_on) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<floatx4_t*>(a.out + row * D + 16 * db + 4 * lg) =
@@ -135,7 +138,9 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
     for (int j = 0; j < NJ; ++j)
       s = mfma_k32(kr[j], *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
     // V rows of the tile to LDS (key l16, d = 8 lg + 32 j), then refill the registers
-    char* tile = s_v[t & 1];
+    // one LDS tile, rewritten each step: the barrier closing the previous step keeps the
+    // compiler from moving these writes above that step's transposed reads
+    char* tile = s_v;
     {
       char* w = tile + l16 * ROWB + lg * 16;
 #pragma unroll
@@ -189,6 +194,7 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
       acc[db] = mfma_k16(va, ph, acc[db]);
       acc[db] = mfma_k16(va, pl, acc[db]);
     }
+    __syncthreads();  // the tile's transposed reads stay before the next tile's writes
   }
 
   l = rows_sum(l);
@@ -209,6 +215,7 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
     }
   }
 }
+
 
 }  // namespace
 
