@@ -230,7 +230,10 @@ __global__ void __launch_bounds__(NW_ * 64)
     return __builtin_amdgcn_readfirstlane(s);
   };
 
-  // sc[0] / sc[1]: the key's K / V row scales (fp8 caches only)
+  // sc[0] / sc[1]: the key's K / V row scales (fp8 caches only).  The L lanes of a group
+  // read L * sizeof(Chunk) >= 128 contiguous bytes per load, whole lines, so the cache
+  // rows are loaded non-temporally (measured ~10% faster than cached loads here).
+  static_assert(L * (int)sizeof(Chunk) >= 128, "a lane group reads whole 128-byte lines");
   auto load = [&](Chunk(&kr)[NCH], Chunk(&vr)[NCH], float(&sc)[2], int step) {
     const int i = k_begin + step * GPW + grp;
     const int ic = i < k_end ? i : k_end - 1;  // past the end: re-read a valid row
@@ -238,11 +241,11 @@ __global__ void __launch_bounds__(NW_ * 64)
     const bool fresh = !FP8 && slot == new_slot;
     const Chunk* kp = fresh ? knew : kbase + (size_t)slot * ROWC;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kr[c] = kp[c * L + j];
+    for (int c = 0; c < NCH; ++c) kr[c] = stream_load(kp + c * L + j);
     if constexpr (!KV_SHARED) {
       const Chunk* vp = fresh ? vnew : vbase + (size_t)slot * ROWC;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) vr[c] = vp[c * L + j];
+      for (int c = 0; c < NCH; ++c) vr[c] = stream_load(vp + c * L + j);
     }
     if constexpr (FP8) {
       sc[0] = kscale[slot];

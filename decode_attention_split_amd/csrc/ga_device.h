@@ -75,6 +75,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Non-temporal load of streamed cache data (read once per call, not worth keeping in L2
+// or the Infinity Cache).  Only for accesses where a lane group reads whole 128-byte lines:
+// a line read in halves by separate instructions would be fetched twice.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  if constexpr (sizeof(T) == 16)
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p)));
+  else
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p)));
+}
 // Soft-cap c * tanh(x / c), with tanh(y) = 1 - 2 / (exp(2y) + 1): bounded by +-c,
 // saturates cleanly (exp -> inf gives 1, exp -> 0 gives -1).  Absolute error of tanh
 // is a few float32 ulps of 1.
