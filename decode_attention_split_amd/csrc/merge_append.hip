@@ -76,8 +76,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
 }
 
 // The same merge with one wave per row (four rows per work-group), for rows with few
-// splits: the weights are recomputed per lane from the (m, l) pairs the whole wave reads,
-// so there is no LDS and no barrier; lane i owns elements i, i + 64, ... of the row.
+// splits.  Lane s < ns reads split s's (m_s, l_s) and forms its weight 2^(m_s - M); the
+// wave reduces M and L across lanes, and each accumulation step reads the weights back
+// from their lanes.  Lane i owns the float4 chunks i, i + 64, ... of the row, and four
+// splits' chunks are loaded before any is used, so their latencies overlap.
 constexpr int kMergeWaveMaxSplits = 64;
 
 __global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
@@ -87,28 +89,47 @@ __global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
   if (bh >= rows) return;
   const int b = (int)(bh / ((size_t)a.T * a.Hq));
   const int t = (int)(bh / a.Hq % a.T);
-  const int S = a.n_split, D = a.D;
+  const int S = a.n_split, D4 = a.D / 4;
   const RowRange r = unit_range(a, b, t / a.Tc);
-  const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S
-  float* out = a.out + bh * D;
+  const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S <= 64
   const float* ml = a.part_ml + bh * S * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  float Lsum = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = ml[2 * s];
-    Lsum += ms == -INFINITY ? 0.0f : ml[2 * s + 1] * exp2_fast(ms - M);
+  float m_s = -INFINITY, l_s = 0.0f;
+  if (lane < ns) {
+    m_s = ml[2 * lane];
+    l_s = ml[2 * lane + 1];
   }
+  float M = m_s;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  // a split with no key of this row (m = -inf) weighs 0; so does every split of a row
+  // with no key at all (M = -inf), whose output is 0
+  const float w_s = m_s == -INFINITY ? 0.0f : exp2_fast(m_s - M);
+  float Lsum = l_s * w_s;
+  for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off, 64);
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  const float* acc = a.part_acc + bh * S * D;
-  for (int d = lane; d < D; d += 64) {
-    float o = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = ml[2 * s];
-      const float w = ms == -INFINITY ? 0.0f : exp2_fast(ms - M);
-      o = fmaf(w, acc[(size_t)s * D + d], o);
+  const float4* acc = reinterpret_cast<const float4*>(a.part_acc + bh * S * a.D);
+  float4* out = reinterpret_cast<float4*>(a.out + bh * a.D);
+  auto weight = [&](int s) {  // s is the same on every lane
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_s),
+                                                    __builtin_amdgcn_readfirstlane(s)));
+  };
+  for (int d = lane; d < D4; d += 64) {
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = acc[(size_t)min(s0 + j, ns - 1) * D4 + d];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (s0 + j < ns) {
+          const float w = weight(s0 + j);
+          o.x = fmaf(w, v[j].x, o.x);
+          o.y = fmaf(w, v[j].y, o.y);
+          o.z = fmaf(w, v[j].z, o.z);
+          o.w = fmaf(w, v[j].w, o.w);
+        }
+      }
     }
-    out[d] = o * inv;
+    out[d] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   }
 }
 
