@@ -78,7 +78,7 @@ template <int D, int G, int NW_, bool KV_SHARED, bool MULTI, bool FP8>
 __global__ void __launch_bounds__(NW_ * 64)
     decode_valu_kernel(DecodeArgs a) {
   using C = ValuCfg<D, G, NW_>;
-  constexpr int L = C::L, DPL = C::DPL, GPW = C::GPW, NW = C::NW, NG = C::NG;
+  constexpr int L = C::L, DPL = C::DPL, GPW = C::GPW, NW = C::NW;
   constexpr int ROW16 = D / 8;  // 16-byte chunks per bf16 row
   // A lane owns elements EPC * (c * L + j) + e (e < EPC) of each row, for its NCH load
   // chunks c: 8 bf16 or 16 fp8 codes per 16-byte chunk (8 codes in 8 bytes when a lane
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(NW_ * 64)
   constexpr int ROWC = (FP8 ? D : 2 * D) / (int)sizeof(Chunk);  // chunks per cache row
   static_assert(NCH >= 1 && DPL % EPC == 0, "lane slice must be whole load chunks");
 
-  __shared__ float s_acc[NW][G][D];
+  __shared__ __attribute__((aligned(16))) float s_acc[NW][G][D];
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
 
@@ -374,46 +374,88 @@ __global__ void __launch_bounds__(NW_ * 64)
   if (sa < n_wsteps) compute(ka, va, ca, sa);
   app.store(a);
 
-  // Merge the groups of this wave (lanes j, j + L, j + 2L, ... hold the same elements),
-  // exchanging values with DPP / permlane swaps on the VALU.
-  auto merge_groups = [&](auto off_tag) {
-    constexpr int OFF = decltype(off_tag)::value;
+  // Merge the GPW groups of this wave (lanes j, j + L, j + 2L, ... hold the same
+  // elements).  Each group first rescales to the wave's common max M, so that merging is
+  // a plain sum.  At the lane offsets 32 and 16 the sum is a reduce-scatter: one
+  // v_permlane32/16_swap of the value pair (x_i, x_{i + n/2}) hands the lower lane both
+  // copies of x_i and the upper lane both copies of x_{i + n/2}, so each level halves the
+  // values a lane holds (while at least 8 remain); the other levels are butterflies
+  // (both lanes keep the full sum).  Both lanes of a pair add the same two numbers in
+  // the same order, so the result does not depend on which lane computes it.
+  constexpr int NV = G * DPL;  // values per lane: acc flattened as [hh][e]
+  constexpr bool RS32 = L <= 32 && NV / 2 >= 8;
+  constexpr int NV1 = RS32 ? NV / 2 : NV;
+  constexpr bool RS16 = L <= 16 && NV1 / 2 >= 8;
+  constexpr int NV2 = RS16 ? NV1 / 2 : NV1;
+  static_assert(NV2 % 4 == 0, "float4 runs of the accumulator");
+  float M[G], Lw[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float mo = xor_lane<OFF>(m[hh], lane);
-      const float lo = xor_lane<OFF>(l[hh], lane);
-      const float mn = fmaxf(m[hh], mo);
-      const float fs = m[hh] == -INFINITY ? 0.0f : exp2_fast(m[hh] - mn);
-      const float fo = mo == -INFINITY ? 0.0f : exp2_fast(mo - mn);
-      l[hh] = l[hh] * fs + lo * fo;
+  for (int hh = 0; hh < G; ++hh) {
+    M[hh] = m[hh];
+    if constexpr (L <= 8) M[hh] = fmaxf(M[hh], xor_lane<8>(M[hh], lane));
+    if constexpr (L <= 16) M[hh] = fmaxf(M[hh], xor_lane<16>(M[hh], lane));
+    if constexpr (L <= 32) M[hh] = fmaxf(M[hh], xor_lane<32>(M[hh], lane));
+  }
+  float vf[NV];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const float ao = xor_lane<OFF>(acc[hh][e], lane);
-        acc[hh][e] = acc[hh][e] * fs + ao * fo;
-      }
-      m[hh] = mn;
+  for (int hh = 0; hh < G; ++hh) {
+    const float f = m[hh] == -INFINITY ? 0.0f : exp2_fast(m[hh] - M[hh]);
+    Lw[hh] = l[hh] * f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vf[hh * DPL + e] = acc[hh][e] * f;
+    float lo, hi;
+    if constexpr (L <= 8) Lw[hh] += dpp<kDppRowRor8>(Lw[hh]);
+    if constexpr (L <= 16) {
+      lane_pair16(Lw[hh], lo, hi);
+      Lw[hh] = lo + hi;
     }
-  };
-  if constexpr (L <= 8) merge_groups(std::integral_constant<int, 8>());
-  if constexpr (L <= 16) merge_groups(std::integral_constant<int, 16>());
-  if constexpr (L <= 32) merge_groups(std::integral_constant<int, 32>());
+    if constexpr (L <= 32) {
+      lane_pair32(Lw[hh], lo, hi);
+      Lw[hh] = lo + hi;
+    }
+  }
+  if constexpr (L <= 32) {
+#pragma unroll
+    for (int i = 0; i < NV1; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(
+          __float_as_int(vf[i]), __float_as_int(vf[RS32 ? i + NV / 2 : i]), false, false);
+      vf[i] = __int_as_float(r[0]) + __int_as_float(r[1]);
+    }
+  }
+  if constexpr (L <= 16) {
+#pragma unroll
+    for (int i = 0; i < NV2; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(
+          __float_as_int(vf[i]), __float_as_int(vf[RS16 ? i + NV1 / 2 : i]), false, false);
+      vf[i] = __int_as_float(r[0]) + __int_as_float(r[1]);
+    }
+  }
+  if constexpr (L <= 8) {
+#pragma unroll
+    for (int i = 0; i < NV2; ++i) vf[i] += dpp<kDppRowRor8>(vf[i]);
+  }
 
-  // Merge the waves through LDS, then write the output or this split's partial.
-  if (lane < L) {
+  // Merge the waves through LDS, then write the output or this split's partial.  Lane
+  // value i is element base + i of the flattened [hh][e] accumulator; of the lanes that
+  // a butterfly level left identical, the one with that lane bit clear writes.
+  const int base = (RS32 ? ((lane >> 5) & 1) * (NV / 2) : 0) +
+                   (RS16 ? ((lane >> 4) & 1) * (NV1 / 2) : 0);
+  const int dup_bits = (L <= 8 ? 8 : 0) | (L <= 16 && !RS16 ? 16 : 0) |
+                       (L <= 32 && !RS32 ? 32 : 0);
+  if ((lane & dup_bits) == 0) {
+#pragma unroll
+    for (int i = 0; i < NV2; i += 4) {
+      const int f = base + i;
+      const int hh = f / DPL, e = f % DPL;
+      float* dst = &s_acc[wave][hh][EPC * ((e / EPC) * L + j) + e % EPC];
+      *reinterpret_cast<float4*>(dst) = make_float4(vf[i], vf[i + 1], vf[i + 2], vf[i + 3]);
+    }
+  }
+  if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        float4* dst = reinterpret_cast<float4*>(&s_acc[wave][hh][EPC * (c * L + j)]);
-#pragma unroll
-        for (int q4 = 0; q4 < EPC / 4; ++q4)
-          dst[q4] = make_float4(acc[hh][EPC * c + 4 * q4 + 0], acc[hh][EPC * c + 4 * q4 + 1],
-                                acc[hh][EPC * c + 4 * q4 + 2], acc[hh][EPC * c + 4 * q4 + 3]);
-      }
-      if (j == 0) {
-        s_m[wave][hh] = m[hh];
-        s_l[wave][hh] = l[hh];
-      }
+      s_m[wave][hh] = M[hh];
+      s_l[wave][hh] = Lw[hh];
     }
   }
   __syncthreads();
