@@ -44,11 +44,14 @@ constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi 
 // work-groups (one split per row) that need more waves in flight per CU.
 template <int D, int G>
 constexpr int valu_nw_base() { return clampi(8192 / (G * D), 1, 4); }
-// The wide variant doubles the waves of small work-groups; only where a lane's
-// accumulators stay at 64 (the lanes per key are not clamped at D / 8), else it spills.
+// The wide variant doubles the waves of small work-groups (two waves per SIMD, so at
+// most 256 VGPRs each); only where a lane's accumulators stay at 64 (the lanes per key
+// are not clamped at D / 8) and its two K + V load buffers at 16 x 16 bytes, else it
+// spills.
 template <int D, int G>
 constexpr bool valu_nw_wide_ok() {
-  return valu_nw_base<D, G>() == 4 && G * D <= 2048 && G * D / clampi(G * D / 64, 8, D / 8) <= 64;
+  return valu_nw_base<D, G>() == 4 && G * D <= 2048 &&
+         G * D / clampi(G * D / 64, 8, D / 8) <= 64 && D / clampi(G * D / 64, 8, D / 8) <= 32;
 }
 
 template <int D, int G, int NW_>
@@ -126,41 +129,9 @@ __global__ void __launch_bounds__(NW_ * 64)
   const int new_slot = appended_slot(a, b);
   AppendRow app;
   app.load(a, b, g, new_slot, threadIdx.x, split == 0);
-  const RowRange r = unit_range(a, b, chunk);
-  const int k_begin = split * a.split_keys;
-  const int k_end = min(r.n, k_begin + a.split_keys);
-  if (k_begin >= k_end) {
-    if (S == 1) {  // the only split of an empty unit: the output is 0
-      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
-        if (row_active(idx / D)) a.out[row_index(idx / D) * D + idx % D] = 0.0f;
-    }
-    app.store(a);
-    return;  // with S > 1 the merge never reads splits past the unit's end
-  }
-  __shared__ int s_next;  // next wave-step to hand out
-  if (threadIdx.x == 0) s_next = 0;
-  __syncthreads();
-
-  // MULTI: each row's own valid positions [row_lo, row_hi] (empty: lo > hi).
-  int row_lo[MULTI ? G : 1], row_hi[MULTI ? G : 1];
-  if constexpr (MULTI) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      row_lo[hh] = 1;
-      row_hi[hh] = 0;
-      if (row_active(hh)) {
-        const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + row_token(hh), a.window, a.kind,
-                                      a.cap, a.max_keys);
-        if (rr.n > 0) {
-          row_lo[hh] = rr.lo;
-          row_hi[hh] = rr.hi;
-        }
-      }
-    }
-  }
-
   // Query rows of this unit in this lane's element order: packed bf16 pairs for the
-  // bf16 cache (dot2 products), float32 values for the fp8 cache.
+  // bf16 cache (dot2 products), float32 values for the fp8 cache.  Loaded before the
+  // context length is known (they do not depend on it), so the two latencies overlap.
   uint32_t qr[G][FP8 ? 1 : DPL / 2];
   float qf[G][FP8 ? DPL : 1];
 #pragma unroll
@@ -183,6 +154,38 @@ __global__ void __launch_bounds__(NW_ * 64)
           qr[hh][4 * c + 1] = v.y;
           qr[hh][4 * c + 2] = v.z;
           qr[hh][4 * c + 3] = v.w;
+        }
+      }
+    }
+  }
+
+  const RowRange r = unit_range(a, b, chunk);
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(r.n, k_begin + a.split_keys);
+  if (k_begin >= k_end) {
+    if (S == 1) {  // the only split of an empty unit: the output is 0
+      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
+        if (row_active(idx / D)) a.out[row_index(idx / D) * D + idx % D] = 0.0f;
+    }
+    app.store(a);
+    return;  // with S > 1 the merge never reads splits past the unit's end
+  }
+  __shared__ int s_next;  // handed-out wave-steps past the first NW
+  if (threadIdx.x == 0) s_next = 0;
+
+  // MULTI: each row's own valid positions [row_lo, row_hi] (empty: lo > hi).
+  int row_lo[MULTI ? G : 1], row_hi[MULTI ? G : 1];
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      row_lo[hh] = 1;
+      row_hi[hh] = 0;
+      if (row_active(hh)) {
+        const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + row_token(hh), a.window, a.kind,
+                                      a.cap, a.max_keys);
+        if (rr.n > 0) {
+          row_lo[hh] = rr.lo;
+          row_hi[hh] = rr.hi;
         }
       }
     }
@@ -215,19 +218,20 @@ __global__ void __launch_bounds__(NW_ * 64)
     for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
   }
 
-  // Wave-step s covers keys k_begin + s * GPW + grp (one per lane group).  Steps are
-  // handed out to waves as they ask for them (an LDS counter), so waves that the SIMD
-  // arbiter serves less still finish together with the others; in deterministic mode the
-  // order is static (wave w takes w, w + NW, ...), which fixes the summation order.
+  // Wave-step s covers keys k_begin + s * GPW + grp (one per lane group).  Wave w's first
+  // step is w, so its first rows are requested before any barrier; later steps are
+  // handed out as waves ask for them (an LDS counter), so waves that the SIMD arbiter
+  // serves less still finish together with the others.  In deterministic mode the order
+  // is static (wave w takes w, w + NW, ...), which fixes the summation order.
   const int n_wsteps = (k_end - k_begin + GPW - 1) / GPW;
   const float scale = a.scale;
   const float softcap = a.softcap, inv_softcap = a.inv_softcap;
   int taken = 0;
   auto grab = [&]() -> int {
-    if (a.deterministic) return wave + NW * (taken++);
+    if (a.deterministic || taken == 0) return wave + NW * (taken++);
     int s = 0;
     if (lane == 0) s = atomicAdd(&s_next, 1);
-    return __builtin_amdgcn_readfirstlane(s);
+    return NW + __builtin_amdgcn_readfirstlane(s);
   };
 
   // sc[0] / sc[1]: the key's K / V row scales (fp8 caches only).  The L lanes of a group
@@ -362,6 +366,7 @@ __global__ void __launch_bounds__(NW_ * 64)
   float ca[2] = {1.0f, 1.0f}, cb[2] = {1.0f, 1.0f};
   int sa = grab();
   load(ka, va, ca, sa);
+  __syncthreads();  // s_next is set before any wave asks for a handed-out step
   int sb = grab();
   while (sb < n_wsteps) {
     load(kb, vb, cb, sb);
