@@ -19,7 +19,6 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
 constexpr int kTargetBlocks = 256;   // one work-group per CU of an MI355X
-constexpr int kWideBelowBlocks = 512;  // fewer work-groups than this: use the wide variant
 constexpr int kMaxSplitKeys = 65536;
 #ifndef GA_MULTI_MAX_ROWS
 #define GA_MULTI_MAX_ROWS 8
@@ -85,7 +84,6 @@ int32_t check_shape(const ga_shape* s, int32_t window, int32_t T = 1) {
 
 struct Plan {
   int impl;        // GA_IMPL_VALU / GA_IMPL_MFMA
-  int n_waves;     // vector path: waves per work-group (0: default)
   int split_keys;  // Ts
   int n_split;     // S
   int max_keys;    // S * Ts
@@ -147,8 +145,6 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   if (S < 1) S = 1;
   if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
   p->impl = GA_IMPL_VALU;
-  const int wide = ga::decode_valu_wide_waves(s->head_dim, G * Tc);
-  p->n_waves = (wide > 0 && units * S < kWideBelowBlocks) ? wide : 0;
   p->split_keys = ts;
   p->n_split = (int)S;
   p->max_keys = (int)(S * ts);
@@ -185,7 +181,6 @@ int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   if (S * ts > (1LL << 30) || units * S > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
   p->impl = GA_IMPL_MFMA;
   p->rows16 = true;
-  p->n_waves = 0;
   p->split_keys = ts;
   p->n_split = (int)S;
   p->max_keys = (int)(S * ts);
@@ -201,7 +196,6 @@ int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
 void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
   long long nmax = max_keys_bound(s, window);
   p->impl = GA_IMPL_MFMA;
-  p->n_waves = 0;
   p->split_keys = 0;
   p->n_split = 0;
   p->max_keys = (int)(nmax > 0 ? nmax : 1);
@@ -412,7 +406,6 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   a.split_keys = p.split_keys;
   a.n_split = p.n_split;
   a.max_keys = p.max_keys;
-  a.n_waves = p.n_waves;
   a.deterministic = opts ? opts->deterministic : 0;
   a.T = p.T;
   a.Tc = p.Tc;

@@ -13,15 +13,6 @@ bool decode_valu_supported(int D, int G) {
   return (D == 128 || D == 256 || D == 512) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
-int decode_valu_wide_waves(int D, int G) {
-  switch (D) {
-    case 128: return wide_waves_d<128>(G);
-    case 256: return wide_waves_d<256>(G);
-    case 512: return wide_waves_d<512>(G);
-    default: return 0;
-  }
-}
-
 hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
   if (a.D == 128) return valu_launch_d<128>(a, k_eq_v, stream);
   if (a.D == 256) return valu_launch_d<256>(a, k_eq_v, stream);

@@ -39,20 +39,11 @@ constexpr float kRescaleLog2 = 8.0f;
 
 constexpr int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// Waves per work-group: the default keeps the end-of-split LDS merge buffer at 32 KiB;
-// the wide variant doubles it when that still fits in 64 KiB, for launches with few
-// work-groups (one split per row) that need more waves in flight per CU.
+// Waves per work-group: keeps the end-of-split LDS merge buffer at 32 KiB (four waves
+// where that fits: with non-temporal loads four waves per CU already stream at the HBM
+// rate measured for plain copies).
 template <int D, int G>
 constexpr int valu_nw_base() { return clampi(8192 / (G * D), 1, 4); }
-// The wide variant doubles the waves of small work-groups (two waves per SIMD, so at
-// most 256 VGPRs each); only where a lane's accumulators stay at 64 (the lanes per key
-// are not clamped at D / 8) and its two K + V load buffers at 16 x 16 bytes, else it
-// spills.
-template <int D, int G>
-constexpr bool valu_nw_wide_ok() {
-  return valu_nw_base<D, G>() == 4 && G * D <= 2048 &&
-         G * D / clampi(G * D / 64, 8, D / 8) <= 64 && D / clampi(G * D / 64, 8, D / 8) <= 32;
-}
 
 template <int D, int G, int NW_>
 struct ValuCfg {
@@ -519,23 +510,7 @@ hipError_t launch_dgw(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
-  constexpr int base = valu_nw_base<D, G>();
-  if constexpr (valu_nw_wide_ok<D, G>()) {
-    if (a.n_waves == 2 * base) return launch_dgw<D, G, 2 * base>(a, k_eq_v, stream);
-  }
-  return launch_dgw<D, G, base>(a, k_eq_v, stream);
-}
-
-template <int D>
-int wide_waves_d(int G) {
-  switch (G) {
-    case 1: return valu_nw_wide_ok<D, 1>() ? 2 * valu_nw_base<D, 1>() : 0;
-    case 2: return valu_nw_wide_ok<D, 2>() ? 2 * valu_nw_base<D, 2>() : 0;
-    case 4: return valu_nw_wide_ok<D, 4>() ? 2 * valu_nw_base<D, 4>() : 0;
-    case 8: return valu_nw_wide_ok<D, 8>() ? 2 * valu_nw_base<D, 8>() : 0;
-    case 16: return valu_nw_wide_ok<D, 16>() ? 2 * valu_nw_base<D, 16>() : 0;
-    default: return 0;
-  }
+  return launch_dgw<D, G, valu_nw_base<D, G>()>(a, k_eq_v, stream);
 }
 
 }  // namespace

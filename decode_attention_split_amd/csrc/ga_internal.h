@@ -29,7 +29,6 @@ struct DecodeArgs {
   int max_keys;           // rows longer than this keep their newest keys
   int* plan;              // matrix-core path: per-unit key prefix sums [B * Hkv + 1]
   int n_blocks;           // matrix-core path: work-groups of the decode launch
-  int n_waves;            // vector path: waves per work-group (0: the default)
   // Fused cache append (gemma_attn_decode_append); new_pos == nullptr: none.
   const uint16_t* k_new;  // [B, Hkv, D]
   const uint16_t* v_new;  // [B, Hkv, D], or nullptr for K = V
@@ -140,7 +139,6 @@ constexpr int kMfmaBlocks = 256 * kMfmaBlocksPerCU;
 // Split kernels.  Each launch covers B * Hkv * S work-groups; with S == 1 the split
 // kernel writes `out` directly, otherwise it writes partials for merge_launch.
 hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream);
-int decode_valu_wide_waves(int D, int G);   // waves of the wide variant, 0 if none
 bool decode_valu_supported(int D, int G);
 
 // Matrix-core path (head_dim 512, G = 16, K = V): decode plus its unit merge.
