@@ -54,49 +54,28 @@ constexpr float kRescaleLog2 = 8.0f;
 // LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
 // (160 KiB each): every CU then holds the same number of equal-work work-groups.
 constexpr int kLdsCU = 160 * 1024;
-constexpr int kLdsOther = 2 * MNW * 64 * 16 + 2 * (kMfmaMaxUnits + 1) * 4 + MNW * 4;
+constexpr int kLdsOther = 2 * MNW * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4;
 constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
 constexpr int kLdsKV = MNW * WAVE_TILE > kLdsTile ? MNW * WAVE_TILE : kLdsTile;
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
-
-// Valid-key count of unit u (batch row b = u / Hkv).
-__device__ __forceinline__ int unit_keys(const DecodeArgs& a, int u) {
-  const int b = u / a.Hkv;
-  return row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys).n;
-}
 
 __device__ __forceinline__ int chunk_keys(int T, int NB) {
   const int per = (T + NB - 1) / NB;
   return T > 0 ? (per + TK - 1) / TK * TK : TK;
 }
 
-// Sum over the work-group (every thread gets it).
-__device__ __forceinline__ int block_sum(int v, int* s_red, int wave, int lane) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < MNW; ++w) t += s_red[w];
-  return t;
-}
-
-// Inclusive prefix sums of s[1..n] in place (s[0] is left as is), by wave 0.
-__device__ __forceinline__ void wave0_scan(int* s, int n, int wave, int lane) {
-  if (wave != 0) return;
-  int carry = 0;
-  for (int base = 1; base <= n; base += 64) {
-    const int idx = base + lane;
-    int v = idx <= n ? s[idx] : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
-    }
-    if (idx <= n) s[idx] = v + carry;
-    carry += __shfl(v, 63, 64);
-  }
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then each row adds the last lane of the rows before it (DPP row
+// broadcasts), all on the VALU.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
+  return v;
 }
 
 __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
@@ -104,32 +83,53 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   __shared__ floatx4_t s_part[2][MNW][64];
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
-  __shared__ int s_red[MNW];
+  __shared__ int s_slot[kMfmaMaxUnits];   // slot of each unit's first valid key
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.B * a.Hkv;
 
-  // ---- the partition (every work-group computes it; work-group 0 also publishes it)
-  for (int u = tid; u < R; u += MNW * 64) s_n[u + 1] = unit_keys(a, u);
-  if (tid == 0) {
-    s_n[0] = 0;
-    s_k[0] = 0;
+  // ---- the partition (every work-group computes it; work-group 0 also publishes it):
+  // each unit's key range, then wave 0 alone forms both prefix sums (two barriers).
+  for (int u = tid; u < R; u += MNW * 64) {
+    const int b = u / a.Hkv;
+    const RowRange rr = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+    s_n[u + 1] = rr.n;
+    s_slot[u] = rr.slot_lo;
   }
   __syncthreads();
-  wave0_scan(s_n, R, wave, lane);
-  __syncthreads();
-  // k_u = ceil(n_u / C) <= n_u / C + 1, so with C = T / (NB - R') (R' non-empty units)
-  // the work-groups with work never exceed NB: all of them are resident at once.
-  int nonempty = 0;
-  for (int u = tid; u < R; u += MNW * 64) nonempty += (s_n[u + 1] > s_n[u]) ? 1 : 0;
-  nonempty = block_sum(nonempty, s_red, wave, lane);
-  const int nb_eff = a.n_blocks - nonempty >= a.n_blocks / 4 ? a.n_blocks - nonempty : a.n_blocks;
-  const int C = chunk_keys(s_n[R], nb_eff);
-  for (int u = tid; u < R; u += MNW * 64) s_k[u + 1] = (s_n[u + 1] - s_n[u] + C - 1) / C;
-  __syncthreads();
-  wave0_scan(s_k, R, wave, lane);
+  if (wave == 0) {
+    int total = 0, nonempty = 0;
+    for (int base = 0; base < R; base += 64) {
+      const int u = base + lane;
+      const int n = u < R ? s_n[u + 1] : 0;
+      nonempty += __popcll(__ballot(n > 0));
+      const int v = wave_incl_scan(n) + total;
+      if (u < R) {
+        s_n[u + 1] = v;
+        s_k[u + 1] = n;  // kept for the second pass, read back by this lane only
+      }
+      total = __builtin_amdgcn_readlane(v, 63);
+    }
+    // k_u = ceil(n_u / C) <= n_u / C + 1, so with C = T / (NB - R') (R' non-empty units)
+    // the work-groups with work never exceed NB: all of them are resident at once.
+    const int nb_eff =
+        a.n_blocks - nonempty >= a.n_blocks / 4 ? a.n_blocks - nonempty : a.n_blocks;
+    const int C = chunk_keys(total, nb_eff);
+    int groups = 0;
+    for (int base = 0; base < R; base += 64) {
+      const int u = base + lane;
+      const int n = u < R ? s_k[u + 1] : 0;
+      const int v = wave_incl_scan((n + C - 1) / C) + groups;
+      if (u < R) s_k[u + 1] = v;
+      groups = __builtin_amdgcn_readlane(v, 63);
+    }
+    if (lane == 0) {
+      s_n[0] = 0;
+      s_k[0] = 0;
+    }
+  }
   __syncthreads();
   if (blockIdx.x == 0)
     for (int u = tid; u <= R; u += MNW * 64) a.plan[u] = s_k[u];
@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   const int seg_hi = min(n_u, seg_lo + per);  // non-empty: (k_u - 1) * per < n_u
 
   const int b = u / a.Hkv, g = u % a.Hkv;
-  const RowRange r = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
+  const int slot_lo = s_slot[u];
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
 
   char* my_tile = s_kv + wave * WAVE_TILE;
@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   auto load = [&](uint4(&rg)[4], int t) {
     const int key = seg_lo + t * TK + l16;
     const int kc = key < seg_hi ? key : seg_hi - 1;
-    const int slot = key_slot(r, kc, a.cap);
+    const int slot = key_slot(slot_lo, kc, a.cap);
     const uint4* rp = (slot == new_slot ? knew : kbase + (size_t)slot * (MD / 8)) + 16 * wave + lg;
 #pragma unroll
     for (int j = 0; j < 4; ++j) rg[j] = rp[4 * j];

@@ -56,9 +56,12 @@ __device__ __forceinline__ RowRange row_range(int ctx, int q_pos, int window, in
 // Physical slot of the i-th valid key (0 <= i < n): positions are consecutive, so the
 // slot advances by one and wraps once at the ring's end (n <= W guarantees no second
 // wrap).  For a linear cache slot_lo + i <= hi < C and the wrap never fires.
-__device__ __forceinline__ int key_slot(const RowRange& r, int i, int cap) {
-  int s = r.slot_lo + i;
+__device__ __forceinline__ int key_slot(int slot_lo, int i, int cap) {
+  const int s = slot_lo + i;
   return s >= cap ? s - cap : s;
+}
+__device__ __forceinline__ int key_slot(const RowRange& r, int i, int cap) {
+  return key_slot(r.slot_lo, i, cap);
 }
 
 // bf16 pair held in one dword -> two floats (exact widening).
