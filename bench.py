@@ -55,7 +55,7 @@ def parse_args():
 # Single-layer workloads measured with --workload (the default line is the 48-layer step).
 SINGLE_LAYER = {"hd128_sliding": "HD128_SLIDING", "g4_12b_sliding": "G4_12B_SLIDING",
                 "g4_12b_global": "G4_12B_GLOBAL", "spec_decode_sliding": "SPEC_DECODE_SLIDING",
-                "fp8_sliding": "FP8_SLIDING"}
+                "fp8_sliding": "FP8_SLIDING", "fp8_global": "FP8_GLOBAL"}
 
 
 def log(msg):

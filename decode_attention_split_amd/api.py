@@ -311,7 +311,8 @@ def kv_append_fp8(k_codes, k_scales, v_codes, v_scales, k_new, v_new, pos, kind:
 
 def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos, window: int,
                softcap: float, scale: float, kind: int, out=None, workspace=None,
-               max_ctx: int = 0, split_keys: int = 0, deterministic: bool = False, stream=None):
+               max_ctx: int = 0, split_keys: int = 0, deterministic: bool = False,
+               impl: int = IMPL_AUTO, stream=None):
     """Decode over fp8 caches; q [B, Hq, D] (one token) or [B, T, Hq, D] (T tokens at
     q_pos[b] + t); returns out of the same shape, float32 (see gemma_attn_decode_fp8)."""
     single = q.dim() == 3
@@ -338,7 +339,7 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos, window:
         _need(out, "out", torch.float32, len(want))
         if tuple(out.shape) != want:
             raise ValueError(f"out must be {list(want)}")
-    opts = make_opts(split_keys, IMPL_AUTO, deterministic)
+    opts = make_opts(split_keys, impl, deterministic)
     lib = _lib.load()
     need = lib.ga_decode_fp8_workspace_bytes(ctypes.byref(shape), int(T), int(window),
                                              ctypes.byref(opts))

@@ -205,7 +205,7 @@ void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
 // k_eq_v: 1 / 0 when known (a decode call), -1 for a workspace query, which then sizes
 // for whichever implementation AUTO may pick.
 int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, int k_eq_v,
-                  Plan* p, int T = 1, bool vector_only = false) {
+                  Plan* p, int T = 1, bool fp8 = false) {
   int impl = GA_IMPL_AUTO, ts = 0;
   if (o) {
     for (int i = 0; i < 5; ++i)
@@ -216,7 +216,7 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
     if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
     if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
   }
-  if (vector_only) {  // fp8 caches: the vector kernel
+  if (fp8 && T > 1) {  // fp8 caches with several tokens: the vector kernel
     if (impl == GA_IMPL_MFMA) return GA_ERR_OPTS;
     return valu_plan(s, window, ts, T, p);
   }

@@ -78,6 +78,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+template <bool FP8>
 __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_kv[kLdsKV];
   __shared__ floatx4_t s_part[2][MNW][64];
@@ -168,17 +169,24 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
 
   char* my_tile = s_kv + wave * WAVE_TILE;
   char* lds_w = my_tile + l16 * ROWQ + lg * 16;                          // row writes
+  char* lds_w8 = my_tile + l16 * ROWQ + lg * 32;                         // fp8: 16 d per lane
   char* lds_r = my_tile + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;  // transposed reads
   int par = 0;  // s_part double buffer
 
-  // Q^T operand for this wave's slice: head l16, d = 128 w + 32 j + 8 lg + 0..7
+  // Q^T operand for this wave's slice, in the order the K rows are loaded: head l16,
+  // d = 128 w + 32 j + 8 lg + 0..7 (bf16 rows: 16 bytes per lane and j), or
+  // d = 128 w + 64 (j / 2) + 16 lg + 8 (j % 2) + 0..7 (fp8 rows: 16 codes per lane and
+  // pair of j).  Any order of d works as long as K and Q^T share it.
   uint4 qv[4];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + (head0 + l16) * MD);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qv[j] = qp[16 * wave + 4 * j + lg];
+    for (int j = 0; j < 4; ++j)
+      qv[j] = FP8 ? qp[16 * wave + 8 * (j / 2) + 2 * lg + (j % 2)] : qp[16 * wave + 4 * j + lg];
   }
   const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + (size_t)u * a.cap * (MD / 8);
+  const uint4* cbase = reinterpret_cast<const uint4*>(a.k8) + (size_t)u * a.cap * (MD / 16);
+  const float* sbase = FP8 ? a.k_scale + (size_t)u * a.cap : nullptr;
   const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
   const uint4* knew = a.new_pos ? reinterpret_cast<const uint4*>(a.k_new) + (size_t)u * (MD / 8)
                                 : kbase;
@@ -190,23 +198,58 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
 
   const int nt = (seg_hi - seg_lo + TK - 1) / TK;
 
+  // One tile's registers: bf16 rows in rg[0..3]; fp8 rows: the 32 codes in rg[0..1] and
+  // the row scales of keys 4 lg + 0..3 (the keys this lane's logits belong to) in rg[2].
   auto load = [&](uint4(&rg)[4], int t) {
     const int key = seg_lo + t * TK + l16;
     const int kc = key < seg_hi ? key : seg_hi - 1;
     const int slot = key_slot(slot_lo, kc, a.cap);
-    const uint4* rp = (slot == new_slot ? knew : kbase + (size_t)slot * (MD / 8)) + 16 * wave + lg;
+    if constexpr (FP8) {
+      const uint4* cp = cbase + (size_t)slot * (MD / 16) + 8 * wave + lg;
+      rg[0] = cp[0];
+      rg[1] = cp[4];
+      float sc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rg[j] = rp[4 * j];
+      for (int i = 0; i < 4; ++i) {
+        const int ks = seg_lo + t * TK + 4 * lg + i;
+        sc[i] = sbase[key_slot(slot_lo, ks < seg_hi ? ks : seg_hi - 1, a.cap)];
+      }
+      rg[2] = make_uint4(__float_as_uint(sc[0]), __float_as_uint(sc[1]),
+                         __float_as_uint(sc[2]), __float_as_uint(sc[3]));
+    } else {
+      const uint4* rp =
+          (slot == new_slot ? knew : kbase + (size_t)slot * (MD / 8)) + 16 * wave + lg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rg[j] = rp[4 * j];
+    }
   };
 
   auto step = [&](uint4(&rg)[4], int t) {
     const int k0 = seg_lo + t * TK;
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+    float ksc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FP8) {
+      // codes -> bf16 (exact); the tile's rows go to LDS in natural d order for V
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s = mfma_k32(rg[j], qv[j], s);
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint4 lo = e4m3x8_to_bf16x8(rg[jj].x, rg[jj].y);
+        const uint4 hi = e4m3x8_to_bf16x8(rg[jj].z, rg[jj].w);
+        s = mfma_k32(lo, qv[2 * jj], s);
+        s = mfma_k32(hi, qv[2 * jj + 1], s);
+        *reinterpret_cast<uint4*>(lds_w8 + jj * 128) = lo;
+        *reinterpret_cast<uint4*>(lds_w8 + jj * 128 + 16) = hi;
+      }
+      ksc[0] = __uint_as_float(rg[2].x);
+      ksc[1] = __uint_as_float(rg[2].y);
+      ksc[2] = __uint_as_float(rg[2].z);
+      ksc[3] = __uint_as_float(rg[2].w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = mfma_k32(rg[j], qv[j], s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(lds_w + j * 64) = rg[j];
+    }
     s_part[par][wave][lane] = s;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(lds_w + j * 64) = rg[j];
     load(rg, t + 4);  // unconditional (clamped past the end): keeps wait counts partial
     __syncthreads();
     const floatx4_t full =
@@ -218,7 +261,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = full[i] * a.scale;
+      float v = full[i] * ksc[i] * a.scale;  // fp8: the key's row scale
       if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
       x[i] = (k0 + 4 * lg + i < seg_hi) ? v * kLog2e : -INFINITY;
       mx = fmaxf(mx, x[i]);
@@ -236,6 +279,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     for (int i = 0; i < 4; ++i) {
       p[i] = exp2_fast(x[i] - m);
       l += p[i];
+      if constexpr (FP8) p[i] *= ksc[i];  // K = V: the value row's scale is the key's
     }
     const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
     const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
@@ -368,7 +412,10 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
   // C = T / NB and the sum stays <= NB + R.  Work-groups u < R also carry unit u's append.
   const unsigned grid =
       (unsigned)(R <= kMfmaBlocks - kMfmaBlocks / 4 ? kMfmaBlocks : kMfmaBlocks + R);
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3(grid), dim3(MNW * 64), 0, stream, a);
+  if (a.fp8)
+    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(MNW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(MNW * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);

@@ -39,6 +39,20 @@ __device__ __forceinline__ floatx4_t mfma_k32(u32x4_t a, u32x4_t b, floatx4_t c)
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Eight e4m3 codes (code i in byte i of w0, w1) -> eight bf16 values, exactly: every
+// e4m3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value.  v_cvt_pk_f32_fp8
+// widens two codes to floats, whose upper halves are the bf16 encodings.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const float2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const float2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  auto hi2 = [](float2_t f) {
+    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+  };
+  return make_uint4(hi2(a), hi2(b), hi2(c), hi2(d));
+}
+
 __device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }

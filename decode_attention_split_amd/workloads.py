@@ -178,6 +178,12 @@ FP8_SLIDING = replace(G4_12B_SLIDING, name="gemma4-12b sliding layer, fp8 e4m3 c
                       "per-row scales, B64 16q/8kv hd256 ring w1024 ctx U[512,8192] softcap50",
                       seed=8, kv_dtype="fp8")
 
+# The 12B global layer (K = V, hd512, 16 query heads on one KV head) over an fp8 cache:
+# the matrix-core kernel widens the codes to bf16 in registers.
+FP8_GLOBAL = replace(G4_12B_GLOBAL, name="gemma4-12b global layer, fp8 e4m3 cache with per-row "
+                     "scales, B16 16q/1kv K=V hd512 linear C32768 ctx U[4096,32768]", seed=10,
+                     kv_dtype="fp8")
+
 # Speculative verification on the 12B sliding layer: 7 draft tokens plus the current one
 # (T = 8, the k = 7 spec decode of the "Gemma 4 12B (unified multimodal)" record, item
 # "(2)"), each masked at its own position.  The ring keeps w + T - 1 = 1031 slots so the

@@ -200,3 +200,58 @@ def test_fp8_sliding_layer_full_size_sampled_rows():
                                            ctx[rows], ctx[rows] - 1, g.window, g.softcap,
                                            g.q_scale, g.kind)
     assert_parity(out[rows], ref, "fp8 sliding full size")
+
+
+@pytest.mark.parametrize("kind", [api.RING, api.LINEAR])
+def test_fp8_global_matrix_cores_match_vector_kernel_and_oracle(kind):
+    """The K = V global geometry (hd512, 16 query heads per KV head) on fp8 codes: the
+    matrix-core kernel (codes widened to bf16 in registers, scales on logits and value
+    weights) and the vector kernel both match the oracle, over ragged contexts that leave
+    partial 16-key tiles, a one-key row and rows split over several work-groups."""
+    Hkv, D = 2, 512
+    if kind == api.RING:
+        cap, window = 300, 300
+        ctx = [1, 16, 17, 299, 300, 1000, 4 * 300 + 7]
+        max_ctx = max(ctx)
+    else:
+        cap, window = 700, 0
+        ctx = [1, 16, 17, 333, 512, 699, 700]
+        max_ctx = cap
+    inp = Fp8Inputs(4242 + kind, len(ctx), 1, 16 * Hkv, Hkv, D, cap, True, ctx)
+    inp.poison(window, kind).to_device()
+    for softcap in [0.0, 30.0]:
+        ref, _ = inp.oracle(window, softcap, default_scale(D), kind)
+        for impl in [api.IMPL_MFMA, api.IMPL_VALU]:
+            out = inp.run(window, softcap, default_scale(D), kind, max_ctx=max_ctx, impl=impl)
+            assert_parity(out, ref, f"fp8 global kind={kind} softcap={softcap} impl={impl}")
+
+
+def test_fp8_global_layer_full_size_sampled_rows():
+    """The 12B global layer (B 16, 16q/1kv K = V hd512, linear C 32768, ctx U[4096, 32768])
+    on an fp8 cache filled by quantizing appends of every valid position; the automatic
+    plan (matrix cores) checked against the oracle on sampled rows."""
+    w = wl.FP8_GLOBAL
+    g = w.layers[0]
+    B, D, C = w.batch, g.head_dim, g.capacity
+    ctx = synth.uniform_int(synth.generator(w.seed), B, w.ctx_lo, w.ctx_hi).numpy() \
+        .astype(np.int32)
+    gd = synth.generator(91, device="cuda")
+    kc = torch.empty((B, 1, C, D), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B, 1, C), dtype=torch.float32, device="cuda")
+    chunk = 1024
+    for p0 in range(0, int(ctx.max()), chunk):
+        kn = synth.normal_bf16(gd, (B, chunk, 1, D), device="cuda")
+        api.kv_append_fp8(kc, ks, None, None, kn, None,
+                          torch.full((B,), p0, dtype=torch.int32, device="cuda"), g.kind)
+    ctx_t = torch.from_numpy(ctx).cuda()
+    q = synth.normal_bf16(gd, (B, g.num_q_heads, D), device="cuda")
+    out = api.decode_fp8(q, kc, ks, None, None, ctx_t, ctx_t - 1, g.window, g.softcap,
+                         g.q_scale, g.kind, max_ctx=C)
+    torch.cuda.synchronize()
+    rows = sorted({0, int(np.argmax(ctx)), int(np.argmin(ctx))})
+    log(f"fp8 global rows {rows} ctx {ctx[rows].tolist()}")
+    kcr, ksr = kc[rows].cpu().numpy(), ks[rows].cpu().numpy()
+    ref, _, _, _ = oracle.decode_fp8_multi(synth.bits(q[rows].cpu())[:, None], kcr, ksr, None,
+                                           None, ctx[rows], ctx[rows] - 1, g.window, g.softcap,
+                                           g.q_scale, g.kind)
+    assert_parity(out[rows].unsqueeze(1), ref, "fp8 global full size")
