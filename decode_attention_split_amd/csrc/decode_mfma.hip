@@ -54,9 +54,9 @@ constexpr float kRescaleLog2 = 8.0f;
 // LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
 // (160 KiB each): every CU then holds the same number of equal-work work-groups.
 constexpr int kLdsCU = 160 * 1024;
-constexpr int kLdsOther = 2 * MNW * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4;
+constexpr int kLdsOther = 2 * MNW * 2 * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4;
 constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
-constexpr int kLdsKV = MNW * WAVE_TILE > kLdsTile ? MNW * WAVE_TILE : kLdsTile;
+constexpr int kLdsKV = 2 * MNW * WAVE_TILE > kLdsTile ? 2 * MNW * WAVE_TILE : kLdsTile;
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
 
@@ -81,7 +81,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 template <bool FP8>
 __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_kv[kLdsKV];
-  __shared__ floatx4_t s_part[2][MNW][64];
+  __shared__ floatx4_t s_part[2][MNW][2][64];  // [buffer][wave][tile of the step][lane]
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
   __shared__ int s_slot[kMfmaMaxUnits];   // slot of each unit's first valid key
@@ -167,10 +167,11 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   const int slot_lo = s_slot[u];
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
 
-  char* my_tile = s_kv + wave * WAVE_TILE;
-  char* lds_w = my_tile + l16 * ROWQ + lg * 16;                          // row writes
-  char* lds_w8 = my_tile + l16 * ROWQ + lg * 32;                         // fp8: 16 d per lane
-  char* lds_r = my_tile + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;  // transposed reads
+  // this wave's two tile buffers (one step's tiles) and its transposed-read addresses
+  char* tile_a = s_kv + wave * 2 * WAVE_TILE;
+  char* tile_b = tile_a + WAVE_TILE;
+  char* lds_ra = tile_a + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;
+  char* lds_rb = tile_b + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;
   int par = 0;  // s_part double buffer
 
   // Q^T operand for this wave's slice, in the order the K rows are loaded: head l16,
@@ -224,20 +225,23 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     }
   };
 
-  auto step = [&](uint4(&rg)[4], int t) {
-    const int k0 = seg_lo + t * TK;
-    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-    float ksc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  // One step = two 16-key tiles (ra: keys k0 .. k0 + 15, rb: the next 16): their products
+  // and softmax chains interleave, and one barrier and one max update cover 32 keys.
+  // A tile's S^T partial over this wave's d slice: K rows (A operand) times Q^T; the
+  // tile's rows also go to LDS in natural d order (the V operand).  fp8 codes are widened
+  // to bf16 first; ksc gets the scales of the keys 4 lg + 0..3 of the tile.
+  auto tile_scores = [&](const uint4(&rg)[4], char* tile, floatx4_t& s, float(&ksc)[4]) {
+    s = floatx4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
-      // codes -> bf16 (exact); the tile's rows go to LDS in natural d order for V
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const uint4 lo = e4m3x8_to_bf16x8(rg[jj].x, rg[jj].y);
         const uint4 hi = e4m3x8_to_bf16x8(rg[jj].z, rg[jj].w);
         s = mfma_k32(lo, qv[2 * jj], s);
         s = mfma_k32(hi, qv[2 * jj + 1], s);
-        *reinterpret_cast<uint4*>(lds_w8 + jj * 128) = lo;
-        *reinterpret_cast<uint4*>(lds_w8 + jj * 128 + 16) = hi;
+        char* w8 = tile + l16 * ROWQ + lg * 32 + jj * 128;  // 16 d per lane and jj
+        *reinterpret_cast<uint4*>(w8) = lo;
+        *reinterpret_cast<uint4*>(w8 + 16) = hi;
       }
       ksc[0] = __uint_as_float(rg[2].x);
       ksc[1] = __uint_as_float(rg[2].y);
@@ -246,27 +250,46 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) s = mfma_k32(rg[j], qv[j], s);
+      char* w = tile + l16 * ROWQ + lg * 16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(lds_w + j * 64) = rg[j];
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(w + j * 64) = rg[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ksc[i] = 1.0f;
     }
-    s_part[par][wave][lane] = s;
-    load(rg, t + 4);  // unconditional (clamped past the end): keeps wait counts partial
+  };
+
+  auto step2 = [&](uint4(&ra)[4], uint4(&rb)[4], int t) {
+    const int k0 = seg_lo + t * TK;
+    floatx4_t sa, sb;
+    float ka[4], kb[4];
+    tile_scores(ra, tile_a, sa, ka);
+    tile_scores(rb, tile_b, sb, kb);
+    s_part[par][wave][0][lane] = sa;
+    s_part[par][wave][1][lane] = sb;
+    load(ra, t + 4);  // unconditional (clamped past the end): keeps wait counts partial
+    load(rb, t + 5);
     __syncthreads();
-    const floatx4_t full =
-        ((s_part[par][0][lane] + s_part[par][1][lane]) + s_part[par][2][lane]) +
-        s_part[par][3][lane];
+    const floatx4_t fa = ((s_part[par][0][0][lane] + s_part[par][1][0][lane]) +
+                          s_part[par][2][0][lane]) + s_part[par][3][0][lane];
+    const floatx4_t fb = ((s_part[par][0][1][lane] + s_part[par][1][1][lane]) +
+                          s_part[par][2][1][lane]) + s_part[par][3][1][lane];
     par ^= 1;
-    // softmax: lane holds head l16, keys k0 + 4 lg + i
-    float x[4];
+    // softmax: lane holds head l16, keys k0 + 4 lg + i (xa) and k0 + 16 + 4 lg + i (xb)
+    float xa[4], xb[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = full[i] * ksc[i] * a.scale;  // fp8: the key's row scale
-      if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
-      x[i] = (k0 + 4 * lg + i < seg_hi) ? v * kLog2e : -INFINITY;
-      mx = fmaxf(mx, x[i]);
+      float va = fa[i] * ka[i] * a.scale;  // fp8: the key's row scale
+      float vb = fb[i] * kb[i] * a.scale;
+      if (a.softcap > 0.0f) {
+        va = softcap_tanh(va, a.softcap, a.inv_softcap);
+        vb = softcap_tanh(vb, a.softcap, a.inv_softcap);
+      }
+      xa[i] = (k0 + 4 * lg + i < seg_hi) ? va * kLog2e : -INFINITY;
+      xb[i] = (k0 + TK + 4 * lg + i < seg_hi) ? vb * kLog2e : -INFINITY;
+      mx = fmaxf(mx, fmaxf(xa[i], xb[i]));
     }
-    mx = rows_max(mx);  // over the 16 keys of the tile (four lane rows)
+    mx = rows_max(mx);  // over the 32 keys of the step (four lane rows)
     if (mx > m + kRescaleLog2) {
       const float f = exp2_fast(m - mx);
       l *= f;
@@ -274,30 +297,46 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
       for (int i = 0; i < 8; ++i) acc[i] *= f;
       m = mx;
     }
-    float p[4];
+    float pa[4], pb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = exp2_fast(x[i] - m);
-      l += p[i];
-      if constexpr (FP8) p[i] *= ksc[i];  // K = V: the value row's scale is the key's
+      pa[i] = exp2_fast(xa[i] - m);
+      pb[i] = exp2_fast(xb[i] - m);
+      l += pa[i] + pb[i];
+      if constexpr (FP8) {  // K = V: the value row's scale is the key's
+        pa[i] *= ka[i];
+        pb[i] *= kb[i];
+      }
     }
-    const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
-    const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-    const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-    const short4_t ph = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
-    const short4_t pl = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
+    // P^T operands (lane: head l16, keys 4 lg + 0..3), split into bf16 hi + lo parts so
+    // the probabilities keep ~16 mantissa bits
+    auto split = [](const float(&p)[4], short4_t& ph, short4_t& pl) {
+      const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+      const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+      const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+      ph = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
+      pl = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
+    };
+    short4_t pah, pal, pbh, pbl;
+    split(pa, pah, pal);
+    split(pb, pbh, pbl);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const short4_t va =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_r + db * 32));
-      acc[db] = mfma_k16(va, ph, acc[db]);
-      acc[db] = mfma_k16(va, pl, acc[db]);
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_ra + db * 32));
+      const short4_t vb =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_rb + db * 32));
+      acc[db] = mfma_k16(va, pah, acc[db]);
+      acc[db] = mfma_k16(va, pal, acc[db]);
+      acc[db] = mfma_k16(vb, pbh, acc[db]);
+      acc[db] = mfma_k16(vb, pbl, acc[db]);
     }
   };
 
-  // Straight-line loop body over whole groups of 4 tiles; the last 0-3 tiles run after
-  // it, so the loop header never sees a path with a buffer's loads still unconsumed
-  // (which would make the compiler drain every prefetch there).
+  // Straight-line loop body over whole groups of 4 tiles (two steps); the last 0-3 tiles
+  // run after it, a step's second tile past the end being all masked, so the loop header
+  // never sees a path with a buffer's loads still unconsumed (which would make the
+  // compiler drain every prefetch there).
   uint4 r0[4], r1[4], r2[4], r3[4];
   load(r0, 0);
   load(r1, 1);
@@ -305,14 +344,11 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   load(r3, 3);
   int t = 0;
   for (; t + 3 < nt; t += 4) {
-    step(r0, t);
-    step(r1, t + 1);
-    step(r2, t + 2);
-    step(r3, t + 3);
+    step2(r0, r1, t);
+    step2(r2, r3, t + 2);
   }
-  if (t < nt) step(r0, t);
-  if (t + 1 < nt) step(r1, t + 1);
-  if (t + 2 < nt) step(r2, t + 2);
+  if (t < nt) step2(r0, r1, t);
+  if (t + 2 < nt) step2(r2, r3, t + 2);
 
   app.store(a);
   // ---- this wave's slice of the result (m and l are identical in every wave)
