@@ -54,7 +54,7 @@ constexpr float kRescaleLog2 = 8.0f;
 // LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
 // (160 KiB each): every CU then holds the same number of equal-work work-groups.
 constexpr int kLdsCU = 160 * 1024;
-constexpr int kLdsOther = 2 * MNW * 2 * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4;
+constexpr int kLdsOther = 2 * MNW * 2 * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4 + 2 * 2 * TK * 4;
 constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
 constexpr int kLdsKV = 2 * MNW * WAVE_TILE > kLdsTile ? 2 * MNW * WAVE_TILE : kLdsTile;
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
@@ -82,6 +82,10 @@ template <bool FP8>
 __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_kv[kLdsKV];
   __shared__ floatx4_t s_part[2][MNW][2][64];  // [buffer][wave][tile of the step][lane]
+  __shared__ __attribute__((aligned(16))) float s_scale[2][2][TK];  // fp8 row scales
+  // Tiles in flight per wave: four bf16 tiles (64 KiB per work-group); fp8 tiles are half
+  // the bytes, so eight keep as many bytes in flight (the loop is latency-bound otherwise).
+  constexpr int NF = FP8 ? 8 : 4;
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
   __shared__ int s_slot[kMfmaMaxUnits];   // slot of each unit's first valid key
@@ -200,7 +204,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   const int nt = (seg_hi - seg_lo + TK - 1) / TK;
 
   // One tile's registers: bf16 rows in rg[0..3]; fp8 rows: the 32 codes in rg[0..1] and
-  // the row scales of keys 4 lg + 0..3 (the keys this lane's logits belong to) in rg[2].
+  // the scale of the lane's key (key l16 of the tile) in rg[2].x.
   auto load = [&](uint4(&rg)[4], int t) {
     const int key = seg_lo + t * TK + l16;
     const int kc = key < seg_hi ? key : seg_hi - 1;
@@ -209,14 +213,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
       const uint4* cp = cbase + (size_t)slot * (MD / 16) + 8 * wave + lg;
       rg[0] = cp[0];
       rg[1] = cp[4];
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ks = seg_lo + t * TK + 4 * lg + i;
-        sc[i] = sbase[key_slot(slot_lo, ks < seg_hi ? ks : seg_hi - 1, a.cap)];
-      }
-      rg[2] = make_uint4(__float_as_uint(sc[0]), __float_as_uint(sc[1]),
-                         __float_as_uint(sc[2]), __float_as_uint(sc[3]));
+      rg[2].x = __float_as_uint(sbase[slot]);  // the scale of this lane's key (l16)
     } else {
       const uint4* rp =
           (slot == new_slot ? knew : kbase + (size_t)slot * (MD / 8)) + 16 * wave + lg;
@@ -229,8 +226,8 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   // and softmax chains interleave, and one barrier and one max update cover 32 keys.
   // A tile's S^T partial over this wave's d slice: K rows (A operand) times Q^T; the
   // tile's rows also go to LDS in natural d order (the V operand).  fp8 codes are widened
-  // to bf16 first; ksc gets the scales of the keys 4 lg + 0..3 of the tile.
-  auto tile_scores = [&](const uint4(&rg)[4], char* tile, floatx4_t& s, float(&ksc)[4]) {
+  // to bf16 first.
+  auto tile_scores = [&](const uint4(&rg)[4], char* tile, floatx4_t& s) {
     s = floatx4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
 #pragma unroll
@@ -243,32 +240,36 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
         *reinterpret_cast<uint4*>(w8) = lo;
         *reinterpret_cast<uint4*>(w8 + 16) = hi;
       }
-      ksc[0] = __uint_as_float(rg[2].x);
-      ksc[1] = __uint_as_float(rg[2].y);
-      ksc[2] = __uint_as_float(rg[2].z);
-      ksc[3] = __uint_as_float(rg[2].w);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) s = mfma_k32(rg[j], qv[j], s);
       char* w = tile + l16 * ROWQ + lg * 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(w + j * 64) = rg[j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ksc[i] = 1.0f;
     }
   };
 
   auto step2 = [&](uint4(&ra)[4], uint4(&rb)[4], int t) {
     const int k0 = seg_lo + t * TK;
     floatx4_t sa, sb;
-    float ka[4], kb[4];
-    tile_scores(ra, tile_a, sa, ka);
-    tile_scores(rb, tile_b, sb, kb);
+    tile_scores(ra, tile_a, sa);
+    tile_scores(rb, tile_b, sb);
     s_part[par][wave][0][lane] = sa;
     s_part[par][wave][1][lane] = sb;
-    load(ra, t + 4);  // unconditional (clamped past the end): keeps wait counts partial
-    load(rb, t + 5);
+    if (FP8 && wave == 0 && lg == 0) {  // the keys' row scales, for every wave's logits
+      s_scale[par][0][l16] = __uint_as_float(ra[2].x);
+      s_scale[par][1][l16] = __uint_as_float(rb[2].x);
+    }
+    load(ra, t + NF);  // unconditional (clamped past the end): keeps wait counts partial
+    load(rb, t + NF + 1);
     __syncthreads();
+    float ka[4] = {1.0f, 1.0f, 1.0f, 1.0f}, kb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FP8) {  // scales of the keys 4 lg + 0..3 this lane's logits belong to
+      const float4 a4 = *reinterpret_cast<const float4*>(&s_scale[par][0][4 * lg]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&s_scale[par][1][4 * lg]);
+      ka[0] = a4.x; ka[1] = a4.y; ka[2] = a4.z; ka[3] = a4.w;
+      kb[0] = b4.x; kb[1] = b4.y; kb[2] = b4.z; kb[3] = b4.w;
+    }
     const floatx4_t fa = ((s_part[par][0][0][lane] + s_part[par][1][0][lane]) +
                           s_part[par][2][0][lane]) + s_part[par][3][0][lane];
     const floatx4_t fb = ((s_part[par][0][1][lane] + s_part[par][1][1][lane]) +
@@ -320,35 +321,38 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     short4_t pah, pal, pbh, pbl;
     split(pa, pah, pal);
     split(pb, pbh, pbl);
+    // O^T += V^T P^T over the step's 32 keys with v_mfma_f32_16x16x32_bf16: lane (l16, lg)
+    // holds k slots 8 lg + 0..7 = keys 4 lg + 0..3 of tile a, then of tile b, in both
+    // operands (the transposed reads give V^T for exactly those keys at column l16, and
+    // the softmax left P for exactly those keys), so one product covers both tiles.
+    const uint4 ph = cat4(pah, pbh), pl = cat4(pal, pbl);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const short4_t va =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_ra + db * 32));
       const short4_t vb =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_rb + db * 32));
-      acc[db] = mfma_k16(va, pah, acc[db]);
-      acc[db] = mfma_k16(va, pal, acc[db]);
-      acc[db] = mfma_k16(vb, pbh, acc[db]);
-      acc[db] = mfma_k16(vb, pbl, acc[db]);
+      const uint4 v8 = cat4(va, vb);
+      acc[db] = mfma_k32(v8, ph, acc[db]);
+      acc[db] = mfma_k32(v8, pl, acc[db]);
     }
   };
 
-  // Straight-line loop body over whole groups of 4 tiles (two steps); the last 0-3 tiles
+  // Straight-line loop body over whole groups of NF tiles (NF / 2 steps); the last tiles
   // run after it, a step's second tile past the end being all masked, so the loop header
   // never sees a path with a buffer's loads still unconsumed (which would make the
   // compiler drain every prefetch there).
-  uint4 r0[4], r1[4], r2[4], r3[4];
-  load(r0, 0);
-  load(r1, 1);
-  load(r2, 2);
-  load(r3, 3);
+  uint4 buf[NF][4];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) load(buf[i], i);
   int t = 0;
-  for (; t + 3 < nt; t += 4) {
-    step2(r0, r1, t);
-    step2(r2, r3, t + 2);
+  for (; t + NF - 1 < nt; t += NF) {
+#pragma unroll
+    for (int i = 0; i < NF; i += 2) step2(buf[i], buf[i + 1], t + i);
   }
-  if (t < nt) step2(r0, r1, t);
-  if (t + 2 < nt) step2(r2, r3, t + 2);
+#pragma unroll
+  for (int i = 0; i < NF; i += 2)
+    if (t + i < nt) step2(buf[i], buf[i + 1], t + i);
 
   app.store(a);
   // ---- this wave's slice of the result (m and l are identical in every wave)

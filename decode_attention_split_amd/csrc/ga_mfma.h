@@ -53,6 +53,12 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return make_uint4(hi2(a), hi2(b), hi2(c), hi2(d));
 }
 
+// Two 4 x bf16 operand halves -> one 8 x bf16 operand (lo in k slots 0..3).
+__device__ __forceinline__ uint4 cat4(short4_t lo, short4_t hi) {
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 __device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
