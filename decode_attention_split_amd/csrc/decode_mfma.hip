@@ -50,6 +50,9 @@ constexpr int MNW = 4;         // waves per work-group, one head_dim slice each
 constexpr int DQ = MD / MNW;   // head_dim slice of a wave
 constexpr int ROWQ = DQ * 2 + 32;   // LDS bytes per key row of a wave's slice (bank spread)
 constexpr int WAVE_TILE = TK * ROWQ;
+#ifndef GA_FP8_TILES
+#define GA_FP8_TILES 8
+#endif
 constexpr float kRescaleLog2 = 8.0f;
 // LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
 // (160 KiB each): every CU then holds the same number of equal-work work-groups.
@@ -85,7 +88,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   __shared__ __attribute__((aligned(16))) float s_scale[2][2][TK];  // fp8 row scales
   // Tiles in flight per wave: four bf16 tiles (64 KiB per work-group); fp8 tiles are half
   // the bytes, so eight keep as many bytes in flight (the loop is latency-bound otherwise).
-  constexpr int NF = FP8 ? 8 : 4;
+  constexpr int NF = FP8 ? GA_FP8_TILES : 4;
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
   __shared__ int s_slot[kMfmaMaxUnits];   // slot of each unit's first valid key

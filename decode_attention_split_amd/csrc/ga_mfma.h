@@ -40,17 +40,17 @@ __device__ __forceinline__ floatx4_t mfma_k32(u32x4_t a, u32x4_t b, floatx4_t c)
 }
 
 // Eight e4m3 codes (code i in byte i of w0, w1) -> eight bf16 values, exactly: every
-// e4m3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value.  v_cvt_pk_f32_fp8
-// widens two codes to floats, whose upper halves are the bf16 encodings.
+// e4m3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value.  One
+// v_cvt_scalef32_pk_bf16_fp8 (scale 1) widens two codes; checked on the GPU to give the
+// same bits as v_cvt_pk_f32_fp8 followed by taking each float's upper half, for all 256
+// codes in both halves of a word.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-  const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const float2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-  const float2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-  auto hi2 = [](float2_t f) {
-    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-  };
-  return make_uint4(hi2(a), hi2(b), hi2(c), hi2(d));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
 // Two 4 x bf16 operand halves -> one 8 x bf16 operand (lo in k slots 0..3).
