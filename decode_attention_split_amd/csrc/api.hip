@@ -170,8 +170,10 @@ int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   const long long units = (long long)s->batch * s->num_kv_heads * n_chunks;
   if (ts == 0) {
     const long long want = units > 0 ? (kRows16Waves + units - 1) / units : 1;
+    // whole 16-key tiles (the kernel's step), so the last split of a unit is not much
+    // shorter than the others; at least 64 keys, so a split outweighs its prologue
     long long t = nmax > 0 ? (nmax + want - 1) / want : 64;
-    t = (t + 63) / 64 * 64;
+    t = (t + 15) / 16 * 16;
     if (t < 64) t = 64;
     if (t > kMaxSplitKeys) t = kMaxSplitKeys;
     ts = (int)t;
