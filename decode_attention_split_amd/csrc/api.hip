@@ -157,10 +157,11 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   return GA_OK;
 }
 
-constexpr int kRows16Waves = 2048;  // one-wave work-groups wanted (8 per CU)
+constexpr int kRows16Waves = 2048;  // waves wanted (8 per CU)
 
 // Several tokens on the matrix cores: 16 query rows per unit (16 / G tokens of G heads),
-// splits sized so that about kRows16Waves single-wave work-groups cover the chip.
+// splits sized so that about kRows16Waves waves cover the chip (each split is one
+// work-group of ga::decode_rows16_waves waves).
 int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   const int G = s->num_q_heads / s->num_kv_heads;
   const int Tc = 16 / G;
@@ -169,7 +170,8 @@ int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   if (window > 0 && nmax > (long long)window + Tc - 1) nmax = (long long)window + Tc - 1;
   const long long units = (long long)s->batch * s->num_kv_heads * n_chunks;
   if (ts == 0) {
-    const long long want = units > 0 ? (kRows16Waves + units - 1) / units : 1;
+    const long long groups = kRows16Waves / ga::decode_rows16_waves(s->head_dim);
+    const long long want = units > 0 ? (groups + units - 1) / units : 1;
     // whole 16-key tiles (the kernel's step), so the last split of a unit is not much
     // shorter than the others; at least 64 keys, so a split outweighs its prologue
     long long t = nmax > 0 ? (nmax + want - 1) / want : 64;

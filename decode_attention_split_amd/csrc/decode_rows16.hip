@@ -4,24 +4,27 @@
 //
 // Why matrix cores: with 16 query rows on one KV head every cached byte feeds about 16
 // flops (q.k and p.v for each row), so the vector kernel, which reduces every row's dot
-// product across the lanes of a key, runs out of ALU long before HBM.  Here one wave is
-// one work-group and owns one split (a run of keys of one unit = batch row, KV head,
-// chunk of tokens); per 16-key tile:
+// product across the lanes of a key, runs out of ALU long before HBM.  Here one
+// work-group of four waves (two at head_dim 512) owns one split (a run of keys of one
+// unit = batch row, KV head, chunk of tokens); its waves take the split's 16-key tiles in
+// turn (wave w: tiles w, w + 4, ...), each with its own softmax state.  Per tile:
 //   S^T[16 keys][16 rows] = K[16][D] . Q^T[D][16]: D / 32 v_mfma_f32_16x16x32_bf16, the
 //     K operand loaded straight from HBM (lane: key l16, d = 8 lg + 32 j + 0..7), Q^T read
-//     from LDS in the same d order;
+//     from LDS (shared by the waves) in the same d order;
 //   S^T leaves lane l holding row l16 for keys 4 lg + 0..3, which is exactly the B operand
 //     of the P.V product, so the softmax works in place (row max / sum over the four lane
 //     groups) and P goes to the matrix cores as bf16 hi + lo parts (~16 mantissa bits);
-//   the V rows go to LDS once and come back transposed with ds_read_b64_tr_b16 as the A
-//     operand of O^T[D][16] += V^T[D][16 keys] . P^T[16 keys][16 rows]: D / 16 pairs of
-//     v_mfma_f32_16x16x16_bf16.
+//   the V rows go to the wave's LDS tile once and come back transposed with
+//     ds_read_b64_tr_b16 as the A operand of O^T[D][16] += V^T[D][16 keys] .
+//     P^T[16 keys][16 rows]: D / 16 pairs of v_mfma_f32_16x16x16_bf16.
 // One register buffer each for K and V, refilled as soon as a tile's products have used it
-// (several waves per SIMD hide the latency), one LDS tile.  Each split leaves (m, l, acc)
-// for the log-sum-exp merge kernel, or writes the output when it is the only split.  (A
-// merge by the last split to arrive would need a device-scope release per work-group,
-// which on this chip writes back the L2 and costs more than the separate merge.)  Softmax in log2 units, lazily rescaled (max raised only past +8); masked keys
-// weigh exactly zero.
+// (eight waves per CU hide the latency).  At the end the waves merge through LDS, so a
+// split is one partial: with one split per unit (batches that fill the chip) the output is
+// written directly and no merge kernel runs; otherwise each split leaves (m, l, acc) for
+// the log-sum-exp merge.  (A merge by the last split to arrive would need a device-scope
+// release per work-group, which on this chip writes back the L2 and costs more than the
+// separate merge.)  Softmax in log2 units, lazily rescaled (max raised only past +8);
+// masked keys weigh exactly zero.
 //
 // Definition followed: the same single-token definition per query token ("Gemma support"
 // pull request, Summary and Performance; "Gemma 4 12B (unified multimodal)" record: the
@@ -36,16 +39,26 @@ namespace {
 
 constexpr float kRescaleLog2R16 = 8.0f;
 
-template <int D, bool KV_SHARED>
-__global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
-  constexpr int NJ = D / 32;         // 16-byte K chunks per lane = QK products per tile
-  constexpr int NDB = D / 16;        // 16-wide head_dim blocks of the output
-  constexpr int ROWB = D * 2 + 32;   // LDS bytes per key row (padding spreads the banks)
-  constexpr int QROWB = D * 2 + 16;  // LDS bytes per query row
-  __shared__ __attribute__((aligned(16))) char s_v[16 * ROWB];
-  __shared__ __attribute__((aligned(16))) char s_q[16 * QROWB];
+template <int D>
+constexpr int rows16_waves() { return D == 512 ? 2 : 4; }
 
-  const int lane = threadIdx.x;
+template <int D, bool KV_SHARED>
+__global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(DecodeArgs a) {
+  constexpr int NW = rows16_waves<D>();  // waves per work-group, one split between them
+  constexpr int NJ = D / 32;             // 16-byte K chunks per lane = QK products per tile
+  constexpr int NDB = D / 16;            // 16-wide head_dim blocks of the output
+  constexpr int ROWB = D * 2 + 32;       // LDS bytes per key row (padding spreads the banks)
+  constexpr int QROWB = D * 2 + 16;      // LDS bytes per query row
+  constexpr int Q_BYTES = 16 * QROWB;
+  constexpr int TILE_BYTES = 16 * ROWB;
+  constexpr int LOOP_BYTES = Q_BYTES + NW * TILE_BYTES;  // Q rows + one V tile per wave
+  constexpr int ACC_BYTES = NW * 16 * D * 4;             // the waves' accumulators (end)
+  __shared__ __attribute__((aligned(16))) char s_mem[LOOP_BYTES > ACC_BYTES ? LOOP_BYTES
+                                                                            : ACC_BYTES];
+  __shared__ float s_ml[NW][16][2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
 
   const int S = a.n_split;
@@ -57,11 +70,14 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
   const int g = bid % a.Hkv;
   const int b = bid / a.Hkv;
 
-  // this lane's query row: l16 -> token chunk * Tc + l16 / Gh, head g * Gh + l16 % Gh
-  const int tok = chunk * a.Tc + l16 / a.Gh;
-  const bool row_on = tok < a.T;
-  const size_t row =
-      ((size_t)b * a.T + (row_on ? tok : a.T - 1)) * a.Hq + (size_t)g * a.Gh + l16 % a.Gh;
+  // query row rr of the unit: token chunk * Tc + rr / Gh, head g * Gh + rr % Gh
+  auto row_token = [&](int rr) { return chunk * a.Tc + rr / a.Gh; };
+  auto row_index = [&](int rr) -> size_t {
+    const int t = min(row_token(rr), a.T - 1);  // inactive rows alias the last token
+    return ((size_t)b * a.T + t) * a.Hq + (size_t)g * a.Gh + rr % a.Gh;
+  };
+  const bool row_on = row_token(l16) < a.T;  // this lane's row is l16
+  const size_t row = row_index(l16);
 
   const RowRange r = unit_range(a, b, chunk);
   const int k_begin = split * a.split_keys;
@@ -69,7 +85,7 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
   if (k_begin >= k_end) {
     // the only split of an empty unit writes its zero output; with several splits the
     // merge writes it
-    if (S == 1 && row_on) {
+    if (S == 1 && row_on && wave == 0) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<floatx4_t*>(a.out + row * D + 16 * db + 4 * lg) =
@@ -80,23 +96,26 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
   // the row's own valid positions (empty: lo > hi)
   int row_lo = 1, row_hi = 0;
   if (row_on) {
-    const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + tok, a.window, a.kind, a.cap,
-                                  a.max_keys);
+    const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + row_token(l16), a.window, a.kind,
+                                  a.cap, a.max_keys);
     if (rr.n > 0) {
       row_lo = rr.lo;
       row_hi = rr.hi;
     }
   }
 
-  // Q^T operand (row l16, d = 8 lg + 32 j + 0..7) parked in LDS and read per product,
-  // which keeps the registers for the K / V tiles in flight and the accumulators
+  // Q^T operand (row l16, d = 8 lg + 32 j + 0..7) parked in LDS (the waves share it) and
+  // read per product, which keeps the registers for the K / V tiles in flight and the
+  // accumulators
+  char* s_q = s_mem;
   {
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + row * D);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = wave; j < NJ; j += NW)
       *reinterpret_cast<u32x4_t*>(s_q + l16 * QROWB + (lg + 4 * j) * 16) = qp[4 * j + lg];
   }
   const char* q_lds = s_q + l16 * QROWB + lg * 16;
+  char* tile = s_mem + Q_BYTES + wave * TILE_BYTES;  // this wave's V tile
   const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
   // (native 4 x u32 vectors: arrays of them stay in registers)
   const u32x4_t* kbase = reinterpret_cast<const u32x4_t*>(a.k) + row0 * (D / 8);
@@ -107,6 +126,7 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
   for (int i = 0; i < NDB; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f;
 
+  // tiles of 16 keys; wave w takes tiles w, w + NW, ... of the split (a fixed order)
   const int nt = (k_end - k_begin + 15) / 16;
   u32x4_t kr[NJ], vr[KV_SHARED ? 1 : NJ];
   // key k_begin + 16 t + l16 of the tile (past the end: re-read the last valid key)
@@ -126,11 +146,19 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
       for (int j = 0; j < NJ; ++j) vr[j] = p[4 * j];
     }
   };
-  load_k(0);
-  load_v(0);
+  // LDS exchange inside one wave (its own tile): the hardware keeps a wave's LDS
+  // accesses in order; the fences keep the compiler from reordering them
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  const int t0 = wave < nt ? wave : nt - 1;  // a wave without tiles loads a valid one
+  load_k(t0);
+  load_v(t0);
   __syncthreads();  // the Q rows are in LDS
 
-  for (int t = 0; t < nt; ++t) {
+  for (int t = wave; t < nt; t += NW) {
     const int k0 = k_begin + 16 * t;
     // S^T for the tile
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -138,9 +166,6 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
     for (int j = 0; j < NJ; ++j)
       s = mfma_k32(kr[j], *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
     // V rows of the tile to LDS (key l16, d = 8 lg + 32 j), then refill the registers
-    // one LDS tile, rewritten each step: the barrier closing the previous step keeps the
-    // compiler from moving these writes above that step's transposed reads
-    char* tile = s_v;
     {
       char* w = tile + l16 * ROWB + lg * 16;
 #pragma unroll
@@ -151,9 +176,9 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
           *reinterpret_cast<u32x4_t*>(w + j * 64) = vr[j];
       }
     }
-    load_k(t + 1 < nt ? t + 1 : t);
-    load_v(t + 1 < nt ? t + 1 : t);
-    __syncthreads();  // one wave: orders the LDS writes before the transposed reads
+    load_k(t + NW < nt ? t + NW : t);
+    load_v(t + NW < nt ? t + NW : t);
+    wave_sync();  // the tile's LDS writes before its transposed reads
 
     // softmax: lane holds row l16, keys k0 + 4 lg + i
     float x[4];
@@ -194,30 +219,57 @@ __global__ void __launch_bounds__(64) decode_rows16_kernel(DecodeArgs a) {
       acc[db] = mfma_k16(va, ph, acc[db]);
       acc[db] = mfma_k16(va, pl, acc[db]);
     }
-    __syncthreads();  // the tile's transposed reads stay before the next tile's writes
+    wave_sync();  // the tile's transposed reads stay before the next tile's writes
   }
 
+  // Merge the waves: each leaves (m, l) per row and acc (row l16, d = 16 db + 4 lg + i)
+  // in LDS (over the Q rows and V tiles, no longer read), then every thread combines
+  // float4 runs of the 16 rows: o = sum_w 2^(m_w - M) acc_w, L = sum_w 2^(m_w - M) l_w.
   l = rows_sum(l);
-  if (!row_on) return;
-  if (S == 1) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    float* o = a.out + row * D + 4 * lg;
+  __syncthreads();
+  float* s_acc = reinterpret_cast<float*>(s_mem);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db] * inv;
-  } else {
-    const size_t ps = row * S + split;
-    float* o = a.part_acc + ps * D + 4 * lg;
+  for (int db = 0; db < NDB; ++db)
+    *reinterpret_cast<floatx4_t*>(s_acc + (wave * 16 + l16) * D + 16 * db + 4 * lg) = acc[db];
+  if (lg == 0) {
+    s_ml[wave][l16][0] = m;
+    s_ml[wave][l16][1] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * (D / 4); idx += NW * 64) {
+    const int rr = idx / (D / 4), d = 4 * (idx % (D / 4));
+    if (row_token(rr) >= a.T) continue;
+    float M = -INFINITY;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db];
-    if (lg == 0) {
-      a.part_ml[ps * 2 + 0] = m;
-      a.part_ml[ps * 2 + 1] = l;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][rr][0]);
+    float L = 0.0f;
+    floatx4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_ml[w][rr][0];
+      const float f = mw == -INFINITY ? 0.0f : exp2_fast(mw - M);
+      L += s_ml[w][rr][1] * f;
+      o += *reinterpret_cast<const floatx4_t*>(s_acc + (w * 16 + rr) * D + d) * f;
+    }
+    const size_t bh = row_index(rr);
+    if (S == 1) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      *reinterpret_cast<floatx4_t*>(a.out + bh * D + d) = o * inv;
+    } else {
+      const size_t ps = bh * S + split;
+      *reinterpret_cast<floatx4_t*>(a.part_acc + ps * D + d) = o;
+      if (d == 0) {
+        a.part_ml[ps * 2 + 0] = M;
+        a.part_ml[ps * 2 + 1] = L;
+      }
     }
   }
 }
 
 
 }  // namespace
+
+int decode_rows16_waves(int D) { return D == 512 ? rows16_waves<512>() : rows16_waves<256>(); }
 
 bool decode_rows16_supported(int D, bool k_eq_v) {
   return D == 128 || D == 256 || (D == 512 && k_eq_v);
@@ -226,7 +278,7 @@ bool decode_rows16_supported(int D, bool k_eq_v) {
 hipError_t decode_rows16_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
   const long long blocks = (long long)a.B * a.Hkv * a.n_chunks * a.n_split;
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(64);
+  const dim3 grid((unsigned)blocks), block(64 * decode_rows16_waves(a.D));
   if (a.D == 128) {
     if (k_eq_v) hipLaunchKernelGGL((decode_rows16_kernel<128, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((decode_rows16_kernel<128, false>), grid, block, 0, stream, a);

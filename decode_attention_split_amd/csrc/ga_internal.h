@@ -149,6 +149,7 @@ size_t decode_mfma_workspace_bytes(int B, int Hkv);  // partials + plan
 // Matrix-core path for 16 query rows per unit (several tokens x heads of one KV head):
 // bf16 caches, head_dim 128 / 256, or 512 with K = V; partials as the vector path's.
 hipError_t decode_rows16_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream);
+int decode_rows16_waves(int D);  // waves per work-group of the multi-token matrix-core kernel
 bool decode_rows16_supported(int D, bool k_eq_v);
 
 hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream);

@@ -222,9 +222,10 @@ def test_multi_workspace_closed_form():
     Vector kernel: 4 tokens per unit (2 heads x 4 tokens = 8 rows), 2 chunks; a unit's keys
     are at most w + 4 - 1 = 1027; 64 units want 4 splits of ceil(1027 / 4) = 257 -> 320
     keys, S = ceil(1027 / 320) = 4.  Matrix cores: 8 tokens per unit (16 rows), 1 chunk,
-    at most w + 8 - 1 = 1031 keys; 32 units want 64 one-wave splits of ceil(1031 / 64) =
-    17 -> 64 keys, S = 17.  Partials: B * T * Hq * S * (D + 2) floats; the automatic choice
-    sizes for the larger."""
+    at most w + 8 - 1 = 1031 keys; 32 units want 2048 / 4 = 512 four-wave splits, 16 each,
+    of ceil(1031 / 16) = 65 -> 80 keys (whole 16-key tiles), S = ceil(1031 / 80) = 13.
+    Partials: B * T * Hq * S * (D + 2) floats; the automatic choice sizes for the
+    larger."""
     lib = _lib.load()
     s = shape(B=4, cap=1031, max_ctx=8192)
     valu = api.make_opts(impl=api.IMPL_VALU)
@@ -232,7 +233,7 @@ def test_multi_workspace_closed_form():
     n_v = lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, ctypes.byref(valu))
     n_m = lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, ctypes.byref(mfma))
     assert n_v == 4 * 8 * 16 * 4 * (256 + 2) * 4
-    assert n_m == 4 * 8 * 16 * 17 * (256 + 2) * 4
+    assert n_m == 4 * 8 * 16 * 13 * (256 + 2) * 4
     assert lib.ga_decode_multi_workspace_bytes(ctypes.byref(s), 8, 1024, None) == max(n_v, n_m)
     # T = 1 is the single-token plan
     o = api.make_opts()
