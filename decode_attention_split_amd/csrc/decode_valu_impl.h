@@ -150,8 +150,56 @@ __global__ void __launch_bounds__(NW_ * 64)
     }
   }
 
-  const RowRange r = unit_range(a, b, chunk);
+  const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
+  const void* kmem = FP8 ? (const void*)a.k8 : (const void*)a.k;
+  const void* vmem = FP8 ? (const void*)(KV_SHARED ? a.k8 : a.v8)
+                         : (const void*)(KV_SHARED ? a.k : a.v);
+  const Chunk* kbase = reinterpret_cast<const Chunk*>(kmem) + row0 * ROWC;
+  const Chunk* vbase = reinterpret_cast<const Chunk*>(vmem) + row0 * ROWC;
+  const float* kscale = FP8 ? a.k_scale + row0 : nullptr;
+  const float* vscale = FP8 ? (KV_SHARED ? a.k_scale : a.v_scale) + row0 : nullptr;
+  // fused append (bf16 caches): the appended token's rows, read in place of its slot
+  const size_t unit = (size_t)b * a.Hkv + g;
+  const Chunk* knew =
+      !FP8 && a.new_pos ? reinterpret_cast<const Chunk*>(a.k_new) + unit * ROW16 : kbase;
+  const Chunk* vnew =
+      !FP8 && a.new_pos
+          ? reinterpret_cast<const Chunk*>(KV_SHARED ? a.k_new : a.v_new) + unit * ROW16
+          : vbase;
+
+  // sc[0] / sc[1]: the key's K / V row scales (fp8 caches only).  The L lanes of a group
+  // read L * sizeof(Chunk) >= 128 contiguous bytes per load, whole lines, so the cache
+  // rows are loaded non-temporally (measured ~10% faster than cached loads here).
+  static_assert(L * (int)sizeof(Chunk) >= 128, "a lane group reads whole 128-byte lines");
+  auto load_rows = [&](Chunk(&kr)[NCH], Chunk(&vr)[NCH], float(&sc)[2], int slot, bool fresh) {
+    const Chunk* kp = fresh ? knew : kbase + (size_t)slot * ROWC;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kr[c] = stream_load(kp + c * L + j);
+    if constexpr (!KV_SHARED) {
+      const Chunk* vp = fresh ? vnew : vbase + (size_t)slot * ROWC;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) vr[c] = stream_load(vp + c * L + j);
+    }
+    if constexpr (FP8) {
+      sc[0] = kscale[slot];
+      sc[1] = KV_SHARED ? sc[0] : vscale[slot];
+    }
+  };
+
+  // Single-token decode visits the keys of a range that starts at slot 0, or fills the
+  // whole ring, in slot order: key i is slot i (any order of the same keys gives the
+  // same result up to rounding).  The rows of a wave's first step (wave w takes step w)
+  // then do not depend on the context length and are requested before it arrives; a lane
+  // whose guess turns out wrong (another range, a key past the end, the appended slot)
+  // reloads once the range is known.
   const int k_begin = split * a.split_keys;
+  const int i_first = k_begin + wave * GPW + grp;
+  Chunk ka[NCH], va[NCH];
+  float ca[2] = {1.0f, 1.0f};
+  if constexpr (!MULTI)
+    load_rows(ka, va, ca, min(i_first, min(a.cap, k_begin + a.split_keys) - 1), false);
+
+  const RowRange r = unit_range(a, b, chunk);
   const int k_end = min(r.n, k_begin + a.split_keys);
   if (k_begin >= k_end) {
     if (S == 1) {  // the only split of an empty unit: the output is 0
@@ -163,6 +211,10 @@ __global__ void __launch_bounds__(NW_ * 64)
   }
   __shared__ int s_next;  // handed-out wave-steps past the first NW
   if (threadIdx.x == 0) s_next = 0;
+  // key i of the range sits in slot key_slot(slot_base, i): position order, or slot order
+  // (slot_base 0) for single-token decode over a full ring; several tokens keep position
+  // order (their masks are by position)
+  const int slot_base = (!MULTI && r.n == a.cap) ? 0 : r.slot_lo;
 
   // MULTI: each row's own valid positions [row_lo, row_hi] (empty: lo > hi).
   int row_lo[MULTI ? G : 1], row_hi[MULTI ? G : 1];
@@ -182,22 +234,6 @@ __global__ void __launch_bounds__(NW_ * 64)
     }
   }
 
-  const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
-  const void* kmem = FP8 ? (const void*)a.k8 : (const void*)a.k;
-  const void* vmem = FP8 ? (const void*)(KV_SHARED ? a.k8 : a.v8)
-                         : (const void*)(KV_SHARED ? a.k : a.v);
-  const Chunk* kbase = reinterpret_cast<const Chunk*>(kmem) + row0 * ROWC;
-  const Chunk* vbase = reinterpret_cast<const Chunk*>(vmem) + row0 * ROWC;
-  const float* kscale = FP8 ? a.k_scale + row0 : nullptr;
-  const float* vscale = FP8 ? (KV_SHARED ? a.k_scale : a.v_scale) + row0 : nullptr;
-  // fused append (bf16 caches): the appended token's rows, read in place of its slot
-  const size_t unit = (size_t)b * a.Hkv + g;
-  const Chunk* knew =
-      !FP8 && a.new_pos ? reinterpret_cast<const Chunk*>(a.k_new) + unit * ROW16 : kbase;
-  const Chunk* vnew =
-      !FP8 && a.new_pos
-          ? reinterpret_cast<const Chunk*>(KV_SHARED ? a.k_new : a.v_new) + unit * ROW16
-          : vbase;
 
   float acc[G][DPL];
   float m[G], l[G];
@@ -225,27 +261,11 @@ __global__ void __launch_bounds__(NW_ * 64)
     return NW + __builtin_amdgcn_readfirstlane(s);
   };
 
-  // sc[0] / sc[1]: the key's K / V row scales (fp8 caches only).  The L lanes of a group
-  // read L * sizeof(Chunk) >= 128 contiguous bytes per load, whole lines, so the cache
-  // rows are loaded non-temporally (measured ~10% faster than cached loads here).
-  static_assert(L * (int)sizeof(Chunk) >= 128, "a lane group reads whole 128-byte lines");
   auto load = [&](Chunk(&kr)[NCH], Chunk(&vr)[NCH], float(&sc)[2], int step) {
     const int i = k_begin + step * GPW + grp;
     const int ic = i < k_end ? i : k_end - 1;  // past the end: re-read a valid row
-    const int slot = key_slot(r, ic, a.cap);
-    const bool fresh = !FP8 && slot == new_slot;
-    const Chunk* kp = fresh ? knew : kbase + (size_t)slot * ROWC;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) kr[c] = stream_load(kp + c * L + j);
-    if constexpr (!KV_SHARED) {
-      const Chunk* vp = fresh ? vnew : vbase + (size_t)slot * ROWC;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) vr[c] = stream_load(vp + c * L + j);
-    }
-    if constexpr (FP8) {
-      sc[0] = kscale[slot];
-      sc[1] = KV_SHARED ? sc[0] : vscale[slot];
-    }
+    const int slot = key_slot(slot_base, ic, a.cap);
+    load_rows(kr, vr, sc, slot, !FP8 && slot == new_slot);
   };
 
   // e4m3 codes of one chunk -> float32 values (v_cvt_pk_f32_fp8, exact)
@@ -353,10 +373,17 @@ __global__ void __launch_bounds__(NW_ * 64)
   // header carries the same outstanding loads (buffer a only) and the compiler keeps
   // partial vmcnt waits instead of draining the prefetch.  Grabs are increasing per wave,
   // so sa < sb < n_wsteps inside the loop.
-  Chunk ka[NCH], va[NCH], kb[NCH], vb[NCH];
-  float ca[2] = {1.0f, 1.0f}, cb[2] = {1.0f, 1.0f};
-  int sa = grab();
-  load(ka, va, ca, sa);
+  Chunk kb[NCH], vb[NCH];
+  float cb[2] = {1.0f, 1.0f};
+  int sa = grab();  // = wave
+  if constexpr (MULTI) {
+    load(ka, va, ca, sa);
+  } else {
+    // the guessed rows stand unless the range is not in slot order, the key is past the
+    // end (the guess may be a slot never written), or the slot is the appended one
+    const int slot = key_slot(slot_base, min(i_first, k_end - 1), a.cap);
+    if (slot_base != 0 || i_first >= k_end || (!FP8 && slot == new_slot)) load(ka, va, ca, sa);
+  }
   __syncthreads();  // s_next is set before any wave asks for a handed-out step
   int sb = grab();
   while (sb < n_wsteps) {

@@ -221,16 +221,17 @@ def test_k_eq_v_null_equals_same_values_passed_twice():
     assert torch.equal(a, b)
 
 
-def test_ring_equals_linear_bitwise():
-    """The same history in a ring and in a linear cache gives the same output bit for
-    bit: keys are visited in position order in both layouts."""
-    B, Hkv, D, W, total = 3, 2, 256, 128, 700
+def test_ring_equals_linear():
+    """The same history in a ring and in a linear cache gives the same output: the same
+    keys, summed in slot order on a full ring and in position order on the linear cache,
+    so the two agree to within float32 rounding (bit for bit where the ring is not full)."""
+    B, Hkv, D, W, total = 4, 2, 256, 128, 700
     gen = synth.generator(83)
     hist_k = synth.bits(synth.normal_bf16(gen, (B, Hkv, total, D)))
     hist_v = synth.bits(synth.normal_bf16(gen, (B, Hkv, total, D)))
     ring_k = np.full((B, Hkv, W, D), synth.BF16_NAN, np.uint16)
     ring_v = ring_k.copy()
-    ctx = np.array([700, 555, 129], np.int32)
+    ctx = np.array([700, 555, 129, 100], np.int32)
     for b in range(B):
         for p in range(max(0, ctx[b] - W), ctx[b]):
             ring_k[b, :, p % W] = hist_k[b, :, p]
@@ -244,7 +245,9 @@ def test_ring_equals_linear_bitwise():
                    W, 0.0, 0.0625, api.LINEAR, deterministic=True)
     torch.cuda.synchronize()
     assert torch.isfinite(a).all()
-    assert torch.equal(a, b)
+    max_abs, rel = errors(a, b.double().cpu().numpy())
+    assert max_abs < 2e-5 and rel < 2e-5, (max_abs, rel)
+    assert torch.equal(a[3], b[3])  # ctx 100 < W: both layouts in position order
 
 
 @pytest.mark.parametrize("geom", ["sliding", "global_valu"])
