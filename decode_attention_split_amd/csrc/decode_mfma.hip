@@ -19,20 +19,22 @@
 // others leave one partial per work-group (slot = work-group index) for
 // merge_units_kernel (log-sum-exp).
 //
-// Per work-group of 4 waves, 16-key tiles; wave w owns head_dim slice [128 w, 128 w + 128):
-//   partial S^T[16 keys][16 heads] = K[16][slice] . Q^T[slice][16] with
+// Per work-group of 4 waves, 16-key tiles taken two per step; wave w owns head_dim slice
+// [128 w, 128 w + 128):
+//   partial S^T[16 keys][16 heads] = K[16][slice] . Q^T[slice][16] per tile with
 //     v_mfma_f32_16x16x32_bf16 (4 per tile): lane l loads key (l % 16), d = 128 w + 32 j +
-//     8 (l / 16) + 0..7 straight into the A operand (16-byte loads, 4 tiles in flight),
-//     Q^T is held in registers in the same d order;
-//   the 4 partials are summed through LDS (one barrier per tile), in the same order in
-//     every wave, so every wave holds the identical S^T and the identical softmax state;
+//     8 (l / 16) + 0..7 straight into the A operand (16-byte loads; 4 tiles in flight, 8
+//     for fp8 codes), Q^T is held in registers in the same d order;
+//   the 4 partials are summed through LDS (one barrier per step of 32 keys), in the same
+//     order in every wave, so every wave holds the identical S^T and softmax state;
 //   the wave's K = V slice goes once to its own LDS rows (288 B stride) and
-//   O^T[slice][16] += V^T[slice][16 keys] . P^T[16 keys][16 heads] with
-//     v_mfma_f32_16x16x16_bf16: the A operand comes from ds_read_b64_tr_b16 (lanes
-//     4e..4e+3 of a 16-lane block read 16 consecutive d of key e; lane i then holds the
-//     4 keys at column d0 + i), the B operand is P exactly as the S^T MFMA left it (lane
-//     l: head l % 16, keys 4 (l / 16) + 0..3), split into bf16 hi + lo parts so the
-//     probabilities keep ~16 mantissa bits (the bf16 cache data is exact).
+//   O^T[slice][16] += V^T[slice][32 keys] . P^T[32 keys][16 heads] with one
+//     v_mfma_f32_16x16x32_bf16 per 16-wide d block: the A operand comes from two
+//     ds_read_b64_tr_b16 (one per tile; lanes 4e..4e+3 of a 16-lane block read 16
+//     consecutive d of key e, lane i then holds the 4 keys at column d0 + i), the B
+//     operand is P exactly as the S^T products left it (lane l: head l % 16, keys
+//     4 (l / 16) + 0..3 of each tile), split into bf16 hi + lo parts so the probabilities
+//     keep ~16 mantissa bits (the bf16 cache data is exact).
 // Each wave writes its own slice of the output or partial: no end-of-segment merge.
 // The K = V row is read from HBM once and used for both products.  Softmax state per
 // head is fp32 in log2 units with lazy rescaling (max raised only past +8).
