@@ -120,11 +120,10 @@ __global__ void __launch_bounds__(NW_ * 64)
   const int new_slot = appended_slot(a, b);
   AppendRow app;
   app.load(a, b, g, new_slot, threadIdx.x, split == 0);
-  // Query rows of this unit in this lane's element order: packed bf16 pairs for the
-  // bf16 cache (dot2 products), float32 values for the fp8 cache.  Loaded before the
+  // Query rows of this unit in this lane's element order, as packed bf16 pairs for the
+  // dot2 products (fp8 keys are widened exactly to bf16 pairs first).  Loaded before the
   // context length is known (they do not depend on it), so the two latencies overlap.
-  uint32_t qr[G][FP8 ? 1 : DPL / 2];
-  float qf[G][FP8 ? DPL : 1];
+  uint32_t qr[G][DPL / 2];  // element pairs (e, e + 1), e even, in lane order
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + row_index(hh) * D);
@@ -133,19 +132,10 @@ __global__ void __launch_bounds__(NW_ * 64)
 #pragma unroll
       for (int h8 = 0; h8 < EPC / 8; ++h8) {
         const uint4 v = qp[(EPC / 8) * (c * L + j) + h8];
-        if constexpr (FP8) {
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            qf[hh][EPC * c + 8 * h8 + 2 * i] = bf16_lo(w4[i]);
-            qf[hh][EPC * c + 8 * h8 + 2 * i + 1] = bf16_hi(w4[i]);
-          }
-        } else {
-          qr[hh][4 * c + 0] = v.x;
-          qr[hh][4 * c + 1] = v.y;
-          qr[hh][4 * c + 2] = v.z;
-          qr[hh][4 * c + 3] = v.w;
-        }
+        qr[hh][EPC * c / 2 + 4 * h8 + 0] = v.x;
+        qr[hh][EPC * c / 2 + 4 * h8 + 1] = v.y;
+        qr[hh][EPC * c / 2 + 4 * h8 + 2] = v.z;
+        qr[hh][EPC * c / 2 + 4 * h8 + 3] = v.w;
       }
     }
   }
@@ -268,7 +258,19 @@ __global__ void __launch_bounds__(NW_ * 64)
     load_rows(kr, vr, sc, slot, !FP8 && slot == new_slot);
   };
 
-  // e4m3 codes of one chunk -> float32 values (v_cvt_pk_f32_fp8, exact)
+  // e4m3 codes of one chunk -> bf16 pairs (v_cvt_scalef32_pk_bf16_fp8 with scale 1,
+  // exact: checked bit for bit on all 256 codes), for the dot2 products with q
+  auto widen_fp8_bf16 = [&](const Chunk& ch, uint32_t* out) {
+#pragma unroll
+    for (int w = 0; w < EPC / 4; ++w) {
+      const int word = (int)chunk_word(ch, w);
+      out[2 * w + 0] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+      out[2 * w + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
+    }
+  };
+  // e4m3 codes of one chunk -> float32 values (v_cvt_pk_f32_fp8, exact), for P.V
   auto widen_fp8 = [&](const Chunk& ch, float* out) {
     typedef float f2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -290,16 +292,16 @@ __global__ void __launch_bounds__(NW_ * 64)
     const int pos = r.lo + i;  // absolute position of the key (MULTI masks)
     float s[G];
     if constexpr (FP8) {
-      float kf[DPL];
+      uint32_t kb[DPL / 2];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) widen_fp8(kr[c], &kf[EPC * c]);
+      for (int c = 0; c < NCH; ++c) widen_fp8_bf16(kr[c], &kb[EPC * c / 2]);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
-        for (int e = 0; e < DPL; e += 2) {
-          d0 = fmaf(qf[hh][e], kf[e], d0);
-          d1 = fmaf(qf[hh][e + 1], kf[e + 1], d1);
+        for (int e2 = 0; e2 < DPL / 2; e2 += 2) {
+          d0 = dot2_bf16(qr[hh][e2], kb[e2], d0);
+          d1 = dot2_bf16(qr[hh][e2 + 1], kb[e2 + 1], d1);
         }
         s[hh] = group_sum<L>(d0 + d1) * sc[0];
       }
