@@ -55,7 +55,8 @@ def parse_args():
 # Single-layer workloads measured with --workload (the default line is the 48-layer step).
 SINGLE_LAYER = {"hd128_sliding": "HD128_SLIDING", "g4_12b_sliding": "G4_12B_SLIDING",
                 "g4_12b_global": "G4_12B_GLOBAL", "spec_decode_sliding": "SPEC_DECODE_SLIDING",
-                "fp8_sliding": "FP8_SLIDING", "fp8_global": "FP8_GLOBAL"}
+                "fp8_sliding": "FP8_SLIDING", "fp8_global": "FP8_GLOBAL",
+                "fp8_spec_decode_sliding": "FP8_SPEC_DECODE_SLIDING"}
 
 
 def log(msg):
@@ -369,10 +370,10 @@ def bench_single_layer(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = getattr(wl, SINGLE_LAYER[args.workload])
-    if w.tokens > 1:
-        return bench_multi_token(args, w)
     if w.kv_dtype == "fp8":
         return bench_fp8(args, w)
+    if w.tokens > 1:
+        return bench_multi_token(args, w)
     g = w.layers[0]
     B = w.batch
     gen_cpu = synth.generator(w.seed)
@@ -583,24 +584,29 @@ def bench_multi_token(args, w):
     print(json.dumps(result), flush=True)
 
 
-def fp8_layer_bytes(g, B, ctx):
-    """Algorithmic bytes of one fp8 layer step: per valid key D codes plus a float32 scale
-    (K, and V unless K = V), q, out, the int inputs, and the quantizing append (read the
-    bf16 row, write its codes and scale)."""
+def fp8_layer_bytes(g, B, ctx, T=1):
+    """Algorithmic bytes of one fp8 layer step with T tokens per row (at ctx - T ..
+    ctx - 1): every key any token attends to (the union of the T windows) read once, D
+    codes plus a float32 scale per key (K, and V unless K = V), q, out, the int inputs,
+    and the quantizing append of T rows (read the bf16 row, write its codes and scale)."""
     import numpy as np
-    n = valid_keys(g, ctx).astype("int64")
+    if T == 1:
+        n = valid_keys(g, ctx).astype("int64")
+    else:
+        n = (np.minimum(ctx, g.window + T - 1) if g.window > 0 else ctx.copy()).astype("int64")
     tensors = 1 if g.k_eq_v else 2
     kv = int(n.sum()) * g.num_kv_heads * (g.head_dim + 4) * tensors
-    q = B * g.num_q_heads * g.head_dim * 2
-    out = B * g.num_q_heads * g.head_dim * 4
+    q = B * T * g.num_q_heads * g.head_dim * 2
+    out = B * T * g.num_q_heads * g.head_dim * 4
     ints = 2 * B * 4
-    append = B * g.num_kv_heads * (g.head_dim * 2 + g.head_dim + 4) * tensors + B * 4
+    append = B * T * g.num_kv_heads * (g.head_dim * 2 + g.head_dim + 4) * tensors + B * 4
     return {"kv": kv, "decode": kv + q + out + ints, "append": append}
 
 
 def bench_fp8(args, w):
-    """One layer over fp8 caches: quantizing append of the current token, then decode,
-    rotating over enough cache copies (>= 1 GiB) to keep the Infinity Cache out of it."""
+    """One layer over fp8 caches: quantizing append of the T current tokens (T = 1, or the
+    tokens verified by speculative decoding), then decode, rotating over enough cache
+    copies (>= 1 GiB) to keep the Infinity Cache out of it."""
     import numpy as np
     import torch
     from decode_attention_split_amd import api, synth
@@ -608,7 +614,7 @@ def bench_fp8(args, w):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     g = w.layers[0]
-    B = w.batch
+    B, T = w.batch, w.tokens
     ctx = synth.uniform_int(synth.generator(w.seed), B, w.ctx_lo, w.ctx_hi).numpy() \
         .astype(np.int32)
     gdev = synth.generator(w.seed, device=dev)
@@ -629,15 +635,17 @@ def bench_fp8(args, w):
             kn = synth.normal_bf16(gdev, (B, n, g.num_kv_heads, g.head_dim), device=dev)
             vn = None if g.k_eq_v else synth.normal_bf16(gdev, kn.shape, device=dev)
             api.kv_append_fp8(kc, ks, vc, vs, kn, vn, ctx_t - W + part, g.kind)
-        q = synth.normal_bf16(gdev, (B, g.num_q_heads, g.head_dim), device=dev)
+        qshape = (B, g.num_q_heads, g.head_dim) if T == 1 else (B, T, g.num_q_heads, g.head_dim)
+        q = synth.normal_bf16(gdev, qshape, device=dev)
         sets.append((q, kc, ks, vc, vs))
-    k_new = synth.normal_bf16(gdev, (B, g.num_kv_heads, g.head_dim), device=dev)
+    nshape = (B, g.num_kv_heads, g.head_dim) if T == 1 else (B, T, g.num_kv_heads, g.head_dim)
+    k_new = synth.normal_bf16(gdev, nshape, device=dev)
     v_new = None if g.k_eq_v else synth.normal_bf16(gdev, k_new.shape, device=dev)
-    out = torch.empty((B, g.num_q_heads, g.head_dim), dtype=torch.float32, device=dev)
-    pos_t = ctx_t - 1
+    out = torch.empty(qshape, dtype=torch.float32, device=dev)
+    pos_t = ctx_t - T
     max_ctx = w.ctx_hi if g.kind == api.RING else g.capacity
     shape = api.make_shape(B, g.num_q_heads, g.num_kv_heads, g.head_dim, W, g.kind, max_ctx)
-    ws = torch.empty((max(1, api.workspace_bytes_fp8(shape, 1, g.window)),), dtype=torch.uint8,
+    ws = torch.empty((max(1, api.workspace_bytes_fp8(shape, T, g.window)),), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream()
 
@@ -658,7 +666,7 @@ def bench_fp8(args, w):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    lb = fp8_layer_bytes(g, B, ctx)
+    lb = fp8_layer_bytes(g, B, ctx, T)
     nbytes = lb["decode"] + lb["append"]
     gbps = nbytes / (ms * 1e-3) / 1e9
     log(f"{w.name}: {ms * 1e3:.2f} us per step (append + decode), {gbps:.1f} GB/s")
@@ -676,10 +684,11 @@ def bench_fp8(args, w):
         "dtype": "fp8e4m3 cache, bf16 q, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name + " (one layer: quantizing append + decode)",
-                   "batch": B, "layers": 1, "ctx_mean": float(ctx.mean()), "accumulate": "fp32",
-                   "algorithmic_bytes_per_step": int(nbytes), "cache_copies": copies},
+                   "batch": B, "tokens": T, "layers": 1, "ctx_mean": float(ctx.mean()),
+                   "accumulate": "fp32", "algorithmic_bytes_per_step": int(nbytes),
+                   "cache_copies": copies},
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
-        "layer_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "layer_tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "roofline": {"kernel": "fp8 quantizing append + decode, per step", "bound": "hbm",
                      "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -698,10 +707,10 @@ def bench_fp8(args, w):
             sl = slice(rows, min(B, rows + 4))
             t0 = time.perf_counter()
             oracle.decode_fp8_multi(qb[sl], kcn[sl], ksn[sl], None if vcn is None else vcn[sl],
-                                    None if vsn is None else vsn[sl], ctx[sl], ctx[sl] - 1,
+                                    None if vsn is None else vsn[sl], ctx[sl], ctx[sl] - T,
                                     g.window, g.softcap, g.q_scale, g.kind, nthreads=threads)
             spent += time.perf_counter() - t0
-            done += fp8_layer_bytes(g, sl.stop - sl.start, ctx[sl])["decode"]
+            done += fp8_layer_bytes(g, sl.stop - sl.start, ctx[sl], T)["decode"]
             rows = sl.stop
         result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
                                   "cores": int(min(threads, rows * g.num_q_heads)),

@@ -209,7 +209,7 @@ void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
 // k_eq_v: 1 / 0 when known (a decode call), -1 for a workspace query, which then sizes
 // for whichever implementation AUTO may pick.
 int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, int k_eq_v,
-                  Plan* p, int T = 1, bool fp8 = false) {
+                  Plan* p, int T = 1) {
   int impl = GA_IMPL_AUTO, ts = 0;
   if (o) {
     for (int i = 0; i < 5; ++i)
@@ -219,10 +219,6 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
     ts = o->split_keys;
     if (impl < GA_IMPL_AUTO || impl > GA_IMPL_MFMA) return GA_ERR_OPTS;
     if (ts != 0 && (ts < 64 || ts > kMaxSplitKeys || ts % 64 != 0)) return GA_ERR_OPTS;
-  }
-  if (fp8 && T > 1) {  // fp8 caches with several tokens: the vector kernel
-    if (impl == GA_IMPL_MFMA) return GA_ERR_OPTS;
-    return valu_plan(s, window, ts, T, p);
   }
   if (T > 1) {
     // several query tokens (per-row masks): 16 query rows per unit on the matrix cores
@@ -317,7 +313,7 @@ size_t ga_decode_fp8_workspace_bytes(const ga_shape* shape, int32_t num_tokens, 
                                      const ga_decode_opts* opts) {
   if (check_shape(shape, window, num_tokens) != GA_OK) return SIZE_MAX;
   Plan p;
-  if (make_plan(shape, window, opts, -1, &p, num_tokens, true) != GA_OK) return SIZE_MAX;
+  if (make_plan(shape, window, opts, -1, &p, num_tokens) != GA_OK) return SIZE_MAX;
   return p.ws_bytes;
 }
 
@@ -366,7 +362,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   if (!std::isfinite(scale)) return GA_ERR_SCALE;
   const bool k_eq_v = v_cache == nullptr || v_cache == k_cache;
   Plan p;
-  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p, T, f8 != nullptr);
+  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p, T);
   if (st != GA_OK) return st;
   const int D = shape->head_dim;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return GA_ERR_WORKSPACE;

@@ -42,7 +42,7 @@ constexpr float kRescaleLog2R16 = 8.0f;
 template <int D>
 constexpr int rows16_waves() { return D == 512 ? 2 : 4; }
 
-template <int D, bool KV_SHARED>
+template <int D, bool KV_SHARED, bool FP8>
 __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(DecodeArgs a) {
   constexpr int NW = rows16_waves<D>();  // waves per work-group, one split between them
   constexpr int NJ = D / 32;             // 16-byte K chunks per lane = QK products per tile
@@ -56,6 +56,7 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   __shared__ __attribute__((aligned(16))) char s_mem[LOOP_BYTES > ACC_BYTES ? LOOP_BYTES
                                                                             : ACC_BYTES];
   __shared__ float s_ml[NW][16][2];
+  __shared__ __attribute__((aligned(16))) float s_scl[NW][2][16];  // fp8: K, V row scales
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -118,8 +119,19 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   char* tile = s_mem + Q_BYTES + wave * TILE_BYTES;  // this wave's V tile
   const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
   // (native 4 x u32 vectors: arrays of them stay in registers)
-  const u32x4_t* kbase = reinterpret_cast<const u32x4_t*>(a.k) + row0 * (D / 8);
-  const u32x4_t* vbase = reinterpret_cast<const u32x4_t*>(KV_SHARED ? a.k : a.v) + row0 * (D / 8);
+  // Cache rows in 16-byte chunks: bf16 rows hold D / 8, fp8 rows D / 16 (16 codes each).
+  // A lane's chunks of a row: bf16 d = 32 j + 8 lg + 0..7 (product j); fp8 codes
+  // d = 64 jj + 16 lg + 0..15, which serve products 2 jj and 2 jj + 1 (Q^T is read from
+  // LDS in the same order).
+  constexpr int ROW16 = FP8 ? D / 16 : D / 8;
+  constexpr int NL = FP8 ? NJ / 2 : NJ;  // 16-byte loads per lane per row
+  const void* kmem = FP8 ? (const void*)a.k8 : (const void*)a.k;
+  const void* vmem = FP8 ? (const void*)(KV_SHARED ? a.k8 : a.v8)
+                         : (const void*)(KV_SHARED ? a.k : a.v);
+  const u32x4_t* kbase = reinterpret_cast<const u32x4_t*>(kmem) + row0 * ROW16;
+  const u32x4_t* vbase = reinterpret_cast<const u32x4_t*>(vmem) + row0 * ROW16;
+  const float* kscale = FP8 ? a.k_scale + row0 : nullptr;
+  const float* vscale = FP8 ? (KV_SHARED ? a.k_scale : a.v_scale) + row0 : nullptr;
 
   floatx4_t acc[NDB];
 #pragma unroll
@@ -128,22 +140,28 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
 
   // tiles of 16 keys; wave w takes tiles w, w + NW, ... of the split (a fixed order)
   const int nt = (k_end - k_begin + 15) / 16;
-  u32x4_t kr[NJ], vr[KV_SHARED ? 1 : NJ];
+  u32x4_t kr[NL], vr[KV_SHARED ? 1 : NL];
+  float ksc = 1.0f, vsc = 1.0f;  // fp8: the row scales of this lane's key (l16)
   // key k_begin + 16 t + l16 of the tile (past the end: re-read the last valid key)
-  auto key_row = [&](int t) {
+  auto key_slot_of = [&](int t) {
     const int i = k_begin + 16 * t + l16;
-    return (size_t)key_slot(r, i < k_end ? i : k_end - 1, a.cap) * (D / 8);
+    return key_slot(r, i < k_end ? i : k_end - 1, a.cap);
   };
   auto load_k = [&](int t) {
-    const u32x4_t* p = kbase + key_row(t) + lg;
+    const int slot = key_slot_of(t);
+    const u32x4_t* p = kbase + (size_t)slot * ROW16 + lg;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) kr[j] = p[4 * j];
+    for (int j = 0; j < NL; ++j) kr[j] = p[4 * j];
+    if constexpr (FP8) {
+      ksc = kscale[slot];
+      vsc = KV_SHARED ? ksc : vscale[slot];
+    }
   };
   auto load_v = [&](int t) {
     if constexpr (!KV_SHARED) {
-      const u32x4_t* p = vbase + key_row(t) + lg;
+      const u32x4_t* p = vbase + (size_t)key_slot_of(t) * ROW16 + lg;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) vr[j] = p[4 * j];
+      for (int j = 0; j < NL; ++j) vr[j] = p[4 * j];
     }
   };
   // LDS exchange inside one wave (its own tile): the hardware keeps a wave's LDS
@@ -162,11 +180,33 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
     const int k0 = k_begin + 16 * t;
     // S^T for the tile
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
+      // codes widened exactly to bf16; the V rows (widened) go to LDS in natural d order
+      const char* q8 = s_q + l16 * QROWB + lg * 32;
+      char* w8 = tile + l16 * ROWB + lg * 32;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      s = mfma_k32(kr[j], *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
-    // V rows of the tile to LDS (key l16, d = 8 lg + 32 j), then refill the registers
-    {
+      for (int jj = 0; jj < NL; ++jj) {
+        const uint4 lo = e4m3x8_to_bf16x8(kr[jj].x, kr[jj].y);
+        const uint4 hi = e4m3x8_to_bf16x8(kr[jj].z, kr[jj].w);
+        s = mfma_k32(lo, *reinterpret_cast<const uint4*>(q8 + jj * 128), s);
+        s = mfma_k32(hi, *reinterpret_cast<const uint4*>(q8 + jj * 128 + 16), s);
+        if constexpr (KV_SHARED) {
+          *reinterpret_cast<uint4*>(w8 + jj * 128) = lo;
+          *reinterpret_cast<uint4*>(w8 + jj * 128 + 16) = hi;
+        } else {
+          *reinterpret_cast<uint4*>(w8 + jj * 128) = e4m3x8_to_bf16x8(vr[jj].x, vr[jj].y);
+          *reinterpret_cast<uint4*>(w8 + jj * 128 + 16) = e4m3x8_to_bf16x8(vr[jj].z, vr[jj].w);
+        }
+      }
+      if (lg == 0) {  // the tile's row scales, read back per key 4 lg + i after the sync
+        s_scl[wave][0][l16] = ksc;
+        s_scl[wave][1][l16] = vsc;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        s = mfma_k32(kr[j], *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
+      // V rows of the tile to LDS (key l16, d = 8 lg + 32 j), then refill the registers
       char* w = tile + l16 * ROWB + lg * 16;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -181,13 +221,20 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
     wave_sync();  // the tile's LDS writes before its transposed reads
 
     // softmax: lane holds row l16, keys k0 + 4 lg + i
+    float kq[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vq[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FP8) {  // the row scales of keys 4 lg + 0..3
+      const float4 k4 = *reinterpret_cast<const float4*>(&s_scl[wave][0][4 * lg]);
+      const float4 v4 = *reinterpret_cast<const float4*>(&s_scl[wave][1][4 * lg]);
+      kq[0] = k4.x; kq[1] = k4.y; kq[2] = k4.z; kq[3] = k4.w;
+      vq[0] = v4.x; vq[1] = v4.y; vq[2] = v4.z; vq[3] = v4.w;
+    }
     float x[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = k0 + 4 * lg + i;
       const int pos = r.lo + key;
-      float v = s[i] * a.scale;
+      float v = s[i] * kq[i] * a.scale;  // fp8: the key's row scale
       if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
       const bool ok = key < k_end && pos >= row_lo && pos <= row_hi;
       x[i] = ok ? v * kLog2e : -INFINITY;
@@ -206,6 +253,7 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
     for (int i = 0; i < 4; ++i) {
       p[i] = x[i] == -INFINITY ? 0.0f : exp2_fast(x[i] - m);
       l += p[i];
+      p[i] *= vq[i];  // fp8: the value row's scale (1 for bf16)
     }
     const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
     const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
@@ -279,17 +327,23 @@ hipError_t decode_rows16_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t st
   const long long blocks = (long long)a.B * a.Hkv * a.n_chunks * a.n_split;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(64 * decode_rows16_waves(a.D));
+#define GA_ROWS16_LAUNCH(DD, KV)                                                           \
+  do {                                                                                     \
+    if (a.fp8)                                                                             \
+      hipLaunchKernelGGL((decode_rows16_kernel<DD, KV, true>), grid, block, 0, stream, a);  \
+    else                                                                                   \
+      hipLaunchKernelGGL((decode_rows16_kernel<DD, KV, false>), grid, block, 0, stream, a); \
+  } while (0)
   if (a.D == 128) {
-    if (k_eq_v) hipLaunchKernelGGL((decode_rows16_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_rows16_kernel<128, false>), grid, block, 0, stream, a);
+    if (k_eq_v) GA_ROWS16_LAUNCH(128, true); else GA_ROWS16_LAUNCH(128, false);
   } else if (a.D == 256) {
-    if (k_eq_v) hipLaunchKernelGGL((decode_rows16_kernel<256, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_rows16_kernel<256, false>), grid, block, 0, stream, a);
+    if (k_eq_v) GA_ROWS16_LAUNCH(256, true); else GA_ROWS16_LAUNCH(256, false);
   } else if (a.D == 512 && k_eq_v) {
-    hipLaunchKernelGGL((decode_rows16_kernel<512, true>), grid, block, 0, stream, a);
+    GA_ROWS16_LAUNCH(512, true);
   } else {
     return hipErrorInvalidValue;
   }
+#undef GA_ROWS16_LAUNCH
   return hipGetLastError();
 }
 

@@ -195,6 +195,14 @@ SPEC_DECODE_SLIDING = Workload("gemma4-12b sliding layer verifying 7 draft token
                                tokens=8)
 
 
+# The same verification over an fp8 cache: BF16 queries with FP8 KV and spec decode on a
+# sliding window, the combination item "(2)" of the "Gemma 4 12B (unified multimodal)"
+# record reports as corrupting in another engine.
+FP8_SPEC_DECODE_SLIDING = replace(SPEC_DECODE_SLIDING, name="gemma4-12b sliding layer verifying "
+                                  "7 draft tokens (T=8) over an fp8 e4m3 cache, B64 16q/8kv "
+                                  "hd256 ring W=1031 w1024 ctx U[512,8192] softcap50", seed=11,
+                                  kv_dtype="fp8")
+
 def layer_seed(workload: Workload, layer: int) -> int:
     """Per-layer seed of a multi-layer workload (single-layer workloads use the seed)."""
     return workload.seed if workload.num_layers == 1 else workload.seed * 1000 + layer

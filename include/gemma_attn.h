@@ -246,10 +246,12 @@ int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* 
  * [B, T, Hq, D], token t at q_pos[b] + t; T = 1 is single-token decode with q [B, Hq, D]).
  * Same definition, with every cached value code * scale; the logits accumulate
  * q . codes in float32 and multiply by the row's K scale, the value weights carry the
- * row's V scale.  With one token on the K = V global geometry (head_dim 512, 16 query
- * heads per KV head) the matrix-core kernel serves it (codes widened exactly to bf16,
- * the K scale on each logit and the V scale on each value weight), as for bf16 caches;
- * every other shape runs on the vector kernel (GA_IMPL_MFMA is refused there).
+ * row's V scale.  The kernels are chosen as for bf16 caches: with one token, the K = V
+ * global geometry (head_dim 512, 16 query heads per KV head) runs on the matrix cores;
+ * with several tokens, 16 query rows per KV head (heads x tokens >= 8; head_dim 128 or
+ * 256, or 512 with K = V) run on the matrix cores; there the codes are widened exactly
+ * to bf16 in registers, the K scale multiplies each logit and the V scale each value
+ * weight.  Every other shape runs on the vector kernel (GA_IMPL_MFMA is refused there).
  * Workspace: ga_decode_fp8_workspace_bytes (covers whichever kernel the call picks).
  */
 size_t ga_decode_fp8_workspace_bytes(const ga_shape* shape, int32_t num_tokens, int32_t window,

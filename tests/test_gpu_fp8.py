@@ -255,3 +255,59 @@ def test_fp8_global_layer_full_size_sampled_rows():
                                            None, ctx[rows], ctx[rows] - 1, g.window, g.softcap,
                                            g.q_scale, g.kind)
     assert_parity(out[rows].unsqueeze(1), ref, "fp8 global full size")
+
+
+@pytest.mark.parametrize("D,G,Hkv,k_eq_v,T", [(256, 2, 4, False, 8), (128, 4, 2, False, 4),
+                                              (512, 16, 1, True, 2), (256, 8, 1, True, 3)])
+def test_fp8_multi_token_matrix_cores_match_vector_kernel_and_oracle(D, G, Hkv, k_eq_v, T):
+    """Several query tokens over fp8 caches on the matrix cores (16 query rows per KV head,
+    codes widened to bf16, K scales on the logits, V scales on the value weights, the
+    work-group's waves merged in LDS) and on the vector kernel: both match the oracle,
+    with one split per unit and with several (merge kernel), over ring windows at the
+    wrap edges."""
+    w = 64
+    cap, window = w + T - 1, w
+    ctx = [T, w - 1, w, w + 1, w + T - 1, 2 * w + 3, 5 * w - 1]
+    inp = Fp8Inputs(777 + D + T, len(ctx), T, G * Hkv, Hkv, D, cap, k_eq_v, ctx)
+    inp.poison(window, api.RING).to_device()
+    ref, _ = inp.oracle(window, 30.0, default_scale(D), api.RING)
+    for impl in [api.IMPL_MFMA, api.IMPL_VALU]:
+        for split in [0, 64]:
+            out = inp.run(window, 30.0, default_scale(D), api.RING, max_ctx=max(ctx), impl=impl,
+                          split_keys=split)
+            assert_parity(out, ref, f"fp8 T={T} D={D} G={G} impl={impl} split={split}")
+
+
+def test_fp8_spec_decode_layer_full_size_sampled_rows():
+    """The 12B sliding layer verifying 8 tokens (ring 1031, w 1024) over an fp8 cache
+    filled by quantizing appends; sampled rows against the oracle (BF16 queries, FP8 KV,
+    spec decode on a sliding window: the combination reported to corrupt in another
+    engine)."""
+    w = wl.FP8_SPEC_DECODE_SLIDING
+    g = w.layers[0]
+    B, T, Hkv, D, W = w.batch, w.tokens, g.num_kv_heads, g.head_dim, g.capacity
+    ctx = synth.uniform_int(synth.generator(w.seed), B, w.ctx_lo, w.ctx_hi).numpy() \
+        .astype(np.int32)
+    gd = synth.generator(78, device="cuda")
+    kc = torch.empty((B, Hkv, W, D), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty((B, Hkv, W), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    ctx_t = torch.from_numpy(ctx).cuda()
+    for part in range(0, W, 512):
+        n = min(512, W - part)
+        kn = synth.normal_bf16(gd, (B, n, Hkv, D), device="cuda")
+        vn = synth.normal_bf16(gd, (B, n, Hkv, D), device="cuda")
+        api.kv_append_fp8(kc, ks, vc, vs, kn, vn, ctx_t - W + part, api.RING)
+    q = synth.normal_bf16(gd, (B, T, g.num_q_heads, D), device="cuda")
+    out = api.decode_fp8(q, kc, ks, vc, vs, ctx_t, ctx_t - T, g.window, g.softcap, g.q_scale,
+                         g.kind, max_ctx=w.ctx_hi)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, int(np.argmax(ctx)), int(np.argmin(ctx))})
+    log(f"fp8 spec decode rows {rows}")
+    ref, _, _, flags = oracle.decode_fp8_multi(
+        synth.bits(q[rows].cpu()), kc[rows].cpu().numpy(), ks[rows].cpu().numpy(),
+        vc[rows].cpu().numpy(), vs[rows].cpu().numpy(), ctx[rows], ctx[rows] - T, g.window,
+        g.softcap, g.q_scale, g.kind)
+    assert not flags.any()
+    assert_parity(out[rows], ref, "fp8 spec decode full size")
