@@ -368,6 +368,24 @@ def test_mfma_matches_valu_and_softcap():
     assert_parity(run(inp, 0, 30.0, scale, api.LINEAR, impl=api.IMPL_MFMA), ref, "mfma softcap")
 
 
+def test_mfma_repeats_bits_without_the_deterministic_option():
+    """The global matrix-core kernel fixes its partition on the device from the context
+    lengths and sums tiles, waves and work-groups in a fixed order: repeated calls give
+    identical bits (bf16 and fp8 caches)."""
+    inp = gen_layer(95, 6, 16, 1, 512, 9000, True, 1, 9000).to_device()
+    scale = default_scale(512)
+    a = run(inp, 0, 0.0, scale, api.LINEAR, impl=api.IMPL_MFMA)
+    for _ in range(3):
+        assert torch.equal(a, run(inp, 0, 0.0, scale, api.LINEAR, impl=api.IMPL_MFMA))
+    codes = torch.randint(0, 126, (6, 1, 9000, 512), dtype=torch.uint8, device="cuda")
+    scales = torch.rand((6, 1, 9000), device="cuda") * 0.01 + 0.001
+    f = lambda: api.decode_fp8(inp.q, codes, scales, None, None, inp.ctx_t, inp.qpos_t, 0, 0.0,
+                               scale, api.LINEAR, impl=api.IMPL_MFMA)
+    b = f()
+    for _ in range(3):
+        assert torch.equal(b, f())
+
+
 def test_mfma_single_key_rows_are_exact():
     """One valid key: P = 1 exactly splits into hi = 1, lo = 0, so the output is the row."""
     inp = gen_layer(93, 3, 16, 1, 512, 64, True, 1, 1, ctx=[1, 1, 1]).to_device()

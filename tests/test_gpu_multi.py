@@ -196,3 +196,22 @@ def test_validate_multi_matches_oracle_flags():
     kc = np.zeros((4, 1, W, 128), np.uint16)
     _, _, _, ref = oracle.decode_multi(q, kc, None, ctx, q0, w, 0.0, 1.0, oracle.RING)
     assert np.array_equal(flags & 15, ref), (flags, ref)
+
+
+@pytest.mark.parametrize("D,G,Hkv,k_eq_v,split", [(256, 2, 8, False, 0), (256, 2, 8, False, 64),
+                                                  (512, 16, 1, True, 0)])
+def test_matrix_core_multi_token_repeats_bits(D, G, Hkv, k_eq_v, split):
+    """The multi-token matrix-core kernel is deterministic without any option: its tiles
+    go to the waves of a split in a fixed order and the waves (and splits) merge in a
+    fixed order, so repeated calls give identical bits, with one split per unit and with
+    several."""
+    T = 16 // G if G < 16 else 2
+    ctx = [T, 100, 900, 3000, 4096, 777, 64, 2500]
+    inp = MultiInputs(4321 + D, len(ctx), T, G * Hkv, Hkv, D, 4096, k_eq_v, ctx).to_device()
+    args = (0, 0.0, default_scale(D), api.LINEAR)
+    first = inp.run(*args, impl=api.IMPL_MFMA, split_keys=split, max_ctx=4096)
+    for _ in range(3):
+        again = inp.run(*args, impl=api.IMPL_MFMA, split_keys=split, max_ctx=4096)
+        assert torch.equal(first, again)
+    ref, _ = inp.oracle(*args)
+    assert_parity(first, ref, f"repeat D={D} split={split}")
