@@ -157,9 +157,10 @@ __global__ void append_kernel(int B, int T, int Hkv, int D, int cap, int kind, u
   if (v_cache) v_cache[dst] = v_new[src];
 }
 
-// Quantizing append into fp8 e4m3 caches: one wave per (b, KV head) walks the T tokens
-// in order (so a later token that lands in the same ring slot stays); lane i < D / 8
-// holds 8 consecutive values of the row.  Per row: amax = max |x|, inv = 448 / amax,
+// Quantizing append into fp8 e4m3 caches: one wave per (b, token, KV head), all tokens at
+// once; when two tokens of the call land in the same ring slot (t + W < T) only the later
+// one writes, so the latest token stays, as with the plain append.  Lane i < D / 8 holds
+// 8 consecutive values of the row.  Per row: amax = max |x|, inv = 448 / amax,
 // code = round-to-nearest-even e4m3 of clamp(x * inv, +-448), scale = amax / 448, all in
 // float32 with correctly rounded division, as the plain definition states.
 __device__ __forceinline__ void quantize_store_row(const uint4* src, uint2* dst_codes,
@@ -196,22 +197,23 @@ __global__ void __launch_bounds__(64)
     append_fp8_kernel(int B, int T, int Hkv, int D, int cap, int kind, uint8_t* k_codes,
                       float* k_scales, uint8_t* v_codes, float* v_scales, const uint4* k_new,
                       const uint4* v_new, const int32_t* pos) {
-  const int bg = blockIdx.x;  // b * Hkv + g
-  const int b = bg / Hkv, g = bg % Hkv;
   const int lane = threadIdx.x;
+  const int btg = blockIdx.x;  // (b * T + t) * Hkv + g (the launcher keeps it below 2^31)
+  const int g = btg % Hkv;
+  const int bt = btg / Hkv;
+  const int b = bt / T, t = bt % T;
+  const long long p = (long long)pos[b] + t;
+  if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) return;  // out of range: skipped
+  if (kind == GA_CACHE_RING && t + cap < T) return;              // a later token owns it
+  const int slot = kind == GA_CACHE_RING ? (int)(p % cap) : (int)p;
+  const size_t row = ((size_t)b * Hkv + g) * cap + slot;
   const int chunks = D / 8;
-  for (int t = 0; t < T; ++t) {
-    const long long p = (long long)pos[b] + t;
-    if (p < 0 || (kind == GA_CACHE_LINEAR && p >= cap)) continue;  // out of range: skipped
-    const int slot = kind == GA_CACHE_RING ? (int)(p % cap) : (int)p;
-    const size_t row = (size_t)bg * cap + slot;
-    const size_t src = (((size_t)b * T + t) * Hkv + g) * chunks;
-    quantize_store_row(k_new + src, reinterpret_cast<uint2*>(k_codes + row * D),
-                       k_scales + row, lane, chunks);
-    if (v_codes)
-      quantize_store_row(v_new + src, reinterpret_cast<uint2*>(v_codes + row * D),
-                         v_scales + row, lane, chunks);
-  }
+  const size_t src = (size_t)btg * chunks;
+  quantize_store_row(k_new + src, reinterpret_cast<uint2*>(k_codes + row * D), k_scales + row,
+                     lane, chunks);
+  if (v_codes)
+    quantize_store_row(v_new + src, reinterpret_cast<uint2*>(v_codes + row * D), v_scales + row,
+                       lane, chunks);
 }
 
 // Rotary embedding fused with the cache append ("Gemma support" pull request, Summary: own
@@ -343,9 +345,10 @@ hipError_t append_fp8_launch(int B, int T, int Hkv, int D, int cap, int kind, ui
                              float* k_scales, uint8_t* v_codes, float* v_scales,
                              const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos,
                              hipStream_t stream) {
-  const long long units = (long long)B * Hkv;
-  if (units <= 0 || T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(append_fp8_kernel, dim3((unsigned)units), dim3(64), 0, stream, B, T, Hkv, D,
+  const long long rows = (long long)B * T * Hkv;  // one single-wave work-group each
+  if (rows <= 0 || T <= 0) return hipSuccess;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(append_fp8_kernel, dim3((unsigned)rows), dim3(64), 0, stream, B, T, Hkv, D,
                      cap, kind, k_codes, k_scales, v_codes, v_scales,
                      reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
                      pos);

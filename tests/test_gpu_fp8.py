@@ -72,7 +72,7 @@ class Fp8Inputs:
 
 @pytest.mark.parametrize("D", [128, 256, 512])
 @pytest.mark.parametrize("k_eq_v", [False, True])
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 12])  # 12 > the ring's 8 slots: later tokens own them
 def test_append_fp8_matches_oracle_bitwise(D, k_eq_v, T):
     B, Hkv = 3, 2
     for kind, cap, pos0 in [(api.RING, 8, [0, 5, 1001]), (api.LINEAR, 16, [-2, 3, 14])]:
