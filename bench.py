@@ -53,7 +53,8 @@ def parse_args():
 
 
 # Single-layer workloads measured with --workload (the default line is the 48-layer step).
-SINGLE_LAYER = {"hd128_sliding": "HD128_SLIDING", "g4_12b_sliding": "G4_12B_SLIDING",
+SINGLE_LAYER = {"g3_1b_sliding": "G3_1B_SLIDING", "hd128_sliding": "HD128_SLIDING",
+                "g4_12b_sliding": "G4_12B_SLIDING",
                 "g4_12b_global": "G4_12B_GLOBAL", "spec_decode_sliding": "SPEC_DECODE_SLIDING",
                 "fp8_sliding": "FP8_SLIDING", "fp8_global": "FP8_GLOBAL",
                 "fp8_spec_decode_sliding": "FP8_SPEC_DECODE_SLIDING"}
@@ -309,7 +310,10 @@ def main():
     log(f"sliding decode kernel: {kern_ms * 1e3:.2f} us avg over {n_launch} launches, "
         f"{kern_gbps:.1f} GB/s")
 
+    extras = step_variants(args, step, stream, cache, qs, ctx_t, qpos_t, outs, L,
+                           sum(x["decode"] for x in per_layer), graph is not None)
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    extras["pct_of_copy_ceiling"] = round(100.0 * value / extras["copy_ceiling_gbps"], 2)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -350,9 +354,70 @@ def main():
         },
     }
 
+    result["extras"] = extras
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cache, qs, ctx, w, per_layer, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def step_variants(args, step, stream, cache, qs, ctx_t, qpos_t, outs, L, decode_bytes, graphed):
+    """Besides the timed step: its per-step time distribution, the step without the append
+    (decode over the resident caches only), the step replayed as a HIP graph, and a
+    copy-kernel ceiling measured on the same GPU (torch copy of 1 GiB: read + write bytes
+    over time), each after the main measurement."""
+    import numpy as np
+    import torch
+    n = max(1, args.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def decode_only():
+        for li in range(L):
+            cache.decode(li, qs[li], ctx_t, qpos_t, out=outs[li])
+
+    ms_decode = timed(decode_only)
+    ms_graph = None
+    if not graphed:
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        ms_graph = timed(g.replay)
+        del g
+    src = torch.ones((COPY_BYTES // 4,), dtype=torch.float32, device=qs[0].device)
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    copy_gbps = 2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9
+    log(f"step p10/p50/p90 {np.percentile(per, [10, 50, 90]).round(4).tolist()} ms; decode only "
+        f"{ms_decode:.4f} ms; graph {ms_graph} ms; copy ceiling {copy_gbps:.0f} GB/s")
+    return {
+        "step_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(per, [10, 50, 90])],
+        "decode_only_ms_per_step": round(ms_decode, 5),
+        "decode_only_gbps": round(decode_bytes / (ms_decode * 1e-3) / 1e9, 2),
+        "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 5),
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+    }
 
 
 def bench_single_layer(args):
@@ -460,7 +525,7 @@ def bench_single_layer(args):
             rows = sl.stop
         result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
                                   "cores": int(min(threads, rows * g.num_q_heads)),
-                                  "kind": "oracle",
+                                  "kind": "oracle", "host": host_cpu(),
                                   "sample": f"rows 0-{rows - 1} of the layer (decode only), "
                                             f"{spent:.1f}s of oracle time"}
     print(json.dumps(result), flush=True)
@@ -578,7 +643,7 @@ def bench_multi_token(args, w):
             rows = sl.stop
         result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
                                   "cores": int(min(threads, rows * T * g.num_q_heads)),
-                                  "kind": "oracle",
+                                  "kind": "oracle", "host": host_cpu(),
                                   "sample": f"rows 0-{rows - 1} of the layer, all {T} tokens "
                                             f"(decode only), {spent:.1f}s of oracle time"}
     print(json.dumps(result), flush=True)
@@ -714,7 +779,7 @@ def bench_fp8(args, w):
             rows = sl.stop
         result["cpu_baseline"] = {"value": round(done / spent / 1e9, 4), "unit": "GB/s",
                                   "cores": int(min(threads, rows * g.num_q_heads)),
-                                  "kind": "oracle",
+                                  "kind": "oracle", "host": host_cpu(),
                                   "sample": f"rows 0-{rows - 1} of the layer (decode only), "
                                             f"{spent:.1f}s of oracle time"}
     print(json.dumps(result), flush=True)
@@ -754,7 +819,21 @@ def cpu_baseline(cache, qs, ctx, w, per_layer, target_s):
         "kind": "oracle",
         "sample": f"layers {layers[0]}-{layers[-1]} of the 48-layer step (whole layers, all "
                   f"{len(ctx)} rows, decode only), {spent:.1f}s of oracle time",
+        "host": host_cpu(),
     }
+
+
+def host_cpu():
+    """Model name and logical CPU count of the host, for the CPU baseline."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{model} ({os.cpu_count()} logical CPUs visible)"
 
 
 if __name__ == "__main__":
