@@ -55,6 +55,9 @@ constexpr int WAVE_TILE = TK * ROWQ;
 #ifndef GA_FP8_TILES
 #define GA_FP8_TILES 8
 #endif
+#ifndef GA_BF16_TILES
+#define GA_BF16_TILES 4
+#endif
 constexpr float kRescaleLog2 = 8.0f;
 // LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
 // (160 KiB each): every CU then holds the same number of equal-work work-groups.
@@ -90,7 +93,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   __shared__ __attribute__((aligned(16))) float s_scale[2][2][TK];  // fp8 row scales
   // Tiles in flight per wave: four bf16 tiles (64 KiB per work-group); fp8 tiles are half
   // the bytes, so eight keep as many bytes in flight (the loop is latency-bound otherwise).
-  constexpr int NF = FP8 ? GA_FP8_TILES : 4;
+  constexpr int NF = FP8 ? GA_FP8_TILES : GA_BF16_TILES;
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
   __shared__ int s_slot[kMfmaMaxUnits];   // slot of each unit's first valid key
@@ -200,6 +203,10 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
   const uint4* knew = a.new_pos ? reinterpret_cast<const uint4*>(a.k_new) + (size_t)u * (MD / 8)
                                 : kbase;
+  // bf16 loads: lane reads 16 bytes (column lane % 16 of the wave's 256-byte slice) of key
+  // lane / 16 + 4 j, so each instruction covers 4 keys x 2 whole 128-byte lines
+  const uint4* kbase_l = kbase + 16 * wave + (lane & 15);
+  const uint4* knew_l = knew + 16 * wave + (lane & 15);
 
   floatx4_t acc[8];
 #pragma unroll
@@ -208,65 +215,91 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
 
   const int nt = (seg_hi - seg_lo + TK - 1) / TK;
 
-  // One tile's registers: bf16 rows in rg[0..3]; fp8 rows: the 32 codes in rg[0..1] and
-  // the scale of the lane's key (key l16 of the tile) in rg[2].x.
+  // One tile's registers: bf16 rows in rg[0..3] (rg[j]: key lane / 16 + 4 j of the tile);
+  // fp8 rows: the 32 codes of key l16 in rg[0..1] and that key's scale in rg[2].x.
   auto load = [&](uint4(&rg)[4], int t) {
-    const int key = seg_lo + t * TK + l16;
-    const int kc = key < seg_hi ? key : seg_hi - 1;
-    const int slot = key_slot(slot_lo, kc, a.cap);
     if constexpr (FP8) {
+      const int key = seg_lo + t * TK + l16;
+      const int kc = key < seg_hi ? key : seg_hi - 1;
+      const int slot = key_slot(slot_lo, kc, a.cap);
       const uint4* cp = cbase + (size_t)slot * (MD / 16) + 8 * wave + lg;
       rg[0] = cp[0];
       rg[1] = cp[4];
       rg[2].x = __float_as_uint(sbase[slot]);  // the scale of this lane's key (l16)
     } else {
-      const uint4* rp =
-          (slot == new_slot ? knew : kbase + (size_t)slot * (MD / 8)) + 16 * wave + lg;
+      const int key0 = seg_lo + t * TK + (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rg[j] = rp[4 * j];
+      for (int j = 0; j < 4; ++j) {
+        const int key = key0 + 4 * j;
+        const int kc = key < seg_hi ? key : seg_hi - 1;
+        const int slot = key_slot(slot_lo, kc, a.cap);
+        rg[j] = stream_load(slot == new_slot ? knew_l : kbase_l + (size_t)slot * (MD / 8));
+      }
     }
   };
 
   // One step = two 16-key tiles (ra: keys k0 .. k0 + 15, rb: the next 16): their products
   // and softmax chains interleave, and one barrier and one max update cover 32 keys.
-  // A tile's S^T partial over this wave's d slice: K rows (A operand) times Q^T; the
-  // tile's rows also go to LDS in natural d order (the V operand).  fp8 codes are widened
-  // to bf16 first.
-  auto tile_scores = [&](const uint4(&rg)[4], char* tile, floatx4_t& s) {
+  // Each tile's rows go to the wave's LDS tile in natural d order (the V operand, and for
+  // bf16 also the K operand); a tile's S^T partial over this wave's d slice is K rows
+  // (A operand) times Q^T.  fp8 codes are widened to bf16 first and feed the products
+  // from registers.
+  auto tile_scores_fp8 = [&](const uint4(&rg)[4], char* tile, floatx4_t& s) {
     s = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (FP8) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const uint4 lo = e4m3x8_to_bf16x8(rg[jj].x, rg[jj].y);
-        const uint4 hi = e4m3x8_to_bf16x8(rg[jj].z, rg[jj].w);
-        s = mfma_k32(lo, qv[2 * jj], s);
-        s = mfma_k32(hi, qv[2 * jj + 1], s);
-        char* w8 = tile + l16 * ROWQ + lg * 32 + jj * 128;  // 16 d per lane and jj
-        *reinterpret_cast<uint4*>(w8) = lo;
-        *reinterpret_cast<uint4*>(w8 + 16) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s = mfma_k32(rg[j], qv[j], s);
-      char* w = tile + l16 * ROWQ + lg * 16;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(w + j * 64) = rg[j];
+    for (int jj = 0; jj < 2; ++jj) {
+      const uint4 lo = e4m3x8_to_bf16x8(rg[jj].x, rg[jj].y);
+      const uint4 hi = e4m3x8_to_bf16x8(rg[jj].z, rg[jj].w);
+      s = mfma_k32(lo, qv[2 * jj], s);
+      s = mfma_k32(hi, qv[2 * jj + 1], s);
+      char* w8 = tile + l16 * ROWQ + lg * 32 + jj * 128;  // 16 d per lane and jj
+      *reinterpret_cast<uint4*>(w8) = lo;
+      *reinterpret_cast<uint4*>(w8 + 16) = hi;
     }
+  };
+  // bf16: lane writes its 16 bytes of keys lane / 16 + 4 j, then (after the wave's writes)
+  // reads the A operand of key l16, d = 32 j + 8 lg + 0..7 of the slice
+  auto tile_write_bf16 = [&](const uint4(&rg)[4], char* tile) {
+    char* w = tile + (lane >> 4) * ROWQ + (lane & 15) * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(w + 4 * j * ROWQ) = rg[j];
   };
 
   auto step2 = [&](uint4(&ra)[4], uint4(&rb)[4], int t) {
     const int k0 = seg_lo + t * TK;
     floatx4_t sa, sb;
-    tile_scores(ra, tile_a, sa);
-    tile_scores(rb, tile_b, sb);
+    if constexpr (FP8) {
+      tile_scores_fp8(ra, tile_a, sa);
+      tile_scores_fp8(rb, tile_b, sb);
+    } else {
+      wave_lds_sync();  // the previous step's transposed reads stay before these writes
+      tile_write_bf16(ra, tile_a);
+      tile_write_bf16(rb, tile_b);
+      // the registers are free once written: the next loads go out before the products
+      // (unconditional, clamped past the end: keeps the wait counts partial)
+      load(ra, t + NF);
+      load(rb, t + NF + 1);
+      wave_lds_sync();
+      sa = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      sb = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      const char* rda = tile_a + l16 * ROWQ + lg * 16;
+      const char* rdb = tile_b + l16 * ROWQ + lg * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sa = mfma_k32(*reinterpret_cast<const uint4*>(rda + 64 * j), qv[j], sa);
+        sb = mfma_k32(*reinterpret_cast<const uint4*>(rdb + 64 * j), qv[j], sb);
+      }
+    }
     s_part[par][wave][0][lane] = sa;
     s_part[par][wave][1][lane] = sb;
     if (FP8 && wave == 0 && lg == 0) {  // the keys' row scales, for every wave's logits
       s_scale[par][0][l16] = __uint_as_float(ra[2].x);
       s_scale[par][1][l16] = __uint_as_float(rb[2].x);
     }
-    load(ra, t + NF);  // unconditional (clamped past the end): keeps wait counts partial
-    load(rb, t + NF + 1);
+    if constexpr (FP8) {
+      load(ra, t + NF);  // unconditional (clamped past the end): keeps wait counts partial
+      load(rb, t + NF + 1);
+    }
     __syncthreads();
     float ka[4] = {1.0f, 1.0f, 1.0f, 1.0f}, kb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
     if constexpr (FP8) {  // scales of the keys 4 lg + 0..3 this lane's logits belong to
@@ -380,15 +413,21 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
 }
 
 // Finishes the units that were split over several work-groups; writes 0 for empty
-// units.  One work-group per (unit, head); each thread owns two output elements and
-// runs an online log-sum-exp over the unit's partial slots, 16 slots per batch of
-// independent loads (slot weights and partial sums are loaded together).
+// units.  One work-group per (unit, head): wave w takes partial slots w, w + 4, ...,
+// with up to 16 slots' loads in flight per wave (so a unit of up to 64 partials costs
+// one round of loads); lane l owns d = 8 l .. 8 l + 7.  Each wave keeps an online
+// log-sum-exp, and the four wave states are combined through LDS.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeBatch = 16;
 
-__global__ void __launch_bounds__(kMergeThreads) merge_units_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kMergeThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+merge_units_kernel(DecodeArgs a) {
+  __shared__ float s_ml[kMergeWaves][2];
+  __shared__ __attribute__((aligned(16))) float s_o[kMergeWaves][MD];
   const int u = blockIdx.x / MG, h = blockIdx.x % MG;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K0 = a.plan[u], K1 = a.plan[u + 1];
   const size_t head = ((size_t)(u / a.Hkv) * a.Hq + (size_t)(u % a.Hkv) * MG + h);
   float* out = a.out + head * MD;
@@ -399,41 +438,73 @@ __global__ void __launch_bounds__(kMergeThreads) merge_units_kernel(DecodeArgs a
   }
   if (ks == 1) return;  // written directly by the decode kernel
   const float* ml = a.part_ml + ((size_t)K0 * MG + h) * 2;
-  const float* acc = a.part_acc + ((size_t)K0 * MG + h) * MD;
-  const size_t ml_stride = (size_t)MG * 2, acc_stride = (size_t)MG * MD;
-  const int d0 = tid, d1 = tid + kMergeThreads;  // MD == 2 * kMergeThreads
-  float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s0 = 0; s0 < ks; s0 += kMergeBatch) {
-    float mb[kMergeBatch], lb[kMergeBatch], a0[kMergeBatch], a1[kMergeBatch];
+  const float4* acc =
+      reinterpret_cast<const float4*>(a.part_acc + ((size_t)K0 * MG + h) * MD) + 2 * lane;
+  const size_t ml_stride = (size_t)MG * 2, acc_stride4 = (size_t)MG * MD / 4;
+  float M = -INFINITY, L = 0.0f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < ks; s0 += kMergeWaves * kMergeBatch) {
+    float mb[kMergeBatch], lb[kMergeBatch];
+    float4 va[kMergeBatch], vb[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const int s = min(s0 + i, ks - 1);
+      const int s = min(s0 + kMergeWaves * i, ks - 1);  // past the end: a valid slot, unused
       mb[i] = ml[s * ml_stride];
       lb[i] = ml[s * ml_stride + 1];
-      a0[i] = acc[s * acc_stride + d0];
-      a1[i] = acc[s * acc_stride + d1];
+      va[i] = acc[s * acc_stride4];
+      vb[i] = acc[s * acc_stride4 + 1];
     }
     float mnew = M;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i)
-      if (s0 + i < ks) mnew = fmaxf(mnew, mb[i]);
+      if (s0 + kMergeWaves * i < ks) mnew = fmaxf(mnew, mb[i]);
     const float f = M == -INFINITY ? 0.0f : exp2_fast(M - mnew);
     L *= f;
-    o0 *= f;
-    o1 *= f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] *= f;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      if (s0 + i >= ks) break;
-      const float w = exp2_fast(mb[i] - mnew);
+      // no early exit: every load is consumed, so all of them are issued up front
+      const float w = s0 + kMergeWaves * i < ks ? exp2_fast(mb[i] - mnew) : 0.0f;
       L = fmaf(lb[i], w, L);
-      o0 = fmaf(a0[i], w, o0);
-      o1 = fmaf(a1[i], w, o1);
+      o[0] = fmaf(va[i].x, w, o[0]);
+      o[1] = fmaf(va[i].y, w, o[1]);
+      o[2] = fmaf(va[i].z, w, o[2]);
+      o[3] = fmaf(va[i].w, w, o[3]);
+      o[4] = fmaf(vb[i].x, w, o[4]);
+      o[5] = fmaf(vb[i].y, w, o[5]);
+      o[6] = fmaf(vb[i].z, w, o[6]);
+      o[7] = fmaf(vb[i].w, w, o[7]);
     }
     M = mnew;
   }
-  const float inv = 1.0f / L;
-  out[d0] = o0 * inv;
-  out[d1] = o1 * inv;
+  // a wave without slots (ks < 4) leaves M = -inf, L = 0, o = 0: weight 0 below
+  if (lane == 0) {
+    s_ml[wave][0] = M;
+    s_ml[wave][1] = L;
+  }
+  float4* so = reinterpret_cast<float4*>(&s_o[wave][0]) + 2 * lane;
+  so[0] = make_float4(o[0], o[1], o[2], o[3]);
+  so[1] = make_float4(o[4], o[5], o[6], o[7]);
+  __syncthreads();
+  float Mall = s_ml[0][0];  // wave 0 always holds slot 0
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) Mall = fmaxf(Mall, s_ml[w][0]);
+  float wt[kMergeWaves], Lall = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    wt[w] = exp2_fast(s_ml[w][0] - Mall);
+    Lall = fmaf(s_ml[w][1], wt[w], Lall);
+  }
+  const float inv = 1.0f / Lall;
+#pragma unroll
+  for (int r = 0; r < MD / kMergeThreads; ++r) {
+    const int d = tid + r * kMergeThreads;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) v = fmaf(s_o[w][d], wt[w], v);
+    out[d] = v * inv;
+  }
 }
 
 }  // namespace

@@ -164,13 +164,6 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
       for (int j = 0; j < NL; ++j) vr[j] = p[4 * j];
     }
   };
-  // LDS exchange inside one wave (its own tile): the hardware keeps a wave's LDS
-  // accesses in order; the fences keep the compiler from reordering them
-  auto wave_sync = [] {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
   const int t0 = wave < nt ? wave : nt - 1;  // a wave without tiles loads a valid one
   load_k(t0);
   load_v(t0);
@@ -218,7 +211,7 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
     }
     load_k(t + NW < nt ? t + NW : t);
     load_v(t + NW < nt ? t + NW : t);
-    wave_sync();  // the tile's LDS writes before its transposed reads
+    wave_lds_sync();  // the tile's LDS writes before its transposed reads
 
     // softmax: lane holds row l16, keys k0 + 4 lg + i
     float kq[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vq[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -267,7 +260,7 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
       acc[db] = mfma_k16(va, ph, acc[db]);
       acc[db] = mfma_k16(va, pl, acc[db]);
     }
-    wave_sync();  // the tile's transposed reads stay before the next tile's writes
+    wave_lds_sync();  // the tile's transposed reads stay before the next tile's writes
   }
 
   // Merge the waves: each leaves (m, l) per row and acc (row l16, d = 16 db + 4 lg + i)

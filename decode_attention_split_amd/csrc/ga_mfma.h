@@ -59,6 +59,15 @@ __device__ __forceinline__ uint4 cat4(short4_t lo, short4_t hi) {
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// LDS exchange inside one wave: the hardware keeps a wave's LDS accesses in order; the
+// wave-scope fences keep the compiler from moving LDS accesses across this point, so
+// lanes may read what other lanes of the same wave wrote before it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
