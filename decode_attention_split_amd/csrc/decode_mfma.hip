@@ -19,12 +19,20 @@
 // others leave one partial per work-group (slot = work-group index) for
 // merge_units_kernel (log-sum-exp).
 //
-// Per work-group of 4 waves, 16-key tiles taken two per step; wave w owns head_dim slice
+// One work-group per CU of 8 waves: two groups of 4 waves in lockstep (one barrier per
+// step), group h taking the work-group's tiles 4 q + 2 h and 4 q + 2 h + 1, each with its own
+// softmax state; the second group's (m, l, acc) join the first's through LDS at the end.
+// One work-group per CU (rather than two of 4 waves) keeps a CU's two streams starting
+// and ending together: a second work-group on a CU queues behind the first ones' opening
+// loads and was measured to finish ~6 us later, leaving its CU half-busy for that time.
+// Per group, 16-key tiles taken two per step; wave w of the group owns head_dim slice
 // [128 w, 128 w + 128):
 //   partial S^T[16 keys][16 heads] = K[16][slice] . Q^T[slice][16] per tile with
-//     v_mfma_f32_16x16x32_bf16 (4 per tile): lane l loads key (l % 16), d = 128 w + 32 j +
-//     8 (l / 16) + 0..7 straight into the A operand (16-byte loads; 4 tiles in flight, 8
-//     for fp8 codes), Q^T is held in registers in the same d order;
+//     v_mfma_f32_16x16x32_bf16 (4 per tile): bf16 rows are loaded 16 bytes per lane with
+//     each instruction covering whole 128-byte lines of 4 keys (non-temporal), written to
+//     the wave's LDS tile and read back as the A operand (key l % 16, d = 128 w + 32 j +
+//     8 (l / 16) + 0..7); fp8 codes go straight from registers into the A operand after
+//     widening; 4 tiles in flight (8 for fp8); Q^T is held in registers in the same d order;
 //   the 4 partials are summed through LDS (one barrier per step of 32 keys), in the same
 //     order in every wave, so every wave holds the identical S^T and softmax state;
 //   the wave's K = V slice goes once to its own LDS rows (288 B stride) and
@@ -48,7 +56,9 @@ namespace {
 constexpr int MD = 512;        // head_dim
 constexpr int MG = 16;         // query heads per KV head
 constexpr int TK = 16;         // keys per tile
-constexpr int MNW = 4;         // waves per work-group, one head_dim slice each
+constexpr int MNW = 4;         // waves per group, one head_dim slice each
+constexpr int MH = kMfmaHalves;  // groups per work-group, in lockstep on alternate key pairs
+constexpr int NWV = MNW * MH;  // waves per work-group
 constexpr int DQ = MD / MNW;   // head_dim slice of a wave
 constexpr int ROWQ = DQ * 2 + 32;   // LDS bytes per key row of a wave's slice (bank spread)
 constexpr int WAVE_TILE = TK * ROWQ;
@@ -62,9 +72,11 @@ constexpr float kRescaleLog2 = 8.0f;
 // LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
 // (160 KiB each): every CU then holds the same number of equal-work work-groups.
 constexpr int kLdsCU = 160 * 1024;
-constexpr int kLdsOther = 2 * MNW * 2 * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4 + 2 * 2 * TK * 4;
+constexpr int kLdsOther = 2 * NWV * 2 * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4 + 2 * MH * 2 * TK * 4;
 constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
-constexpr int kLdsKV = 2 * MNW * WAVE_TILE > kLdsTile ? 2 * MNW * WAVE_TILE : kLdsTile;
+constexpr int kLdsKV = 2 * NWV * WAVE_TILE > kLdsTile ? 2 * NWV * WAVE_TILE : kLdsTile;
+// the second group's (acc, m, l) go to the first through the second group's tile area
+static_assert(2 * WAVE_TILE >= 64 * 8 * 16, "combine area per wave");
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
 
@@ -87,10 +99,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 template <bool FP8>
-__global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_kv[kLdsKV];
-  __shared__ floatx4_t s_part[2][MNW][2][64];  // [buffer][wave][tile of the step][lane]
-  __shared__ __attribute__((aligned(16))) float s_scale[2][2][TK];  // fp8 row scales
+  __shared__ floatx4_t s_part[2][MH][MNW][2][64];  // [buffer][group][wave][tile][lane]
+  __shared__ __attribute__((aligned(16))) float s_scale[2][MH][2][TK];  // fp8 row scales
+  __shared__ float s_ml[MG][2];  // the second group's m and l per head
   // Tiles in flight per wave: four bf16 tiles (64 KiB per work-group); fp8 tiles are half
   // the bytes, so eight keep as many bytes in flight (the loop is latency-bound otherwise).
   constexpr int NF = FP8 ? GA_FP8_TILES : GA_BF16_TILES;
@@ -100,12 +113,13 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int half = wave / MNW, wsl = wave % MNW;  // group, and the wave's head_dim slice
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.B * a.Hkv;
 
   // ---- the partition (every work-group computes it; work-group 0 also publishes it):
   // each unit's key range, then wave 0 alone forms both prefix sums (two barriers).
-  for (int u = tid; u < R; u += MNW * 64) {
+  for (int u = tid; u < R; u += NWV * 64) {
     const int b = u / a.Hkv;
     const RowRange rr = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
     s_n[u + 1] = rr.n;
@@ -145,7 +159,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   }
   __syncthreads();
   if (blockIdx.x == 0)
-    for (int u = tid; u <= R; u += MNW * 64) a.plan[u] = s_k[u];
+    for (int u = tid; u <= R; u += NWV * 64) a.plan[u] = s_k[u];
   // fused append: work-group u (< R <= grid) moves unit u's new row (stored at the end)
   AppendRow app;
   {
@@ -195,7 +209,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + (head0 + l16) * MD);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      qv[j] = FP8 ? qp[16 * wave + 8 * (j / 2) + 2 * lg + (j % 2)] : qp[16 * wave + 4 * j + lg];
+      qv[j] = FP8 ? qp[16 * wsl + 8 * (j / 2) + 2 * lg + (j % 2)] : qp[16 * wsl + 4 * j + lg];
   }
   const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + (size_t)u * a.cap * (MD / 8);
   const uint4* cbase = reinterpret_cast<const uint4*>(a.k8) + (size_t)u * a.cap * (MD / 16);
@@ -205,29 +219,36 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
                                 : kbase;
   // bf16 loads: lane reads 16 bytes (column lane % 16 of the wave's 256-byte slice) of key
   // lane / 16 + 4 j, so each instruction covers 4 keys x 2 whole 128-byte lines
-  const uint4* kbase_l = kbase + 16 * wave + (lane & 15);
-  const uint4* knew_l = knew + 16 * wave + (lane & 15);
+  const uint4* kbase_l = kbase + 16 * wsl + (lane & 15);
+  const uint4* knew_l = knew + 16 * wsl + (lane & 15);
 
   floatx4_t acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f;
 
-  const int nt = (seg_hi - seg_lo + TK - 1) / TK;
+  // The work-group's tiles go to the groups in pairs: tiles 4 q, 4 q + 1 to group 0, 4 q + 2,
+  // 4 q + 3 to group 1.  Both groups step through group 0's tile count (group 1's extra
+  // tiles are past the end: masked, their loads clamped to a valid row).
+  const int ntw = (seg_hi - seg_lo + TK - 1) / TK;
+  const int nt = MH == 1 ? ntw : 2 * (ntw / 4) + min(ntw % 4, 2);
+  auto tile_key0 = [&](int t) {  // first key of this group's local tile t
+    return seg_lo + TK * (MH == 1 ? t : 4 * (t >> 1) + 2 * half + (t & 1));
+  };
 
   // One tile's registers: bf16 rows in rg[0..3] (rg[j]: key lane / 16 + 4 j of the tile);
   // fp8 rows: the 32 codes of key l16 in rg[0..1] and that key's scale in rg[2].x.
   auto load = [&](uint4(&rg)[4], int t) {
     if constexpr (FP8) {
-      const int key = seg_lo + t * TK + l16;
+      const int key = tile_key0(t) + l16;
       const int kc = key < seg_hi ? key : seg_hi - 1;
       const int slot = key_slot(slot_lo, kc, a.cap);
-      const uint4* cp = cbase + (size_t)slot * (MD / 16) + 8 * wave + lg;
+      const uint4* cp = cbase + (size_t)slot * (MD / 16) + 8 * wsl + lg;
       rg[0] = cp[0];
       rg[1] = cp[4];
       rg[2].x = __float_as_uint(sbase[slot]);  // the scale of this lane's key (l16)
     } else {
-      const int key0 = seg_lo + t * TK + (lane >> 4);
+      const int key0 = tile_key0(t) + (lane >> 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int key = key0 + 4 * j;
@@ -266,7 +287,7 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   };
 
   auto step2 = [&](uint4(&ra)[4], uint4(&rb)[4], int t) {
-    const int k0 = seg_lo + t * TK;
+    const int k0 = tile_key0(t);  // tile b (local t + 1, t even) starts at k0 + TK
     floatx4_t sa, sb;
     if constexpr (FP8) {
       tile_scores_fp8(ra, tile_a, sa);
@@ -290,11 +311,11 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
         sb = mfma_k32(*reinterpret_cast<const uint4*>(rdb + 64 * j), qv[j], sb);
       }
     }
-    s_part[par][wave][0][lane] = sa;
-    s_part[par][wave][1][lane] = sb;
-    if (FP8 && wave == 0 && lg == 0) {  // the keys' row scales, for every wave's logits
-      s_scale[par][0][l16] = __uint_as_float(ra[2].x);
-      s_scale[par][1][l16] = __uint_as_float(rb[2].x);
+    s_part[par][half][wsl][0][lane] = sa;
+    s_part[par][half][wsl][1][lane] = sb;
+    if (FP8 && wsl == 0 && lg == 0) {  // the keys' row scales, for the group's logits
+      s_scale[par][half][0][l16] = __uint_as_float(ra[2].x);
+      s_scale[par][half][1][l16] = __uint_as_float(rb[2].x);
     }
     if constexpr (FP8) {
       load(ra, t + NF);  // unconditional (clamped past the end): keeps wait counts partial
@@ -303,15 +324,15 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     __syncthreads();
     float ka[4] = {1.0f, 1.0f, 1.0f, 1.0f}, kb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
     if constexpr (FP8) {  // scales of the keys 4 lg + 0..3 this lane's logits belong to
-      const float4 a4 = *reinterpret_cast<const float4*>(&s_scale[par][0][4 * lg]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&s_scale[par][1][4 * lg]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&s_scale[par][half][0][4 * lg]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&s_scale[par][half][1][4 * lg]);
       ka[0] = a4.x; ka[1] = a4.y; ka[2] = a4.z; ka[3] = a4.w;
       kb[0] = b4.x; kb[1] = b4.y; kb[2] = b4.z; kb[3] = b4.w;
     }
-    const floatx4_t fa = ((s_part[par][0][0][lane] + s_part[par][1][0][lane]) +
-                          s_part[par][2][0][lane]) + s_part[par][3][0][lane];
-    const floatx4_t fb = ((s_part[par][0][1][lane] + s_part[par][1][1][lane]) +
-                          s_part[par][2][1][lane]) + s_part[par][3][1][lane];
+    const floatx4_t fa = ((s_part[par][half][0][0][lane] + s_part[par][half][1][0][lane]) +
+                          s_part[par][half][2][0][lane]) + s_part[par][half][3][0][lane];
+    const floatx4_t fb = ((s_part[par][half][0][1][lane] + s_part[par][half][1][1][lane]) +
+                          s_part[par][half][2][1][lane]) + s_part[par][half][3][1][lane];
     par ^= 1;
     // softmax: lane holds head l16, keys k0 + 4 lg + i (xa) and k0 + 16 + 4 lg + i (xb)
     float xa[4], xb[4];
@@ -336,11 +357,14 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
       for (int i = 0; i < 8; ++i) acc[i] *= f;
       m = mx;
     }
+    // m stays -inf only while every key so far was masked (the second group's steps past
+    // the end): then every x is -inf and p must be 0, not exp2(-inf + inf)
+    const float mref = m == -INFINITY ? 0.0f : m;
     float pa[4], pb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pa[i] = exp2_fast(xa[i] - m);
-      pb[i] = exp2_fast(xb[i] - m);
+      pa[i] = exp2_fast(xa[i] - mref);
+      pb[i] = exp2_fast(xb[i] - mref);
       l += pa[i] + pb[i];
       if constexpr (FP8) {  // K = V: the value row's scale is the key's
         pa[i] *= ka[i];
@@ -393,19 +417,42 @@ __global__ void __launch_bounds__(MNW * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     if (t + i < nt) step2(buf[i], buf[i + 1], t + i);
 
   app.store(a);
-  // ---- this wave's slice of the result (m and l are identical in every wave)
+  // ---- this wave's slice of the result (m and l are identical in every wave of a group)
   l = rows_sum(l);
+  if constexpr (MH == 2) {
+    // the second group hands (m, l, acc) to the first through its own tile area; the
+    // first group's first key is always valid, so its m is finite
+    floatx4_t* comb = reinterpret_cast<floatx4_t*>(s_kv + (MNW + wsl) * 2 * WAVE_TILE);
+    if (half == 1) {
+      wave_lds_sync();  // this wave's last transposed reads stay before these writes
+#pragma unroll
+      for (int db = 0; db < 8; ++db) comb[db * 64 + lane] = acc[db];
+      if (wsl == 0 && lane < MG) {
+        s_ml[lane][0] = m;
+        s_ml[lane][1] = l;
+      }
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float m1 = s_ml[l16][0], l1 = s_ml[l16][1];
+    const float mx = fmaxf(m, m1);
+    const float f0 = exp2_fast(m - mx), f1 = exp2_fast(m1 - mx);  // m1 = -inf: f1 = 0
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = acc[db] * f0 + comb[db * 64 + lane] * f1;
+    l = l * f0 + l1 * f1;
+    m = mx;
+  }
   if (k_u == 1) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    float* o = a.out + (head0 + l16) * MD + DQ * wave + 4 * lg;
+    float* o = a.out + (head0 + l16) * MD + DQ * wsl + 4 * lg;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db] * inv;
   } else {
     const size_t slot = (size_t)g_id;
-    float* o = a.part_acc + (slot * MG + l16) * MD + DQ * wave + 4 * lg;
+    float* o = a.part_acc + (slot * MG + l16) * MD + DQ * wsl + 4 * lg;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db];
-    if (wave == 0 && lane < MG) {
+    if (wsl == 0 && lane < MG) {
       a.part_ml[(slot * MG + lane) * 2 + 0] = m;
       a.part_ml[(slot * MG + lane) * 2 + 1] = l;
     }
@@ -529,9 +576,9 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
   const unsigned grid =
       (unsigned)(R <= kMfmaBlocks - kMfmaBlocks / 4 ? kMfmaBlocks : kMfmaBlocks + R);
   if (a.fp8)
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(MNW * 64), 0, stream, a);
+    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(NWV * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(MNW * 64), 0, stream, a);
+    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(NWV * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);

@@ -127,13 +127,15 @@ struct AppendRow {
   }
 };
 
-// Matrix-core path limits: units (batch rows x KV heads) per call, and the fixed grid
-// (work-groups of 4 waves, kMfmaBlocksPerCU per CU of an MI355X).
+// Matrix-core path limits: units (batch rows x KV heads) per call, and the fixed grid:
+// work-groups of kMfmaHalves groups of 4 waves, kMfmaBlocksPerCU per CU of an MI355X
+// (8 waves per CU either way).
 constexpr int kMfmaMaxUnits = 1024;
-#ifndef GA_MFMA_BLOCKS_PER_CU
-#define GA_MFMA_BLOCKS_PER_CU 2
+#ifndef GA_MFMA_HALVES
+#define GA_MFMA_HALVES 2
 #endif
-constexpr int kMfmaBlocksPerCU = GA_MFMA_BLOCKS_PER_CU;
+constexpr int kMfmaHalves = GA_MFMA_HALVES;
+constexpr int kMfmaBlocksPerCU = 2 / kMfmaHalves;
 constexpr int kMfmaBlocks = 256 * kMfmaBlocksPerCU;
 
 // Split kernels.  Each launch covers B * Hkv * S work-groups; with S == 1 the split

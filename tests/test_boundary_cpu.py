@@ -134,10 +134,10 @@ def test_workspace_bytes_closed_form():
     assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == \
         16 * 16 * 64 * 514 * 4
     # K = V global geometry: AUTO may pick the matrix-core path, whose workspace is
-    # (512 work-groups + B * Hkv units) partial slots of 16 heads x (512 + 2) floats, plus
-    # B * Hkv + 1 ints of prefix sums; the query covers the larger of the two paths
+    # (256 work-groups, one per CU, + B * Hkv units) partial slots of 16 heads x (512 + 2)
+    # floats, plus B * Hkv + 1 ints of prefix sums; the query covers the larger of the two
     s = shape(B=16, Hq=16, Hkv=1, D=512, cap=32768, kind=api.LINEAR)
-    mfma = (512 + 16) * 16 * 514 * 4 + 17 * 4
+    mfma = (256 + 16) * 16 * 514 * 4 + 17 * 4
     o = api.make_opts(impl=api.IMPL_MFMA)
     assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == mfma
     auto = lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, None)
