@@ -80,6 +80,15 @@ static_assert(2 * WAVE_TILE >= 64 * 8 * 16, "combine area per wave");
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
 
+// Largest value over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return rows_max(x);
+}
+
 __device__ __forceinline__ int chunk_keys(int T, int NB) {
   const int per = (T + NB - 1) / NB;
   return T > 0 ? (per + TK - 1) / TK * TK : TK;
@@ -104,6 +113,7 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   __shared__ floatx4_t s_part[2][MH][MNW][2][64];  // [buffer][group][wave][tile][lane]
   __shared__ __attribute__((aligned(16))) float s_scale[2][MH][2][TK];  // fp8 row scales
   __shared__ float s_ml[MG][2];  // the second group's m and l per head
+  __shared__ float s_norm[2][NWV];  // fp8: per-wave largest key scale and |q|
   // Tiles in flight per wave: four bf16 tiles (64 KiB per work-group); fp8 tiles are half
   // the bytes, so eight keep as many bytes in flight (the loop is latency-bound otherwise).
   constexpr int NF = FP8 ? GA_FP8_TILES : GA_BF16_TILES;
@@ -203,7 +213,8 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   // Q^T operand for this wave's slice, in the order the K rows are loaded: head l16,
   // d = 128 w + 32 j + 8 lg + 0..7 (bf16 rows: 16 bytes per lane and j), or
   // d = 128 w + 64 (j / 2) + 16 lg + 8 (j % 2) + 0..7 (fp8 rows: 16 codes per lane and
-  // pair of j).  Any order of d works as long as K and Q^T share it.
+  // pair of j).  Any order of d works as long as K and Q^T share it.  The fp8 path
+  // converts q to fp16 below, once the work-group's range normalization is known.
   uint4 qv[4];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + (head0 + l16) * MD);
@@ -226,6 +237,7 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f;
+  float p_norm = 1.0f, logit_scale = a.scale;  // fp8 range normalization (set below)
 
   // The work-group's tiles go to the groups in pairs: tiles 4 q, 4 q + 1 to group 0, 4 q + 2,
   // 4 q + 3 to group 1.  Both groups step through group 0's tile count (group 1's extra
@@ -263,16 +275,16 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   // and softmax chains interleave, and one barrier and one max update cover 32 keys.
   // Each tile's rows go to the wave's LDS tile in natural d order (the V operand, and for
   // bf16 also the K operand); a tile's S^T partial over this wave's d slice is K rows
-  // (A operand) times Q^T.  fp8 codes are widened to bf16 first and feed the products
+  // (A operand) times Q^T.  fp8 codes are widened exactly to fp16 and feed the products
   // from registers.
   auto tile_scores_fp8 = [&](const uint4(&rg)[4], char* tile, floatx4_t& s) {
     s = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const uint4 lo = e4m3x8_to_bf16x8(rg[jj].x, rg[jj].y);
-      const uint4 hi = e4m3x8_to_bf16x8(rg[jj].z, rg[jj].w);
-      s = mfma_k32(lo, qv[2 * jj], s);
-      s = mfma_k32(hi, qv[2 * jj + 1], s);
+      const uint4 lo = e4m3x8_to_f16x8(rg[jj].x, rg[jj].y);
+      const uint4 hi = e4m3x8_to_f16x8(rg[jj].z, rg[jj].w);
+      s = mfma_k32_f16(lo, qv[2 * jj], s);
+      s = mfma_k32_f16(hi, qv[2 * jj + 1], s);
       char* w8 = tile + l16 * ROWQ + lg * 32 + jj * 128;  // 16 d per lane and jj
       *reinterpret_cast<uint4*>(w8) = lo;
       *reinterpret_cast<uint4*>(w8 + 16) = hi;
@@ -313,9 +325,9 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     }
     s_part[par][half][wsl][0][lane] = sa;
     s_part[par][half][wsl][1][lane] = sb;
-    if (FP8 && wsl == 0 && lg == 0) {  // the keys' row scales, for the group's logits
-      s_scale[par][half][0][l16] = __uint_as_float(ra[2].x);
-      s_scale[par][half][1][l16] = __uint_as_float(rb[2].x);
+    if (FP8 && wsl == 0 && lg == 0) {  // the keys' row scales (times p_norm), for the group
+      s_scale[par][half][0][l16] = __uint_as_float(ra[2].x) * p_norm;
+      s_scale[par][half][1][l16] = __uint_as_float(rb[2].x) * p_norm;
     }
     if constexpr (FP8) {
       load(ra, t + NF);  // unconditional (clamped past the end): keeps wait counts partial
@@ -339,8 +351,8 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float va = fa[i] * ka[i] * a.scale;  // fp8: the key's row scale
-      float vb = fb[i] * kb[i] * a.scale;
+      float va = fa[i] * ka[i] * logit_scale;  // fp8: the key's row scale
+      float vb = fb[i] * kb[i] * logit_scale;
       if (a.softcap > 0.0f) {
         va = softcap_tanh(va, a.softcap, a.inv_softcap);
         vb = softcap_tanh(vb, a.softcap, a.inv_softcap);
@@ -370,6 +382,21 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
         pa[i] *= ka[i];
         pb[i] *= kb[i];
       }
+    }
+    if constexpr (FP8) {
+      // fp16 operands: V^T exact (widened codes), P^T (p * s * p_norm < 2^15) rounded once
+      // to 11 significant bits
+      const uint4 pf = make_uint4(pack_f16x2(pa[0], pa[1]), pack_f16x2(pa[2], pa[3]),
+                                  pack_f16x2(pb[0], pb[1]), pack_f16x2(pb[2], pb[3]));
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const short4_t va =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_ra + db * 32));
+        const short4_t vb =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_rb + db * 32));
+        acc[db] = mfma_k32_f16(cat4(va, vb), pf, acc[db]);
+      }
+      return;
     }
     // P^T operands (lane: head l16, keys 4 lg + 0..3), split into bf16 hi + lo parts so
     // the probabilities keep ~16 mantissa bits
@@ -404,9 +431,56 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   // run after it, a step's second tile past the end being all masked, so the loop header
   // never sees a path with a buffer's loads still unconsumed (which would make the
   // compiler drain every prefetch there).
+  // fp8 computes in fp16 (every e4m3 value is an fp16 value; products accumulate in fp32).
+  // Two powers of two per work-group keep the fp16 operands in range: q * q_norm with
+  // |q * q_norm| < 2^15, and value weights p * s * p_norm < 2^15 (p <= 2^8 with the lazy
+  // rescale, s * p_norm < 2^7 for every key scale s of the work-group's keys).  The logits
+  // take 1 / (q_norm p_norm) and the result 1 / p_norm back, both exact.  The key scales'
+  // loads go out before the tiles' so that waiting for them leaves the tiles in flight.
+  float sk[4];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = min(seg_lo + tid + r * NWV * 64, seg_hi - 1);
+      sk[r] = sbase[key_slot(slot_lo, key, a.cap)];
+    }
+  }
   uint4 buf[NF][4];
 #pragma unroll
   for (int i = 0; i < NF; ++i) load(buf[i], i);
+  if constexpr (FP8) {
+    float smax = fmaxf(fmaxf(sk[0], sk[1]), fmaxf(sk[2], sk[3]));
+    for (int key = seg_lo + tid + 4 * NWV * 64; key < seg_hi; key += NWV * 64)
+      smax = fmaxf(smax, sbase[key_slot(slot_lo, key, a.cap)]);
+    float qmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+    }
+    smax = wave_max(smax);
+    qmax = wave_max(qmax);
+    if (lane == 0) {
+      s_norm[0][wave] = smax;
+      s_norm[1][wave] = qmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      smax = fmaxf(smax, s_norm[0][w]);
+      qmax = fmaxf(qmax, s_norm[1][w]);
+    }
+    int es, eq;
+    frexpf(smax, &es);  // smax < 2^es (es = 0 for 0)
+    frexpf(qmax, &eq);
+    p_norm = ldexpf(1.0f, 7 - es);
+    const float q_norm = ldexpf(1.0f, 15 - eq);
+    logit_scale = a.scale * ldexpf(1.0f, eq - 15 + es - 7);  // 1 / (q_norm p_norm)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qv[j] = bf16x8_to_f16x8(qv[j], q_norm);
+  }
   int t = 0;
   for (; t + NF - 1 < nt; t += NF) {
 #pragma unroll
@@ -441,6 +515,10 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     for (int db = 0; db < 8; ++db) acc[db] = acc[db] * f0 + comb[db * 64 + lane] * f1;
     l = l * f0 + l1 * f1;
     m = mx;
+  }
+  if constexpr (FP8) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] *= 1.0f / p_norm;  // exact: a power of two
   }
   if (k_u == 1) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;

@@ -33,6 +33,33 @@ __device__ __forceinline__ floatx4_t mfma_k32(const uint4& a, const uint4& b, fl
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_16x16x32_f16: the same operand layouts as the bf16 product.
+__device__ __forceinline__ floatx4_t mfma_k32_f16(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> an fp16 pair, rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
+}
+
+// Eight bf16 values times a power of two -> fp16.  Exact while the scaled magnitude is in
+// [2^-14, 65504] (a bf16 value has 8 significant bits, fp16 11); smaller ones become fp16
+// subnormals (absolute error below 2^-24), larger ones saturate at 65504 (round toward
+// zero never makes an inf).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w, float pow2) {
+  auto cv = [pow2](uint32_t x) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x << 16) * pow2,
+                                                         __uint_as_float(x & 0xffff0000u) * pow2));
+  };
+  return make_uint4(cv(w.x), cv(w.y), cv(w.z), cv(w.w));
+}
 
 __device__ __forceinline__ floatx4_t mfma_k32(u32x4_t a, u32x4_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -53,7 +80,19 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                     __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
-// Two 4 x bf16 operand halves -> one 8 x bf16 operand (lo in k slots 0..3).
+// Eight e4m3 codes (code i in byte i of w0, w1) -> eight fp16 values, exactly: every e4m3
+// value (3 mantissa bits, exponents 2^-9 .. 2^8) is an fp16 value.  One
+// v_cvt_scalef32_pk_f16_fp8 (scale 1) widens two codes.
+__device__ __forceinline__ uint4 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
+// Two 4 x 16-bit operand halves -> one 8 x 16-bit operand (lo in k slots 0..3).
 __device__ __forceinline__ uint4 cat4(short4_t lo, short4_t hi) {
   const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   return make_uint4(a.x, a.y, b.x, b.y);

@@ -4,6 +4,8 @@ bit, and decode (one or several query tokens) against the fp64 oracle over the s
 Parity cases poison every slot outside the valid set: codes 0x7f (NaN) and scale NaN, so
 a stray read turns the output NaN.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -12,7 +14,7 @@ import oracle
 from decode_attention_split_amd import api, synth
 from decode_attention_split_amd import workloads as wl
 
-from common import assert_parity, default_scale, errors, log
+from common import assert_parity, default_scale, errors, f32, log
 
 pytestmark = pytest.mark.gpu
 
@@ -224,6 +226,39 @@ def test_fp8_global_matrix_cores_match_vector_kernel_and_oracle(kind):
         for impl in [api.IMPL_MFMA, api.IMPL_VALU]:
             out = inp.run(window, softcap, default_scale(D), kind, max_ctx=max_ctx, impl=impl)
             assert_parity(out, ref, f"fp8 global kind={kind} softcap={softcap} impl={impl}")
+
+
+@pytest.mark.parametrize("s_lo,s_hi,q_pow2", [
+    (1e-7, 2e-7, 0),    # quiet rows: p * s far below fp16's normal range unless normalized
+    (50.0, 400.0, 0),   # loud rows: p * s * 448 far beyond fp16's range unless normalized
+    (1e-4, 0.4, 0),     # row scales spanning 2^12 inside one unit
+    (0.002, 0.02, 16),  # |q| up to ~2^18: beyond fp16's range unless normalized
+    (0.002, 0.02, -24),  # |q| ~ 2^-24: fp16 subnormals unless normalized
+])
+def test_fp8_global_matrix_cores_extreme_ranges(s_lo, s_hi, q_pow2):
+    """The matrix-core fp8 path multiplies in fp16 (exact for e4m3 codes) and keeps q and
+    the value weights p * s in fp16's range with powers of two per work-group; row scales
+    and query magnitudes far from 1 must still match the oracle.  The attention scale keeps
+    the logits near unit size (scaled q comes with the inverse scale, an exact power of
+    two), and both outputs are divided by the largest reference value before the usual
+    tolerances apply, since those are absolute."""
+    Hkv, D, cap = 1, 512, 4096
+    ctx = [1, 700, 2500, 4096]
+    inp = Fp8Inputs(777, len(ctx), 1, 16, Hkv, D, cap, True, ctx)
+    rng = np.random.default_rng(778)
+    inp.ks = np.exp(rng.uniform(np.log(s_lo), np.log(s_hi), inp.ks.shape)).astype(np.float32)
+    att = f32(1.0 / (math.sqrt(D) * 120.0 * math.sqrt(s_lo * s_hi)))
+    if q_pow2:
+        q = synth.from_bits(inp.q_bits, "cpu").float() * 2.0 ** q_pow2
+        inp.q_bits = synth.bits(q.to(torch.bfloat16))
+        att = f32(att * 2.0 ** -q_pow2)
+    inp.to_device()
+    ref, _ = inp.oracle(0, 0.0, att, api.LINEAR)
+    out = inp.run(0, 0.0, att, api.LINEAR, max_ctx=cap, impl=api.IMPL_MFMA)
+    big = float(np.abs(ref).max())
+    assert big > 0
+    assert_parity(out.double().cpu().numpy() / big, ref / big,
+                  f"fp8 global extreme ranges s=[{s_lo}, {s_hi}] q*2^{q_pow2}")
 
 
 def test_fp8_global_layer_full_size_sampled_rows():
