@@ -8,17 +8,22 @@
 // work-group of four waves (two at head_dim 512) owns one split (a run of keys of one
 // unit = batch row, KV head, chunk of tokens); its waves take the split's 16-key tiles in
 // turn (wave w: tiles w, w + 4, ...), each with its own softmax state.  Per tile:
+//   the tile's K and V rows are loaded with every instruction covering whole rows (whole
+//     128-byte lines, non-temporal), then written to the wave's LDS tiles in natural d order
+//     (fp8 codes widened exactly to bf16 on the way);
 //   S^T[16 keys][16 rows] = K[16][D] . Q^T[D][16]: D / 32 v_mfma_f32_16x16x32_bf16, the
-//     K operand loaded straight from HBM (lane: key l16, d = 8 lg + 32 j + 0..7), Q^T read
+//     K operand read back from the K tile (lane: key l16, d = 8 lg + 32 j + 0..7), Q^T read
 //     from LDS (shared by the waves) in the same d order;
 //   S^T leaves lane l holding row l16 for keys 4 lg + 0..3, which is exactly the B operand
 //     of the P.V product, so the softmax works in place (row max / sum over the four lane
 //     groups) and P goes to the matrix cores as bf16 hi + lo parts (~16 mantissa bits);
-//   the V rows go to the wave's LDS tile once and come back transposed with
-//     ds_read_b64_tr_b16 as the A operand of O^T[D][16] += V^T[D][16 keys] .
-//     P^T[16 keys][16 rows]: D / 16 pairs of v_mfma_f32_16x16x16_bf16.
-// One register buffer each for K and V, refilled as soon as a tile's products have used it
-// (eight waves per CU hide the latency).  At the end the waves merge through LDS, so a
+//   the V tile comes back transposed with ds_read_b64_tr_b16 as the A operand of
+//     O^T[D][16] += V^T[D][16 keys] . P^T[16 keys][16 rows]: D / 16 pairs of
+//     v_mfma_f32_16x16x16_bf16 (with K = V one tile serves both products).
+// One register buffer each for K and V, refilled as soon as the tile's rows are in LDS
+// (eight waves per CU hide the latency).  Loading each key's row in 16-byte pieces straight
+// into the K operand (lane l16 = key) reads half lines per instruction and streamed at
+// 5.45 TB/s on the spec-decode layer; whole-row loads stream faster.  At the end the waves merge through LDS, so a
 // split is one partial: with one split per unit (batches that fill the chip) the output is
 // written directly and no merge kernel runs; otherwise each split leaves (m, l, acc) for
 // the log-sum-exp merge.  (A merge by the last split to arrive would need a device-scope
@@ -38,6 +43,9 @@ namespace ga {
 namespace {
 
 constexpr float kRescaleLog2R16 = 8.0f;
+#ifndef GA_ROWS16_BUFS
+#define GA_ROWS16_BUFS 1
+#endif
 
 template <int D>
 constexpr int rows16_waves() { return D == 512 ? 2 : 4; }
@@ -51,7 +59,8 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   constexpr int QROWB = D * 2 + 16;      // LDS bytes per query row
   constexpr int Q_BYTES = 16 * QROWB;
   constexpr int TILE_BYTES = 16 * ROWB;
-  constexpr int LOOP_BYTES = Q_BYTES + NW * TILE_BYTES;  // Q rows + one V tile per wave
+  constexpr int NTILES = KV_SHARED ? 1 : 2;                       // K (and V) tile per wave
+  constexpr int LOOP_BYTES = Q_BYTES + NW * NTILES * TILE_BYTES;  // Q rows + the tiles
   constexpr int ACC_BYTES = NW * 16 * D * 4;             // the waves' accumulators (end)
   __shared__ __attribute__((aligned(16))) char s_mem[LOOP_BYTES > ACC_BYTES ? LOOP_BYTES
                                                                             : ACC_BYTES];
@@ -116,15 +125,18 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
       *reinterpret_cast<u32x4_t*>(s_q + l16 * QROWB + (lg + 4 * j) * 16) = qp[4 * j + lg];
   }
   const char* q_lds = s_q + l16 * QROWB + lg * 16;
-  char* tile = s_mem + Q_BYTES + wave * TILE_BYTES;  // this wave's V tile
+  char* ktile = s_mem + Q_BYTES + wave * NTILES * TILE_BYTES;  // this wave's K tile
+  char* tile = ktile + (NTILES - 1) * TILE_BYTES;              // and V tile (K = V: the same)
   const size_t row0 = (size_t)(b * a.Hkv + g) * a.cap;
   // (native 4 x u32 vectors: arrays of them stay in registers)
   // Cache rows in 16-byte chunks: bf16 rows hold D / 8, fp8 rows D / 16 (16 codes each).
-  // A lane's chunks of a row: bf16 d = 32 j + 8 lg + 0..7 (product j); fp8 codes
-  // d = 64 jj + 16 lg + 0..15, which serve products 2 jj and 2 jj + 1 (Q^T is read from
-  // LDS in the same order).
+  // A load instruction covers KPI whole rows: lane reads chunk lane % ROW16 of key
+  // lane / ROW16 + KPI j of the tile (NL loads per lane and tile).
   constexpr int ROW16 = FP8 ? D / 16 : D / 8;
-  constexpr int NL = FP8 ? NJ / 2 : NJ;  // 16-byte loads per lane per row
+  static_assert(64 % ROW16 == 0, "rows per load instruction");
+  constexpr int KPI = 64 / ROW16;
+  constexpr int NL = 16 / KPI;
+  const int lrow = lane / ROW16, lcol = lane % ROW16;
   const void* kmem = FP8 ? (const void*)a.k8 : (const void*)a.k;
   const void* vmem = FP8 ? (const void*)(KV_SHARED ? a.k8 : a.v8)
                          : (const void*)(KV_SHARED ? a.k : a.v);
@@ -140,78 +152,72 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
 
   // tiles of 16 keys; wave w takes tiles w, w + NW, ... of the split (a fixed order)
   const int nt = (k_end - k_begin + 15) / 16;
-  u32x4_t kr[NL], vr[KV_SHARED ? 1 : NL];
-  float ksc = 1.0f, vsc = 1.0f;  // fp8: the row scales of this lane's key (l16)
-  // key k_begin + 16 t + l16 of the tile (past the end: re-read the last valid key)
-  auto key_slot_of = [&](int t) {
-    const int i = k_begin + 16 * t + l16;
-    return key_slot(r, i < k_end ? i : k_end - 1, a.cap);
+  // one tile's registers: its K (and V) row pieces, and (fp8) the row scales of key l16
+  struct Regs {
+    u32x4_t k[NL], v[KV_SHARED ? 1 : NL];
+    float ks, vs;
   };
-  auto load_k = [&](int t) {
-    const int slot = key_slot_of(t);
-    const u32x4_t* p = kbase + (size_t)slot * ROW16 + lg;
+  // slot of key i of the split (past the end: the last valid key, re-read)
+  auto slot_at = [&](int i) { return key_slot(r, i < k_end ? i : k_end - 1, a.cap); };
+  auto load = [&](Regs& rg, int t) {
+    const int k0 = k_begin + 16 * t;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) kr[j] = p[4 * j];
-    if constexpr (FP8) {
-      ksc = kscale[slot];
-      vsc = KV_SHARED ? ksc : vscale[slot];
-    }
-  };
-  auto load_v = [&](int t) {
+    for (int j = 0; j < NL; ++j)
+      rg.k[j] = stream_load(kbase + (size_t)slot_at(k0 + lrow + KPI * j) * ROW16 + lcol);
     if constexpr (!KV_SHARED) {
-      const u32x4_t* p = vbase + (size_t)key_slot_of(t) * ROW16 + lg;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) vr[j] = p[4 * j];
+      for (int j = 0; j < NL; ++j)
+        rg.v[j] = stream_load(vbase + (size_t)slot_at(k0 + lrow + KPI * j) * ROW16 + lcol);
+    }
+    if constexpr (FP8) {
+      const int slot = slot_at(k0 + l16);
+      rg.ks = kscale[slot];
+      rg.vs = KV_SHARED ? rg.ks : vscale[slot];
     }
   };
-  const int t0 = wave < nt ? wave : nt - 1;  // a wave without tiles loads a valid one
-  load_k(t0);
-  load_v(t0);
+  // a loaded row piece to its LDS tile (fp8 codes widened exactly to bf16)
+  auto put = [&](char* dst, int j, const u32x4_t& x) {
+    char* row = dst + (lrow + KPI * j) * ROWB;
+    if constexpr (FP8) {
+      *reinterpret_cast<uint4*>(row + lcol * 32) = e4m3x8_to_bf16x8(x.x, x.y);
+      *reinterpret_cast<uint4*>(row + lcol * 32 + 16) = e4m3x8_to_bf16x8(x.z, x.w);
+    } else {
+      *reinterpret_cast<u32x4_t*>(row + lcol * 16) = x;
+    }
+  };
+  // NB tiles in flight per wave: wave w's i-th tile t = w + NW i sits in regs[i % NB]
+  constexpr int NB = GA_ROWS16_BUFS;
+  Regs regs[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) load(regs[i], min(wave + NW * i, nt - 1));
   __syncthreads();  // the Q rows are in LDS
 
-  for (int t = wave; t < nt; t += NW) {
+  auto step = [&](Regs& rg, int t) {
     const int k0 = k_begin + 16 * t;
-    // S^T for the tile
-    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+    // the tile's rows to LDS, then the registers refill with the wave's tile NB ahead
+#pragma unroll
+    for (int j = 0; j < NL; ++j) put(ktile, j, rg.k[j]);
+    if constexpr (!KV_SHARED) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) put(tile, j, rg.v[j]);
+    }
     if constexpr (FP8) {
-      // codes widened exactly to bf16; the V rows (widened) go to LDS in natural d order
-      const char* q8 = s_q + l16 * QROWB + lg * 32;
-      char* w8 = tile + l16 * ROWB + lg * 32;
-#pragma unroll
-      for (int jj = 0; jj < NL; ++jj) {
-        const uint4 lo = e4m3x8_to_bf16x8(kr[jj].x, kr[jj].y);
-        const uint4 hi = e4m3x8_to_bf16x8(kr[jj].z, kr[jj].w);
-        s = mfma_k32(lo, *reinterpret_cast<const uint4*>(q8 + jj * 128), s);
-        s = mfma_k32(hi, *reinterpret_cast<const uint4*>(q8 + jj * 128 + 16), s);
-        if constexpr (KV_SHARED) {
-          *reinterpret_cast<uint4*>(w8 + jj * 128) = lo;
-          *reinterpret_cast<uint4*>(w8 + jj * 128 + 16) = hi;
-        } else {
-          *reinterpret_cast<uint4*>(w8 + jj * 128) = e4m3x8_to_bf16x8(vr[jj].x, vr[jj].y);
-          *reinterpret_cast<uint4*>(w8 + jj * 128 + 16) = e4m3x8_to_bf16x8(vr[jj].z, vr[jj].w);
-        }
-      }
       if (lg == 0) {  // the tile's row scales, read back per key 4 lg + i after the sync
-        s_scl[wave][0][l16] = ksc;
-        s_scl[wave][1][l16] = vsc;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        s = mfma_k32(kr[j], *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
-      // V rows of the tile to LDS (key l16, d = 8 lg + 32 j), then refill the registers
-      char* w = tile + l16 * ROWB + lg * 16;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if constexpr (KV_SHARED)
-          *reinterpret_cast<u32x4_t*>(w + j * 64) = kr[j];
-        else
-          *reinterpret_cast<u32x4_t*>(w + j * 64) = vr[j];
+        s_scl[wave][0][l16] = rg.ks;
+        s_scl[wave][1][l16] = rg.vs;
       }
     }
-    load_k(t + NW < nt ? t + NW : t);
-    load_v(t + NW < nt ? t + NW : t);
-    wave_lds_sync();  // the tile's LDS writes before its transposed reads
+    load(rg, t + NB * NW < nt ? t + NB * NW : t);
+    wave_lds_sync();  // the tile's LDS writes before the reads below
+    // S^T for the tile: K rows from the K tile (key l16, d = 32 j + 8 lg + 0..7)
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+    {
+      const char* kq_lds = ktile + l16 * ROWB + lg * 16;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        s = mfma_k32(*reinterpret_cast<const u32x4_t*>(kq_lds + j * 64),
+                     *reinterpret_cast<const u32x4_t*>(q_lds + j * 64), s);
+    }
 
     // softmax: lane holds row l16, keys k0 + 4 lg + i
     float kq[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vq[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -261,6 +267,12 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
       acc[db] = mfma_k16(va, pl, acc[db]);
     }
     wave_lds_sync();  // the tile's transposed reads stay before the next tile's writes
+  };
+  for (int t = wave; t < nt; t += NB * NW) {
+    step(regs[0], t);
+#pragma unroll
+    for (int i = 1; i < NB; ++i)
+      if (t + NW * i < nt) step(regs[i], t + NW * i);
   }
 
   // Merge the waves: each leaves (m, l) per row and acc (row l16, d = 16 db + 4 lg + i)
