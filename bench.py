@@ -44,6 +44,11 @@ def parse_args():
                    help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
+    p.add_argument("--counter-kernel", default="",
+                   help="with --summarize-counters: kernel name substring (default: the "
+                        "dominant sliding decode kernel)")
+    p.add_argument("--summarize-sq", nargs="+", metavar="PMC_CSV",
+                   help="print per-kernel SQ counter averages of rocprofv3 --pmc runs and exit")
     p.add_argument("--command", default="", help="command line recorded in summaries")
     p.add_argument("--workload", default="hybrid48",
                    choices=sorted(SINGLE_LAYER) + ["hybrid48", "hybrid48_rope"],
@@ -135,9 +140,10 @@ def summarize_trace(path, command):
               f"{float(r['Percentage']):.2f} |")
 
 
-def summarize_counters(fetch_csv, write_csv, command):
-    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and WRITE_SIZE runs (KiB
-    per dispatch), each scaled by what the counter reads for the 1 GiB calibration copy."""
+def summarize_counters(fetch_csv, write_csv, command, kernel=""):
+    """HBM bytes per launch of the dominant kernel (or of `kernel`) from FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the counter reads for the 1 GiB
+    calibration copy."""
     import csv
 
     def per_kernel(path, counter):
@@ -156,10 +162,11 @@ def summarize_counters(fetch_csv, write_csv, command):
         return COPY_BYTES / (sum(copies) / len(copies))
 
     f_scale, w_scale = calib(fetch), calib(write)
-    dom = [k for k in fetch if DOMINANT in k]
+    dom = [k for k in fetch if (kernel or DOMINANT) in k]
     f = sum(sum(fetch[k]) for k in dom) / sum(len(fetch[k]) for k in dom)
     w = sum(sum(write[k]) for k in dom) / sum(len(write[k]) for k in dom)
-    print("# HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    what = "the dominant kernel" if not kernel else "one kernel"
+    print(f"# HBM traffic of {what} (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     print(f"command: {command}")
     print(f"kernel: {dom[0][:100] if dom else 'n/a'}")
     print(f"fetch_calibration (1 GiB copy bytes / counter bytes): {f_scale:.4f}")
@@ -171,13 +178,51 @@ def summarize_counters(fetch_csv, write_csv, command):
     print(f"sources_sha256: {sources_digest(TRAFFIC_SOURCES)}")
 
 
+def summarize_sq(csvs, command):
+    """Per-kernel averages (over dispatches, summed over the chip) of the SQ counters in
+    rocprofv3 --pmc runs, with the ratios that say where waves spend their cycles."""
+    import csv
+    vals = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            k = r["Kernel_Name"]
+            if not k.startswith("void ga::") and not k.startswith("ga::"):
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    print("# SQ counters per dispatch (rocprofv3 --pmc, summed over the chip, averaged)")
+    print(f"command: {command}")
+    for k, cs in vals.items():
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        print(f"\nkernel: {k[:100]}  (dispatches per counter: {n})")
+        for c in sorted(avg):
+            print(f"  {c:28s} {avg[c]:.4g}")
+        cyc = avg.get("SQ_WAVE_CYCLES")
+        if cyc:
+            ratio = lambda c: f"{avg[c] / cyc:.2f}" if c in avg else "n/a"
+            print(f"  derived: waiting to issue (WAIT_INST_ANY / WAVE_CYCLES) "
+                  f"{ratio('SQ_WAIT_INST_ANY')}; waiting on counters or barriers (WAIT_ANY / "
+                  f"WAVE_CYCLES) {ratio('SQ_WAIT_ANY')}; VALU issue (ACTIVE_INST_VALU / "
+                  f"WAVE_CYCLES) {ratio('SQ_ACTIVE_INST_VALU')}")
+        if avg.get("SQ_INSTS_LDS"):
+            print(f"  derived: LDS bank-conflict cycles per LDS instruction "
+                  f"{avg.get('SQ_LDS_BANK_CONFLICT', 0) / avg['SQ_INSTS_LDS']:.2f}")
+        if avg.get("SQ_INSTS_MFMA"):
+            print(f"  derived: VALU instructions per MFMA "
+                  f"{avg.get('SQ_INSTS_VALU', 0) / avg['SQ_INSTS_MFMA']:.1f}")
+
+
 def main():
     args = parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.command)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.command)
+        summarize_counters(*args.summarize_counters, args.command, args.counter_kernel)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.command)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "

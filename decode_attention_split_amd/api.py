@@ -54,12 +54,19 @@ def make_opts(split_keys=0, impl=IMPL_AUTO, deterministic=False):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # the prototypes declare c_void_p: a plain int converts without building an object
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream_handle(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:  # the current stream's handle without a Stream object
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _need(t, name, dtype, ndim=None, device=True):
@@ -127,13 +134,15 @@ def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, work
         if tuple(out.shape) != (shape.batch, shape.num_q_heads, shape.head_dim):
             raise ValueError("out must be [B, Hq, D]")
     opts = make_opts(split_keys, impl, deterministic)
-    lib = _lib.load()
-    need = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window), ctypes.byref(opts))
-    if need == ctypes.c_size_t(-1).value:
-        need = 0  # let the library report the precise error
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
-    if workspace is not None:
+    if workspace is None:  # a given workspace is checked against its size by the library
+        lib = _lib.load()
+        need = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window),
+                                             ctypes.byref(opts))
+        if need == ctypes.c_size_t(-1).value:
+            need = 0  # let the library report the precise error
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    else:
         _need(workspace, "workspace", torch.uint8, 1)
     return shape, out, opts, workspace
 
@@ -214,13 +223,14 @@ def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: flo
             raise ValueError("out must be [B, T, Hq, D]")
     opts = make_opts(split_keys, impl, deterministic)
     lib = _lib.load()
-    need = lib.ga_decode_multi_workspace_bytes(ctypes.byref(shape), int(T), int(window),
-                                               ctypes.byref(opts))
-    if need == ctypes.c_size_t(-1).value:
-        need = 0  # let the library report the precise error
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
-    if workspace is not None:
+    if workspace is None:  # a given workspace is checked against its size by the library
+        need = lib.ga_decode_multi_workspace_bytes(ctypes.byref(shape), int(T), int(window),
+                                                   ctypes.byref(opts))
+        if need == ctypes.c_size_t(-1).value:
+            need = 0  # let the library report the precise error
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    else:
         _need(workspace, "workspace", torch.uint8, 1)
     ws_bytes = 0 if workspace is None else workspace.numel()
     rc = lib.gemma_attn_decode_multi(
@@ -341,13 +351,14 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos, window:
             raise ValueError(f"out must be {list(want)}")
     opts = make_opts(split_keys, impl, deterministic)
     lib = _lib.load()
-    need = lib.ga_decode_fp8_workspace_bytes(ctypes.byref(shape), int(T), int(window),
-                                             ctypes.byref(opts))
-    if need == ctypes.c_size_t(-1).value:
-        need = 0  # let the library report the precise error
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
-    if workspace is not None:
+    if workspace is None:  # a given workspace is checked against its size by the library
+        need = lib.ga_decode_fp8_workspace_bytes(ctypes.byref(shape), int(T), int(window),
+                                                 ctypes.byref(opts))
+        if need == ctypes.c_size_t(-1).value:
+            need = 0  # let the library report the precise error
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    else:
         _need(workspace, "workspace", torch.uint8, 1)
     ws_bytes = 0 if workspace is None else workspace.numel()
     rc = lib.gemma_attn_decode_fp8(
