@@ -80,15 +80,6 @@ static_assert(2 * WAVE_TILE >= 64 * 8 * 16, "combine area per wave");
 static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
 
 
-// Largest value over the 64 lanes of a wave, in every lane.
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
-  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  x = fmaxf(x, dpp<kDppMirror>(x));
-  return rows_max(x);
-}
-
 __device__ __forceinline__ int chunk_keys(int T, int NB) {
   const int per = (T + NB - 1) / NB;
   return T > 0 ? (per + TK - 1) / TK * TK : TK;
@@ -472,12 +463,9 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
       smax = fmaxf(smax, s_norm[0][w]);
       qmax = fmaxf(qmax, s_norm[1][w]);
     }
-    int es, eq;
-    frexpf(smax, &es);  // smax < 2^es (es = 0 for 0)
-    frexpf(qmax, &eq);
-    p_norm = ldexpf(1.0f, 7 - es);
-    const float q_norm = ldexpf(1.0f, 15 - eq);
-    logit_scale = a.scale * ldexpf(1.0f, eq - 15 + es - 7);  // 1 / (q_norm p_norm)
+    p_norm = pow2_norm(smax, 7);
+    const float q_norm = pow2_norm(qmax, 15);
+    logit_scale = a.scale / (q_norm * p_norm);  // exact: powers of two
 #pragma unroll
     for (int j = 0; j < 4; ++j) qv[j] = bf16x8_to_f16x8(qv[j], q_norm);
   }

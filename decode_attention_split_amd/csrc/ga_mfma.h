@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ga_device.h"
+
 namespace ga {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -109,6 +111,31 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_f16: the layouts of the bf16 16x16x16 product.
+__device__ __forceinline__ floatx4_t mfma_k16_f16(short4_t a, short4_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                               __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+}
+
+// Largest value over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return rows_max(x);
+}
+
+// fp16 range normalization for fp8 caches: the power of two n with |x * n| < 2^target for
+// every |x| <= xmax (n = 2^(target - e), xmax < 2^e; 2^target for xmax = 0).
+__device__ __forceinline__ float pow2_norm(float xmax, int target) {
+  int e;
+  frexpf(xmax, &e);
+  return ldexpf(1.0f, target - e);
 }
 
 }  // namespace ga

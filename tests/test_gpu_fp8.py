@@ -261,6 +261,33 @@ def test_fp8_global_matrix_cores_extreme_ranges(s_lo, s_hi, q_pow2):
                   f"fp8 global extreme ranges s=[{s_lo}, {s_hi}] q*2^{q_pow2}")
 
 
+@pytest.mark.parametrize("s_lo,s_hi,q_pow2", [
+    (1e-7, 2e-7, 0), (50.0, 400.0, 0), (1e-4, 0.4, 0), (0.002, 0.02, 16), (0.002, 0.02, -24),
+])
+def test_fp8_multi_token_matrix_cores_extreme_ranges(s_lo, s_hi, q_pow2):
+    """The multi-token matrix-core fp8 path (16 query rows per KV head: 2 heads x 8 tokens,
+    separate K and V): K and V row scales and query magnitudes far from 1 must still match
+    the oracle (compared after dividing by the largest reference value)."""
+    B, T, Hq, Hkv, D, cap = 3, 8, 4, 2, 256, 300
+    ctx = [9, 150, 300]
+    inp = Fp8Inputs(779, B, T, Hq, Hkv, D, cap, False, ctx)
+    rng = np.random.default_rng(780)
+    draw = lambda shape: np.exp(rng.uniform(np.log(s_lo), np.log(s_hi), shape)).astype(np.float32)
+    inp.ks, inp.vs = draw(inp.ks.shape), draw(inp.vs.shape)
+    att = f32(1.0 / (math.sqrt(D) * 120.0 * math.sqrt(s_lo * s_hi)))
+    if q_pow2:
+        q = synth.from_bits(inp.q_bits, "cpu").float() * 2.0 ** q_pow2
+        inp.q_bits = synth.bits(q.to(torch.bfloat16))
+        att = f32(att * 2.0 ** -q_pow2)
+    inp.to_device()
+    ref, _ = inp.oracle(0, 0.0, att, api.LINEAR)
+    out = inp.run(0, 0.0, att, api.LINEAR, max_ctx=cap, impl=api.IMPL_MFMA)
+    big = float(np.abs(ref).max())
+    assert big > 0
+    assert_parity(out.double().cpu().numpy() / big, ref / big,
+                  f"fp8 multi-token extreme ranges s=[{s_lo}, {s_hi}] q*2^{q_pow2}")
+
+
 def test_fp8_global_layer_full_size_sampled_rows():
     """The 12B global layer (B 16, 16q/1kv K = V hd512, linear C 32768, ctx U[4096, 32768])
     on an fp8 cache filled by quantizing appends of every valid position; the automatic
