@@ -250,8 +250,10 @@ int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* 
  * global geometry (head_dim 512, 16 query heads per KV head) runs on the matrix cores;
  * with several tokens, 16 query rows per KV head (heads x tokens >= 8; head_dim 128 or
  * 256, or 512 with K = V) run on the matrix cores; there the codes are widened exactly
- * to bf16 in registers, the K scale multiplies each logit and the V scale each value
- * weight.  Every other shape runs on the vector kernel (GA_IMPL_MFMA is refused there).
+ * (to fp16 on the global geometry, with q and the value weights brought into fp16's range
+ * by powers of two per work-group; to bf16 for several tokens), the K scale multiplies
+ * each logit and the V scale each value weight.  Every other shape runs on the vector
+ * kernel (GA_IMPL_MFMA is refused there).
  * Workspace: ga_decode_fp8_workspace_bytes (covers whichever kernel the call picks).
  */
 size_t ga_decode_fp8_workspace_bytes(const ga_shape* shape, int32_t num_tokens, int32_t window,
