@@ -454,3 +454,32 @@ def test_decode_append_equals_append_then_decode(case):
     host = LayerInputs(inp.q_bits, synth.bits(k1), None if k_eq_v else synth.bits(v1), ctx,
                        inp.qpos)
     assert_parity(got, oracle_out(host, window, 20.0, scale, kind), f"decode_append {case}")
+
+
+def test_binding_passes_a_small_workspace_to_the_library_which_refuses_it():
+    """A caller-given workspace is not re-checked by the binding: the library compares it
+    with what the plan needs and refuses a short one before launching anything (for the
+    single-token, multi-token and fp8 entry points)."""
+    B, Hq, Hkv, D, cap = 2, 16, 8, 256, 4096
+    g = synth.generator(71, device="cuda")
+    q = synth.normal_bf16(g, (B, Hq, D), "cuda")
+    k = synth.normal_bf16(g, (B, Hkv, cap, D), "cuda")
+    ctx = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+    small = torch.empty((16,), dtype=torch.uint8, device="cuda")
+    shape = api.shape_of(q, k, api.LINEAR, cap)
+    assert api.workspace_bytes(shape, 0) > small.numel()  # 16 units over 8 splits
+    with pytest.raises(api.GemmaAttnError) as e:
+        api.decode(q, k, k, ctx, ctx - 1, 0, 0.0, default_scale(D), api.LINEAR,
+                   workspace=small, max_ctx=cap)
+    assert e.value.code == -7
+    with pytest.raises(api.GemmaAttnError) as e:
+        api.decode_multi(q[:, None].contiguous(), k, k, ctx, ctx - 1, 0, 0.0, default_scale(D),
+                         api.LINEAR, workspace=small, max_ctx=cap)
+    assert e.value.code == -7
+    codes = torch.zeros((B, Hkv, cap, D), dtype=torch.uint8, device="cuda")
+    scales = torch.ones((B, Hkv, cap), dtype=torch.float32, device="cuda")
+    with pytest.raises(api.GemmaAttnError) as e:
+        api.decode_fp8(q, codes, scales, codes, scales, ctx, ctx - 1, 0, 0.0, default_scale(D),
+                       api.LINEAR, workspace=small, max_ctx=cap)
+    assert e.value.code == -7
+    torch.cuda.synchronize()
