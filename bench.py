@@ -113,6 +113,7 @@ TRAFFIC_SOURCES = ["decode_attention_split_amd/csrc/decode_valu_impl.h",
                    "decode_attention_split_amd/csrc/decode_valu_d256.hip",
                    "decode_attention_split_amd/csrc/ga_device.h",
                    "decode_attention_split_amd/csrc/ga_internal.h",
+                   "decode_attention_split_amd/csrc/ga_rope.h",
                    "decode_attention_split_amd/csrc/api.hip"]
 DOMINANT = "decode_valu_kernel<256, 2"
 COPY_BYTES = 1 << 30
@@ -290,10 +291,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        if rope:  # per layer: fused rotary + append, then decode with the rotated q
-            for li in range(L):
-                cache.rope_append(li, qs[li], q_rot[li], k_new[li], v_new[li], pos_t)
-                cache.decode(li, q_rot[li], ctx_t, qpos_t, out=outs[li])
+        if rope:  # per layer: rotary + append + decode in one call (see HybridKVCache.step)
+            cache.step(qs, k_new, v_new, pos_t, ctx_t, qpos_t, outs, q_rot=q_rot)
             return
         # per layer, one launch: append the current token to the cache and attend
         for li in range(L):
@@ -339,18 +338,25 @@ def main():
     kern_steps = max(1, args.steps)
     k0 = torch.cuda.Event(enable_timing=True)
     k1 = torch.cuda.Event(enable_timing=True)
+    tables = cache.rope_tables(pos_t) if rope else {}
     torch.cuda.synchronize()
     k0.record(stream)
     for _ in range(kern_steps):
         for li in sliding:
-            cache.decode_append(li, qs[li], k_new[li], v_new[li], pos_t, ctx_t, qpos_t,
-                                out=outs[li])
+            if rope:
+                g = w.layers[li]
+                cache.decode_rope_append(li, qs[li], q_rot[li], k_new[li], v_new[li], pos_t,
+                                         ctx_t, qpos_t, tables[(g.rope_base, g.rotary_dim)],
+                                         out=outs[li])
+            else:
+                cache.decode_append(li, qs[li], k_new[li], v_new[li], pos_t, ctx_t, qpos_t,
+                                    out=outs[li])
     k1.record(stream)
     torch.cuda.synchronize()
     n_launch = kern_steps * len(sliding)
     kern_ms = k0.elapsed_time(k1) / n_launch
-    kern_bytes = float(np.mean([sum(layer_bytes(w.layers[li], B, ctx)[k]
-                                    for k in ("decode", "append")) for li in sliding]))
+    kern_bytes = float(np.mean([per_layer[li]["decode"] + per_layer[li]["append"]
+                                for li in sliding]))
     kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"sliding decode kernel: {kern_ms * 1e3:.2f} us avg over {n_launch} launches, "
         f"{kern_gbps:.1f} GB/s")
@@ -387,13 +393,16 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "layer_tokens_per_s": round(B * L / (ms_step * 1e-3), 1),
         "roofline": {
-            "kernel": "sliding-layer fused append + decode (hd256, 16q/8kv, ring 1024), per launch",
+            "kernel": ("sliding-layer fused RoPE + append + decode" if rope else
+                       "sliding-layer fused append + decode") +
+                      " (hd256, 16q/8kv, ring 1024), per launch",
             "bound": "hbm",
             "achieved": round(kern_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": read_traffic("sliding_decode_hybrid48"),
+            "traffic": read_traffic("sliding_rope_decode_hybrid48" if rope
+                                    else "sliding_decode_hybrid48"),
             "bytes_per_launch": int(kern_bytes),
             "avg_launch_us": round(kern_ms * 1e3, 3),
         },

@@ -7,8 +7,10 @@ package does not load the library; the first call does, and fails loudly if it h
 been built.
 """
 from .api import (IMPL_AUTO, IMPL_MFMA, IMPL_VALU, LINEAR, RING, GemmaAttnError, debug_ranges,
-                  decode, decode_append, kv_append, make_opts, make_shape, validate, version, workspace_bytes)
+                  decode, decode_append, decode_rope_append, kv_append, make_opts, make_shape,
+                  rope_append, rope_table, validate, version, workspace_bytes)
 
 __all__ = ["IMPL_AUTO", "IMPL_MFMA", "IMPL_VALU", "LINEAR", "RING", "GemmaAttnError",
-           "debug_ranges", "decode", "decode_append", "kv_append", "make_opts", "make_shape", "validate",
-           "version", "workspace_bytes"]
+           "debug_ranges", "decode", "decode_append", "decode_rope_append", "kv_append",
+           "make_opts", "make_shape", "rope_append", "rope_table", "validate", "version",
+           "workspace_bytes"]

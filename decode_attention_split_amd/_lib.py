@@ -29,7 +29,8 @@ EXPORTS = ["ga_decode_workspace_bytes", "gemma_attn_decode", "gemma_attn_decode_
            "gemma_attn_strerror", "gemma_attn_version",
            "ga_decode_multi_workspace_bytes", "gemma_attn_decode_multi", "gemma_kv_append_multi",
            "gemma_attn_validate_multi", "gemma_kv_append_fp8", "ga_decode_fp8_workspace_bytes",
-           "gemma_attn_decode_fp8", "gemma_rope_append"]
+           "gemma_attn_decode_fp8", "gemma_rope_append", "gemma_attn_decode_rope_append",
+           "gemma_rope_table"]
 
 _lib = None
 
@@ -79,6 +80,11 @@ def load():
     lib.gemma_attn_decode_fp8.restype = i32
     lib.gemma_rope_append.argtypes = [SP, i32, P, P, P, P, P, P, P, f32, i32, P]
     lib.gemma_rope_append.restype = i32
+    lib.gemma_attn_decode_rope_append.argtypes = [SP, P, P, P, P, P, P, P, P, P, i32, f32, f32,
+                                                  P, i32, P, P, sz, OP, P]
+    lib.gemma_attn_decode_rope_append.restype = i32
+    lib.gemma_rope_table.argtypes = [i32, P, f32, i32, P, P]
+    lib.gemma_rope_table.restype = i32
     lib.gemma_attn_strerror.argtypes = [i32]
     lib.gemma_attn_strerror.restype = ctypes.c_char_p
     lib.gemma_attn_version.argtypes = []

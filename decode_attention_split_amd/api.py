@@ -195,6 +195,60 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, windo
     return out
 
 
+def rope_table(pos, rope_base: float, rotary_dim: int, out=None, stream=None):
+    """cos / sin of every rotate-half pair at pos[b]: float64 [B, rotary_dim / 2, 2] (see
+    gemma_rope_table)."""
+    _need(pos, "pos", torch.int32, 1)
+    B = pos.numel()
+    if out is None:
+        out = torch.empty((B, max(rotary_dim, 0) // 2, 2), dtype=torch.float64,
+                          device=pos.device)
+    elif out.dtype != torch.float64 or not out.is_contiguous() or \
+            tuple(out.shape) != (B, rotary_dim // 2, 2):
+        raise ValueError("out must be a contiguous float64 [B, rotary_dim / 2, 2] tensor")
+    rc = _lib.load().gemma_rope_table(int(B), _ptr(pos), float(rope_base), int(rotary_dim),
+                                      _ptr(out), _stream_handle(stream))
+    _check(rc, "gemma_rope_table")
+    return out
+
+
+def decode_rope_append(q, q_out, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos,
+                       window: int, softcap: float, scale: float, kind: int, table,
+                       rotary_dim: int, out=None, workspace=None, max_ctx: int = 0,
+                       split_keys: int = 0, impl: int = IMPL_AUTO, deterministic: bool = False,
+                       stream=None):
+    """rope_append(q, q_out, ...) of one token then decode(q_out, ...), one launch where the
+    vector kernel serves the shape; table = rope_table(pos, base, rotary_dim) (see
+    gemma_attn_decode_rope_append)."""
+    if table is not None and (table.dtype != torch.float64 or not table.is_contiguous() or
+                              tuple(table.shape) != (pos.numel(), rotary_dim // 2, 2)):
+        raise ValueError("table must be rope_table(pos, base, rotary_dim)")
+    shape, out, opts, workspace = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window,
+                                                 kind, out, workspace, max_ctx, split_keys, impl,
+                                                 deterministic)
+    _need(q_out, "q_out", torch.bfloat16, 3)
+    if q_out.shape != q.shape:
+        raise ValueError("q_out must have q's shape")
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    if (v_cache is None) != (v_new is None):
+        _check(-9, "gemma_attn_decode_rope_append")
+    if v_new is not None:
+        _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(pos, "pos", torch.int32, 1)
+    B, Hkv, _, D = k_cache.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or (v_new is not None and v_new.shape != k_new.shape) \
+            or pos.numel() != B:
+        raise ValueError("k_new / v_new must be [B, Hkv, D] and pos [B]")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = _lib.load().gemma_attn_decode_rope_append(
+        ctypes.byref(shape), _ptr(q), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+        _ptr(v_new), _ptr(pos), _ptr(ctx_lens), _ptr(q_pos), int(window), float(softcap),
+        float(scale), _ptr(table), int(rotary_dim), _ptr(out), _ptr(workspace), ws_bytes,
+        ctypes.byref(opts), _stream_handle(stream))
+    _check(rc, "gemma_attn_decode_rope_append")
+    return out
+
+
 def decode_multi(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, scale: float,
                  kind: int, out=None, workspace=None, max_ctx: int = 0, split_keys: int = 0,
                  deterministic: bool = False, impl: int = IMPL_AUTO, stream=None):

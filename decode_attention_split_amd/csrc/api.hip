@@ -25,6 +25,7 @@ constexpr int kMaxSplitKeys = 65536;
 #endif
 constexpr int kMultiMaxRows = GA_MULTI_MAX_ROWS;  // multi-token: query rows per unit
 constexpr int kMaxTokens = 4096;  // multi-token: query tokens per row
+constexpr int kMaxRotaryDim = 512;  // the largest head_dim
 
 int32_t check_arch() {
   int dev = -1;
@@ -331,6 +332,14 @@ struct Fp8Cache {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Rotary embedding applied to q and the appended K row before the decode (single token,
+// bf16 caches): the rotated q goes to q_out.
+struct RopeIn {
+  ga_bf16* q_out;
+  const double* table;  // [B, dim / 2] (cos, sin) pairs at pos[b]
+  int dim;
+};
+
 // Decode, optionally fused with the cache append of one token per row (k_new != nullptr),
 // over bf16 caches (k_cache / v_cache) or fp8 caches (f8 != nullptr).
 int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, ga_bf16* v_cache,
@@ -338,7 +347,7 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
                     const int32_t* ctx_lens, const int32_t* q_pos, int32_t window, float softcap,
                     float scale, float* out, void* workspace, size_t workspace_bytes,
                     const ga_decode_opts* opts, void* stream, int32_t T = 1,
-                    const Fp8Cache* f8 = nullptr) {
+                    const Fp8Cache* f8 = nullptr, const RopeIn* rope = nullptr) {
   int32_t st = check_shape(shape, window, T);
   if (st != GA_OK) return st;
   if (f8) {
@@ -427,6 +436,29 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (rope) {
+    // Fused into the vector kernel's single-token launch; every work-group of a unit
+    // rotates from q, so an in-place q_out needs a single split.  Otherwise the RoPE +
+    // append kernel runs first and the decode reads the rotated q and the appended cache.
+    const bool fused = !p.rows16 && p.impl != GA_IMPL_MFMA &&
+                       (p.n_split == 1 || (const void*)rope->q_out != (const void*)q);
+    if (fused) {
+      a.rope = 1;
+      a.rope_dim = rope->dim;
+      a.rope_table = rope->table;
+      a.q_rot_out = rope->q_out;
+    } else {
+      // (the base is not read: with one token every angle comes from the table)
+      e = ga::rope_append_launch(a.B, 1, a.Hq, a.Hkv, D, a.cap, a.kind, rope->dim, 1.0, q,
+                                 rope->q_out, k_cache, k_eq_v ? nullptr : v_cache, k_new,
+                                 k_eq_v ? nullptr : v_new, new_pos, rope->table, s);
+      if (e != hipSuccess) return GA_ERR_LAUNCH;
+      a.q = rope->q_out;
+      a.k_new = nullptr;
+      a.v_new = nullptr;
+      a.new_pos = nullptr;
+    }
+  }
   if (p.rows16) {
     e = ga::decode_rows16_launch(a, k_eq_v, s);
     if (e == hipSuccess && p.n_split > 1) e = ga::merge_launch(a, s);
@@ -462,6 +494,27 @@ int32_t gemma_attn_decode_append(const ga_shape* shape, const ga_bf16* q, ga_bf1
   if (!k_new) return GA_ERR_NULL;
   return decode_impl(shape, q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, window,
                      softcap, scale, out, workspace, workspace_bytes, opts, stream);
+}
+
+int32_t gemma_attn_decode_rope_append(const ga_shape* shape, const ga_bf16* q, ga_bf16* q_out,
+                                      ga_bf16* k_cache, ga_bf16* v_cache, const ga_bf16* k_new,
+                                      const ga_bf16* v_new, const int32_t* pos,
+                                      const int32_t* ctx_lens, const int32_t* q_pos,
+                                      int32_t window, float softcap, float scale,
+                                      const double* rope_table, int32_t rotary_dim, float* out,
+                                      void* workspace, size_t workspace_bytes,
+                                      const ga_decode_opts* opts, void* stream) {
+  if (!shape) return GA_ERR_NULL;
+  if (!k_new || !q_out) return GA_ERR_NULL;
+  if (!aligned16(q_out)) return GA_ERR_NULL;
+  if (shape->head_dim > 0 && (rotary_dim < 0 || rotary_dim > shape->head_dim ||
+                              rotary_dim % 2 != 0))
+    return GA_ERR_OPTS;
+  if (rotary_dim > 0 && (!rope_table || !aligned16(rope_table))) return GA_ERR_NULL;
+  const RopeIn rope{q_out, rope_table, rotary_dim};
+  return decode_impl(shape, q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, window,
+                     softcap, scale, out, workspace, workspace_bytes, opts, stream, 1, nullptr,
+                     &rope);
 }
 
 int32_t gemma_attn_decode(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
@@ -605,7 +658,22 @@ int32_t gemma_rope_append(const ga_shape* shape, int32_t num_tokens, const ga_bf
   hipError_t e = ga::rope_append_launch(
       shape->batch, num_tokens, shape->num_q_heads, shape->num_kv_heads, shape->head_dim,
       shape->capacity, shape->kind, rotary_dim, (double)rope_base, q, q_out, k_cache, v_cache,
-      k_new, v_new, pos, static_cast<hipStream_t>(stream));
+      k_new, v_new, pos, nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}
+
+int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int32_t rotary_dim,
+                         double* table, void* stream) {
+  if (batch < 0 || rotary_dim < 0 || rotary_dim % 2 != 0) return GA_ERR_DIMS;
+  if (rotary_dim > kMaxRotaryDim) return GA_ERR_TOO_LARGE;
+  if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return GA_ERR_OPTS;
+  if (batch == 0 || rotary_dim == 0) return GA_OK;
+  if (!pos || !table) return GA_ERR_NULL;
+  if (!aligned16(table)) return GA_ERR_NULL;
+  int32_t st = check_arch();
+  if (st != GA_OK) return st;
+  hipError_t e = ga::rope_table_launch(batch, rotary_dim, (double)rope_base, pos, table,
+                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
 }
 

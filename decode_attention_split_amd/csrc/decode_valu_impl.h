@@ -31,6 +31,7 @@
 
 #include "ga_device.h"
 #include "ga_internal.h"
+#include "ga_rope.h"
 
 namespace ga {
 namespace {
@@ -68,9 +69,13 @@ __device__ __forceinline__ uint32_t chunk_word(const uint2& v, int i) { return i
 
 // FP8: the cache holds e4m3 codes with one float32 scale per row (K and V each); a key's
 // logit is scale_k * <q, codes> and its value weight p * scale_v multiplies the codes.
-template <int D, int G, int NW_, bool KV_SHARED, bool MULTI, bool FP8>
+// ROPE: the rotary embedding fused with the append (single token, bf16 caches): q and the
+// new K row rotate at new_pos[b] in the work-group (the same per-element function as the
+// RoPE + append kernel, so the launch equals RoPE + append followed by decode, bit for bit).
+template <int D, int G, int NW_, bool KV_SHARED, bool MULTI, bool FP8, bool ROPE = false>
 __global__ void __launch_bounds__(NW_ * 64)
     decode_valu_kernel(DecodeArgs a) {
+  static_assert(!ROPE || (!MULTI && !FP8), "RoPE is fused for single-token bf16 decode only");
   using C = ValuCfg<D, G, NW_>;
   constexpr int L = C::L, DPL = C::DPL, GPW = C::GPW, NW = C::NW;
   constexpr int ROW16 = D / 8;  // 16-byte chunks per bf16 row
@@ -86,6 +91,7 @@ __global__ void __launch_bounds__(NW_ * 64)
   __shared__ __attribute__((aligned(16))) float s_acc[NW][G][D];
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
+  __shared__ __attribute__((aligned(16))) uint16_t s_rot[ROPE ? (G + 1) * D : 8];  // q, k_new
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -124,19 +130,45 @@ __global__ void __launch_bounds__(NW_ * 64)
   // dot2 products (fp8 keys are widened exactly to bf16 pairs first).  Loaded before the
   // context length is known (they do not depend on it), so the two latencies overlap.
   uint32_t qr[G][DPL / 2];  // element pairs (e, e + 1), e even, in lane order
+  auto put_q = [&](int hh, int c, int h8, const uint4& v) {
+    qr[hh][EPC * c / 2 + 4 * h8 + 0] = v.x;
+    qr[hh][EPC * c / 2 + 4 * h8 + 1] = v.y;
+    qr[hh][EPC * c / 2 + 4 * h8 + 2] = v.z;
+    qr[hh][EPC * c / 2 + 4 * h8 + 3] = v.w;
+  };
+  // ROPE: the unit's G query rows and its new K row, unrotated, in 16-byte chunks (RPT
+  // per thread), and the (cos, sin) of the rotate-half pairs this thread turns (NPR), all
+  // requested here, ahead of the first K rows; the rotation follows once those are out.
+  constexpr int RCH = ROPE ? (G + 1) * D / 8 : 1;
+  constexpr int RPT = (RCH + NW * 64 - 1) / (NW * 64);
+  constexpr int NPR = ROPE ? (D / 2 + NW * 64 - 1) / (NW * 64) : 1;
+  uint4 raw[RPT];
+  double2 rcs[NPR];
+  Chunk kfresh[ROPE ? NCH : 1];  // this lane's chunks of the rotated new K row
+  if constexpr (!ROPE) {  // (with ROPE: from the rotated rows, once they are in LDS)
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + row_index(hh) * D);
+    for (int hh = 0; hh < G; ++hh) {
+      const uint4* qp = reinterpret_cast<const uint4*>(a.q + row_index(hh) * D);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+      for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-      for (int h8 = 0; h8 < EPC / 8; ++h8) {
-        const uint4 v = qp[(EPC / 8) * (c * L + j) + h8];
-        qr[hh][EPC * c / 2 + 4 * h8 + 0] = v.x;
-        qr[hh][EPC * c / 2 + 4 * h8 + 1] = v.y;
-        qr[hh][EPC * c / 2 + 4 * h8 + 2] = v.z;
-        qr[hh][EPC * c / 2 + 4 * h8 + 3] = v.w;
+        for (int h8 = 0; h8 < EPC / 8; ++h8) put_q(hh, c, h8, qp[(EPC / 8) * (c * L + j) + h8]);
       }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NPR; ++r) {
+      const int i = threadIdx.x + r * NW * 64, half = a.rope_dim / 2;
+      rcs[r] = i < half ? reinterpret_cast<const double2*>(a.rope_table)[(size_t)b * half + i]
+                        : make_double2(1.0, 0.0);
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int t = threadIdx.x + r * NW * 64;
+      const int hh = t / (D / 8), c = t % (D / 8);
+      const uint16_t* src =
+          hh < G ? a.q + row_index(hh) * D : a.k_new + ((size_t)b * a.Hkv + g) * D;
+      raw[r] = t < RCH ? *reinterpret_cast<const uint4*>(src + 8 * c) : make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -189,6 +221,48 @@ __global__ void __launch_bounds__(NW_ * 64)
   if constexpr (!MULTI)
     load_rows(ka, va, ca, min(i_first, min(a.cap, k_begin + a.split_keys) - 1), false);
 
+  if constexpr (ROPE) {
+    // Rotate at the appended position: each thread takes rotate-half pairs i and turns
+    // them in place in all G + 1 rows in LDS.  Every work-group of the unit does this; the
+    // first split also writes the rotated q out and appends the rotated K row.
+    const int half = a.rope_dim / 2;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int t = threadIdx.x + r * NW * 64;
+      if (t < RCH) *reinterpret_cast<uint4*>(s_rot + 8 * t) = raw[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NPR; ++r) {
+      const int i = threadIdx.x + r * NW * 64;
+      if (i < half) {
+#pragma unroll
+        for (int hh = 0; hh <= G; ++hh) {
+          uint16_t* row = s_rot + hh * D;
+          const uint16_t x0 = row[i], x1 = row[i + half];
+          row[i] = rope_first(x0, x1, rcs[r].x, rcs[r].y);
+          row[i + half] = rope_second(x0, x1, rcs[r].x, rcs[r].y);
+        }
+      }
+    }
+    __syncthreads();
+    if (split == 0)
+      for (int e = threadIdx.x; e < G * D; e += NW * 64)
+        a.q_rot_out[row_index(e / D) * D + e % D] = s_rot[e];
+    if (app.on) app.k = *reinterpret_cast<const AppendRow::u32x4*>(s_rot + G * D + 8 * threadIdx.x);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      kfresh[c] = *reinterpret_cast<const Chunk*>(s_rot + G * D + (c * L + j) * 8);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const uint4* qp = reinterpret_cast<const uint4*>(s_rot + hh * D);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int h8 = 0; h8 < EPC / 8; ++h8) put_q(hh, c, h8, qp[(EPC / 8) * (c * L + j) + h8]);
+      }
+    }
+  }
   const RowRange r = unit_range(a, b, chunk);
   const int k_end = min(r.n, k_begin + a.split_keys);
   if (k_begin >= k_end) {
@@ -289,12 +363,24 @@ __global__ void __launch_bounds__(NW_ * 64)
                      int step) {
     const int i = k_begin + step * GPW + grp;
     const bool valid = i < k_end;
+    // The key rows; with ROPE the appended key (its slot's load read the unrotated k_new)
+    // takes the rotated row held in registers, selected here where the loaded rows are
+    // consumed, so the loads themselves stay unconditional.
+    Chunk kx[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kx[c] = kr[c];
+    if constexpr (ROPE) {
+      if (key_slot(slot_base, valid ? i : k_end - 1, a.cap) == new_slot) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kx[c] = kfresh[c];
+      }
+    }
     const int pos = r.lo + i;  // absolute position of the key (MULTI masks)
     float s[G];
     if constexpr (FP8) {
       uint32_t kb[DPL / 2];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) widen_fp8_bf16(kr[c], &kb[EPC * c / 2]);
+      for (int c = 0; c < NCH; ++c) widen_fp8_bf16(kx[c], &kb[EPC * c / 2]);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float d0 = 0.0f, d1 = 0.0f;
@@ -311,10 +397,10 @@ __global__ void __launch_bounds__(NW_ * 64)
         float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          d0 = dot2_bf16(qr[hh][4 * c + 0], chunk_word(kr[c], 0), d0);
-          d1 = dot2_bf16(qr[hh][4 * c + 1], chunk_word(kr[c], 1), d1);
-          d0 = dot2_bf16(qr[hh][4 * c + 2], chunk_word(kr[c], 2), d0);
-          d1 = dot2_bf16(qr[hh][4 * c + 3], chunk_word(kr[c], 3), d1);
+          d0 = dot2_bf16(qr[hh][4 * c + 0], chunk_word(kx[c], 0), d0);
+          d1 = dot2_bf16(qr[hh][4 * c + 1], chunk_word(kx[c], 1), d1);
+          d0 = dot2_bf16(qr[hh][4 * c + 2], chunk_word(kx[c], 2), d0);
+          d1 = dot2_bf16(qr[hh][4 * c + 3], chunk_word(kx[c], 3), d1);
         }
         s[hh] = group_sum<L>(d0 + d1);
       }
@@ -337,7 +423,7 @@ __global__ void __launch_bounds__(NW_ * 64)
       p[hh] = vh ? exp2_fast(x - m[hh]) : 0.0f;
       l[hh] += p[hh];
     }
-    const Chunk(&vv)[NCH] = KV_SHARED ? kr : vr;
+    const Chunk(&vv)[NCH] = KV_SHARED ? kx : vr;
     if constexpr (FP8) {
       float pv[G];
 #pragma unroll
@@ -520,7 +606,13 @@ hipError_t launch_dgw(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
   // K = V, several tokens, fp8 cache: one instantiation per combination
 #define GA_VALU_LAUNCH(KV, MU, F8)                                                             \
   hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, KV, MU, F8>), grid, block, 0, stream, a)
-  if (a.fp8) {
+#define GA_VALU_LAUNCH_ROPE(KV)                                                                \
+  hipLaunchKernelGGL((decode_valu_kernel<D, G, NW, KV, false, false, true>), grid, block, 0,    \
+                     stream, a)
+  if (a.rope) {  // single token, bf16 caches (the plan checks)
+    if (multi || a.fp8) return hipErrorInvalidValue;
+    if (k_eq_v) GA_VALU_LAUNCH_ROPE(true); else GA_VALU_LAUNCH_ROPE(false);
+  } else if (a.fp8) {
     if (multi) {
       if (k_eq_v) GA_VALU_LAUNCH(true, true, true); else GA_VALU_LAUNCH(false, true, true);
     } else {
@@ -534,6 +626,7 @@ hipError_t launch_dgw(const DecodeArgs& a, bool k_eq_v, hipStream_t stream) {
     }
   }
 #undef GA_VALU_LAUNCH
+#undef GA_VALU_LAUNCH_ROPE
   return hipGetLastError();
 }
 

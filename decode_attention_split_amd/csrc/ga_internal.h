@@ -36,6 +36,12 @@ struct DecodeArgs {
   uint16_t* k_dst;        // == k, writable
   uint16_t* v_dst;        // == v, writable (nullptr for K = V)
   int deterministic;      // vector path: fixed step order (bit-reproducible sums)
+  // Rotary embedding fused with the append (vector path, one token): q and the new K row
+  // rotate at new_pos[b] inside the decode; the rotated q also goes to q_rot_out.
+  int rope = 0;
+  int rope_dim = 0;
+  const double* rope_table = nullptr;  // [B, rope_dim / 2] (cos, sin) pairs
+  uint16_t* q_rot_out = nullptr;
   // Multi-token decode: T query tokens per row, handled in chunks of Tc tokens; a unit
   // (b, g, chunk) walks the union of its tokens' key ranges (at most max_union keys).
   int T = 1, Tc = 1, n_chunks = 1;
@@ -173,7 +179,10 @@ hipError_t append_fp8_launch(int B, int T, int Hkv, int D, int cap, int kind, ui
 hipError_t rope_append_launch(int B, int T, int Hq, int Hkv, int D, int cap, int kind, int R,
                               double base, const uint16_t* q, uint16_t* q_out, uint16_t* k_cache,
                               uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
-                              const int32_t* pos, hipStream_t stream);
+                              const int32_t* pos, const double* table, hipStream_t stream);
+// cos / sin of every rotate-half pair at position pos[b]: table [B, R / 2, 2] doubles.
+hipError_t rope_table_launch(int B, int R, double base, const int32_t* pos, double* table,
+                             hipStream_t stream);
 
 // Flags of the B * T query tokens at positions q_pos[b] + t.
 hipError_t validate_launch(int B, int T, int cap, int kind, int window, int max_ctx,

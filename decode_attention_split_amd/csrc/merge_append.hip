@@ -2,6 +2,7 @@
 // debug kernels (precondition flags, key-range dump).  gfx950.
 #include "ga_device.h"
 #include "ga_internal.h"
+#include "ga_rope.h"
 
 namespace ga {
 namespace {
@@ -226,22 +227,12 @@ __global__ void __launch_bounds__(64)
 // rows without a cache).  Every thread reads its element and its partner before a barrier
 // and writes after it, so q_out may alias q.
 
-// double -> bf16 bits, nearest with ties to even, in one rounding
-__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-  if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
-  int e;
-  const double f = frexp(fabs(x), &e);     // |x| = f 2^e, f in [0.5, 1)
-  const double m = rint(ldexp(f, 8));       // 8 significant bits (128..256), ties to even
-  const float r = (float)ldexp(m, e - 8);   // exact
-  return (uint16_t)((__float_as_uint(r) >> 16) | (signbit(x) ? 0x8000u : 0u));
-}
-
 // One thread per element (blockDim.x = D), one block per row.
 __global__ void __launch_bounds__(512)
     rope_append_kernel(int B, int T, int Hq, int Hkv, int D, int cap, int kind, int R,
                        double base, const uint16_t* q, uint16_t* q_out, uint16_t* k_cache,
                        uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
-                       const int32_t* pos) {
+                       const int32_t* pos, const double* table) {
   const int d = threadIdx.x;
   const int rows_per_tok = Hq + (k_cache ? Hkv : 0) + (v_cache ? Hkv : 0);
   const long long row = blockIdx.x;  // ((b * T + t) * rows_per_tok + r)
@@ -268,19 +259,30 @@ __global__ void __launch_bounds__(512)
     dst = (is_k ? k_cache : v_cache) + (((long long)b * Hkv + g) * cap + slot) * D;
     rotate = is_k;
   }
-  uint16_t y = src[d];
-  if (rotate && d < R) {
-    const int half = R / 2;
-    const int i = d < half ? d : d - half;
-    const double a = (double)__uint_as_float((uint32_t)src[i] << 16);
-    const double bb = (double)__uint_as_float((uint32_t)src[i + half] << 16);
-    const double ang = (double)p * pow(base, -2.0 * i / R);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    y = f64_to_bf16(d < half ? a * cs - bb * sn : bb * cs + a * sn);
+  uint16_t y;
+  if (table && rotate && d < R) {  // one token (T = 1): the angles of the cos / sin table
+    const int half = R / 2, i = d < half ? d : d - half;
+    const double cs = table[((size_t)b * half + i) * 2], sn = table[((size_t)b * half + i) * 2 + 1];
+    y = d < half ? rope_first(src[i], src[i + half], cs, sn)
+                 : rope_second(src[i], src[i + half], cs, sn);
+  } else {
+    y = rope_element(src, d, rotate ? R : 0, base, p);
   }
   __syncthreads();  // every element and partner of the row is read before any write
   dst[d] = y;
+}
+
+// Thread (b, i): cos and sin of rotate-half pair i at position pos[b].
+__global__ void __launch_bounds__(256)
+    rope_table_kernel(int B, int R, double base, const int32_t* pos, double* table) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = R / 2;
+  if (e >= (long long)B * half) return;
+  const int b = (int)(e / half), i = (int)(e % half);
+  double cs, sn;
+  rope_angle(i, R, base, pos[b], &cs, &sn);
+  table[2 * e] = cs;
+  table[2 * e + 1] = sn;
 }
 
 // Precondition flags of every query token (b, t) at position q_pos[b] + t.
@@ -358,11 +360,21 @@ hipError_t append_fp8_launch(int B, int T, int Hkv, int D, int cap, int kind, ui
 hipError_t rope_append_launch(int B, int T, int Hq, int Hkv, int D, int cap, int kind, int R,
                               double base, const uint16_t* q, uint16_t* q_out, uint16_t* k_cache,
                               uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
-                              const int32_t* pos, hipStream_t stream) {
+                              const int32_t* pos, const double* table, hipStream_t stream) {
   const long long rows = (long long)B * T * (Hq + (k_cache ? Hkv : 0) + (v_cache ? Hkv : 0));
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)rows), dim3(D), 0, stream, B, T, Hq, Hkv,
-                     D, cap, kind, R, base, q, q_out, k_cache, v_cache, k_new, v_new, pos);
+                     D, cap, kind, R, base, q, q_out, k_cache, v_cache, k_new, v_new, pos,
+                     T == 1 ? table : nullptr);
+  return hipGetLastError();
+}
+
+hipError_t rope_table_launch(int B, int R, double base, const int32_t* pos, double* table,
+                             hipStream_t stream) {
+  const long long n = (long long)B * (R / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     B, R, base, pos, table);
   return hipGetLastError();
 }
 

@@ -124,15 +124,48 @@ class HybridKVCache:
                                None if g.k_eq_v else v_new, pos, g.kind, g.rope_base,
                                g.rotary_dim, stream=stream)
 
+    def rope_tables(self, pos, stream=None):
+        """cos / sin tables at pos, one per (base, rotary_dim) among the rotary layers, keyed
+        by that pair; every layer of a type reads its type's table."""
+        tables = {}
+        for g in self.layers:
+            key = (g.rope_base, g.rotary_dim)
+            if g.rope_base > 0 and key not in tables:
+                tables[key] = api.rope_table(pos, g.rope_base, g.rotary_dim, stream=stream)
+        return tables
+
+    def decode_rope_append(self, layer: int, q, q_out, k_new, v_new, pos, ctx_lens, q_pos,
+                           table, out=None, deterministic=False, stream=None):
+        """Rotary embedding, append and decode of a cache-owning layer in one call (one
+        launch where the vector kernel serves the layer); table from rope_tables(pos)."""
+        g = self.layers[layer]
+        if not self.owns_cache(layer):
+            raise ValueError(f"layer {layer} shares layer {self.kv_source[layer]}'s cache and "
+                             "does not append")
+        return api.decode_rope_append(q, q_out, self.k[layer], self.v[layer], k_new,
+                                      None if g.k_eq_v else v_new, pos, ctx_lens, q_pos,
+                                      g.window, g.softcap, g.q_scale, g.kind, table,
+                                      g.rotary_dim, out=out, workspace=self.workspace,
+                                      max_ctx=self.shape(g).max_ctx, deterministic=deterministic,
+                                      stream=stream)
+
     def step(self, q_list, k_new_list, v_new_list, pos, ctx_lens, q_pos, outs, stream=None,
              fused=True, deterministic=False, q_rot=None):
         """One decode step through every layer: append the new token, then attend.  Layers
-        with a rotary embedding (rope_base > 0) run the fused rotary + append, then decode
-        with the rotated q (written to q_rot[layer], or in place when q_rot is None)."""
+        with a rotary embedding (rope_base > 0) rotate q (into q_rot[layer], or in place when
+        q_rot is None) and the new K row before the append; with fused, a cache-owning layer
+        does all of it in one call, on the step's cos / sin table of its layer type."""
+        tables = self.rope_tables(pos, stream=stream) if fused else {}
         for li in range(len(self.layers)):
             g = self.layers[li]
             if g.rope_base > 0:
                 qo = q_list[li] if q_rot is None else q_rot[li]
+                if fused and self.owns_cache(li):
+                    self.decode_rope_append(li, q_list[li], qo, k_new_list[li], v_new_list[li],
+                                            pos, ctx_lens, q_pos,
+                                            tables[(g.rope_base, g.rotary_dim)], out=outs[li],
+                                            deterministic=deterministic, stream=stream)
+                    continue
                 self.rope_append(li, q_list[li], qo, k_new_list[li], v_new_list[li], pos,
                                  stream=stream)
                 self.decode(li, qo, ctx_lens, q_pos, out=outs[li], deterministic=deterministic,

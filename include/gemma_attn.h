@@ -266,6 +266,52 @@ int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const g
                               size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
 
 /*
+ * cos / sin table of the rotary embedding of one token per row, at position pos[b]:
+ *   table[b, i, 0] = cos(pos[b] * rope_base^(-2i/R)), table[b, i, 1] = sin(...)
+ * for the R / 2 rotate-half pairs i of R = rotary_dim (definition at gemma_rope_append),
+ * computed in double by the same function as gemma_rope_append's angles, so the two give
+ * the same bits.  The angles depend on the position, the base and R only, so a decode step
+ * computes one table per layer type (all sliding layers share one base and R, all global
+ * layers another: "Gemma support" pull request, Summary) and every layer of that type
+ * reads it.  table: device float64 [batch, R / 2, 2], 16-byte aligned, fully written.
+ * pos: device int32 [batch].  Errors: GA_ERR_DIMS (batch < 0, R odd or negative),
+ * GA_ERR_TOO_LARGE (R > 512), GA_ERR_OPTS (rope_base not finite and > 0), GA_ERR_NULL.
+ * Nothing is launched when batch or R is 0.
+ */
+int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int32_t rotary_dim,
+                         double* table, void* stream);
+
+/*
+ * RoPE, cache append and single-token decode in one call: exactly
+ *   gemma_rope_append(shape, 1, q, q_out, k_cache, v_cache, k_new, v_new, pos, rope_base,
+ *                     rotary_dim, stream)
+ * followed by gemma_attn_decode_ex(shape, q_out, k_cache, v_cache, ctx_lens, q_pos, window,
+ * softcap, scale, out, workspace, workspace_bytes, opts, stream), bit for bit (q_out, the
+ * caches and out), where rope_table is gemma_rope_table(B, pos, rope_base, rotary_dim).
+ * q [B, Hq, D] and k_new [B, Hkv, D] are rotated at position pos[b]; v_new is appended
+ * unrotated, NULL with v_cache for K = V.  q_out [B, Hq, D] device bf16, non-NULL, 16-byte
+ * aligned; it may equal q and must not otherwise overlap it.  rope_table as written by
+ * gemma_rope_table (may be NULL when rotary_dim is 0).  Workspace: ga_decode_workspace_bytes,
+ * as for the decode.  Where the vector kernel serves the call, one launch does it all (the
+ * GQA sliding geometry of the Gemma 3 / 4 stacks, "Gemma 3 Technical Report", section 2:
+ * local layers, head_dim 256, several query heads per KV head): each work-group rotates
+ * its unit's query rows and the new K row into LDS, the first split writes the rotated q
+ * and appends the rotated row, and every reader of the appended slot takes the rotated row
+ * from LDS; with q_out == q that needs a single split per row.  Otherwise (matrix-core
+ * shapes, an in-place q_out with several splits) the RoPE + append kernel runs first, on
+ * the table's angles, then the decode.  Errors: those of both calls (GA_ERR_OPTS for
+ * rotary_dim), checked before anything is launched.
+ */
+int32_t gemma_attn_decode_rope_append(const ga_shape* shape, const ga_bf16* q, ga_bf16* q_out,
+                                      ga_bf16* k_cache, ga_bf16* v_cache, const ga_bf16* k_new,
+                                      const ga_bf16* v_new, const int32_t* pos,
+                                      const int32_t* ctx_lens, const int32_t* q_pos,
+                                      int32_t window, float softcap, float scale,
+                                      const double* rope_table, int32_t rotary_dim, float* out,
+                                      void* workspace, size_t workspace_bytes,
+                                      const ga_decode_opts* opts, void* stream);
+
+/*
  * Rotary position embedding fused with the cache append, one launch for T = num_tokens
  * tokens per row at positions pos[b] + t (T = 1: decode):
  *   q_out[b,t,h,:] = rope(q[b,t,h,:], pos[b] + t)            (q, q_out [B, T, Hq, D])

@@ -1,0 +1,156 @@
+"""GPU: RoPE + append + decode in one call equals RoPE + append followed by decode.
+
+gemma_attn_decode_rope_append promises the bits of gemma_rope_append then
+gemma_attn_decode_ex: the same rotated q, the same caches, the same output.  Where the
+vector kernel serves the call, the rotation runs inside the decode launch (every
+work-group rotates its unit's rows into LDS from the same per-element function); on
+matrix-core shapes, and for an in-place q_out with several splits, the two calls run in
+turn.  Each case below runs both routes on copies of the same inputs and compares bit for
+bit, and one case also checks the output against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_split_amd import api, synth
+
+from common import LayerInputs, assert_parity, log, oracle_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, Hq, Hkv, D, cap, kind, k_eq_v, ctx, seed):
+    gen = synth.generator(seed)
+    t = lambda shape: synth.normal_bf16(gen, shape).cuda()
+    q = t((B, Hq, D))
+    k = t((B, Hkv, cap, D))
+    v = None if k_eq_v else t((B, Hkv, cap, D))
+    kn = t((B, Hkv, D))
+    vn = None if k_eq_v else t((B, Hkv, D))
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    return q, k, v, kn, vn, ctx_t
+
+
+def _clone(x):
+    return None if x is None else x.clone()
+
+
+def _both_routes(q, k, v, kn, vn, ctx, window, softcap, scale, kind, base, R, in_place,
+                 split_keys=0, impl=api.IMPL_AUTO):
+    pos = ctx - 1
+    # fused call
+    kf, vf = k.clone(), _clone(v)
+    qf = q.clone()
+    qo = qf if in_place else torch.empty_like(q)
+    table = api.rope_table(pos, base, R)
+    out_f = api.decode_rope_append(qf, qo, kf, vf, kn, vn, pos, ctx, pos, window, softcap,
+                                   scale, kind, table, R, split_keys=split_keys, impl=impl,
+                                   deterministic=True)
+    # the two calls
+    kr, vr = k.clone(), _clone(v)
+    qr = q.clone()
+    qo_r = qr if in_place else torch.empty_like(q)
+    api.rope_append(qr, qo_r, kr, vr, kn, vn, pos, kind, base, R)
+    out_r = api.decode(qo_r, kr, vr, ctx, pos, window, softcap, scale, kind,
+                       split_keys=split_keys, impl=impl, deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qo.view(torch.int16), qo_r.view(torch.int16)), "rotated q"
+    assert torch.equal(kf.view(torch.int16), kr.view(torch.int16)), "k cache"
+    if v is not None:
+        assert torch.equal(vf.view(torch.int16), vr.view(torch.int16)), "v cache"
+    assert torch.equal(out_f.view(torch.int32), out_r.view(torch.int32)), "output bits"
+    return out_f, qo, kf, vf
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("split_keys", [0, 64])
+def test_sliding_layer_fused_equals_two_calls(in_place, split_keys):
+    """Gemma 3 / 4 sliding geometry: head_dim 256, 2 query heads per KV head, ring of the
+    window; split_keys 64 gives four splits per row (fused with a separate q_out, the two
+    calls with an in-place one); rows at an empty context, a partial ring, a wrapped ring."""
+    B, Hq, Hkv, D, W = 5, 8, 4, 256, 256
+    ctx = [0, 1, 100, 256, 9000]
+    q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, W, api.RING, False, ctx, 11 + split_keys)
+    log(f"sliding rope decode: in_place={in_place} split_keys={split_keys}")
+    _both_routes(q, k, v, kn, vn, ctx_t, W, 0.0, D ** -0.5, api.RING, 1e4, D, in_place,
+                 split_keys=split_keys)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,k_eq_v,R,kind,cap,window,softcap", [
+    (128, 8, 2, False, 64, api.LINEAR, 300, 0, 50.0),      # partial rotary, 4 heads per KV
+    (256, 4, 4, True, 256, api.RING, 32, 32, 0.0),          # K = V on the vector kernel
+    (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 0.0),      # global geometry: matrix cores
+    (256, 16, 8, False, 0, api.RING, 128, 128, 0.0),        # no rotary part
+])
+def test_other_shapes_fused_equals_two_calls(D, Hq, Hkv, k_eq_v, R, kind, cap, window, softcap):
+    B = 4
+    ctx = [1, cap // 2, cap, cap] if kind == api.LINEAR else [3, cap, 5 * cap + 7, 1]
+    q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, cap, kind, k_eq_v, ctx, D + Hq + R)
+    log(f"rope decode D={D} Hq={Hq} Hkv={Hkv} K=V={k_eq_v} R={R}")
+    base = 1e6 if D == 512 else 1e4
+    for in_place in (False, True):
+        _both_routes(q, k, v, kn, vn, ctx_t, window, softcap, D ** -0.5, kind, base, R,
+                     in_place)
+
+
+def test_fused_sliding_layer_matches_oracle():
+    """The fused route against the oracle: rotate q and the new K row (the oracle's RoPE),
+    append, attend."""
+    import oracle
+    B, Hq, Hkv, D, W = 3, 8, 4, 256, 256
+    ctx = [2, 256, 700]
+    q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, W, api.RING, False, ctx, 5)
+    kb, vb = synth.bits(k.cpu()), synth.bits(v.cpu())
+    out, qo, kf, vf = _both_routes(q, k, v, kn, vn, ctx_t, W, 0.0, D ** -0.5, api.RING, 1e4, D,
+                                   False, split_keys=64)
+    pos = np.asarray(ctx, np.int64) - 1
+    q_ref, _ = oracle.rope(synth.bits(q.cpu()), np.repeat(pos, Hq), 1e4, D)
+    kn_ref, _ = oracle.rope(synth.bits(kn.cpu()), np.repeat(pos, Hkv), 1e4, D)
+    k_ref, v_ref = kb.copy(), vb.copy()
+    vnb = synth.bits(vn.cpu())
+    for b in range(B):
+        k_ref[b, :, pos[b] % W] = kn_ref[b]
+        v_ref[b, :, pos[b] % W] = vnb[b]
+    # rotation: same double arithmetic on both sides, at most rare one-ulp rounding ties
+    diff = synth.bits(qo.cpu()).astype(np.int32) - q_ref.astype(np.int32)
+    assert (np.abs(diff) <= 1).all() and (diff != 0).sum() <= 2
+    diff = synth.bits(kf.cpu()).astype(np.int32) - k_ref.astype(np.int32)
+    assert (np.abs(diff) <= 1).all() and (diff != 0).sum() <= 2
+    assert np.array_equal(synth.bits(vf.cpu()), v_ref)
+    ref = oracle_out(LayerInputs(q_ref, k_ref, v_ref, np.asarray(ctx, np.int32), pos), W, 0.0,
+                     D ** -0.5, api.RING)
+    assert_parity(out, ref, "fused rope decode")
+
+
+def test_fused_call_rejects_bad_rotary_arguments():
+    B, Hq, Hkv, D, W = 2, 4, 2, 128, 16
+    q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, W, api.RING, False, [3, 5], 3)
+    pos = ctx_t - 1
+    for R, base in ((3, 1e4), (-2, 1e4), (D, 0.0), (D, float("inf")), (1024, 1e4)):
+        with pytest.raises(api.GemmaAttnError):
+            api.rope_table(pos, base, R)
+    table = api.rope_table(pos, 1e4, D)
+    for R in (3, D + 2, -2):
+        with pytest.raises(api.GemmaAttnError):
+            api.decode_rope_append(q, torch.empty_like(q), k, v, kn, vn, pos, ctx_t, pos, W,
+                                   0.0, 1.0, api.RING, None, R)
+    with pytest.raises(api.GemmaAttnError):  # no table for a rotary part
+        api.decode_rope_append(q, torch.empty_like(q), k, v, kn, vn, pos, ctx_t, pos, W, 0.0,
+                               1.0, api.RING, None, D)
+    with pytest.raises(ValueError):  # a table of another rotary width
+        api.decode_rope_append(q, torch.empty_like(q), k, v, kn, vn, pos, ctx_t, pos, W, 0.0,
+                               1.0, api.RING, table, 64)
+
+
+@pytest.mark.parametrize("base,R", [(1e4, 256), (1e6, 128), (1e4, 2)])
+def test_rope_table_matches_definition(base, R):
+    """table[b, i] = (cos, sin) of pos[b] * base^(-2i/R), against numpy in double (angles up
+    to about 1e5 radians lose a few digits to argument reduction on either side)."""
+    pos = torch.tensor([0, 1, 255, 16383, 99999, -3], dtype=torch.int32, device="cuda")
+    tab = api.rope_table(pos, base, R).cpu().numpy()
+    i = np.arange(R // 2)
+    ang = pos.cpu().numpy().astype(np.float64)[:, None] * np.power(float(base), -2.0 * i / R)
+    assert tab.shape == (6, R // 2, 2)
+    np.testing.assert_allclose(tab[..., 0], np.cos(ang), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(tab[..., 1], np.sin(ang), rtol=0, atol=1e-10)
+    assert (tab[0, :, 0] == 1.0).all() and (tab[0, :, 1] == 0.0).all()
