@@ -76,21 +76,24 @@ def test_sliding_layer_fused_equals_two_calls(in_place, split_keys):
                  split_keys=split_keys)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,k_eq_v,R,kind,cap,window,softcap", [
-    (128, 8, 2, False, 64, api.LINEAR, 300, 0, 50.0),      # partial rotary, 4 heads per KV
-    (256, 4, 4, True, 256, api.RING, 32, 32, 0.0),          # K = V on the vector kernel
-    (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 0.0),      # global geometry: matrix cores
-    (256, 16, 8, False, 0, api.RING, 128, 128, 0.0),        # no rotary part
+@pytest.mark.parametrize("D,Hq,Hkv,k_eq_v,R,kind,cap,window,softcap,impl", [
+    (128, 8, 2, False, 64, api.LINEAR, 300, 0, 50.0, api.IMPL_AUTO),   # partial, 4 per KV
+    (256, 4, 4, True, 256, api.RING, 32, 32, 0.0, api.IMPL_AUTO),      # K = V, vector kernel
+    (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 0.0, api.IMPL_AUTO),  # global: matrix cores
+    (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 0.0, api.IMPL_VALU),  # global: vector kernel
+    (512, 2, 2, False, 512, api.RING, 64, 64, 30.0, api.IMPL_AUTO),    # one head per KV head
+    (256, 16, 8, False, 0, api.RING, 128, 128, 0.0, api.IMPL_AUTO),    # no rotary part
 ])
-def test_other_shapes_fused_equals_two_calls(D, Hq, Hkv, k_eq_v, R, kind, cap, window, softcap):
+def test_other_shapes_fused_equals_two_calls(D, Hq, Hkv, k_eq_v, R, kind, cap, window, softcap,
+                                             impl):
     B = 4
     ctx = [1, cap // 2, cap, cap] if kind == api.LINEAR else [3, cap, 5 * cap + 7, 1]
     q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, cap, kind, k_eq_v, ctx, D + Hq + R)
-    log(f"rope decode D={D} Hq={Hq} Hkv={Hkv} K=V={k_eq_v} R={R}")
+    log(f"rope decode D={D} Hq={Hq} Hkv={Hkv} K=V={k_eq_v} R={R} impl={impl}")
     base = 1e6 if D == 512 else 1e4
     for in_place in (False, True):
         _both_routes(q, k, v, kn, vn, ctx_t, window, softcap, D ** -0.5, kind, base, R,
-                     in_place)
+                     in_place, impl=impl)
 
 
 def test_fused_sliding_layer_matches_oracle():
