@@ -770,6 +770,11 @@ def bench_fp8(args, w):
 
     def step(i):
         q, kc, ks, vc, vs = sets[i % copies]
+        if T == 1:  # quantizing append + decode in one call (one launch on the vector kernel)
+            api.decode_append_fp8(q, kc, ks, vc, vs, k_new, v_new, pos_t, ctx_t, pos_t,
+                                  g.window, g.softcap, g.q_scale, g.kind, out=out, workspace=ws,
+                                  max_ctx=max_ctx)
+            return
         api.kv_append_fp8(kc, ks, vc, vs, k_new, v_new, pos_t, g.kind)
         api.decode_fp8(q, kc, ks, vc, vs, ctx_t, pos_t, g.window, g.softcap, g.q_scale, g.kind,
                        out=out, workspace=ws, max_ctx=max_ctx)

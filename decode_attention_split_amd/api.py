@@ -423,6 +423,63 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, ctx_lens, q_pos, window:
     return out
 
 
+def decode_append_fp8(q, k_codes, k_scales, v_codes, v_scales, k_new, v_new, pos, ctx_lens,
+                      q_pos, window: int, softcap: float, scale: float, kind: int, out=None,
+                      workspace=None, max_ctx: int = 0, split_keys: int = 0,
+                      deterministic: bool = False, impl: int = IMPL_AUTO, stream=None):
+    """kv_append_fp8 of one token then decode_fp8 of one token, in one launch where the
+    vector kernel serves the shape (see gemma_attn_decode_append_fp8); q [B, Hq, D]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_codes, "k_codes", torch.uint8, 4)
+    _need(k_scales, "k_scales", torch.float32, 3)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    if (v_codes is None) != (v_new is None) or (v_codes is None) != (v_scales is None):
+        _check(-9, "gemma_attn_decode_append_fp8")
+    if v_codes is not None:
+        _need(v_codes, "v_codes", torch.uint8, 4)
+        _need(v_scales, "v_scales", torch.float32, 3)
+        _need(v_new, "v_new", torch.bfloat16, 3)
+        if v_codes.shape != k_codes.shape or v_scales.shape != k_scales.shape or \
+                v_new.shape != k_new.shape:
+            raise ValueError("V tensors must have the shapes of the K tensors")
+    _need(pos, "pos", torch.int32, 1)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    B, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k_codes.shape
+    if Bk != B or Dk != D or tuple(k_scales.shape) != (B, Hkv, cap) or \
+            tuple(k_new.shape) != (B, Hkv, D):
+        raise ValueError("q, k_codes, k_scales and k_new disagree")
+    if ctx_lens.numel() != B or q_pos.numel() != B or pos.numel() != B:
+        raise ValueError("ctx_lens, q_pos and pos must have one entry per batch row")
+    shape = make_shape(B, Hq, Hkv, D, cap, kind, max_ctx)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (B, Hq, D):
+            raise ValueError("out must be [B, Hq, D]")
+    opts = make_opts(split_keys, impl, deterministic)
+    lib = _lib.load()
+    if workspace is None:  # a given workspace is checked against its size by the library
+        need = lib.ga_decode_fp8_workspace_bytes(ctypes.byref(shape), 1, int(window),
+                                                 ctypes.byref(opts))
+        if need == ctypes.c_size_t(-1).value:
+            need = 0  # let the library report the precise error
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib.gemma_attn_decode_append_fp8(
+        ctypes.byref(shape), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+        _ptr(v_scales), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(ctx_lens), _ptr(q_pos),
+        int(window), float(softcap), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+        ctypes.byref(opts), _stream_handle(stream))
+    _check(rc, "gemma_attn_decode_append_fp8")
+    return out
+
+
 def rope_append(q, q_out, k_cache, v_cache, k_new, v_new, pos, kind: int, rope_base: float,
                 rotary_dim: int, stream=None):
     """Rotary embedding of q (-> q_out, may be q) and k_new fused with the append of T

@@ -436,6 +436,28 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (f8 && k_new) {
+    // The quantizing append runs inside the vector kernel's single-token launch; on the
+    // matrix cores it is its own launch before the decode.
+    if (!p.rows16 && p.impl != GA_IMPL_MFMA && T == 1) {
+      a.k8_dst = const_cast<uint8_t*>(f8->k);
+      a.ks_dst = const_cast<float*>(f8->ks);
+      a.v8_dst = k_eq_v ? nullptr : const_cast<uint8_t*>(f8->v);
+      a.vs_dst = k_eq_v ? nullptr : const_cast<float*>(f8->vs);
+      a.k_dst = nullptr;  // no bf16 row moves
+      a.v_dst = nullptr;
+    } else {
+      e = ga::append_fp8_launch(a.B, 1, a.Hkv, D, a.cap, a.kind, const_cast<uint8_t*>(f8->k),
+                                const_cast<float*>(f8->ks),
+                                k_eq_v ? nullptr : const_cast<uint8_t*>(f8->v),
+                                k_eq_v ? nullptr : const_cast<float*>(f8->vs), k_new,
+                                k_eq_v ? nullptr : v_new, new_pos, s);
+      if (e != hipSuccess) return GA_ERR_LAUNCH;
+      a.k_new = nullptr;
+      a.v_new = nullptr;
+      a.new_pos = nullptr;
+    }
+  }
   if (rope) {
     // Fused into the vector kernel's single-token launch; every work-group of a unit
     // rotates from q, so an in-place q_out needs a single split.  Otherwise the RoPE +
@@ -603,6 +625,20 @@ int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const g
   return decode_impl(shape, q, nullptr, nullptr, nullptr, nullptr, nullptr, ctx_lens, q_pos,
                      window, softcap, scale, out, workspace, workspace_bytes, opts, stream,
                      num_tokens, &f8);
+}
+
+int32_t gemma_attn_decode_append_fp8(const ga_shape* shape, const ga_bf16* q, uint8_t* k_codes,
+                                     float* k_scales, uint8_t* v_codes, float* v_scales,
+                                     const ga_bf16* k_new, const ga_bf16* v_new,
+                                     const int32_t* pos, const int32_t* ctx_lens,
+                                     const int32_t* q_pos, int32_t window, float softcap,
+                                     float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, const ga_decode_opts* opts,
+                                     void* stream) {
+  if (!k_new) return GA_ERR_NULL;
+  const Fp8Cache f8{k_codes, k_scales, v_codes, v_scales};
+  return decode_impl(shape, q, nullptr, nullptr, k_new, v_new, pos, ctx_lens, q_pos, window,
+                     softcap, scale, out, workspace, workspace_bytes, opts, stream, 1, &f8);
 }
 
 int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* k_codes,

@@ -31,6 +31,7 @@
 
 #include "ga_device.h"
 #include "ga_internal.h"
+#include "ga_quant.h"
 #include "ga_rope.h"
 
 namespace ga {
@@ -124,8 +125,24 @@ __global__ void __launch_bounds__(NW_ * 64)
   // Fused append: split 0 of each unit moves the new row; its loads are issued here and
   // the stores happen after the key loop, so nothing waits on them.
   const int new_slot = appended_slot(a, b);
-  AppendRow app;
-  app.load(a, b, g, new_slot, threadIdx.x, split == 0);
+  AppendRow app;  // (bf16 rows; fp8 caches append their quantized rows below)
+  app.load(a, b, g, new_slot, threadIdx.x, !FP8 && split == 0);
+  // FP8 fused append (one token): wave 0 quantizes the new K row and wave 1 the new V row
+  // (wave 0 both with one wave) exactly as the quantizing append does; their loads go out
+  // here, ahead of the first K rows.
+  constexpr bool APP8 = FP8 && !MULTI;
+  constexpr int NROW8 = KV_SHARED ? 1 : 2;
+  const bool app8 = APP8 && new_slot >= 0;  // the same in the whole work-group
+  uint4 src8[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if constexpr (APP8) {
+    if (app8 && lane < D / 8) {
+      const size_t at = ((size_t)b * a.Hkv + g) * (D / 8) + lane;
+#pragma unroll
+      for (int rr = 0; rr < NROW8; ++rr)
+        if (NW == 1 || wave == rr)
+          src8[rr] = reinterpret_cast<const uint4*>(rr ? a.v_new : a.k_new)[at];
+    }
+  }
   // Query rows of this unit in this lane's element order, as packed bf16 pairs for the
   // dot2 products (fp8 keys are widened exactly to bf16 pairs first).  Loaded before the
   // context length is known (they do not depend on it), so the two latencies overlap.
@@ -263,6 +280,45 @@ __global__ void __launch_bounds__(NW_ * 64)
       }
     }
   }
+  // FP8 fused append: the quantized rows into LDS, this lane's chunks of them and their
+  // scales into registers (they replace the appended key's loaded rows where the loop
+  // consumes them), and the first split stores them into the slot.  Every reader of that
+  // slot in this launch is a work-group of this unit and takes the registers, so when the
+  // store lands does not matter.
+  __shared__ __attribute__((aligned(16))) uint8_t s_c8[APP8 ? 2 * D : 16];
+  __shared__ float s_c8s[2];
+  Chunk kf8[APP8 ? NCH : 1], vf8[APP8 ? NCH : 1];
+  float sf8[2] = {1.0f, 1.0f};
+  if constexpr (APP8) {
+    if (app8) {
+      if (wave < NROW8) {
+        const size_t row8 = ((size_t)b * a.Hkv + g) * a.cap + new_slot;
+#pragma unroll
+        for (int rr = 0; rr < NROW8; ++rr) {
+          if (NW > 1 && wave != rr) continue;  // (the same in the whole wave)
+          float s8;
+          const uint2 c8 = quantize_row_e4m3(src8[rr], lane < D / 8, &s8);
+          if (lane < D / 8) {
+            *reinterpret_cast<uint2*>(s_c8 + rr * D + 8 * lane) = c8;
+            if (split == 0) reinterpret_cast<uint2*>((rr ? a.v8_dst : a.k8_dst) + row8 * D)[lane] = c8;
+          }
+          if (lane == 0) {
+            s_c8s[rr] = s8;
+            if (split == 0) (rr ? a.vs_dst : a.ks_dst)[row8] = s8;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        kf8[c] = *reinterpret_cast<const Chunk*>(s_c8 + EPC * (c * L + j));
+        if constexpr (!KV_SHARED) vf8[c] = *reinterpret_cast<const Chunk*>(s_c8 + D + EPC * (c * L + j));
+      }
+      sf8[0] = s_c8s[0];
+      sf8[1] = KV_SHARED ? sf8[0] : s_c8s[1];
+    }
+  }
+
   const RowRange r = unit_range(a, b, chunk);
   const int k_end = min(r.n, k_begin + a.split_keys);
   if (k_begin >= k_end) {
@@ -366,13 +422,29 @@ __global__ void __launch_bounds__(NW_ * 64)
     // The key rows; with ROPE the appended key (its slot's load read the unrotated k_new)
     // takes the rotated row held in registers, selected here where the loaded rows are
     // consumed, so the loads themselves stay unconditional.
-    Chunk kx[NCH];
+    // (FP8 appending: the appended key's quantized rows and scales likewise.)
+    Chunk kx[NCH], vx[NCH];
+    float scx[2] = {sc[0], sc[1]};
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kx[c] = kr[c];
+    for (int c = 0; c < NCH; ++c) {
+      kx[c] = kr[c];
+      vx[c] = vr[c];
+    }
     if constexpr (ROPE) {
       if (key_slot(slot_base, valid ? i : k_end - 1, a.cap) == new_slot) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) kx[c] = kfresh[c];
+      }
+    }
+    if constexpr (APP8) {
+      if (app8 && key_slot(slot_base, valid ? i : k_end - 1, a.cap) == new_slot) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          kx[c] = kf8[c];
+          if constexpr (!KV_SHARED) vx[c] = vf8[c];
+        }
+        scx[0] = sf8[0];
+        scx[1] = sf8[1];
       }
     }
     const int pos = r.lo + i;  // absolute position of the key (MULTI masks)
@@ -389,7 +461,7 @@ __global__ void __launch_bounds__(NW_ * 64)
           d0 = dot2_bf16(qr[hh][e2], kb[e2], d0);
           d1 = dot2_bf16(qr[hh][e2 + 1], kb[e2 + 1], d1);
         }
-        s[hh] = group_sum<L>(d0 + d1) * sc[0];
+        s[hh] = group_sum<L>(d0 + d1) * scx[0];
       }
     } else {
 #pragma unroll
@@ -423,11 +495,11 @@ __global__ void __launch_bounds__(NW_ * 64)
       p[hh] = vh ? exp2_fast(x - m[hh]) : 0.0f;
       l[hh] += p[hh];
     }
-    const Chunk(&vv)[NCH] = KV_SHARED ? kx : vr;
+    const Chunk(&vv)[NCH] = KV_SHARED ? kx : vx;
     if constexpr (FP8) {
       float pv[G];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) pv[hh] = p[hh] * sc[1];
+      for (int hh = 0; hh < G; ++hh) pv[hh] = p[hh] * scx[1];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         float vf[EPC];

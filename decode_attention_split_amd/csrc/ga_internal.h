@@ -50,6 +50,11 @@ struct DecodeArgs {
   // fp8 e4m3 caches (fp8 != 0): codes [B, Hkv, cap, D] and float32 row scales
   // [B, Hkv, cap]; for K = V the V fields equal the K fields.
   int fp8 = 0;
+  // fp8 fused append (single token): where the quantized new rows go (codes, scales)
+  uint8_t* k8_dst = nullptr;
+  float* ks_dst = nullptr;
+  uint8_t* v8_dst = nullptr;  // nullptr for K = V
+  float* vs_dst = nullptr;
   const uint8_t* k8 = nullptr;
   const uint8_t* v8 = nullptr;
   const float* k_scale = nullptr;

@@ -2,6 +2,7 @@
 // debug kernels (precondition flags, key-range dump).  gfx950.
 #include "ga_device.h"
 #include "ga_internal.h"
+#include "ga_quant.h"
 #include "ga_rope.h"
 
 namespace ga {
@@ -168,30 +169,10 @@ __device__ __forceinline__ void quantize_store_row(const uint4* src, uint2* dst_
                                                    float* dst_scale, int lane, int chunks) {
   const bool on = lane < chunks;
   const uint4 w = on ? src[lane] : make_uint4(0, 0, 0, 0);
-  float x[8];
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_lo(ws[i]);
-    x[2 * i + 1] = bf16_hi(ws[i]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] * inv, -448.0f), 448.0f);
-  // codes of elements 0..3 in bytes 0..3 of the first dword, 4..7 in the second (the
-  // second operand of each conversion lands in the higher byte of its pair)
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-  if (on) dst_codes[lane] = make_uint2((uint32_t)w0, (uint32_t)w1);
-  if (lane == 0) *dst_scale = amax / 448.0f;
+  float scale;
+  const uint2 codes = quantize_row_e4m3(w, on, &scale);
+  if (on) dst_codes[lane] = codes;
+  if (lane == 0) *dst_scale = scale;
 }
 
 __global__ void __launch_bounds__(64)

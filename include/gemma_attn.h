@@ -266,6 +266,28 @@ int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const g
                               size_t workspace_bytes, const ga_decode_opts* opts, void* stream);
 
 /*
+ * Quantizing append of one token fused with single-token decode over fp8 caches: exactly
+ * gemma_kv_append_fp8(shape, 1, k_codes, k_scales, v_codes, v_scales, k_new, v_new, pos)
+ * followed by gemma_attn_decode_fp8(shape, 1, q, k_codes, k_scales, v_codes, v_scales,
+ * ctx_lens, q_pos, ...), bit for bit (codes, scales and out).  Where the vector kernel
+ * serves the call (the sliding geometry), one launch does both: one wave of each
+ * work-group quantizes the new rows with the append's own arithmetic, every reader of the
+ * appended slot takes those codes and scales from registers, and the first split stores
+ * them.  On the matrix cores (the K = V global geometry) the quantizing append runs first.
+ * k_new, v_new [B, Hkv, D] device bf16 (v_new NULL exactly when v_codes is, K = V) and
+ * pos [B] device int32, non-NULL; other arguments and errors as in the two calls;
+ * workspace: ga_decode_fp8_workspace_bytes(shape, 1, window, opts).
+ */
+int32_t gemma_attn_decode_append_fp8(const ga_shape* shape, const ga_bf16* q, uint8_t* k_codes,
+                                     float* k_scales, uint8_t* v_codes, float* v_scales,
+                                     const ga_bf16* k_new, const ga_bf16* v_new,
+                                     const int32_t* pos, const int32_t* ctx_lens,
+                                     const int32_t* q_pos, int32_t window, float softcap,
+                                     float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, const ga_decode_opts* opts,
+                                     void* stream);
+
+/*
  * cos / sin table of the rotary embedding of one token per row, at position pos[b]:
  *   table[b, i, 0] = cos(pos[b] * rope_base^(-2i/R)), table[b, i, 1] = sin(...)
  * for the R / 2 rotate-half pairs i of R = rotary_dim (definition at gemma_rope_append),

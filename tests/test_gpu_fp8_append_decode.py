@@ -1,0 +1,102 @@
+"""GPU: the quantizing append fused with single-token decode over fp8 caches.
+
+gemma_attn_decode_append_fp8 promises the bits of gemma_kv_append_fp8 (one token) then
+gemma_attn_decode_fp8: the same codes and scales in the caches and the same output.  On
+the vector kernel one launch does both (each work-group quantizes the new rows with the
+append's arithmetic and substitutes them for the appended key); on the matrix cores the
+append runs first.  Each case runs both routes on copies of the same caches and compares
+bit for bit; one case also checks the caches and the output against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_split_amd import api, synth
+
+from common import assert_parity, default_scale, log
+from test_gpu_fp8 import Fp8Inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _new_rows(seed, B, Hkv, D, k_eq_v):
+    gen = synth.generator(seed)
+    kn = synth.normal_bf16(gen, (B, Hkv, D)) * 3
+    kn[1, 0] = 0  # an all-zero row: codes 0, scale 0
+    vn = None if k_eq_v else synth.normal_bf16(gen, (B, Hkv, D))
+    return kn, vn
+
+
+def _both_routes(inp, kn, vn, window, softcap, kind, max_ctx, split_keys=0, impl=api.IMPL_AUTO):
+    q = inp.q[:, 0].contiguous()
+    pos = inp.ctx_t - 1
+    c = lambda t: None if t is None else t.clone()
+    kd, vd = kn.cuda(), None if vn is None else vn.cuda()
+    scale = default_scale(kn.shape[-1])
+    # one call
+    f = [c(inp.kc_d), c(inp.ks_d), c(inp.vc_d), c(inp.vs_d)]
+    out_f = api.decode_append_fp8(q, f[0], f[1], f[2], f[3], kd, vd, pos, inp.ctx_t, pos, window,
+                                  softcap, scale, kind, max_ctx=max_ctx, split_keys=split_keys,
+                                  deterministic=True, impl=impl)
+    # the two calls
+    r = [c(inp.kc_d), c(inp.ks_d), c(inp.vc_d), c(inp.vs_d)]
+    api.kv_append_fp8(r[0], r[1], r[2], r[3], kd[:, None], None if vd is None else vd[:, None],
+                      pos, kind)
+    out_r = api.decode_fp8(q, r[0], r[1], r[2], r[3], inp.ctx_t, pos, window, softcap, scale,
+                           kind, max_ctx=max_ctx, split_keys=split_keys, deterministic=True,
+                           impl=impl)
+    torch.cuda.synchronize()
+    for a, b, what in zip(f, r, ("K codes", "K scales", "V codes", "V scales")):
+        if a is not None:
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), what
+    assert torch.equal(out_f.view(torch.int32), out_r.view(torch.int32)), "output bits"
+    return out_f, f
+
+
+@pytest.mark.parametrize("D,G,Hkv,k_eq_v,kind,impl", [
+    (256, 2, 4, False, api.RING, api.IMPL_AUTO),     # 12B sliding geometry
+    (128, 4, 2, False, api.LINEAR, api.IMPL_AUTO),
+    (256, 1, 2, True, api.RING, api.IMPL_AUTO),      # K = V on the vector kernel
+    (256, 8, 1, False, api.RING, api.IMPL_AUTO),
+    (512, 16, 1, True, api.LINEAR, api.IMPL_AUTO),   # global geometry: matrix cores, 2 launches
+    (512, 16, 1, True, api.LINEAR, api.IMPL_VALU),   # global geometry on the vector kernel
+])
+@pytest.mark.parametrize("split_keys", [0, 64])
+def test_fused_fp8_append_decode_equals_two_calls(D, G, Hkv, k_eq_v, kind, impl, split_keys):
+    if impl == api.IMPL_AUTO and G == 16 and split_keys:
+        pytest.skip("the matrix cores take no split size")
+    if kind == api.RING:
+        cap = window = 100
+        ctx = [0, 1, 37, 100, 503]   # an empty row (nothing appended), partial, full, wrapped
+        max_ctx = max(ctx)
+    else:
+        cap, window = 300, 0
+        ctx = [0, 1, 150, 299, 300]
+        max_ctx = cap
+    log(f"fp8 append+decode D={D} G={G} Hkv={Hkv} K=V={k_eq_v} kind={kind} impl={impl} "
+        f"split={split_keys}")
+    inp = Fp8Inputs(D + G + kind + split_keys, len(ctx), 1, G * Hkv, Hkv, D, cap, k_eq_v,
+                    ctx).to_device()
+    kn, vn = _new_rows(D + G, len(ctx), Hkv, D, k_eq_v)
+    _both_routes(inp, kn, vn, window, 30.0 if G % 2 == 0 else 0.0, kind, max_ctx, split_keys,
+                 impl)
+
+
+def test_fused_fp8_append_decode_matches_oracle():
+    """Caches after the one call equal the oracle's quantizing append, and the output the
+    oracle's decode over those caches."""
+    D, G, Hkv, W = 256, 2, 4, 100
+    ctx = [2, 100, 503]
+    inp = Fp8Inputs(77, len(ctx), 1, G * Hkv, Hkv, D, W, False, ctx).to_device()
+    kn, vn = _new_rows(78, len(ctx), Hkv, D, False)
+    out, f = _both_routes(inp, kn, vn, W, 0.0, api.RING, max(ctx), split_keys=64)
+    pos = np.asarray(ctx, np.int32) - 1
+    oracle.append_fp8(inp.kc, inp.ks, synth.bits(kn)[:, None], pos, api.RING)
+    oracle.append_fp8(inp.vc, inp.vs, synth.bits(vn)[:, None], pos, api.RING)
+    assert np.array_equal(f[0].cpu().numpy(), inp.kc)
+    assert np.array_equal(f[1].cpu().numpy().view(np.uint32), inp.ks.view(np.uint32))
+    assert np.array_equal(f[2].cpu().numpy(), inp.vc)
+    assert np.array_equal(f[3].cpu().numpy().view(np.uint32), inp.vs.view(np.uint32))
+    ref, _ = inp.oracle(W, 0.0, default_scale(D), api.RING)
+    assert_parity(out.unsqueeze(1), ref, "fused fp8 append + decode")
