@@ -114,6 +114,7 @@ TRAFFIC_SOURCES = ["decode_attention_split_amd/csrc/decode_valu_impl.h",
                    "decode_attention_split_amd/csrc/ga_device.h",
                    "decode_attention_split_amd/csrc/ga_internal.h",
                    "decode_attention_split_amd/csrc/ga_rope.h",
+                   "decode_attention_split_amd/csrc/ga_quant.h",
                    "decode_attention_split_amd/csrc/api.hip"]
 DOMINANT = "decode_valu_kernel<256, 2"
 COPY_BYTES = 1 << 30
