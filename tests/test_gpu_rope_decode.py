@@ -157,3 +157,49 @@ def test_rope_table_matches_definition(base, R):
     np.testing.assert_allclose(tab[..., 0], np.cos(ang), rtol=0, atol=1e-10)
     np.testing.assert_allclose(tab[..., 1], np.sin(ang), rtol=0, atol=1e-10)
     assert (tab[0, :, 0] == 1.0).all() and (tab[0, :, 1] == 0.0).all()
+
+
+@pytest.mark.parametrize("layer", [0, 5])
+def test_rope_step_layer_full_size_sampled_rows(layer):
+    """The 48-layer RoPE step's layers at full size, in the launch the bench times (one
+    call per layer on the step's cos / sin table): sliding layer 0 (one launch) and global
+    layer 5 (matrix cores: two launches), sampled rows against the oracle's rotate, append,
+    attend."""
+    from decode_attention_split_amd import workloads as wl
+    from common import gen_layer
+    import oracle
+    w = wl.HYBRID_48_ROPE
+    g = w.layers[layer]
+    log(f"rope step layer {layer}: {'global' if g.k_eq_v else 'sliding'} R={g.rotary_dim}")
+    inp = gen_layer(wl.layer_seed(w, layer), w.batch, g.num_q_heads, g.num_kv_heads,
+                    g.head_dim, g.capacity, g.k_eq_v, w.ctx_lo, w.ctx_hi).to_device()
+    gen = synth.generator(1000 + layer)
+    kn = synth.normal_bf16(gen, (w.batch, g.num_kv_heads, g.head_dim))
+    vn = None if g.k_eq_v else synth.normal_bf16(gen, (w.batch, g.num_kv_heads, g.head_dim))
+    pos_t = inp.ctx_t - 1
+    max_ctx = min(w.ctx_hi, g.capacity) if g.kind == api.LINEAR else w.ctx_hi
+    table = api.rope_table(pos_t, g.rope_base, g.rotary_dim)
+    q_out = torch.empty_like(inp.q)
+    out = api.decode_rope_append(inp.q, q_out, inp.k, inp.v, kn.cuda(),
+                                 None if vn is None else vn.cuda(), pos_t, inp.ctx_t, pos_t,
+                                 g.window, g.softcap, g.q_scale, g.kind, table, g.rotary_dim,
+                                 max_ctx=max_ctx)
+    torch.cuda.synchronize()
+    rows = sorted({0, 7, int(np.argmax(inp.ctx)), int(np.argmin(inp.ctx))})
+    pos = inp.ctx[rows].astype(np.int64) - 1
+    q_ref, _ = oracle.rope(inp.q_bits[rows], np.repeat(pos, g.num_q_heads), g.rope_base,
+                           g.rotary_dim)
+    kn_ref, _ = oracle.rope(synth.bits(kn)[rows], np.repeat(pos, g.num_kv_heads), g.rope_base,
+                            g.rotary_dim)
+    k_ref = inp.k_bits[rows].copy()
+    v_ref = None if vn is None else inp.v_bits[rows].copy()
+    for i, p in enumerate(pos):
+        s = p % g.capacity if g.kind == api.RING else p
+        k_ref[i, :, s] = kn_ref[i]
+        if v_ref is not None:
+            v_ref[i, :, s] = synth.bits(vn)[rows[i]]
+    diff = synth.bits(q_out.cpu())[rows].astype(np.int32) - q_ref.astype(np.int32)
+    assert (np.abs(diff) <= 1).all() and (diff != 0).sum() <= max(2, diff.size // 10000)
+    ref = oracle_out(LayerInputs(q_ref, k_ref, v_ref, inp.ctx[rows], pos), g.window, g.softcap,
+                     g.q_scale, g.kind)
+    assert_parity(out[rows], ref, f"rope step layer {layer} rows {rows}")
