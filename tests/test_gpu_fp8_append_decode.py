@@ -100,3 +100,45 @@ def test_fused_fp8_append_decode_matches_oracle():
     assert np.array_equal(f[3].cpu().numpy().view(np.uint32), inp.vs.view(np.uint32))
     ref, _ = inp.oracle(W, 0.0, default_scale(D), api.RING)
     assert_parity(out.unsqueeze(1), ref, "fused fp8 append + decode")
+
+
+def test_fused_fp8_sliding_layer_full_size_sampled_rows():
+    """The 12B fp8 sliding layer at full size in the launch the bench times: the cache filled
+    by a quantizing append of the previous 1023 tokens, then the current token appended and
+    attended in one call; sampled rows against the oracle (the new slot's codes and scales,
+    and the output over the resulting cache)."""
+    from decode_attention_split_amd import workloads as wl
+    w = wl.G4_12B_SLIDING
+    g = w.layers[0]
+    B, Hkv, D, W = w.batch, g.num_kv_heads, g.head_dim, g.capacity
+    ctx = synth.uniform_int(synth.generator(w.seed), B, w.ctx_lo, w.ctx_hi).numpy() \
+        .astype(np.int32)
+    gd = synth.generator(91, device="cuda")
+    kc = torch.empty((B, Hkv, W, D), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty((B, Hkv, W), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    ctx_t = torch.from_numpy(ctx).cuda()
+    old = synth.normal_bf16(gd, (B, W - 1, Hkv, D), device="cuda")
+    api.kv_append_fp8(kc, ks, vc, vs, old, synth.normal_bf16(gd, old.shape, device="cuda"),
+                      ctx_t - W, api.RING)
+    kn = synth.normal_bf16(gd, (B, Hkv, D), device="cuda")
+    vn = synth.normal_bf16(gd, (B, Hkv, D), device="cuda")
+    q = synth.normal_bf16(gd, (B, g.num_q_heads, D), device="cuda")
+    out = api.decode_append_fp8(q, kc, ks, vc, vs, kn, vn, ctx_t - 1, ctx_t, ctx_t - 1,
+                                g.window, g.softcap, g.q_scale, g.kind, max_ctx=w.ctx_hi)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, int(np.argmax(ctx)), int(np.argmin(ctx))})
+    log(f"fused fp8 sliding rows {rows}")
+    kcr, ksr = kc[rows].cpu().numpy(), ks[rows].cpu().numpy()
+    vcr, vsr = vc[rows].cpu().numpy(), vs[rows].cpu().numpy()
+    for i, b in enumerate(rows):
+        slot = (int(ctx[b]) - 1) % W
+        c, s = oracle.quantize_rows_fp8(synth.bits(kn[b].cpu()))
+        assert np.array_equal(kcr[i, :, slot], c) and np.array_equal(ksr[i, :, slot], s)
+        c, s = oracle.quantize_rows_fp8(synth.bits(vn[b].cpu()))
+        assert np.array_equal(vcr[i, :, slot], c) and np.array_equal(vsr[i, :, slot], s)
+    ref, _, _, _ = oracle.decode_fp8_multi(synth.bits(q[rows].cpu())[:, None], kcr, ksr, vcr, vsr,
+                                           ctx[rows], ctx[rows] - 1, g.window, g.softcap,
+                                           g.q_scale, g.kind)
+    assert_parity(out[rows].unsqueeze(1), ref, "fused fp8 sliding full size")
