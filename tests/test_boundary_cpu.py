@@ -251,3 +251,65 @@ def test_append_multi_argument_checks():
                                      P(FAKE), None) == -9
     assert lib.gemma_attn_validate_multi(ctypes.byref(shape(cap=1024, max_ctx=8192)), 8, P(FAKE),
                                          P(FAKE), 1024, P(FAKE), None) == -6
+
+
+def test_rope_table_argument_checks():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    assert lib.gemma_rope_table(-1, P(FAKE), 1e4, 256, P(FAKE), None) == -2   # batch < 0
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 255, P(FAKE), None) == -2    # R odd
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, -2, P(FAKE), None) == -2     # R < 0
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 514, P(FAKE), None) == -14   # R > 512
+    assert lib.gemma_rope_table(4, P(FAKE), 0.0, 256, P(FAKE), None) == -12   # base <= 0
+    assert lib.gemma_rope_table(4, P(FAKE), math.inf, 256, P(FAKE), None) == -12
+    assert lib.gemma_rope_table(4, None, 1e4, 256, P(FAKE), None) == -1
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 256, None, None) == -1
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 256, P(FAKE + 8), None) == -1  # alignment
+    # nothing to compute: OK without touching a device
+    assert lib.gemma_rope_table(0, None, 1e4, 256, None, None) == 0
+    assert lib.gemma_rope_table(4, None, 1e4, 0, None, None) == 0
+
+
+def test_decode_rope_append_argument_checks():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    s = shape()
+
+    def call(q_out=FAKE, k_new=FAKE, table=FAKE, R=256, v=FAKE, v_new=FAKE):
+        return lib.gemma_attn_decode_rope_append(
+            ctypes.byref(s), P(FAKE), P(q_out) if q_out else None, P(FAKE),
+            P(v) if v else None, P(k_new) if k_new else None, P(v_new) if v_new else None,
+            P(FAKE), P(FAKE), P(FAKE), 1024, 0.0, 0.0625, P(table) if table else None, R, P(FAKE),
+            P(FAKE), 1 << 40, None, None)
+    assert call(q_out=0) == -1
+    assert call(q_out=FAKE + 8) == -1
+    assert call(k_new=0) == -1
+    assert call(R=255) == -12
+    assert call(R=258) == -12      # > head_dim
+    assert call(R=-2) == -12
+    assert call(table=0) == -1     # a rotary part needs the table
+    assert call(table=FAKE + 8) == -1
+    assert call(v_new=0) == -9     # v_cache without v_new
+    if no_gpu():
+        assert call(table=0, R=0) == -10  # valid: reaches the device check
+        assert call() == -10
+
+
+def test_decode_append_fp8_argument_checks():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    s = shape()
+
+    def call(k_new=FAKE, v_codes=FAKE, v_scales=FAKE, v_new=FAKE, pos=FAKE):
+        return lib.gemma_attn_decode_append_fp8(
+            ctypes.byref(s), P(FAKE), P(FAKE), P(FAKE), P(v_codes) if v_codes else None,
+            P(v_scales) if v_scales else None, P(k_new) if k_new else None,
+            P(v_new) if v_new else None, P(pos) if pos else None, P(FAKE), P(FAKE), 1024, 0.0,
+            0.0625, P(FAKE), P(FAKE), 1 << 40, None, None)
+    assert call(k_new=0) == -1
+    assert call(pos=0) == -1
+    assert call(v_new=0) == -9              # V codes without V rows
+    assert call(v_scales=0) == -9           # V codes without V scales
+    if no_gpu():
+        assert call() == -10
+        assert call(v_codes=0, v_scales=0, v_new=0) == -10  # K = V
