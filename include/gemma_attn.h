@@ -315,8 +315,9 @@ int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int
  * aligned; it may equal q and must not otherwise overlap it.  rope_table as written by
  * gemma_rope_table (may be NULL when rotary_dim is 0).  Workspace: ga_decode_workspace_bytes,
  * as for the decode.  Where the vector kernel serves the call, one launch does it all (the
- * GQA sliding geometry of the Gemma 3 / 4 stacks, "Gemma 3 Technical Report", section 2:
- * local layers, head_dim 256, several query heads per KV head): each work-group rotates
+ * sliding layers: head_dim 256 with their own RoPE base, "Gemma support" pull request,
+ * Summary; 8 KV heads under 16 query heads, "Gemma 4 12B (unified multimodal)" record, KV
+ * geometry): each work-group rotates
  * its unit's query rows and the new K row into LDS, the first split writes the rotated q
  * and appends the rotated row, and every reader of the appended slot takes the rotated row
  * from LDS; with q_out == q that needs a single split per row.  Otherwise (matrix-core
@@ -367,7 +368,12 @@ enum {
 
 /*
  * Debug check of the device-side preconditions: writes GA_FLAG_* bits for each row to
- * dev_flags (device int32 [B]) on `stream`.  The decode itself does not need it.
+ * dev_flags (device int32 [B]) on `stream`.  The decode itself does not need it.  Host
+ * arguments are checked as for the decode (same status codes, nothing launched on error).
+ * Passage: "Gemma 4 12B (unified multimodal)" record, "(6) On Apple Silicon": a cache
+ * class that silently grows past its bound or fails only on the first request; this call
+ * reports at call time, per row, which device-side precondition a decode would violate
+ * (the decode itself clamps every index and never reads out of bounds).
  */
 int32_t gemma_attn_validate(const ga_shape* shape, const int32_t* ctx_lens, const int32_t* q_pos,
                             int32_t window, int32_t* dev_flags, void* stream);
@@ -382,15 +388,21 @@ int32_t gemma_attn_validate_multi(const ga_shape* shape, int32_t num_tokens,
  * Debug dump of the key range each row attends to, computed by the same device code
  * the decode kernels use: dev_out (device int32 [B, 4]) receives
  * (lo, hi, slot(lo), n) with n = hi - lo + 1 (n = 0 and lo = hi + 1 for an empty row).
+ * Passage: "Gemma 4 12B (unified multimodal)" record, "required kernel class" (a local
+ * layer reads exactly w entries) and "(2) On B200" (a kernel that picked the wrong window
+ * keys at some sequence-length alignments): the dump lets a caller check, bit for bit,
+ * which positions the kernels select.  Errors as for gemma_attn_validate.
  */
 int32_t gemma_attn_debug_ranges(const ga_shape* shape, const int32_t* ctx_lens,
                                 const int32_t* q_pos, int32_t window, int32_t* dev_out,
                                 void* stream);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL).  Every failure is reported by a
+ * distinct code at call time rather than silently ("Gemma 4 12B (unified multimodal)"
+ * record, "(6) On Apple Silicon"). */
 const char* gemma_attn_strerror(int32_t status);
 
-/* Library version, as major * 10000 + minor * 100 + patch. */
+/* Library version, as major * 10000 + minor * 100 + patch (no passage: bookkeeping). */
 int32_t gemma_attn_version(void);
 
 #ifdef __cplusplus

@@ -55,9 +55,15 @@
  * request, Summary: own RoPE base for sliding layers, proportional RoPE; "Gemma4-26B-A4B
  * on Apple Silicon", Results (Break 4): dual bases, partial rotary on full layers, and
  * Ablations / negative controls: the rotary acts on the low portion of the head dimension;
- * the model-loader page's header: bases 10,000 and 1,000,000).  Readings: the first R (even) elements rotate in rotate-half pairs
- * (i, i + R/2), angle p * base^(-2i/R) for i < R/2; the rest pass through; computed in
- * double and rounded once to bf16 (round to nearest even).
+ * the model-loader page's header: bases 10,000 and 1,000,000).  Readings: the first R
+ * (even) elements rotate in rotate-half pairs (i, i + R/2), angle p * base^(-2i/R) for
+ * i < R/2; the rest pass through; computed in double and rounded once to bf16 (round to
+ * nearest even).
+ * PARITY UNPINNED for the full-layer case: the exponent over the rotated width R (not
+ * over D), the width R itself (the callers pass R = D/4 on full layers) and the use of
+ * the rotated key row as the value row on K = V layers are readings that nothing on the
+ * pages fixes, so no test can tell them from another plausible reading.  The rotate-half
+ * pairing, the per-pair angle, the rotation itself and the single rounding are pinned.
  *
  * Arithmetic: every bf16 input is widened exactly (bits << 16 -> float -> double);
  * scale and softcap are widened from their float32 values; libm exp, tanh, log in

@@ -55,12 +55,18 @@ def gen_layer(seed, B, Hq, Hkv, D, cap, k_eq_v, ctx_lo, ctx_hi, ctx=None):
 def poison_invalid_slots(inp: LayerInputs, window, kind, cap):
     """Fill every slot outside each row's valid set (per the oracle) with bf16 NaN, so
     any stray read turns the GPU output NaN."""
-    for bits in [inp.k_bits] + ([inp.v_bits] if inp.v_bits is not None else []):
-        for b in range(bits.shape[0]):
-            _, slots = oracle.valid_positions(inp.ctx[b], inp.qpos[b], window, kind, cap)
-            keep = np.zeros(cap, bool)
-            keep[slots] = True
-            bits[b][:, ~keep, :] = BF16_NAN
+    for b in range(inp.ctx.shape[0]):
+        _, slots = oracle.valid_positions(inp.ctx[b], inp.qpos[b], window, kind, cap)
+        keep = np.zeros(cap, bool)
+        keep[slots] = True
+        drop = np.flatnonzero(~keep)
+        if drop.size == 0:
+            continue
+        for bits in [inp.k_bits] + ([inp.v_bits] if inp.v_bits is not None else []):
+            if drop[-1] - drop[0] + 1 == drop.size:  # one run of slots: a plain slice
+                bits[b][:, drop[0]:drop[-1] + 1, :] = BF16_NAN
+            else:
+                bits[b][:, drop, :] = BF16_NAN
 
 
 def oracle_out(inp: LayerInputs, window, softcap, scale, kind, rows=None):

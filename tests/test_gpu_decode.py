@@ -58,8 +58,9 @@ def test_global_layer_full_size_sampled_rows():
     w = wl.G4_12B_GLOBAL
     g = w.layers[0]
     log(f"full size: {w.name}")
-    inp = layer_case(w.seed, w.batch, g, w.ctx_lo, w.ctx_hi, poison=False)
+    inp = layer_case(w.seed, w.batch, g, w.ctx_lo, w.ctx_hi)  # never-valid slots NaN
     out = run(inp, g.window, g.softcap, g.q_scale, g.kind)
+    assert torch.isfinite(out).all(), "a never-valid slot was read"
     rows = sorted({0, 1, int(np.argmax(inp.ctx)), int(np.argmin(inp.ctx))})
     ref = oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind, rows=rows)
     assert_parity(out[rows], ref, f"{w.name} rows {rows}")
@@ -70,9 +71,10 @@ def test_hybrid_step_layer_sampled_rows(layer):
     w = wl.HYBRID_48
     g = w.layers[layer]
     log(f"hybrid layer {layer}: {'global' if g.k_eq_v else 'sliding'}")
-    inp = layer_case(wl.layer_seed(w, layer), w.batch, g, w.ctx_lo, w.ctx_hi, poison=False)
+    inp = layer_case(wl.layer_seed(w, layer), w.batch, g, w.ctx_lo, w.ctx_hi)  # NaN-poisoned
     out = run(inp, g.window, g.softcap, g.q_scale, g.kind, max_ctx=min(w.ctx_hi, g.capacity)
               if g.kind == api.LINEAR else w.ctx_hi)
+    assert torch.isfinite(out).all(), "a never-valid slot was read"
     rows = sorted({0, 7, int(np.argmax(inp.ctx)), int(np.argmin(inp.ctx))})
     ref = oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind, rows=rows)
     assert_parity(out[rows], ref, f"hybrid layer {layer} rows {rows}")

@@ -215,3 +215,48 @@ def test_matrix_core_multi_token_repeats_bits(D, G, Hkv, k_eq_v, split):
         assert torch.equal(first, again)
     ref, _ = inp.oracle(*args)
     assert_parity(first, ref, f"repeat D={D} split={split}")
+
+
+# ------------------------------------------------------------------ chunked prefill sizes
+
+def _prefill_ctxs(T, w):
+    """Contexts around window and ring edges for a chunk of T tokens ending at ctx - 1."""
+    return [T, w - 1, w, w + 1, w + T - 1, w + T, 2 * w + 3, 3 * w + T - 5]
+
+
+@pytest.mark.parametrize("T", [64, 256])
+@pytest.mark.parametrize("impl", [api.IMPL_AUTO, api.IMPL_VALU], ids=["auto", "valu"])
+def test_chunked_prefill_sliding_12b_geometry(T, impl):
+    """A prefill chunk of T = 64 / 256 tokens on the 12B sliding geometry (16 query heads
+    on 8 KV heads, head_dim 256, window 1024, soft-cap 50) over a ring of w + T - 1 slots,
+    contexts at window and ring edges; every never-valid slot poisoned with bf16 NaN.
+    Element-wise against the oracle's multi-token definition."""
+    w = 1024
+    cap = w + T - 1
+    ctx = _prefill_ctxs(T, w)
+    inp = MultiInputs(5000 + T, len(ctx), T, 16, 8, 256, cap, False, ctx)
+    inp.poison(w, api.RING).to_device()
+    log(f"chunked prefill sliding T={T} impl={impl} ctx={ctx}")
+    ref, flags = inp.oracle(w, 50.0, 1.0 / 16, api.RING)
+    assert not flags.any()
+    for split in ([0, 256] if impl == api.IMPL_AUTO else [0]):
+        out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=max(ctx), split_keys=split, impl=impl)
+        assert_parity(out, ref, f"sliding T={T} impl={impl} split={split}")
+
+
+@pytest.mark.parametrize("T", [64, 256])
+def test_chunked_prefill_global_kv_shared_geometry(T):
+    """A prefill chunk of T tokens on the K = V global geometry (16 query heads on one KV
+    head, head_dim 512, linear cache, full causal): each token sees every position up to
+    its own.  Positions past ctx - 1 are poisoned with bf16 NaN."""
+    C = 4096
+    ctx = [T, T + 1, 700, 1500] if T == 256 else [T, 1000, 2047, 3001]
+    inp = MultiInputs(6000 + T, len(ctx), T, 16, 1, 512, C, True, ctx)
+    inp.poison(0, api.LINEAR).to_device()
+    log(f"chunked prefill global T={T} ctx={ctx}")
+    scale = default_scale(512)
+    ref, flags = inp.oracle(0, 0.0, scale, api.LINEAR)
+    assert not flags.any()
+    for split in [0, 512]:
+        out = inp.run(0, 0.0, scale, api.LINEAR, max_ctx=C, split_keys=split)
+        assert_parity(out, ref, f"global T={T} split={split}")
