@@ -15,10 +15,15 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-// Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other.
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other; and the
+// device's compute-unit count (read with it).
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
-constexpr int kTargetBlocks = 256;   // one work-group per CU of an MI355X
+// Work-groups wanted to cover the chip: one per CU.  Plans made before the device is
+// known (workspace sizes, host-side checks) assume the most CUs a gfx950 device has, so
+// the workspace they size covers any launch on a device with fewer.
+constexpr int kTargetBlocks = ga::kMaxBlocks;
 constexpr int kMaxSplitKeys = 65536;
 #ifndef GA_MULTI_MAX_ROWS
 #define GA_MULTI_MAX_ROWS 8
@@ -34,7 +39,7 @@ int32_t check_arch() {
     return GA_ERR_ARCH;
   }
   if (dev >= kMaxDevices) return GA_ERR_ARCH;
-  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  int st = g_arch_ok[dev].load(std::memory_order_acquire);
   if (st == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -42,9 +47,20 @@ int32_t check_arch() {
       return GA_ERR_ARCH;
     }
     st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    const int cus = prop.multiProcessorCount;
+    g_cus[dev].store(cus < 1 ? 1 : (cus > ga::kMaxBlocks ? ga::kMaxBlocks : cus),
+                     std::memory_order_relaxed);
+    g_arch_ok[dev].store(st, std::memory_order_release);
   }
   return st == 1 ? GA_OK : GA_ERR_ARCH;
+}
+
+// Compute units of the current device (after a successful check_arch), at most kMaxBlocks.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kTargetBlocks;
+  const int c = g_cus[dev].load(std::memory_order_relaxed);
+  return c > 0 ? c : kTargetBlocks;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -92,6 +108,7 @@ struct Plan {
   int Tc = 1;      // tokens per unit (multi-token)
   int n_chunks = 1;
   bool rows16 = false;  // multi-token on the matrix cores (16 query rows per unit)
+  int mfma_rows = 0;    // global matrix-core path: batch rows per launch
   size_t ws_bytes;
 };
 
@@ -106,7 +123,7 @@ long long max_keys_bound(const ga_shape* s, int32_t window) {
 bool mfma_eligible(const ga_shape* s, bool k_eq_v) {
   const int G = s->num_q_heads / s->num_kv_heads;
   return ga::decode_mfma_supported(s->head_dim, G, k_eq_v) &&
-         (long long)s->batch * s->num_kv_heads <= ga::kMfmaMaxUnits;
+         s->num_kv_heads <= ga::kMfmaMaxUnits;
 }
 
 // Tokens per unit for T query tokens: the largest power of two that keeps heads x tokens
@@ -119,7 +136,8 @@ int tokens_per_unit(int G, int T) {
   return tc;
 }
 
-int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
+int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p,
+                  int n_blocks = kTargetBlocks) {
   const int G = s->num_q_heads / s->num_kv_heads;
   const int Tc = tokens_per_unit(G, T);
   const int n_chunks = (T + Tc - 1) / Tc;
@@ -135,7 +153,7 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
     // Enough work-groups to reach every CU, but at least 128 keys each so the per-split
     // partial (G * (D + 2) floats) stays small next to the split's KV bytes.  Rows that
     // fit one split are written directly, with no partials and no merge launch.
-    long long want_splits = units > 0 ? (kTargetBlocks + units - 1) / units : 1;
+    long long want_splits = units > 0 ? (n_blocks + units - 1) / units : 1;
     long long t = nmax > 0 ? (nmax + want_splits - 1) / want_splits : 64;
     t = (t + 63) / 64 * 64;
     if (t < 128) t = 128;
@@ -158,12 +176,13 @@ int32_t valu_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   return GA_OK;
 }
 
-constexpr int kRows16Waves = 2048;  // waves wanted (8 per CU)
+constexpr int kRows16WavesPerCU = 8;  // waves wanted per CU
 
 // Several tokens on the matrix cores: 16 query rows per unit (16 / G tokens of G heads),
 // splits sized so that about kRows16Waves waves cover the chip (each split is one
 // work-group of ga::decode_rows16_waves waves).
-int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
+int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p,
+                    int n_blocks = kTargetBlocks) {
   const int G = s->num_q_heads / s->num_kv_heads;
   const int Tc = 16 / G;
   const int n_chunks = (T + Tc - 1) / Tc;
@@ -171,7 +190,8 @@ int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   if (window > 0 && nmax > (long long)window + Tc - 1) nmax = (long long)window + Tc - 1;
   const long long units = (long long)s->batch * s->num_kv_heads * n_chunks;
   if (ts == 0) {
-    const long long groups = kRows16Waves / ga::decode_rows16_waves(s->head_dim);
+    const long long groups =
+        (long long)kRows16WavesPerCU * n_blocks / ga::decode_rows16_waves(s->head_dim);
     const long long want = units > 0 ? (groups + units - 1) / units : 1;
     // whole 16-key tiles (the kernel's step), so the last split of a unit is not much
     // shorter than the others; at least 64 keys, so a split outweighs its prologue
@@ -198,19 +218,34 @@ int32_t rows16_plan(const ga_shape* s, int32_t window, int ts, int T, Plan* p) {
   return GA_OK;
 }
 
-void mfma_plan(const ga_shape* s, int32_t window, Plan* p) {
+// Global K = V geometry on the matrix cores: balanced over the chip (ts = 0) or in
+// splits of ts keys.  One launch covers at most ga::kMfmaMaxUnits units (whole rows), and
+// at most 2^31 - 1 keys in all; larger batches run as several launches that reuse the
+// workspace, which is sized for one.
+int32_t mfma_plan(const ga_shape* s, int32_t window, int ts, int n_blocks, Plan* p) {
   long long nmax = max_keys_bound(s, window);
+  if (nmax < 1) nmax = 1;
+  long long rows = ga::kMfmaMaxUnits / s->num_kv_heads;
+  const long long by_keys = ((1LL << 31) - 1) / (nmax * s->num_kv_heads);
+  if (rows > by_keys) rows = by_keys;
+  if (rows < 1) return GA_ERR_TOO_LARGE;
+  if (rows > s->batch) rows = s->batch;
+  const long long units = rows * s->num_kv_heads;
+  const long long grid = ga::decode_mfma_grid((int)units, n_blocks, ts, (int)nmax);
+  if (grid > (1LL << 31) - 1) return GA_ERR_TOO_LARGE;
   p->impl = GA_IMPL_MFMA;
-  p->split_keys = 0;
+  p->split_keys = ts;
   p->n_split = 0;
-  p->max_keys = (int)(nmax > 0 ? nmax : 1);
-  p->ws_bytes = ga::decode_mfma_workspace_bytes(s->batch, s->num_kv_heads);
+  p->max_keys = (int)nmax;
+  p->mfma_rows = (int)rows;
+  p->ws_bytes = units > 0 ? ga::decode_mfma_workspace_bytes(grid, (int)units) : 0;
+  return GA_OK;
 }
 
 // k_eq_v: 1 / 0 when known (a decode call), -1 for a workspace query, which then sizes
 // for whichever implementation AUTO may pick.
 int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, int k_eq_v,
-                  Plan* p, int T = 1) {
+                  Plan* p, int T = 1, int n_blocks = kTargetBlocks) {
   int impl = GA_IMPL_AUTO, ts = 0;
   if (o) {
     for (int i = 0; i < 5; ++i)
@@ -230,39 +265,37 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
                                        ga::decode_rows16_supported(s->head_dim, true);
     if (impl == GA_IMPL_MFMA) {
       if (!ok) return GA_ERR_OPTS;
-      return rows16_plan(s, window, ts, T, p);
+      return rows16_plan(s, window, ts, T, p, n_blocks);
     }
     if (impl == GA_IMPL_AUTO && ok && (long long)G * T >= 8) {
-      if (k_eq_v != -1) return rows16_plan(s, window, ts, T, p);
+      if (k_eq_v != -1) return rows16_plan(s, window, ts, T, p, n_blocks);
       Plan v;  // workspace query: size for whichever the call may pick
-      int32_t st = valu_plan(s, window, ts, T, &v);
+      int32_t st = valu_plan(s, window, ts, T, &v, n_blocks);
       if (st != GA_OK) return st;
-      st = rows16_plan(s, window, ts, T, p);
+      st = rows16_plan(s, window, ts, T, p, n_blocks);
       if (st != GA_OK) return st;
       if (v.ws_bytes > p->ws_bytes) p->ws_bytes = v.ws_bytes;
       return GA_OK;
     }
-    return valu_plan(s, window, ts, T, p);
+    return valu_plan(s, window, ts, T, p, n_blocks);
   }
   if (impl == GA_IMPL_MFMA) {
-    // the matrix-core kernel balances keys over a fixed grid: no split size to choose
-    if (ts != 0 || k_eq_v == 0 || !mfma_eligible(s, true)) return GA_ERR_OPTS;
-    mfma_plan(s, window, p);
-    return GA_OK;
+    // the matrix-core kernel balances keys over the chip, or takes the given split size
+    if (k_eq_v == 0 || !mfma_eligible(s, true)) return GA_ERR_OPTS;
+    return mfma_plan(s, window, ts, n_blocks, p);
   }
-  if (impl == GA_IMPL_AUTO && ts == 0 && k_eq_v != 0 && mfma_eligible(s, true)) {
-    if (k_eq_v == 1) {
-      mfma_plan(s, window, p);
-      return GA_OK;
-    }
-    Plan v;
-    int32_t st = valu_plan(s, window, 0, 1, &v);
+  if (impl == GA_IMPL_AUTO && k_eq_v != 0 && mfma_eligible(s, true)) {
+    // the global K = V geometry stays on the matrix cores for every batch and split size
+    if (k_eq_v == 1) return mfma_plan(s, window, ts, n_blocks, p);
+    Plan v;  // workspace query: K = V is not known yet, size for either kernel
+    int32_t st = valu_plan(s, window, ts, 1, &v, n_blocks);
     if (st != GA_OK) return st;
-    mfma_plan(s, window, p);
+    st = mfma_plan(s, window, ts, n_blocks, p);
+    if (st != GA_OK) return st;
     if (v.ws_bytes > p->ws_bytes) p->ws_bytes = v.ws_bytes;
     return GA_OK;
   }
-  return valu_plan(s, window, ts, 1, p);
+  return valu_plan(s, window, ts, 1, p, n_blocks);
 }
 
 }  // namespace
@@ -378,6 +411,13 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   st = check_arch();
   if (st != GA_OK) return st;
   if (shape->batch == 0) return GA_OK;
+  const int n_blocks = device_cus();
+  if (n_blocks != kTargetBlocks) {
+    // fewer CUs than the plan assumed: the same choices with fewer work-groups, which
+    // need no more workspace than was checked above
+    st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p, T, n_blocks);
+    if (st != GA_OK) return st;
+  }
 
   ga::DecodeArgs a;
   a.q = q;
@@ -392,10 +432,13 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   a.plan = nullptr;
   a.n_blocks = 0;
   if (p.impl == GA_IMPL_MFMA && !p.rows16) {
-    const size_t slots = (size_t)ga::kMfmaBlocks + (size_t)shape->batch * shape->num_kv_heads;
+    const size_t slots = (size_t)ga::decode_mfma_grid(p.mfma_rows * shape->num_kv_heads,
+                                                      n_blocks, p.split_keys, p.max_keys);
     a.part_acc = ws;
     a.part_ml = ws + slots * 16 * D;
     a.plan = reinterpret_cast<int*>(a.part_ml + slots * 16 * 2);
+    a.n_blocks = n_blocks;
+    a.launch_rows = p.mfma_rows;
   } else if (p.n_split > 1) {
     const size_t n_acc = (size_t)shape->batch * T * shape->num_q_heads * (size_t)p.n_split * D;
     a.part_acc = ws;

@@ -7,83 +7,90 @@
 // the HBM roofline ("Gemma4-26B-A4B on Apple Silicon", Results, Break 4: 16 query heads
 // on one shared K/V head, no separate value projection).
 //
-// Work partition: the chip gets NB work-groups' worth of keys, C = ceil(T / NB) keys each
-// (T = valid keys of the whole batch, rounded to tiles), and every (batch row, KV head)
-// unit u with n_u keys gets k_u = ceil(n_u / C) work-groups, each an equal tile-aligned
-// share of that unit's keys.  The counts come from prefix sums computed on the device
-// from ctx_lens / q_pos, so ragged contexts with few units (one KV head, batch 16-32)
-// still spread evenly over every CU -- the failure mode of decode kernels that ignore
-// key splitting ("Gemma 4 12B (unified multimodal)" record, item (4): 2 of 132 SMs
-// busy) -- and no work-group ever switches units, so its load pipeline never drains.
-// Sum k_u <= NB + units, the grid size.  A unit with k_u = 1 is written directly; the
-// others leave one partial per work-group (slot = work-group index) for
-// merge_units_kernel (log-sum-exp).
+// Work partition: the chip gets NB work-groups' worth of keys (NB = the device's compute
+// units, one work-group each), C = ceil(T / NB) keys each (T = valid keys of the whole
+// batch, rounded to whole steps of the work-group's four waves), and every (batch row, KV
+// head) unit u with n_u keys gets k_u = ceil(n_u / C) work-groups, each an equal share of
+// that unit's keys.  The counts come from prefix sums computed on the device from
+// ctx_lens / q_pos, so ragged contexts with few units (one KV head, batch 16-32) still
+// spread evenly over every CU -- the failure mode of decode kernels that ignore key
+// splitting ("Gemma 4 12B (unified multimodal)" record, item (4): 2 of 132 SMs busy) -- and
+// no work-group ever switches units.  Sum k_u <= NB + units, the grid size.  A unit with
+// k_u = 1 is written directly; the others leave one partial per work-group (slot =
+// work-group index) for merge_units_kernel (log-sum-exp).  With a split size given, C is
+// that size instead and the host sizes the grid for it.
 //
-// One work-group per CU of 8 waves: two groups of 4 waves in lockstep (one barrier per
-// step), group h taking the work-group's tiles 4 q + 2 h and 4 q + 2 h + 1, each with its own
-// softmax state; the second group's (m, l, acc) join the first's through LDS at the end.
-// One work-group per CU (rather than two of 4 waves) keeps a CU's two streams starting
-// and ending together: a second work-group on a CU queues behind the first ones' opening
-// loads and was measured to finish ~6 us later, leaving its CU half-busy for that time.
-// Per group, 16-key tiles taken two per step; wave w of the group owns head_dim slice
-// [128 w, 128 w + 128):
-//   partial S^T[16 keys][16 heads] = K[16][slice] . Q^T[slice][16] per tile with
-//     v_mfma_f32_16x16x32_bf16 (4 per tile): bf16 rows are loaded 16 bytes per lane with
-//     each instruction covering whole 128-byte lines of 4 keys (non-temporal), written to
-//     the wave's LDS tile and read back as the A operand (key l % 16, d = 128 w + 32 j +
-//     8 (l / 16) + 0..7); fp8 codes go straight from registers into the A operand after
-//     widening; 4 tiles in flight (8 for fp8); Q^T is held in registers in the same d order;
-//   the 4 partials are summed through LDS (one barrier per step of 32 keys), in the same
-//     order in every wave, so every wave holds the identical S^T and softmax state;
-//   the wave's K = V slice goes once to its own LDS rows (288 B stride) and
-//   O^T[slice][16] += V^T[slice][32 keys] . P^T[32 keys][16 heads] with one
-//     v_mfma_f32_16x16x32_bf16 per 16-wide d block: the A operand comes from two
-//     ds_read_b64_tr_b16 (one per tile; lanes 4e..4e+3 of a 16-lane block read 16
-//     consecutive d of key e, lane i then holds the 4 keys at column d0 + i), the B
-//     operand is P exactly as the S^T products left it (lane l: head l % 16, keys
-//     4 (l / 16) + 0..3 of each tile), split into bf16 hi + lo parts so the probabilities
-//     keep ~16 mantissa bits (the bf16 cache data is exact).
-// Each wave writes its own slice of the output or partial: no end-of-segment merge.
-// The K = V row is read from HBM once and used for both products.  Softmax state per
-// head is fp32 in log2 units with lazy rescaling (max raised only past +8).
+// One work-group of 4 waves per CU, one wave per SIMD, and every wave works alone: wave w
+// takes the work-group's steps w, w + 4, ... (bf16: one 16-key tile per step; fp8: two),
+// with its own softmax state over the whole head_dim, so the key loop has no barrier and
+// no exchange between waves.  Per step:
+//   the step's rows sit in registers (16 load instructions, non-temporal: bf16 one 1 KiB
+//     key row each, eight whole 128-byte lines; fp8 two rows of 512 codes each); they go to
+//     the wave's LDS tiles row by row (fp8 codes widened exactly to bf16 on the way), each
+//     row's registers refilling at once with the next step's row, so every wave keeps 16
+//     loads in flight (a streaming probe on this chip: 6.5 TB/s with 16 per wave, 4.7 with
+//     32);
+//   S^T[16 keys][16 heads] = K[16][512] . Q^T[512][16] per tile with 16
+//     v_mfma_f32_16x16x32_bf16: the A operand read back from the tile (lane: key l16,
+//     d = 32 j + 8 lg + 0..7), Q^T read in the same d order from the unit's query rows in
+//     LDS (lane: head l16);
+//   the product leaves lane l with head l16 and keys 4 lg + 0..3, which is the B operand
+//     layout of the P.V product, so the softmax runs in place (max and sum over the four
+//     lane groups) and P goes to the matrix cores as bf16 hi + lo parts (~16 bits);
+//   O^T[512][16] += V^T[512][keys] . P^T[keys][16 heads]: per 16-wide d block and P part one
+//     v_mfma_f32_16x16x16_bf16 (one tile) or v_mfma_f32_16x16x32_bf16 (two tiles), the A
+//     operand from ds_read_b64_tr_b16 (lanes 4e..4e+3 of a 16-lane block read 16
+//     consecutive d of key e, lane i then holds the 4 keys at column d0 + i); the K = V
+//     row is read from HBM once and used for both products.
+// LDS rows are 1 KiB with 16-byte chunk c of row r stored at chunk c ^ swz(r), which keeps
+// the row writes, the A-operand reads and the transposed reads free of bank conflicts.
+// At the end the four waves combine through LDS (each wave one quarter of head_dim) and the
+// work-group writes its output or partial.  Softmax state per head is fp32 in log2 units:
+// the reference is the wave's first maximum and stays fixed while no logit exceeds it by
+// 64 (the accumulator then only ever sees the matrix cores); past that the wave continues
+// with lazy rescaling (reference raised past +8).
 #include "ga_device.h"
 #include "ga_internal.h"
 #include "ga_mfma.h"
 
+#include <type_traits>
+
 namespace ga {
 namespace {
 
-constexpr int MD = 512;        // head_dim
-constexpr int MG = 16;         // query heads per KV head
-constexpr int TK = 16;         // keys per tile
-constexpr int MNW = 4;         // waves per group, one head_dim slice each
-constexpr int MH = kMfmaHalves;  // groups per work-group, in lockstep on alternate key pairs
-constexpr int NWV = MNW * MH;  // waves per work-group
-constexpr int DQ = MD / MNW;   // head_dim slice of a wave
-constexpr int ROWQ = DQ * 2 + 32;   // LDS bytes per key row of a wave's slice (bank spread)
-constexpr int WAVE_TILE = TK * ROWQ;
-#ifndef GA_FP8_TILES
-#define GA_FP8_TILES 8
-#endif
-#ifndef GA_BF16_TILES
-#define GA_BF16_TILES 4
-#endif
+constexpr int MD = 512;          // head_dim
+constexpr int MG = 16;           // query heads per KV head
+constexpr int TK = 16;           // keys per tile (the matrix-core operand height)
+constexpr int NWV = kMfmaWaves;  // waves per work-group
+constexpr int ROWB = MD * 2;     // LDS bytes per key row (bf16)
+constexpr int TILEB = TK * ROWB;
+constexpr int WAVE_LDS = 2 * TILEB;  // a wave's LDS: its tiles, and its accumulator at the end
 constexpr float kRescaleLog2 = 8.0f;
-// LDS per work-group is sized so that exactly kMfmaBlocksPerCU work-groups fit on a CU
-// (160 KiB each): every CU then holds the same number of equal-work work-groups.
-constexpr int kLdsCU = 160 * 1024;
-constexpr int kLdsOther = 2 * NWV * 2 * 64 * 16 + 3 * (kMfmaMaxUnits + 1) * 4 + 2 * MH * 2 * TK * 4;
-constexpr int kLdsTile = kLdsCU / (kMfmaBlocksPerCU + 1) + 1024 - kLdsOther;
-constexpr int kLdsKV = 2 * NWV * WAVE_TILE > kLdsTile ? 2 * NWV * WAVE_TILE : kLdsTile;
-// the second group's (acc, m, l) go to the first through the second group's tile area
-static_assert(2 * WAVE_TILE >= 64 * 8 * 16, "combine area per wave");
-static_assert(kLdsKV + kLdsOther <= kLdsCU / kMfmaBlocksPerCU, "LDS budget per work-group");
+// Fast-form headroom (log2 units): with the reference at the wave's first maximum, weights
+// stay below 2^64, far inside fp32 (and bf16) range for the accumulator and the sum.
+constexpr float kFastHeadroom = 64.0f;
+static_assert(NWV * WAVE_LDS + MG * ROWB + 2 * (kMfmaMaxUnits + 1) * 4 + NWV * MG * 2 * 4 +
+                      NWV * 32 * 4 <=
+                  160 * 1024,
+              "LDS budget per work-group");
+static_assert(WAVE_LDS >= 32 * 64 * 16, "a wave's LDS holds its accumulator at the end");
 
+// LDS chunk swizzle (16-byte chunks, rows 0..15 of a tile): chunk c of row r sits at
+// c ^ (2 r mod 16).  Measured on gfx950 (SQ_LDS_BANK_CONFLICT of each access pattern in
+// isolation): no bank conflicts for the row writes, the A-operand reads (16 rows, one
+// chunk each) and the transposed reads (4 rows x 32 bytes per 16 lanes).
+__device__ __forceinline__ int swz(int r) { return (2 * r) & 15; }
 
-__device__ __forceinline__ int chunk_keys(int T, int NB) {
+// Keys per work-group, a multiple of the NWV steps a work-group starts on (wg_keys): then
+// k_u = ceil(n_u / C) <= ceil(n_u / wg_keys), so the first wave of every work-group of a
+// unit has a first step, and every work-group's result covers at least one key.
+__device__ __forceinline__ int chunk_keys(int T, int NB, int wg_keys) {
   const int per = (T + NB - 1) / NB;
-  return T > 0 ? (per + TK - 1) / TK * TK : TK;
+  return T > 0 ? (per + wg_keys - 1) / wg_keys * wg_keys : wg_keys;
 }
+// The smallest wg_keys of the kernels (bf16: one 16-key tile per step), which the host
+// uses to bound the grid for a given split size.
+constexpr int kMinWgKeys = NWV * TK;
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each
 // 16-lane row, then each row adds the last lane of the rows before it (DPP row
@@ -98,23 +105,27 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <bool FP8>
-__global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_kv[kLdsKV];
-  __shared__ floatx4_t s_part[2][MH][MNW][2][64];  // [buffer][group][wave][tile][lane]
-  __shared__ __attribute__((aligned(16))) float s_scale[2][MH][2][TK];  // fp8 row scales
-  __shared__ float s_ml[MG][2];  // the second group's m and l per head
-  __shared__ float s_norm[2][NWV];  // fp8: per-wave largest key scale and |q|
-  // Tiles in flight per wave: four bf16 tiles (64 KiB per work-group); fp8 tiles are half
-  // the bytes, so eight keep as many bytes in flight (the loop is latency-bound otherwise).
-  constexpr int NF = FP8 ? GA_FP8_TILES : GA_BF16_TILES;
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_mfma_kernel(DecodeArgs a) {
+  // Tiles per step: bf16 one (16 load instructions of a whole 1 KiB row each); fp8 two
+  // (8 instructions of two 512-code rows each per tile).  Either way a wave keeps NLS = 16
+  // load instructions in flight.
+  constexpr int TPS = FP8 ? 2 : 1;
+  constexpr int STEP = TPS * TK;
+  constexpr int NLS = 16;
+  constexpr int WG_KEYS = NWV * STEP;
+  __shared__ __attribute__((aligned(16))) char s_kv[NWV * WAVE_LDS];
+  __shared__ __attribute__((aligned(16))) float s_scl[NWV][32];  // fp8: the step's row scales
+  __shared__ __attribute__((aligned(16))) char s_q[MG * ROWB];  // the unit's 16 query rows
+  __shared__ float s_ml[NWV][MG][2];
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
-  __shared__ int s_slot[kMfmaMaxUnits];   // slot of each unit's first valid key
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int half = wave / MNW, wsl = wave % MNW;  // group, and the wave's head_dim slice
+  const int lane = tid & 63, wave = uni(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.B * a.Hkv;
 
@@ -122,9 +133,7 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
   // each unit's key range, then wave 0 alone forms both prefix sums (two barriers).
   for (int u = tid; u < R; u += NWV * 64) {
     const int b = u / a.Hkv;
-    const RowRange rr = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
-    s_n[u + 1] = rr.n;
-    s_slot[u] = rr.slot_lo;
+    s_n[u + 1] = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys).n;
   }
   __syncthreads();
   if (wave == 0) {
@@ -140,11 +149,18 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
       }
       total = __builtin_amdgcn_readlane(v, 63);
     }
-    // k_u = ceil(n_u / C) <= n_u / C + 1, so with C = T / (NB - R') (R' non-empty units)
-    // the work-groups with work never exceed NB: all of them are resident at once.
-    const int nb_eff =
-        a.n_blocks - nonempty >= a.n_blocks / 4 ? a.n_blocks - nonempty : a.n_blocks;
-    const int C = chunk_keys(total, nb_eff);
+    int C;
+    if (a.split_keys > 0) {
+      // a given split size (rounded up to whole work-group starts): the host sized the
+      // grid for it
+      C = (a.split_keys + WG_KEYS - 1) / WG_KEYS * WG_KEYS;
+    } else {
+      // k_u = ceil(n_u / C) <= n_u / C + 1, so with C = T / (NB - R') (R' non-empty units)
+      // the work-groups with work never exceed NB: all of them are resident at once.
+      const int nb_eff =
+          a.n_blocks - nonempty >= a.n_blocks / 4 ? a.n_blocks - nonempty : a.n_blocks;
+      C = chunk_keys(total, nb_eff, WG_KEYS);
+    }
     int groups = 0;
     for (int base = 0; base < R; base += 64) {
       const int u = base + lane;
@@ -174,354 +190,352 @@ __global__ void __launch_bounds__(NWV * 64, kMfmaBlocksPerCU) decode_mfma_kernel
     return;
   }
   // unit of this work-group: the u with s_k[u] <= g_id < s_k[u + 1]
-  int u, hi_u = R - 1;
+  int u;
   {
-    int lo_u = 0;
+    int lo_u = 0, hi_u = R - 1;
     while (lo_u < hi_u) {
       const int mid = (lo_u + hi_u) >> 1;
       if (s_k[mid + 1] > g_id) hi_u = mid; else lo_u = mid + 1;
     }
-    u = lo_u;
+    u = uni(lo_u);
   }
-  const int n_u = s_n[u + 1] - s_n[u];
-  const int k_u = s_k[u + 1] - s_k[u];
-  const int part = g_id - s_k[u];
-  const int per = ((n_u + k_u - 1) / k_u + TK - 1) / TK * TK;
+  const int n_u = uni(s_n[u + 1] - s_n[u]);
+  const int k_u = uni(s_k[u + 1] - s_k[u]);
+  const int part = g_id - uni(s_k[u]);
+  const int per = ((n_u + k_u - 1) / k_u + WG_KEYS - 1) / WG_KEYS * WG_KEYS;
   const int seg_lo = part * per;
   const int seg_hi = min(n_u, seg_lo + per);  // non-empty: (k_u - 1) * per < n_u
+  const int nsteps = (seg_hi - seg_lo + STEP - 1) / STEP;
+  // wave w takes the segment's steps w, w + NWV, ...; every wave has one (per >= WG_KEYS)
+  // except in a unit's last work-group
+  const int my_steps = wave < nsteps ? (nsteps - wave + NWV - 1) / NWV : 0;
 
   const int b = u / a.Hkv, g = u % a.Hkv;
-  const int slot_lo = s_slot[u];
+  const int slot_lo =
+      uni(row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys).slot_lo);
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
+  const int cap = a.cap;
 
-  // this wave's two tile buffers (one step's tiles) and its transposed-read addresses
-  char* tile_a = s_kv + wave * 2 * WAVE_TILE;
-  char* tile_b = tile_a + WAVE_TILE;
-  char* lds_ra = tile_a + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;
-  char* lds_rb = tile_b + (4 * lg + (l16 >> 2)) * ROWQ + (l16 & 3) * 8;
-  int par = 0;  // s_part double buffer
-
-  // Q^T operand for this wave's slice, in the order the K rows are loaded: head l16,
-  // d = 128 w + 32 j + 8 lg + 0..7 (bf16 rows: 16 bytes per lane and j), or
-  // d = 128 w + 64 (j / 2) + 16 lg + 8 (j % 2) + 0..7 (fp8 rows: 16 codes per lane and
-  // pair of j).  Any order of d works as long as K and Q^T share it.  The fp8 path
-  // converts q to fp16 below, once the work-group's range normalization is known.
-  uint4 qv[4];
+  // the unit's 16 query rows to LDS in the key rows' layout (row = head, chunk c at
+  // c ^ swz(row)): the Q^T operand is read from there like the K operand (lane: head l16,
+  // d = 32 j + 8 lg + 0..7), which leaves the registers to the rows in flight
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + (head0 + l16) * MD);
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + head0 * MD);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      qv[j] = FP8 ? qp[16 * wsl + 8 * (j / 2) + 2 * lg + (j % 2)] : qp[16 * wsl + 4 * j + lg];
+    for (int k = 0; k < MG * MD / 8 / (NWV * 64); ++k) {
+      const int idx = tid + k * NWV * 64, r = idx >> 6, c = idx & 63;
+      *reinterpret_cast<uint4*>(s_q + r * ROWB + ((c ^ swz(r)) * 16)) = qp[idx];
+    }
   }
-  const uint4* kbase = reinterpret_cast<const uint4*>(a.k) + (size_t)u * a.cap * (MD / 8);
-  const uint4* cbase = reinterpret_cast<const uint4*>(a.k8) + (size_t)u * a.cap * (MD / 16);
-  const float* sbase = FP8 ? a.k_scale + (size_t)u * a.cap : nullptr;
+
+  // ---- loads.  Tile h of step t (of this wave: the segment's step wave + NWV t) holds the
+  // segment's keys seg_lo + STEP (wave + NWV t) + 16 h + 0..15.  Keys past the segment's end
+  // re-read its last key (a valid row, masked), so every load is unconditional.
   const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
-  const uint4* knew = a.new_pos ? reinterpret_cast<const uint4*>(a.k_new) + (size_t)u * (MD / 8)
-                                : kbase;
-  // bf16 loads: lane reads 16 bytes (column lane % 16 of the wave's 256-byte slice) of key
-  // lane / 16 + 4 j, so each instruction covers 4 keys x 2 whole 128-byte lines
-  const uint4* kbase_l = kbase + 16 * wsl + (lane & 15);
-  const uint4* knew_l = knew + 16 * wsl + (lane & 15);
-
-  floatx4_t acc[8];
+  const char* kmem = FP8 ? reinterpret_cast<const char*>(a.k8) : reinterpret_cast<const char*>(a.k);
+  constexpr int CROWB = FP8 ? MD : MD * 2;  // bytes per cached row
+  const char* kunit = kmem + (size_t)u * cap * CROWB;
+  const char* knew = a.new_pos ? reinterpret_cast<const char*>(a.k_new) + (size_t)u * ROWB
+                               : kunit;
+  const float* sunit = FP8 ? a.k_scale + (size_t)u * cap : nullptr;
+  auto slot_of = [&](int key) { return key_slot(slot_lo, key < seg_hi ? key : seg_hi - 1, cap); };
+  auto key0 = [&](int t) { return seg_lo + STEP * (wave + NWV * t); };
+  // one step's registers: NLS load instructions (bf16: 16 rows of one tile; fp8: 8 row
+  // pairs of each of two tiles) and (fp8) the row scale of key lane % 32 of the step
+  struct Regs {
+    uint4 r[NLS];
+    float sc;
+  };
+  auto load_row = [&](Regs& t, int j, int k0) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      // rows 2 j and 2 j + 1 of the step: lanes 0..31 the first, 32..63 the second
+      const int sa = uni(slot_of(k0 + 2 * j)), sb = uni(slot_of(k0 + 2 * j + 1));
+      const char* row = kunit + (size_t)(lane < 32 ? sa : sb) * CROWB;
+      t.r[j] = stream_load(reinterpret_cast<const uint4*>(row) + (lane & 31));
+    } else {
+      const int slot = uni(slot_of(k0 + j));
+      const char* row = slot == new_slot ? knew : kunit + (size_t)slot * CROWB;
+      t.r[j] = stream_load(reinterpret_cast<const uint4*>(row) + lane);
+    }
+  };
+  auto load_scale = [&](Regs& t, int k0) __attribute__((always_inline)) {
+    if constexpr (FP8) t.sc = sunit[slot_of(k0 + (lane & 31))];
+  };
+  char* my_tiles = s_kv + wave * WAVE_LDS;
+  // load instruction j of a step to LDS (row r of tile r / 16, 16-byte chunk c at c ^ swz)
+  auto put_row = [&](const Regs& t, int j) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      // lane widens 16 codes (d = 16 m + 0..15, m = lane % 32) of step row 2 j + lane / 32
+      // to the two chunks 2 m and 2 m + 1, storing first the one that keeps 8 / 16
+      // consecutive lanes on distinct banks
+      const int m = lane & 31, fb = ((m >> 2) ^ (m >> 3)) & 1;
+      const int rs = 2 * j + (lane >> 5), r = rs & 15, sw = swz(r);
+      const uint4 lo = e4m3x8_to_bf16x8(t.r[j].x, t.r[j].y);
+      const uint4 hi = e4m3x8_to_bf16x8(t.r[j].z, t.r[j].w);
+      char* row = my_tiles + (rs >> 4) * TILEB + r * ROWB;
+      const uint32_t mk = 0u - (uint32_t)fb;  // all ones where the high chunk goes first
+      const uint4 d = make_uint4((lo.x ^ hi.x) & mk, (lo.y ^ hi.y) & mk, (lo.z ^ hi.z) & mk,
+                                 (lo.w ^ hi.w) & mk);
+      *reinterpret_cast<uint4*>(row + ((2 * m + fb) ^ sw) * 16) =
+          make_uint4(lo.x ^ d.x, lo.y ^ d.y, lo.z ^ d.z, lo.w ^ d.w);
+      *reinterpret_cast<uint4*>(row + ((2 * m + 1 - fb) ^ sw) * 16) =
+          make_uint4(hi.x ^ d.x, hi.y ^ d.y, hi.z ^ d.z, hi.w ^ d.w);
+    } else {
+      *reinterpret_cast<uint4*>(my_tiles + j * ROWB + ((lane ^ swz(j)) * 16)) = t.r[j];
+    }
+  };
+  auto put_scale = [&](const Regs& t) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      if (lane < 32) s_scl[wave][lane] = t.sc;
+    }
+  };
+  // The step's registers to LDS, each load instruction's register refilled with the same
+  // instruction of step t_next as soon as its row is stored: the wave keeps NLS loads in
+  // flight at all times (more per wave measured slower on this chip).  The scheduling
+  // barriers keep every store before the next row's refill; without them the compiler
+  // stores all of a step's rows first, which waits for every load in flight.
+  auto cycle = [&](Regs& t, int t_next) __attribute__((always_inline)) {
+    const int k0 = key0(t_next);
+    put_scale(t);
+    load_scale(t, k0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NLS; ++j) {
+      put_row(t, j);
+      load_row(t, j, k0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto put = [&](const Regs& t) __attribute__((always_inline)) {
+    put_scale(t);
+#pragma unroll
+    for (int j = 0; j < NLS; ++j) put_row(t, j);
+  };
+  // per-lane LDS offsets: A operand (row l16, chunk 4 jj + lg for jj = j % 4; j / 4 adds
+  // 16 chunks) and transposed reads (row 4 lg + l16 / 4, chunk 2 e + (l16 / 2) % 2 of the
+  // d block db = 8 (db / 8) + e, byte 8 (l16 % 2) in it)
+  int a_off[4], t_off[8];
+  {
+    const int sa = swz(l16);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) a_off[jj] = l16 * ROWB + ((4 * jj + lg) ^ sa) * 16;
+    const int rr = 4 * lg + (l16 >> 2), st = swz(rr), hh = (l16 >> 1) & 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t_off[e] = rr * ROWB + ((2 * e + hh) ^ st) * 16 + (l16 & 1) * 8;
+  }
+
+  floatx4_t acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f;
-  float p_norm = 1.0f, logit_scale = a.scale;  // fp8 range normalization (set below)
 
-  // The work-group's tiles go to the groups in pairs: tiles 4 q, 4 q + 1 to group 0, 4 q + 2,
-  // 4 q + 3 to group 1.  Both groups step through group 0's tile count (group 1's extra
-  // tiles are past the end: masked, their loads clamped to a valid row).
-  const int ntw = (seg_hi - seg_lo + TK - 1) / TK;
-  const int nt = MH == 1 ? ntw : 2 * (ntw / 4) + min(ntw % 4, 2);
-  auto tile_key0 = [&](int t) {  // first key of this group's local tile t
-    return seg_lo + TK * (MH == 1 ? t : 4 * (t >> 1) + 2 * half + (t & 1));
-  };
-
-  // One tile's registers: bf16 rows in rg[0..3] (rg[j]: key lane / 16 + 4 j of the tile);
-  // fp8 rows: the 32 codes of key l16 in rg[0..1] and that key's scale in rg[2].x.
-  auto load = [&](uint4(&rg)[4], int t) {
-    if constexpr (FP8) {
-      const int key = tile_key0(t) + l16;
-      const int kc = key < seg_hi ? key : seg_hi - 1;
-      const int slot = key_slot(slot_lo, kc, a.cap);
-      const uint4* cp = cbase + (size_t)slot * (MD / 16) + 8 * wsl + lg;
-      rg[0] = cp[0];
-      rg[1] = cp[4];
-      rg[2].x = __float_as_uint(sbase[slot]);  // the scale of this lane's key (l16)
-    } else {
-      const int key0 = tile_key0(t) + (lane >> 4);
+  // One step from the LDS tiles.  The reference m per head is the wave's first maximum;
+  // in the fast form (SAFE = false) it never moves afterwards, so the accumulator is only
+  // ever touched by the matrix cores, and a step whose maximum exceeds m + kFastHeadroom
+  // (where 2^(x - m) could leave the fp32 range) returns false before using any of its
+  // values; the caller then finishes in the safe form, which rescales the accumulator
+  // whenever the maximum grows by more than kRescaleLog2 (lazy rescaling).
+  auto compute = [&](auto safe_tag, int t) __attribute__((always_inline)) -> bool {
+    constexpr bool SAFE = decltype(safe_tag)::value;
+    const int k0 = key0(t);
+    // S^T per tile: 16 products over head_dim, in two chains per tile (even / odd j); the
+    // K and Q operands are read a group of QG products ahead
+    floatx4_t sc2[TPS][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = key0 + 4 * j;
-        const int kc = key < seg_hi ? key : seg_hi - 1;
-        const int slot = key_slot(slot_lo, kc, a.cap);
-        rg[j] = stream_load(slot == new_slot ? knew_l : kbase_l + (size_t)slot * (MD / 8));
+    for (int h = 0; h < TPS; ++h) sc2[h][0] = sc2[h][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int QG = 2;
+    uint4 kk[2][TPS][QG], qq[2][QG];
+    auto read_k = [&](int grp, uint4(&x)[TPS][QG], uint4(&z)[QG]) {
+#pragma unroll
+      for (int jj = 0; jj < QG; ++jj) {
+        const int j = grp * QG + jj;
+        const int off = a_off[j & 3] + 256 * (j >> 2);
+#pragma unroll
+        for (int h = 0; h < TPS; ++h)
+          x[h][jj] = *reinterpret_cast<const uint4*>(my_tiles + h * TILEB + off);
+        z[jj] = *reinterpret_cast<const uint4*>(s_q + off);
       }
-    }
-  };
-
-  // One step = two 16-key tiles (ra: keys k0 .. k0 + 15, rb: the next 16): their products
-  // and softmax chains interleave, and one barrier and one max update cover 32 keys.
-  // Each tile's rows go to the wave's LDS tile in natural d order (the V operand, and for
-  // bf16 also the K operand); a tile's S^T partial over this wave's d slice is K rows
-  // (A operand) times Q^T.  fp8 codes are widened exactly to fp16 and feed the products
-  // from registers.
-  auto tile_scores_fp8 = [&](const uint4(&rg)[4], char* tile, floatx4_t& s) {
-    s = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const uint4 lo = e4m3x8_to_f16x8(rg[jj].x, rg[jj].y);
-      const uint4 hi = e4m3x8_to_f16x8(rg[jj].z, rg[jj].w);
-      s = mfma_k32_f16(lo, qv[2 * jj], s);
-      s = mfma_k32_f16(hi, qv[2 * jj + 1], s);
-      char* w8 = tile + l16 * ROWQ + lg * 32 + jj * 128;  // 16 d per lane and jj
-      *reinterpret_cast<uint4*>(w8) = lo;
-      *reinterpret_cast<uint4*>(w8 + 16) = hi;
-    }
-  };
-  // bf16: lane writes its 16 bytes of keys lane / 16 + 4 j, then (after the wave's writes)
-  // reads the A operand of key l16, d = 32 j + 8 lg + 0..7 of the slice
-  auto tile_write_bf16 = [&](const uint4(&rg)[4], char* tile) {
-    char* w = tile + (lane >> 4) * ROWQ + (lane & 15) * 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(w + 4 * j * ROWQ) = rg[j];
-  };
-
-  auto step2 = [&](uint4(&ra)[4], uint4(&rb)[4], int t) {
-    const int k0 = tile_key0(t);  // tile b (local t + 1, t even) starts at k0 + TK
-    floatx4_t sa, sb;
-    if constexpr (FP8) {
-      tile_scores_fp8(ra, tile_a, sa);
-      tile_scores_fp8(rb, tile_b, sb);
-    } else {
-      wave_lds_sync();  // the previous step's transposed reads stay before these writes
-      tile_write_bf16(ra, tile_a);
-      tile_write_bf16(rb, tile_b);
-      // the registers are free once written: the next loads go out before the products
-      // (unconditional, clamped past the end: keeps the wait counts partial)
-      load(ra, t + NF);
-      load(rb, t + NF + 1);
-      wave_lds_sync();
-      sa = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      sb = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      const char* rda = tile_a + l16 * ROWQ + lg * 16;
-      const char* rdb = tile_b + l16 * ROWQ + lg * 16;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sa = mfma_k32(*reinterpret_cast<const uint4*>(rda + 64 * j), qv[j], sa);
-        sb = mfma_k32(*reinterpret_cast<const uint4*>(rdb + 64 * j), qv[j], sb);
-      }
-    }
-    s_part[par][half][wsl][0][lane] = sa;
-    s_part[par][half][wsl][1][lane] = sb;
-    if (FP8 && wsl == 0 && lg == 0) {  // the keys' row scales (times p_norm), for the group
-      s_scale[par][half][0][l16] = __uint_as_float(ra[2].x) * p_norm;
-      s_scale[par][half][1][l16] = __uint_as_float(rb[2].x) * p_norm;
-    }
-    if constexpr (FP8) {
-      load(ra, t + NF);  // unconditional (clamped past the end): keeps wait counts partial
-      load(rb, t + NF + 1);
-    }
-    __syncthreads();
-    float ka[4] = {1.0f, 1.0f, 1.0f, 1.0f}, kb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (FP8) {  // scales of the keys 4 lg + 0..3 this lane's logits belong to
-      const float4 a4 = *reinterpret_cast<const float4*>(&s_scale[par][half][0][4 * lg]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&s_scale[par][half][1][4 * lg]);
-      ka[0] = a4.x; ka[1] = a4.y; ka[2] = a4.z; ka[3] = a4.w;
-      kb[0] = b4.x; kb[1] = b4.y; kb[2] = b4.z; kb[3] = b4.w;
-    }
-    const floatx4_t fa = ((s_part[par][half][0][0][lane] + s_part[par][half][1][0][lane]) +
-                          s_part[par][half][2][0][lane]) + s_part[par][half][3][0][lane];
-    const floatx4_t fb = ((s_part[par][half][0][1][lane] + s_part[par][half][1][1][lane]) +
-                          s_part[par][half][2][1][lane]) + s_part[par][half][3][1][lane];
-    par ^= 1;
-    // softmax: lane holds head l16, keys k0 + 4 lg + i (xa) and k0 + 16 + 4 lg + i (xb)
-    float xa[4], xb[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float va = fa[i] * ka[i] * logit_scale;  // fp8: the key's row scale
-      float vb = fb[i] * kb[i] * logit_scale;
-      if (a.softcap > 0.0f) {
-        va = softcap_tanh(va, a.softcap, a.inv_softcap);
-        vb = softcap_tanh(vb, a.softcap, a.inv_softcap);
-      }
-      xa[i] = (k0 + 4 * lg + i < seg_hi) ? va * kLog2e : -INFINITY;
-      xb[i] = (k0 + TK + 4 * lg + i < seg_hi) ? vb * kLog2e : -INFINITY;
-      mx = fmaxf(mx, fmaxf(xa[i], xb[i]));
-    }
-    mx = rows_max(mx);  // over the 32 keys of the step (four lane rows)
-    if (mx > m + kRescaleLog2) {
-      const float f = exp2_fast(m - mx);
-      l *= f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= f;
-      m = mx;
-    }
-    // m stays -inf only while every key so far was masked (the second group's steps past
-    // the end): then every x is -inf and p must be 0, not exp2(-inf + inf)
-    const float mref = m == -INFINITY ? 0.0f : m;
-    float pa[4], pb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pa[i] = exp2_fast(xa[i] - mref);
-      pb[i] = exp2_fast(xb[i] - mref);
-      l += pa[i] + pb[i];
-      if constexpr (FP8) {  // K = V: the value row's scale is the key's
-        pa[i] *= ka[i];
-        pb[i] *= kb[i];
-      }
-    }
-    if constexpr (FP8) {
-      // fp16 operands: V^T exact (widened codes), P^T (p * s * p_norm < 2^15) rounded once
-      // to 11 significant bits
-      const uint4 pf = make_uint4(pack_f16x2(pa[0], pa[1]), pack_f16x2(pa[2], pa[3]),
-                                  pack_f16x2(pb[0], pb[1]), pack_f16x2(pb[2], pb[3]));
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const short4_t va =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_ra + db * 32));
-        const short4_t vb =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_rb + db * 32));
-        acc[db] = mfma_k32_f16(cat4(va, vb), pf, acc[db]);
-      }
-      return;
-    }
-    // P^T operands (lane: head l16, keys 4 lg + 0..3), split into bf16 hi + lo parts so
-    // the probabilities keep ~16 mantissa bits
-    auto split = [](const float(&p)[4], short4_t& ph, short4_t& pl) {
-      const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
-      const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-      const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-      ph = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
-      pl = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
     };
-    short4_t pah, pal, pbh, pbl;
-    split(pa, pah, pal);
-    split(pb, pbh, pbl);
-    // O^T += V^T P^T over the step's 32 keys with v_mfma_f32_16x16x32_bf16: lane (l16, lg)
-    // holds k slots 8 lg + 0..7 = keys 4 lg + 0..3 of tile a, then of tile b, in both
-    // operands (the transposed reads give V^T for exactly those keys at column l16, and
-    // the softmax left P for exactly those keys), so one product covers both tiles.
-    const uint4 ph = cat4(pah, pbh), pl = cat4(pal, pbl);
+    read_k(0, kk[0], qq[0]);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const short4_t va =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_ra + db * 32));
-      const short4_t vb =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(lds_rb + db * 32));
-      const uint4 v8 = cat4(va, vb);
-      acc[db] = mfma_k32(v8, ph, acc[db]);
-      acc[db] = mfma_k32(v8, pl, acc[db]);
+    for (int grp = 0; grp < 16 / QG; ++grp) {
+      const int nx = (grp + 1) & 1;
+      if (grp + 1 < 16 / QG) read_k(grp + 1, kk[nx], qq[nx]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < QG; ++jj)
+#pragma unroll
+        for (int h = 0; h < TPS; ++h)
+          sc2[h][jj & 1] = mfma_k32(kk[grp & 1][h][jj], qq[grp & 1][jj], sc2[h][jj & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // softmax: lane holds head l16, keys k0 + 16 h + 4 lg + e of tile h
+    float ks[TPS][4];
+    if constexpr (FP8) {  // the keys' row scales
+#pragma unroll
+      for (int h = 0; h < TPS; ++h) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_scl[wave][16 * h + 4 * lg]);
+        ks[h][0] = v.x; ks[h][1] = v.y; ks[h][2] = v.z; ks[h][3] = v.w;
+      }
+    }
+    float x[TPS][4], mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < TPS; ++h) {
+      const floatx4_t sv = sc2[h][0] + sc2[h][1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = sv[e] * a.scale;
+        if constexpr (FP8) v *= ks[h][e];
+        if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
+        x[h][e] = (k0 + TK * h + 4 * lg + e < seg_hi) ? v * kLog2e : -INFINITY;
+        mx = fmaxf(mx, x[h][e]);
+      }
+    }
+    mx = rows_max(mx);  // over the step's keys (four lane groups)
+    if constexpr (SAFE) {
+      if (mx > m + kRescaleLog2) {
+        const float f = exp2_fast(m - mx);  // 0 while m = -inf
+        l *= f;
+#pragma unroll
+        for (int d = 0; d < 32; ++d) acc[d] *= f;
+        m = mx;
+      }
+    } else {
+      if (__ballot(m != -INFINITY && mx > m + kFastHeadroom) != 0) return false;
+      if (m == -INFINITY) m = mx;  // the wave's first step (the accumulator is still 0)
+    }
+    // every step holds at least one valid key, so m is finite from the first step on
+    const float mref = m == -INFINITY ? 0.0f : m;
+    float p[TPS][4];
+#pragma unroll
+    for (int h = 0; h < TPS; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[h][e] = exp2_fast(x[h][e] - mref);
+        l += p[h][e];
+        if constexpr (FP8) p[h][e] *= ks[h][e];  // K = V: the value row's scale is the key's
+      }
+    // P^T operands (lane: head l16, keys 4 lg + 0..3 of each tile), bf16 hi + lo parts
+    uint32_t ph[2 * TPS], pl[2 * TPS];
+#pragma unroll
+    for (int h = 0; h < TPS; ++h)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t hv = pack_bf16x2(p[h][2 * k], p[h][2 * k + 1]);
+        ph[2 * h + k] = hv;
+        pl[2 * h + k] = pack_bf16x2(p[h][2 * k] - bf16_lo(hv), p[h][2 * k + 1] - bf16_hi(hv));
+      }
+    // O^T += V^T P^T per 16-wide d block: one tile -> v_mfma_f32_16x16x16_bf16 on the
+    // tile's transposed read; two tiles -> v_mfma_f32_16x16x32_bf16 on both (k slots
+    // 8 lg + 0..3 = tile 0's keys 4 lg + 0..3, 8 lg + 4..7 = tile 1's), each for P's hi
+    // and lo parts.  The V^T operands are read a group of VG blocks ahead.
+    constexpr int VG = 4;
+    uint4 vv[2][VG];
+    auto read_v = [&](int grp, uint4(&y)[VG]) {
+#pragma unroll
+      for (int k = 0; k < VG; ++k) {
+        const int db = grp * VG + k;
+        const int off = t_off[db & 7] + 256 * (db >> 3);
+        const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(my_tiles + off));
+        short4_t vb = va;
+        if constexpr (TPS == 2)
+          vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(my_tiles + TILEB + off));
+        y[k] = cat4(va, vb);
+      }
+    };
+    read_v(0, vv[0]);
+#pragma unroll
+    for (int grp = 0; grp < 32 / VG; ++grp) {
+      if (grp + 1 < 32 / VG) read_v(grp + 1, vv[(grp + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int part2 = 0; part2 < 2; ++part2)
+#pragma unroll
+        for (int k = 0; k < VG; ++k) {
+          const int db = grp * VG + k;
+          const uint32_t* pp = part2 == 0 ? ph : pl;
+          if constexpr (TPS == 2) {
+            acc[db] = mfma_k32(vv[grp & 1][k], make_uint4(pp[0], pp[1], pp[2], pp[3]), acc[db]);
+          } else {
+            const uint4 v = vv[grp & 1][k];
+            acc[db] = mfma_k16(__builtin_bit_cast(short4_t, make_uint2(v.x, v.y)),
+                               __builtin_bit_cast(short4_t, make_uint2(pp[0], pp[1])), acc[db]);
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return true;
   };
 
-  // Straight-line loop body over whole groups of NF tiles (NF / 2 steps); the last tiles
-  // run after it, a step's second tile past the end being all masked, so the loop header
-  // never sees a path with a buffer's loads still unconsumed (which would make the
-  // compiler drain every prefetch there).
-  // fp8 computes in fp16 (every e4m3 value is an fp16 value; products accumulate in fp32).
-  // Two powers of two per work-group keep the fp16 operands in range: q * q_norm with
-  // |q * q_norm| < 2^15, and value weights p * s * p_norm < 2^15 (p <= 2^8 with the lazy
-  // rescale, s * p_norm < 2^7 for every key scale s of the work-group's keys).  The logits
-  // take 1 / (q_norm p_norm) and the result 1 / p_norm back, both exact.  The key scales'
-  // loads go out before the tiles' so that waiting for them leaves the tiles in flight.
-  float sk[4];
-  if constexpr (FP8) {
+  // ---- the key loop: the current step's rows sit in registers; per step they go to LDS
+  // row by row, each row's registers refilling with the next step's row, and the step is
+  // computed from LDS.  The wave's last step only goes to LDS.
+  Regs buf;
+  load_scale(buf, key0(0));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = min(seg_lo + tid + r * NWV * 64, seg_hi - 1);
-      sk[r] = sbase[key_slot(slot_lo, key, a.cap)];
-    }
+  for (int j = 0; j < NLS; ++j) load_row(buf, j, key0(0));  // (a wave without steps: unused)
+  __syncthreads();  // the query rows are in LDS
+  // one step: 0 to go on, 1 when it was the wave's last, 2 when the fast form stopped on it
+  // (its tiles are in LDS)
+  auto body = [&](auto safe_tag, int t) __attribute__((always_inline)) -> int {
+    wave_lds_sync();  // the previous step's LDS reads stay before these writes
+    const bool last = t + 1 >= my_steps;
+    if (last) put(buf); else cycle(buf, t + 1);
+    wave_lds_sync();
+    if (!compute(safe_tag, t)) return 2;
+    return last ? 1 : 0;
+  };
+  const std::integral_constant<bool, false> fast;
+  const std::integral_constant<bool, true> safe;
+  int t = 0, st = 1;
+  for (; t < my_steps; ++t)
+    if ((st = body(fast, t)) != 0) break;
+  if (st == 2) {
+    // finish in the safe form: the step that stopped (its tiles are in LDS), then the rest
+    compute(safe, t);
+    for (++t; t < my_steps; ++t)
+      if (body(safe, t) != 0) break;
   }
-  uint4 buf[NF][4];
-#pragma unroll
-  for (int i = 0; i < NF; ++i) load(buf[i], i);
-  if constexpr (FP8) {
-    float smax = fmaxf(fmaxf(sk[0], sk[1]), fmaxf(sk[2], sk[3]));
-    for (int key = seg_lo + tid + 4 * NWV * 64; key < seg_hi; key += NWV * 64)
-      smax = fmaxf(smax, sbase[key_slot(slot_lo, key, a.cap)]);
-    float qmax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
-    }
-    smax = wave_max(smax);
-    qmax = wave_max(qmax);
-    if (lane == 0) {
-      s_norm[0][wave] = smax;
-      s_norm[1][wave] = qmax;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      smax = fmaxf(smax, s_norm[0][w]);
-      qmax = fmaxf(qmax, s_norm[1][w]);
-    }
-    p_norm = pow2_norm(smax, 7);
-    const float q_norm = pow2_norm(qmax, 15);
-    logit_scale = a.scale / (q_norm * p_norm);  // exact: powers of two
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qv[j] = bf16x8_to_f16x8(qv[j], q_norm);
-  }
-  int t = 0;
-  for (; t + NF - 1 < nt; t += NF) {
-#pragma unroll
-    for (int i = 0; i < NF; i += 2) step2(buf[i], buf[i + 1], t + i);
-  }
-#pragma unroll
-  for (int i = 0; i < NF; i += 2)
-    if (t + i < nt) step2(buf[i], buf[i + 1], t + i);
 
   app.store(a);
-  // ---- this wave's slice of the result (m and l are identical in every wave of a group)
+  // ---- combine the waves: each leaves (m, l) per head and its accumulator (in its own
+  // tile area), then wave w combines d blocks 8 w .. 8 w + 7 of all four
   l = rows_sum(l);
-  if constexpr (MH == 2) {
-    // the second group hands (m, l, acc) to the first through its own tile area; the
-    // first group's first key is always valid, so its m is finite
-    floatx4_t* comb = reinterpret_cast<floatx4_t*>(s_kv + (MNW + wsl) * 2 * WAVE_TILE);
-    if (half == 1) {
-      wave_lds_sync();  // this wave's last transposed reads stay before these writes
+  wave_lds_sync();
+  floatx4_t* mine = reinterpret_cast<floatx4_t*>(s_kv + wave * WAVE_LDS);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) comb[db * 64 + lane] = acc[db];
-      if (wsl == 0 && lane < MG) {
-        s_ml[lane][0] = m;
-        s_ml[lane][1] = l;
-      }
-    }
-    __syncthreads();
-    if (half == 1) return;
-    const float m1 = s_ml[l16][0], l1 = s_ml[l16][1];
-    const float mx = fmaxf(m, m1);
-    const float f0 = exp2_fast(m - mx), f1 = exp2_fast(m1 - mx);  // m1 = -inf: f1 = 0
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = acc[db] * f0 + comb[db * 64 + lane] * f1;
-    l = l * f0 + l1 * f1;
-    m = mx;
+  for (int db = 0; db < 32; ++db) mine[db * 64 + lane] = acc[db];
+  if (lg == 0) {
+    s_ml[wave][l16][0] = m;
+    s_ml[wave][l16][1] = l;
   }
-  if constexpr (FP8) {
+  __syncthreads();
+  float fw[NWV], M = -INFINITY, L = 0.0f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] *= 1.0f / p_norm;  // exact: a power of two
+  for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_ml[w][l16][0]);
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const float mw = s_ml[w][l16][0];
+    fw[w] = mw == -INFINITY ? 0.0f : exp2_fast(mw - M);  // a wave without keys: weight 0
+    L = fmaf(s_ml[w][l16][1], fw[w], L);
   }
-  if (k_u == 1) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    float* o = a.out + (head0 + l16) * MD + DQ * wsl + 4 * lg;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db] * inv;
-  } else {
-    const size_t slot = (size_t)g_id;
-    float* o = a.part_acc + (slot * MG + l16) * MD + DQ * wsl + 4 * lg;
+  for (int dd = 0; dd < 32 / NWV; ++dd) {
+    const int db = (32 / NWV) * wave + dd;
+    floatx4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4_t*>(o + 16 * db) = acc[db];
-    if (wsl == 0 && lane < MG) {
-      a.part_ml[(slot * MG + lane) * 2 + 0] = m;
-      a.part_ml[(slot * MG + lane) * 2 + 1] = l;
+    for (int w = 0; w < NWV; ++w)
+      o += reinterpret_cast<const floatx4_t*>(s_kv + w * WAVE_LDS)[db * 64 + lane] * fw[w];
+    const int d = 16 * db + 4 * lg;
+    if (k_u == 1) {
+      *reinterpret_cast<floatx4_t*>(a.out + (head0 + l16) * MD + d) = o * inv;
+    } else {
+      *reinterpret_cast<floatx4_t*>(a.part_acc + ((size_t)g_id * MG + l16) * MD + d) = o;
     }
+  }
+  if (k_u > 1 && wave == 0 && lg == 0) {
+    a.part_ml[((size_t)g_id * MG + l16) * 2 + 0] = M;
+    a.part_ml[((size_t)g_id * MG + l16) * 2 + 1] = L;
   }
 }
 
@@ -578,7 +592,8 @@ merge_units_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       // no early exit: every load is consumed, so all of them are issued up front
-      const float w = s0 + kMergeWaves * i < ks ? exp2_fast(mb[i] - mnew) : 0.0f;
+      const float w =
+          s0 + kMergeWaves * i < ks && mb[i] != -INFINITY ? exp2_fast(mb[i] - mnew) : 0.0f;
       L = fmaf(lb[i], w, L);
       o[0] = fmaf(va[i].x, w, o[0]);
       o[1] = fmaf(va[i].y, w, o[1]);
@@ -606,7 +621,7 @@ merge_units_kernel(DecodeArgs a) {
   float wt[kMergeWaves], Lall = 0.0f;
 #pragma unroll
   for (int w = 0; w < kMergeWaves; ++w) {
-    wt[w] = exp2_fast(s_ml[w][0] - Mall);
+    wt[w] = s_ml[w][0] == -INFINITY ? 0.0f : exp2_fast(s_ml[w][0] - Mall);
     Lall = fmaf(s_ml[w][1], wt[w], Lall);
   }
   const float inv = 1.0f / Lall;
@@ -624,31 +639,70 @@ merge_units_kernel(DecodeArgs a) {
 
 bool decode_mfma_supported(int D, int G, bool k_eq_v) { return D == MD && G == MG && k_eq_v; }
 
-size_t decode_mfma_workspace_bytes(int B, int Hkv) {
-  const size_t units = (size_t)B * Hkv;
-  const size_t slots = (size_t)kMfmaBlocks + units;  // >= sum of k_u, the grid size
-  return slots * MG * MD * 4 + slots * MG * 2 * 4 + (units + 1) * 4;
+size_t decode_mfma_workspace_bytes(long long grid, int units) {
+  const size_t slots = (size_t)grid;  // one partial per work-group
+  // partials and the plan [units + 1]
+  return slots * MG * MD * 4 + slots * MG * 2 * 4 + ((size_t)units + 1) * 4;
 }
 
-hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
-  DecodeArgs a = a0;
-  const long long R = (long long)a.B * a.Hkv;
-  if (R <= 0) return hipSuccess;
-  if (R > kMfmaMaxUnits) return hipErrorInvalidValue;
-  a.n_blocks = kMfmaBlocks;
+long long decode_mfma_grid(int units, int n_blocks, int split_keys, int max_keys) {
+  if (split_keys > 0) {
+    // every unit at most ceil(max_keys / C) work-groups, C the split size rounded up to
+    // whole work-group starts (as the kernel rounds it)
+    const long long c = ((long long)split_keys + kMinWgKeys - 1) / kMinWgKeys * kMinWgKeys;
+    const long long per_unit = ((long long)max_keys + c - 1) / c;
+    return (long long)units * (per_unit > 0 ? per_unit : 1);
+  }
   // Work-groups with work: with R <= 3/4 NB at most R units are non-empty, the kernel
   // takes C = T / (NB - non-empty) and the sum of k_u stays <= NB; past that it takes
   // C = T / NB and the sum stays <= NB + R.  Work-groups u < R also carry unit u's append.
-  const unsigned grid =
-      (unsigned)(R <= kMfmaBlocks - kMfmaBlocks / 4 ? kMfmaBlocks : kMfmaBlocks + R);
-  if (a.fp8)
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(NWV * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(NWV * 64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return units <= n_blocks - n_blocks / 4 ? n_blocks : (long long)n_blocks + units;
+}
+
+hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
+  if (a0.B <= 0) return hipSuccess;
+  // batches of more than kMfmaMaxUnits units run as several launches of whole rows (the
+  // plan lives in LDS); the workspace is reused in stream order
+  const int rows = a0.launch_rows > 0 ? a0.launch_rows : kMfmaMaxUnits / a0.Hkv;
+  if (rows < 1 || (long long)rows * a0.Hkv > kMfmaMaxUnits) return hipErrorInvalidValue;
+  for (int b0 = 0; b0 < a0.B; b0 += rows) {
+    DecodeArgs a = a0;
+    a.B = min(rows, a0.B - b0);
+    const size_t qo = (size_t)b0 * a0.Hq * MD, unit0 = (size_t)b0 * a0.Hkv;
+    a.q += qo;
+    a.out += qo;
+    a.ctx += b0;
+    a.q_pos += b0;
+    if (a.fp8) {
+      a.k8 += unit0 * a0.cap * MD;
+      a.v8 = a.k8;
+      a.k_scale += unit0 * a0.cap;
+      a.v_scale = a.k_scale;
+    } else {
+      a.k += unit0 * a0.cap * MD;
+      a.v = a.k;
+    }
+    if (a.new_pos) {
+      a.new_pos += b0;
+      a.k_new += unit0 * MD;
+      a.k_dst += unit0 * a0.cap * MD;
+    }
+    const long long R = (long long)a.B * a.Hkv;
+    const long long grid = decode_mfma_grid((int)R, a.n_blocks, a.split_keys, a.max_keys);
+    if (grid < R || grid > (1LL << 31) - 1) return hipErrorInvalidValue;
+    if (a.fp8)
+      hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3((unsigned)grid), dim3(NWV * 64), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3((unsigned)grid), dim3(NWV * 64), 0,
+                         stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ga

@@ -27,8 +27,9 @@ struct DecodeArgs {
   int split_keys;         // keys per split (Ts)
   int n_split;            // S, splits per row (host upper bound)
   int max_keys;           // rows longer than this keep their newest keys
-  int* plan;              // matrix-core path: per-unit key prefix sums [B * Hkv + 1]
-  int n_blocks;           // matrix-core path: work-groups of the decode launch
+  int* plan;              // matrix-core path: per-unit work-group prefix sums [B * Hkv + 1]
+  int n_blocks;           // matrix-core path: work-groups that cover the chip (its CUs)
+  int launch_rows = 0;    // matrix-core path: batch rows per launch (0: kMfmaMaxUnits / Hkv)
   // Fused cache append (gemma_attn_decode_append); new_pos == nullptr: none.
   const uint16_t* k_new;  // [B, Hkv, D]
   const uint16_t* v_new;  // [B, Hkv, D], or nullptr for K = V
@@ -138,26 +139,25 @@ struct AppendRow {
   }
 };
 
-// Matrix-core path limits: units (batch rows x KV heads) per call, and the fixed grid:
-// work-groups of kMfmaHalves groups of 4 waves, kMfmaBlocksPerCU per CU of an MI355X
-// (8 waves per CU either way).
+// Matrix-core path (global K = V geometry): work-groups of kMfmaWaves waves, one per CU
+// (the grid follows the device's CU count, at most kMaxBlocks); at most kMfmaMaxUnits
+// units (batch rows x KV heads) per launch, larger batches run as several launches.
+constexpr int kMfmaWaves = 4;
 constexpr int kMfmaMaxUnits = 1024;
-#ifndef GA_MFMA_HALVES
-#define GA_MFMA_HALVES 2
-#endif
-constexpr int kMfmaHalves = GA_MFMA_HALVES;
-constexpr int kMfmaBlocksPerCU = 2 / kMfmaHalves;
-constexpr int kMfmaBlocks = 256 * kMfmaBlocksPerCU;
+constexpr int kMaxBlocks = 256;  // the CU count of an MI355X
 
 // Split kernels.  Each launch covers B * Hkv * S work-groups; with S == 1 the split
 // kernel writes `out` directly, otherwise it writes partials for merge_launch.
 hipError_t decode_valu_launch(const DecodeArgs& a, bool k_eq_v, hipStream_t stream);
 bool decode_valu_supported(int D, int G);
 
-// Matrix-core path (head_dim 512, G = 16, K = V): decode plus its unit merge.
+// Matrix-core path (head_dim 512, G = 16, K = V): decode plus its unit merge.  The grid
+// of one launch for `units` units (split_keys 0: balanced over n_blocks work-groups), and
+// the workspace of one launch: a partial per work-group plus the plan.
 hipError_t decode_mfma_launch(const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(int D, int G, bool k_eq_v);
-size_t decode_mfma_workspace_bytes(int B, int Hkv);  // partials + plan
+long long decode_mfma_grid(int units, int n_blocks, int split_keys, int max_keys);
+size_t decode_mfma_workspace_bytes(long long grid, int units);
 
 // Matrix-core path for 16 query rows per unit (several tokens x heads of one KV head):
 // bf16 caches, head_dim 128 / 256, or 512 with K = V; partials as the vector path's.

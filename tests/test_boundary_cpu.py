@@ -128,22 +128,40 @@ def test_workspace_bytes_closed_form():
     # a window shorter than the ring bounds the keys: w = 100 -> one 128-key split
     o = api.make_opts(split_keys=128)
     assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 100, ctypes.byref(o)) == 0
-    # linear C 32768, full causal, split 512: S = 64
+    # linear C 32768, full causal, split 512 on the vector kernel: S = 64
     s = shape(B=16, Hq=16, Hkv=1, D=512, cap=32768, kind=api.LINEAR)
-    o = api.make_opts(split_keys=512)
-    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == \
-        16 * 16 * 64 * 514 * 4
-    # K = V global geometry: AUTO may pick the matrix-core path, whose workspace is
-    # (256 work-groups, one per CU, + B * Hkv units) partial slots of 16 heads x (512 + 2)
-    # floats, plus B * Hkv + 1 ints of prefix sums; the query covers the larger of the two
-    s = shape(B=16, Hq=16, Hkv=1, D=512, cap=32768, kind=api.LINEAR)
-    mfma = (256 + 16) * 16 * 514 * 4 + 17 * 4
+    o = api.make_opts(split_keys=512, impl=api.IMPL_VALU)
+    valu512 = 16 * 16 * 64 * 514 * 4
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == valu512
+    # K = V global geometry: AUTO may pick the matrix-core path, whose workspace is one
+    # partial slot per work-group (16 heads x (512 + 2) floats) plus B * Hkv + 1 ints of
+    # prefix sums.  Balanced: with B * Hkv <= 3/4 of the 256 CUs the grid is 256 work-
+    # groups, one per CU; the query covers the larger of the two kernels
+    mfma = 256 * 16 * 514 * 4 + 17 * 4
     o = api.make_opts(impl=api.IMPL_MFMA)
     assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == mfma
     auto = lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, None)
     valu = lib.ga_decode_workspace_bytes(ctypes.byref(s), 0,
                                          ctypes.byref(api.make_opts(impl=api.IMPL_VALU)))
     assert auto == max(mfma, valu)
+    # past 3/4 of the CUs in units the grid is 256 + B * Hkv work-groups
+    s2 = shape(B=200, Hq=16, Hkv=1, D=512, cap=4096, kind=api.LINEAR)
+    o = api.make_opts(impl=api.IMPL_MFMA)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s2), 0, ctypes.byref(o)) == \
+        (256 + 200) * 16 * 514 * 4 + 201 * 4
+    # a split size keeps the matrix cores: every unit at most ceil(C / split) work-groups,
+    # one partial each; AUTO sizes for either kernel
+    o = api.make_opts(split_keys=512)
+    mfma512 = 16 * 64 * 16 * 514 * 4 + 17 * 4
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == \
+        max(mfma512, valu512)
+    o = api.make_opts(split_keys=512, impl=api.IMPL_MFMA)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) == mfma512
+    # more units than one launch takes (1024): launches of 1024 / Hkv rows reuse one
+    # workspace sized for a launch
+    s3 = shape(B=3000, Hq=16, Hkv=1, D=512, cap=2048, kind=api.LINEAR)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s3), 0, ctypes.byref(o)) == \
+        1024 * 4 * 16 * 514 * 4 + 1025 * 4
     # invalid shape -> SIZE_MAX
     bad = shape(D=100)
     assert lib.ga_decode_workspace_bytes(ctypes.byref(bad), 0, None) == ctypes.c_size_t(-1).value

@@ -319,7 +319,7 @@ def test_device_errors_launch_nothing():
 # ------------------------------------------------------------------ matrix-core global path
 
 @pytest.mark.parametrize("case", ["one_long_row", "many_short_rows", "rows_at_grid_bound",
-                                  "tile_edges", "ring_kv_shared"])
+                                  "rows_past_grid_bound", "tile_edges", "ring_kv_shared"])
 def test_mfma_partition_cases(case):
     """The matrix-core kernel cuts the batch's keys into equal chunks per work-group:
     one row spread over every work-group, hundreds of rows shorter than a tile, rows
@@ -331,9 +331,13 @@ def test_mfma_partition_cases(case):
         ctx = list(np.random.default_rng(90).integers(0, 40, size=600))
         cap = 64
     elif case == "rows_at_grid_bound":
-        # 384 = 3/4 of the 512 work-groups, all non-empty: the last unit count for which
-        # the launch uses the plain grid; one work-group per row plus the chunked rest
-        ctx = list(np.random.default_rng(92).integers(1, 400, size=384))
+        # 192 = 3/4 of the 256 work-groups (one per CU), all non-empty: the last unit count
+        # for which the launch uses the plain grid; one work-group per row plus the rest
+        ctx = list(np.random.default_rng(92).integers(1, 400, size=192))
+        cap = 400
+    elif case == "rows_past_grid_bound":
+        # 193 non-empty rows: the grid grows by one work-group per unit
+        ctx = list(np.random.default_rng(93).integers(1, 400, size=193))
         cap = 400
     elif case == "tile_edges":
         ctx = [16, 17, 15, 1, 0, 32, 4096, 4095, 4097, 0, 33, 1000]
@@ -355,6 +359,88 @@ def test_mfma_partition_cases(case):
     empty = [b for b in range(B) if ctx[b] == 0]
     if empty:
         assert (out[empty] == 0).all()
+
+
+def test_mfma_growing_logits_take_the_rescaling_path():
+    """Logits that keep growing along the context (every key a larger multiple of q's
+    direction): a wave's maximum rises far past its first step's, so the kernel leaves
+    its fixed-reference loop for the rescaling one; rows of several lengths stop at
+    different steps.  Against the oracle."""
+    B, C = 4, 4096
+    ctx = [4096, 3000, 1500, 700]
+    inp = gen_layer(191, B, 16, 1, 512, C, True, 1, 1, ctx=ctx)
+    # q = 1 in every head; key p = (p // 16) / 2 in every element (bf16-exact: at most 8
+    # significant bits), so the scaled logit grows by 512 / 32 / sqrt(512) ~ 0.71 per
+    # position (~1 log2 unit): a wave's steps 128 positions apart differ by ~130
+    # (plus N(0, 1) noise per element, the sum rounded to bf16, so the values differ)
+    inp.q_bits[:] = 0x3F80
+    vals = ((np.arange(C) // 16) / 2.0).astype(np.float32)
+    noise = torch.randn((B, 1, C, 512), generator=torch.Generator().manual_seed(7))
+    grow = torch.from_numpy(vals)[None, None, :, None] + noise
+    inp.k_bits[:] = synth.bits(grow.to(torch.bfloat16))
+    bits = synth.bits((torch.from_numpy(vals[::-1].copy())[None, None, :, None] +
+                       noise).to(torch.bfloat16))
+    poison_invalid_slots(inp, 0, api.LINEAR, C)
+    inp.to_device()
+    scale = default_scale(512)
+    ref = oracle_out(inp, 0, 0.0, scale, api.LINEAR)
+    # balanced, and with long splits (1024 / 4096 keys: eight or more steps per wave)
+    for split in [0, 1024, 4096]:
+        out = run(inp, 0, 0.0, scale, api.LINEAR, split_keys=split, max_ctx=C)
+        assert_parity(out, ref, f"growing logits split={split}")
+    # decreasing logits stay on the fixed-reference loop: same check
+    inp2 = gen_layer(192, B, 16, 1, 512, C, True, 1, 1, ctx=ctx)
+    inp2.q_bits[:] = 0x3F80
+    inp2.k_bits[:] = bits
+    poison_invalid_slots(inp2, 0, api.LINEAR, C)
+    inp2.to_device()
+    ref2 = oracle_out(inp2, 0, 0.0, scale, api.LINEAR)
+    for split in [0, 1024]:
+        out = run(inp2, 0, 0.0, scale, api.LINEAR, split_keys=split, max_ctx=C)
+        assert_parity(out, ref2, f"falling logits split={split}")
+
+
+def test_mfma_more_units_than_one_launch():
+    """B * Hkv = 2048 global-geometry units (more than the 1024 one launch takes): the
+    library runs whole-row launches in stream order over one workspace, on the matrix
+    cores.  NaN-poisoned slots, sampled rows against the oracle."""
+    B, C = 2048, 256
+    ctx = np.random.default_rng(94).integers(0, C + 1, size=B).astype(np.int32)
+    ctx[:3] = [C, 1, 0]
+    inp = gen_layer(193, B, 16, 1, 512, C, True, 1, 1, ctx=ctx)
+    kb = inp.k_bits.reshape(B, C, 512)
+    kb[np.arange(C)[None, :] >= ctx[:, None]] = synth.BF16_NAN  # never-valid slots
+    inp.to_device()
+    scale = default_scale(512)
+    ws_auto = api.workspace_bytes(api.make_shape(B, 16, 1, 512, C, api.LINEAR), 0)
+    out = run(inp, 0, 0.0, scale, api.LINEAR, max_ctx=C)
+    assert torch.isfinite(out).all(), "a never-valid slot was read"
+    rows = sorted({0, 1, 2, 1023, 1024, 1025, 2047} | set(range(5, B, 97)))
+    ref = oracle_out(inp, 0, 0.0, scale, api.LINEAR, rows=rows)
+    assert_parity(out[rows], ref, "2048 units")
+    assert (out[2] == 0).all()
+    # the same on the matrix cores explicitly, with a split size (fixed chunks per unit)
+    out2 = run(inp, 0, 0.0, scale, api.LINEAR, max_ctx=C, split_keys=64, impl=api.IMPL_MFMA)
+    assert_parity(out2[rows], ref, "2048 units, split 64")
+    log(f"  workspace for the auto plan: {ws_auto} bytes")
+
+
+def test_mfma_split_sizes_match_the_oracle():
+    """A split size on the K = V global geometry keeps the matrix-core kernel (each unit in
+    chunks of that many keys, merged by log-sum-exp): every size agrees with the oracle
+    and with the balanced partition."""
+    inp = gen_layer(194, 5, 16, 1, 512, 5000, True, 1, 1, ctx=[5000, 4097, 1, 0, 2500])
+    poison_invalid_slots(inp, 0, api.LINEAR, 5000)
+    inp.to_device()
+    scale = default_scale(512)
+    ref = oracle_out(inp, 0, 0.0, scale, api.LINEAR)
+    base = run(inp, 0, 0.0, scale, api.LINEAR, impl=api.IMPL_MFMA)
+    assert_parity(base, ref, "balanced")
+    for split in [64, 128, 1024, 4096, 65536]:
+        out = run(inp, 0, 0.0, scale, api.LINEAR, split_keys=split)
+        assert_parity(out, ref, f"mfma split={split}")
+        max_abs, rel = errors(out, base.double().cpu().numpy())
+        assert max_abs < 1e-4 and rel < 1e-4, (split, max_abs, rel)
 
 
 def test_mfma_matches_valu_and_softcap():
