@@ -30,7 +30,7 @@ EXPORTS = ["ga_decode_workspace_bytes", "gemma_attn_decode", "gemma_attn_decode_
            "ga_decode_multi_workspace_bytes", "gemma_attn_decode_multi", "gemma_kv_append_multi",
            "gemma_attn_validate_multi", "gemma_kv_append_fp8", "ga_decode_fp8_workspace_bytes",
            "gemma_attn_decode_fp8", "gemma_rope_append", "gemma_attn_decode_rope_append",
-           "gemma_rope_table", "gemma_attn_decode_append_fp8"]
+           "gemma_rope_table", "gemma_attn_decode_append_fp8", "gemma_attn_decode_noalloc"]
 
 _lib = None
 
@@ -88,6 +88,8 @@ def load():
     lib.gemma_attn_decode_append_fp8.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, i32, f32, f32,
                                                  P, P, sz, OP, P]
     lib.gemma_attn_decode_append_fp8.restype = i32
+    lib.gemma_attn_decode_noalloc.argtypes = [SP, P, P, P, P, P, i32, f32, f32, P, OP, P]
+    lib.gemma_attn_decode_noalloc.restype = i32
     lib.gemma_attn_strerror.argtypes = [i32]
     lib.gemma_attn_strerror.restype = ctypes.c_char_p
     lib.gemma_attn_version.argtypes = []

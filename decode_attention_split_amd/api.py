@@ -23,8 +23,9 @@ ERRORS = {
     -1: "GA_ERR_NULL", -2: "GA_ERR_DIMS", -3: "GA_ERR_HEAD_DIM", -4: "GA_ERR_GQA",
     -5: "GA_ERR_KIND", -6: "GA_ERR_WINDOW", -7: "GA_ERR_WORKSPACE", -8: "GA_ERR_SCALE",
     -9: "GA_ERR_V_MISMATCH", -10: "GA_ERR_ARCH", -11: "GA_ERR_LAUNCH", -12: "GA_ERR_OPTS",
-    -13: "GA_ERR_MAX_CTX", -14: "GA_ERR_TOO_LARGE",
+    -13: "GA_ERR_MAX_CTX", -14: "GA_ERR_TOO_LARGE", -15: "GA_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20  # GA_NOALLOC_SCRATCH_BYTES
 FLAG_QPOS_GE_CTX, FLAG_EVICTED, FLAG_LINEAR_OVER, FLAG_NEGATIVE, FLAG_OVER_MAX_CTX = 1, 2, 4, 8, 16
 
 
@@ -114,7 +115,7 @@ def shape_of(q, k_cache, kind, max_ctx=0):
 
 
 def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, workspace, max_ctx,
-                   split_keys, impl, deterministic):
+                   split_keys, impl, deterministic, need_workspace=True):
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     if v_cache is not None:
@@ -134,6 +135,8 @@ def _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind, out, work
         if tuple(out.shape) != (shape.batch, shape.num_q_heads, shape.head_dim):
             raise ValueError("out must be [B, Hq, D]")
     opts = make_opts(split_keys, impl, deterministic)
+    if not need_workspace:
+        return shape, out, opts, None
     if workspace is None:  # a given workspace is checked against its size by the library
         lib = _lib.load()
         need = lib.ga_decode_workspace_bytes(ctypes.byref(shape), int(window),
@@ -165,6 +168,23 @@ def decode(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float, sc
         int(window), float(softcap), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
         ctypes.byref(opts), _stream_handle(stream))
     _check(rc, "gemma_attn_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, ctx_lens, q_pos, window: int, softcap: float,
+                   scale: float, kind: int, out=None, max_ctx: int = 0, split_keys: int = 0,
+                   impl: int = IMPL_AUTO, deterministic: bool = False, stream=None):
+    """decode() without a workspace: gemma_attn_decode_noalloc uses the library's fixed
+    device scratch (see gemma_attn.h); nothing is allocated here except `out` when it is
+    not given."""
+    shape, out, opts, _ = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window, kind,
+                                         out, None, max_ctx, split_keys, impl, deterministic,
+                                         need_workspace=False)
+    rc = _lib.load().gemma_attn_decode_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens), _ptr(q_pos),
+        int(window), float(softcap), float(scale), _ptr(out), ctypes.byref(opts),
+        _stream_handle(stream))
+    _check(rc, "gemma_attn_decode_noalloc")
     return out
 
 

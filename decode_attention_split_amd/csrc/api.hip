@@ -323,6 +323,9 @@ const char* gemma_attn_strerror(int32_t st) {
     case GA_ERR_OPTS: return "decode options invalid or unsupported for this shape";
     case GA_ERR_MAX_CTX: return "max_ctx must be >= 0 and, for a linear cache, <= capacity";
     case GA_ERR_TOO_LARGE: return "sizes overflow the kernels' index or grid range";
+    case GA_ERR_SCRATCH:
+      return "the call needs more workspace than the fixed device scratch of "
+             "gemma_attn_decode_noalloc holds (GA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -788,3 +791,58 @@ int32_t gemma_attn_debug_ranges(const ga_shape* shape, const int32_t* ctx_lens,
 }
 
 }  // extern "C"
+
+// ---- allocation-free decode: the same as gemma_attn_decode_ex with the library's own
+// device scratch instead of a caller workspace.
+namespace {
+
+// The scratch: one copy per device (a __device__ array lives in each device's copy of the
+// code object), zero-filled when the code object loads, kept until the process ends.  In
+// host code `g_scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+__device__ __attribute__((aligned(256))) unsigned char g_scratch[GA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The scratch's device address on the current device (nullptr on failure).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);  // the same address if two race
+  return p;
+}
+
+}  // namespace
+
+extern "C" int32_t gemma_attn_decode_noalloc(const ga_shape* shape, const ga_bf16* q,
+                                             const ga_bf16* k_cache, const ga_bf16* v_cache,
+                                             const int32_t* ctx_lens, const int32_t* q_pos,
+                                             int32_t window, float softcap, float scale,
+                                             float* out, const ga_decode_opts* opts,
+                                             void* stream) {
+  // the workspace this call needs, from the same plan gemma_attn_decode_ex makes (all its
+  // host checks first, so a bad call returns the same error with nothing launched)
+  int32_t st = check_shape(shape, window);
+  if (st != GA_OK) return st;
+  if (!std::isfinite(scale)) return GA_ERR_SCALE;
+  if (!q || !k_cache || !ctx_lens || !q_pos || !out) return GA_ERR_NULL;
+  const bool k_eq_v = v_cache == nullptr || v_cache == k_cache;
+  Plan p;
+  st = make_plan(shape, window, opts, k_eq_v ? 1 : 0, &p);
+  if (st != GA_OK) return st;
+  if (p.ws_bytes > (size_t)GA_NOALLOC_SCRATCH_BYTES) return GA_ERR_SCRATCH;
+  st = check_arch();
+  if (st != GA_OK) return st;
+  void* ws = scratch_ptr();
+  if (!ws) return GA_ERR_LAUNCH;
+  return gemma_attn_decode_ex(shape, q, k_cache, v_cache, ctx_lens, q_pos, window, softcap,
+                              scale, out, ws, (size_t)GA_NOALLOC_SCRATCH_BYTES, opts, stream);
+}

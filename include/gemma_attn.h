@@ -79,7 +79,9 @@ enum {
   GA_ERR_LAUNCH = -11,       /* a kernel launch failed (hipGetLastError)                  */
   GA_ERR_OPTS = -12,         /* decode options out of range or not valid for this shape   */
   GA_ERR_MAX_CTX = -13,      /* max_ctx < 0, or linear max_ctx > capacity                 */
-  GA_ERR_TOO_LARGE = -14     /* a size overflows the 32-bit grid or index arithmetic      */
+  GA_ERR_TOO_LARGE = -14,    /* a size overflows the 32-bit grid or index arithmetic      */
+  GA_ERR_SCRATCH = -15       /* gemma_attn_decode_noalloc: the call needs more workspace
+                                than its fixed device scratch holds                       */
 };
 
 /* Shape of one layer's decode call. */
@@ -356,6 +358,31 @@ int32_t gemma_rope_append(const ga_shape* shape, int32_t num_tokens, const ga_bf
                           ga_bf16* q_out, ga_bf16* k_cache, ga_bf16* v_cache,
                           const ga_bf16* k_new, const ga_bf16* v_new, const int32_t* pos,
                           float rope_base, int32_t rotary_dim, void* stream);
+
+/*
+ * Allocation-free single-token decode, for callers that cannot allocate device memory or
+ * manage a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): exactly gemma_attn_decode_ex(shape, q, k_cache, v_cache, ctx_lens,
+ * q_pos, window, softcap, scale, out, <scratch>, GA_NOALLOC_SCRATCH_BYTES, opts, stream),
+ * same kernels and same results, with the library's own device scratch as the workspace.
+ * The scratch is a fixed array of GA_NOALLOC_SCRATCH_BYTES in device memory, one per
+ * device the library runs on, held until the process ends; the call itself allocates and
+ * frees nothing.  A call whose workspace (ga_decode_workspace_bytes for the same shape,
+ * window and options) exceeds it returns GA_ERR_SCRATCH with nothing launched.  32 MiB
+ * holds 1020 partials of the global matrix-core path (its balanced partition for up to 764
+ * units of batch rows x KV heads; the Gemma-4-12B global layer at batch 16 needs 8.4 MB)
+ * and the vector path's split partials up to the same size.  Every call on one device
+ * shares that device's scratch: calls that overlap in time on one device (on different
+ * streams, or from different threads without ordering) race on it and must not be issued;
+ * calls ordered on one stream are safe.  Other arguments, ownership and errors as for
+ * gemma_attn_decode_ex.
+ */
+#define GA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t gemma_attn_decode_noalloc(const ga_shape* shape, const ga_bf16* q, const ga_bf16* k_cache,
+                                  const ga_bf16* v_cache, const int32_t* ctx_lens,
+                                  const int32_t* q_pos, int32_t window, float softcap,
+                                  float scale, float* out, const ga_decode_opts* opts,
+                                  void* stream);
 
 /* Precondition flags written by gemma_attn_validate, per batch row. */
 enum {

@@ -331,3 +331,23 @@ def test_decode_append_fp8_argument_checks():
     if no_gpu():
         assert call() == -10
         assert call(v_codes=0, v_scales=0, v_new=0) == -10  # K = V
+
+
+def test_noalloc_refuses_a_call_beyond_its_scratch_before_any_launch():
+    """gemma_attn_decode_noalloc returns GA_ERR_SCRATCH (nothing launched, no device call)
+    when the plan's workspace exceeds its fixed scratch, and the host checks of
+    gemma_attn_decode_ex before that."""
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    s = shape(B=4, Hq=16, Hkv=1, D=512, cap=1 << 16, kind=api.LINEAR)
+    o = api.make_opts(split_keys=64, impl=api.IMPL_MFMA)
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(s), 0, ctypes.byref(o)) > \
+        api.NOALLOC_SCRATCH_BYTES
+    rc = lib.gemma_attn_decode_noalloc(ctypes.byref(s), P(FAKE), P(FAKE), None, P(FAKE), P(FAKE),
+                                       0, 0.0, 1.0, P(FAKE), ctypes.byref(o), None)
+    assert rc == -15
+    bad = shape(D=100)
+    assert lib.gemma_attn_decode_noalloc(ctypes.byref(bad), P(FAKE), P(FAKE), None, P(FAKE),
+                                         P(FAKE), 0, 0.0, 1.0, P(FAKE), None, None) == -3
+    assert lib.gemma_attn_decode_noalloc(ctypes.byref(shape()), None, P(FAKE), None, P(FAKE),
+                                         P(FAKE), 1024, 0.0, 1.0, P(FAKE), None, None) == -1
