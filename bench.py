@@ -108,16 +108,25 @@ def read_traffic(kernel_tag):
         return None
 
 
-# Sources whose change invalidates counter-measured traffic of the dominant kernel.
-TRAFFIC_SOURCES = ["decode_attention_split_amd/csrc/decode_valu_impl.h",
-                   "decode_attention_split_amd/csrc/decode_valu_d256.hip",
-                   "decode_attention_split_amd/csrc/ga_device.h",
-                   "decode_attention_split_amd/csrc/ga_internal.h",
-                   "decode_attention_split_amd/csrc/ga_rope.h",
-                   "decode_attention_split_amd/csrc/ga_quant.h",
-                   "decode_attention_split_amd/csrc/api.hip"]
+# Sources whose change invalidates counter-measured traffic of a kernel (by name).
+_CSRC = "decode_attention_split_amd/csrc/"
+TRAFFIC_SOURCES = {
+    "decode_valu_kernel": [_CSRC + f for f in ["decode_valu_impl.h", "decode_valu_d256.hip",
+                                               "ga_device.h", "ga_internal.h", "ga_rope.h",
+                                               "ga_quant.h", "api.hip"]],
+    "decode_mfma_kernel": [_CSRC + f for f in ["decode_mfma.hip", "ga_mfma.h", "ga_device.h",
+                                               "ga_internal.h", "api.hip"]],
+}
+
+
+def traffic_sources(kernel):
+    for key, files in TRAFFIC_SOURCES.items():
+        if key in kernel:
+            return files
+    raise KeyError(f"no source list for kernel {kernel}")
 DOMINANT = "decode_valu_kernel<256, 2"
 COPY_BYTES = 1 << 30
+READ_BYTES = 1 << 30
 
 
 def sources_digest(rels):
@@ -176,8 +185,9 @@ def summarize_counters(fetch_csv, write_csv, command, kernel=""):
     print(f"fetch_bytes_per_launch: {f * f_scale:.0f}")
     print(f"write_bytes_per_launch: {w * w_scale:.0f}")
     print(f"hbm_bytes_per_launch: {f * f_scale + w * w_scale:.0f}")
-    print(f"sources: {' '.join(TRAFFIC_SOURCES)}")
-    print(f"sources_sha256: {sources_digest(TRAFFIC_SOURCES)}")
+    files = traffic_sources(dom[0] if dom else (kernel or DOMINANT))
+    print(f"sources: {' '.join(files)}")
+    print(f"sources_sha256: {sources_digest(files)}")
 
 
 def summarize_sq(csvs, command):
@@ -365,7 +375,9 @@ def main():
     extras = step_variants(args, step, stream, cache, qs, ctx_t, qpos_t, outs, L,
                            sum(x["decode"] for x in per_layer), graph is not None)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    extras["pct_of_copy_ceiling"] = round(100.0 * value / extras["copy_ceiling_gbps"], 2)
+    extras["pct_of_read_ceiling"] = round(100.0 * value / extras["read_ceiling_gbps"], 2)
+    if not rope:
+        extras["single_layer_workloads"] = gated_layers(args)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -411,15 +423,40 @@ def main():
 
     result["extras"] = extras
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cache, qs, ctx, w, per_layer, args.cpu_seconds)
+        # (with the rotary embedding the decode read the rotated q of each layer)
+        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(
+            cache, q_rot if rope else qs, outs, ctx, w, per_layer, args.cpu_seconds)
+    # release the device memory before the line is printed, so the process ends promptly
+    del cache, qs, k_new, v_new, outs, q_rot, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
+
+
+def gated_layers(args):
+    """The single-layer workloads with a bandwidth target besides the 48-layer step (the
+    Gemma-4-12B sliding and global layers), each timed as its own fused append + decode
+    launch over rotating cache copies: us per launch, algorithmic bytes, GB/s and the
+    fraction of the 8 TB/s peak."""
+    import torch
+    from decode_attention_split_amd import workloads as wl
+    res = {}
+    for name, w in [("g4_12b_sliding", wl.G4_12B_SLIDING), ("g4_12b_global", wl.G4_12B_GLOBAL)]:
+        r = time_single_layer(w, max(10, args.steps), max(3, args.warmup))
+        gbps = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        log(f"{name}: {r['ms'] * 1e3:.2f} us per launch, {gbps:.1f} GB/s")
+        res[name] = {"workload": w.name, "us_per_launch": round(r["ms"] * 1e3, 3),
+                     "algorithmic_bytes": int(r["bytes"]), "gbps": round(gbps, 1),
+                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        torch.cuda.empty_cache()
+    return res
 
 
 def step_variants(args, step, stream, cache, qs, ctx_t, qpos_t, outs, L, decode_bytes, graphed):
     """Besides the timed step: its per-step time distribution, the step without the append
-    (decode over the resident caches only), the step replayed as a HIP graph, and a
-    copy-kernel ceiling measured on the same GPU (torch copy of 1 GiB: read + write bytes
-    over time), each after the main measurement."""
+    (decode over the resident caches only), the step replayed as a HIP graph, and the read
+    ceiling measured on the same GPU (gemma_stream_read over 1 GiB), each after the main
+    measurement."""
     import numpy as np
     import torch
     n = max(1, args.steps)
@@ -459,41 +496,51 @@ def step_variants(args, step, stream, cache, qs, ctx_t, qpos_t, outs, L, decode_
         torch.cuda.synchronize()
         ms_graph = timed(g.replay)
         del g
-    src = torch.ones((COPY_BYTES // 4,), dtype=torch.float32, device=qs[0].device)
-    dst = torch.empty_like(src)
-    ms_copy = timed(lambda: dst.copy_(src))
-    del src, dst
-    copy_gbps = 2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9
+    read_gbps = read_ceiling(stream, qs[0].device, n)
     log(f"step p10/p50/p90 {np.percentile(per, [10, 50, 90]).round(4).tolist()} ms; decode only "
-        f"{ms_decode:.4f} ms; graph {ms_graph} ms; copy ceiling {copy_gbps:.0f} GB/s")
+        f"{ms_decode:.4f} ms; graph {ms_graph} ms; read ceiling {read_gbps:.0f} GB/s")
     return {
         "step_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(per, [10, 50, 90])],
         "decode_only_ms_per_step": round(ms_decode, 5),
         "decode_only_gbps": round(decode_bytes / (ms_decode * 1e-3) / 1e9, 2),
         "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 5),
-        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "read_ceiling_gbps": round(read_gbps, 1),
     }
 
 
-def bench_single_layer(args):
-    """One layer type: fused append + decode of its workload, rotating over enough cache
-    copies (>= 1 GiB in all) that no launch finds its keys in the 256 MB Infinity Cache."""
+def read_ceiling(stream, device, reps):
+    """The practical read ceiling on this GPU: gemma_stream_read (the decode kernels' own
+    16-byte non-temporal loads, 16 in flight per wave, four waves per CU) over two 1 GiB
+    buffers read in turn (8x the 256 MB Infinity Cache), timed with HIP events."""
+    import torch
+    from decode_attention_split_amd import api
+    bufs = [torch.ones((READ_BYTES // 4,), dtype=torch.float32, device=device) for _ in range(2)]
+    sink = api.stream_read(bufs[0])
+    for i in range(2):
+        api.stream_read(bufs[i % 2], sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(4, reps)
+    a.record(stream)
+    for i in range(reps):
+        api.stream_read(bufs[i % 2], sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del bufs, sink
+    return READ_BYTES / (ms * 1e-3) / 1e9
+
+
+def time_single_layer(w, steps, warmup, keep=False):
+    """Fused append + decode of one single-token bf16 layer workload, rotating over enough
+    cache copies (>= 1 GiB in all) that no launch finds its keys in the 256 MB Infinity
+    Cache.  Returns the time per launch and the algorithmic bytes; with keep, also the
+    inputs of the first copy (for the oracle)."""
     import numpy as np
     import torch
-    sys.path.insert(0, ROOT)
     from decode_attention_split_amd import api, synth
-    from decode_attention_split_amd import workloads as wl
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = getattr(wl, SINGLE_LAYER[args.workload])
-    if w.kv_dtype == "fp8":
-        return bench_fp8(args, w)
-    if w.tokens > 1:
-        return bench_multi_token(args, w)
     g = w.layers[0]
     B = w.batch
     gen_cpu = synth.generator(w.seed)
@@ -525,19 +572,48 @@ def bench_single_layer(args):
         api.decode_append(q, k, v, k_new, v_new, pos_t, ctx_t, pos_t, g.window, g.softcap,
                           g.q_scale, g.kind, out=out, workspace=ws, max_ctx=max_ctx)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / steps
     lb = layer_bytes(g, B, ctx)
-    nbytes = lb["decode"] + lb["append"]
+    res = {"ms": ms, "bytes": lb["decode"] + lb["append"], "ctx": ctx, "copies": copies}
+    if keep:
+        res["inputs"] = sets[0]
+    del sets, ws, out
+    return res
+
+
+def bench_single_layer(args):
+    """One layer type: fused append + decode of its workload, rotating over enough cache
+    copies (>= 1 GiB in all) that no launch finds its keys in the 256 MB Infinity Cache."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    from decode_attention_split_amd import api, synth
+    from decode_attention_split_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = getattr(wl, SINGLE_LAYER[args.workload])
+    if w.kv_dtype == "fp8":
+        return bench_fp8(args, w)
+    if w.tokens > 1:
+        return bench_multi_token(args, w)
+    g = w.layers[0]
+    B = w.batch
+    r = time_single_layer(w, args.steps, args.warmup, keep=not args.no_cpu_baseline)
+    ms, nbytes, ctx, copies = r["ms"], r["bytes"], r["ctx"], r["copies"]
     gbps = nbytes / (ms * 1e-3) / 1e9
     log(f"{w.name}: {ms * 1e3:.2f} us per launch, {gbps:.1f} GB/s, {copies} cache copies")
     result = {
@@ -565,7 +641,7 @@ def bench_single_layer(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        q, k, v = sets[0]
+        q, k, v = r["inputs"]
         qb, kb, vb = synth.bits(q), synth.bits(k), None if v is None else synth.bits(v)
         threads = oracle.num_threads_default()
         rows, spent, done = 0, 0.0, 0
@@ -845,9 +921,12 @@ def bench_fp8(args, w):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cache, qs, ctx, w, per_layer, target_s):
+def cpu_baseline(cache, qs, outs, ctx, w, per_layer, target_s):
     """The fp64 oracle, as it stands, on whole layers of the same step (all 32 rows),
-    taken in schedule order until about target_s seconds of oracle time."""
+    taken in schedule order until about target_s seconds of oracle time.  Each layer's
+    oracle output is also compared with the layer's GPU output from the timed run (the
+    caches hold the appended token, the outputs the last step's decode): max-abs and
+    relative L2 per layer against the parity bar (1e-2, 2e-3)."""
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
@@ -856,22 +935,40 @@ def cpu_baseline(cache, qs, ctx, w, per_layer, target_s):
 
     ctx = np.asarray(ctx, np.int32)
     qpos = ctx - 1
-    done_bytes, spent, layers = 0, 0.0, []
+    done_bytes, spent, layers, errs = 0, 0.0, [], []
     threads = oracle.num_threads_default()
     for li, g in enumerate(w.layers):
         k = synth.bits(cache.k[li])
         v = None if cache.v[li] is None else synth.bits(cache.v[li])
         q = synth.bits(qs[li])
         t0 = time.perf_counter()
-        oracle.decode(q, k, v, ctx, qpos, g.window, g.softcap, g.q_scale, g.kind, nthreads=threads)
+        ref, _, _, _ = oracle.decode(q, k, v, ctx, qpos, g.window, g.softcap, g.q_scale, g.kind,
+                                     nthreads=threads)
         spent += time.perf_counter() - t0
         done_bytes += per_layer[li]["decode"]
         layers.append(li)
+        got = outs[li].double().cpu().numpy()
+        d = got - ref
+        errs.append((li, float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref)),
+                     bool(np.isfinite(got).all())))
         del k, v
         log(f"oracle layer {li}: {spent:.1f}s cumulative")
         if spent >= target_s and li % 6 == 5:
             break
     units = max(g.num_q_heads for g in w.layers) * len(ctx)
+    worst_abs = max(errs, key=lambda e: e[1])
+    worst_rel = max(errs, key=lambda e: e[2])
+    check = {
+        "layers_checked": len(errs),
+        "max_abs": worst_abs[1], "max_abs_layer": worst_abs[0],
+        "rel_l2": worst_rel[2], "rel_l2_layer": worst_rel[0],
+        "all_finite": all(e[3] for e in errs),
+        "tolerance": {"max_abs": 1e-2, "rel_l2": 2e-3},
+        "pass": all(e[3] and e[1] <= 1e-2 and e[2] <= 2e-3 for e in errs),
+        "per_layer": [[e[0], float(f"{e[1]:.3e}"), float(f"{e[2]:.3e}")] for e in errs],
+    }
+    log(f"oracle check: {len(errs)} layers, worst max_abs {worst_abs[1]:.2e} (layer "
+        f"{worst_abs[0]}), worst rel_l2 {worst_rel[2]:.2e} (layer {worst_rel[0]})")
     return {
         "value": round(done_bytes / spent / 1e9, 4),
         "unit": "GB/s",
@@ -880,7 +977,7 @@ def cpu_baseline(cache, qs, ctx, w, per_layer, target_s):
         "sample": f"layers {layers[0]}-{layers[-1]} of the 48-layer step (whole layers, all "
                   f"{len(ctx)} rows, decode only), {spent:.1f}s of oracle time",
         "host": host_cpu(),
-    }
+    }, check
 
 
 def host_cpu():

@@ -30,7 +30,8 @@ EXPORTS = ["ga_decode_workspace_bytes", "gemma_attn_decode", "gemma_attn_decode_
            "ga_decode_multi_workspace_bytes", "gemma_attn_decode_multi", "gemma_kv_append_multi",
            "gemma_attn_validate_multi", "gemma_kv_append_fp8", "ga_decode_fp8_workspace_bytes",
            "gemma_attn_decode_fp8", "gemma_rope_append", "gemma_attn_decode_rope_append",
-           "gemma_rope_table", "gemma_attn_decode_append_fp8", "gemma_attn_decode_noalloc"]
+           "gemma_rope_table", "gemma_attn_decode_append_fp8", "gemma_attn_decode_noalloc",
+           "gemma_stream_read_sink_bytes", "gemma_stream_read"]
 
 _lib = None
 
@@ -90,6 +91,10 @@ def load():
     lib.gemma_attn_decode_append_fp8.restype = i32
     lib.gemma_attn_decode_noalloc.argtypes = [SP, P, P, P, P, P, i32, f32, f32, P, OP, P]
     lib.gemma_attn_decode_noalloc.restype = i32
+    lib.gemma_stream_read_sink_bytes.argtypes = []
+    lib.gemma_stream_read_sink_bytes.restype = sz
+    lib.gemma_stream_read.argtypes = [P, sz, P, P]
+    lib.gemma_stream_read.restype = i32
     lib.gemma_attn_strerror.argtypes = [i32]
     lib.gemma_attn_strerror.restype = ctypes.c_char_p
     lib.gemma_attn_version.argtypes = []

@@ -583,3 +583,16 @@ def debug_ranges(shape, ctx_lens, q_pos, window: int, stream=None):
                                              int(window), _ptr(out), _stream_handle(stream))
     _check(rc, "gemma_attn_debug_ranges")
     return out
+
+
+def stream_read(src, sink=None, stream=None):
+    """One streaming read of the whole uint8/any-dtype device tensor `src` (its byte size a
+    multiple of 1024) with gemma_stream_read; returns the sink tensor."""
+    lib = _lib.load()
+    if sink is None:
+        sink = torch.empty((lib.gemma_stream_read_sink_bytes(),), dtype=torch.uint8,
+                           device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check(lib.gemma_stream_read(_ptr(src), nbytes, _ptr(sink), _stream_handle(stream)),
+           "gemma_stream_read")
+    return sink

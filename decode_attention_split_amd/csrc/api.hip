@@ -846,3 +846,18 @@ extern "C" int32_t gemma_attn_decode_noalloc(const ga_shape* shape, const ga_bf1
   return gemma_attn_decode_ex(shape, q, k_cache, v_cache, ctx_lens, q_pos, window, softcap,
                               scale, out, ws, (size_t)GA_NOALLOC_SCRATCH_BYTES, opts, stream);
 }
+
+extern "C" size_t gemma_stream_read_sink_bytes(void) {
+  return (size_t)ga::kMaxBlocks * 4 * 64 * 16;
+}
+
+extern "C" int32_t gemma_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return GA_ERR_NULL;
+  if (!aligned16(src) || !aligned16(sink)) return GA_ERR_NULL;
+  if (bytes == 0 || bytes % 1024 != 0) return GA_ERR_DIMS;
+  int32_t st = check_arch();
+  if (st != GA_OK) return st;
+  const hipError_t e =
+      ga::stream_read_launch(src, bytes, sink, device_cus(), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
+}

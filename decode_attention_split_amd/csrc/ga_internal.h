@@ -167,6 +167,11 @@ bool decode_rows16_supported(int D, bool k_eq_v);
 
 hipError_t merge_launch(const DecodeArgs& a, hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 1 KiB) over `blocks` work-groups of four waves;
+// sink receives blocks * 4 * 64 16-byte values.
+hipError_t stream_read_launch(const void* src, size_t bytes, void* sink, int blocks,
+                              hipStream_t stream);
+
 // T tokens per row at positions pos[b] + t (T = 1: the single-token append).
 hipError_t append_launch(int B, int T, int Hkv, int D, int cap, int kind, uint16_t* k_cache,
                          uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,

@@ -384,6 +384,20 @@ int32_t gemma_attn_decode_noalloc(const ga_shape* shape, const ga_bf16* q, const
                                   float scale, float* out, const ga_decode_opts* opts,
                                   void* stream);
 
+/*
+ * Measurement aid: the practical read ceiling the decode kernels are measured against.
+ * Decode attention is bound by streaming the cache ("Gemma 4 12B (unified multimodal)"
+ * record, "required kernel class"), so a bare streaming read with the decode kernels' own
+ * loads (16 bytes per lane, non-temporal, one contiguous KiB per instruction, 16 in flight
+ * per wave, four waves per CU) gives the rate no decode kernel can beat on this device.
+ * gemma_stream_read reads `bytes` (a non-zero multiple of 1024) of device memory at src
+ * (16-byte aligned) once, on `stream`, and writes a reduction of what it read to sink
+ * (device, 16-byte aligned, gemma_stream_read_sink_bytes() bytes) so that nothing is
+ * skipped.  Errors: GA_ERR_NULL, GA_ERR_DIMS, GA_ERR_ARCH, GA_ERR_LAUNCH.
+ */
+size_t gemma_stream_read_sink_bytes(void);
+int32_t gemma_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* Precondition flags written by gemma_attn_validate, per batch row. */
 enum {
   GA_FLAG_QPOS_GE_CTX = 1, /* q_pos >= ctx                                         */
