@@ -50,6 +50,9 @@ def parse_args():
     p.add_argument("--summarize-sq", nargs="+", metavar="PMC_CSV",
                    help="print per-kernel SQ counter averages of rocprofv3 --pmc runs and exit")
     p.add_argument("--command", default="", help="command line recorded in summaries")
+    p.add_argument("--step-only", action="store_true",
+                   help="48-layer step: leave out the single-layer lines (counter runs that "
+                        "must see the step's launches only)")
     p.add_argument("--workload", default="hybrid48",
                    choices=sorted(SINGLE_LAYER) + ["hybrid48", "hybrid48_rope"],
                    help="hybrid48: the 48-layer step (default); hybrid48_rope: the same step "
@@ -158,34 +161,42 @@ def summarize_counters(fetch_csv, write_csv, command, kernel=""):
     import csv
 
     def per_kernel(path, counter):
+        # keyed by (kernel, grid size): the same kernel also serves other workloads of the
+        # run (the single-layer lines), whose launches have other grids
         vals = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+            vals.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(
+                float(r["Counter_Value"]) * 1024.0)
         return vals
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
 
     def calib(vals):
-        copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs if v > 1e8]
+        copies = [v for k, vs in vals.items() if "copyBuffer" in k[0] for v in vs if v > 1e8]
         return COPY_BYTES / (sum(copies) / len(copies))
 
     f_scale, w_scale = calib(fetch), calib(write)
-    dom = [k for k in fetch if (kernel or DOMINANT) in k]
-    f = sum(sum(fetch[k]) for k in dom) / sum(len(fetch[k]) for k in dom)
-    w = sum(sum(write[k]) for k in dom) / sum(len(write[k]) for k in dom)
+    # the timed workload's launches: the matching (kernel, grid) with the most dispatches
+    dom = max((k for k in fetch if (kernel or DOMINANT) in k[0]),
+              key=lambda k: len(fetch[k]), default=None)
+    if dom is None or dom not in write:
+        raise SystemExit(f"no dispatches of {kernel or DOMINANT} in both counter runs")
+    f = sum(fetch[dom]) / len(fetch[dom])
+    w = sum(write[dom]) / len(write[dom])
     what = "the dominant kernel" if not kernel else "one kernel"
     print(f"# HBM traffic of {what} (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     print(f"command: {command}")
-    print(f"kernel: {dom[0][:100] if dom else 'n/a'}")
+    print(f"kernel: {dom[0][:100]}")
+    print(f"grid_size: {dom[1]} (dispatches: {len(fetch[dom])} fetch, {len(write[dom])} write)")
     print(f"fetch_calibration (1 GiB copy bytes / counter bytes): {f_scale:.4f}")
     print(f"write_calibration (1 GiB copy bytes / counter bytes): {w_scale:.4f}")
     print(f"fetch_bytes_per_launch: {f * f_scale:.0f}")
     print(f"write_bytes_per_launch: {w * w_scale:.0f}")
     print(f"hbm_bytes_per_launch: {f * f_scale + w * w_scale:.0f}")
-    files = traffic_sources(dom[0] if dom else (kernel or DOMINANT))
+    files = traffic_sources(dom[0])
     print(f"sources: {' '.join(files)}")
     print(f"sources_sha256: {sources_digest(files)}")
 
@@ -200,6 +211,7 @@ def summarize_sq(csvs, command):
             k = r["Kernel_Name"]
             if not k.startswith("void ga::") and not k.startswith("ga::"):
                 continue
+            k = f"{k[:100]}  (grid {r['Grid_Size']})"
             vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
     print("# SQ counters per dispatch (rocprofv3 --pmc, summed over the chip, averaged)")
@@ -207,7 +219,7 @@ def summarize_sq(csvs, command):
     for k, cs in vals.items():
         avg = {c: sum(v) / len(v) for c, v in cs.items()}
         n = max(len(v) for v in cs.values())
-        print(f"\nkernel: {k[:100]}  (dispatches per counter: {n})")
+        print(f"\nkernel: {k}  (dispatches per counter: {n})")
         for c in sorted(avg):
             print(f"  {c:28s} {avg[c]:.4g}")
         cyc = avg.get("SQ_WAVE_CYCLES")
@@ -376,7 +388,7 @@ def main():
                            sum(x["decode"] for x in per_layer), graph is not None)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     extras["pct_of_read_ceiling"] = round(100.0 * value / extras["read_ceiling_gbps"], 2)
-    if not rope:
+    if not rope and not args.step_only:
         extras["single_layer_workloads"] = gated_layers(args)
     result = {
         "metric": METRIC,

@@ -258,7 +258,9 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
   }
   if (T > 1) {
     // several query tokens (per-row masks): 16 query rows per unit on the matrix cores
-    // when heads x tokens fill at least half of them, else the vector kernel
+    // when heads x tokens fill at least a quarter of them (measured on the 12B sliding
+    // layer with 2 and 4 heads per KV head: the matrix cores win from 4 rows on, by up
+    // to 4x), else the vector kernel
     const int G = s->num_q_heads / s->num_kv_heads;
     const bool ok = k_eq_v != -1 ? ga::decode_rows16_supported(s->head_dim, k_eq_v == 1)
                                  : ga::decode_rows16_supported(s->head_dim, false) ||
@@ -267,7 +269,7 @@ int32_t make_plan(const ga_shape* s, int32_t window, const ga_decode_opts* o, in
       if (!ok) return GA_ERR_OPTS;
       return rows16_plan(s, window, ts, T, p, n_blocks);
     }
-    if (impl == GA_IMPL_AUTO && ok && (long long)G * T >= 8) {
+    if (impl == GA_IMPL_AUTO && ok && (long long)G * T >= 4) {
       if (k_eq_v != -1) return rows16_plan(s, window, ts, T, p, n_blocks);
       Plan v;  // workspace query: size for whichever the call may pick
       int32_t st = valu_plan(s, window, ts, T, &v, n_blocks);

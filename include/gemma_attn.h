@@ -115,11 +115,16 @@ typedef struct ga_decode_opts {
  * Vector path: split partials in fp32, acc [B, Hq, S, D] then (m, l) [B, Hq, S, 2], with
  * S the host upper bound of splits per row; 0 when every row fits in one split (no
  * workspace is touched).  Matrix-core path (head_dim 512, 16 query heads per KV head,
- * K = V): one partial per work-group with work, acc [P, 16, 512] and (m, l) [P, 16, 2]
- * in fp32 with P = 512 + B * Hkv slots, then the per-unit work-group prefix sums
- * [B * Hkv + 1] int32.  With GA_IMPL_AUTO and no split size given, the maximum of both,
- * since the implementation is picked per call.  Returns SIZE_MAX when the arguments
- * are invalid (the decode call would fail).
+ * K = V): one launch covers at most 1024 units (B * Hkv, whole rows; larger batches run
+ * as several launches that reuse the workspace), and each of its P work-groups writes
+ * one partial, acc [P, 16, 512] then (m, l) [P, 16, 2] in fp32, followed by the per-unit
+ * work-group prefix sums [U + 1] int32 (U units in one launch).  Without a split size
+ * P = N when U <= 3N/4 and N + U otherwise, N = 256 (a call on a device with fewer
+ * compute units uses that count and needs less); with a split size of s keys,
+ * P = U * ceil(Kmax / round_up(s, 64)), Kmax the largest key count any row can see.
+ * When the query cannot tell which path a call will take (GA_IMPL_AUTO and the
+ * matrix-core geometry, K = V not known), the maximum of both.  Returns SIZE_MAX when
+ * the arguments are invalid (the decode call would fail).
  */
 size_t ga_decode_workspace_bytes(const ga_shape* shape, int32_t window, const ga_decode_opts* opts);
 
@@ -250,10 +255,9 @@ int32_t gemma_kv_append_fp8(const ga_shape* shape, int32_t num_tokens, uint8_t* 
  * q . codes in float32 and multiply by the row's K scale, the value weights carry the
  * row's V scale.  The kernels are chosen as for bf16 caches: with one token, the K = V
  * global geometry (head_dim 512, 16 query heads per KV head) runs on the matrix cores;
- * with several tokens, 16 query rows per KV head (heads x tokens >= 8; head_dim 128 or
- * 256, or 512 with K = V) run on the matrix cores; there the codes are widened exactly
- * (to fp16 on the global geometry, with q and the value weights brought into fp16's range
- * by powers of two per work-group; to bf16 for several tokens), the K scale multiplies
+ * with several tokens, 16 query rows per KV head (heads x tokens >= 4, padded to 16;
+ * head_dim 128 or 256, or 512 with K = V) run on the matrix cores; there the codes are
+ * widened exactly to bf16 (every e4m3 value is a bf16 value), the K scale multiplies
  * each logit and the V scale each value weight.  Every other shape runs on the vector
  * kernel (GA_IMPL_MFMA is refused there).
  * Workspace: ga_decode_fp8_workspace_bytes (covers whichever kernel the call picks).
