@@ -507,11 +507,14 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
     }
   }
   if (rope) {
-    // Fused into the vector kernel's single-token launch; every work-group of a unit
-    // rotates from q, so an in-place q_out needs a single split.  Otherwise the RoPE +
-    // append kernel runs first and the decode reads the rotated q and the appended cache.
-    const bool fused = !p.rows16 && p.impl != GA_IMPL_MFMA &&
-                       (p.n_split == 1 || (const void*)rope->q_out != (const void*)q);
+    // Fused into the single-token launch (vector kernel, or the matrix-core kernel on
+    // bf16 caches); every work-group of a unit rotates from q, so an in-place q_out needs
+    // a single split (the matrix-core kernel has several per unit: never in place).
+    // Otherwise the RoPE + append kernel runs first and the decode reads the rotated q
+    // and the appended cache.
+    const bool separate_out = (const void*)rope->q_out != (const void*)q;
+    const bool fused = !p.rows16 && (p.impl == GA_IMPL_MFMA ? !f8 && separate_out
+                                                            : p.n_split == 1 || separate_out);
     if (fused) {
       a.rope = 1;
       a.rope_dim = rope->dim;

@@ -52,6 +52,7 @@
 #include "ga_device.h"
 #include "ga_internal.h"
 #include "ga_mfma.h"
+#include "ga_rope.h"
 
 #include <type_traits>
 
@@ -70,7 +71,7 @@ constexpr float kRescaleLog2 = 8.0f;
 // stay below 2^64, far inside fp32 (and bf16) range for the accumulator and the sum.
 constexpr float kFastHeadroom = 64.0f;
 static_assert(NWV * WAVE_LDS + MG * ROWB + 2 * (kMfmaMaxUnits + 1) * 4 + NWV * MG * 2 * 4 +
-                      NWV * 32 * 4 <=
+                      NWV * 32 * 4 + ROWB <=
                   160 * 1024,
               "LDS budget per work-group");
 static_assert(WAVE_LDS >= 32 * 64 * 16, "a wave's LDS holds its accumulator at the end");
@@ -107,9 +108,28 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-template <bool FP8>
+// Rotary embedding of element d (of 2 half rotated ones) of a row at the angles of tab
+// (the (cos, sin) pairs of one position); elements d >= 2 half pass through.  The same
+// per-pair arithmetic as the RoPE + append kernel, so both give the same bits.
+__device__ __forceinline__ uint16_t rope_at(const uint16_t* row, int d, int half,
+                                            const double2* tab) {
+  if (d >= 2 * half) return row[d];
+  const int i = d < half ? d : d - half;
+  const double2 cs = tab[i];
+  return d < half ? rope_first(row[i], row[i + half], cs.x, cs.y)
+                  : rope_second(row[i], row[i + half], cs.x, cs.y);
+}
+
+// ROPE (bf16 caches): the rotary embedding at new_pos[b] fused in.  Every work-group
+// rotates its unit's 16 query rows and new K row in LDS (from the same (cos, sin) table
+// as the RoPE + append kernel); the unit's first work-group writes the rotated rows out
+// (q_rot_out, and the K row into its cache slot), and the work-group holding the appended
+// key puts the rotated row into its tile in place of the one it loaded from k_new.  A
+// unit with no keys has no work-group of its own: work-group u writes its rows.
+template <bool FP8, bool ROPE>
 __global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_mfma_kernel(DecodeArgs a) {
+  static_assert(!(FP8 && ROPE), "RoPE is fused on bf16 caches only");
   // Tiles per step: bf16 one (16 load instructions of a whole 1 KiB row each); fp8 two
   // (8 instructions of two 512-code rows each per tile).  Either way a wave keeps NLS = 16
   // load instructions in flight.
@@ -123,6 +143,7 @@ decode_mfma_kernel(DecodeArgs a) {
   __shared__ float s_ml[NWV][MG][2];
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
+  __shared__ __attribute__((aligned(16))) uint16_t s_krot[ROPE ? MD : 8];  // rotated new K row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uni(tid >> 6);
@@ -182,9 +203,25 @@ decode_mfma_kernel(DecodeArgs a) {
   {
     const int u = blockIdx.x < R ? blockIdx.x : 0;
     const int ub = u / a.Hkv;
-    app.load(a, ub, u % a.Hkv, appended_slot(a, ub), tid, blockIdx.x < R);
+    app.load(a, ub, u % a.Hkv, appended_slot(a, ub), tid, !ROPE && blockIdx.x < R);
   }
+  // ROPE: rows of a unit without work-groups (no valid keys), by work-group u, directly
+  // from global memory
+  auto rope_unit_direct = [&](int uu) {
+    const int bb = uu / a.Hkv, gg = uu % a.Hkv, half = a.rope_dim / 2;
+    const double2* tab = reinterpret_cast<const double2*>(a.rope_table) + (size_t)bb * half;
+    const size_t h0 = (size_t)bb * a.Hq + (size_t)gg * MG;
+    for (int e = tid; e < MG * MD; e += NWV * 64)
+      a.q_rot_out[(h0 + e / MD) * MD + e % MD] = rope_at(a.q + (h0 + e / MD) * MD, e % MD, half, tab);
+    const int slot = appended_slot(a, bb);
+    if (slot >= 0)
+      for (int d = tid; d < MD; d += NWV * 64)
+        a.k_dst[((size_t)uu * a.cap + slot) * MD + d] = rope_at(a.k_new + (size_t)uu * MD, d, half, tab);
+  };
   const int g_id = blockIdx.x;
+  if constexpr (ROPE) {
+    if (g_id < R && s_k[g_id + 1] == s_k[g_id]) rope_unit_direct(g_id);
+  }
   if (g_id >= s_k[R]) {
     app.store(a);
     return;
@@ -215,6 +252,18 @@ decode_mfma_kernel(DecodeArgs a) {
       uni(row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys).slot_lo);
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
   const int cap = a.cap;
+  // ROPE: the unit's new K row, unrotated, to LDS, and the (cos, sin) pairs this thread
+  // turns (pair i = tid % half of rows tid / half, tid / half + groups, ...)
+  const int rhalf = ROPE ? a.rope_dim / 2 : 0;
+  const int rgroups = rhalf > 0 ? (NWV * 64) / rhalf : 0;
+  double2 rcs = make_double2(1.0, 0.0);
+  if constexpr (ROPE) {
+    if (tid < MD / 8)
+      *reinterpret_cast<uint4*>(s_krot + 8 * tid) =
+          reinterpret_cast<const uint4*>(a.k_new + (size_t)u * MD)[tid];
+    if (tid < rgroups * rhalf)
+      rcs = reinterpret_cast<const double2*>(a.rope_table)[(size_t)b * rhalf + tid % rhalf];
+  }
 
   // the unit's 16 query rows to LDS in the key rows' layout (row = head, chunk c at
   // c ^ swz(row)): the Q^T operand is read from there like the K operand (lane: head l16,
@@ -232,6 +281,12 @@ decode_mfma_kernel(DecodeArgs a) {
   // segment's keys seg_lo + STEP (wave + NWV t) + 16 h + 0..15.  Keys past the segment's end
   // re-read its last key (a valid row, masked), so every load is unconditional.
   const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
+  // ROPE: the appended key's index in the unit's range (-1 when it has none)
+  int new_key = -1;
+  if (ROPE && new_slot >= 0) {
+    const int nk = new_slot - slot_lo < 0 ? new_slot - slot_lo + cap : new_slot - slot_lo;
+    if (nk < n_u) new_key = nk;
+  }
   const char* kmem = FP8 ? reinterpret_cast<const char*>(a.k8) : reinterpret_cast<const char*>(a.k);
   constexpr int CROWB = FP8 ? MD : MD * 2;  // bytes per cached row
   const char* kunit = kmem + (size_t)u * cap * CROWB;
@@ -474,12 +529,53 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < NLS; ++j) load_row(buf, j, key0(0));  // (a wave without steps: unused)
   __syncthreads();  // the query rows are in LDS
+  if constexpr (ROPE) {
+    // rotate in place: rows 0..15 the query rows (swizzled chunks), row 16 the K row
+    if (tid < rgroups * rhalf) {
+      const int i = tid % rhalf;
+      for (int r = tid / rhalf; r <= MG; r += rgroups) {
+        uint16_t* e0;
+        uint16_t* e1;
+        if (r < MG) {
+          char* row = s_q + r * ROWB;
+          e0 = reinterpret_cast<uint16_t*>(row + ((i / 8) ^ swz(r)) * 16) + i % 8;
+          e1 = reinterpret_cast<uint16_t*>(row + (((i + rhalf) / 8) ^ swz(r)) * 16) + (i + rhalf) % 8;
+        } else {
+          e0 = s_krot + i;
+          e1 = s_krot + i + rhalf;
+        }
+        const uint16_t x0 = *e0, x1 = *e1;
+        *e0 = rope_first(x0, x1, rcs.x, rcs.y);
+        *e1 = rope_second(x0, x1, rcs.x, rcs.y);
+      }
+    }
+    __syncthreads();
+    if (part == 0) {
+      // the unit's first work-group: rotated q out, rotated K row into its slot (no
+      // reader in this launch takes that slot from the cache)
+      for (int idx = tid; idx < MG * MD / 8; idx += NWV * 64) {
+        const int r = idx / (MD / 8), c = idx % (MD / 8);
+        reinterpret_cast<uint4*>(a.q_rot_out + (head0 + r) * MD)[c] =
+            *reinterpret_cast<const uint4*>(s_q + r * ROWB + (c ^ swz(r)) * 16);
+      }
+      if (new_slot >= 0 && tid < MD / 8)
+        reinterpret_cast<uint4*>(a.k_dst + ((size_t)u * cap + new_slot) * MD)[tid] =
+            *reinterpret_cast<const uint4*>(s_krot + 8 * tid);
+    }
+  }
   // one step: 0 to go on, 1 when it was the wave's last, 2 when the fast form stopped on it
   // (its tiles are in LDS)
   auto body = [&](auto safe_tag, int t) __attribute__((always_inline)) -> int {
     wave_lds_sync();  // the previous step's LDS reads stay before these writes
     const bool last = t + 1 >= my_steps;
     if (last) put(buf); else cycle(buf, t + 1);
+    if constexpr (ROPE) {
+      // the appended key's row came from k_new unrotated: the rotated one replaces it
+      const int j = new_key - key0(t);
+      if (new_key >= 0 && j >= 0 && j < TK && new_key < seg_hi)
+        *reinterpret_cast<uint4*>(my_tiles + j * ROWB + ((lane ^ swz(j)) * 16)) =
+            *reinterpret_cast<const uint4*>(s_krot + 8 * lane);
+    }
     wave_lds_sync();
     if (!compute(safe_tag, t)) return 2;
     return last ? 1 : 0;
@@ -687,15 +783,23 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
       a.k_new += unit0 * MD;
       a.k_dst += unit0 * a0.cap * MD;
     }
+    if (a.rope) {
+      a.q_rot_out += qo;
+      if (a.rope_table) a.rope_table += (size_t)b0 * a0.rope_dim;  // rope_dim / 2 pairs a row
+    }
     const long long R = (long long)a.B * a.Hkv;
     const long long grid = decode_mfma_grid((int)R, a.n_blocks, a.split_keys, a.max_keys);
     if (grid < R || grid > (1LL << 31) - 1) return hipErrorInvalidValue;
+    if (a.fp8 && a.rope) return hipErrorInvalidValue;  // (the plan never asks for it)
     if (a.fp8)
-      hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3((unsigned)grid), dim3(NWV * 64), 0,
-                         stream, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<true, false>), dim3((unsigned)grid),
+                         dim3(NWV * 64), 0, stream, a);
+    else if (a.rope)
+      hipLaunchKernelGGL((decode_mfma_kernel<false, true>), dim3((unsigned)grid),
+                         dim3(NWV * 64), 0, stream, a);
     else
-      hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3((unsigned)grid), dim3(NWV * 64), 0,
-                         stream, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<false, false>), dim3((unsigned)grid),
+                         dim3(NWV * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);

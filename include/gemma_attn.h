@@ -326,10 +326,13 @@ int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int
  * geometry): each work-group rotates
  * its unit's query rows and the new K row into LDS, the first split writes the rotated q
  * and appends the rotated row, and every reader of the appended slot takes the rotated row
- * from LDS; with q_out == q that needs a single split per row.  Otherwise (matrix-core
- * shapes, an in-place q_out with several splits) the RoPE + append kernel runs first, on
- * the table's angles, then the decode.  Errors: those of both calls (GA_ERR_OPTS for
- * rotary_dim), checked before anything is launched.
+ * from LDS; with q_out == q that needs a single split per row.  The matrix-core kernel
+ * of the K = V global geometry (partial rotary on its low dimensions, "Gemma4-26B-A4B on
+ * Apple Silicon ... (NO-GO)", Results, Break 4) does the same in its one launch when
+ * q_out is a separate buffer.  Otherwise (an in-place q_out with several splits, the
+ * multi-token matrix-core kernel) the RoPE + append kernel runs first, on the table's
+ * angles, then the decode.  Errors: those of both calls (GA_ERR_OPTS for rotary_dim),
+ * checked before anything is launched.
  */
 int32_t gemma_attn_decode_rope_append(const ga_shape* shape, const ga_bf16* q, ga_bf16* q_out,
                                       ga_bf16* k_cache, ga_bf16* v_cache, const ga_bf16* k_new,

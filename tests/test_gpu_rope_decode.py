@@ -4,8 +4,8 @@ gemma_attn_decode_rope_append promises the bits of gemma_rope_append then
 gemma_attn_decode_ex: the same rotated q, the same caches, the same output.  Where the
 vector kernel serves the call, the rotation runs inside the decode launch (every
 work-group rotates its unit's rows into LDS from the same per-element function); on
-matrix-core shapes, and for an in-place q_out with several splits, the two calls run in
-turn.  Each case below runs both routes on copies of the same inputs and compares bit for
+the global matrix-core kernel with a separate q_out too; for an in-place q_out with
+several splits, and on the multi-token matrix-core kernel, the two calls run in turn.  Each case below runs both routes on copies of the same inputs and compares bit for
 bit, and one case also checks the output against the oracle.
 """
 import numpy as np
@@ -36,14 +36,15 @@ def _clone(x):
 
 
 def _both_routes(q, k, v, kn, vn, ctx, window, softcap, scale, kind, base, R, in_place,
-                 split_keys=0, impl=api.IMPL_AUTO):
+                 split_keys=0, impl=api.IMPL_AUTO, q_pos=None):
     pos = ctx - 1
+    q_pos = pos if q_pos is None else q_pos
     # fused call
     kf, vf = k.clone(), _clone(v)
     qf = q.clone()
     qo = qf if in_place else torch.empty_like(q)
     table = api.rope_table(pos, base, R)
-    out_f = api.decode_rope_append(qf, qo, kf, vf, kn, vn, pos, ctx, pos, window, softcap,
+    out_f = api.decode_rope_append(qf, qo, kf, vf, kn, vn, pos, ctx, q_pos, window, softcap,
                                    scale, kind, table, R, split_keys=split_keys, impl=impl,
                                    deterministic=True)
     # the two calls
@@ -51,7 +52,7 @@ def _both_routes(q, k, v, kn, vn, ctx, window, softcap, scale, kind, base, R, in
     qr = q.clone()
     qo_r = qr if in_place else torch.empty_like(q)
     api.rope_append(qr, qo_r, kr, vr, kn, vn, pos, kind, base, R)
-    out_r = api.decode(qo_r, kr, vr, ctx, pos, window, softcap, scale, kind,
+    out_r = api.decode(qo_r, kr, vr, ctx, q_pos, window, softcap, scale, kind,
                        split_keys=split_keys, impl=impl, deterministic=True)
     torch.cuda.synchronize()
     assert torch.equal(qo.view(torch.int16), qo_r.view(torch.int16)), "rotated q"
@@ -94,6 +95,35 @@ def test_other_shapes_fused_equals_two_calls(D, Hq, Hkv, k_eq_v, R, kind, cap, w
     for in_place in (False, True):
         _both_routes(q, k, v, kn, vn, ctx_t, window, softcap, D ** -0.5, kind, base, R,
                      in_place, impl=impl)
+
+
+def test_global_fused_rows_without_keys_and_split_sizes():
+    """The global geometry on the matrix cores with the rotation fused: rows with no valid
+    key (an empty context, and q_pos = -1 with an append at position 4) have no work-group
+    of their own, so work-group u writes their rotated q and appended row; the others
+    several work-groups each.  Balanced over the chip and with split sizes 64 and 512."""
+    B, Hq, Hkv, D, cap = 6, 16, 1, 512, 2048
+    ctx = [0, 5, 1, 700, 2048, 1500]
+    q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, cap, api.LINEAR, True, ctx, 808)
+    q_pos = ctx_t - 1
+    q_pos[1] = -1
+    for split in (0, 64, 512):
+        log(f"global fused rope: split={split}")
+        _both_routes(q, k, v, kn, vn, ctx_t, 0, 0.0, D ** -0.5, api.LINEAR, 1e6, 128, False,
+                     split_keys=split, impl=api.IMPL_MFMA if split else api.IMPL_AUTO,
+                     q_pos=q_pos)
+
+
+def test_global_fused_more_units_than_one_launch():
+    """1100 rows of one KV head: two matrix-core launches (at most 1024 units each) over
+    one workspace, the rotation fused into both (the cos / sin table and q_out offset per
+    launch)."""
+    B, Hq, Hkv, D, cap = 1100, 16, 1, 512, 64
+    gen = synth.generator(909)
+    ctx = synth.uniform_int(gen, B, 1, cap).numpy().astype(np.int32).tolist()
+    q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, cap, api.LINEAR, True, ctx, 910)
+    log("global fused rope: B=1100")
+    _both_routes(q, k, v, kn, vn, ctx_t, 0, 0.0, D ** -0.5, api.LINEAR, 1e6, 128, False)
 
 
 def test_fused_sliding_layer_matches_oracle():
@@ -162,9 +192,8 @@ def test_rope_table_matches_definition(base, R):
 @pytest.mark.parametrize("layer", [0, 5])
 def test_rope_step_layer_full_size_sampled_rows(layer):
     """The 48-layer RoPE step's layers at full size, in the launch the bench times (one
-    call per layer on the step's cos / sin table): sliding layer 0 (one launch) and global
-    layer 5 (matrix cores: two launches), sampled rows against the oracle's rotate, append,
-    attend."""
+    call per layer on the step's cos / sin table): sliding layer 0 and global layer 5 (matrix
+    cores), each one launch, sampled rows against the oracle's rotate, append, attend."""
     from decode_attention_split_amd import workloads as wl
     from common import gen_layer
     import oracle
