@@ -485,9 +485,10 @@ int32_t decode_impl(const ga_shape* shape, const ga_bf16* q, ga_bf16* k_cache, g
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (f8 && k_new) {
-    // The quantizing append runs inside the vector kernel's single-token launch; on the
-    // matrix cores it is its own launch before the decode.
-    if (!p.rows16 && p.impl != GA_IMPL_MFMA && T == 1) {
+    // The quantizing append runs inside the single-token launch (vector kernel, or the
+    // matrix-core kernel of the global geometry); before the multi-token matrix-core
+    // decode it is its own launch.
+    if (!p.rows16 && T == 1) {
       a.k8_dst = const_cast<uint8_t*>(f8->k);
       a.ks_dst = const_cast<float*>(f8->ks);
       a.v8_dst = k_eq_v ? nullptr : const_cast<uint8_t*>(f8->v);

@@ -52,6 +52,7 @@
 #include "ga_device.h"
 #include "ga_internal.h"
 #include "ga_mfma.h"
+#include "ga_quant.h"
 #include "ga_rope.h"
 
 #include <type_traits>
@@ -120,6 +121,12 @@ __device__ __forceinline__ uint16_t rope_at(const uint16_t* row, int d, int half
                   : rope_second(row[i], row[i + half], cs.x, cs.y);
 }
 
+// FP8 with new_pos: the quantizing append fused in.  Wave 0 of every work-group quantizes
+// its unit's new row (the same row quantizer as the quantizing append kernel, so the same
+// codes and scale); the unit's first work-group stores them into the slot, and the wave
+// whose step holds the appended key puts the widened codes and the scale into its tile and
+// scale array in place of what it loaded from the slot.  A unit with no keys: work-group u
+// appends its row directly.
 // ROPE (bf16 caches): the rotary embedding at new_pos[b] fused in.  Every work-group
 // rotates its unit's 16 query rows and new K row in LDS (from the same (cos, sin) table
 // as the RoPE + append kernel); the unit's first work-group writes the rotated rows out
@@ -144,6 +151,8 @@ decode_mfma_kernel(DecodeArgs a) {
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
   __shared__ __attribute__((aligned(16))) uint16_t s_krot[ROPE ? MD : 8];  // rotated new K row
+  __shared__ __attribute__((aligned(16))) uint8_t s_kq[FP8 ? MD : 16];      // its e4m3 codes
+  __shared__ float s_kqs;                                                   // and scale
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uni(tid >> 6);
@@ -203,8 +212,22 @@ decode_mfma_kernel(DecodeArgs a) {
   {
     const int u = blockIdx.x < R ? blockIdx.x : 0;
     const int ub = u / a.Hkv;
-    app.load(a, ub, u % a.Hkv, appended_slot(a, ub), tid, !ROPE && blockIdx.x < R);
+    app.load(a, ub, u % a.Hkv, appended_slot(a, ub), tid, !ROPE && !FP8 && blockIdx.x < R);
   }
+  // FP8: the quantizing append of unit uu's new row w (lane: values 8 lane .. 8 lane + 7)
+  // by wave 0 (codes in LDS and, when store, in the cache); every lane of wave 0 calls it
+  auto new_row = [&](int uu) { return reinterpret_cast<const uint4*>(a.k_new + (size_t)uu * MD)[lane]; };
+  auto quant_append = [&](int uu, const uint4& w, bool store) {
+    const int slot = appended_slot(a, uu / a.Hkv);
+    float sc;
+    const uint2 c8 = quantize_row_e4m3(w, true, &sc);
+    reinterpret_cast<uint2*>(s_kq)[lane] = c8;
+    if (lane == 0) s_kqs = sc;
+    if (store && slot >= 0) {
+      reinterpret_cast<uint2*>(a.k8_dst + ((size_t)uu * a.cap + slot) * MD)[lane] = c8;
+      if (lane == 0) a.ks_dst[(size_t)uu * a.cap + slot] = sc;
+    }
+  };
   // ROPE: rows of a unit without work-groups (no valid keys), by work-group u, directly
   // from global memory
   auto rope_unit_direct = [&](int uu) {
@@ -221,6 +244,10 @@ decode_mfma_kernel(DecodeArgs a) {
   const int g_id = blockIdx.x;
   if constexpr (ROPE) {
     if (g_id < R && s_k[g_id + 1] == s_k[g_id]) rope_unit_direct(g_id);
+  }
+  if constexpr (FP8) {
+    if (a.new_pos && g_id < R && s_k[g_id + 1] == s_k[g_id] && wave == 0)
+      quant_append(g_id, new_row(g_id), true);
   }
   if (g_id >= s_k[R]) {
     app.store(a);
@@ -265,6 +292,11 @@ decode_mfma_kernel(DecodeArgs a) {
       rcs = reinterpret_cast<const double2*>(a.rope_table)[(size_t)b * rhalf + tid % rhalf];
   }
 
+  // FP8: the unit's new row requested ahead of the query rows (quantized once they are in)
+  uint4 kw = make_uint4(0, 0, 0, 0);
+  if constexpr (FP8) {
+    if (a.new_pos && wave == 0) kw = new_row(u);
+  }
   // the unit's 16 query rows to LDS in the key rows' layout (row = head, chunk c at
   // c ^ swz(row)): the Q^T operand is read from there like the K operand (lane: head l16,
   // d = 32 j + 8 lg + 0..7), which leaves the registers to the rows in flight
@@ -276,14 +308,19 @@ decode_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<uint4*>(s_q + r * ROWB + ((c ^ swz(r)) * 16)) = qp[idx];
     }
   }
+  if constexpr (FP8) {
+    // the unit's new row quantized (stored by the unit's first work-group); measured
+    // 1 us faster per launch here than after the first rows are requested
+    if (a.new_pos && wave == 0) quant_append(u, kw, part == 0);
+  }
 
   // ---- loads.  Tile h of step t (of this wave: the segment's step wave + NWV t) holds the
   // segment's keys seg_lo + STEP (wave + NWV t) + 16 h + 0..15.  Keys past the segment's end
   // re-read its last key (a valid row, masked), so every load is unconditional.
   const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
-  // ROPE: the appended key's index in the unit's range (-1 when it has none)
+  // ROPE / FP8: the appended key's index in the unit's range (-1 when it has none)
   int new_key = -1;
-  if (ROPE && new_slot >= 0) {
+  if ((ROPE || FP8) && new_slot >= 0) {
     const int nk = new_slot - slot_lo < 0 ? new_slot - slot_lo + cap : new_slot - slot_lo;
     if (nk < n_u) new_key = nk;
   }
@@ -528,7 +565,7 @@ decode_mfma_kernel(DecodeArgs a) {
   load_scale(buf, key0(0));
 #pragma unroll
   for (int j = 0; j < NLS; ++j) load_row(buf, j, key0(0));  // (a wave without steps: unused)
-  __syncthreads();  // the query rows are in LDS
+  __syncthreads();  // the query rows (and the quantized new row) are in LDS
   if constexpr (ROPE) {
     // rotate in place: rows 0..15 the query rows (swizzled chunks), row 16 the K row
     if (tid < rgroups * rhalf) {
@@ -575,6 +612,24 @@ decode_mfma_kernel(DecodeArgs a) {
       if (new_key >= 0 && j >= 0 && j < TK && new_key < seg_hi)
         *reinterpret_cast<uint4*>(my_tiles + j * ROWB + ((lane ^ swz(j)) * 16)) =
             *reinterpret_cast<const uint4*>(s_krot + 8 * lane);
+    }
+    if constexpr (FP8) {
+      // the appended key's slot may still hold the row it replaces (any bits, NaN codes
+      // included): its codes (widened) and scale from the quantized new row instead, also
+      // in the rows past the segment's end, which re-read the segment's last key (masked,
+      // but a NaN would survive the zero weight)
+      const int j = new_key - key0(t);
+      if (new_key >= 0 && j >= 0 && j < STEP && new_key < seg_hi) {
+        const uint2 c8 = reinterpret_cast<const uint2*>(s_kq)[lane];
+        const uint4 wide = e4m3x8_to_bf16x8(c8.x, c8.y);
+        const int j_end = new_key == seg_hi - 1 ? STEP : j + 1;
+        for (int jj = j; jj < j_end; ++jj) {
+          const int r = jj & 15;
+          *reinterpret_cast<uint4*>(my_tiles + (jj >> 4) * TILEB + r * ROWB +
+                                    ((lane ^ swz(r)) * 16)) = wide;
+          if (lane == 0) s_scl[wave][jj] = s_kqs;
+        }
+      }
     }
     wave_lds_sync();
     if (!compute(safe_tag, t)) return 2;
@@ -781,7 +836,11 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
     if (a.new_pos) {
       a.new_pos += b0;
       a.k_new += unit0 * MD;
-      a.k_dst += unit0 * a0.cap * MD;
+      if (a.k_dst) a.k_dst += unit0 * a0.cap * MD;
+      if (a.k8_dst) {
+        a.k8_dst += unit0 * a0.cap * MD;
+        a.ks_dst += unit0 * a0.cap;
+      }
     }
     if (a.rope) {
       a.q_rot_out += qo;

@@ -279,7 +279,10 @@ int32_t gemma_attn_decode_fp8(const ga_shape* shape, int32_t num_tokens, const g
  * serves the call (the sliding geometry), one launch does both: one wave of each
  * work-group quantizes the new rows with the append's own arithmetic, every reader of the
  * appended slot takes those codes and scales from registers, and the first split stores
- * them.  On the matrix cores (the K = V global geometry) the quantizing append runs first.
+ * them.  The matrix-core kernel of the K = V global geometry does the same in its one
+ * launch: every work-group quantizes its unit's new row, the unit's first work-group stores
+ * it, and the wave whose step holds the appended key puts the new codes (widened) and scale
+ * in place of what it loaded from the slot.
  * k_new, v_new [B, Hkv, D] device bf16 (v_new NULL exactly when v_codes is, K = V) and
  * pos [B] device int32, non-NULL; other arguments and errors as in the two calls;
  * workspace: ga_decode_fp8_workspace_bytes(shape, 1, window, opts).
