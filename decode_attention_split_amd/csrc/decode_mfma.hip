@@ -360,18 +360,15 @@ decode_mfma_kernel(DecodeArgs a) {
       // lane widens 16 codes (d = 16 m + 0..15, m = lane % 32) of step row 2 j + lane / 32
       // to the two chunks 2 m and 2 m + 1, storing first the one that keeps 8 / 16
       // consecutive lanes on distinct banks
+      // (the swap picks the source words before widening: four selects per row pair)
       const int m = lane & 31, fb = ((m >> 2) ^ (m >> 3)) & 1;
       const int rs = 2 * j + (lane >> 5), r = rs & 15, sw = swz(r);
-      const uint4 lo = e4m3x8_to_bf16x8(t.r[j].x, t.r[j].y);
-      const uint4 hi = e4m3x8_to_bf16x8(t.r[j].z, t.r[j].w);
+      const uint4 v = t.r[j];
+      const uint4 first = e4m3x8_to_bf16x8(fb ? v.z : v.x, fb ? v.w : v.y);
+      const uint4 second = e4m3x8_to_bf16x8(fb ? v.x : v.z, fb ? v.y : v.w);
       char* row = my_tiles + (rs >> 4) * TILEB + r * ROWB;
-      const uint32_t mk = 0u - (uint32_t)fb;  // all ones where the high chunk goes first
-      const uint4 d = make_uint4((lo.x ^ hi.x) & mk, (lo.y ^ hi.y) & mk, (lo.z ^ hi.z) & mk,
-                                 (lo.w ^ hi.w) & mk);
-      *reinterpret_cast<uint4*>(row + ((2 * m + fb) ^ sw) * 16) =
-          make_uint4(lo.x ^ d.x, lo.y ^ d.y, lo.z ^ d.z, lo.w ^ d.w);
-      *reinterpret_cast<uint4*>(row + ((2 * m + 1 - fb) ^ sw) * 16) =
-          make_uint4(hi.x ^ d.x, hi.y ^ d.y, hi.z ^ d.z, hi.w ^ d.w);
+      *reinterpret_cast<uint4*>(row + ((2 * m + fb) ^ sw) * 16) = first;
+      *reinterpret_cast<uint4*>(row + ((2 * m + 1 - fb) ^ sw) * 16) = second;
     } else {
       *reinterpret_cast<uint4*>(my_tiles + j * ROWB + ((lane ^ swz(j)) * 16)) = t.r[j];
     }
