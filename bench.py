@@ -388,6 +388,8 @@ def main():
                            sum(x["decode"] for x in per_layer), graph is not None)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     extras["pct_of_read_ceiling"] = round(100.0 * value / extras["read_ceiling_gbps"], 2)
+    kern_read_us = same_size_read_us(int(kern_bytes), stream)
+    log(f"a streaming read of the sliding kernel's bytes: {kern_read_us:.2f} us")
     if not rope and not args.step_only:
         extras["single_layer_workloads"] = gated_layers(args)
     result = {
@@ -430,6 +432,8 @@ def main():
                                     else "sliding_decode_hybrid48"),
             "bytes_per_launch": int(kern_bytes),
             "avg_launch_us": round(kern_ms * 1e3, 3),
+            "same_size_read_us": round(kern_read_us, 3),
+            "frac_of_same_size_read": round(kern_read_us / (kern_ms * 1e3), 4),
         },
     }
 
@@ -456,10 +460,15 @@ def gated_layers(args):
     for name, w in [("g4_12b_sliding", wl.G4_12B_SLIDING), ("g4_12b_global", wl.G4_12B_GLOBAL)]:
         r = time_single_layer(w, max(10, args.steps), max(3, args.warmup))
         gbps = r["bytes"] / (r["ms"] * 1e-3) / 1e9
-        log(f"{name}: {r['ms'] * 1e3:.2f} us per launch, {gbps:.1f} GB/s")
+        torch.cuda.empty_cache()
+        read_us = same_size_read_us(int(r["bytes"]), torch.cuda.current_stream())
+        log(f"{name}: {r['ms'] * 1e3:.2f} us per launch, {gbps:.1f} GB/s; a streaming read of "
+            f"the same bytes {read_us:.2f} us")
         res[name] = {"workload": w.name, "us_per_launch": round(r["ms"] * 1e3, 3),
                      "algorithmic_bytes": int(r["bytes"]), "gbps": round(gbps, 1),
-                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                     "same_size_read_us": round(read_us, 3),
+                     "frac_of_same_size_read": round(read_us / (r["ms"] * 1e3), 4)}
         torch.cuda.empty_cache()
     return res
 
@@ -541,6 +550,36 @@ def read_ceiling(stream, device, reps):
     ms = a.elapsed_time(b) / reps
     del bufs, sink
     return READ_BYTES / (ms * 1e-3) / 1e9
+
+
+def same_size_read_us(nbytes, stream, reps=20):
+    """gemma_stream_read over nbytes (rounded down to whole KiB), rotating over buffers of
+    that size that together pass 1 GiB, launched back to back like the decode: the
+    streaming-read time of a launch that moves the same bytes, ramp and drain included
+    (a launch's fixed cost weighs more the fewer bytes it moves)."""
+    import torch
+    from decode_attention_split_amd import api
+    nbytes = nbytes // 1024 * 1024
+    n = max(2, -(-(READ_BYTES + nbytes) // nbytes))
+    bufs = [torch.ones((nbytes // 4,), dtype=torch.float32, device="cuda") for _ in range(n)]
+    sink = api.stream_read(bufs[0])
+    for i in range(n):
+        api.stream_read(bufs[i], sink)
+    torch.cuda.synchronize()
+    reps = max(reps, 2 * n)
+    batches = []
+    for _ in range(5):  # the median of five batches of back-to-back launches
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            api.stream_read(bufs[i % n], sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        batches.append(a.elapsed_time(b) / reps * 1e3)
+    us = sorted(batches)[2]
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return us
 
 
 def time_single_layer(w, steps, warmup, keep=False):
