@@ -338,6 +338,21 @@ decode_mfma_kernel(DecodeArgs a) {
     uint4 r[NLS];
     float sc;
   };
+  // fp8: a step whose keys are all inside the segment and on consecutive slots (no ring
+  // wrap) -- every step but a few -- has its row pairs at kunit + (first + 2 j) * CROWB,
+  // i.e. base + 1024 j + 16 lane: one base per step instead of two slots per load
+  // (1.7 us faster per launch on the 12B fp8 global layer; the same on bf16 rows measured
+  // 10 us slower, the compiler then keeping the accumulator partly outside the AGPRs).
+  auto step_first = [&](int k0) { return uni(slot_of(k0)); };
+  auto step_contig = [&](int k0, int first) {
+    return FP8 && k0 + STEP <= seg_hi && first + STEP <= cap;
+  };
+  auto load_row_at = [&](Regs& t, int j, const char* base) __attribute__((always_inline)) {
+    t.r[j] = stream_load(reinterpret_cast<const uint4*>(base + 1024 * j) + lane);
+  };
+  auto load_scale_at = [&](Regs& t, int first) __attribute__((always_inline)) {
+    if constexpr (FP8) t.sc = sunit[first + (lane & 31)];
+  };
   auto load_row = [&](Regs& t, int j, int k0) __attribute__((always_inline)) {
     if constexpr (FP8) {
       // rows 2 j and 2 j + 1 of the step: lanes 0..31 the first, 32..63 the second
@@ -386,6 +401,20 @@ decode_mfma_kernel(DecodeArgs a) {
   auto cycle = [&](Regs& t, int t_next) __attribute__((always_inline)) {
     const int k0 = key0(t_next);
     put_scale(t);
+    if constexpr (FP8) {
+      const int first = step_first(k0);
+      if (step_contig(k0, first)) {
+        const char* base = kunit + (size_t)first * CROWB;
+        load_scale_at(t, first);
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+          put_row(t, j);
+          load_row_at(t, j, base);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
+    }
     load_scale(t, k0);
 #pragma unroll
     for (int j = 0; j < NLS; ++j) {
