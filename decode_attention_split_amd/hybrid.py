@@ -137,7 +137,8 @@ class HybridKVCache:
     def decode_rope_append(self, layer: int, q, q_out, k_new, v_new, pos, ctx_lens, q_pos,
                            table, out=None, deterministic=False, stream=None):
         """Rotary embedding, append and decode of a cache-owning layer in one call (one
-        launch where the vector kernel serves the layer); table from rope_tables(pos)."""
+        launch on the vector kernel, and on the global matrix-core kernel when q_out is a
+        buffer of its own); table from rope_tables(pos)."""
         g = self.layers[layer]
         if not self.owns_cache(layer):
             raise ValueError(f"layer {layer} shares layer {self.kv_source[layer]}'s cache and "
