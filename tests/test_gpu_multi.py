@@ -260,3 +260,37 @@ def test_chunked_prefill_global_kv_shared_geometry(T):
     for split in [0, 512]:
         out = inp.run(0, 0.0, scale, api.LINEAR, max_ctx=C, split_keys=split)
         assert_parity(out, ref, f"global T={T} split={split}")
+
+
+def _sampled_tokens_vs_oracle(inp, toks, window, softcap, scale, kind, out, what):
+    """Tokens `toks` of every row against the oracle's single-token definition at their
+    own positions (q_pos + t)."""
+    for t in toks:
+        ref, _, _, flags = oracle.decode_multi(
+            inp.q_bits[:, t:t + 1], inp.k_bits, inp.v_bits, inp.ctx, inp.q0 + t, window,
+            softcap, scale, kind)
+        assert not flags.any()
+        assert_parity(out[:, t:t + 1], ref, f"{what} token {t}")
+
+
+def test_chunked_prefill_at_the_token_limit():
+    """T = 4096 query tokens per row (the library's limit) on the 12B sliding geometry
+    (ring of w + T - 1 = 5119 slots, one row starting at position 0 and one wrapped past the
+    ring) and on the K = V global geometry (linear cache of 8192); every never-valid slot
+    NaN-poisoned, the whole output finite, sampled tokens against the oracle."""
+    T, w = 4096, 1024
+    toks = [0, 1, w - 1, w, 2047, 3000, T - 2, T - 1]
+    inp = MultiInputs(7100, 2, T, 16, 8, 256, w + T - 1, False, [T, 7000])
+    inp.poison(w, api.RING).to_device()
+    log("chunked prefill sliding T=4096")
+    out = inp.run(w, 50.0, 1.0 / 16, api.RING, max_ctx=7000)
+    assert torch.isfinite(out).all()
+    _sampled_tokens_vs_oracle(inp, toks, w, 50.0, 1.0 / 16, api.RING, out, "sliding T=4096")
+    del inp, out
+    inp = MultiInputs(7200, 1, T, 16, 1, 512, 8192, True, [6000])
+    inp.poison(0, api.LINEAR).to_device()
+    log("chunked prefill global T=4096")
+    scale = default_scale(512)
+    out = inp.run(0, 0.0, scale, api.LINEAR, max_ctx=8192)
+    assert torch.isfinite(out).all()
+    _sampled_tokens_vs_oracle(inp, toks, 0, 0.0, scale, api.LINEAR, out, "global T=4096")
