@@ -66,6 +66,21 @@ def test_global_layer_full_size_sampled_rows():
     assert_parity(out[rows], ref, f"{w.name} rows {rows}")
 
 
+def test_global_layer_at_128k_context():
+    """The K = V global geometry at a 128K-token linear cache (128 MiB of keys per row):
+    a full row and a ragged one, 16 query heads each, never-valid slots NaN-poisoned, the
+    whole output against the oracle; balanced over the chip and in splits of 4096 keys."""
+    g = wl.global_geom(16, 131072)
+    inp = layer_case(8128, 2, g, 1, 131072, ctx=[131072, 70001])
+    log("global layer, 128K context")
+    ref = oracle_out(inp, g.window, g.softcap, g.q_scale, g.kind)
+    for split in (0, 4096):
+        out = run(inp, g.window, g.softcap, g.q_scale, g.kind, split_keys=split,
+                  impl=api.IMPL_MFMA)
+        assert torch.isfinite(out).all(), "a never-valid slot was read"
+        assert_parity(out, ref, f"global 128K split={split}")
+
+
 @pytest.mark.parametrize("layer", [0, 5, 46, 47])
 def test_hybrid_step_layer_sampled_rows(layer):
     w = wl.HYBRID_48
