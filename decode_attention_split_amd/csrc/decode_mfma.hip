@@ -37,8 +37,9 @@
 //   the product leaves lane l with head l16 and keys 4 lg + 0..3, which is the B operand
 //     layout of the P.V product, so the softmax runs in place (max and sum over the four
 //     lane groups) and P goes to the matrix cores as bf16 hi + lo parts (~16 bits);
-//   O^T[512][16] += V^T[512][keys] . P^T[keys][16 heads]: per 16-wide d block and P part one
-//     v_mfma_f32_16x16x16_bf16 (one tile) or v_mfma_f32_16x16x32_bf16 (two tiles), the A
+//   O^T[512][16] += V^T[512][keys] . P^T[keys][16 heads] with v_mfma_f32_16x16x32_bf16:
+//     per 16-wide d block one (one tile: its keys in both halves of the k slots, against
+//     P's hi and lo parts) or two (two tiles: one per P part), the A
 //     operand from ds_read_b64_tr_b16 (lanes 4e..4e+3 of a 16-lane block read 16
 //     consecutive d of key e, lane i then holds the 4 keys at column d0 + i); the K = V
 //     row is read from HBM once and used for both products.
@@ -542,10 +543,13 @@ decode_mfma_kernel(DecodeArgs a) {
         ph[2 * h + k] = hv;
         pl[2 * h + k] = pack_bf16x2(p[h][2 * k] - bf16_lo(hv), p[h][2 * k + 1] - bf16_hi(hv));
       }
-    // O^T += V^T P^T per 16-wide d block: one tile -> v_mfma_f32_16x16x16_bf16 on the
-    // tile's transposed read; two tiles -> v_mfma_f32_16x16x32_bf16 on both (k slots
-    // 8 lg + 0..3 = tile 0's keys 4 lg + 0..3, 8 lg + 4..7 = tile 1's), each for P's hi
-    // and lo parts.  The V^T operands are read a group of VG blocks ahead.
+    // O^T += V^T P^T per 16-wide d block with v_mfma_f32_16x16x32_bf16: one tile -> the
+    // tile's transposed read in both halves of the k slots (8 lg + 0..3 and 8 lg + 4..7:
+    // keys 4 lg + 0..3), against P's hi part in the first half and its lo part in the
+    // second, so one product covers both parts (on gfx950 the 16x16x16 form costs as many
+    // cycles as this one); two tiles -> both tiles (k slots 8 lg + 0..3 = tile 0's keys
+    // 4 lg + 0..3, 8 lg + 4..7 = tile 1's), once for P's hi and once for its lo part.
+    // The V^T operands are read a group of VG blocks ahead.
     constexpr int VG = 4;
     uint4 vv[2][VG];
     auto read_v = [&](int grp, uint4(&y)[VG]) {
@@ -566,17 +570,15 @@ decode_mfma_kernel(DecodeArgs a) {
       if (grp + 1 < 32 / VG) read_v(grp + 1, vv[(grp + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int part2 = 0; part2 < 2; ++part2)
+      for (int part2 = 0; part2 < TPS; ++part2)
 #pragma unroll
         for (int k = 0; k < VG; ++k) {
           const int db = grp * VG + k;
-          const uint32_t* pp = part2 == 0 ? ph : pl;
           if constexpr (TPS == 2) {
+            const uint32_t* pp = part2 == 0 ? ph : pl;
             acc[db] = mfma_k32(vv[grp & 1][k], make_uint4(pp[0], pp[1], pp[2], pp[3]), acc[db]);
           } else {
-            const uint4 v = vv[grp & 1][k];
-            acc[db] = mfma_k16(__builtin_bit_cast(short4_t, make_uint2(v.x, v.y)),
-                               __builtin_bit_cast(short4_t, make_uint2(pp[0], pp[1])), acc[db]);
+            acc[db] = mfma_k32(vv[grp & 1][k], make_uint4(ph[0], ph[1], pl[0], pl[1]), acc[db]);
           }
         }
       __builtin_amdgcn_sched_barrier(0);

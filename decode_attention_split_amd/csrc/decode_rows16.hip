@@ -18,8 +18,9 @@
 //     of the P.V product, so the softmax works in place (row max / sum over the four lane
 //     groups) and P goes to the matrix cores as bf16 hi + lo parts (~16 mantissa bits);
 //   the V tile comes back transposed with ds_read_b64_tr_b16 as the A operand of
-//     O^T[D][16] += V^T[D][16 keys] . P^T[16 keys][16 rows]: D / 16 pairs of
-//     v_mfma_f32_16x16x16_bf16 (with K = V one tile serves both products).
+//     O^T[D][16] += V^T[D][16 keys] . P^T[16 keys][16 rows]: D / 16
+//     v_mfma_f32_16x16x32_bf16, each with the tile's keys in both halves of the k slots
+//     against P's hi and lo parts (with K = V one tile serves both products).
 // One register buffer each for K and V, refilled as soon as the tile's rows are in LDS
 // (eight waves per CU hide the latency).  Loading each key's row in 16-byte pieces straight
 // into the K operand (lane l16 = key) reads half lines per instruction and streamed at
@@ -263,8 +264,10 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(rd + db * 32));
-      acc[db] = mfma_k16(va, ph, acc[db]);
-      acc[db] = mfma_k16(va, pl, acc[db]);
+      // both halves of the k slots hold the tile's keys: P's hi part against the first,
+      // its lo part against the second (one 16x16x32 product; the 16x16x16 form costs as
+      // many cycles on gfx950)
+      acc[db] = mfma_k32(cat4(va, va), cat4(ph, pl), acc[db]);
     }
     wave_lds_sync();  // the tile's transposed reads stay before the next tile's writes
   };
