@@ -134,7 +134,9 @@ __device__ __forceinline__ uint16_t rope_at(const uint16_t* row, int d, int half
 // (q_rot_out, and the K row into its cache slot), and the work-group holding the appended
 // key puts the rotated row into its tile in place of the one it loaded from k_new.  A
 // unit with no keys has no work-group of its own: work-group u writes its rows.
-template <bool FP8, bool ROPE>
+// CAP: the soft-cap is on (a separate instantiation: a condition inside the step is
+// turned into selects, which evaluates the cap's exp and reciprocal when it is off).
+template <bool FP8, bool ROPE, bool CAP>
 __global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_mfma_kernel(DecodeArgs a) {
   static_assert(!(FP8 && ROPE), "RoPE is fused on bf16 caches only");
@@ -504,7 +506,7 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) {
         float v = sv[e] * a.scale;
         if constexpr (FP8) v *= ks[h][e];
-        if (a.softcap > 0.0f) v = softcap_tanh(v, a.softcap, a.inv_softcap);
+        if constexpr (CAP) v = softcap_tanh(v, a.softcap, a.inv_softcap);
         x[h][e] = (k0 + TK * h + 4 * lg + e < seg_hi) ? v * kLog2e : -INFINITY;
         mx = fmaxf(mx, x[h][e]);
       }
@@ -878,15 +880,18 @@ hipError_t decode_mfma_launch(const DecodeArgs& a0, hipStream_t stream) {
     const long long grid = decode_mfma_grid((int)R, a.n_blocks, a.split_keys, a.max_keys);
     if (grid < R || grid > (1LL << 31) - 1) return hipErrorInvalidValue;
     if (a.fp8 && a.rope) return hipErrorInvalidValue;  // (the plan never asks for it)
-    if (a.fp8)
-      hipLaunchKernelGGL((decode_mfma_kernel<true, false>), dim3((unsigned)grid),
-                         dim3(NWV * 64), 0, stream, a);
-    else if (a.rope)
-      hipLaunchKernelGGL((decode_mfma_kernel<false, true>), dim3((unsigned)grid),
-                         dim3(NWV * 64), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<false, false>), dim3((unsigned)grid),
-                         dim3(NWV * 64), 0, stream, a);
+    const dim3 g3((unsigned)grid), b3(NWV * 64);
+    const bool cap = a.softcap > 0.0f;
+    if (a.fp8) {
+      if (cap) hipLaunchKernelGGL((decode_mfma_kernel<true, false, true>), g3, b3, 0, stream, a);
+      else hipLaunchKernelGGL((decode_mfma_kernel<true, false, false>), g3, b3, 0, stream, a);
+    } else if (a.rope) {
+      if (cap) hipLaunchKernelGGL((decode_mfma_kernel<false, true, true>), g3, b3, 0, stream, a);
+      else hipLaunchKernelGGL((decode_mfma_kernel<false, true, false>), g3, b3, 0, stream, a);
+    } else {
+      if (cap) hipLaunchKernelGGL((decode_mfma_kernel<false, false, true>), g3, b3, 0, stream, a);
+      else hipLaunchKernelGGL((decode_mfma_kernel<false, false, false>), g3, b3, 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_units_kernel, dim3((unsigned)(R * MG)), dim3(256), 0, stream, a);

@@ -81,6 +81,7 @@ def test_sliding_layer_fused_equals_two_calls(in_place, split_keys):
     (128, 8, 2, False, 64, api.LINEAR, 300, 0, 50.0, api.IMPL_AUTO),   # partial, 4 per KV
     (256, 4, 4, True, 256, api.RING, 32, 32, 0.0, api.IMPL_AUTO),      # K = V, vector kernel
     (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 0.0, api.IMPL_AUTO),  # global: matrix cores
+    (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 30.0, api.IMPL_AUTO),  # the same, soft-capped
     (512, 16, 1, True, 128, api.LINEAR, 2048, 0, 0.0, api.IMPL_VALU),  # global: vector kernel
     (512, 2, 2, False, 512, api.RING, 64, 64, 30.0, api.IMPL_AUTO),    # one head per KV head
     (256, 16, 8, False, 0, api.RING, 128, 128, 0.0, api.IMPL_AUTO),    # no rotary part
