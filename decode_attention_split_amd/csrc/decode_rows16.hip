@@ -241,12 +241,17 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
       mx = fmaxf(mx, x[i]);
     }
     mx = rows_max(mx);  // over the 16 keys of the tile (four lane groups)
-    if (mx > m + kRescaleLog2R16) {
-      const float f = exp2_fast(m - mx);  // 0 while m = -inf
+    // rescale when some row's maximum grew past its reference: a branch on the whole
+    // wave (rows that did not grow multiply by exactly 1), so the tiles that need none
+    // leave the accumulators alone (a per-row condition is turned into selects, which
+    // multiply and write back every accumulator register on every tile)
+    const bool grow = mx > m + kRescaleLog2R16;
+    if (__ballot(grow) != 0) {
+      const float f = grow ? exp2_fast(m - mx) : 1.0f;  // 0 while m = -inf
       l *= f;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) acc[i] *= f;
-      m = mx;
+      m = grow ? mx : m;
     }
     float p[4];
 #pragma unroll
