@@ -80,9 +80,12 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
 // The same merge with one wave per row (four rows per work-group), for rows with few
 // splits.  Lane s < ns reads split s's (m_s, l_s) and forms its weight 2^(m_s - M); the
 // wave reduces M and L across lanes, and each accumulation step reads the weights back
-// from their lanes.  Lane i owns the float4 chunks i, i + 64, ... of the row, and four
-// splits' chunks are loaded before any is used, so their latencies overlap.
+// from their lanes.  Lane i owns the float4 chunks i, i + 64, ... of the row; eight
+// splits' chunks are loaded before any is used, and the first eight of the lane's first
+// chunk are requested together with (m_s, l_s), so a row of up to eight splits costs one
+// round of loads.
 constexpr int kMergeWaveMaxSplits = 64;
+constexpr int kMergeWaveBatch = 8;
 
 __global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
@@ -95,6 +98,16 @@ __global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
   const RowRange r = unit_range(a, b, t / a.Tc);
   const int ns = (r.n + a.split_keys - 1) / a.split_keys;  // <= S <= 64
   const float* ml = a.part_ml + bh * S * 2;
+  const float4* acc = reinterpret_cast<const float4*>(a.part_acc + bh * S * a.D);
+  // the first batch of the lane's first chunk (a split past the row's last is split
+  // ns - 1, or 0: in the workspace, never used)
+  constexpr int NB = kMergeWaveBatch;
+  const int s_last = ns > 0 ? ns - 1 : 0;
+  float4 first[NB];
+  if (lane < D4) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) first[j] = acc[(size_t)min(j, s_last) * D4 + lane];
+  }
   float m_s = -INFINITY, l_s = 0.0f;
   if (lane < ns) {
     m_s = ml[2 * lane];
@@ -108,7 +121,6 @@ __global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
   float Lsum = l_s * w_s;
   for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off, 64);
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  const float4* acc = reinterpret_cast<const float4*>(a.part_acc + bh * S * a.D);
   float4* out = reinterpret_cast<float4*>(a.out + bh * a.D);
   auto weight = [&](int s) {  // s is the same on every lane
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_s),
@@ -116,12 +128,17 @@ __global__ void __launch_bounds__(256) merge_wave_kernel(DecodeArgs a) {
   };
   for (int d = lane; d < D4; d += 64) {
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int s0 = 0; s0 < ns; s0 += 4) {
-      float4 v[4];
+    for (int s0 = 0; s0 < ns; s0 += NB) {
+      float4 v[NB];
+      if (d == lane && s0 == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = acc[(size_t)min(s0 + j, ns - 1) * D4 + d];
+        for (int j = 0; j < NB; ++j) v[j] = first[j];
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NB; ++j) v[j] = acc[(size_t)min(s0 + j, s_last) * D4 + d];
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
         if (s0 + j < ns) {
           const float w = weight(s0 + j);
           o.x = fmaf(w, v[j].x, o.x);
