@@ -48,7 +48,7 @@ def _counter_csv(path, counter, rows):
 
 
 def test_counter_summary_keeps_the_timed_launches_and_scales_by_the_copy(tmp_path, capsys):
-    kern = "void ga::(anonymous namespace)::decode_mfma_kernel<false, false>(ga::DecodeArgs)"
+    kern = "void ga::(anonymous namespace)::decode_mfma_kernel<false, false, false>(ga::DecodeArgs)"
     copy = "__amd_rocclr_copyBuffer"
     gib_kib = (1 << 30) / 1024.0
     # the copy's FETCH_SIZE reads half its bytes (calibration 2), WRITE_SIZE all of them;
@@ -60,7 +60,7 @@ def test_counter_summary_keeps_the_timed_launches_and_scales_by_the_copy(tmp_pat
     f, w = tmp_path / "f.csv", tmp_path / "w.csv"
     _counter_csv(f, "FETCH_SIZE", fetch)
     _counter_csv(w, "WRITE_SIZE", write)
-    bench.summarize_counters(str(f), str(w), "cmd", "decode_mfma_kernel<false, false>")
+    bench.summarize_counters(str(f), str(w), "cmd", "decode_mfma_kernel<false, false, false>")
     out = dict(line.split(": ", 1) for line in capsys.readouterr().out.splitlines()
                if ": " in line and not line.startswith("#"))
     assert out["grid_size"].startswith("65536")
