@@ -190,6 +190,21 @@ def test_empty_rows_give_zero():
         out = run(inp, 0, 0.0, default_scale(512), api.LINEAR, split_keys=split)
         assert (out[0] == 0).all() and (out[2] == 0).all()
         assert torch.isfinite(out[1]).all() and out[1].abs().sum() > 0
+    # the vector kernel's splits and the few-split merge (an empty row has no split to read;
+    # the workspace is NaN-filled so any use of an unwritten partial would show)
+    inp = gen_layer(78, 3, 4, 1, 256, 512, False, 1, 1, ctx=[0, 300, 0]).to_device()
+    shape = api.shape_of(inp.q, inp.k, api.LINEAR, 512)
+    for split in [64, 128]:
+        nbytes = api.workspace_bytes(shape, 0, split_keys=split, impl=api.IMPL_VALU)
+        assert nbytes > 0 and nbytes % 4 == 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ws.view(torch.float32).fill_(float("nan"))
+        out = run(inp, 0, 0.0, default_scale(256), api.LINEAR, split_keys=split, max_ctx=512,
+                  workspace=ws, impl=api.IMPL_VALU)
+        assert (out[0] == 0).all() and (out[2] == 0).all(), split
+        assert torch.isfinite(out[1]).all() and out[1].abs().sum() > 0, split
+        ref = oracle_out(inp, 0, 0.0, default_scale(256), api.LINEAR)
+        assert_parity(out, ref, f"empty rows, split {split}")
 
 
 # ------------------------------------------------------------------ invariants
