@@ -4,7 +4,6 @@
 //   v_mfma_f32_16x16x32_bf16  A[m][k]: lane holds m = l16, k = 8 lg + 0..7;
 //                             B[k][n]: lane holds n = l16, k = 8 lg + 0..7;
 //                             C[m][n]: lane holds n = l16, m = 4 lg + 0..3.
-//   v_mfma_f32_16x16x16_bf16  A: m = l16, k = 4 lg + 0..3; B: n = l16, k = 4 lg + 0..3.
 //   ds_read_b64_tr_b16        within a 16-lane block, lane i receives element i of each of
 //                             the four 8-byte rows read by lanes 4e..4e+3 (a 4x16 -> 16x4
 //                             transpose of bf16 values).
@@ -67,10 +66,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ floatx4_t mfma_k16(short4_t a, short4_t b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 }  // namespace ga
