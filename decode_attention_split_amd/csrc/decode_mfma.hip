@@ -147,9 +147,12 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int STEP = TPS * TK;
   constexpr int NLS = 16;
   constexpr int WG_KEYS = NWV * STEP;
-  __shared__ __attribute__((aligned(16))) char s_kv[NWV * WAVE_LDS];
+  // the unit's 16 query rows first, then the waves' tiles: the query rows then sit low
+  // enough in LDS for every read of them to take its offset in the instruction
+  __shared__ __attribute__((aligned(16))) char s_qkv[MG * ROWB + NWV * WAVE_LDS];
+  char* const s_q = s_qkv;                // the unit's 16 query rows
+  char* const s_kv = s_qkv + MG * ROWB;   // the waves' tiles
   __shared__ __attribute__((aligned(16))) float s_scl[NWV][32];  // fp8: the step's row scales
-  __shared__ __attribute__((aligned(16))) char s_q[MG * ROWB];  // the unit's 16 query rows
   __shared__ float s_ml[NWV][MG][2];
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
