@@ -502,18 +502,31 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
     float x[TPS][4], mx = -INFINITY;
+    // without the cap the logit in log2 units is s * (scale log2 e) (* the row scale)
+    const float s2 = CAP ? a.scale : a.scale * kLog2e;
 #pragma unroll
     for (int h = 0; h < TPS; ++h) {
       const floatx4_t sv = sc2[h][0] + sc2[h][1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v = sv[e] * a.scale;
+        float v = sv[e] * s2;
         if constexpr (FP8) v *= ks[h][e];
-        if constexpr (CAP) v = softcap_tanh(v, a.softcap, a.inv_softcap);
-        x[h][e] = (k0 + TK * h + 4 * lg + e < seg_hi) ? v * kLog2e : -INFINITY;
-        mx = fmaxf(mx, x[h][e]);
+        if constexpr (CAP) v = softcap_tanh(v, a.softcap, a.inv_softcap) * kLog2e;
+        x[h][e] = v;
       }
     }
+    if (k0 + STEP > seg_hi) {  // the segment's last step: keys past its end weigh 0
+      asm volatile("");  // (a branch, not selects evaluated on every step)
+#pragma unroll
+      for (int h = 0; h < TPS; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k0 + TK * h + 4 * lg + e >= seg_hi) x[h][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int h = 0; h < TPS; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[h][e]);
     mx = rows_max(mx);  // over the step's keys (four lane groups)
     if constexpr (SAFE) {
       if (mx > m + kRescaleLog2) {
