@@ -25,6 +25,11 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source flags.  The multi-token kernel keeps its matrix-core accumulators in ordinary
+# VGPRs (it has the room at its occupancy), so the rescale of the accumulators takes no
+# copies between AGPRs and VGPRs; the global kernel needs the AGPRs for its 128-register
+# accumulator.
+SOURCE_FLAGS = {"decode_rows16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():
@@ -41,8 +46,8 @@ def build(verbose: bool = False, extra_flags=None, out=None, jobs: int = 0) -> s
             while pending and len(procs) < jobs:
                 src = pending.pop(0)
                 obj = os.path.join(tmp, os.path.basename(src) + ".o")
-                cmd = ([HIPCC] + HIPCC_FLAGS + list(extra_flags or []) +
-                       ["-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
+                cmd = ([HIPCC] + HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
+                       list(extra_flags or []) + ["-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
                 if verbose:
                     print(" ".join(cmd), flush=True)
                 procs.append((subprocess.Popen(cmd), cmd))
