@@ -52,18 +52,22 @@
  * Rotary position embedding (oracle_rope_row): sliding layers use base 10,000 over the
  * whole head, full layers base 1,000,000 applied as a partial rotary to the low part of
  * the head dimension with no positional encoding on the rest ("Gemma support" pull
- * request, Summary: own RoPE base for sliding layers, proportional RoPE; "Gemma4-26B-A4B
- * on Apple Silicon", Results (Break 4): dual bases, partial rotary on full layers, and
- * Ablations / negative controls: the rotary acts on the low portion of the head dimension;
- * the model-loader page's header: bases 10,000 and 1,000,000).  Readings: the first R
- * (even) elements rotate in rotate-half pairs (i, i + R/2), angle p * base^(-2i/R) for
- * i < R/2; the rest pass through; computed in double and rounded once to bf16 (round to
- * nearest even).
- * PARITY UNPINNED for the full-layer case: the exponent over the rotated width R (not
- * over D), the width R itself (the callers pass R = D/4 on full layers) and the use of
- * the rotated key row as the value row on K = V layers are readings that nothing on the
- * pages fixes, so no test can tell them from another plausible reading.  The rotate-half
- * pairing, the per-pair angle, the rotation itself and the single rounding are pinned.
+ * request, Summary: own RoPE base for sliding layers, proportional RoPE; "Gemma 4 12B
+ * (unified multimodal)" record, CONTEXT_SCALING_METHOD: rope_type "default" on sliding
+ * layers and "proportional" on full layers; "Gemma4-26B-A4B on Apple Silicon", Results
+ * (Break 4) and the falsification paragraph: partial rotary on the low portion of the
+ * head dimension, nothing on the remainder; the model-loader page's header: bases 10,000
+ * and 1,000,000).  With H = D/2 and R (even, <= D) the rotated width: element i and
+ * element i + H form rotate-half pair i, which turns by the angle p * base^(-2i/D) for
+ * i < R/2; every other element passes through (R = D: the default type, the whole head;
+ * R < D: the proportional type, whose frequencies keep the exponent over the whole head
+ * and whose rotated pairs are the lowest R/2 of each half).  Computed in double and
+ * rounded once to bf16 (round to nearest even).  Pinned against the transformers
+ * library's Gemma 4 model code (its rotary embedding for the "default" and "proportional"
+ * rope types and its rotate-half application), for both layer types.
+ * PARITY UNPINNED: the use of the rotated key row as the value row on K = V layers (one
+ * stored row per position is what K = V means here; the pages do not say what the value
+ * row is).
  *
  * Arithmetic: every bf16 input is widened exactly (bits << 16 -> float -> double);
  * scale and softcap are widened from their float32 values; libm exp, tanh, log in
@@ -203,15 +207,15 @@ uint16_t oracle_f64_to_bf16(double x) {
  * rounded result, out_f64 [D] (may be NULL) the unrounded one. */
 void oracle_rope_row(int D, const uint16_t* x, long p, double base, int R, uint16_t* out_bf16,
                      double* out_f64) {
+  const int H = D / 2;
   for (int d = 0; d < D; ++d) {
     double y = oracle_bf16_to_f64(x[d]);
-    if (d < R) {
-      const int half = R / 2;
-      const int i = d < half ? d : d - half;
-      const double ang = (double)p * pow(base, -2.0 * i / R);
+    const int i = d < H ? d : d - H;  /* the pair of element d */
+    if (2 * i < R) {
+      const double ang = (double)p * pow(base, -2.0 * i / D);
       const double c = cos(ang), s = sin(ang);
-      const double a = oracle_bf16_to_f64(x[i]), b = oracle_bf16_to_f64(x[i + half]);
-      y = d < half ? a * c - b * s : b * c + a * s;
+      const double a = oracle_bf16_to_f64(x[i]), b = oracle_bf16_to_f64(x[i + H]);
+      y = d < H ? a * c - b * s : b * c + a * s;
     }
     if (out_f64) out_f64[d] = y;
     out_bf16[d] = oracle_f64_to_bf16(y);
