@@ -369,7 +369,8 @@ def main():
             if rope:
                 g = w.layers[li]
                 cache.decode_rope_append(li, qs[li], q_rot[li], k_new[li], v_new[li], pos_t,
-                                         ctx_t, qpos_t, tables[(g.rope_base, g.rotary_dim)],
+                                         ctx_t, qpos_t,
+                                         tables[(g.rope_base, g.rotary_dim, g.head_dim)],
                                          out=outs[li])
             else:
                 cache.decode_append(li, qs[li], k_new[li], v_new[li], pos_t, ctx_t, qpos_t,

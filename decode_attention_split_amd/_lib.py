@@ -84,7 +84,7 @@ def load():
     lib.gemma_attn_decode_rope_append.argtypes = [SP, P, P, P, P, P, P, P, P, P, i32, f32, f32,
                                                   P, i32, P, P, sz, OP, P]
     lib.gemma_attn_decode_rope_append.restype = i32
-    lib.gemma_rope_table.argtypes = [i32, P, f32, i32, P, P]
+    lib.gemma_rope_table.argtypes = [i32, P, f32, i32, i32, P, P]
     lib.gemma_rope_table.restype = i32
     lib.gemma_attn_decode_append_fp8.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, i32, f32, f32,
                                                  P, P, sz, OP, P]

@@ -215,9 +215,9 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, pos, ctx_lens, q_pos, windo
     return out
 
 
-def rope_table(pos, rope_base: float, rotary_dim: int, out=None, stream=None):
-    """cos / sin of every rotate-half pair at pos[b]: float64 [B, rotary_dim / 2, 2] (see
-    gemma_rope_table)."""
+def rope_table(pos, rope_base: float, rotary_dim: int, head_dim: int, out=None, stream=None):
+    """cos / sin of every turning rotate-half pair of a head_dim head at pos[b]: float64
+    [B, rotary_dim / 2, 2] (see gemma_rope_table)."""
     _need(pos, "pos", torch.int32, 1)
     B = pos.numel()
     if out is None:
@@ -227,7 +227,7 @@ def rope_table(pos, rope_base: float, rotary_dim: int, out=None, stream=None):
             tuple(out.shape) != (B, rotary_dim // 2, 2):
         raise ValueError("out must be a contiguous float64 [B, rotary_dim / 2, 2] tensor")
     rc = _lib.load().gemma_rope_table(int(B), _ptr(pos), float(rope_base), int(rotary_dim),
-                                      _ptr(out), _stream_handle(stream))
+                                      int(head_dim), _ptr(out), _stream_handle(stream))
     _check(rc, "gemma_rope_table")
     return out
 
@@ -238,11 +238,11 @@ def decode_rope_append(q, q_out, k_cache, v_cache, k_new, v_new, pos, ctx_lens, 
                        split_keys: int = 0, impl: int = IMPL_AUTO, deterministic: bool = False,
                        stream=None):
     """rope_append(q, q_out, ...) of one token then decode(q_out, ...), one launch where the
-    vector kernel serves the shape; table = rope_table(pos, base, rotary_dim) (see
+    vector kernel serves the shape; table = rope_table(pos, base, rotary_dim, D) (see
     gemma_attn_decode_rope_append)."""
     if table is not None and (table.dtype != torch.float64 or not table.is_contiguous() or
                               tuple(table.shape) != (pos.numel(), rotary_dim // 2, 2)):
-        raise ValueError("table must be rope_table(pos, base, rotary_dim)")
+        raise ValueError("table must be rope_table(pos, base, rotary_dim, head_dim)")
     shape, out, opts, workspace = _decode_common(q, k_cache, v_cache, ctx_lens, q_pos, window,
                                                  kind, out, workspace, max_ctx, split_keys, impl,
                                                  deterministic)

@@ -30,7 +30,6 @@ constexpr int kMaxSplitKeys = 65536;
 #endif
 constexpr int kMultiMaxRows = GA_MULTI_MAX_ROWS;  // multi-token: query rows per unit
 constexpr int kMaxTokens = 4096;  // multi-token: query tokens per row
-constexpr int kMaxRotaryDim = 512;  // the largest head_dim
 
 int32_t check_arch() {
   int dev = -1;
@@ -753,17 +752,18 @@ int32_t gemma_rope_append(const ga_shape* shape, int32_t num_tokens, const ga_bf
 }
 
 int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int32_t rotary_dim,
-                         double* table, void* stream) {
+                         int32_t head_dim, double* table, void* stream) {
   if (batch < 0 || rotary_dim < 0 || rotary_dim % 2 != 0) return GA_ERR_DIMS;
-  if (rotary_dim > kMaxRotaryDim) return GA_ERR_TOO_LARGE;
+  if (!head_dim_ok(head_dim)) return GA_ERR_HEAD_DIM;
+  if (rotary_dim > head_dim) return GA_ERR_DIMS;
   if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return GA_ERR_OPTS;
   if (batch == 0 || rotary_dim == 0) return GA_OK;
   if (!pos || !table) return GA_ERR_NULL;
   if (!aligned16(table)) return GA_ERR_NULL;
   int32_t st = check_arch();
   if (st != GA_OK) return st;
-  hipError_t e = ga::rope_table_launch(batch, rotary_dim, (double)rope_base, pos, table,
-                                       static_cast<hipStream_t>(stream));
+  hipError_t e = ga::rope_table_launch(batch, rotary_dim, head_dim, (double)rope_base, pos,
+                                       table, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GA_OK : GA_ERR_LAUNCH;
 }
 

@@ -110,16 +110,17 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Rotary embedding of element d (of 2 half rotated ones) of a row at the angles of tab
-// (the (cos, sin) pairs of one position); elements d >= 2 half pass through.  The same
-// per-pair arithmetic as the RoPE + append kernel, so both give the same bits.
-__device__ __forceinline__ uint16_t rope_at(const uint16_t* row, int d, int half,
+// Rotary embedding of element d of a row at the angles of tab (the (cos, sin) pairs of one
+// position): rotate-half pairs (i, i + MD/2) with i < nrot turn, the rest pass through.
+// The same per-pair arithmetic as the RoPE + append kernel, so both give the same bits.
+__device__ __forceinline__ uint16_t rope_at(const uint16_t* row, int d, int nrot,
                                             const double2* tab) {
-  if (d >= 2 * half) return row[d];
-  const int i = d < half ? d : d - half;
+  constexpr int H = MD / 2;
+  const int i = d < H ? d : d - H;
+  if (i >= nrot) return row[d];
   const double2 cs = tab[i];
-  return d < half ? rope_first(row[i], row[i + half], cs.x, cs.y)
-                  : rope_second(row[i], row[i + half], cs.x, cs.y);
+  return d < H ? rope_first(row[i], row[i + H], cs.x, cs.y)
+               : rope_second(row[i], row[i + H], cs.x, cs.y);
 }
 
 // FP8 with new_pos: the quantizing append fused in.  Wave 0 of every work-group quantizes
@@ -622,10 +623,10 @@ decode_mfma_kernel(DecodeArgs a) {
         if (r < MG) {
           char* row = s_q + r * ROWB;
           e0 = reinterpret_cast<uint16_t*>(row + ((i / 8) ^ swz(r)) * 16) + i % 8;
-          e1 = reinterpret_cast<uint16_t*>(row + (((i + rhalf) / 8) ^ swz(r)) * 16) + (i + rhalf) % 8;
+          e1 = reinterpret_cast<uint16_t*>(row + (((i + MD / 2) / 8) ^ swz(r)) * 16) + (i + MD / 2) % 8;
         } else {
           e0 = s_krot + i;
-          e1 = s_krot + i + rhalf;
+          e1 = s_krot + i + MD / 2;
         }
         const uint16_t x0 = *e0, x1 = *e1;
         *e0 = rope_first(x0, x1, rcs.x, rcs.y);

@@ -154,7 +154,8 @@ __global__ void __launch_bounds__(NW_ * 64)
     qr[hh][EPC * c / 2 + 4 * h8 + 3] = v.w;
   };
   // ROPE: the unit's G query rows and its new K row, unrotated, in 16-byte chunks (RPT
-  // per thread), and the (cos, sin) of the rotate-half pairs this thread turns (NPR), all
+  // per thread), and the (cos, sin) of the rotate-half pairs (i, i + D/2) this thread turns
+  // (NPR, i < rope_dim / 2), all
   // requested here, ahead of the first K rows; the rotation follows once those are out.
   constexpr int RCH = ROPE ? (G + 1) * D / 8 : 1;
   constexpr int RPT = (RCH + NW * 64 - 1) / (NW * 64);
@@ -239,8 +240,8 @@ __global__ void __launch_bounds__(NW_ * 64)
     load_rows(ka, va, ca, min(i_first, min(a.cap, k_begin + a.split_keys) - 1), false);
 
   if constexpr (ROPE) {
-    // Rotate at the appended position: each thread takes rotate-half pairs i and turns
-    // them in place in all G + 1 rows in LDS.  Every work-group of the unit does this; the
+    // Rotate at the appended position: each thread takes rotate-half pairs (i, i + D/2)
+    // and turns them in place in all G + 1 rows in LDS.  Every work-group of the unit does this; the
     // first split also writes the rotated q out and appends the rotated K row.
     const int half = a.rope_dim / 2;
 #pragma unroll
@@ -256,9 +257,9 @@ __global__ void __launch_bounds__(NW_ * 64)
 #pragma unroll
         for (int hh = 0; hh <= G; ++hh) {
           uint16_t* row = s_rot + hh * D;
-          const uint16_t x0 = row[i], x1 = row[i + half];
+          const uint16_t x0 = row[i], x1 = row[i + D / 2];
           row[i] = rope_first(x0, x1, rcs[r].x, rcs[r].y);
-          row[i + half] = rope_second(x0, x1, rcs[r].x, rcs[r].y);
+          row[i + D / 2] = rope_second(x0, x1, rcs[r].x, rcs[r].y);
         }
       }
     }

@@ -191,7 +191,7 @@ hipError_t rope_append_launch(int B, int T, int Hq, int Hkv, int D, int cap, int
                               uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
                               const int32_t* pos, const double* table, hipStream_t stream);
 // cos / sin of every rotate-half pair at position pos[b]: table [B, R / 2, 2] doubles.
-hipError_t rope_table_launch(int B, int R, double base, const int32_t* pos, double* table,
+hipError_t rope_table_launch(int B, int R, int D, double base, const int32_t* pos, double* table,
                              hipStream_t stream);
 
 // Flags of the B * T query tokens at positions q_pos[b] + t.

@@ -218,9 +218,9 @@ __global__ void __launch_bounds__(64)
 // Rotary embedding fused with the cache append ("Gemma support" pull request, Summary: own
 // RoPE base on sliding layers, proportional RoPE; "Gemma4-26B-A4B on Apple Silicon",
 // Results (Break 4) and Ablations / negative controls: partial rotary on the low part of
-// the head dimension on full layers).  The first R elements rotate in rotate-half pairs
-// (i, i + R/2) by pos * base^(-2i/R); the rest pass through; double precision, rounded once
-// to bf16 (nearest, ties to even).  One block of D threads per row (a thread per element):
+// the head dimension on full layers).  Rotate-half pairs (i, i + D/2) with i < R/2 turn by
+// pos * base^(-2i/D); the rest pass through; double precision, rounded once to bf16
+// (nearest, ties to even).  One block of D threads per row (a thread per element):
 // q rows -> q_out, k rows -> their cache slot, v rows copied unrotated to theirs (no k / v
 // rows without a cache).  Every thread reads its element and its partner before a barrier
 // and writes after it, so q_out may alias q.
@@ -258,27 +258,27 @@ __global__ void __launch_bounds__(512)
     rotate = is_k;
   }
   uint16_t y;
-  if (table && rotate && d < R) {  // one token (T = 1): the angles of the cos / sin table
-    const int half = R / 2, i = d < half ? d : d - half;
-    const double cs = table[((size_t)b * half + i) * 2], sn = table[((size_t)b * half + i) * 2 + 1];
-    y = d < half ? rope_first(src[i], src[i + half], cs, sn)
-                 : rope_second(src[i], src[i + half], cs, sn);
+  const int H = D / 2, i = d < H ? d : d - H;
+  if (table && rotate && 2 * i < R) {  // one token (T = 1): the angles of the cos / sin table
+    const int n = R / 2;
+    const double cs = table[((size_t)b * n + i) * 2], sn = table[((size_t)b * n + i) * 2 + 1];
+    y = d < H ? rope_first(src[i], src[i + H], cs, sn) : rope_second(src[i], src[i + H], cs, sn);
   } else {
-    y = rope_element(src, d, rotate ? R : 0, base, p);
+    y = rope_element(src, d, D, rotate ? R : 0, base, p);
   }
   __syncthreads();  // every element and partner of the row is read before any write
   dst[d] = y;
 }
 
-// Thread (b, i): cos and sin of rotate-half pair i at position pos[b].
+// Thread (b, i): cos and sin of rotate-half pair i (of a D-element head) at position pos[b].
 __global__ void __launch_bounds__(256)
-    rope_table_kernel(int B, int R, double base, const int32_t* pos, double* table) {
+    rope_table_kernel(int B, int R, int D, double base, const int32_t* pos, double* table) {
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = R / 2;
   if (e >= (long long)B * half) return;
   const int b = (int)(e / half), i = (int)(e % half);
   double cs, sn;
-  rope_angle(i, R, base, pos[b], &cs, &sn);
+  rope_angle(i, D, base, pos[b], &cs, &sn);
   table[2 * e] = cs;
   table[2 * e + 1] = sn;
 }
@@ -367,12 +367,12 @@ hipError_t rope_append_launch(int B, int T, int Hq, int Hkv, int D, int cap, int
   return hipGetLastError();
 }
 
-hipError_t rope_table_launch(int B, int R, double base, const int32_t* pos, double* table,
-                             hipStream_t stream) {
+hipError_t rope_table_launch(int B, int R, int D, double base, const int32_t* pos,
+                             double* table, hipStream_t stream) {
   const long long n = (long long)B * (R / 2);
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     B, R, base, pos, table);
+                     B, R, D, base, pos, table);
   return hipGetLastError();
 }
 

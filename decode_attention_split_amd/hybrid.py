@@ -125,13 +125,14 @@ class HybridKVCache:
                                g.rotary_dim, stream=stream)
 
     def rope_tables(self, pos, stream=None):
-        """cos / sin tables at pos, one per (base, rotary_dim) among the rotary layers, keyed
-        by that pair; every layer of a type reads its type's table."""
+        """cos / sin tables at pos, one per (base, rotary_dim, head_dim) among the rotary
+        layers, keyed by that triple; every layer of a type reads its type's table."""
         tables = {}
         for g in self.layers:
-            key = (g.rope_base, g.rotary_dim)
+            key = (g.rope_base, g.rotary_dim, g.head_dim)
             if g.rope_base > 0 and key not in tables:
-                tables[key] = api.rope_table(pos, g.rope_base, g.rotary_dim, stream=stream)
+                tables[key] = api.rope_table(pos, g.rope_base, g.rotary_dim, g.head_dim,
+                                             stream=stream)
         return tables
 
     def decode_rope_append(self, layer: int, q, q_out, k_new, v_new, pos, ctx_lens, q_pos,
@@ -164,7 +165,8 @@ class HybridKVCache:
                 if fused and self.owns_cache(li):
                     self.decode_rope_append(li, q_list[li], qo, k_new_list[li], v_new_list[li],
                                             pos, ctx_lens, q_pos,
-                                            tables[(g.rope_base, g.rotary_dim)], out=outs[li],
+                                            tables[(g.rope_base, g.rotary_dim, g.head_dim)],
+                                            out=outs[li],
                                             deterministic=deterministic, stream=stream)
                     continue
                 self.rope_append(li, q_list[li], qo, k_new_list[li], v_new_list[li], pos,

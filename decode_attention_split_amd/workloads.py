@@ -47,7 +47,7 @@ class LayerGeom:
     softcap: float = 0.0  # <= 0: off
     scale: Optional[float] = None  # None: 1/sqrt(head_dim)
     rope_base: float = 0.0  # > 0: rotary embedding applied by the step (base)
-    rotary_dim: int = 0     # rotated elements at the low end of the head (even)
+    rotary_dim: int = 0     # rotated width R (even): pairs (i, i + D/2), i < R/2, turn
 
     @property
     def q_scale(self) -> float:

@@ -298,19 +298,20 @@ int32_t gemma_attn_decode_append_fp8(const ga_shape* shape, const ga_bf16* q, ui
 
 /*
  * cos / sin table of the rotary embedding of one token per row, at position pos[b]:
- *   table[b, i, 0] = cos(pos[b] * rope_base^(-2i/R)), table[b, i, 1] = sin(...)
- * for the R / 2 rotate-half pairs i of R = rotary_dim (definition at gemma_rope_append),
- * computed in double by the same function as gemma_rope_append's angles, so the two give
- * the same bits.  The angles depend on the position, the base and R only, so a decode step
- * computes one table per layer type (all sliding layers share one base and R, all global
- * layers another: "Gemma support" pull request, Summary) and every layer of that type
- * reads it.  table: device float64 [batch, R / 2, 2], 16-byte aligned, fully written.
- * pos: device int32 [batch].  Errors: GA_ERR_DIMS (batch < 0, R odd or negative),
- * GA_ERR_TOO_LARGE (R > 512), GA_ERR_OPTS (rope_base not finite and > 0), GA_ERR_NULL.
- * Nothing is launched when batch or R is 0.
+ *   table[b, i, 0] = cos(pos[b] * rope_base^(-2i/D)), table[b, i, 1] = sin(...)
+ * for the R / 2 turning rotate-half pairs i of R = rotary_dim and D = head_dim (definition
+ * at gemma_rope_append), computed in double by the same function as gemma_rope_append's
+ * angles, so the two give the same bits.  The angles depend on the position, the base, R
+ * and D only, so a decode step computes one table per layer type (all sliding layers share
+ * one base, R and D, all global layers another: "Gemma support" pull request, Summary) and
+ * every layer of that type reads it.  table: device float64 [batch, R / 2, 2], 16-byte
+ * aligned, fully written.  pos: device int32 [batch].  Errors: GA_ERR_DIMS (batch < 0, R
+ * odd, negative or above head_dim), GA_ERR_HEAD_DIM (head_dim not 128, 256 or 512),
+ * GA_ERR_OPTS (rope_base not finite and > 0), GA_ERR_NULL.  Nothing is launched when batch
+ * or R is 0.
  */
 int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int32_t rotary_dim,
-                         double* table, void* stream);
+                         int32_t head_dim, double* table, void* stream);
 
 /*
  * RoPE, cache append and single-token decode in one call: exactly
@@ -318,7 +319,8 @@ int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int
  *                     rotary_dim, stream)
  * followed by gemma_attn_decode_ex(shape, q_out, k_cache, v_cache, ctx_lens, q_pos, window,
  * softcap, scale, out, workspace, workspace_bytes, opts, stream), bit for bit (q_out, the
- * caches and out), where rope_table is gemma_rope_table(B, pos, rope_base, rotary_dim).
+ * caches and out), where rope_table is gemma_rope_table(B, pos, rope_base, rotary_dim,
+ * shape->head_dim).
  * q [B, Hq, D] and k_new [B, Hkv, D] are rotated at position pos[b]; v_new is appended
  * unrotated, NULL with v_cache for K = V.  q_out [B, Hq, D] device bf16, non-NULL, 16-byte
  * aligned; it may equal q and must not otherwise overlap it.  rope_table as written by
@@ -352,13 +354,15 @@ int32_t gemma_attn_decode_rope_append(const ga_shape* shape, const ga_bf16* q, g
  *   q_out[b,t,h,:] = rope(q[b,t,h,:], pos[b] + t)            (q, q_out [B, T, Hq, D])
  *   k_cache[b,g,slot(pos[b]+t),:] = rope(k_new[b,t,g,:], ...) (k_new [B, T, Hkv, D])
  *   v_cache[...] = v_new[b,t,g,:] unrotated (v_cache and v_new NULL for K = V)
- * rope(x, p): the first R = rotary_dim elements (even, 0 <= R <= D) rotate in rotate-half
- * pairs (i, i + R/2) by the angle p * rope_base^(-2i/R); elements R..D-1 pass through.
- * Sliding layers: base 10,000 over the whole head; full layers: base 1,000,000 on the low
- * part of the head only ("Gemma support" pull request, Summary: own RoPE base for sliding
- * layers, proportional RoPE; "Gemma4-26B-A4B on Apple Silicon", Results (Break 4) and
- * Ablations / negative controls; the pair layout and the frequency exponent over R are
- * this library's reading).  Computed in double, rounded once to bf16 (nearest, ties to
+ * rope(x, p): elements i and i + D/2 form rotate-half pair i; for i < R/2 (R = rotary_dim,
+ * even, 0 <= R <= D) the pair turns by the angle p * rope_base^(-2i/D), and every other
+ * element passes through.  Sliding layers: base 10,000, R = D (the whole head, rope_type
+ * default); full layers: base 1,000,000, R = D/4 (rope_type proportional: the lowest
+ * quarter of the pairs turn, their frequencies still over the whole head) ("Gemma support"
+ * pull request, Summary: own RoPE base for sliding layers, proportional RoPE; "Gemma 4 12B
+ * (unified multimodal)" record, CONTEXT_SCALING_METHOD: the rope types per layer type;
+ * "Gemma4-26B-A4B on Apple Silicon", Results (Break 4): partial rotary on the low portion
+ * of full-attention heads).  Computed in double, rounded once to bf16 (nearest, ties to
  * even).  q_out may equal q (in place).  Append rules as in gemma_kv_append_multi
  * (out-of-range positions skipped; the latest token owns a shared ring slot).  One pass
  * over q and the new rows replaces a rotary pass plus an append pass.  k_cache, k_new,

@@ -274,18 +274,20 @@ def test_append_multi_argument_checks():
 def test_rope_table_argument_checks():
     lib = _lib.load()
     P = ctypes.c_void_p
-    assert lib.gemma_rope_table(-1, P(FAKE), 1e4, 256, P(FAKE), None) == -2   # batch < 0
-    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 255, P(FAKE), None) == -2    # R odd
-    assert lib.gemma_rope_table(4, P(FAKE), 1e4, -2, P(FAKE), None) == -2     # R < 0
-    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 514, P(FAKE), None) == -14   # R > 512
-    assert lib.gemma_rope_table(4, P(FAKE), 0.0, 256, P(FAKE), None) == -12   # base <= 0
-    assert lib.gemma_rope_table(4, P(FAKE), math.inf, 256, P(FAKE), None) == -12
-    assert lib.gemma_rope_table(4, None, 1e4, 256, P(FAKE), None) == -1
-    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 256, None, None) == -1
-    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 256, P(FAKE + 8), None) == -1  # alignment
+    assert lib.gemma_rope_table(-1, P(FAKE), 1e4, 256, 256, P(FAKE), None) == -2  # batch < 0
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 255, 256, P(FAKE), None) == -2   # R odd
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, -2, 256, P(FAKE), None) == -2    # R < 0
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 258, 256, P(FAKE), None) == -2   # R > D
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 128, 100, P(FAKE), None) == -3   # D
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 128, 1024, P(FAKE), None) == -3
+    assert lib.gemma_rope_table(4, P(FAKE), 0.0, 256, 256, P(FAKE), None) == -12  # base <= 0
+    assert lib.gemma_rope_table(4, P(FAKE), math.inf, 256, 256, P(FAKE), None) == -12
+    assert lib.gemma_rope_table(4, None, 1e4, 256, 256, P(FAKE), None) == -1
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 256, 256, None, None) == -1
+    assert lib.gemma_rope_table(4, P(FAKE), 1e4, 256, 256, P(FAKE + 8), None) == -1  # align
     # nothing to compute: OK without touching a device
-    assert lib.gemma_rope_table(0, None, 1e4, 256, None, None) == 0
-    assert lib.gemma_rope_table(4, None, 1e4, 0, None, None) == 0
+    assert lib.gemma_rope_table(0, None, 1e4, 256, 256, None, None) == 0
+    assert lib.gemma_rope_table(4, None, 1e4, 0, 256, None, None) == 0
 
 
 def test_decode_rope_append_argument_checks():

@@ -43,7 +43,7 @@ def _both_routes(q, k, v, kn, vn, ctx, window, softcap, scale, kind, base, R, in
     kf, vf = k.clone(), _clone(v)
     qf = q.clone()
     qo = qf if in_place else torch.empty_like(q)
-    table = api.rope_table(pos, base, R)
+    table = api.rope_table(pos, base, R, q.shape[-1])
     out_f = api.decode_rope_append(qf, qo, kf, vf, kn, vn, pos, ctx, q_pos, window, softcap,
                                    scale, kind, table, R, split_keys=split_keys, impl=impl,
                                    deterministic=True)
@@ -160,10 +160,11 @@ def test_fused_call_rejects_bad_rotary_arguments():
     B, Hq, Hkv, D, W = 2, 4, 2, 128, 16
     q, k, v, kn, vn, ctx_t = _case(B, Hq, Hkv, D, W, api.RING, False, [3, 5], 3)
     pos = ctx_t - 1
-    for R, base in ((3, 1e4), (-2, 1e4), (D, 0.0), (D, float("inf")), (1024, 1e4)):
+    for R, base, hd in ((3, 1e4, D), (-2, 1e4, D), (D, 0.0, D), (D, float("inf"), D),
+                        (D + 2, 1e4, D), (D, 1e4, 100), (D, 1e4, 0)):
         with pytest.raises(api.GemmaAttnError):
-            api.rope_table(pos, base, R)
-    table = api.rope_table(pos, 1e4, D)
+            api.rope_table(pos, base, R, hd)
+    table = api.rope_table(pos, 1e4, D, D)
     for R in (3, D + 2, -2):
         with pytest.raises(api.GemmaAttnError):
             api.decode_rope_append(q, torch.empty_like(q), k, v, kn, vn, pos, ctx_t, pos, W,
@@ -176,14 +177,15 @@ def test_fused_call_rejects_bad_rotary_arguments():
                                1.0, api.RING, table, 64)
 
 
-@pytest.mark.parametrize("base,R", [(1e4, 256), (1e6, 128), (1e4, 2)])
-def test_rope_table_matches_definition(base, R):
-    """table[b, i] = (cos, sin) of pos[b] * base^(-2i/R), against numpy in double (angles up
-    to about 1e5 radians lose a few digits to argument reduction on either side)."""
+@pytest.mark.parametrize("base,R,D", [(1e4, 256, 256), (1e6, 128, 512), (1e4, 2, 128)])
+def test_rope_table_matches_definition(base, R, D):
+    """table[b, i] = (cos, sin) of pos[b] * base^(-2i/D) for the R/2 turning pairs, against
+    numpy in double (angles up to about 1e5 radians lose a few digits to argument reduction
+    on either side)."""
     pos = torch.tensor([0, 1, 255, 16383, 99999, -3], dtype=torch.int32, device="cuda")
-    tab = api.rope_table(pos, base, R).cpu().numpy()
+    tab = api.rope_table(pos, base, R, D).cpu().numpy()
     i = np.arange(R // 2)
-    ang = pos.cpu().numpy().astype(np.float64)[:, None] * np.power(float(base), -2.0 * i / R)
+    ang = pos.cpu().numpy().astype(np.float64)[:, None] * np.power(float(base), -2.0 * i / D)
     assert tab.shape == (6, R // 2, 2)
     np.testing.assert_allclose(tab[..., 0], np.cos(ang), rtol=0, atol=1e-10)
     np.testing.assert_allclose(tab[..., 1], np.sin(ang), rtol=0, atol=1e-10)
@@ -208,7 +210,7 @@ def test_rope_step_layer_full_size_sampled_rows(layer):
     vn = None if g.k_eq_v else synth.normal_bf16(gen, (w.batch, g.num_kv_heads, g.head_dim))
     pos_t = inp.ctx_t - 1
     max_ctx = min(w.ctx_hi, g.capacity) if g.kind == api.LINEAR else w.ctx_hi
-    table = api.rope_table(pos_t, g.rope_base, g.rotary_dim)
+    table = api.rope_table(pos_t, g.rope_base, g.rotary_dim, g.head_dim)
     q_out = torch.empty_like(inp.q)
     out = api.decode_rope_append(inp.q, q_out, inp.k, inp.v, kn.cuda(),
                                  None if vn is None else vn.cuda(), pos_t, inp.ctx_t, pos_t,
