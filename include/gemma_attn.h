@@ -322,7 +322,8 @@ int32_t gemma_rope_table(int32_t batch, const int32_t* pos, float rope_base, int
  * caches and out), where rope_table is gemma_rope_table(B, pos, rope_base, rotary_dim,
  * shape->head_dim).
  * q [B, Hq, D] and k_new [B, Hkv, D] are rotated at position pos[b]; v_new is appended
- * unrotated, NULL with v_cache for K = V.  q_out [B, Hq, D] device bf16, non-NULL, 16-byte
+ * unrotated, NULL with v_cache for K = V (the one stored row is then the rotated key, and
+ * the values are read from it as well).  q_out [B, Hq, D] device bf16, non-NULL, 16-byte
  * aligned; it may equal q and must not otherwise overlap it.  rope_table as written by
  * gemma_rope_table (may be NULL when rotary_dim is 0).  Workspace: ga_decode_workspace_bytes,
  * as for the decode.  Where the vector kernel serves the call, one launch does it all (the
@@ -353,7 +354,8 @@ int32_t gemma_attn_decode_rope_append(const ga_shape* shape, const ga_bf16* q, g
  * tokens per row at positions pos[b] + t (T = 1: decode):
  *   q_out[b,t,h,:] = rope(q[b,t,h,:], pos[b] + t)            (q, q_out [B, T, Hq, D])
  *   k_cache[b,g,slot(pos[b]+t),:] = rope(k_new[b,t,g,:], ...) (k_new [B, T, Hkv, D])
- *   v_cache[...] = v_new[b,t,g,:] unrotated (v_cache and v_new NULL for K = V)
+ *   v_cache[...] = v_new[b,t,g,:] unrotated (v_cache and v_new NULL for K = V, whose one
+ *   cached row is the rotated key, read as the value row too)
  * rope(x, p): elements i and i + D/2 form rotate-half pair i; for i < R/2 (R = rotary_dim,
  * even, 0 <= R <= D) the pair turns by the angle p * rope_base^(-2i/D), and every other
  * element passes through.  Sliding layers: base 10,000, R = D (the whole head, rope_type
