@@ -72,8 +72,8 @@ constexpr float kRescaleLog2 = 8.0f;
 // Fast-form headroom (log2 units): with the reference at the wave's first maximum, weights
 // stay below 2^64, far inside fp32 (and bf16) range for the accumulator and the sum.
 constexpr float kFastHeadroom = 64.0f;
-static_assert(NWV * WAVE_LDS + MG * ROWB + 2 * (kMfmaMaxUnits + 1) * 4 + NWV * MG * 2 * 4 +
-                      NWV * 32 * 4 + ROWB <=
+static_assert(NWV * WAVE_LDS + MG * ROWB + 2 * (kMfmaMaxUnits + 1) * 4 + kMfmaMaxUnits * 4 +
+                      NWV * MG * 2 * 4 + NWV * 32 * 4 + ROWB <=
                   160 * 1024,
               "LDS budget per work-group");
 static_assert(WAVE_LDS >= 32 * 64 * 16, "a wave's LDS holds its accumulator at the end");
@@ -157,6 +157,7 @@ decode_mfma_kernel(DecodeArgs a) {
   __shared__ float s_ml[NWV][MG][2];
   __shared__ int s_n[kMfmaMaxUnits + 1];  // valid keys per unit, then their prefix sums
   __shared__ int s_k[kMfmaMaxUnits + 1];  // work-groups per unit, then their prefix sums
+  __shared__ int s_slot[kMfmaMaxUnits];   // each unit's first slot
   __shared__ __attribute__((aligned(16))) uint16_t s_krot[ROPE ? MD : 8];  // rotated new K row
   __shared__ __attribute__((aligned(16))) uint8_t s_kq[FP8 ? MD : 16];      // its e4m3 codes
   __shared__ float s_kqs;                                                   // and scale
@@ -165,12 +166,34 @@ decode_mfma_kernel(DecodeArgs a) {
   const int lane = tid & 63, wave = uni(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.B * a.Hkv;
+  // fused append: work-group u (< R <= grid) moves unit u's new row, stored at its end;
+  // the row's position is requested here, ahead of everything, and used only there
+  const int app_u = blockIdx.x < R ? blockIdx.x : 0;
+  const int app_pos = a.new_pos && blockIdx.x < R ? a.new_pos[app_u / a.Hkv] : -1;
 
   // ---- the partition (every work-group computes it; work-group 0 also publishes it):
-  // each unit's key range, then wave 0 alone forms both prefix sums (two barriers).
-  for (int u = tid; u < R; u += NWV * 64) {
-    const int b = u / a.Hkv;
-    s_n[u + 1] = row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys).n;
+  // each unit's key range (its first slot kept for the unit's own work-groups), then wave 0
+  // alone forms both prefix sums (two barriers).
+  {
+    // every thread's loads first (a unit past R re-reads row 0), then their ranges
+    constexpr int UPT = (kMfmaMaxUnits + NWV * 64 - 1) / (NWV * 64);
+    int cx[UPT], qx[UPT];
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NWV * 64;
+      const int b = u < R ? u / a.Hkv : 0;
+      cx[i] = a.ctx[b];
+      qx[i] = a.q_pos[b];
+    }
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NWV * 64;
+      if (u < R) {
+        const RowRange rr = row_range(cx[i], qx[i], a.window, a.kind, a.cap, a.max_keys);
+        s_n[u + 1] = rr.n;
+        s_slot[u] = rr.slot_lo;
+      }
+    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -214,18 +237,16 @@ decode_mfma_kernel(DecodeArgs a) {
   __syncthreads();
   if (blockIdx.x == 0)
     for (int u = tid; u <= R; u += NWV * 64) a.plan[u] = s_k[u];
-  // fused append: work-group u (< R <= grid) moves unit u's new row (stored at the end)
-  AppendRow app;
-  {
-    const int u = blockIdx.x < R ? blockIdx.x : 0;
-    const int ub = u / a.Hkv;
-    app.load(a, ub, u % a.Hkv, appended_slot(a, ub), tid, !ROPE && !FP8 && blockIdx.x < R);
-  }
+  AppendRow app;  // (its slot is given at the store, from app_pos)
+  app.load_unplaced(a, app_u / a.Hkv, app_u % a.Hkv, tid, !ROPE && !FP8 && blockIdx.x < R);
+  auto app_store = [&]() {
+    app.place(a, appended_slot_at(a, app_pos), tid);
+    app.store(a);
+  };
   // FP8: the quantizing append of unit uu's new row w (lane: values 8 lane .. 8 lane + 7)
   // by wave 0 (codes in LDS and, when store, in the cache); every lane of wave 0 calls it
   auto new_row = [&](int uu) { return reinterpret_cast<const uint4*>(a.k_new + (size_t)uu * MD)[lane]; };
-  auto quant_append = [&](int uu, const uint4& w, bool store) {
-    const int slot = appended_slot(a, uu / a.Hkv);
+  auto quant_append = [&](int uu, const uint4& w, bool store, int slot) {
     float sc;
     const uint2 c8 = quantize_row_e4m3(w, true, &sc);
     reinterpret_cast<uint2*>(s_kq)[lane] = c8;
@@ -254,10 +275,10 @@ decode_mfma_kernel(DecodeArgs a) {
   }
   if constexpr (FP8) {
     if (a.new_pos && g_id < R && s_k[g_id + 1] == s_k[g_id] && wave == 0)
-      quant_append(g_id, new_row(g_id), true);
+      quant_append(g_id, new_row(g_id), true, appended_slot(a, g_id / a.Hkv));
   }
   if (g_id >= s_k[R]) {
-    app.store(a);
+    app_store();
     return;
   }
   // unit of this work-group: the u with s_k[u] <= g_id < s_k[u + 1]
@@ -282,8 +303,13 @@ decode_mfma_kernel(DecodeArgs a) {
   const int my_steps = wave < nsteps ? (nsteps - wave + NWV - 1) / NWV : 0;
 
   const int b = u / a.Hkv, g = u % a.Hkv;
-  const int slot_lo =
-      uni(row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys).slot_lo);
+  const int slot_lo = uni(s_slot[u]);
+  // the appended token's position, requested ahead of the query rows and waited for with
+  // them (a zero the compiler cannot see through keeps it a vector load, not one waited
+  // for at once)
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  const int new_pos_b = a.new_pos ? a.new_pos[b + zero] : -1;
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * MG;
   const int cap = a.cap;
   // ROPE: the unit's new K row, unrotated, to LDS, and the (cos, sin) pairs this thread
@@ -315,16 +341,16 @@ decode_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<uint4*>(s_q + r * ROWB + ((c ^ swz(r)) * 16)) = qp[idx];
     }
   }
+  const int new_slot = uni(appended_slot_at(a, new_pos_b));  // fused append: from k_new
   if constexpr (FP8) {
     // the unit's new row quantized (stored by the unit's first work-group); measured
     // 1 us faster per launch here than after the first rows are requested
-    if (a.new_pos && wave == 0) quant_append(u, kw, part == 0);
+    if (a.new_pos && wave == 0) quant_append(u, kw, part == 0, new_slot);
   }
 
   // ---- loads.  Tile h of step t (of this wave: the segment's step wave + NWV t) holds the
   // segment's keys seg_lo + STEP (wave + NWV t) + 16 h + 0..15.  Keys past the segment's end
   // re-read its last key (a valid row, masked), so every load is unconditional.
-  const int new_slot = appended_slot(a, b);  // fused append: read from k_new instead
   // ROPE / FP8: the appended key's index in the unit's range (-1 when it has none)
   int new_key = -1;
   if ((ROPE || FP8) && new_slot >= 0) {
@@ -694,7 +720,7 @@ decode_mfma_kernel(DecodeArgs a) {
       if (body(safe, t) != 0) break;
   }
 
-  app.store(a);
+  app_store();
   // ---- combine the waves: each leaves (m, l) per head and its accumulator (in its own
   // tile area), then wave w combines d blocks 8 w .. 8 w + 7 of all four
   l = rows_sum(l);

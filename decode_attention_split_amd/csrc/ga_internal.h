@@ -98,11 +98,13 @@ __device__ __forceinline__ RowRange unit_range(const DecodeArgs& a, int b, int c
 // Fused append: the physical slot the appended token of batch row b goes to, or -1 when
 // nothing is appended (no fused append, or a position out of range, which the plain
 // append skips too).
-__device__ __forceinline__ int appended_slot(const DecodeArgs& a, int b) {
-  if (!a.new_pos) return -1;
-  const int p = a.new_pos[b];
+// The slot of the new token at position p (-1: out of range, nothing appended).
+__device__ __forceinline__ int appended_slot_at(const DecodeArgs& a, int p) {
   if (p < 0 || (a.kind == GA_CACHE_LINEAR && p >= a.cap)) return -1;
   return a.kind == GA_CACHE_RING ? p % a.cap : p;
+}
+__device__ __forceinline__ int appended_slot(const DecodeArgs& a, int b) {
+  return a.new_pos ? appended_slot_at(a, a.new_pos[b]) : -1;
 }
 
 // Fused append: moves the new K (and V) row of unit (b, g) into its slot, bit for bit.
@@ -131,6 +133,25 @@ struct AppendRow {
                                     : ks;
     k = *ks;
     v = *vs;
+  }
+  // The same loads before the slot is known (place() gives it before store()), so the
+  // work-group does not wait for the position at its start.
+  __device__ __forceinline__ void load_unplaced(const DecodeArgs& a, int b, int g, int tid,
+                                                bool mine) {
+    const int chunks = a.D / 8;
+    on = mine && a.new_pos != nullptr && tid < chunks;  // (new_pos set: k_new is too)
+    const size_t unit = (size_t)b * a.Hkv + g;
+    dst = unit;
+    const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
+    const u32x4* ks = on ? reinterpret_cast<const u32x4*>(a.k_new) + unit * chunks + tid : q;
+    const u32x4* vs = on && a.v_dst ? reinterpret_cast<const u32x4*>(a.v_new) + unit * chunks + tid
+                                    : ks;
+    k = *ks;
+    v = *vs;
+  }
+  __device__ __forceinline__ void place(const DecodeArgs& a, int slot, int tid) {
+    on = on && slot >= 0;
+    dst = (dst * a.cap + (on ? slot : 0)) * (a.D / 8) + tid;
   }
   __device__ __forceinline__ void store(const DecodeArgs& a) const {
     if (!on) return;
