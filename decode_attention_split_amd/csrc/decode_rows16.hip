@@ -90,7 +90,8 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   const bool row_on = row_token(l16) < a.T;  // this lane's row is l16
   const size_t row = row_index(l16);
 
-  const RowRange r = unit_range(a, b, chunk);
+  const int ctx_b = a.ctx[b], qpos_b = a.q_pos[b];  // (read once: the row ranges below too)
+  const RowRange r = unit_range_of(a, ctx_b, qpos_b, chunk);
   const int k_begin = split * a.split_keys;
   const int k_end = min(r.n, k_begin + a.split_keys);
   if (k_begin >= k_end) {
@@ -107,8 +108,8 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   // the row's own valid positions (empty: lo > hi)
   int row_lo = 1, row_hi = 0;
   if (row_on) {
-    const RowRange rr = row_range(a.ctx[b], a.q_pos[b] + row_token(l16), a.window, a.kind,
-                                  a.cap, a.max_keys);
+    const RowRange rr = row_range(ctx_b, qpos_b + row_token(l16), a.window, a.kind, a.cap,
+                                  a.max_keys);
     if (rr.n > 0) {
       row_lo = rr.lo;
       row_hi = rr.hi;
@@ -119,12 +120,25 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   // read per product, which keeps the registers for the K / V tiles in flight and the
   // accumulators
   char* s_q = s_mem;
+  // this wave's chunks j = wave, wave + NW, ... requested together; at head_dim <= 256 they
+  // go to LDS only once the first tiles are requested too (so those do not wait for them)
+  constexpr int QJ = (NJ + NW - 1) / NW;
+  constexpr bool Q_LATE = D <= 256;
+  u32x4_t qv[QJ];
   {
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + row * D);
 #pragma unroll
-    for (int j = wave; j < NJ; j += NW)
-      *reinterpret_cast<u32x4_t*>(s_q + l16 * QROWB + (lg + 4 * j) * 16) = qp[4 * j + lg];
+    for (int i = 0; i < QJ; ++i) qv[i] = qp[4 * min(wave + NW * i, NJ - 1) + lg];
   }
+  __builtin_amdgcn_sched_barrier(0);  // (issued before the tiles' loads, waited for first)
+  auto put_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < QJ; ++i) {
+      const int j = wave + NW * i;
+      if (j < NJ) *reinterpret_cast<u32x4_t*>(s_q + l16 * QROWB + (lg + 4 * j) * 16) = qv[i];
+    }
+  };
+  if constexpr (!Q_LATE) put_q();
   const char* q_lds = s_q + l16 * QROWB + lg * 16;
   char* ktile = s_mem + Q_BYTES + wave * NTILES * TILE_BYTES;  // this wave's K tile
   char* tile = ktile + (NTILES - 1) * TILE_BYTES;              // and V tile (K = V: the same)
@@ -191,6 +205,7 @@ __global__ void __launch_bounds__(64 * rows16_waves<D>()) decode_rows16_kernel(D
   Regs regs[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) load(regs[i], min(wave + NW * i, nt - 1));
+  if constexpr (Q_LATE) put_q();
   __syncthreads();  // the Q rows are in LDS
 
   auto step = [&](Regs& rg, int t) {

@@ -69,9 +69,11 @@ struct DecodeArgs {
 // the cache's present positions (ring: ctx - W .. ctx - 1), so its slots wrap at most
 // once.  Longer than max_union only when preconditions are violated: then it keeps its
 // newest keys, as row_range does.
-__device__ __forceinline__ RowRange unit_range(const DecodeArgs& a, int b, int chunk) {
-  if (a.T == 1) return row_range(a.ctx[b], a.q_pos[b], a.window, a.kind, a.cap, a.max_keys);
-  const int ctx = a.ctx[b], q0 = a.q_pos[b];
+// (unit_range_of: the same from row b's context length and first position, read once by
+// a caller that needs them again)
+__device__ __forceinline__ RowRange unit_range_of(const DecodeArgs& a, int ctx, int q0,
+                                                  int chunk) {
+  if (a.T == 1) return row_range(ctx, q0, a.window, a.kind, a.cap, a.max_keys);
   const int t0 = chunk * a.Tc;
   const int t1 = min(a.T, t0 + a.Tc) - 1;
   int lo = 0, hi = -1;
@@ -94,15 +96,18 @@ __device__ __forceinline__ RowRange unit_range(const DecodeArgs& a, int b, int c
   u.slot_lo = n > 0 ? (a.kind == GA_CACHE_RING ? lo % a.cap : lo) : 0;
   return u;
 }
+__device__ __forceinline__ RowRange unit_range(const DecodeArgs& a, int b, int chunk) {
+  return unit_range_of(a, a.ctx[b], a.q_pos[b], chunk);
+}
 
-// Fused append: the physical slot the appended token of batch row b goes to, or -1 when
-// nothing is appended (no fused append, or a position out of range, which the plain
+// The slot a token appended at position p goes to (-1: out of range, which the plain
 // append skips too).
-// The slot of the new token at position p (-1: out of range, nothing appended).
 __device__ __forceinline__ int appended_slot_at(const DecodeArgs& a, int p) {
   if (p < 0 || (a.kind == GA_CACHE_LINEAR && p >= a.cap)) return -1;
   return a.kind == GA_CACHE_RING ? p % a.cap : p;
 }
+// Fused append: the physical slot the appended token of batch row b goes to, or -1 when
+// nothing is appended (no fused append, or a position out of range).
 __device__ __forceinline__ int appended_slot(const DecodeArgs& a, int b) {
   return a.new_pos ? appended_slot_at(a, a.new_pos[b]) : -1;
 }
