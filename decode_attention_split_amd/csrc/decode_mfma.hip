@@ -754,7 +754,10 @@ decode_mfma_kernel(DecodeArgs a) {
     if (k_u == 1) {
       *reinterpret_cast<floatx4_t*>(a.out + (head0 + l16) * MD + d) = o * inv;
     } else {
-      *reinterpret_cast<floatx4_t*>(a.part_acc + ((size_t)g_id * MG + l16) * MD + d) = o;
+      // non-temporal: read once, by the merge, most often on another XCD (the step's
+      // 48 layers 2.117-2.118 -> 2.113-2.115 ms, three alternating pairs)
+      __builtin_nontemporal_store(
+          o, reinterpret_cast<floatx4_t*>(a.part_acc + ((size_t)g_id * MG + l16) * MD + d));
     }
   }
   if (k_u > 1 && wave == 0 && lg == 0) {
